@@ -1,0 +1,410 @@
+"""Pins for the CPU oracle: checks against what the paper and mathematics fix.
+
+Each ``pin_*`` function raises AssertionError on a mismatch. They are run by
+``test_oracle_pins.py`` against the oracle as written, and by
+``test_oracle_mutations.py`` against copies of the oracle with one planted
+mistake each, to show that a plausible mistake fails at least one pin.
+
+Brute-force references here are written independently of the oracle: plain
+Python loops and ``sorted`` over explicit (score, index) keys, ``math.fsum``
+dot products, and torch's float64 softmax for the dense-attention special case.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from sparse_long_context_head_amd.workload import f32_to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def bits(a) -> np.ndarray:
+    return f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+def as_float(b) -> np.ndarray:
+    """Independent bf16 decode for the brute-force side (struct-free shift)."""
+    return np.frombuffer((np.asarray(b, np.uint16).astype(np.uint32) << 16).tobytes(),
+                         dtype=np.float32).astype(np.float64).reshape(np.shape(b))
+
+
+def brute_dot(a, b) -> float:
+    return math.fsum(float(x) * float(y) for x, y in zip(a, b))
+
+
+def brute_topk(scores, idx, k):
+    """Rank each element against all others: larger score first, then lower index."""
+    n = len(scores)
+    chosen = []
+    for i in range(n):
+        better = 0
+        for j in range(n):
+            if scores[j] > scores[i] or (scores[j] == scores[i] and idx[j] < idx[i]):
+                better += 1
+        if better < k:
+            chosen.append(int(idx[i]))
+    return sorted(chosen)
+
+
+def brute_exact_support(q, keys, length, k):
+    s = [brute_dot(q, keys[i]) for i in range(length)]
+    return brute_topk(s, list(range(length)), k), s
+
+
+def brute_attention(scores_sel, v_sel, d):
+    e = torch.tensor([float(x) for x in scores_sel], dtype=torch.float64) / math.sqrt(d)
+    w = torch.softmax(e, dim=0)
+    return (w[:, None] * torch.tensor(np.asarray(v_sel, dtype=np.float64))).sum(0).numpy()
+
+
+def tiny_problem(seed, d=8, length=40, hq=2, hkv=1, n_steps=12, integer=True, rho=0.9):
+    """Tiny inputs; integer-valued keys make exact score ties common."""
+    rng = np.random.default_rng(seed)
+    if integer:
+        k = rng.integers(-3, 4, size=(1, hkv, length + n_steps, d)).astype(np.float32)
+        v = rng.integers(-4, 5, size=(1, hkv, length + n_steps, d)).astype(np.float32)
+    else:
+        k = rng.standard_normal((1, hkv, length + n_steps, d)).astype(np.float32)
+        v = rng.standard_normal((1, hkv, length + n_steps, d)).astype(np.float32)
+    qs = [rng.standard_normal((1, hq, d))]
+    for _ in range(40 + n_steps):
+        qs.append(rho * qs[-1] + math.sqrt(1 - rho * rho) * rng.standard_normal((1, hq, d)))
+    q = np.stack(qs).astype(np.float32)   # [n, 1, hq, d]
+    if integer:
+        q = np.round(q * 2) / 2
+    return bits(k), bits(v), bits(q)
+
+
+# ----------------------------------------------------------------------------
+# Pins
+# ----------------------------------------------------------------------------
+
+def pin_bf16_decode(o):
+    assert o.bf16_to_f64(np.array([0x3F80], np.uint16))[0] == 1.0
+    assert o.bf16_to_f64(np.array([0xBF80], np.uint16))[0] == -1.0
+    assert o.bf16_to_f64(np.array([0x4049], np.uint16))[0] == 3.140625
+    assert o.bf16_to_f64(np.array([0x0001], np.uint16))[0] == 2.0 ** -133
+    assert o.bf16_to_f64(np.array([0x7F7F], np.uint16))[0] == (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def pin_normalize(o):
+    q = np.zeros(8, np.float32)
+    q[0], q[1] = 3.0, 4.0
+    qb = o.normalize_query(bits(q))
+    assert qb.dtype == np.float32
+    assert qb[0] == np.float32(0.6) and qb[1] == np.float32(0.8) and not np.any(qb[2:])
+    assert not np.any(o.normalize_query(bits(np.zeros(8))))
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        x = rng.standard_normal(128)
+        qb = o.normalize_query(bits(x)).astype(np.float64)
+        assert abs(math.sqrt(math.fsum(qb * qb)) - 1.0) < 1e-6
+        assert np.all(np.sign(qb) == np.sign(as_float(bits(x))))
+        # Self-similarity is 1 (Eq. (6) with c = t).
+        assert abs(o.cosine_recall(qb.astype(np.float32), [qb.astype(np.float32)])[0] - 1.0) < 1e-6
+
+
+def pin_top_k(o):
+    rng = np.random.default_rng(5)
+    for trial in range(60):
+        n = int(rng.integers(1, 30))
+        s = rng.integers(-3, 4, size=n).astype(np.float64)      # many ties
+        idx = np.sort(rng.choice(200, size=n, replace=False))
+        k = int(rng.integers(1, 12))
+        assert list(o.top_k(idx, s, k)) == brute_topk(list(s), list(idx), k), trial
+
+
+def pin_top_r(o):
+    rho = [0.5, 0.9, 0.9, -1.0, 0.7]
+    r, m = o.top_r(rho, 3)
+    assert list(r) == [1, 2, 4] and m == 0.9
+    r, m = o.top_r(rho[:2], 4)
+    assert list(r) == [1, 0]
+    r, m = o.top_r([], 4)
+    assert list(r) == [] and m == -math.inf
+
+
+def pin_window_and_union(o):
+    assert list(o.recent_window(10, 3)) == [7, 8, 9]
+    assert list(o.recent_window(2, 5)) == [0, 1]
+    assert list(o.recent_window(4, 0)) == []
+    sup = [np.array([1, 5, 9]), np.array([2, 5]), np.array([0, 9])]
+    assert list(o.candidate_set(sup, [0, 2], 12, 2)) == [0, 1, 5, 9, 10, 11]
+    assert list(o.candidate_set(sup, [1], 6, 3)) == [2, 3, 4, 5]
+
+
+def pin_dense_special_case(o):
+    """K >= L: sparse attention over all keys is textbook dense softmax attention."""
+    rng = np.random.default_rng(7)
+    for d, length in ((8, 17), (128, 33)):
+        q = bits(rng.standard_normal((2, 3, d)))
+        k = bits(rng.standard_normal((2, 1, length, d)))
+        v = bits(rng.standard_normal((2, 1, length, d)))
+        out, sel = o.exact_topk_attention(q, k, v, length, length + 5)
+        for b in range(2):
+            for h in range(3):
+                assert list(sel[b][h]) == list(range(length))
+                qt = torch.tensor(as_float(q[b, h]))
+                kt = torch.tensor(as_float(k[b, 0]))
+                vt = torch.tensor(as_float(v[b, 0]))
+                ref = torch.softmax(kt @ qt / math.sqrt(d), dim=0) @ vt
+                np.testing.assert_allclose(out[b, h], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def pin_softmax_properties(o):
+    rng = np.random.default_rng(11)
+    d = 16
+    s = rng.standard_normal(9) * 10
+    eye = np.eye(9)
+    w = o.sparse_softmax_v(s, eye, d)
+    assert np.all(w >= 0) and abs(w.sum() - 1) < 1e-12
+    ref = torch.softmax(torch.tensor(s) / 4.0, dim=0).numpy()
+    np.testing.assert_allclose(w, ref, rtol=1e-12, atol=1e-15)
+    v = rng.standard_normal((9, 5))
+    np.testing.assert_allclose(o.sparse_softmax_v(s + 123.0, v, d), o.sparse_softmax_v(s, v, d),
+                               rtol=1e-10, atol=1e-12)
+
+
+def pin_split_merge(o):
+    """Partial softmax merge over disjoint parts equals the one-shot softmax.
+
+    From the RetrievalAttention reading notes (merging the GPU-resident and the
+    retrieved attention parts): m_S = max z, Z_S = sum exp(z - m_S),
+    o_S = sum exp(z - m_S) v / Z_S, gamma_S = exp(m_S - m) Z_S / sum_S' ...
+    """
+    rng = np.random.default_rng(13)
+    d = 32
+    s = rng.standard_normal(50) * 8
+    v = rng.standard_normal((50, 6))
+    whole = o.sparse_softmax_v(s, v, d)
+    perm = rng.permutation(50)
+    parts = [perm[:17], perm[17:]]
+    ms, zs, os_ = [], [], []
+    for p in parts:
+        z = s[p] / math.sqrt(d)
+        m = z.max()
+        w = np.exp(z - m)
+        ms.append(m)
+        zs.append(w.sum())
+        os_.append(o.sparse_softmax_v(s[p], v[p], d))
+    m = max(ms)
+    denom = sum(math.exp(mi - m) * zi for mi, zi in zip(ms, zs))
+    merged = sum(math.exp(mi - m) * zi / denom * oi for mi, zi, oi in zip(ms, zs, os_))
+    np.testing.assert_allclose(merged, whole, rtol=1e-12, atol=1e-12)
+
+
+def pin_micro_example(o):
+    with open(os.path.join(GOLDEN, "micro_example.json")) as f:
+        g = json.load(f)
+    p = g["params"]
+    orc = o.ReTopKOracle(**p)
+    keys = bits(np.array(g["keys"])[None, None])
+    vals = bits(np.array(g["values"])[None, None])
+    qt = bits(np.array(g["prompt_tail_queries"])[None, None])
+    orc.init_from_prefill(qt, keys, g["prompt_len"])
+    ent = orc.cache[0][0]
+    assert [list(e[1]) for e in ent] == g["init"]["cache_support"]
+    assert [list(e[0]) for e in ent] == g["init"]["cache_qbar"]
+    for st, q in zip(g["steps"], g["decode_queries"]):
+        before = [e[0] for e in orc.cache[0][0]]
+        qb = bits(np.array(q)[None, None])
+        rho = o.cosine_recall(o.normalize_query(qb[0, 0]), before)
+        np.testing.assert_allclose(rho, st["rho"], rtol=0, atol=1e-7)
+        rec = orc.step(qb, keys, vals, st["length"], st["t_dec"])
+        assert rec.path[0, 0] == (o.EXACT if st["path"] == "exact" else o.REUSE), st["t_dec"]
+        assert abs(rec.rho_max[0, 0] - st["rho_max"]) < 1e-7
+        assert list(rec.retrieved[0][0]) == st["retrieved"]
+        if st["candidates"] is None:
+            assert rec.candidates[0][0] is None
+        else:
+            assert list(rec.candidates[0][0]) == st["candidates"]
+        assert rec.n_cand[0, 0] == st["n_cand"]
+        assert list(rec.support[0][0]) == st["support"]
+        assert list(rec.support_scores[0][0]) == st["support_scores"]
+        np.testing.assert_allclose(rec.out[0, 0], st["out"], rtol=1e-12, atol=1e-12)
+        assert [list(e[1]) for e in orc.cache[0][0]] == st["cache_support_after"]
+
+
+def _run(o, seed, n_steps=12, **kw):
+    params = dict(batch=1, n_q_heads=2, n_kv_heads=1, head_dim=8, top_k=6, cache_cap=4,
+                  window=3, top_r=2, refresh_every=0, tau=0.85)
+    params.update(kw)
+    length0 = 40
+    k, v, q = tiny_problem(seed, d=params["head_dim"], length=length0,
+                           hq=params["n_q_heads"], hkv=params["n_kv_heads"], n_steps=n_steps)
+    orc = o.ReTopKOracle(**params)
+    n0 = min(params["cache_cap"], length0)
+    q_tail = np.ascontiguousarray(q[40 - n0:40].transpose(1, 2, 0, 3))
+    orc.init_from_prefill(q_tail, k, length0)
+    return orc, params, k, v, q, length0
+
+
+def pin_forced_exact(o):
+    """tau > 1: every step is exact and equals brute-force Exact Top-K attention."""
+    for seed in (1, 2):
+        orc, p, k, v, q, l0 = _run(o, seed, tau=2.0)
+        d = p["head_dim"]
+        for t in range(1, 10):
+            length = l0 + t
+            rec = orc.step(q[40 + t - 1], k, v, length, t)
+            for h in range(p["n_q_heads"]):
+                assert rec.path[0, h] == o.EXACT
+                qf = as_float(q[40 + t - 1, 0, h])
+                kf = as_float(k[0, 0])
+                sup, s = brute_exact_support(qf, kf, length, p["top_k"])
+                assert list(rec.support[0][h]) == sup, (seed, t, h)
+                ref = brute_attention([s[i] for i in sup], as_float(v[0, 0, sup]), d)
+                np.testing.assert_allclose(rec.out[0, h], ref, rtol=1e-10, atol=1e-12)
+                # The cache stores S_hat_t = S_t on exact steps.
+                assert list(orc.cache[0][h][-1][1]) == sup
+
+
+def pin_forced_reuse_and_candidates(o):
+    """tau <= -1, T_r = 0: every step reuses; A_t, M_t and S_hat_t follow Eqs. (6)-(11)."""
+    for seed in (3, 4, 5):
+        orc, p, k, v, q, l0 = _run(o, seed, tau=-2.0)
+        kk, r, w = p["top_k"], p["top_r"], p["window"]
+        for t in range(1, 12):
+            length = l0 + t
+            before = [[(e[0].copy(), list(e[1])) for e in orc.cache[0][h]]
+                      for h in range(p["n_q_heads"])]
+            rec = orc.step(q[40 + t - 1], k, v, length, t)
+            for h in range(p["n_q_heads"]):
+                assert rec.path[0, h] == o.REUSE
+                qf = as_float(q[40 + t - 1, 0, h])
+                nq = math.sqrt(math.fsum(x * x for x in qf))
+                qbar = [float(np.float32(x / nq)) for x in qf]
+                rho = [brute_dot(qbar, e[0]) for e in before[h]]
+                ranked = sorted(range(len(rho)), key=lambda c: (-rho[c], c))[:r]
+                assert list(rec.retrieved[0][h]) == ranked
+                assert abs(rec.rho_max[0, h] - max(rho)) < 1e-12
+                pool = set(range(max(0, length - w), length))
+                for c in ranked:
+                    pool |= set(before[h][c][1])
+                cand = sorted(pool)
+                assert list(rec.candidates[0][h]) == cand
+                assert rec.n_cand[0, h] == len(cand) <= r * kk + w
+                sc = [brute_dot(qf, as_float(k[0, 0, i])) for i in cand]
+                sel = brute_topk(sc, cand, kk)
+                assert list(rec.support[0][h]) == sel
+                assert len(sel) == min(kk, len(cand))
+                exact, _ = brute_exact_support(qf, as_float(k[0, 0]), length, kk)
+                if set(exact) <= pool:
+                    assert sel == exact      # reranking recovers S_t
+                assert list(orc.cache[0][h][-1][1]) == sel
+
+
+def pin_refresh_schedule(o):
+    orc, p, k, v, q, l0 = _run(o, 6, tau=-2.0, refresh_every=3)
+    for t in range(1, 11):
+        rec = orc.step(q[40 + t - 1], k, v, l0 + t, t)
+        want = o.EXACT if t % 3 == 0 else o.REUSE
+        assert rec.refresh == (t % 3 == 0)
+        assert all(rec.path[0, h] == want for h in range(p["n_q_heads"])), t
+
+
+def pin_fallback_threshold(o):
+    """Strict rho_max < tau: with tau equal to rho_max the step reuses."""
+    orc, p, k, v, q, l0 = _run(o, 7, tau=0.0)
+    qb = q[40]
+    rhos = []
+    for h in range(p["n_q_heads"]):
+        qbar = o.normalize_query(qb[0, h])
+        rhos.append(max(o.cosine_recall(qbar, [e[0] for e in orc.cache[0][h]])))
+    orc.tau = rhos[0]
+    rec = orc.step(qb, k, v, l0 + 1, 1)
+    assert rec.path[0, 0] == o.REUSE
+    orc2, *_ = _run(o, 7, tau=0.0)
+    orc2.tau = float(np.nextafter(rhos[0], 2.0))
+    rec2 = orc2.step(qb, k, v, l0 + 1, 1)
+    assert rec2.path[0, 0] == o.EXACT
+
+
+def pin_window_covers_history(o):
+    """W >= L_t: A_t holds every key, so reuse returns the Exact Top-K support."""
+    orc, p, k, v, q, l0 = _run(o, 8, tau=-2.0, window=1000)
+    for t in range(1, 8):
+        length = l0 + t
+        rec = orc.step(q[40 + t - 1], k, v, length, t)
+        for h in range(p["n_q_heads"]):
+            exact, _ = brute_exact_support(as_float(q[40 + t - 1, 0, h]), as_float(k[0, 0]),
+                                           length, p["top_k"])
+            assert rec.path[0, h] == o.REUSE and list(rec.support[0][h]) == exact
+
+
+def pin_fifo(o):
+    orc = o.ReTopKOracle(batch=1, n_q_heads=1, n_kv_heads=1, head_dim=4, top_k=2,
+                         cache_cap=3, window=1, top_r=1, refresh_every=0, tau=0.5)
+    pushed = []
+    for n in range(8):
+        qb = np.full(4, n, np.float32)
+        orc.push(0, 0, qb, np.array([n, n + 1]))
+        pushed.append(n)
+        ent = orc.cache[0][0]
+        assert len(ent) == min(n + 1, 3)
+        assert [int(e[0][0]) for e in ent] == pushed[-3:]
+    # Both paths update the cache: step 1 reuses, step 2 is a scheduled refresh.
+    orc, p, k, v, q, l0 = _run(o, 9, tau=-2.0, cache_cap=8, refresh_every=2)
+    for t, path in ((1, o.REUSE), (2, o.EXACT)):
+        old = [list(e[1]) for e in orc.cache[0][0]]
+        rec = orc.step(q[40 + t - 1], k, v, l0 + t, t)
+        assert rec.path[0, 0] == path
+        ent = orc.cache[0][0]
+        assert len(ent) == 8
+        assert [list(e[1]) for e in ent[:-1]] == old[1:]
+        assert list(ent[-1][1]) == list(rec.support[0][0])
+        qf = as_float(q[40 + t - 1, 0, 0])
+        nq = math.sqrt(math.fsum(x * x for x in qf))
+        assert list(ent[-1][0]) == [np.float32(x / nq) for x in qf]
+
+
+def pin_init(o):
+    orc, p, k, v, q, l0 = _run(o, 10, cache_cap=5)
+    n0 = 5
+    for h in range(p["n_q_heads"]):
+        ent = orc.cache[0][h]
+        assert len(ent) == n0
+        for i, (qb, sup) in enumerate(ent):
+            pos = l0 - n0 + i
+            qf = as_float(q[40 - n0 + i, 0, h])
+            exp_sup, _ = brute_exact_support(qf, as_float(k[0, 0]), pos + 1, p["top_k"])
+            assert list(sup) == exp_sup
+            assert all(idx <= pos for idx in sup)
+
+
+def pin_gqa_mapping(o):
+    """Query head h reads KV head floor(h * Hkv / Hq): 4 q heads over 2 KV heads."""
+    rng = np.random.default_rng(12)
+    d, length = 8, 9
+    q = bits(rng.standard_normal((1, 4, d)))
+    k = bits(rng.standard_normal((1, 2, length, d)))
+    v = bits(rng.standard_normal((1, 2, length, d)))
+    out, _ = o.exact_topk_attention(q, k, v, length, length)
+    for h in range(4):
+        g = h // 2
+        s = [brute_dot(as_float(q[0, h]), as_float(k[0, g, i])) for i in range(length)]
+        ref = brute_attention(s, as_float(v[0, g]), d)
+        np.testing.assert_allclose(out[0, h], ref, rtol=1e-10, atol=1e-12)
+    # The decode step keeps the same mapping: forced-exact steps, 4 q heads, 2 KV heads.
+    orc, p, k, v, q, l0 = _run(o, 14, tau=2.0, n_q_heads=4, n_kv_heads=2)
+    for t in (1, 2):
+        length = l0 + t
+        rec = orc.step(q[40 + t - 1], k, v, length, t)
+        for h in range(4):
+            sup, sc = brute_exact_support(as_float(q[40 + t - 1, 0, h]), as_float(k[0, h // 2]),
+                                          length, p["top_k"])
+            assert list(rec.support[0][h]) == sup
+            ref = brute_attention([sc[i] for i in sup], as_float(v[0, h // 2, sup]), p["head_dim"])
+            np.testing.assert_allclose(rec.out[0, h], ref, rtol=1e-10, atol=1e-12)
+
+
+ALL_PINS = [pin_bf16_decode, pin_normalize, pin_top_k, pin_top_r, pin_window_and_union,
+            pin_dense_special_case, pin_softmax_properties, pin_split_merge, pin_micro_example,
+            pin_forced_exact, pin_forced_reuse_and_candidates, pin_refresh_schedule,
+            pin_fallback_threshold, pin_window_covers_history, pin_fifo, pin_init,
+            pin_gqa_mapping]
