@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the ReTopK decode-step attention path on one MI355X.
+
+A step is one retopk_decode_step call on one attention layer (recall, path
+decision, candidate union, candidate scores, rerank, the exact path for heads
+that fall back or refresh, softmax-V and the cache update). Layers are
+rotated, as a decoder visits them token by token, over enough distinct KV
+buffers (each with its own handle and query-support caches) that no layer's
+keys stay in the 256 MB Infinity Cache between its steps. Inputs are
+resident in HBM before the timed region; nothing is allocated inside it.
+
+Prints one JSON line: the metric is microseconds per decode step per layer
+(lower is better) on the 128K-context, K = 512 GQA layer, with the exact
+Top-K baseline, a forced-reuse run, the path mix, a per-kernel breakdown, the
+roofline of the full-history score kernel and the CPU oracle baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ReTopK decode attn µs/step/layer @128K K=512 (HBM GB/s %peak; vs exact Top-K)"
+HBM_PEAK_GBS = 8000.0
+ROW_BYTES = 256  # one bf16 key or value row of 128 dims
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2048, help="timed layer-steps")
+    ap.add_argument("--warmup", type=int, default=64, help="untimed layer-steps before timing")
+    ap.add_argument("--workload", default="headline128k")
+    ap.add_argument("--layers", type=int, default=0, help="rotated layers (0: enough to exceed 1 GiB of KV)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["natural", "exact", "reuse"], default=None,
+                    help="run one timed leg only (for profiler runs)")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "sparse_long_context_head_amd", "csrc", "retopk_kernels.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rows = json.load(f)
+    for r in rows:
+        if r.get("kernel") == kernel and r.get("workload") == workload and \
+                r.get("kernel_source_sha") == kernel_source_hash():
+            return r.get("hbm_bytes_per_launch")
+    return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path has no "
+              f"multi-GPU leg", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from sparse_long_context_head_amd import binding as B
+    from sparse_long_context_head_amd.workload import WORKLOADS, generate
+
+    wl = WORKLOADS[args.workload]
+    kv_bytes = 2 * wl.batch * wl.n_kv_heads * wl.max_len * ROW_BYTES
+    nl = args.layers or max(1, math.ceil((1 << 30) / kv_bytes))
+    n_pos = math.ceil((args.warmup + args.steps) / nl)
+    if n_pos > wl.decode_steps:
+        wl = wl.replace(decode_steps=n_pos)
+    L0, G = wl.prompt_len, wl.n_q_heads // wl.n_kv_heads
+    log(f"workload {wl.name}: B={wl.batch} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} L0={L0} "
+        f"K={wl.top_k}; {nl} rotated layers; {n_pos} decode positions")
+    t0 = time.time()
+    data = generate(wl)
+    log(f"generated inputs in {time.time() - t0:.1f}s")
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    k0 = B.bf16_tensor(data["k"], dev)
+    v0 = B.bf16_tensor(data["v"], dev)
+    q_tail = B.bf16_tensor(data["q_tail"], dev)
+    q_dec = B.bf16_tensor(data["q_dec"], dev)
+    ks = [k0] + [k0.clone() for _ in range(nl - 1)]
+    vs = [v0] + [v0.clone() for _ in range(nl - 1)]
+    out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def make_layers(**override):
+        layers = [B.ReTopKLayer.from_workload(wl, **override) for _ in range(nl)]
+        for l in range(nl):
+            layers[l].init_from_prefill(q_tail, ks[l], L0, stream)
+        torch.cuda.synchronize()
+        return layers
+
+    def schedule(s):
+        """layer-step s -> (layer, decode position)"""
+        return s % nl, s // nl + 1
+
+    def run(layers, s0, n, exact=False):
+        for s in range(s0, s0 + n):
+            l, pos = schedule(s)
+            if exact:
+                layers[l].exact_topk_attn(q_dec[pos - 1], ks[l], vs[l], L0 + pos, out, None, stream)
+            else:
+                layers[l].decode_step(q_dec[pos - 1], ks[l], vs[l], L0 + pos, pos, out, stream)
+
+    def timed(layers, exact=False):
+        run(layers, 0, args.warmup, exact)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run(layers, args.warmup, args.steps, exact)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps * 1000.0  # us per layer-step
+
+    def kernel_breakdown(layers, exact=False):
+        for layer in layers:
+            B.retopk_set_timing(layer.handle, True)
+            B.retopk_read_kernel_times(layer.handle)
+        run(layers, args.warmup, args.steps, exact)
+        tot = {}
+        for layer in layers:
+            for name, (ms, n) in B.retopk_read_kernel_times(layer.handle).items():
+                t = tot.setdefault(name, [0.0, 0])
+                t[0] += ms
+                t[1] += n
+            B.retopk_set_timing(layer.handle, False)
+        return {k: {"us_per_step": round(v[0] * 1000 / args.steps, 3),
+                    "us_per_launch": round(v[0] * 1000 / max(v[1], 1), 3), "launches": v[1]}
+                for k, v in tot.items() if v[1]}
+
+    result = {"metric": METRIC, "unit": "us/step/layer", "n_gpus": 1, "steps": args.steps,
+              "warmup": args.warmup, "higher_is_better": False, "scaling": "weak",
+              "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+              "config": {"workload": wl.name, "batch": wl.batch, "n_q_heads": wl.n_q_heads,
+                         "n_kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
+                         "prompt_len": L0, "top_k": wl.top_k, "cache_cap": wl.cache_cap,
+                         "window": wl.window, "top_r": wl.top_r, "tau": wl.tau,
+                         "refresh_every": wl.refresh_every, "rotated_layers": nl,
+                         "decode_positions": n_pos, "parallelism": "single GPU"}}
+
+    # --- natural ReTopK step (the headline value) ---------------------------
+    if args.only in (None, "natural"):
+        nat = make_layers()
+        init_state = nat[0].read_state()
+        us = timed(nat)
+        result["value"] = round(us, 3)
+        result["ms_per_step"] = round(us / 1000.0, 6)
+        log(f"natural ReTopK: {us:.2f} us/step/layer")
+        # path mix over the timed positions
+        p0 = args.warmup // nl + 1
+        npos = args.steps // nl
+        paths, ms = [], []
+        for layer in nat:
+            path, _, m = layer.stats(p0, npos)
+            paths.append(path)
+            ms.append(m)
+        path = np.concatenate(paths)
+        m = np.concatenate(ms)
+        exact = (path & 1) == 1
+        refresh = (path & 2) == 2
+        gexact = exact.reshape(exact.shape[0], wl.batch, wl.n_kv_heads, G).any(-1)
+        mr = m[~exact]
+        result["path_mix"] = {
+            "head_steps": int(exact.size), "reuse": round(float((~exact).mean()), 5),
+            "exact_fallback": round(float((exact & ~refresh).mean()), 5),
+            "exact_refresh": round(float(refresh.mean()), 5),
+            "kv_group_steps_with_exact": round(float(gexact.mean()), 5),
+            "M_t": {"mean": round(float(mr.mean()), 1) if mr.size else None,
+                    "p50": int(np.percentile(mr, 50)) if mr.size else None,
+                    "p90": int(np.percentile(mr, 90)) if mr.size else None,
+                    "max": int(mr.max()) if mr.size else None}}
+        for layer in nat:
+            layer.close()
+        nat = make_layers()
+        result["kernels_natural"] = kernel_breakdown(nat)
+        for layer in nat:
+            layer.close()
+
+    # --- exact Top-K baseline -----------------------------------------------
+    if args.only in (None, "exact"):
+        ex = make_layers()
+        us_ex = timed(ex, exact=True)
+        result["exact_topk_us_per_step"] = round(us_ex, 3)
+        log(f"exact Top-K: {us_ex:.2f} us/step/layer")
+        kb = kernel_breakdown(ex, exact=True)
+        result["kernels_exact"] = kb
+        for layer in ex:
+            layer.close()
+        # roofline of the full-history score kernel (all KV groups streamed per launch)
+        kq = kb.get("k_exact_qk")
+        if kq:
+            mean_len = L0 + (args.warmup + args.steps / 2) / nl
+            alg = ROW_BYTES * mean_len * wl.batch * wl.n_kv_heads \
+                + 2 * wl.batch * wl.n_q_heads * wl.head_dim
+            gbs = alg / (kq["us_per_launch"] * 1e-6) / 1e9
+            result["roofline"] = {"kernel": "k_exact_qk", "bound": "hbm",
+                                  "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                  "traffic": load_traffic("k_exact_qk", wl.name),
+                                  "algorithmic_bytes_per_launch": int(alg),
+                                  "us_per_launch": kq["us_per_launch"]}
+        if "value" in result:
+            result["speedup_vs_exact"] = round(us_ex / result["value"], 3)
+
+    # --- forced reuse (every head reuses every step) ------------------------
+    if args.only in (None, "reuse"):
+        ru = make_layers(tau=-2.0, refresh_every=0)
+        us_ru = timed(ru)
+        result["forced_reuse_us_per_step"] = round(us_ru, 3)
+        log(f"forced reuse: {us_ru:.2f} us/step/layer")
+        result["kernels_forced_reuse"] = kernel_breakdown(ru)
+        for layer in ru:
+            layer.close()
+        if "exact_topk_us_per_step" in result:
+            result["speedup_reuse_vs_exact"] = round(result["exact_topk_us_per_step"] / us_ru, 3)
+
+    # --- CPU oracle baseline ------------------------------------------------
+    if not args.no_cpu_baseline and args.only in (None, "natural"):
+        result["cpu_baseline"] = cpu_baseline(wl, data, init_state, args.cpu_seconds)
+    if "value" not in result:
+        result["value"] = None
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, data, init_state, budget_s):
+    """The CPU oracle, as written, on a bounded sample of the same workload:
+    layer 0 from the GPU's post-initialisation cache, decode steps from
+    t_dec = 1 on, until the time budget is spent."""
+    import oracle.retopk_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    orc = O.ReTopKOracle.from_workload(wl)
+    orc.set_state(*init_state)
+    L0 = wl.prompt_len
+    spent, steps, exact_steps = 0.0, 0, 0
+    while spent < budget_s and steps < wl.decode_steps:
+        t = steps + 1
+        a = time.perf_counter()
+        rec = orc.step(data["q_dec"][t - 1], data["k"], data["v"], L0 + t, t)
+        spent += time.perf_counter() - a
+        steps += 1
+        exact_steps += int(rec.path.sum())
+    us = spent / steps * 1e6
+    log(f"cpu oracle: {us:.0f} us/step/layer over {steps} steps")
+    return {"value": round(us, 1), "unit": "us/step/layer", "cores": cores, "kind": "oracle",
+            "sample": f"{steps} ReTopK decode steps (t_dec 1..{steps}) of one {wl.name} layer "
+                      f"from the post-initialisation cache, {exact_steps} exact head-steps of "
+                      f"{steps * wl.batch * wl.n_q_heads}; float64 NumPy"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,197 @@
+/*
+ * retopk.h - C ABI of the ReTopK decode-step attention library (MI355X, gfx950).
+ *
+ * The method is the one of "Recall Before You Rank: Similarity-Guided Top-K
+ * Reuse for Efficient Long-Context Attention" (ReTopK). For each query head a
+ * decode step:
+ *   1. normalises the current query and compares it by cosine similarity with a
+ *      bounded FIFO cache of C normalised past queries (Methodology, Eqs. 5-6);
+ *   2. takes the R most similar cache entries and rho_max (Eq. 7);
+ *   3. unions their stored supports with the W most recent token positions and
+ *      de-duplicates the result into the candidate set A_t (Eqs. 8-9);
+ *   4. scores the current query exactly against the candidate keys only (Eq. 10);
+ *   5. reranks to exactly K indices (Eq. 11);
+ *   6. computes softmax-weighted values over that support (Eq. 12);
+ * and takes the exact path - full-history scores (Eq. 4) and global Top-K
+ * (Eq. 1) - when rho_max < tau or on every T_r-th decode step (Reliable Reuse
+ * via Fallback and Refresh, Eq. 13). The cache is updated after either path.
+ * The path is decided on the device; a step performs no host synchronisation
+ * and no allocation.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Types. bf16 tensors are passed as uint16_t bit patterns. All tensors are
+ *   dense, row-major, C-contiguous, in device memory unless stated otherwise.
+ * Shapes. B = batch, Hq = query heads, Hkv = KV heads (Hq % Hkv == 0, Hq/Hkv
+ *   <= 16), D = head dimension (must be 128), Lmax = max_len.
+ *     q      [B, Hq, D]          bf16, post-positional-encoding query
+ *     k, v   [B, Hkv, Lmax, D]   bf16 KV cache; query head h reads KV head
+ *                                 h / (Hq / Hkv) (contiguous GQA groups)
+ *     out    [B, Hq, D]          float32 attention output
+ *   q, k and v must be 16-byte aligned; out 4-byte aligned.
+ * Positions. Token indices are 0-based. A call with visible length L reads
+ *   key/value rows 0 .. L-1 only; the caller has already written the current
+ *   token's key and value at row L-1, so the query attends to itself. The
+ *   recent window is rows max(0, L-W) .. L-1. L must not decrease between
+ *   calls on one handle.
+ * Ties. Top-K ties go to the lower token index; TopR ties go to the older
+ *   cache entry. Supports are stored and returned in ascending index order.
+ *   When fewer than K keys (or candidates) exist, all of them are taken.
+ * Ownership. The caller owns q, k, v, out and every host buffer. The library
+ *   owns the handle and all device state below it (cache and workspaces,
+ *   allocated once by retopk_create and freed by retopk_destroy).
+ * Streams. `stream` is a hipStream_t passed as void*; NULL means the default
+ *   stream. Work is enqueued asynchronously; errors of the asynchronous work
+ *   itself appear at the next synchronising call. A handle must be used from
+ *   one host thread and one stream at a time; calls that overlap on one
+ *   handle race.
+ * Errors. Every entry point returns a retopk_status. Arguments are checked
+ *   before any device work is enqueued; on error nothing is enqueued and the
+ *   handle's state is unchanged. retopk_last_error() gives a message for the
+ *   calling thread's last failure. No C++ exception crosses the ABI.
+ */
+#ifndef RETOPK_H
+#define RETOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum retopk_status {
+  RETOPK_OK = 0,
+  RETOPK_INVALID_ARG = 1,      /* null or misaligned pointer, inconsistent parameters */
+  RETOPK_OUT_OF_RANGE = 2,     /* a length, step or index outside its valid range   */
+  RETOPK_HIP_ERROR = 3,        /* a HIP runtime call or kernel launch failed         */
+  RETOPK_NOT_INITIALIZED = 4,  /* null handle                                        */
+  RETOPK_NO_DEVICE = 5         /* no usable GPU                                      */
+} retopk_status;
+
+/* Method and shape parameters (defaults of the paper's experiments:
+ * K = 512, C = W = 32, R = 4, tau = 0.85, T_r = 128). */
+typedef struct retopk_params {
+  int32_t batch;          /* B >= 1                                              */
+  int32_t n_q_heads;      /* Hq >= 1                                             */
+  int32_t n_kv_heads;     /* Hkv >= 1, divides Hq, Hq / Hkv <= 16                */
+  int32_t head_dim;       /* D, must be 128                                      */
+  int32_t max_len;        /* Lmax: rows of the k / v buffers, 1 .. 2^24          */
+  int32_t top_k;          /* K, 1 .. 8192                                        */
+  int32_t cache_cap;      /* C, 1 .. 64 (query-support cache capacity, Eq. 5)    */
+  int32_t window;         /* W >= 0 (recent-token window, Eq. 8)                 */
+  int32_t top_r;          /* R, 1 .. C (retrieved entries, Eq. 7)                */
+  int32_t refresh_every;  /* T_r >= 0; 0 disables scheduled refresh (Eq. 13)     */
+  double  tau;            /* similarity threshold: rho_max < tau takes the exact
+                             path (Eq. 13); compared against rho in float64      */
+} retopk_params;
+
+typedef struct retopk_handle retopk_handle;
+
+/* Stable message for a status code. */
+const char* retopk_status_string(retopk_status s);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* retopk_last_error(void);
+
+/* Create a handle on the current HIP device: validates *params and allocates
+ * the per-head query-support caches (empty) and every workspace at worst-case
+ * size (R*K + W candidates, Lmax scores per head). Synchronous. On success
+ * *out receives the handle; on failure *out is set to NULL. */
+retopk_status retopk_create(const retopk_params* params, retopk_handle** out);
+
+/* Free the handle and all its device memory (synchronises the device first).
+ * A NULL handle is ignored. */
+void retopk_destroy(retopk_handle* h);
+
+/* Initialise every cache from the final n0 = min(C, prompt_len) prompt queries
+ * ("initialized from the final C prompt tokens during prefill", Query-support
+ * cache paragraph). q_tail is bf16 [B, Hq, n0, D], holding the queries of
+ * prompt positions prompt_len - n0 .. prompt_len - 1 in order. The entry of
+ * position p is (q_p / ||q_p||, causal Exact Top-K support of q_p over keys
+ * 0 .. p). Entries are pushed oldest first, replacing any previous contents.
+ * 1 <= prompt_len <= Lmax. Asynchronous on `stream`. */
+retopk_status retopk_init_from_prefill(retopk_handle* h, const uint16_t* q_tail,
+                                       const uint16_t* k, int32_t prompt_len, void* stream);
+
+/* One ReTopK decode step (Eqs. 5-13) for all B * Hq heads at visible length
+ * `length` (1 .. Lmax) and decode-step offset t_dec (>= 1; refresh fires when
+ * T_r > 0 and t_dec is a multiple of T_r). Writes out [B, Hq, D] and pushes
+ * (q_bar_t, S_hat_t) into every head's cache. The path decision stays on the
+ * device: no host synchronisation, no allocation. Asynchronous on `stream`.
+ * When the handle records statistics, step t_dec is stored in slot
+ * (t_dec - 1) mod 4096 of the statistics ring. */
+retopk_status retopk_decode_step(retopk_handle* h, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, int32_t length, int32_t t_dec,
+                                 float* out, void* stream);
+
+/* Exact Top-K attention baseline (Problem Setup: Eq. 4 scores over all
+ * `length` keys, Eq. 1 global Top-K, then Eq. 12): the same full-history
+ * kernels the exact path of retopk_decode_step uses, with every head exact and
+ * the cache left untouched. out [B, Hq, D] float32. sel_out, if not NULL,
+ * receives the selected indices, int32 [B, Hq, K] ascending; rows with fewer
+ * than K keys are padded with -1. Asynchronous on `stream`. */
+retopk_status retopk_exact_topk_attn(retopk_handle* h, const uint16_t* q, const uint16_t* k,
+                                     const uint16_t* v, int32_t length, float* out,
+                                     int32_t* sel_out, void* stream);
+
+/* Copy the caches to host buffers, entries oldest first; unused slots zero.
+ *   qbar      float32 [B, Hq, C, D]   normalised queries
+ *   supp      int32   [B, Hq, C, K]   supports (ascending), padded with 0
+ *   supp_len  int32   [B, Hq, C]      support sizes
+ *   count     int32   [B, Hq]         entries held (<= C)
+ * Synchronises the device (a test and checkpoint facility, not for the step
+ * loop). */
+retopk_status retopk_read_state(retopk_handle* h, float* qbar, int32_t* supp,
+                                int32_t* supp_len, int32_t* count);
+
+/* Replace the caches from host buffers in the retopk_read_state layout
+ * (resume from a snapshot). Each count must be 0 .. C, each supp_len 0 .. K,
+ * and each support entry 0 .. Lmax-1. Synchronous. */
+retopk_status retopk_write_state(retopk_handle* h, const float* qbar, const int32_t* supp,
+                                 const int32_t* supp_len, const int32_t* count);
+
+/* Copy the decisions of the most recent retopk_decode_step (or exact call) to
+ * host buffers. Any pointer may be NULL to skip that field. Synchronises.
+ *   path        int32   [B, Hq]          1 = exact, 0 = reuse
+ *   rho_max     double  [B, Hq]          -inf when the cache was empty
+ *   retrieved   int32   [B, Hq, R]       FIFO positions (0 = oldest) of the
+ *                                        retrieved entries, best first, -1 pad
+ *   n_cand      int32   [B, Hq]          M_t (0 on exact heads)
+ *   cand        int32   [B, Hq, R*K+W]   A_t ascending, first n_cand valid
+ *   sel         int32   [B, Hq, K]       S_hat_t ascending, first sel_len valid
+ *   sel_len     int32   [B, Hq]
+ *   sel_scores  float   [B, Hq, K]       unscaled q.k of the selected keys */
+retopk_status retopk_read_step_info(retopk_handle* h, int32_t* path, double* rho_max,
+                                    int32_t* retrieved, int32_t* n_cand, int32_t* cand,
+                                    int32_t* sel, int32_t* sel_len, float* sel_scores);
+
+/* Statistics ring: per decode step and head, the path (bit 0: exact, bit 1:
+ * scheduled refresh), rho_max and M_t. Reads n_steps consecutive steps
+ * starting at decode offset first_t_dec (>= 1) into host buffers
+ * path [n_steps, B, Hq], rho_max [n_steps, B, Hq], n_cand [n_steps, B, Hq].
+ * n_steps <= 4096. Synchronises. Recording is on by default. */
+retopk_status retopk_read_stats(retopk_handle* h, int32_t first_t_dec, int32_t n_steps,
+                                uint8_t* path, double* rho_max, int32_t* n_cand);
+retopk_status retopk_set_stats(retopk_handle* h, int32_t enabled);
+
+/* Kernel timing: when enabled, every kernel launch of the handle is bracketed
+ * by HIP events recorded on the launch stream. retopk_read_kernel_times
+ * synchronises, accumulates the elapsed time of every recorded launch per
+ * kernel, writes total milliseconds and launch counts for kernel ids
+ * 0 .. n-1 (n <= retopk_kernel_count()), and clears the record. Up to 65536
+ * launches are kept between reads; later ones are not timed. */
+retopk_status retopk_set_timing(retopk_handle* h, int32_t enabled);
+retopk_status retopk_read_kernel_times(retopk_handle* h, int32_t n, double* total_ms,
+                                       int64_t* launches);
+int32_t retopk_kernel_count(void);
+const char* retopk_kernel_name(int32_t id);
+
+/* Bytes of device memory the handle holds. */
+size_t retopk_device_bytes(const retopk_handle* h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RETOPK_H */

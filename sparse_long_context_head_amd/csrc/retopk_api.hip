@@ -1,0 +1,474 @@
+// C ABI of the ReTopK decode-step attention library: handle management,
+// argument checks, launch sequencing and host-side state exchange.
+// The interface and its contracts are documented in include/retopk.h.
+
+#include "retopk.h"
+#include "retopk_internal.h"
+
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace retopk;
+
+namespace {
+
+constexpr int kMaxTimed = 65536;
+
+thread_local std::string g_last_error;
+
+retopk_status fail(retopk_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+retopk_status hip_fail(hipError_t e, const char* what) {
+  return fail(RETOPK_HIP_ERROR, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Makes the handle's device current for the duration of a call.
+class DeviceGuard {
+ public:
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&old_) != hipSuccess) old_ = -1;
+    if (old_ != dev) (void)hipSetDevice(dev);
+    dev_ = dev;
+  }
+  ~DeviceGuard() {
+    if (old_ >= 0 && old_ != dev_) (void)hipSetDevice(old_);
+  }
+
+ private:
+  int old_ = -1, dev_ = -1;
+};
+
+}  // namespace
+
+struct retopk_handle {
+  retopk_params p{};
+  Dims d{};
+  Bufs b{};
+  int device = 0;
+  std::vector<void*> allocs;
+  size_t bytes = 0;
+  bool stats = true;
+  bool timing = false;
+  std::vector<hipEvent_t> events;   // pairs (start, stop)
+  std::vector<int> event_kernel;    // kernel id of each recorded pair
+  int timed = 0;                    // pairs recorded since the last read
+
+  template <typename T>
+  hipError_t alloc(T** ptr, size_t count) {
+    const size_t n = count * sizeof(T);
+    void* raw = nullptr;
+    hipError_t e = hipMalloc(&raw, n > 0 ? n : 16);
+    if (e != hipSuccess) return e;
+    allocs.push_back(raw);
+    bytes += n;
+    *ptr = static_cast<T*>(raw);
+    return hipMemset(raw, 0, n > 0 ? n : 16);
+  }
+
+  void release() {
+    for (void* a : allocs) (void)hipFree(a);
+    allocs.clear();
+    for (hipEvent_t e : events) (void)hipEventDestroy(e);
+    events.clear();
+  }
+
+  // Run one kernel launch, bracketing it with timing events when enabled.
+  template <typename F>
+  retopk_status run(int id, hipStream_t s, F&& launch) {
+    bool timed_launch = false;
+    if (timing && timed < kMaxTimed) {
+      if (static_cast<int>(events.size()) < 2 * (timed + 1)) {
+        for (int i = 0; i < 256; ++i) {
+          hipEvent_t ev;
+          if (hipEventCreate(&ev) != hipSuccess) break;
+          events.push_back(ev);
+        }
+        event_kernel.resize(events.size() / 2);
+      }
+      if (static_cast<int>(events.size()) >= 2 * (timed + 1)) {
+        timed_launch = hipEventRecord(events[2 * timed], s) == hipSuccess;
+      }
+    }
+    const hipError_t e = launch();
+    if (e != hipSuccess) return hip_fail(e, kernel_name(id));
+    if (timed_launch && hipEventRecord(events[2 * timed + 1], s) == hipSuccess) {
+      event_kernel[timed] = id;
+      ++timed;
+    }
+    return RETOPK_OK;
+  }
+};
+
+extern "C" {
+
+const char* retopk_status_string(retopk_status s) {
+  switch (s) {
+    case RETOPK_OK: return "ok";
+    case RETOPK_INVALID_ARG: return "invalid argument";
+    case RETOPK_OUT_OF_RANGE: return "argument out of range";
+    case RETOPK_HIP_ERROR: return "HIP runtime error";
+    case RETOPK_NOT_INITIALIZED: return "handle not initialised";
+    case RETOPK_NO_DEVICE: return "no GPU device";
+  }
+  return "unknown status";
+}
+
+const char* retopk_last_error(void) { return g_last_error.c_str(); }
+
+int32_t retopk_kernel_count(void) { return kNumKernels; }
+
+const char* retopk_kernel_name(int32_t id) { return kernel_name(id); }
+
+size_t retopk_device_bytes(const retopk_handle* h) { return h ? h->bytes : 0; }
+
+retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
+  if (out == nullptr) return fail(RETOPK_INVALID_ARG, "retopk_create: out is NULL");
+  *out = nullptr;
+  if (params == nullptr) return fail(RETOPK_INVALID_ARG, "retopk_create: params is NULL");
+  const retopk_params& p = *params;
+  if (p.batch < 1 || p.n_q_heads < 1 || p.n_kv_heads < 1)
+    return fail(RETOPK_INVALID_ARG, "retopk_create: batch and head counts must be >= 1");
+  if (p.n_q_heads % p.n_kv_heads != 0)
+    return fail(RETOPK_INVALID_ARG, "retopk_create: n_q_heads must be a multiple of n_kv_heads");
+  if (p.n_q_heads / p.n_kv_heads > kMaxGroup)
+    return fail(RETOPK_INVALID_ARG, "retopk_create: at most 16 query heads per KV head");
+  if (p.head_dim != kHeadDim) return fail(RETOPK_INVALID_ARG, "retopk_create: head_dim must be 128");
+  if (p.max_len < 1 || p.max_len > (1 << 24))
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_create: max_len must be in 1 .. 2^24");
+  if (p.top_k < 1 || p.top_k > 8192) return fail(RETOPK_OUT_OF_RANGE, "retopk_create: top_k must be in 1 .. 8192");
+  if (p.cache_cap < 1 || p.cache_cap > 64)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_create: cache_cap must be in 1 .. 64");
+  if (p.window < 0) return fail(RETOPK_OUT_OF_RANGE, "retopk_create: window must be >= 0");
+  if (p.top_r < 1 || p.top_r > p.cache_cap)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_create: top_r must be in 1 .. cache_cap");
+  if (p.refresh_every < 0) return fail(RETOPK_OUT_OF_RANGE, "retopk_create: refresh_every must be >= 0");
+  if (std::isnan(p.tau)) return fail(RETOPK_INVALID_ARG, "retopk_create: tau is NaN");
+  const long long cand = static_cast<long long>(p.top_r) * p.top_k + p.window;
+  if (cand > kMaxCand)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_create: top_r * top_k + window must be <= 16384");
+  const long long bh = static_cast<long long>(p.batch) * p.n_q_heads;
+  if (bh > (1 << 20)) return fail(RETOPK_OUT_OF_RANGE, "retopk_create: batch * n_q_heads too large");
+
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return fail(RETOPK_NO_DEVICE, "retopk_create: no HIP device visible");
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(RETOPK_NO_DEVICE, "retopk_create: hipGetDevice failed");
+
+  auto* h = new (std::nothrow) retopk_handle();
+  if (h == nullptr) return fail(RETOPK_HIP_ERROR, "retopk_create: out of host memory");
+  h->p = p;
+  h->device = dev;
+  Dims& d = h->d;
+  d.B = p.batch;
+  d.Hq = p.n_q_heads;
+  d.Hkv = p.n_kv_heads;
+  d.G = p.n_q_heads / p.n_kv_heads;
+  d.max_len = p.max_len;
+  d.score_stride = (p.max_len + 15) / 16 * 16;
+  d.K = p.top_k;
+  d.C = p.cache_cap;
+  d.W = p.window;
+  d.R = p.top_r;
+  d.Tr = p.refresh_every;
+  d.cand_cap = static_cast<int>(cand);
+  d.tau = p.tau;
+
+  Bufs& b = h->b;
+  const size_t BH = static_cast<size_t>(bh);
+  const size_t D = kHeadDim;
+  hipError_t e = hipSuccess;
+  auto A = [&](auto** ptr, size_t n) {
+    if (e == hipSuccess) e = h->alloc(ptr, n);
+  };
+  A(&b.cache_qbar, BH * d.C * D);
+  A(&b.cache_supp, BH * d.C * d.K);
+  A(&b.cache_len, BH * d.C);
+  A(&b.fifo, BH * 2);
+  A(&b.qbar, BH * D);
+  A(&b.path, BH);
+  A(&b.gexact, static_cast<size_t>(d.B) * d.Hkv);
+  A(&b.rho, BH);
+  A(&b.ret, BH * d.R);
+  A(&b.retslot, BH * d.R);
+  A(&b.m, BH);
+  A(&b.cand, BH * d.cand_cap);
+  A(&b.cscore, BH * d.cand_cap);
+  A(&b.score, BH * d.score_stride);
+  A(&b.hist, BH * kNumBins);
+  A(&b.cnt, BH * 4);
+  A(&b.above, BH * d.K);
+  A(&b.bnd, BH * d.max_len);
+  A(&b.sel, BH * d.K);
+  A(&b.selsc, BH * d.K);
+  A(&b.sellen, BH);
+  A(&b.part, BH * kAttendSplit * (D + 4));
+  A(&b.done, BH);
+  A(&b.st_path, BH * kStatsCap);
+  A(&b.st_rho, BH * kStatsCap);
+  A(&b.st_m, BH * kStatsCap);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    h->release();
+    delete h;
+    return hip_fail(e, "retopk_create: device allocation");
+  }
+  *out = h;
+  return RETOPK_OK;
+}
+
+void retopk_destroy(retopk_handle* h) {
+  if (h == nullptr) return;
+  {
+    DeviceGuard guard(h->device);
+    (void)hipDeviceSynchronize();
+    h->release();
+  }
+  delete h;
+}
+
+retopk_status retopk_init_from_prefill(retopk_handle* h, const uint16_t* q_tail, const uint16_t* k,
+                                       int32_t prompt_len, void* stream) {
+  if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_init_from_prefill: NULL handle");
+  if (q_tail == nullptr || k == nullptr)
+    return fail(RETOPK_INVALID_ARG, "retopk_init_from_prefill: NULL tensor");
+  if (!aligned(q_tail, 16) || !aligned(k, 16))
+    return fail(RETOPK_INVALID_ARG, "retopk_init_from_prefill: q_tail and k must be 16-byte aligned");
+  if (prompt_len < 1 || prompt_len > h->d.max_len)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_init_from_prefill: prompt_len must be in 1 .. max_len");
+  DeviceGuard guard(h->device);
+  const Dims& d = h->d;
+  const Bufs& b = h->b;
+  auto s = static_cast<hipStream_t>(stream);
+  const int n0 = prompt_len < d.C ? prompt_len : d.C;
+  const long q_sb = static_cast<long>(d.Hq) * n0 * kHeadDim, q_sh = static_cast<long>(n0) * kHeadDim;
+  retopk_status st = h->run(kKReset, s, [&] { return launch_reset(d, b, s); });
+  for (int i = 0; i < n0 && st == RETOPK_OK; ++i) {
+    const int len = prompt_len - n0 + i + 1;  // causal: keys 0 .. p
+    const uint16_t* qi = q_tail + static_cast<long>(i) * kHeadDim;
+    st = h->run(kKRecall, s, [&] { return launch_recall(d, b, qi, q_sb, q_sh, kModeExact, 0, -1, s); });
+    if (st == RETOPK_OK) st = h->run(kKExactQK, s, [&] { return launch_exact_qk(d, b, qi, q_sb, q_sh, k, len, s); });
+    if (st == RETOPK_OK) st = h->run(kKCollect, s, [&] { return launch_collect(d, b, len, s); });
+    if (st == RETOPK_OK) st = h->run(kKFinish, s, [&] { return launch_finish(d, b, len, s); });
+    if (st == RETOPK_OK)
+      st = h->run(kKAttend, s, [&] { return launch_attend(d, b, nullptr, nullptr, nullptr, 1, s); });
+  }
+  return st;
+}
+
+retopk_status retopk_decode_step(retopk_handle* h, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, int32_t length, int32_t t_dec, float* out,
+                                 void* stream) {
+  if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_decode_step: NULL handle");
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(RETOPK_INVALID_ARG, "retopk_decode_step: NULL tensor");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 4))
+    return fail(RETOPK_INVALID_ARG, "retopk_decode_step: misaligned tensor");
+  if (length < 1 || length > h->d.max_len)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_decode_step: length must be in 1 .. max_len");
+  if (t_dec < 1) return fail(RETOPK_OUT_OF_RANGE, "retopk_decode_step: t_dec must be >= 1");
+  DeviceGuard guard(h->device);
+  const Dims& d = h->d;
+  const Bufs& b = h->b;
+  auto s = static_cast<hipStream_t>(stream);
+  const int slot = h->stats ? (t_dec - 1) % kStatsCap : -1;
+  const long q_sb = static_cast<long>(d.Hq) * kHeadDim, q_sh = kHeadDim;
+  retopk_status st =
+      h->run(kKRecall, s, [&] { return launch_recall(d, b, q, q_sb, q_sh, kModeDecode, t_dec, slot, s); });
+  if (st == RETOPK_OK) st = h->run(kKUnion, s, [&] { return launch_union(d, b, length, slot, s); });
+  if (st == RETOPK_OK) st = h->run(kKCandQK, s, [&] { return launch_cand_qk(d, b, q, k, s); });
+  if (st == RETOPK_OK) st = h->run(kKRerank, s, [&] { return launch_rerank(d, b, s); });
+  if (st == RETOPK_OK) st = h->run(kKExactQK, s, [&] { return launch_exact_qk(d, b, q, q_sb, q_sh, k, length, s); });
+  if (st == RETOPK_OK) st = h->run(kKCollect, s, [&] { return launch_collect(d, b, length, s); });
+  if (st == RETOPK_OK) st = h->run(kKFinish, s, [&] { return launch_finish(d, b, length, s); });
+  if (st == RETOPK_OK) st = h->run(kKAttend, s, [&] { return launch_attend(d, b, v, out, nullptr, 1, s); });
+  return st;
+}
+
+retopk_status retopk_exact_topk_attn(retopk_handle* h, const uint16_t* q, const uint16_t* k,
+                                     const uint16_t* v, int32_t length, float* out, int32_t* sel_out,
+                                     void* stream) {
+  if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_exact_topk_attn: NULL handle");
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(RETOPK_INVALID_ARG, "retopk_exact_topk_attn: NULL tensor");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 4) ||
+      (sel_out != nullptr && !aligned(sel_out, 4)))
+    return fail(RETOPK_INVALID_ARG, "retopk_exact_topk_attn: misaligned tensor");
+  if (length < 1 || length > h->d.max_len)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_exact_topk_attn: length must be in 1 .. max_len");
+  DeviceGuard guard(h->device);
+  const Dims& d = h->d;
+  const Bufs& b = h->b;
+  auto s = static_cast<hipStream_t>(stream);
+  const long q_sb = static_cast<long>(d.Hq) * kHeadDim, q_sh = kHeadDim;
+  retopk_status st =
+      h->run(kKRecall, s, [&] { return launch_recall(d, b, q, q_sb, q_sh, kModeExact, 0, -1, s); });
+  if (st == RETOPK_OK) st = h->run(kKExactQK, s, [&] { return launch_exact_qk(d, b, q, q_sb, q_sh, k, length, s); });
+  if (st == RETOPK_OK) st = h->run(kKCollect, s, [&] { return launch_collect(d, b, length, s); });
+  if (st == RETOPK_OK) st = h->run(kKFinish, s, [&] { return launch_finish(d, b, length, s); });
+  if (st == RETOPK_OK) st = h->run(kKAttend, s, [&] { return launch_attend(d, b, v, out, sel_out, 0, s); });
+  return st;
+}
+
+retopk_status retopk_read_state(retopk_handle* h, float* qbar, int32_t* supp, int32_t* supp_len,
+                                int32_t* count) {
+  if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_read_state: NULL handle");
+  if (qbar == nullptr || supp == nullptr || supp_len == nullptr || count == nullptr)
+    return fail(RETOPK_INVALID_ARG, "retopk_read_state: NULL buffer");
+  DeviceGuard guard(h->device);
+  const Dims& d = h->d;
+  const size_t BH = static_cast<size_t>(d.B) * d.Hq, C = d.C, K = d.K, D = kHeadDim;
+  std::vector<float> rq(BH * C * D);
+  std::vector<int32_t> rs(BH * C * K), rl(BH * C), rf(BH * 2);
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(rq.data(), h->b.cache_qbar, rq.size() * 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(rs.data(), h->b.cache_supp, rs.size() * 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(rl.data(), h->b.cache_len, rl.size() * 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(rf.data(), h->b.fifo, rf.size() * 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "retopk_read_state");
+  std::memset(qbar, 0, BH * C * D * 4);
+  std::memset(supp, 0, BH * C * K * 4);
+  std::memset(supp_len, 0, BH * C * 4);
+  for (size_t bh = 0; bh < BH; ++bh) {
+    const int head = rf[2 * bh], n = rf[2 * bh + 1];
+    const int oldest = (head - n + d.C) % d.C;
+    count[bh] = n;
+    for (int i = 0; i < n; ++i) {
+      const size_t src = bh * C + (oldest + i) % d.C, dst = bh * C + i;
+      std::memcpy(qbar + dst * D, rq.data() + src * D, D * 4);
+      const int len = rl[src];
+      supp_len[dst] = len;
+      std::memcpy(supp + dst * K, rs.data() + src * K, static_cast<size_t>(len) * 4);
+    }
+  }
+  return RETOPK_OK;
+}
+
+retopk_status retopk_write_state(retopk_handle* h, const float* qbar, const int32_t* supp,
+                                 const int32_t* supp_len, const int32_t* count) {
+  if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_write_state: NULL handle");
+  if (qbar == nullptr || supp == nullptr || supp_len == nullptr || count == nullptr)
+    return fail(RETOPK_INVALID_ARG, "retopk_write_state: NULL buffer");
+  const Dims& d = h->d;
+  const size_t BH = static_cast<size_t>(d.B) * d.Hq, C = d.C, K = d.K, D = kHeadDim;
+  std::vector<int32_t> rs(BH * C * K, 0), rl(BH * C, 0), rf(BH * 2, 0);
+  std::vector<float> rq(BH * C * D, 0.f);
+  for (size_t bh = 0; bh < BH; ++bh) {
+    const int n = count[bh];
+    if (n < 0 || n > d.C) return fail(RETOPK_OUT_OF_RANGE, "retopk_write_state: count out of range");
+    for (int i = 0; i < n; ++i) {
+      const size_t e = bh * C + i;
+      const int len = supp_len[e];
+      if (len < 1 || len > d.K) return fail(RETOPK_OUT_OF_RANGE, "retopk_write_state: supp_len out of range");
+      for (int j = 0; j < len; ++j) {
+        const int x = supp[e * K + j];
+        if (x < 0 || x >= d.max_len) return fail(RETOPK_OUT_OF_RANGE, "retopk_write_state: support index out of range");
+        rs[e * K + j] = x;
+      }
+      rl[e] = len;
+      std::memcpy(rq.data() + e * D, qbar + e * D, D * 4);
+    }
+    rf[2 * bh] = n % d.C;
+    rf[2 * bh + 1] = n;
+  }
+  DeviceGuard guard(h->device);
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(h->b.cache_qbar, rq.data(), rq.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(h->b.cache_supp, rs.data(), rs.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(h->b.cache_len, rl.data(), rl.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(h->b.fifo, rf.data(), rf.size() * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "retopk_write_state");
+  return RETOPK_OK;
+}
+
+retopk_status retopk_read_step_info(retopk_handle* h, int32_t* path, double* rho_max, int32_t* retrieved,
+                                    int32_t* n_cand, int32_t* cand, int32_t* sel, int32_t* sel_len,
+                                    float* sel_scores) {
+  if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_read_step_info: NULL handle");
+  DeviceGuard guard(h->device);
+  const Dims& d = h->d;
+  const size_t BH = static_cast<size_t>(d.B) * d.Hq;
+  hipError_t e = hipDeviceSynchronize();
+  auto copy = [&](void* dst, const void* src, size_t n) {
+    if (e == hipSuccess && dst != nullptr) e = hipMemcpy(dst, src, n, hipMemcpyDeviceToHost);
+  };
+  copy(path, h->b.path, BH * 4);
+  copy(rho_max, h->b.rho, BH * 8);
+  copy(retrieved, h->b.ret, BH * d.R * 4);
+  copy(n_cand, h->b.m, BH * 4);
+  copy(cand, h->b.cand, BH * d.cand_cap * 4);
+  copy(sel, h->b.sel, BH * d.K * 4);
+  copy(sel_len, h->b.sellen, BH * 4);
+  copy(sel_scores, h->b.selsc, BH * d.K * 4);
+  if (e != hipSuccess) return hip_fail(e, "retopk_read_step_info");
+  return RETOPK_OK;
+}
+
+retopk_status retopk_read_stats(retopk_handle* h, int32_t first_t_dec, int32_t n_steps, uint8_t* path,
+                                double* rho_max, int32_t* n_cand) {
+  if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_read_stats: NULL handle");
+  if (path == nullptr || rho_max == nullptr || n_cand == nullptr)
+    return fail(RETOPK_INVALID_ARG, "retopk_read_stats: NULL buffer");
+  if (first_t_dec < 1 || n_steps < 0 || n_steps > kStatsCap)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_read_stats: first_t_dec >= 1 and n_steps <= 4096 required");
+  DeviceGuard guard(h->device);
+  const size_t BH = static_cast<size_t>(h->d.B) * h->d.Hq;
+  hipError_t e = hipDeviceSynchronize();
+  for (int i = 0; i < n_steps && e == hipSuccess; ++i) {
+    const size_t slot = static_cast<size_t>(first_t_dec - 1 + i) % kStatsCap;
+    e = hipMemcpy(path + i * BH, h->b.st_path + slot * BH, BH, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(rho_max + i * BH, h->b.st_rho + slot * BH, BH * 8, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(n_cand + i * BH, h->b.st_m + slot * BH, BH * 4, hipMemcpyDeviceToHost);
+  }
+  if (e != hipSuccess) return hip_fail(e, "retopk_read_stats");
+  return RETOPK_OK;
+}
+
+retopk_status retopk_set_stats(retopk_handle* h, int32_t enabled) {
+  if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_set_stats: NULL handle");
+  h->stats = enabled != 0;
+  return RETOPK_OK;
+}
+
+retopk_status retopk_set_timing(retopk_handle* h, int32_t enabled) {
+  if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_set_timing: NULL handle");
+  h->timing = enabled != 0;
+  return RETOPK_OK;
+}
+
+retopk_status retopk_read_kernel_times(retopk_handle* h, int32_t n, double* total_ms, int64_t* launches) {
+  if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_read_kernel_times: NULL handle");
+  if (n < 0 || n > kNumKernels || (n > 0 && (total_ms == nullptr || launches == nullptr)))
+    return fail(RETOPK_INVALID_ARG, "retopk_read_kernel_times: bad output buffers");
+  DeviceGuard guard(h->device);
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "retopk_read_kernel_times");
+  for (int i = 0; i < n; ++i) {
+    total_ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  for (int i = 0; i < h->timed; ++i) {
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, h->events[2 * i], h->events[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "retopk_read_kernel_times: hipEventElapsedTime");
+    const int id = h->event_kernel[i];
+    if (id < n) {
+      total_ms[id] += ms;
+      launches[id] += 1;
+    }
+  }
+  h->timed = 0;
+  return RETOPK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Internal declarations shared by the ReTopK kernels and the C-ABI host code.
+// Not part of the public interface (that is include/retopk.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace retopk {
+
+constexpr int kHeadDim = 128;        // D; one bf16 key row is 256 bytes
+constexpr int kWave = 64;            // CDNA wavefront width
+constexpr int kMaxGroup = 16;        // query heads per KV head handled by one MFMA tile
+constexpr int kHistBits = 10;        // first-level histogram: top 10 bits of the ordered key
+constexpr int kNumBins = 1 << kHistBits;
+constexpr int kHistShift = 32 - kHistBits;
+constexpr int kStatsCap = 4096;      // decode steps kept in the statistics ring
+constexpr int kExactChunk = 1024;    // key rows per work item of the full-history QK kernel
+constexpr int kCollectChunk = 4096;  // scores per work item of the threshold/collect kernel
+constexpr int kAttendSplit = 8;      // work groups per head in the softmax-V kernel
+constexpr int kCandRowsPerBlock = 128;
+constexpr int kBitmapWords = 8192;   // LDS bitmap window: 262144 token positions (32 KiB)
+constexpr int kBoundaryLds = 4096;   // boundary entries resolved in LDS (32 KiB of 64-bit keys)
+constexpr int kMaxCand = 16384;      // R*K + W limit (candidate keys kept in LDS for reranking)
+
+// Problem dimensions, passed by value to every kernel.
+struct Dims {
+  int B, Hq, Hkv, G;       // G = Hq / Hkv query heads per KV head
+  int max_len;             // rows of the k / v buffers
+  int score_stride;        // row stride of the full-history score workspace (max_len rounded to 16)
+  int K, C, W, R, Tr;
+  int cand_cap;            // R*K + W
+  double tau;
+};
+
+// Device buffers owned by a handle. BH = B * Hq.
+struct Bufs {
+  // query-support cache (Eq. 5), a ring per head
+  float* cache_qbar;       // [BH, C, D]
+  int32_t* cache_supp;     // [BH, C, K]
+  int32_t* cache_len;      // [BH, C]
+  int32_t* fifo;           // [BH, 2]: next slot to write, entries held
+  // per-step workspaces
+  float* qbar;             // [BH, D]   normalised current query
+  int32_t* path;           // [BH]      1 exact, 0 reuse
+  int32_t* gexact;         // [B*Hkv]   exact heads in the KV group
+  double* rho;             // [BH]      rho_max
+  int32_t* ret;            // [BH, R]   retrieved FIFO positions, -1 pad
+  int32_t* retslot;        // [BH, R]   their ring slots
+  int32_t* m;              // [BH]      M_t
+  int32_t* cand;           // [BH, cand_cap]  A_t ascending
+  float* cscore;           // [BH, cand_cap]  q.k of A_t
+  float* score;            // [BH, score_stride]  full-history q.k
+  uint32_t* hist;          // [BH, kNumBins]  histogram of ordered score keys
+  int32_t* cnt;            // [BH, 4]   above-count, boundary-count
+  int32_t* above;          // [BH, K]   indices above the boundary bin, then resolved boundary
+  int32_t* bnd;            // [BH, max_len] indices in the boundary bin
+  int32_t* sel;            // [BH, K]   S_hat_t ascending
+  float* selsc;            // [BH, K]   q.k of S_hat_t
+  int32_t* sellen;         // [BH]
+  float* part;             // [BH, kAttendSplit, D + 4] partial softmax-V sums
+  int32_t* done;           // [BH]      arrival counter of the softmax-V work groups
+  // statistics ring
+  uint8_t* st_path;        // [kStatsCap, BH]
+  double* st_rho;          // [kStatsCap, BH]
+  int32_t* st_m;           // [kStatsCap, BH]
+};
+
+enum KernelId : int {
+  kKRecall = 0,
+  kKUnion,
+  kKCandQK,
+  kKRerank,
+  kKExactQK,
+  kKCollect,
+  kKFinish,
+  kKAttend,
+  kKReset,
+  kNumKernels
+};
+
+const char* kernel_name(int id);
+
+// Launch helpers (retopk_kernels.hip). Each returns the hipError_t of the launch.
+enum RecallMode : int { kModeDecode = 0, kModeExact = 1 };
+
+hipError_t launch_reset(const Dims& d, const Bufs& b, hipStream_t s);
+hipError_t launch_recall(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
+                         int mode, int t_dec, int stats_slot, hipStream_t s);
+hipError_t launch_union(const Dims& d, const Bufs& b, int length, int stats_slot, hipStream_t s);
+hipError_t launch_cand_qk(const Dims& d, const Bufs& b, const uint16_t* q, const uint16_t* k,
+                          hipStream_t s);
+hipError_t launch_rerank(const Dims& d, const Bufs& b, hipStream_t s);
+hipError_t launch_exact_qk(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
+                           const uint16_t* k, int length, hipStream_t s);
+hipError_t launch_collect(const Dims& d, const Bufs& b, int length, hipStream_t s);
+hipError_t launch_finish(const Dims& d, const Bufs& b, int length, hipStream_t s);
+hipError_t launch_attend(const Dims& d, const Bufs& b, const uint16_t* v, float* out,
+                         int32_t* sel_out, int push, hipStream_t s);
+
+}  // namespace retopk

@@ -1,0 +1,383 @@
+"""HIP path (through the C ABI) against the CPU oracle, element by element.
+
+Workloads are the seeded synthetic configurations of
+sparse_long_context_head_amd.workload; smaller variants keep the oracle's
+run time to seconds while still spanning several work-group tiles and a ragged
+tail. Full-size configurations are checked on sampled (batch row, KV group)
+sub-problems, which the oracle computes independently of the other heads.
+"""
+from __future__ import annotations
+
+import functools
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle.retopk_oracle as O
+from parity_util import (check_output, check_support, compare_cache_entry, compare_step,
+                         sub_problem)
+from sparse_long_context_head_amd.workload import WORKLOADS, f32_to_bf16_bits, generate
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _B():
+    from sparse_long_context_head_amd import binding
+    return binding
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@functools.lru_cache(maxsize=4)
+def _data(name, **kw):
+    wl = WORKLOADS[name].replace(**kw) if kw else WORKLOADS[name]
+    return wl, generate(wl)
+
+
+def data_for(name, **kw):
+    return _data(name, **kw)
+
+
+def upload(data):
+    B = _B()
+    return {k: B.bf16_tensor(v) for k, v in data.items()}
+
+
+def _oracle_for(wl, sub, override):
+    p = dict(batch=wl.batch, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+             head_dim=wl.head_dim, top_k=wl.top_k, cache_cap=wl.cache_cap, window=wl.window,
+             top_r=wl.top_r, refresh_every=wl.refresh_every, tau=wl.tau)
+    p.update(override)
+    if sub is not None:
+        p.update(batch=1, n_q_heads=p["n_q_heads"] // p["n_kv_heads"], n_kv_heads=1)
+    return O.ReTopKOracle(**p), p
+
+
+def compare_init(layer, orc, odata, prompt_len, sl, swaps):
+    gq, gs, gl, gc = [a[sl] for a in layer.read_state()]
+    oq, os_, ol, oc = orc.get_state()
+    assert np.array_equal(gc, oc), "init: entry counts differ"
+    n0 = odata["q_tail"].shape[2]
+    for b in range(orc.batch):
+        for h in range(orc.hq):
+            g = orc.kv_head(h)
+            for i in range(int(oc[b, h])):
+                p = prompt_len - n0 + i
+                where = f"init b={b} h={h} entry={i}"
+                assert np.array_equal(gq[b, h, i].view(np.uint32), oq[b, h, i].view(np.uint32)), (
+                    f"{where}: q_bar not bit-identical")
+                sel = gs[b, h, i, :gl[b, h, i]]
+                assert len(sel) and sel.max() <= p, f"{where}: support not causal"
+                check_support(sel, os_[b, h, i, :ol[b, h, i]], odata["q_tail"][b, h, i],
+                              odata["k"][b, g], where, swaps)
+
+
+def run_lockstep(name, n_steps, sub=None, override=None, check_init=True, wl_kw=None):
+    """Run n_steps decode steps; before each, the oracle adopts the GPU's cache."""
+    torch = _torch()
+    B = _B()
+    override = dict(override or {})
+    wl, data = data_for(name, **(wl_kw or {}))
+    dev = upload(data)
+    layer = B.ReTopKLayer.from_workload(wl, **override)
+    orc, p = _oracle_for(wl, sub, override)
+    G = wl.n_q_heads // wl.n_kv_heads
+    if sub is None:
+        odata, sl = data, (slice(None), slice(None))
+    else:
+        odata = sub_problem(data, sub[0], sub[1], G)
+        sl = (slice(sub[0], sub[0] + 1), slice(sub[1] * G, (sub[1] + 1) * G))
+    L0 = wl.prompt_len
+    swaps, errs = [], []
+    log(f"[lockstep] {name} sub={sub} override={override} steps={n_steps}")
+    layer.init_from_prefill(dev["q_tail"], dev["k"], L0)
+    if check_init:
+        orc.init_from_prefill(odata["q_tail"], odata["k"], L0)
+        compare_init(layer, orc, odata, L0, sl, swaps)
+    out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    paths, ms = [], []
+    heads = [(b, h) for b in range(orc.batch) for h in range(orc.hq)]
+    for t in range(1, n_steps + 1):
+        L = L0 + t
+        before = [a[sl] for a in layer.read_state()]
+        orc.set_state(*before)
+        layer.decode_step(dev["q_dec"][t - 1], dev["k"], dev["v"], L, t, out)
+        rec = orc.step(odata["q_dec"][t - 1], odata["k"], odata["v"], L, t)
+        info = {k: v[sl] for k, v in layer.step_info().items()}
+        o = out.cpu().numpy()[sl]
+        compare_step(rec, info, o, odata["q_dec"][t - 1], odata["k"], odata["v"], orc, p["tau"],
+                     heads, swaps, errs)
+        after = [a[sl] for a in layer.read_state()]
+        for b, h in heads:
+            where = f"t={t} b={b} h={h}"
+            n_prev = int(before[3][b, h])
+            n_new = int(after[3][b, h])
+            assert n_new == min(n_prev + 1, p["cache_cap"]), f"{where}: FIFO count"
+            drop = 1 if n_prev == p["cache_cap"] else 0
+            for i in range(n_new - 1):
+                assert np.array_equal(after[0][b, h, i], before[0][b, h, i + drop]), f"{where}: FIFO order"
+                assert after[2][b, h, i] == before[2][b, h, i + drop], f"{where}: FIFO order"
+            compare_cache_entry(after, O.normalize_query(odata["q_dec"][t - 1][b, h]), b, h,
+                                info["sel"][b, h, :info["sel_len"][b, h]], where)
+        paths.append(rec.path.copy())
+        ms.extend(int(m) for m, pth in zip(rec.n_cand.ravel(), rec.path.ravel()) if pth == O.REUSE)
+    paths = np.array(paths)
+    log(f"[lockstep] {name}: exact head-steps {int(paths.sum())}/{paths.size}, "
+        f"M_t mean {np.mean(ms) if ms else 0:.1f} max {max(ms) if ms else 0}, "
+        f"swaps {len(swaps)}, max out err {max(errs):.2e}")
+    layer.close()
+    return dict(paths=paths, swaps=swaps, max_err=max(errs), ms=ms)
+
+
+# ---------------------------------------------------------------------------
+# Exact Top-K attention baseline
+# ---------------------------------------------------------------------------
+
+def run_exact(name, lengths, top_k=None, sub=None, wl_kw=None, q_override=None):
+    torch = _torch()
+    B = _B()
+    wl, data = data_for(name, **(wl_kw or {}))
+    K = top_k or wl.top_k
+    layer = B.ReTopKLayer.from_workload(wl, top_k=K, window=min(wl.window, 16384 - wl.top_r * K))
+    dev = upload({"k": data["k"], "v": data["v"]})
+    G = wl.n_q_heads // wl.n_kv_heads
+    q = data["q_dec"][0] if q_override is None else q_override
+    qd = _B().bf16_tensor(q)
+    out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    sel = torch.empty((wl.batch, wl.n_q_heads, K), dtype=torch.int32, device="cuda")
+    swaps = []
+    for L in lengths:
+        log(f"[exact] {name} L={L} K={K}")
+        layer.exact_topk_attn(qd, dev["k"], dev["v"], L, out, sel)
+        o = out.cpu().numpy()
+        s = sel.cpu().numpy()
+        info = layer.step_info()
+        bs = range(wl.batch) if sub is None else [sub[0]]
+        hs = range(wl.n_q_heads) if sub is None else range(sub[1] * G, (sub[1] + 1) * G)
+        for b in bs:
+            for h in hs:
+                g = h // G
+                where = f"exact L={L} b={b} h={h}"
+                keff = min(K, L)
+                assert np.all(s[b, h, keff:] == -1), f"{where}: sel_out padding"
+                osel, _ = O.exact_topk_support(q[b, h], data["k"][b, g], L, K)
+                gs = check_support(s[b, h, :keff], osel, q[b, h], data["k"][b, g], where, swaps)
+                assert info["path"][b, h] == 1
+                check_output(o[b, h], gs, data["v"][b, g, s[b, h, :keff]], wl.head_dim, where)
+    layer.close()
+    return swaps
+
+
+def test_exact_tiny_lengths():
+    """Single head, K=64: lengths below K, at tile edges and ragged."""
+    run_exact("tiny", [1, 2, 63, 64, 65, 1023, 1024, 1025, 4096, 4160])
+
+
+def test_exact_gqa16k():
+    """28 query heads over 4 KV heads, K=512, several lengths incl. ragged tails."""
+    run_exact("gqa16k", [300, 512, 513, 5000, 16385, 16640])
+
+
+def test_exact_integer_ties():
+    """Integer-valued keys and queries make fp32 scores exact, so equal scores
+    are real ties: the lower index must win, with no near-tie allowance."""
+    torch = _torch()
+    B = _B()
+    rng = np.random.default_rng(21)
+    L, Hq, Hkv, D, K = 3000, 8, 2, 128, 100
+    k = f32_to_bf16_bits(rng.integers(-2, 3, size=(1, Hkv, L, D)).astype(np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((1, Hkv, L, D)).astype(np.float32))
+    q = f32_to_bf16_bits(rng.integers(-1, 2, size=(1, Hq, D)).astype(np.float32))
+    layer = B.ReTopKLayer(batch=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, max_len=L, top_k=K,
+                          cache_cap=4, window=4, top_r=2, refresh_every=0, tau=0.5)
+    out = torch.empty((1, Hq, D), dtype=torch.float32, device="cuda")
+    sel = torch.empty((1, Hq, K), dtype=torch.int32, device="cuda")
+    for length in (L, 1500, 99, 100, 101):
+        layer.exact_topk_attn(B.bf16_tensor(q), B.bf16_tensor(k), B.bf16_tensor(v), length, out, sel)
+        s = sel.cpu().numpy()
+        for h in range(Hq):
+            osel, _ = O.exact_topk_support(q[0, h], k[0, h // 4], length, K)
+            assert np.array_equal(s[0, h, :min(K, length)], osel), f"L={length} h={h}"
+    layer.close()
+
+
+def test_exact_degenerate_all_equal():
+    """Zero query: every score is 0, the support is the K lowest indices.
+    The boundary bin holds every key (more than the LDS capacity)."""
+    torch = _torch()
+    B = _B()
+    rng = np.random.default_rng(22)
+    L, K = 9000, 300
+    k = f32_to_bf16_bits(rng.standard_normal((1, 1, L, 128)).astype(np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((1, 1, L, 128)).astype(np.float32))
+    q = np.zeros((1, 1, 128), np.uint16)
+    layer = B.ReTopKLayer(batch=1, n_q_heads=1, n_kv_heads=1, head_dim=128, max_len=L, top_k=K,
+                          cache_cap=2, window=1, top_r=1, refresh_every=0, tau=0.5)
+    out = torch.empty((1, 1, 128), dtype=torch.float32, device="cuda")
+    sel = torch.empty((1, 1, K), dtype=torch.int32, device="cuda")
+    layer.exact_topk_attn(B.bf16_tensor(q), B.bf16_tensor(k), B.bf16_tensor(v), L, out, sel)
+    assert np.array_equal(sel.cpu().numpy()[0, 0], np.arange(K))
+    ref = O.bf16_to_f64(v[0, 0, :K]).mean(0)
+    np.testing.assert_allclose(out.cpu().numpy()[0, 0], ref, rtol=1e-4, atol=1e-5)
+    layer.close()
+
+
+# ---------------------------------------------------------------------------
+# Decode steps
+# ---------------------------------------------------------------------------
+
+def test_decode_tiny_lockstep():
+    r = run_lockstep("tiny", 64)
+    assert r["paths"].sum() >= 0
+
+
+def test_decode_tiny_refresh_every_8():
+    r = run_lockstep("tiny", 40, override=dict(refresh_every=8))
+    for t in (8, 16, 24, 32, 40):
+        assert r["paths"][t - 1].all()
+
+
+def test_decode_tiny_forced_exact():
+    r = run_lockstep("tiny", 20, override=dict(tau=2.0))
+    assert r["paths"].all()
+
+
+def test_decode_tiny_forced_reuse():
+    r = run_lockstep("tiny", 40, override=dict(tau=-2.0, refresh_every=0))
+    assert not r["paths"].any()
+
+
+def test_decode_tiny_window_covers_history():
+    """W >= L_t: the candidate set is every key, so reuse equals exact Top-K."""
+    run_lockstep("tiny", 6, override=dict(tau=-2.0, refresh_every=0, window=8192))
+
+
+def test_decode_small_cache_no_window():
+    """C = R = 1 and W = 0 (the ablation without the recent-token guard)."""
+    run_lockstep("tiny", 30, override=dict(cache_cap=1, top_r=1, window=0))
+
+
+def test_decode_gqa16k_lockstep():
+    run_lockstep("gqa16k", 24, override=dict(refresh_every=12))
+
+
+def test_decode_gqa32k_batch4_lockstep():
+    run_lockstep("gqa32k_b4", 6, wl_kw=dict(decode_steps=8), override=dict(refresh_every=3))
+
+
+def test_decode_free_running_tiny():
+    """Without re-synchronisation the GPU trajectory matches the oracle's until
+    the first near-tie swap (if any)."""
+    torch = _torch()
+    B = _B()
+    wl, data = data_for("tiny")
+    dev = upload(data)
+    layer = B.ReTopKLayer.from_workload(wl, refresh_every=16)
+    orc = O.ReTopKOracle.from_workload(wl, refresh_every=16)
+    layer.init_from_prefill(dev["q_tail"], dev["k"], wl.prompt_len)
+    orc.init_from_prefill(data["q_tail"], data["k"], wl.prompt_len)
+    out = torch.empty((1, 1, 128), dtype=torch.float32, device="cuda")
+    matched = 0
+    for t in range(1, wl.decode_steps + 1):
+        L = wl.prompt_len + t
+        layer.decode_step(dev["q_dec"][t - 1], dev["k"], dev["v"], L, t, out)
+        rec = orc.step(data["q_dec"][t - 1], data["k"], data["v"], L, t)
+        info = layer.step_info()
+        swaps, errs = [], []
+        compare_step(rec, info, out.cpu().numpy(), data["q_dec"][t - 1], data["k"], data["v"], orc,
+                     wl.tau, [(0, 0)], swaps, errs)
+        if swaps:
+            break
+        matched = t
+    log(f"[free-running] tiny: identical for {matched} of {wl.decode_steps} steps")
+    layer.close()
+
+
+def test_determinism_and_resume():
+    """Same inputs give bit-identical outputs and caches; a snapshot restored
+    into a fresh handle continues identically."""
+    torch = _torch()
+    B = _B()
+    wl, data = data_for("gqa16k")
+    dev = upload(data)
+    n1, n2 = 6, 6
+
+    def run(layer, t0, n):
+        outs = []
+        out = torch.empty((1, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
+        for t in range(t0, t0 + n):
+            layer.decode_step(dev["q_dec"][t - 1], dev["k"], dev["v"], wl.prompt_len + t, t, out)
+            outs.append(out.cpu().numpy().copy())
+        return np.stack(outs)
+
+    a = B.ReTopKLayer.from_workload(wl, refresh_every=4)
+    a.init_from_prefill(dev["q_tail"], dev["k"], wl.prompt_len)
+    oa1 = run(a, 1, n1)
+    snap = a.read_state()
+    oa2 = run(a, 1 + n1, n2)
+    sa = a.read_state()
+    b = B.ReTopKLayer.from_workload(wl, refresh_every=4)
+    b.init_from_prefill(dev["q_tail"], dev["k"], wl.prompt_len)
+    ob1 = run(b, 1, n1)
+    assert np.array_equal(oa1.view(np.uint32), ob1.view(np.uint32))
+    c = B.ReTopKLayer.from_workload(wl, refresh_every=4)
+    c.write_state(*snap)
+    assert all(np.array_equal(x, y) for x, y in zip(c.read_state(), snap))
+    oc2 = run(c, 1 + n1, n2)
+    assert np.array_equal(oa2.view(np.uint32), oc2.view(np.uint32))
+    assert all(np.array_equal(x, y) for x, y in zip(c.read_state(), sa))
+    for layer in (a, b, c):
+        layer.close()
+
+
+def test_stats_ring_matches_step_info():
+    torch = _torch()
+    B = _B()
+    wl, data = data_for("gqa16k")
+    dev = upload(data)
+    layer = B.ReTopKLayer.from_workload(wl, refresh_every=5)
+    layer.init_from_prefill(dev["q_tail"], dev["k"], wl.prompt_len)
+    out = torch.empty((1, wl.n_q_heads, 128), dtype=torch.float32, device="cuda")
+    infos = []
+    for t in range(1, 11):
+        layer.decode_step(dev["q_dec"][t - 1], dev["k"], dev["v"], wl.prompt_len + t, t, out)
+        infos.append(layer.step_info())
+    path, rho, m = layer.stats(1, 10)
+    for i, info in enumerate(infos):
+        t = i + 1
+        assert np.array_equal(path[i] & 1, info["path"])
+        assert np.all(((path[i] >> 1) & 1) == (1 if t % 5 == 0 else 0))
+        assert np.array_equal(rho[i], info["rho_max"])
+        assert np.array_equal(m[i], np.where(info["path"] == 1, 0, info["n_cand"]))
+    layer.close()
+
+
+# ---------------------------------------------------------------------------
+# Full-size configurations, sampled
+# ---------------------------------------------------------------------------
+
+@pytest.mark.slow
+def test_headline_128k_sampled():
+    """L0 = 131072, 28/4 heads, K = 512: the oracle follows KV group 1 in
+    lockstep (init included) for 6 steps with a refresh at step 3."""
+    run_lockstep("headline128k", 6, sub=(0, 1), override=dict(refresh_every=3),
+                 wl_kw=dict(decode_steps=16))
+    swaps = run_exact("headline128k", [131072 + 5], sub=(0, 3), wl_kw=dict(decode_steps=16))
+    log(f"[exact] headline group 3: swaps {len(swaps)}")
+
+
+@pytest.mark.slow
+def test_stress_128k_b8_sampled():
+    """Batch 8 at L0 = 131072 with K = 2048 and tau = 0.99 (mostly exact): one
+    sampled (batch row, KV group), 3 lockstep steps without the init check."""
+    run_lockstep("stress128k_b8", 3, sub=(5, 2), check_init=False, wl_kw=dict(decode_steps=8))
