@@ -153,6 +153,14 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   const long long cand = static_cast<long long>(p.top_r) * p.top_k + p.window;
   if (cand > kMaxCand)
     return fail(RETOPK_OUT_OF_RANGE, "retopk_create: top_r * top_k + window must be <= 16384");
+  {
+    Dims probe{};
+    probe.K = p.top_k;
+    probe.cand_cap = static_cast<int>(cand);
+    if (head_lds_bytes(probe) > static_cast<size_t>(kLdsLimit) ||
+        finish_lds_bytes(probe) > static_cast<size_t>(kLdsLimit))
+      return fail(RETOPK_OUT_OF_RANGE, "retopk_create: top_k / top_r / window need more LDS than a work group has");
+  }
   const long long bh = static_cast<long long>(p.batch) * p.n_q_heads;
   if (bh > (1 << 20)) return fail(RETOPK_OUT_OF_RANGE, "retopk_create: batch * n_q_heads too large");
 
@@ -196,7 +204,6 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   A(&b.fifo, BH * 2);
   A(&b.qbar, BH * D);
   A(&b.path, BH);
-  A(&b.gexact, static_cast<size_t>(d.B) * d.Hkv);
   A(&b.rho, BH);
   A(&b.ret, BH * d.R);
   A(&b.retslot, BH * d.R);
@@ -211,11 +218,10 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   A(&b.sel, BH * d.K);
   A(&b.selsc, BH * d.K);
   A(&b.sellen, BH);
-  A(&b.part, BH * kAttendSplit * (D + 4));
-  A(&b.done, BH);
   A(&b.st_path, BH * kStatsCap);
   A(&b.st_rho, BH * kStatsCap);
   A(&b.st_m, BH * kStatsCap);
+  if (e == hipSuccess) e = configure_kernels(d);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     h->release();
@@ -255,12 +261,13 @@ retopk_status retopk_init_from_prefill(retopk_handle* h, const uint16_t* q_tail,
   for (int i = 0; i < n0 && st == RETOPK_OK; ++i) {
     const int len = prompt_len - n0 + i + 1;  // causal: keys 0 .. p
     const uint16_t* qi = q_tail + static_cast<long>(i) * kHeadDim;
-    st = h->run(kKRecall, s, [&] { return launch_recall(d, b, qi, q_sb, q_sh, kModeExact, 0, -1, s); });
+    st = h->run(kKHead, s, [&] {
+      return launch_head(d, b, qi, q_sb, q_sh, nullptr, nullptr, nullptr, len, 0, kModeExact, -1, s);
+    });
     if (st == RETOPK_OK) st = h->run(kKExactQK, s, [&] { return launch_exact_qk(d, b, qi, q_sb, q_sh, k, len, s); });
     if (st == RETOPK_OK) st = h->run(kKCollect, s, [&] { return launch_collect(d, b, len, s); });
-    if (st == RETOPK_OK) st = h->run(kKFinish, s, [&] { return launch_finish(d, b, len, s); });
     if (st == RETOPK_OK)
-      st = h->run(kKAttend, s, [&] { return launch_attend(d, b, nullptr, nullptr, nullptr, 1, s); });
+      st = h->run(kKFinish, s, [&] { return launch_finish(d, b, nullptr, nullptr, nullptr, len, 1, s); });
   }
   return st;
 }
@@ -282,15 +289,12 @@ retopk_status retopk_decode_step(retopk_handle* h, const uint16_t* q, const uint
   auto s = static_cast<hipStream_t>(stream);
   const int slot = h->stats ? (t_dec - 1) % kStatsCap : -1;
   const long q_sb = static_cast<long>(d.Hq) * kHeadDim, q_sh = kHeadDim;
-  retopk_status st =
-      h->run(kKRecall, s, [&] { return launch_recall(d, b, q, q_sb, q_sh, kModeDecode, t_dec, slot, s); });
-  if (st == RETOPK_OK) st = h->run(kKUnion, s, [&] { return launch_union(d, b, length, slot, s); });
-  if (st == RETOPK_OK) st = h->run(kKCandQK, s, [&] { return launch_cand_qk(d, b, q, k, s); });
-  if (st == RETOPK_OK) st = h->run(kKRerank, s, [&] { return launch_rerank(d, b, s); });
+  retopk_status st = h->run(kKHead, s, [&] {
+    return launch_head(d, b, q, q_sb, q_sh, k, v, out, length, t_dec, kModeDecode, slot, s);
+  });
   if (st == RETOPK_OK) st = h->run(kKExactQK, s, [&] { return launch_exact_qk(d, b, q, q_sb, q_sh, k, length, s); });
   if (st == RETOPK_OK) st = h->run(kKCollect, s, [&] { return launch_collect(d, b, length, s); });
-  if (st == RETOPK_OK) st = h->run(kKFinish, s, [&] { return launch_finish(d, b, length, s); });
-  if (st == RETOPK_OK) st = h->run(kKAttend, s, [&] { return launch_attend(d, b, v, out, nullptr, 1, s); });
+  if (st == RETOPK_OK) st = h->run(kKFinish, s, [&] { return launch_finish(d, b, v, out, nullptr, length, 1, s); });
   return st;
 }
 
@@ -310,12 +314,12 @@ retopk_status retopk_exact_topk_attn(retopk_handle* h, const uint16_t* q, const 
   const Bufs& b = h->b;
   auto s = static_cast<hipStream_t>(stream);
   const long q_sb = static_cast<long>(d.Hq) * kHeadDim, q_sh = kHeadDim;
-  retopk_status st =
-      h->run(kKRecall, s, [&] { return launch_recall(d, b, q, q_sb, q_sh, kModeExact, 0, -1, s); });
+  retopk_status st = h->run(kKHead, s, [&] {
+    return launch_head(d, b, q, q_sb, q_sh, nullptr, nullptr, nullptr, length, 0, kModeExact, -1, s);
+  });
   if (st == RETOPK_OK) st = h->run(kKExactQK, s, [&] { return launch_exact_qk(d, b, q, q_sb, q_sh, k, length, s); });
   if (st == RETOPK_OK) st = h->run(kKCollect, s, [&] { return launch_collect(d, b, length, s); });
-  if (st == RETOPK_OK) st = h->run(kKFinish, s, [&] { return launch_finish(d, b, length, s); });
-  if (st == RETOPK_OK) st = h->run(kKAttend, s, [&] { return launch_attend(d, b, v, out, sel_out, 0, s); });
+  if (st == RETOPK_OK) st = h->run(kKFinish, s, [&] { return launch_finish(d, b, v, out, sel_out, length, 0, s); });
   return st;
 }
 

@@ -16,12 +16,13 @@ constexpr int kHistBits = 10;        // first-level histogram: top 10 bits of th
 constexpr int kNumBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
 constexpr int kStatsCap = 4096;      // decode steps kept in the statistics ring
-constexpr int kExactChunk = 1024;    // key rows per work item of the full-history QK kernel
-constexpr int kCollectChunk = 4096;  // scores per work item of the threshold/collect kernel
-constexpr int kAttendSplit = 8;      // work groups per head in the softmax-V kernel
-constexpr int kCandRowsPerBlock = 128;
+constexpr int kExactWGTarget = 1024; // work groups of the full-history QK kernel (about 4 per CU)
+constexpr int kExactMinRows = 512;   // ... each with at least this many key rows
+constexpr int kCollectChunk = 4096;  // scores per work group of the threshold/collect kernel
+constexpr int kHeadThreads = 512;    // threads of the per-head kernels
 constexpr int kBitmapWords = 8192;   // LDS bitmap window: 262144 token positions (32 KiB)
 constexpr int kBoundaryLds = 4096;   // boundary entries resolved in LDS (32 KiB of 64-bit keys)
+constexpr int kLdsLimit = 160 * 1024 - 12 * 1024;  // dynamic LDS a per-head kernel may use
 constexpr int kMaxCand = 16384;      // R*K + W limit (candidate keys kept in LDS for reranking)
 
 // Problem dimensions, passed by value to every kernel.
@@ -44,7 +45,6 @@ struct Bufs {
   // per-step workspaces
   float* qbar;             // [BH, D]   normalised current query
   int32_t* path;           // [BH]      1 exact, 0 reuse
-  int32_t* gexact;         // [B*Hkv]   exact heads in the KV group
   double* rho;             // [BH]      rho_max
   int32_t* ret;            // [BH, R]   retrieved FIFO positions, -1 pad
   int32_t* retslot;        // [BH, R]   their ring slots
@@ -59,44 +59,37 @@ struct Bufs {
   int32_t* sel;            // [BH, K]   S_hat_t ascending
   float* selsc;            // [BH, K]   q.k of S_hat_t
   int32_t* sellen;         // [BH]
-  float* part;             // [BH, kAttendSplit, D + 4] partial softmax-V sums
-  int32_t* done;           // [BH]      arrival counter of the softmax-V work groups
   // statistics ring
   uint8_t* st_path;        // [kStatsCap, BH]
   double* st_rho;          // [kStatsCap, BH]
   int32_t* st_m;           // [kStatsCap, BH]
 };
 
-enum KernelId : int {
-  kKRecall = 0,
-  kKUnion,
-  kKCandQK,
-  kKRerank,
-  kKExactQK,
-  kKCollect,
-  kKFinish,
-  kKAttend,
-  kKReset,
-  kNumKernels
-};
+enum KernelId : int { kKHead = 0, kKExactQK, kKCollect, kKFinish, kKReset, kNumKernels };
 
 const char* kernel_name(int id);
 
-// Launch helpers (retopk_kernels.hip). Each returns the hipError_t of the launch.
-enum RecallMode : int { kModeDecode = 0, kModeExact = 1 };
+// Dynamic LDS of the per-head kernels for the given dimensions.
+size_t head_lds_bytes(const Dims& d);
+size_t finish_lds_bytes(const Dims& d);
 
+// Launch helpers (retopk_kernels.hip). Each returns the hipError_t of the launch.
+enum HeadMode : int { kModeDecode = 0, kModeExact = 1 };
+
+// Raise the dynamic-LDS limit of the per-head kernels to what `d` needs.
+hipError_t configure_kernels(const Dims& d);
 hipError_t launch_reset(const Dims& d, const Bufs& b, hipStream_t s);
-hipError_t launch_recall(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
-                         int mode, int t_dec, int stats_slot, hipStream_t s);
-hipError_t launch_union(const Dims& d, const Bufs& b, int length, int stats_slot, hipStream_t s);
-hipError_t launch_cand_qk(const Dims& d, const Bufs& b, const uint16_t* q, const uint16_t* k,
-                          hipStream_t s);
-hipError_t launch_rerank(const Dims& d, const Bufs& b, hipStream_t s);
+// Recall, path decision and (for reuse heads) the whole reuse path with the
+// cache update. In kModeExact every head is marked exact (no recall).
+hipError_t launch_head(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
+                       const uint16_t* k, const uint16_t* v, float* out, int length, int t_dec,
+                       int mode, int stats_slot, hipStream_t s);
 hipError_t launch_exact_qk(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
                            const uint16_t* k, int length, hipStream_t s);
 hipError_t launch_collect(const Dims& d, const Bufs& b, int length, hipStream_t s);
-hipError_t launch_finish(const Dims& d, const Bufs& b, int length, hipStream_t s);
-hipError_t launch_attend(const Dims& d, const Bufs& b, const uint16_t* v, float* out,
-                         int32_t* sel_out, int push, hipStream_t s);
+// Global Top-K resolution, softmax-V (skipped when v or out is NULL) and the
+// cache update (when push) for exact heads.
+hipError_t launch_finish(const Dims& d, const Bufs& b, const uint16_t* v, float* out, int32_t* sel_out,
+                         int length, int push, hipStream_t s);
 
 }  // namespace retopk

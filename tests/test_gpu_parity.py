@@ -88,6 +88,9 @@ def run_lockstep(name, n_steps, sub=None, override=None, check_init=True, wl_kw=
     B = _B()
     override = dict(override or {})
     wl, data = data_for(name, **(wl_kw or {}))
+    n0 = min(override.get("cache_cap", wl.cache_cap), wl.prompt_len)
+    if n0 != data["q_tail"].shape[2]:
+        data = {**data, "q_tail": np.ascontiguousarray(data["q_tail"][:, :, -n0:])}
     dev = upload(data)
     layer = B.ReTopKLayer.from_workload(wl, **override)
     orc, p = _oracle_for(wl, sub, override)
