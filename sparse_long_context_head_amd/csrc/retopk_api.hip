@@ -157,6 +157,7 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
     Dims probe{};
     probe.K = p.top_k;
     probe.cand_cap = static_cast<int>(cand);
+    probe.n_chunks = (p.max_len + kCollectChunk - 1) / kCollectChunk;
     if (head_lds_bytes(probe) > static_cast<size_t>(kLdsLimit) ||
         finish_lds_bytes(probe) > static_cast<size_t>(kLdsLimit))
       return fail(RETOPK_OUT_OF_RANGE, "retopk_create: top_k / top_r / window need more LDS than a work group has");
@@ -189,6 +190,7 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   d.R = p.top_r;
   d.Tr = p.refresh_every;
   d.cand_cap = static_cast<int>(cand);
+  d.n_chunks = (p.max_len + kCollectChunk - 1) / kCollectChunk;
   d.tau = p.tau;
 
   Bufs& b = h->b;
@@ -211,10 +213,9 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   A(&b.cand, BH * d.cand_cap);
   A(&b.cscore, BH * d.cand_cap);
   A(&b.score, BH * d.score_stride);
-  A(&b.hist, BH * kNumBins);
-  A(&b.cnt, BH * 4);
-  A(&b.above, BH * d.K);
-  A(&b.bnd, BH * d.max_len);
+  A(&b.hist, BH * kHistSeg * kNumBins);
+  A(&b.hits, BH * d.max_len);
+  A(&b.ccnt, BH * d.n_chunks);
   A(&b.sel, BH * d.K);
   A(&b.selsc, BH * d.K);
   A(&b.sellen, BH);

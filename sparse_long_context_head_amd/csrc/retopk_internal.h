@@ -16,13 +16,14 @@ constexpr int kHistBits = 10;        // first-level histogram: top 10 bits of th
 constexpr int kNumBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
 constexpr int kStatsCap = 4096;      // decode steps kept in the statistics ring
-constexpr int kExactWGTarget = 1024; // work groups of the full-history QK kernel (about 4 per CU)
-constexpr int kExactMinRows = 512;   // ... each with at least this many key rows
+constexpr int kExactWGTarget = 512;  // work groups of the full-history QK kernel (about 2 per CU)
+constexpr int kExactMinRows = 1024;  // ... each with at least this many key rows
+constexpr int kHistSeg = 8;          // copies of each head's histogram (spreads the atomics)
 constexpr int kCollectChunk = 4096;  // scores per work group of the threshold/collect kernel
 constexpr int kHeadThreads = 512;    // threads of the per-head kernels
 constexpr int kBitmapWords = 8192;   // LDS bitmap window: 262144 token positions (32 KiB)
 constexpr int kBoundaryLds = 4096;   // boundary entries resolved in LDS (32 KiB of 64-bit keys)
-constexpr int kLdsLimit = 160 * 1024 - 12 * 1024;  // dynamic LDS a per-head kernel may use
+constexpr int kLdsLimit = 160 * 1024 - 20 * 1024;  // dynamic LDS a per-head kernel may use
 constexpr int kMaxCand = 16384;      // R*K + W limit (candidate keys kept in LDS for reranking)
 
 // Problem dimensions, passed by value to every kernel.
@@ -32,6 +33,7 @@ struct Dims {
   int score_stride;        // row stride of the full-history score workspace (max_len rounded to 16)
   int K, C, W, R, Tr;
   int cand_cap;            // R*K + W
+  int n_chunks;            // ceil(max_len / kCollectChunk)
   double tau;
 };
 
@@ -52,10 +54,11 @@ struct Bufs {
   int32_t* cand;           // [BH, cand_cap]  A_t ascending
   float* cscore;           // [BH, cand_cap]  q.k of A_t
   float* score;            // [BH, score_stride]  full-history q.k
-  uint32_t* hist;          // [BH, kNumBins]  histogram of ordered score keys
-  int32_t* cnt;            // [BH, 4]   above-count, boundary-count
-  int32_t* above;          // [BH, K]   indices above the boundary bin, then resolved boundary
-  int32_t* bnd;            // [BH, max_len] indices in the boundary bin
+  uint32_t* hist;          // [BH, kHistSeg, kNumBins]  histogram of ordered score keys
+  uint2* hits;             // [BH, max_len] per score chunk of kCollectChunk positions: the
+                           //   boundary-bin entries from the front, the entries above it from
+                           //   the back; each entry is (index, score bits)
+  int2* ccnt;              // [BH, n_chunks] (above count, boundary count) of each chunk
   int32_t* sel;            // [BH, K]   S_hat_t ascending
   float* selsc;            // [BH, K]   q.k of S_hat_t
   int32_t* sellen;         // [BH]

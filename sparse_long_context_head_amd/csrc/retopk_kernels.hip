@@ -43,28 +43,108 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ double wave_sum_f64(double x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+// ---- cross-lane primitives on DPP row operations (no LDS traffic) ----
+// A DPP "row" is 16 consecutive lanes. Lanes whose source is out of range
+// read 0.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within each row
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+
+template <int Ctrl>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, Ctrl, 0xF, 0xF, false);
+}
+template <int Ctrl>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(dpp_i<Ctrl>(__float_as_int(x)));
+}
+template <int Ctrl>
+__device__ __forceinline__ double dpp_d(double x) {
+  const unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(x));
+  const int lo = dpp_i<Ctrl>(static_cast<int>(u & 0xffffffffull));
+  const int hi = dpp_i<Ctrl>(static_cast<int>(u >> 32));
+  return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) |
+                                                     static_cast<unsigned>(lo)));
+}
+
+// Sum / maximum over each 16-lane row; every lane of the row gets the result.
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  x += dpp_f<kDppMirror>(x);
+  return x;
+}
+__device__ __forceinline__ double row_sum(double x) {
+  x += dpp_d<kDppXor1>(x);
+  x += dpp_d<kDppXor2>(x);
+  x += dpp_d<kDppHalfMirror>(x);
+  x += dpp_d<kDppMirror>(x);
+  return x;
+}
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, dpp_f<kDppXor1>(x));
+  x = fmaxf(x, dpp_f<kDppXor2>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp_f<kDppMirror>(x));
   return x;
 }
 
-__device__ __forceinline__ float wave_max_f32(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+__device__ __forceinline__ double row_max(double x) {
+  x = fmax(x, dpp_d<kDppXor1>(x));
+  x = fmax(x, dpp_d<kDppXor2>(x));
+  x = fmax(x, dpp_d<kDppHalfMirror>(x));
+  x = fmax(x, dpp_d<kDppMirror>(x));
   return x;
+}
+
+__device__ __forceinline__ double readlane_d(double x, int lane) {
+  const unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(x));
+  const unsigned lo = __builtin_amdgcn_readlane(static_cast<int>(u & 0xffffffffull), lane);
+  const unsigned hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), lane);
+  return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+
+// Wave-wide sum (fixed order: rows 0+1, 2+3, then both), in every lane.
+__device__ __forceinline__ double wave_sum_f64(double x) {
+  x = row_sum(x);
+  return (readlane_d(x, 0) + readlane_d(x, 16)) + (readlane_d(x, 32) + readlane_d(x, 48));
+}
+
+__device__ __forceinline__ double wave_max_f64(double x) {
+  x = row_max(x);
+  return fmax(fmax(readlane_d(x, 0), readlane_d(x, 16)), fmax(readlane_d(x, 32), readlane_d(x, 48)));
+}
+
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = row_max(x);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_i<kDppShr1>(x);
+  x += dpp_i<kDppShr2>(x);
+  x += dpp_i<kDppShr4>(x);
+  x += dpp_i<kDppShr8>(x);
+  const int t0 = __builtin_amdgcn_readlane(x, 15);
+  const int t1 = __builtin_amdgcn_readlane(x, 31);
+  const int t2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row > 0 ? t0 : 0) + (row > 1 ? t1 : 0) + (row > 2 ? t2 : 0);
 }
 
 // Block-wide exclusive prefix sum of one int per thread. `tmp` holds at
 // least blockDim.x / 64 ints. Every thread of the block must call it.
-__device__ int block_exclusive_scan(int v, int* total, int* tmp) {
+__device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
+  const int incl = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = incl;
   __syncthreads();
   int before = 0, tot = 0;
@@ -78,7 +158,7 @@ __device__ int block_exclusive_scan(int v, int* total, int* tmp) {
   return before + incl - v;
 }
 
-__device__ float block_max_f32(float v, float* tmp) {
+__device__ __forceinline__ float block_max_f32(float v, float* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   v = wave_max_f32(v);
   if (lane == 0) tmp[wave] = v;
@@ -89,22 +169,44 @@ __device__ float block_max_f32(float v, float* tmp) {
   return m;
 }
 
+// LDS bitmap windows of kBitmapWords words. Each thread owns a slice of 16
+// consecutive words; word w is stored at w + w/16 so that the 64 lanes of a
+// wave reading "their" i-th word hit distinct banks.
+constexpr int kSliceWords = kBitmapWords / kHeadThreads;
+static_assert(kSliceWords == 16, "bitmap slice layout");
+constexpr int kBitmapLdsWords = kBitmapWords + kBitmapWords / kSliceWords;
+
+__device__ __forceinline__ int bm_at(int w) { return w + (w >> 4); }
+
+__device__ __forceinline__ void bitmap_clear(uint32_t* bm) {
+  uint32_t* p = bm + threadIdx.x * (kSliceWords + 1);
+#pragma unroll
+  for (int i = 0; i <= kSliceWords; ++i) p[i] = 0u;
+}
+
+__device__ __forceinline__ void bitmap_set(uint32_t* bm, int x) { atomicOr(&bm[bm_at(x >> 5)], 1u << (x & 31)); }
+
 // Emit, in ascending order, the positions base + bit of every set bit of an
-// LDS bitmap of `nwords` words to out[0 ..). Returns the number emitted (the
-// same value in every thread). Every thread of the block must call it.
-__device__ int bitmap_emit(const uint32_t* bm, int nwords, int base, int32_t* out, int* tmp) {
-  const int per = (nwords + blockDim.x - 1) / blockDim.x;
-  const int w0 = threadIdx.x * per;
-  const int w1 = min(w0 + per, nwords);
+// LDS bitmap window of `nwords` words to out[0 ..). Returns the number emitted
+// (the same value in every thread). Every thread of the block must call it.
+__device__ __forceinline__ int bitmap_emit(const uint32_t* bm, int nwords, int base, int32_t* out, int* tmp) {
+  uint32_t w[kSliceWords];
+  const uint32_t* p = bm + threadIdx.x * (kSliceWords + 1);
+  const int w0 = threadIdx.x * kSliceWords;
   int cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += __popc(bm[w]);
+#pragma unroll
+  for (int i = 0; i < kSliceWords; ++i) {
+    w[i] = (w0 + i < nwords) ? p[i] : 0u;
+    cnt += __popc(w[i]);
+  }
   int total;
   int off = block_exclusive_scan(cnt, &total, tmp);
-  for (int w = w0; w < w1; ++w) {
-    uint32_t bits = bm[w];
+#pragma unroll
+  for (int i = 0; i < kSliceWords; ++i) {
+    uint32_t bits = w[i];
     while (bits) {
       const int b = __ffs(bits) - 1;
-      out[off++] = base + w * 32 + b;
+      out[off++] = base + (w0 + i) * 32 + b;
       bits &= bits - 1;
     }
   }
@@ -113,72 +215,135 @@ __device__ int bitmap_emit(const uint32_t* bm, int nwords, int base, int32_t* ou
 
 // Shared scratch of the per-head kernels (static LDS).
 struct HeadShared {
-  float q[kHeadDim];           // raw query as float
-  float qbar[kHeadDim];        // normalised query
-  double rho[64];
-  int slot[64], len[64];       // retrieved ring slots and their support sizes
-  int hist[256];
+  float q[kHeadDim];                   // raw query as float
+  float qbar[kHeadDim];                // normalised query
+  double rho[64];                      // rho of each ring slot
+  int len[64];                         // support size of each ring slot
+  int rslot[64];                       // ring slots of the retrieved entries, best first
+  __align__(16) int whist[kHeadThreads / 64][256];   // one radix histogram per wave
   int tmp[16];
   float red[kHeadThreads / 64][kHeadDim + 4];
   int i0, i1, i2, i3;
   double d0;
 };
 
-// K-th largest of n scores (LDS) under (score desc, position asc): radix
-// select over the order-preserving keys, 8 bits per pass. Returns the key T of
-// the K-th largest; *need receives how many entries equal to T are taken (the
-// lowest positions first). Every thread of the block must call it.
-__device__ uint32_t radix_kth(const float* sc, int n, int k, HeadShared& sh, int* need) {
-  uint32_t prefix = 0u, mask = 0u;
-  int rem = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0;
+// Wave 0 turns the per-wave histograms into the digit holding the rem-th
+// largest key (digits scanned from 255 down): sh.i0 = digit, sh.i1 = rank
+// within it, sh.i2 = its count. Called by every thread; only wave 0 works.
+__device__ __forceinline__ void pick_digit(HeadShared& sh, int rem) {
+  const int lane = threadIdx.x & 63;
+  if ((threadIdx.x >> 6) != 0) return;
+  // lane owns digits 255-4*lane .. 252-4*lane, read as one 128-bit word per wave histogram
+  int4 acc = make_int4(0, 0, 0, 0);
+#pragma unroll
+  for (int w = 0; w < kHeadThreads / 64; ++w) {
+    const int4 h = *reinterpret_cast<const int4*>(&sh.whist[w][252 - 4 * lane]);
+    acc.x += h.x;
+    acc.y += h.y;
+    acc.z += h.z;
+    acc.w += h.w;
+  }
+  const int c[4] = {acc.w, acc.z, acc.y, acc.x};  // digits 255-4l, 254-4l, 253-4l, 252-4l
+  const int s4 = c[0] + c[1] + c[2] + c[3];
+  int run = wave_incl_scan(s4) - s4;
+  if (run < rem && run + s4 >= rem) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (run + c[j] >= rem) {
+        sh.i0 = 255 - 4 * lane - j;
+        sh.i1 = rem - run;
+        sh.i2 = c[j];
+        break;
+      }
+      run += c[j];
+    }
+  }
+}
+
+__device__ __forceinline__ void clear_whist(HeadShared& sh) {
+  int4* w = reinterpret_cast<int4*>(&sh.whist[0][0]);
+  for (int i = threadIdx.x; i < (kHeadThreads / 64) * 64; i += blockDim.x) w[i] = make_int4(0, 0, 0, 0);
+}
+
+// Radix select of the k largest of n scores (LDS) under (score desc,
+// position asc) on the order-preserving keys: a first pass over the top 11
+// bits (2048 bins), then 8-, 8- and 5-bit passes over the remaining bits,
+// stopping as soon as every remaining candidate is needed. On return the
+// kept entries are those with (key & *mask) > T, plus the first *need (by
+// position) with (key & *mask) == T. Every thread of the block must call it.
+__device__ __forceinline__ uint32_t radix_kth(const float* sc, int n, int k, HeadShared& sh, uint32_t* mask_out,
+                                              int* need) {
+  const int wave = threadIdx.x >> 6;
+  int* bins = &sh.whist[0][0];  // 2048 bins for the first pass
+  reinterpret_cast<int4*>(bins)[threadIdx.x] = make_int4(0, 0, 0, 0);
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&bins[order_key(sc[i]) >> 21], 1);
+  __syncthreads();
+  {
+    const int4 h = reinterpret_cast<const int4*>(bins)[511 - threadIdx.x];  // bins 2047-4t .. 2044-4t
+    const int c[4] = {h.w, h.z, h.y, h.x};
+    const int s4 = c[0] + c[1] + c[2] + c[3];
+    int tot;
+    int run = block_exclusive_scan(s4, &tot, sh.tmp);
+    if (run < k && run + s4 >= k) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (run + c[j] >= k) {
+          sh.i0 = 2047 - 4 * static_cast<int>(threadIdx.x) - j;
+          sh.i1 = k - run;
+          sh.i2 = c[j];
+          break;
+        }
+        run += c[j];
+      }
+    }
+    __syncthreads();
+  }
+  uint32_t prefix = static_cast<uint32_t>(sh.i0) << 21, mask = 0x7FFu << 21;
+  int rem = sh.i1, ncand = sh.i2;
+  const int shifts[3] = {13, 5, 0};
+  for (int p = 0; p < 3 && ncand > rem; ++p) {
+    const int shift = shifts[p];
+    const uint32_t dmask = shift == 0 ? 31u : 255u;
+    clear_whist(sh);
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
       const uint32_t u = order_key(sc[i]);
-      if ((u & mask) == prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1);
+      if ((u & mask) == prefix) atomicAdd(&sh.whist[wave][(u >> shift) & dmask], 1);
     }
     __syncthreads();
-    const int digit = 255 - static_cast<int>(threadIdx.x & 255);
-    const int c = threadIdx.x < 256 ? sh.hist[digit] : 0;
-    int tot;
-    const int above = block_exclusive_scan(c, &tot, sh.tmp);
-    if (threadIdx.x < 256 && above < rem && above + c >= rem) {
-      sh.i0 = digit;
-      sh.i1 = rem - above;
-    }
+    pick_digit(sh, rem);
     __syncthreads();
     prefix |= static_cast<uint32_t>(sh.i0) << shift;
-    mask |= 255u << shift;
+    mask |= dmask << shift;
     rem = sh.i1;
-    __syncthreads();
+    ncand = sh.i2;
   }
+  *mask_out = mask;
   *need = rem;
   return prefix;
 }
 
-// Keep, in position order, the entries with key > T and the first `need`
-// entries with key == T; write their positions' values idx[i] / sc[i] to
-// out_idx / out_sc. Returns the number kept. Every thread must call it.
-__device__ int select_in_order(const int32_t* idx, const float* sc, int n, uint32_t T, int need,
-                               int32_t* out_idx, float* out_sc, HeadShared& sh) {
+// Keep, in position order, the entries with (key & mask) > T and the first
+// `need` entries with (key & mask) == T; write idx[i] / sc[i] of the kept
+// positions to out_idx / out_sc. Returns the number kept. Every thread must
+// call it.
+__device__ __forceinline__ int select_in_order(const int32_t* idx, const float* sc, int n, uint32_t T, uint32_t mask,
+                                               int need, int32_t* out_idx, float* out_sc, HeadShared& sh) {
   const int per = (n + blockDim.x - 1) / blockDim.x;
   const int i0 = threadIdx.x * per, i1 = min(i0 + per, n);
-  int eq = 0;
-  for (int i = i0; i < i1; ++i) eq += (order_key(sc[i]) == T);
-  int tot;
-  const int eq_before = block_exclusive_scan(eq, &tot, sh.tmp);
-  int nsel = 0, e = eq_before;
+  int gt = 0, eq = 0;
   for (int i = i0; i < i1; ++i) {
-    const uint32_t u = order_key(sc[i]);
-    nsel += (u > T) || (u == T && e < need);
-    e += (u == T);
+    const uint32_t u = order_key(sc[i]) & mask;
+    gt += u > T;
+    eq += u == T;
   }
-  int kept;
-  int o = block_exclusive_scan(nsel, &kept, sh.tmp);
-  e = eq_before;
+  int tot;
+  const int pre = block_exclusive_scan((eq << 16) | gt, &tot, sh.tmp);  // n < 2^15
+  int e = pre >> 16;
+  int o = (pre & 0xffff) + min(e, need);
   for (int i = i0; i < i1; ++i) {
-    const uint32_t u = order_key(sc[i]);
+    const uint32_t u = order_key(sc[i]) & mask;
     if ((u > T) || (u == T && e < need)) {
       out_idx[o] = idx[i];
       out_sc[o] = sc[i];
@@ -187,18 +352,18 @@ __device__ int select_in_order(const int32_t* idx, const float* sc, int n, uint3
     e += (u == T);
   }
   __syncthreads();
-  return kept;
+  return (tot & 0xffff) + min(tot >> 16, need);
 }
 
 // Sparse softmax-V (Eq. 12) over n selected rows (indices and unscaled
 // scores in LDS; mx = their maximum): 16 lanes per value row (16 bytes
-// each), 8 row loads in flight per thread. Writes out[0 .. 127] when out is
+// each), 16 row loads in flight per thread. Writes out[0 .. 127] when out is
 // not NULL. Every thread of the block must call it.
-__device__ void attend(const int32_t* sel, const float* sc, int n, float mx, const uint16_t* vb, float* out,
+__device__ __forceinline__ void attend(const int32_t* sel, const float* sc, int n, float mx, const uint16_t* vb, float* out,
                        HeadShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int sub = threadIdx.x & 15, rg = threadIdx.x >> 4, rpr = blockDim.x >> 4;
-  constexpr int U = 8;
+  constexpr int U = 16;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float z = 0.f;
   for (int r0 = 0; r0 < n; r0 += rpr * U) {
@@ -206,14 +371,14 @@ __device__ void attend(const int32_t* sel, const float* sc, int n, float mx, con
     float p[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      // clamped row: always a valid address, weight 0 past the end
+      const int i = min(r0 + u * rpr + rg, n - 1);
+      w[u] = *reinterpret_cast<const uint4*>(vb + static_cast<long>(sel[i]) * kHeadDim + 8 * sub);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       const int i = r0 + u * rpr + rg;
-      if (i < n) {
-        w[u] = *reinterpret_cast<const uint4*>(vb + static_cast<long>(sel[i]) * kHeadDim + 8 * sub);
-        p[u] = expf((sc[i] - mx) * kInvSqrtD);
-      } else {
-        w[u] = make_uint4(0u, 0u, 0u, 0u);
-        p[u] = 0.f;
-      }
+      p[u] = (i < n) ? expf((sc[min(i, n - 1)] - mx) * kInvSqrtD) : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -254,7 +419,7 @@ __device__ void attend(const int32_t* sel, const float* sc, int n, float mx, con
 
 // Push (q_bar_t, S_hat_t) into the head's FIFO (Query-support cache
 // paragraph: after either path; the oldest entry is overwritten when full).
-__device__ void cache_push(const Dims& d, const Bufs& b, int bh, const float* qbar, const int32_t* sel, int n) {
+__device__ __forceinline__ void cache_push(const Dims& d, const Bufs& b, int bh, const float* qbar, const int32_t* sel, int n) {
   const int slot = b.fifo[2 * bh];
   const int count = b.fifo[2 * bh + 1];
   const long e = static_cast<long>(bh) * d.C + slot;
@@ -275,12 +440,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 }  // namespace
 
 size_t head_lds_bytes(const Dims& d) {
-  const size_t region0 = std::max<size_t>(kBitmapWords * 4, 8 * static_cast<size_t>(d.K));
+  const size_t region0 = std::max<size_t>(kBitmapLdsWords * 4, 8 * static_cast<size_t>(d.K));
   return region0 + 8 * static_cast<size_t>(d.cand_cap);
 }
 
 size_t finish_lds_bytes(const Dims& d) {
-  return std::max<size_t>(kBoundaryLds * 8, kBitmapWords * 4) + 8 * static_cast<size_t>(d.K);
+  return static_cast<size_t>(kBitmapLdsWords) * 4 * 2 + 16 * static_cast<size_t>(d.K) +
+         8 * (static_cast<size_t>(d.n_chunks) + 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -297,18 +463,18 @@ __global__ void k_reset(Dims d, Bufs b) {
 // Per-head kernel: recall, path decision, and the reuse path.
 //
 // Recall (Eqs. 5-7): q_bar = fp32(x / ||x||) with fp64 sum of squares, sqrt
-// and divide; rho_c = fp64 dot of the fp32 q_bar values for each held entry
-// (16 threads per entry); R_t = the R largest rho (ties: older entry);
-// rho_max. Path (Eq. 13): exact if refresh, empty cache or rho_max < tau.
-// Exact heads clear the counters and histogram of the exact-path kernels and
-// stop here.
+// and divide; rho = fp64 dot of the fp32 q_bar values for every ring slot
+// (16 threads per slot, all slots loaded at once); R_t = the R largest rho
+// over the held entries (ties: older entry); rho_max. Path (Eq. 13): exact if
+// refresh, empty cache or rho_max < tau. Exact heads clear the histogram of
+// the exact-path kernels and stop here.
 //
 // Reuse path, same work group:
 //   union (Eqs. 8-9): retrieved supports and the window [max(0, L-W), L) set
 //     bits of an LDS bitmap over token positions (windows of 262144), read
 //     back in ascending order -> A_t in LDS, M_t;
 //   scores (Eq. 10): q . k_i for i in A_t straight from the KV cache, 16 lanes
-//     per key row, 8 rows in flight per thread, fp32 accumulation of exact
+//     per key row, 16 rows in flight per thread, fp32 accumulation of exact
 //     bf16 products;
 //   rerank (Eq. 11): radix select of the K-th largest, kept in candidate
 //     (= ascending index) order, ties to the lower index;
@@ -326,14 +492,29 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ HeadShared sh;
   extern __shared__ __align__(16) unsigned char dyn[];
-  const size_t region0 = (kBitmapWords * 4 > 8 * d.K) ? kBitmapWords * 4 : 8 * d.K;
+  const size_t region0 = (kBitmapLdsWords * 4 > 8 * d.K) ? kBitmapLdsWords * 4 : 8 * d.K;
   uint32_t* bm = reinterpret_cast<uint32_t*>(dyn);
   int32_t* s_sel = reinterpret_cast<int32_t*>(dyn);
   float* s_selsc = reinterpret_cast<float*>(dyn + 4 * static_cast<size_t>(d.K));
   int32_t* s_cand = reinterpret_cast<int32_t*>(dyn + region0);
   float* s_sc = reinterpret_cast<float*>(dyn + region0 + 4 * static_cast<size_t>(d.cand_cap));
 
-  // ---- normalised query (wave 0) ----
+  // ---- one round of loads: query, FIFO state, every ring slot's q_bar and support size ----
+  const int fifo_head = b.fifo[2 * bh];
+  const int count = b.fifo[2 * bh + 1];
+  const int part = tid & 15;
+  float4 ent[2][2];
+  if (mode == kModeDecode) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = min(i * (kHeadThreads / 16) + (tid >> 4), d.C - 1);
+      const float* e = b.cache_qbar + (static_cast<long>(bh) * d.C + c) * kHeadDim + 8 * part;
+      ent[i][0] = *reinterpret_cast<const float4*>(e);
+      ent[i][1] = *reinterpret_cast<const float4*>(e + 4);
+    }
+    const int len_c = b.cache_len[static_cast<long>(bh) * d.C + min(tid, d.C - 1)];
+    if (tid < d.C) sh.len[tid] = len_c;
+  }
   if (wave == 0) {
     const uint32_t w2 = *reinterpret_cast<const uint32_t*>(q + bb * q_sb + h * q_sh + 2 * lane);
     const double x0 = bf16_lo(w2), x1 = bf16_hi(w2);
@@ -349,8 +530,6 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
     sh.qbar[2 * lane + 1] = qb1;
     *reinterpret_cast<float2*>(b.qbar + static_cast<long>(bh) * kHeadDim + 2 * lane) = make_float2(qb0, qb1);
   }
-  const int count = b.fifo[2 * bh + 1];
-  const int oldest = (b.fifo[2 * bh] - count + d.C) % d.C;
   __syncthreads();
 
   bool exact = true, refresh = false;
@@ -358,43 +537,44 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
   int n_ret = 0;
   if (mode == kModeDecode) {
     refresh = d.Tr > 0 && (t_dec % d.Tr) == 0;
-    // rho for entry c by 16 threads, 8 dimensions each
-    for (int c0 = 0; c0 < count; c0 += kHeadThreads / 16) {
-      const int c = c0 + (tid >> 4), part = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * (kHeadThreads / 16) + (tid >> 4);
+      const float* t = sh.qbar + 8 * part;
       double s = 0.0;
-      if (c < count) {
-        const float* e = b.cache_qbar + (static_cast<long>(bh) * d.C + (oldest + c) % d.C) * kHeadDim + 8 * part;
-        const float4 e0 = *reinterpret_cast<const float4*>(e);
-        const float4 e1 = *reinterpret_cast<const float4*>(e + 4);
-        const float* t = sh.qbar + 8 * part;
-        s = fma(static_cast<double>(t[0]), static_cast<double>(e0.x), s);
-        s = fma(static_cast<double>(t[1]), static_cast<double>(e0.y), s);
-        s = fma(static_cast<double>(t[2]), static_cast<double>(e0.z), s);
-        s = fma(static_cast<double>(t[3]), static_cast<double>(e0.w), s);
-        s = fma(static_cast<double>(t[4]), static_cast<double>(e1.x), s);
-        s = fma(static_cast<double>(t[5]), static_cast<double>(e1.y), s);
-        s = fma(static_cast<double>(t[6]), static_cast<double>(e1.z), s);
-        s = fma(static_cast<double>(t[7]), static_cast<double>(e1.w), s);
-      }
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      s += __shfl_xor(s, 8);
-      if (part == 0 && c < count) sh.rho[c] = s;
+      s = fma(static_cast<double>(t[0]), static_cast<double>(ent[i][0].x), s);
+      s = fma(static_cast<double>(t[1]), static_cast<double>(ent[i][0].y), s);
+      s = fma(static_cast<double>(t[2]), static_cast<double>(ent[i][0].z), s);
+      s = fma(static_cast<double>(t[3]), static_cast<double>(ent[i][0].w), s);
+      s = fma(static_cast<double>(t[4]), static_cast<double>(ent[i][1].x), s);
+      s = fma(static_cast<double>(t[5]), static_cast<double>(ent[i][1].y), s);
+      s = fma(static_cast<double>(t[6]), static_cast<double>(ent[i][1].z), s);
+      s = fma(static_cast<double>(t[7]), static_cast<double>(ent[i][1].w), s);
+      s = row_sum(s);
+      if (part == 0 && c < d.C) sh.rho[c] = s;
     }
     __syncthreads();
-    if (tid < count) {
-      const double mine = sh.rho[tid];
-      int rank = 0;
-      for (int j = 0; j < count; ++j) {
-        const double o = sh.rho[j];
-        rank += (o > mine) || (o == mine && j < tid);
+    // FIFO position p (0 = oldest) lives in ring slot (oldest + p) mod C.
+    // Wave 0, lane p holds position p; R rounds of a wave argmax pick the
+    // most similar entries, ties to the lowest position (the older entry).
+    const int oldest = (fifo_head - count + d.C) % d.C;
+    if (wave == 0) {
+      int slot = oldest + lane;
+      if (slot >= d.C) slot -= d.C;
+      double v = (lane < count) ? sh.rho[min(slot, d.C - 1)] : -INFINITY;
+      const int rounds = min(d.R, count);
+      for (int r = 0; r < rounds; ++r) {
+        const double m = wave_max_f64(v);
+        const uint64_t tie = __ballot(lane < count && v == m);
+        const int win = __ffsll(static_cast<unsigned long long>(tie)) - 1;
+        if (r == 0) sh.d0 = m;
+        if (lane == win) {
+          b.ret[bh * d.R + r] = lane;
+          b.retslot[bh * d.R + r] = slot;
+          sh.rslot[r] = slot;
+          v = -INFINITY;
+        }
       }
-      if (rank < d.R) {
-        b.ret[bh * d.R + rank] = tid;
-        b.retslot[bh * d.R + rank] = (oldest + tid) % d.C;
-      }
-      if (rank == 0) sh.d0 = mine;
     }
     n_ret = min(d.R, count);
     __syncthreads();
@@ -417,49 +597,49 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
   }
   if (exact) {
     if (tid == 0) b.m[bh] = 0;
-    if (tid < 4) b.cnt[bh * 4 + tid] = 0;
-    for (int i = tid; i < kNumBins; i += blockDim.x) b.hist[static_cast<long>(bh) * kNumBins + i] = 0u;
+    uint4* hz = reinterpret_cast<uint4*>(b.hist + static_cast<long>(bh) * kHistSeg * kNumBins);
+    for (int i = tid; i < kHistSeg * kNumBins / 4; i += blockDim.x) hz[i] = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
 
   // ---- candidate union (Eqs. 8-9) ----
+  // Support entries below the window go through an LDS bitmap over token
+  // positions (windows of 262144) and come out ascending and de-duplicated;
+  // the window [max(0, L-W), L) holds the largest positions and is appended
+  // after them (support entries inside it are already covered).
   const int wlo = max(0, length - d.W);
-  if (tid < n_ret) {
-    const int slot = b.retslot[bh * d.R + tid];
-    sh.slot[tid] = slot;
-    sh.len[tid] = b.cache_len[static_cast<long>(bh) * d.C + slot];
-  }
-  __syncthreads();
   int M = 0;
-  for (int base = 0; base < length; base += kBitmapWords * 32) {
-    const int nbits = min(kBitmapWords * 32, length - base);
+  for (int base = 0; base < wlo; base += kBitmapWords * 32) {
+    const int nbits = min(kBitmapWords * 32, wlo - base);
     const int nwords = (nbits + 31) >> 5;
-    for (int i = tid; i < nwords; i += blockDim.x) bm[i] = 0u;
+    bitmap_clear(bm);
     __syncthreads();
-    const int total = n_ret * d.K;
-    for (int i0 = 0; i0 < total; i0 += blockDim.x * 4) {
-      int x[4];
+    for (int j0 = 0; j0 < d.K; j0 += blockDim.x) {
+      const int j = j0 + tid;
+      for (int r0 = 0; r0 < n_ret; r0 += 4) {
+        int x[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * blockDim.x + tid;
-        x[u] = -1;
-        if (i < total) {
-          const int r = i / d.K, j = i - r * d.K;
-          if (j < sh.len[r]) x[u] = b.cache_supp[(static_cast<long>(bh) * d.C + sh.slot[r]) * d.K + j] - base;
+        for (int u = 0; u < 4; ++u) {
+          // clamped entry: always a valid address, discarded when out of range
+          const int r = min(r0 + u, n_ret - 1);
+          const int slot = sh.rslot[r];
+          x[u] = b.cache_supp[(static_cast<long>(bh) * d.C + slot) * d.K + min(j, d.K - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = r0 + u;
+          const int y = x[u] - base;
+          if (r < n_ret && j < sh.len[sh.rslot[min(r, n_ret - 1)]] && y >= 0 && y < nbits) bitmap_set(bm, y);
         }
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (x[u] >= 0 && x[u] < nbits) atomicOr(&bm[x[u] >> 5], 1u << (x[u] & 31));
-    }
-    for (int x = max(wlo, base) + tid; x < base + nbits; x += blockDim.x) {
-      const int y = x - base;
-      atomicOr(&bm[y >> 5], 1u << (y & 31));
     }
     __syncthreads();
     M += bitmap_emit(bm, nwords, base, s_cand + M, sh.tmp);
     __syncthreads();
   }
+  for (int x = wlo + tid; x < length; x += blockDim.x) s_cand[M + (x - wlo)] = x;
+  M += length - wlo;
+  __syncthreads();
   for (int i = tid; i < M; i += blockDim.x) b.cand[static_cast<long>(bh) * d.cand_cap + i] = s_cand[i];
   if (tid == 0) {
     b.m[bh] = M;
@@ -469,18 +649,17 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
   // ---- candidate scores (Eq. 10) ----
   const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
   {
-    const int sub = tid & 15, rg = tid >> 4, rpr = blockDim.x >> 4;
+    const int rg = tid >> 4, rpr = blockDim.x >> 4;
     float qf[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qf[e] = sh.q[8 * sub + e];
-    constexpr int U = 8;
+    for (int e = 0; e < 8; ++e) qf[e] = sh.q[8 * part + e];
+    constexpr int U = 20;
     for (int r0 = 0; r0 < M; r0 += rpr * U) {
       uint4 kv[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = r0 + u * rpr + rg;
-        kv[u] = (i < M) ? *reinterpret_cast<const uint4*>(kb + static_cast<long>(s_cand[i]) * kHeadDim + 8 * sub)
-                        : make_uint4(0u, 0u, 0u, 0u);
+        const int i = min(r0 + u * rpr + rg, M - 1);
+        kv[u] = *reinterpret_cast<const uint4*>(kb + static_cast<long>(s_cand[i]) * kHeadDim + 8 * part);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -493,11 +672,8 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
         s = fmaf(qf[5], bf16_hi(kv[u].z), s);
         s = fmaf(qf[6], bf16_lo(kv[u].w), s);
         s = fmaf(qf[7], bf16_hi(kv[u].w), s);
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 8);
-        if (sub == 0 && i < M) s_sc[i] = s;
+        s = row_sum(s);
+        if (part == 0 && i < M) s_sc[i] = s;
       }
     }
   }
@@ -520,8 +696,9 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
     __syncthreads();
   } else {
     int need;
-    const uint32_t T = radix_kth(s_sc, M, d.K, sh, &need);
-    n = select_in_order(s_cand, s_sc, M, T, need, s_sel, s_selsc, sh);
+    uint32_t mask;
+    const uint32_t T = radix_kth(s_sc, M, d.K, sh, &mask, &need);
+    n = select_in_order(s_cand, s_sc, M, T, mask, need, s_sel, s_selsc, sh);
   }
   for (int i = tid; i < n; i += blockDim.x) {
     b.sel[static_cast<long>(bh) * d.K + i] = s_sel[i];
@@ -540,11 +717,61 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
 // the rows of one KV head are split evenly over `wpg` work groups; each
 // streams its rows exactly once and scores them for all query heads of the
 // group with MFMA 16x16x32 bf16 tiles (A = 16 key rows x 32 dims, B = 32 dims
-// x 16 query heads, fp32 accumulation). Scores go to the workspace and into a
-// per-head histogram of the top 10 bits of their ordered keys (LDS, flushed
-// with global atomics); the collect kernel finds the Top-K boundary from it.
-// Work groups whose KV group has no exact head return at once.
+// x 16 query heads, fp32 accumulation). The loads of the next 256 rows are in
+// flight while the current ones are scored (two register buffers; rows past
+// the end are clamped to a valid row and masked). Scores go to the workspace
+// and into a per-head histogram of the top 10 bits of their ordered keys
+// (LDS, flushed with global atomics into one of kHistSeg copies chosen by the
+// work group); the collect kernel finds the Top-K boundary from it. Work
+// groups whose KV group has no exact head return at once.
 // ---------------------------------------------------------------------------
+namespace {
+constexpr int kQkUnroll = 4;  // 16-row tiles per wave per stage: 256 rows per work group
+
+struct QkTiles {
+  uint4 a[kQkUnroll][4];
+};
+
+__device__ __forceinline__ void qk_load(QkTiles& t, const uint16_t* kb, int t0, int rend, int wave, int j, int kq) {
+#pragma unroll
+  for (int u = 0; u < kQkUnroll; ++u) {
+    const int r = min(t0 + (u * 4 + wave) * 16 + j, rend - 1);
+    const uint16_t* row = kb + static_cast<long>(r) * kHeadDim + 8 * kq;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) t.a[u][s] = *reinterpret_cast<const uint4*>(row + 32 * s);
+  }
+}
+
+__device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4], int t0, int rend, int wave, int kq,
+                                         bool hv, float* srow, uint32_t* hrow) {
+#pragma unroll
+  for (int u = 0; u < kQkUnroll; ++u) {
+    const int rbase = t0 + (u * 4 + wave) * 16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.a[u][s]), bq[s], acc, 0, 0, 0);
+    // lane holds query head j for rows rbase + 4*kq + 0..3
+    if (hv) {
+      const int r = rbase + 4 * kq;
+      if (r + 3 < rend) {
+        *reinterpret_cast<float4*>(srow + r) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) atomicAdd(&hrow[order_key(acc[e]) >> kHistShift], 1u);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (r + e < rend) {
+            srow[r + e] = acc[e];
+            atomicAdd(&hrow[order_key(acc[e]) >> kHistShift], 1u);
+          }
+        }
+      }
+    }
+  }
+}
+}  // namespace
+
 __global__ __launch_bounds__(256) void k_exact_qk(Dims d, Bufs b, const uint16_t* q, long q_sb, long q_sh,
                                                   const uint16_t* k, int length, int wpg) {
   const int bg = blockIdx.x / wpg, part = blockIdx.x % wpg;
@@ -565,77 +792,50 @@ __global__ __launch_bounds__(256) void k_exact_qk(Dims d, Bufs b, const uint16_t
     if (hv) u = *reinterpret_cast<const uint4*>(q + bb * q_sb + h * q_sh + 8 * kq + 32 * s);
     bq[s] = as_bf16x8(u);
   }
+  const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
+  QkTiles ta, tb;
+  qk_load(ta, kb, row0, rend, wave, j, kq);
   for (int i = threadIdx.x; i < d.G * kNumBins; i += blockDim.x) s_hist[i] = 0u;
   __syncthreads();
-  const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
   float* srow = b.score + static_cast<long>(bb * d.Hq + h) * d.score_stride;
   uint32_t* hrow = s_hist + j * kNumBins;
-  constexpr int kUnroll = 4;
-  for (int t0 = row0; t0 < rend; t0 += 64 * kUnroll) {
-    uint4 a[kUnroll][4];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int r = t0 + (u * 4 + wave) * 16 + j;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        a[u][s] = (r < rend) ? *reinterpret_cast<const uint4*>(kb + static_cast<long>(r) * kHeadDim + 8 * kq + 32 * s)
-                             : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int rbase = t0 + (u * 4 + wave) * 16;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][s]), bq[s], acc, 0, 0, 0);
-      // lane holds query head j for rows rbase + 4*kq + 0..3
-      if (hv) {
-        const int r = rbase + 4 * kq;
-        if (r + 3 < rend) {
-          *reinterpret_cast<float4*>(srow + r) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) atomicAdd(&hrow[order_key(acc[e]) >> kHistShift], 1u);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (r + e < rend) {
-              srow[r + e] = acc[e];
-              atomicAdd(&hrow[order_key(acc[e]) >> kHistShift], 1u);
-            }
-          }
-        }
-      }
-    }
+  constexpr int kStage = 64 * kQkUnroll;  // rows per stage
+  for (int t0 = row0; t0 < rend; t0 += 2 * kStage) {
+    qk_load(tb, kb, t0 + kStage, rend, wave, j, kq);
+    qk_score(ta, bq, t0, rend, wave, kq, hv, srow, hrow);
+    if (t0 + kStage >= rend) break;
+    qk_load(ta, kb, t0 + 2 * kStage, rend, wave, j, kq);
+    qk_score(tb, bq, t0 + kStage, rend, wave, kq, hv, srow, hrow);
   }
   __syncthreads();
+  uint32_t* ghist = b.hist + static_cast<long>(bb * d.Hq + g * d.G) * kHistSeg * kNumBins +
+                    (blockIdx.x % kHistSeg) * kNumBins;
   for (int i = threadIdx.x; i < d.G * kNumBins; i += blockDim.x) {
     const uint32_t c = s_hist[i];
-    if (c) {
-      const int hh = g * d.G + i / kNumBins;
-      atomicAdd(&b.hist[static_cast<long>(bb * d.Hq + hh) * kNumBins + (i % kNumBins)], c);
-    }
+    if (c) atomicAdd(&ghist[(i / kNumBins) * kHistSeg * kNumBins + (i % kNumBins)], c);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Global Top-K (Eq. 1), step 1, for exact heads: from the histogram find the
-// boundary bin (the bin holding the K-th largest score), then classify a
-// chunk of scores: indices in higher bins go to the "above" list (fewer than
-// K in all), those in the boundary bin to the boundary list. Hits are staged
-// in LDS; one atomic per list and work group reserves the global space.
+// Global Top-K (Eq. 1), step 1, for exact heads. Every work group takes a
+// chunk of 4096 scores of one head, finds the boundary bin from the
+// histogram (the bin holding the K-th largest score) and classifies its
+// scores: entries in higher bins ("above", fewer than K in all) and entries
+// in the boundary bin are written, as (index, score bits), to the chunk's own
+// region of the hit buffer (boundary from the front, above from the back) in
+// position order, with the two counts. No global atomics.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_collect(Dims d, Bufs b, int length) {
   const int bh = blockIdx.x;
   if (!b.path[bh]) return;
-  const int c0 = blockIdx.y * kCollectChunk;
+  const int chunk = blockIdx.y;
+  const int c0 = chunk * kCollectChunk;
   if (c0 >= length) return;
+  const int clen = min(kCollectChunk, length - c0);
   __shared__ int tmp[8];
   __shared__ int s_b1;
-  __shared__ int32_t s_list[kCollectChunk];
-  __shared__ int s_nu, s_nb, s_gu, s_gb;
   const int keff = min(d.K, length);
   const float* srow = b.score + static_cast<long>(bh) * d.score_stride;
-  // this thread's 16 consecutive scores, loaded before the histogram scan
   constexpr int kPerThread = kCollectChunk / 256;
   const int i0 = c0 + threadIdx.x * kPerThread;
   float v[kPerThread];
@@ -652,20 +852,24 @@ __global__ __launch_bounds__(256) void k_collect(Dims d, Bufs b, int length) {
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u) v[u] = (i0 + u < length) ? srow[i0 + u] : 0.f;
   }
-  const uint32_t* hist = b.hist + static_cast<long>(bh) * kNumBins;
+  // this thread's 4 bins, in descending order, summed over the histogram copies
+  const uint32_t* hist = b.hist + static_cast<long>(bh) * kHistSeg * kNumBins;
   constexpr int kPer = kNumBins / 256;
-  int c[kPer];
-  int csum = 0;
+  static_assert(kPer == 4, "4 bins per thread");
+  uint4 hs[kHistSeg];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    c[i] = static_cast<int>(hist[kNumBins - 1 - (kPer * threadIdx.x + i)]);
-    csum += c[i];
+  for (int sgm = 0; sgm < kHistSeg; ++sgm)
+    hs[sgm] = *reinterpret_cast<const uint4*>(hist + sgm * kNumBins + kNumBins - 4 * (threadIdx.x + 1));
+  int c[kPer] = {0, 0, 0, 0};
+#pragma unroll
+  for (int sgm = 0; sgm < kHistSeg; ++sgm) {
+    c[0] += hs[sgm].w;
+    c[1] += hs[sgm].z;
+    c[2] += hs[sgm].y;
+    c[3] += hs[sgm].x;
   }
-  if (threadIdx.x == 0) {
-    s_nu = 0;
-    s_nb = 0;
-    s_b1 = 0;
-  }
+  const int csum = c[0] + c[1] + c[2] + c[3];
+  if (threadIdx.x == 0) s_b1 = 0;
   int tot;
   const int ex = block_exclusive_scan(csum, &tot, tmp);
   if (ex < keff && ex + csum >= keff) {
@@ -688,46 +892,48 @@ __global__ __launch_bounds__(256) void k_collect(Dims d, Bufs b, int length) {
     nu += valid && bin > b1;
     nbd += valid && bin == b1;
   }
-  int ou = 0, ob = 0;
-  if (nu) ou = atomicAdd(&s_nu, nu);
-  if (nbd) ob = atomicAdd(&s_nb, nbd);
+  const int pre = block_exclusive_scan((nu << 16) | nbd, &tot, tmp);
+  int ou = pre >> 16, ob = pre & 0xffff;
+  uint2* region = b.hits + static_cast<long>(bh) * d.max_len + c0;
 #pragma unroll
   for (int u = 0; u < kPerThread; ++u) {
     if (i0 + u < length) {
       const uint32_t bin = order_key(v[u]) >> kHistShift;
-      if (bin > b1) s_list[kCollectChunk - 1 - (ou++)] = i0 + u;
-      else if (bin == b1) s_list[ob++] = i0 + u;
+      const uint2 e = make_uint2(static_cast<uint32_t>(i0 + u), __float_as_uint(v[u]));
+      if (bin > b1) region[clen - 1 - (ou++)] = e;
+      else if (bin == b1) region[ob++] = e;
     }
   }
-  __syncthreads();
-  const int tu = s_nu, tb = s_nb;
-  if (threadIdx.x == 0) {
-    s_gu = tu ? atomicAdd(&b.cnt[bh * 4 + 0], tu) : 0;
-    s_gb = tb ? atomicAdd(&b.cnt[bh * 4 + 1], tb) : 0;
-  }
-  __syncthreads();
-  int32_t* above = b.above + static_cast<long>(bh) * d.K;
-  int32_t* bnd = b.bnd + static_cast<long>(bh) * d.max_len;
-  // (fewer than K scores lie above the boundary bin; the guards only keep a
-  // broken invariant from writing out of bounds)
-  for (int t = threadIdx.x; t < tu; t += blockDim.x)
-    if (s_gu + t < d.K) above[s_gu + t] = s_list[kCollectChunk - 1 - t];
-  for (int t = threadIdx.x; t < tb; t += blockDim.x)
-    if (s_gb + t < d.max_len) bnd[s_gb + t] = s_list[t];
+  if (threadIdx.x == 0) b.ccnt[static_cast<long>(bh) * d.n_chunks + chunk] = make_int2(tot >> 16, tot & 0xffff);
 }
 
 // ---------------------------------------------------------------------------
 // Global Top-K, step 2, for exact heads, then softmax-V and the cache update.
-// Of the boundary-bin entries keep the `need` best under (score desc, index
-// asc): a radix select over 64-bit keys (ordered score << 32 | ~index), in
-// LDS when the boundary holds at most 4096 entries, else over global memory.
-// Then the K indices are put in ascending order through an LDS bitmap (S_t,
-// stored as the cache entry's support), the values are aggregated (Eq. 12)
-// and (q_bar_t, S_t) is pushed. One work group per head.
+// The chunks' "above" entries (all selected) and boundary entries are
+// gathered with their scores into LDS. Of the boundary entries the `need`
+// best under (score desc, index asc) are kept: a radix select over 64-bit
+// keys (ordered score << 32 | ~index) with per-wave histograms, in LDS when
+// the boundary holds at most 4096 entries, else read from the hit buffer.
+// The K selected indices are put in ascending order by their rank in an LDS
+// bitmap (prefix popcount), giving S_t and its scores; the values are
+// aggregated (Eq. 12) and (q_bar_t, S_t) is pushed. One work group per head.
+//
+// LDS (dynamic): A = boundary keys, later word prefix counts (32 KiB);
+// B = bitmap window (32 KiB); C = selected (index, score) pairs, unordered
+// (K); D = S_t indices and scores, ordered (K each); E = chunk offsets.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t comp_key(float s, int idx) {
-  return (static_cast<uint64_t>(order_key(s)) << 32) |
-         static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(idx));
+__device__ __forceinline__ uint64_t comp_key(float s, uint32_t idx) {
+  return (static_cast<uint64_t>(order_key(s)) << 32) | static_cast<uint64_t>(0xffffffffu - idx);
+}
+
+// Boundary entry g of a head: chunk found by binary search over the offsets.
+__device__ __forceinline__ uint2 boundary_entry(const uint2* hits_row, const int* boff, int nch, int g) {
+  int lo = 0, hi = nch;  // boff[lo] <= g < boff[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (boff[mid] <= g) lo = mid; else hi = mid;
+  }
+  return hits_row[static_cast<long>(lo) * kCollectChunk + (g - boff[lo])];
 }
 
 __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const uint16_t* v, float* out,
@@ -735,105 +941,190 @@ __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const u
   const int bh = blockIdx.x;
   if (!b.path[bh]) return;
   const int bb = bh / d.Hq, h = bh % d.Hq, g = h / d.G;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6;
   __shared__ HeadShared sh;
   extern __shared__ __align__(16) unsigned char dyn[];
-  const size_t region0 = (kBoundaryLds * 8 > kBitmapWords * 4) ? kBoundaryLds * 8 : kBitmapWords * 4;
-  uint64_t* keys = reinterpret_cast<uint64_t*>(dyn);
-  uint32_t* bm = reinterpret_cast<uint32_t*>(dyn);
-  int32_t* s_sel = reinterpret_cast<int32_t*>(dyn + region0);
-  float* s_selsc = reinterpret_cast<float*>(dyn + region0 + 4 * static_cast<size_t>(d.K));
+  constexpr size_t kRegion = kBitmapLdsWords * 4;                            // >= 4096 64-bit keys
+  static_assert(kRegion >= kBoundaryLds * 8, "boundary keys fit region A");
+  uint64_t* keys = reinterpret_cast<uint64_t*>(dyn);                         // A
+  int32_t* wpre = reinterpret_cast<int32_t*>(dyn);                           // A, later
+  uint32_t* bm = reinterpret_cast<uint32_t*>(dyn + kRegion);                 // B
+  uint2* chosen = reinterpret_cast<uint2*>(dyn + 2 * kRegion);               // C
+  int32_t* s_sel = reinterpret_cast<int32_t*>(dyn + 2 * kRegion + 8 * static_cast<size_t>(d.K));  // D
+  float* s_selsc = reinterpret_cast<float*>(dyn + 2 * kRegion + 12 * static_cast<size_t>(d.K));
+  int* aoff = reinterpret_cast<int*>(dyn + 2 * kRegion + 16 * static_cast<size_t>(d.K));           // E
+  int* boff = aoff + d.n_chunks + 1;
   const int keff = min(d.K, length);
-  const int n_above = min(b.cnt[bh * 4 + 0], keff);
-  const int nb = min(b.cnt[bh * 4 + 1], length);
-  const float* srow = b.score + static_cast<long>(bh) * d.score_stride;
-  int32_t* above = b.above + static_cast<long>(bh) * d.K;
-  const int32_t* bnd = b.bnd + static_cast<long>(bh) * d.max_len;
+  const int nch = (length + kCollectChunk - 1) / kCollectChunk;
+  const uint2* hits_row = b.hits + static_cast<long>(bh) * d.max_len;
+  const int2* ccnt = b.ccnt + static_cast<long>(bh) * d.n_chunks;
+
+  // chunk offsets of the above and boundary lists
+  {
+    const int per = (nch + blockDim.x - 1) / blockDim.x;
+    const int c0 = tid * per, c1 = min(c0 + per, nch);
+    int sa = 0, sb = 0;
+    for (int c = c0; c < c1; ++c) {
+      const int2 cc = ccnt[c];
+      sa += cc.x;
+      sb += cc.y;
+    }
+    int ta, tb;
+    int oa = block_exclusive_scan(sa, &ta, sh.tmp);
+    int ob = block_exclusive_scan(sb, &tb, sh.tmp);
+    for (int c = c0; c < c1; ++c) {
+      const int2 cc = ccnt[c];
+      aoff[c] = oa;
+      boff[c] = ob;
+      oa += cc.x;
+      ob += cc.y;
+    }
+    if (tid == 0) {
+      aoff[nch] = ta;
+      boff[nch] = tb;
+    }
+    __syncthreads();
+  }
+  const int na = min(aoff[nch], keff);
+  const int nb = boff[nch];
   const bool in_lds = nb <= kBoundaryLds;
-  if (in_lds) {
-    for (int i0 = 0; i0 < nb; i0 += blockDim.x * 4) {
-      int ix[4];
+
+  // gather: above entries into C, boundary keys into A
+  {
+    const int tot = na + (in_lds ? nb : 0);
+    for (int f0 = 0; f0 < tot; f0 += blockDim.x * 4) {
+      uint2 e[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * blockDim.x + tid;
-        ix[u] = i < nb ? bnd[i] : 0;
+        const int f = f0 + u * blockDim.x + tid;
+        e[u] = make_uint2(0u, 0u);
+        if (f < na) {
+          int lo = 0, hi = nch;
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (aoff[mid] <= f) lo = mid; else hi = mid;
+          }
+          const int clen = min(kCollectChunk, length - lo * kCollectChunk);
+          e[u] = hits_row[static_cast<long>(lo) * kCollectChunk + clen - 1 - (f - aoff[lo])];
+        } else if (f < tot) {
+          e[u] = boundary_entry(hits_row, boff, nch, f - na);
+        }
       }
-      float sv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) sv[u] = (i0 + u * blockDim.x + tid < nb) ? srow[ix[u]] : 0.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * blockDim.x + tid;
-        if (i < nb) keys[i] = comp_key(sv[u], ix[u]);
+        const int f = f0 + u * blockDim.x + tid;
+        if (f < na) chosen[f] = e[u];
+        else if (f < tot) keys[f - na] = comp_key(__uint_as_float(e[u].y), e[u].x);
       }
     }
   }
   if (tid == 0) sh.i3 = 0;
   __syncthreads();
+
+  // radix select of the `need` best boundary entries
   uint64_t prefix = 0ull, mask = 0ull;
-  int need = keff - n_above;
+  int need = keff - na;
   int ncand = nb;
   for (int shift = 56; shift >= 0 && ncand > need; shift -= 8) {
-    if (tid < 256) sh.hist[tid] = 0;
+    clear_whist(sh);
     __syncthreads();
     for (int i = tid; i < nb; i += blockDim.x) {
-      const uint64_t u = in_lds ? keys[i] : comp_key(srow[bnd[i]], bnd[i]);
-      if ((u & mask) == prefix) atomicAdd(&sh.hist[(u >> shift) & 255ull], 1);
+      uint64_t u;
+      if (in_lds) {
+        u = keys[i];
+      } else {
+        const uint2 e = boundary_entry(hits_row, boff, nch, i);
+        u = comp_key(__uint_as_float(e.y), e.x);
+      }
+      if ((u & mask) == prefix) atomicAdd(&sh.whist[wave][(u >> shift) & 255ull], 1);
     }
     __syncthreads();
-    const int digit = 255 - static_cast<int>(tid & 255);
-    const int c = (tid < 256) ? sh.hist[digit] : 0;
-    int tot;
-    const int above_cnt = block_exclusive_scan(c, &tot, sh.tmp);
-    if (tid < 256 && above_cnt < need && above_cnt + c >= need) {
-      sh.i0 = digit;
-      sh.i1 = need - above_cnt;
-      sh.i2 = c;
-    }
+    pick_digit(sh, need);
     __syncthreads();
     prefix |= static_cast<uint64_t>(sh.i0) << shift;
     mask |= 255ull << shift;
     need = sh.i1;
     ncand = sh.i2;
-    __syncthreads();
   }
   // boundary entries whose masked key is >= prefix are exactly the kept ones
   for (int i = tid; i < nb; i += blockDim.x) {
-    const int ix = bnd[i];
-    const uint64_t u = in_lds ? keys[i] : comp_key(srow[ix], ix);
+    uint2 e;
+    uint64_t u;
+    if (in_lds) {
+      u = keys[i];
+      e = make_uint2(0xffffffffu - static_cast<uint32_t>(u & 0xffffffffull), 0u);
+    } else {
+      e = boundary_entry(hits_row, boff, nch, i);
+      u = comp_key(__uint_as_float(e.y), e.x);
+    }
     if ((u & mask) >= prefix) {
       const int o = atomicAdd(&sh.i3, 1);
-      if (n_above + o < d.K) above[n_above + o] = ix;
+      if (na + o < d.K) {
+        // the score half of the key holds the ordered score; map it back
+        const uint32_t ok = static_cast<uint32_t>(u >> 32);
+        const uint32_t bits = (ok & 0x80000000u) ? (ok & 0x7fffffffu) : ~ok;
+        chosen[na + o] = make_uint2(e.x, bits);
+      }
     }
   }
   __syncthreads();
-  // ascending order through the bitmap
-  int total = 0;
+  const int n = min(na + sh.i3, keff);
+
+  // ascending order: rank of each chosen index = popcount of the set bits below it
+  int base_out = 0;
   for (int base = 0; base < length; base += kBitmapWords * 32) {
     const int nbits = min(kBitmapWords * 32, length - base);
     const int nwords = (nbits + 31) >> 5;
-    for (int i = tid; i < nwords; i += blockDim.x) bm[i] = 0u;
+    bitmap_clear(bm);
     __syncthreads();
-    for (int i = tid; i < keff; i += blockDim.x) {
-      const int x = above[i] - base;
-      if (x >= 0 && x < nbits) atomicOr(&bm[x >> 5], 1u << (x & 31));
+    for (int i = tid; i < n; i += blockDim.x) {
+      const int x = static_cast<int>(chosen[i].x) - base;
+      if (x >= 0 && x < nbits) bitmap_set(bm, x);
     }
     __syncthreads();
-    total += bitmap_emit(bm, nwords, base, s_sel + total, sh.tmp);
+    // word prefix counts: fixed 16-word slice per thread (same padded layout)
+    {
+      const int w0 = tid * kSliceWords;
+      const uint32_t* p = bm + tid * (kSliceWords + 1);
+      uint32_t w[kSliceWords];
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < kSliceWords; ++i) {
+        w[i] = p[i];
+        cnt += __popc(w[i]);
+      }
+      int wtot;
+      int run = block_exclusive_scan(cnt, &wtot, sh.tmp);
+      int* q = wpre + tid * (kSliceWords + 1);
+#pragma unroll
+      for (int i = 0; i < kSliceWords; ++i) {
+        q[i] = run;
+        run += __popc(w[i]);
+      }
+      (void)w0;
+      sh.i2 = wtot;  // read after the barrier below
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += blockDim.x) {
+      const uint2 e = chosen[i];
+      const int x = static_cast<int>(e.x) - base;
+      if (x >= 0 && x < nbits) {
+        const int w = x >> 5;
+        const int pos = base_out + wpre[bm_at(w)] + __popc(bm[bm_at(w)] & ((1u << (x & 31)) - 1u));
+        s_sel[pos] = static_cast<int32_t>(e.x);
+        s_selsc[pos] = __uint_as_float(e.y);
+      }
+    }
+    base_out += sh.i2;
     __syncthreads();
   }
-  const int n = min(total, keff);
   float mx = kNegInf;
   for (int i = tid; i < n; i += blockDim.x) {
-    const float s = srow[s_sel[i]];
-    s_selsc[i] = s;
-    mx = fmaxf(mx, s);
-  }
-  mx = block_max_f32(mx, reinterpret_cast<float*>(sh.tmp));
-  for (int i = tid; i < n; i += blockDim.x) {
+    mx = fmaxf(mx, s_selsc[i]);
     b.sel[static_cast<long>(bh) * d.K + i] = s_sel[i];
     b.selsc[static_cast<long>(bh) * d.K + i] = s_selsc[i];
   }
+  mx = block_max_f32(mx, reinterpret_cast<float*>(sh.tmp));
   if (tid == 0) b.sellen[bh] = n;
   if (sel_out != nullptr)
     for (int i = tid; i < d.K; i += blockDim.x) sel_out[static_cast<long>(bh) * d.K + i] = i < n ? s_sel[i] : -1;
