@@ -12,7 +12,14 @@ resident in HBM before the timed region; nothing is allocated inside it.
 Prints one JSON line: the metric is microseconds per decode step per layer
 (lower is better) on the 128K-context, K = 512 GQA layer, with the exact
 Top-K baseline, a forced-reuse run, the path mix, a per-kernel breakdown, the
-roofline of the full-history score kernel and the CPU oracle baseline.
+roofline of the kernel with the largest share of the step (and of every
+kernel of the step), of the score kernel on all-exact steps, whole-step
+rooflines of the exact and the forced-reuse steps, and the CPU oracle
+baseline.
+
+Counter support: --copy-calibration runs plain copies of known size, and
+--summarize-traffic turns rocprofv3 FETCH_SIZE / WRITE_SIZE runs into the
+per-launch HBM bytes that the roofline objects report as "traffic".
 """
 from __future__ import annotations
 
@@ -49,7 +56,102 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["natural", "exact", "reuse"], default=None,
                     help="run one timed leg only (for profiler runs)")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the per-kernel event-timed pass (counter runs: the last --steps "
+                         "dispatches of each kernel are then the timed steps)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 8 plain device-to-device copies of 256 MiB each, the known-size "
+                         "reference for the HBM byte counters")
+    ap.add_argument("--summarize-traffic", metavar="DIR", default=None,
+                    help="turn rocprofv3 counter runs under DIR (<leg>_<COUNTER>/ and "
+                         "copy_<COUNTER>/) into profiles/traffic.json and exit")
+    ap.add_argument("--last", type=int, default=64,
+                    help="with --summarize-traffic: dispatches per kernel to average (the last ones)")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20
+COPY_REPS = 8
+TRAFFIC_COUNTERS = ("FETCH_SIZE", "WRITE_SIZE")
+
+
+def copy_calibration():
+    """Eight plain device copies of COPY_BYTES: each reads and writes exactly that
+    many bytes of HBM, which scales the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(COPY_REPS):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "copies": COPY_REPS}), flush=True)
+
+
+def _counter_rows(path):
+    import csv
+    rows = []
+    for dirpath, _, files in os.walk(path):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                with open(os.path.join(dirpath, fn)) as f:
+                    rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _per_dispatch(rows, counter):
+    """{kernel short name: [counter value per dispatch, in dispatch order]} (KiB)."""
+    per = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r["Kernel_Name"].split("(")[0].split("::")[-1].strip()
+        per.setdefault(name, {}).setdefault(int(r["Dispatch_Id"]), 0.0)
+        per[name][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return {k: [v[i] for i in sorted(v)] for k, v in per.items()}
+
+
+def summarize_traffic(root, last, workload):
+    """Average FETCH_SIZE / WRITE_SIZE over the last `last` dispatches of each
+    library kernel per leg, scaled so that a plain copy of known size reads
+    (and writes) exactly its size; written to profiles/traffic.json."""
+    scale = {}
+    for c in TRAFFIC_COUNTERS:
+        per = _per_dispatch(_counter_rows(os.path.join(root, f"copy_{c}")), c)
+        vals = [v for k, vs in per.items() if "copy" in k.lower() for v in vs
+                if v * 1024 > COPY_BYTES / 2]
+        if not vals:
+            raise SystemExit(f"no copy dispatch with {c} under {root}/copy_{c}")
+        scale[c] = COPY_BYTES / (1024.0 * float(np.median(vals)))
+    out = []
+    for leg in ("natural", "exact", "reuse"):
+        got = {}
+        for c in TRAFFIC_COUNTERS:
+            d = os.path.join(root, f"{leg}_{c}")
+            if os.path.isdir(d):
+                got[c] = _per_dispatch(_counter_rows(d), c)
+        if len(got) != len(TRAFFIC_COUNTERS):
+            continue
+        for kern in sorted(got["FETCH_SIZE"]):
+            if not kern.startswith("k_") or kern not in got["WRITE_SIZE"]:
+                continue
+            f = got["FETCH_SIZE"][kern][-last:]
+            w = got["WRITE_SIZE"][kern][-last:]
+            fb = float(np.mean(f)) * 1024 * scale["FETCH_SIZE"]
+            wb = float(np.mean(w)) * 1024 * scale["WRITE_SIZE"]
+            out.append({"kernel": kern, "workload": workload, "leg": leg, "dispatches": len(f),
+                        "fetch_bytes_per_launch": int(fb), "write_bytes_per_launch": int(wb),
+                        "hbm_bytes_per_launch": int(fb + wb),
+                        "copy_scale": {c: round(scale[c], 4) for c in TRAFFIC_COUNTERS},
+                        "kernel_source_sha": kernel_source_hash()})
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    for r in out:
+        print(f"{r['leg']:8s} {r['kernel']:12s} fetch {r['fetch_bytes_per_launch'] / 1e6:9.3f} MB "
+              f"write {r['write_bytes_per_launch'] / 1e6:8.3f} MB per launch")
+    print(f"copy scale {scale}; wrote {path}")
 
 
 def kernel_source_hash():
@@ -59,7 +161,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, workload):
+def load_traffic(kernel, workload, leg):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -69,17 +171,23 @@ def load_traffic(kernel, workload):
         rows = json.load(f)
     for r in rows:
         if r.get("kernel") == kernel and r.get("workload") == workload and \
-                r.get("kernel_source_sha") == kernel_source_hash():
+                r.get("leg") == leg and r.get("kernel_source_sha") == kernel_source_hash():
             return r.get("hbm_bytes_per_launch")
     return None
 
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic, args.last, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path has no "
               f"multi-GPU leg", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
 
     from sparse_long_context_head_amd import binding as B
@@ -139,6 +247,8 @@ def main():
         return a.elapsed_time(b) / args.steps * 1000.0  # us per layer-step
 
     def kernel_breakdown(layers, exact=False):
+        run(layers, 0, args.warmup, exact)
+        torch.cuda.synchronize()
         for layer in layers:
             B.retopk_set_timing(layer.handle, True)
             B.retopk_read_kernel_times(layer.handle)
@@ -164,6 +274,51 @@ def main():
                          "refresh_every": wl.refresh_every, "rotated_layers": nl,
                          "decode_positions": n_pos, "parallelism": "single GPU"}}
 
+    def timed_paths(layers):
+        """Path bits and M_t of every head over the timed layer-steps."""
+        p0 = args.warmup // nl + 1
+        npos = args.steps // nl
+        paths, ms = [], []
+        for layer in layers:
+            path, _, m = layer.stats(p0, npos)
+            paths.append(path)
+            ms.append(m)
+        return np.concatenate(paths), np.concatenate(ms)
+
+    def kernel_bytes(path, m, length):
+        """Algorithmic HBM bytes per launch of each decode-step kernel,
+        averaged over the timed steps (path bits and M_t per head-step from
+        the statistics ring). Only what the method must move is counted:
+        queries, the q_bar cache, the retrieved supports, key and value rows,
+        outputs and cache entries; candidate, score and histogram workspaces
+        are not. k_head: every head's query and C cached normalised queries; a
+        reusing head's R supports, M_t key rows, min(K, M_t) value rows, its
+        output and cache entry. k_score: every key row of a KV group holding
+        an exact head. k_collect: nothing (it reads and writes workspaces).
+        k_finish: an exact head's K value rows, output and cache entry."""
+        d, K, C, R = wl.head_dim, wl.top_k, wl.cache_cap, wl.top_r
+        T = path.shape[0]
+        exact = (path & 1) == 1
+        reuse = ~exact
+        gex = exact.reshape(T, wl.batch, wl.n_kv_heads, G).any(-1)
+        n = np.minimum(K, m)
+        entry = 4 * d + 4 * K
+        per = {
+            "k_head": (2 * d + 4 * C * d
+                       + reuse * (4 * R * K + ROW_BYTES * (m + n) + 4 * d + entry)).sum(),
+            "k_score": gex.sum() * ROW_BYTES * length,
+            "k_collect": 0.0,
+            "k_finish": (exact * (ROW_BYTES * min(K, length) + 4 * d + entry)).sum(),
+        }
+        return {k: float(v) / T for k, v in per.items()}
+
+    def roofline(kernel, alg, us_launch, leg):
+        gbs = alg / (us_launch * 1e-6) / 1e9
+        return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic(kernel, wl.name, leg),
+                "algorithmic_bytes_per_launch": int(alg), "us_per_launch": us_launch}
+
     # --- natural ReTopK step (the headline value) ---------------------------
     if args.only in (None, "natural"):
         nat = make_layers()
@@ -172,16 +327,7 @@ def main():
         result["value"] = round(us, 3)
         result["ms_per_step"] = round(us / 1000.0, 6)
         log(f"natural ReTopK: {us:.2f} us/step/layer")
-        # path mix over the timed positions
-        p0 = args.warmup // nl + 1
-        npos = args.steps // nl
-        paths, ms = [], []
-        for layer in nat:
-            path, _, m = layer.stats(p0, npos)
-            paths.append(path)
-            ms.append(m)
-        path = np.concatenate(paths)
-        m = np.concatenate(ms)
+        path, m = timed_paths(nat)
         exact = (path & 1) == 1
         refresh = (path & 2) == 2
         gexact = exact.reshape(exact.shape[0], wl.batch, wl.n_kv_heads, G).any(-1)
@@ -197,10 +343,26 @@ def main():
                     "max": int(mr.max()) if mr.size else None}}
         for layer in nat:
             layer.close()
-        nat = make_layers()
-        result["kernels_natural"] = kernel_breakdown(nat)
-        for layer in nat:
-            layer.close()
+        if not args.no_breakdown:
+            nat = make_layers()
+            kb = kernel_breakdown(nat)
+            result["kernels_natural"] = kb
+            # roofline of every kernel of the step; the headline one is the
+            # kernel with the largest share of the step time
+            path_b, m_b = timed_paths(nat)
+            mean_len = L0 + (args.warmup + args.steps / 2) / nl
+            alg = kernel_bytes(path_b, m_b, mean_len)
+            rl = {kn: roofline(kn, alg[kn], kb[kn]["us_per_launch"], "natural")
+                  for kn in alg if kn in kb}
+            if rl:
+                dom = max(rl, key=lambda kn: kb[kn]["us_per_step"])
+                result["roofline"] = rl[dom]
+                result["rooflines_natural"] = {kn: {k: r[k] for k in ("achieved", "frac", "traffic",
+                                                                      "algorithmic_bytes_per_launch",
+                                                                      "us_per_launch")}
+                                               for kn, r in rl.items()}
+            for layer in nat:
+                layer.close()
 
     # --- exact Top-K baseline -----------------------------------------------
     if args.only in (None, "exact"):
@@ -208,23 +370,38 @@ def main():
         us_ex = timed(ex, exact=True)
         result["exact_topk_us_per_step"] = round(us_ex, 3)
         log(f"exact Top-K: {us_ex:.2f} us/step/layer")
-        kb = kernel_breakdown(ex, exact=True)
-        result["kernels_exact"] = kb
+        mean_len = L0 + (args.warmup + args.steps / 2) / nl
+        # the whole exact step: every KV group's key rows once, the union of the
+        # selected value rows per group (measured), q in and out
+        pos = (args.warmup + args.steps // 2) // nl + 1
+        sel = torch.empty((wl.batch, wl.n_q_heads, wl.top_k), dtype=torch.int32, device=dev)
+        ex[0].exact_topk_attn(q_dec[pos - 1], ks[0], vs[0], L0 + pos, out, sel, stream)
+        torch.cuda.synchronize()
+        s_ = sel.cpu().numpy().reshape(wl.batch, wl.n_kv_heads, G * wl.top_k)
+        v_rows = sum(len(np.unique(r[r >= 0])) for r in s_.reshape(-1, G * wl.top_k))
+        step_alg = ROW_BYTES * (mean_len * wl.batch * wl.n_kv_heads + v_rows) \
+            + wl.batch * wl.n_q_heads * wl.head_dim * (2 + 4)
+        gbs = step_alg / (us_ex * 1e-6) / 1e9
+        result["exact_step_roofline"] = {"bound": "hbm", "achieved": round(gbs, 1),
+                                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                         "algorithmic_bytes_per_step": int(step_alg),
+                                         "unique_v_rows": int(v_rows)}
         for layer in ex:
             layer.close()
-        # roofline of the full-history score kernel (all KV groups streamed per launch)
-        kq = kb.get("k_exact_qk")
-        if kq:
-            mean_len = L0 + (args.warmup + args.steps / 2) / nl
-            alg = ROW_BYTES * mean_len * wl.batch * wl.n_kv_heads \
-                + 2 * wl.batch * wl.n_q_heads * wl.head_dim
-            gbs = alg / (kq["us_per_launch"] * 1e-6) / 1e9
-            result["roofline"] = {"kernel": "k_exact_qk", "bound": "hbm",
-                                  "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                  "traffic": load_traffic("k_exact_qk", wl.name),
-                                  "algorithmic_bytes_per_launch": int(alg),
-                                  "us_per_launch": kq["us_per_launch"]}
+        if not args.no_breakdown:
+            ex = make_layers()
+            kb = kernel_breakdown(ex, exact=True)
+            result["kernels_exact"] = kb
+            for layer in ex:
+                layer.close()
+            # the score kernel on all-exact steps: every KV group's key rows once
+            kq = kb.get("k_score")
+            if kq:
+                alg = ROW_BYTES * mean_len * wl.batch * wl.n_kv_heads \
+                    + 2 * wl.batch * wl.n_q_heads * wl.head_dim
+                result["roofline_exact_score"] = roofline("k_score", alg, kq["us_per_launch"],
+                                                          "exact")
         if "value" in result:
             result["speedup_vs_exact"] = round(us_ex / result["value"], 3)
 
@@ -234,9 +411,21 @@ def main():
         us_ru = timed(ru)
         result["forced_reuse_us_per_step"] = round(us_ru, 3)
         log(f"forced reuse: {us_ru:.2f} us/step/layer")
-        result["kernels_forced_reuse"] = kernel_breakdown(ru)
+        path_r, m_r = timed_paths(ru)
+        alg = sum(kernel_bytes(path_r, m_r, L0 + (args.warmup + args.steps / 2) / nl).values())
+        gbs = alg / (us_ru * 1e-6) / 1e9
+        result["reuse_step_roofline"] = {"bound": "hbm", "achieved": round(gbs, 1),
+                                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                         "algorithmic_bytes_per_step": int(alg),
+                                         "M_t_mean": round(float(m_r.mean()), 1)}
         for layer in ru:
             layer.close()
+        if not args.no_breakdown:
+            ru = make_layers(tau=-2.0, refresh_every=0)
+            result["kernels_forced_reuse"] = kernel_breakdown(ru)
+            for layer in ru:
+                layer.close()
         if "exact_topk_us_per_step" in result:
             result["speedup_reuse_vs_exact"] = round(result["exact_topk_us_per_step"] / us_ru, 3)
 

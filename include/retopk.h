@@ -74,7 +74,7 @@ typedef enum retopk_status {
 typedef struct retopk_params {
   int32_t batch;          /* B >= 1                                              */
   int32_t n_q_heads;      /* Hq >= 1                                             */
-  int32_t n_kv_heads;     /* Hkv >= 1, divides Hq, Hq / Hkv <= 16                */
+  int32_t n_kv_heads;     /* Hkv >= 1, divides Hq, Hq / Hkv <= 16, B*Hkv <= 1024 */
   int32_t head_dim;       /* D, must be 128                                      */
   int32_t max_len;        /* Lmax: rows of the k / v buffers, 1 .. 2^24          */
   int32_t top_k;          /* K, 1 .. 8192                                        */

@@ -156,14 +156,18 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   {
     Dims probe{};
     probe.K = p.top_k;
+    probe.G = p.n_q_heads / p.n_kv_heads;
     probe.cand_cap = static_cast<int>(cand);
     probe.n_chunks = (p.max_len + kCollectChunk - 1) / kCollectChunk;
     if (head_lds_bytes(probe) > static_cast<size_t>(kLdsLimit) ||
-        finish_lds_bytes(probe) > static_cast<size_t>(kLdsLimit))
+        finish_lds_bytes(probe) > static_cast<size_t>(kLdsLimit) ||
+        score_lds_bytes(probe) > static_cast<size_t>(kLdsLimit))
       return fail(RETOPK_OUT_OF_RANGE, "retopk_create: top_k / top_r / window need more LDS than a work group has");
   }
   const long long bh = static_cast<long long>(p.batch) * p.n_q_heads;
   if (bh > (1 << 20)) return fail(RETOPK_OUT_OF_RANGE, "retopk_create: batch * n_q_heads too large");
+  if (static_cast<long long>(p.batch) * p.n_kv_heads > 1024)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_create: batch * n_kv_heads must be <= 1024");
 
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
@@ -211,7 +215,6 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   A(&b.retslot, BH * d.R);
   A(&b.m, BH);
   A(&b.cand, BH * d.cand_cap);
-  A(&b.cscore, BH * d.cand_cap);
   A(&b.score, BH * d.score_stride);
   A(&b.hist, BH * kHistSeg * kNumBins);
   A(&b.hits, BH * d.max_len);
@@ -265,7 +268,7 @@ retopk_status retopk_init_from_prefill(retopk_handle* h, const uint16_t* q_tail,
     st = h->run(kKHead, s, [&] {
       return launch_head(d, b, qi, q_sb, q_sh, nullptr, nullptr, nullptr, len, 0, kModeExact, -1, s);
     });
-    if (st == RETOPK_OK) st = h->run(kKExactQK, s, [&] { return launch_exact_qk(d, b, qi, q_sb, q_sh, k, len, s); });
+    if (st == RETOPK_OK) st = h->run(kKScore, s, [&] { return launch_score(d, b, qi, q_sb, q_sh, k, len, s); });
     if (st == RETOPK_OK) st = h->run(kKCollect, s, [&] { return launch_collect(d, b, len, s); });
     if (st == RETOPK_OK)
       st = h->run(kKFinish, s, [&] { return launch_finish(d, b, nullptr, nullptr, nullptr, len, 1, s); });
@@ -293,7 +296,7 @@ retopk_status retopk_decode_step(retopk_handle* h, const uint16_t* q, const uint
   retopk_status st = h->run(kKHead, s, [&] {
     return launch_head(d, b, q, q_sb, q_sh, k, v, out, length, t_dec, kModeDecode, slot, s);
   });
-  if (st == RETOPK_OK) st = h->run(kKExactQK, s, [&] { return launch_exact_qk(d, b, q, q_sb, q_sh, k, length, s); });
+  if (st == RETOPK_OK) st = h->run(kKScore, s, [&] { return launch_score(d, b, q, q_sb, q_sh, k, length, s); });
   if (st == RETOPK_OK) st = h->run(kKCollect, s, [&] { return launch_collect(d, b, length, s); });
   if (st == RETOPK_OK) st = h->run(kKFinish, s, [&] { return launch_finish(d, b, v, out, nullptr, length, 1, s); });
   return st;
@@ -318,7 +321,7 @@ retopk_status retopk_exact_topk_attn(retopk_handle* h, const uint16_t* q, const 
   retopk_status st = h->run(kKHead, s, [&] {
     return launch_head(d, b, q, q_sb, q_sh, nullptr, nullptr, nullptr, length, 0, kModeExact, -1, s);
   });
-  if (st == RETOPK_OK) st = h->run(kKExactQK, s, [&] { return launch_exact_qk(d, b, q, q_sb, q_sh, k, length, s); });
+  if (st == RETOPK_OK) st = h->run(kKScore, s, [&] { return launch_score(d, b, q, q_sb, q_sh, k, length, s); });
   if (st == RETOPK_OK) st = h->run(kKCollect, s, [&] { return launch_collect(d, b, length, s); });
   if (st == RETOPK_OK) st = h->run(kKFinish, s, [&] { return launch_finish(d, b, v, out, sel_out, length, 0, s); });
   return st;

@@ -16,13 +16,13 @@ constexpr int kHistBits = 10;        // first-level histogram: top 10 bits of th
 constexpr int kNumBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
 constexpr int kStatsCap = 4096;      // decode steps kept in the statistics ring
-constexpr int kExactWGTarget = 512;  // work groups of the full-history QK kernel (about 2 per CU)
-constexpr int kExactMinRows = 1024;  // ... each with at least this many key rows
+constexpr int kExactWGTarget = 512;  // work groups of the full-history score kernel (2 per CU)
+constexpr int kExactMinRows = 1024;  // ... with about this many key rows each, at least
 constexpr int kHistSeg = 8;          // copies of each head's histogram (spreads the atomics)
-constexpr int kCollectChunk = 4096;  // scores per work group of the threshold/collect kernel
+constexpr int kCollectChunk = 16384; // scores per work group of the threshold/collect step
+constexpr int kBoundaryLds = 4096;   // boundary entries resolved in LDS (32 KiB of 64-bit keys)
 constexpr int kHeadThreads = 512;    // threads of the per-head kernels
 constexpr int kBitmapWords = 8192;   // LDS bitmap window: 262144 token positions (32 KiB)
-constexpr int kBoundaryLds = 4096;   // boundary entries resolved in LDS (32 KiB of 64-bit keys)
 constexpr int kLdsLimit = 160 * 1024 - 20 * 1024;  // dynamic LDS a per-head kernel may use
 constexpr int kMaxCand = 16384;      // R*K + W limit (candidate keys kept in LDS for reranking)
 
@@ -52,7 +52,6 @@ struct Bufs {
   int32_t* retslot;        // [BH, R]   their ring slots
   int32_t* m;              // [BH]      M_t
   int32_t* cand;           // [BH, cand_cap]  A_t ascending
-  float* cscore;           // [BH, cand_cap]  q.k of A_t
   float* score;            // [BH, score_stride]  full-history q.k
   uint32_t* hist;          // [BH, kHistSeg, kNumBins]  histogram of ordered score keys
   uint2* hits;             // [BH, max_len] per score chunk of kCollectChunk positions: the
@@ -68,30 +67,38 @@ struct Bufs {
   int32_t* st_m;           // [kStatsCap, BH]
 };
 
-enum KernelId : int { kKHead = 0, kKExactQK, kKCollect, kKFinish, kKReset, kNumKernels };
+enum KernelId : int { kKHead = 0, kKScore, kKCollect, kKFinish, kKReset, kNumKernels };
 
 const char* kernel_name(int id);
 
-// Dynamic LDS of the per-head kernels for the given dimensions.
+// Dynamic LDS of the kernels for the given dimensions.
 size_t head_lds_bytes(const Dims& d);
+size_t score_lds_bytes(const Dims& d);
 size_t finish_lds_bytes(const Dims& d);
+// Grid of the full-history score kernel at this length.
+int score_grid(const Dims& d, int length);
 
-// Launch helpers (retopk_kernels.hip). Each returns the hipError_t of the launch.
+// Launch helpers (retopk_kernels.hip). Each returns the hipError_t of the
+// launch. A decode step, the exact Top-K baseline and the cache
+// initialisation are each head -> score -> collect -> finish on one stream.
 enum HeadMode : int { kModeDecode = 0, kModeExact = 1 };
 
-// Raise the dynamic-LDS limit of the per-head kernels to what `d` needs.
+// Raise the dynamic-LDS limit of the kernels to what `d` needs.
 hipError_t configure_kernels(const Dims& d);
 hipError_t launch_reset(const Dims& d, const Bufs& b, hipStream_t s);
-// Recall, path decision and (for reuse heads) the whole reuse path with the
-// cache update. In kModeExact every head is marked exact (no recall).
-hipError_t launch_head(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
-                       const uint16_t* k, const uint16_t* v, float* out, int length, int t_dec,
-                       int mode, int stats_slot, hipStream_t s);
-hipError_t launch_exact_qk(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
-                           const uint16_t* k, int length, hipStream_t s);
+// Recall, path decision and the reuse path of reuse heads (k, v, out are
+// used by reuse heads only). In kModeExact every head is marked exact (no
+// recall).
+hipError_t launch_head(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh, const uint16_t* k,
+                       const uint16_t* v, float* out, int length, int t_dec, int mode, int stats_slot,
+                       hipStream_t s);
+// Full-history scores and histogram of exact heads.
+hipError_t launch_score(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
+                        const uint16_t* k, int length, hipStream_t s);
+// Exact heads, global Top-K step 1: threshold bin and collection.
 hipError_t launch_collect(const Dims& d, const Bufs& b, int length, hipStream_t s);
-// Global Top-K resolution, softmax-V (skipped when v or out is NULL) and the
-// cache update (when push) for exact heads.
+// Exact heads, global Top-K step 2, softmax-V (skipped when v or out is NULL),
+// S_t to sel_out (when not NULL) and the cache update (when push).
 hipError_t launch_finish(const Dims& d, const Bufs& b, const uint16_t* v, float* out, int32_t* sel_out,
                          int length, int push, hipStream_t s);
 

@@ -2,23 +2,30 @@
 //
 // Method: "Recall Before You Rank: Similarity-Guided Top-K Reuse for
 // Efficient Long-Context Attention", Methodology section. A decode step is
-// four launches on one stream:
+// four launches on one stream; a kernel boundary is the only point where
+// data passes between work groups (an in-kernel handoff across work groups
+// costs more than a launch on this part, because a device-scope release or
+// acquire writes back or invalidates a whole L2):
 //
-//   k_head      one work group per query head: recall (Eqs. 5-7) and the path
-//               rule (Eq. 13); for reuse heads, in the same work group, the
-//               candidate union (Eqs. 8-9), candidate scores (Eq. 10), the
-//               rerank to K (Eq. 11), sparse softmax-V (Eq. 12) and the cache
-//               update. No data crosses work groups, so no inter-group sync.
-//   k_exact_qk  full-history scores (Eq. 4) for the KV groups holding at least
-//               one exact head, GQA-grouped on MFMA, plus a score histogram;
-//   k_collect   global Top-K (Eq. 1), step 1: threshold bin and collection;
-//   k_finish    global Top-K, step 2: boundary resolution and ascending order;
-//               then softmax-V and the cache update for exact heads.
+//   k_head     one work group per query head: recall (Eqs. 5-7) and the path
+//              rule (Eq. 13); a reuse head runs its whole path in the same
+//              work group: candidate union (Eqs. 8-9), candidate scores
+//              (Eq. 10), rerank (Eq. 11), softmax-V (Eq. 12) and the cache
+//              update;
+//   k_score    full-history scores (Eq. 4) and a score histogram of every
+//              exact head, GQA-grouped on MFMA, the rows of the exact KV groups
+//              spread over the whole grid;
+//   k_collect  global Top-K (Eq. 1) step 1: threshold bin and collection,
+//              many work groups per exact head;
+//   k_finish   global Top-K step 2, softmax-V and the cache update, one work
+//              group per exact head.
 //
-// The path flag stays on the device: the exact-path kernels read it and
-// return at once where no head of theirs is exact, so the host never waits.
-// Every phase issues its global loads before consuming them, so a phase costs
-// about one memory round trip rather than one per loop iteration.
+// The exact Top-K baseline and the cache initialisation are the same four
+// kernels with every head marked exact. The path flag stays on the device:
+// each kernel reads it and work of the other path returns at once, so the
+// host never waits. Every phase issues its global loads before consuming
+// them, so a phase costs about one memory round trip rather than one per loop
+// iteration.
 
 #include "retopk_internal.h"
 
@@ -140,6 +147,22 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x + (row > 0 ? t0 : 0) + (row > 1 ? t1 : 0) + (row > 2 ? t2 : 0);
 }
 
+// Slot for every lane with `pred` in an LDS list whose length is *counter:
+// one atomic per wave (ballot, then rank by mbcnt). The value is meaningful
+// only where pred holds. Every lane of the wave must call it.
+__device__ __forceinline__ int wave_slot(bool pred, int* counter) {
+  const uint64_t m = __ballot(pred);
+  const uint32_t lo = static_cast<uint32_t>(m), hi = static_cast<uint32_t>(m >> 32);
+  const int rank = __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+  int base = 0;
+  if (m != 0ull) {
+    const int leader = __builtin_amdgcn_readfirstlane(__ffsll(static_cast<long long>(m)) - 1);
+    if ((threadIdx.x & 63) == leader) base = atomicAdd(counter, __popcll(m));
+    base = __builtin_amdgcn_readlane(base, leader);
+  }
+  return base + rank;
+}
+
 // Block-wide exclusive prefix sum of one int per thread. `tmp` holds at
 // least blockDim.x / 64 ints. Every thread of the block must call it.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* tmp) {
@@ -186,23 +209,31 @@ __device__ __forceinline__ void bitmap_clear(uint32_t* bm) {
 
 __device__ __forceinline__ void bitmap_set(uint32_t* bm, int x) { atomicOr(&bm[bm_at(x >> 5)], 1u << (x & 31)); }
 
+// Clear the words 0 .. nwords-1 (nwords >= 1) of a bitmap window, any block size.
+__device__ __forceinline__ void bitmap_clear_n(uint32_t* bm, int nwords) {
+  const int n = bm_at(nwords - 1) + 1;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) bm[i] = 0u;
+}
+
 // Emit, in ascending order, the positions base + bit of every set bit of an
 // LDS bitmap window of `nwords` words to out[0 ..). Returns the number emitted
-// (the same value in every thread). Every thread of the block must call it.
+// (the same value in every thread). Each thread takes Per consecutive words
+// (Per = 8 covers windows of up to 4096 words with every thread busy).
+// Every thread of the block must call it.
+template <int Per>
 __device__ __forceinline__ int bitmap_emit(const uint32_t* bm, int nwords, int base, int32_t* out, int* tmp) {
-  uint32_t w[kSliceWords];
-  const uint32_t* p = bm + threadIdx.x * (kSliceWords + 1);
-  const int w0 = threadIdx.x * kSliceWords;
+  uint32_t w[Per];
+  const int w0 = threadIdx.x * Per;
   int cnt = 0;
 #pragma unroll
-  for (int i = 0; i < kSliceWords; ++i) {
-    w[i] = (w0 + i < nwords) ? p[i] : 0u;
+  for (int i = 0; i < Per; ++i) {
+    w[i] = (w0 + i < nwords) ? bm[bm_at(w0 + i)] : 0u;
     cnt += __popc(w[i]);
   }
   int total;
   int off = block_exclusive_scan(cnt, &total, tmp);
 #pragma unroll
-  for (int i = 0; i < kSliceWords; ++i) {
+  for (int i = 0; i < Per; ++i) {
     uint32_t bits = w[i];
     while (bits) {
       const int b = __ffs(bits) - 1;
@@ -217,7 +248,7 @@ __device__ __forceinline__ int bitmap_emit(const uint32_t* bm, int nwords, int b
 struct HeadShared {
   float q[kHeadDim];                   // raw query as float
   float qbar[kHeadDim];                // normalised query
-  double rho[64];                      // rho of each ring slot
+  double rho[64];                      // rho of each held entry, by FIFO position
   int len[64];                         // support size of each ring slot
   int rslot[64];                       // ring slots of the retrieved entries, best first
   __align__(16) int whist[kHeadThreads / 64][256];   // one radix histogram per wave
@@ -356,11 +387,15 @@ __device__ __forceinline__ int select_in_order(const int32_t* idx, const float* 
 }
 
 // Sparse softmax-V (Eq. 12) over n selected rows (indices and unscaled
-// scores in LDS; mx = their maximum): 16 lanes per value row (16 bytes
-// each), 16 row loads in flight per thread. Writes out[0 .. 127] when out is
-// not NULL. Every thread of the block must call it.
+// scores in LDS; mx = the maximum over the whole support): 16 lanes per
+// value row (16 bytes each), 16 row loads in flight per thread. With out_z
+// NULL it writes the normalised output out[0 .. 127]; otherwise the
+// unnormalised sums sum_i exp((s_i - mx)/sqrt(d)) v_i to out[0 .. 127] and
+// sum_i exp((s_i - mx)/sqrt(d)) to *out_z, so that disjoint slices of one
+// support can be merged by adding them. Nothing is written when out is NULL.
+// Every thread of the block must call it.
 __device__ __forceinline__ void attend(const int32_t* sel, const float* sc, int n, float mx, const uint16_t* vb, float* out,
-                       HeadShared& sh) {
+                                       float* out_z, HeadShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int sub = threadIdx.x & 15, rg = threadIdx.x >> 4, rpr = blockDim.x >> 4;
   constexpr int U = 16;
@@ -412,7 +447,12 @@ __device__ __forceinline__ void attend(const int32_t* sel, const float* sc, int 
       a += sh.red[w][threadIdx.x];
       zz += sh.red[w][kHeadDim];
     }
-    out[threadIdx.x] = a / zz;
+    if (out_z == nullptr) {
+      out[threadIdx.x] = a / zz;
+    } else {
+      out[threadIdx.x] = a;
+      if (threadIdx.x == 0) *out_z = zz;
+    }
   }
   __syncthreads();
 }
@@ -444,9 +484,17 @@ size_t head_lds_bytes(const Dims& d) {
   return region0 + 8 * static_cast<size_t>(d.cand_cap);
 }
 
+size_t score_lds_bytes(const Dims& d) { return static_cast<size_t>(d.G) * kNumBins * 4; }
+
 size_t finish_lds_bytes(const Dims& d) {
   return static_cast<size_t>(kBitmapLdsWords) * 4 * 2 + 16 * static_cast<size_t>(d.K) +
          8 * (static_cast<size_t>(d.n_chunks) + 1);
+}
+
+int score_grid(const Dims& d, int length) {
+  const long groups = static_cast<long>(d.B) * d.Hkv;
+  const long want = groups * ((length + kExactMinRows - 1) / kExactMinRows);
+  return static_cast<int>(std::max(1L, std::min<long>(kExactWGTarget, want)));
 }
 
 // ---------------------------------------------------------------------------
@@ -459,272 +507,6 @@ __global__ void k_reset(Dims d, Bufs b) {
   b.fifo[2 * bh + 1] = 0;
 }
 
-// ---------------------------------------------------------------------------
-// Per-head kernel: recall, path decision, and the reuse path.
-//
-// Recall (Eqs. 5-7): q_bar = fp32(x / ||x||) with fp64 sum of squares, sqrt
-// and divide; rho = fp64 dot of the fp32 q_bar values for every ring slot
-// (16 threads per slot, all slots loaded at once); R_t = the R largest rho
-// over the held entries (ties: older entry); rho_max. Path (Eq. 13): exact if
-// refresh, empty cache or rho_max < tau. Exact heads clear the histogram of
-// the exact-path kernels and stop here.
-//
-// Reuse path, same work group:
-//   union (Eqs. 8-9): retrieved supports and the window [max(0, L-W), L) set
-//     bits of an LDS bitmap over token positions (windows of 262144), read
-//     back in ascending order -> A_t in LDS, M_t;
-//   scores (Eq. 10): q . k_i for i in A_t straight from the KV cache, 16 lanes
-//     per key row, 16 rows in flight per thread, fp32 accumulation of exact
-//     bf16 products;
-//   rerank (Eq. 11): radix select of the K-th largest, kept in candidate
-//     (= ascending index) order, ties to the lower index;
-//   softmax-V (Eq. 12) and the cache update.
-//
-// LDS (dynamic): region0 = bitmap window (32 KiB), later the selected indices
-// and scores (K each); then A_t and its scores (cand_cap each).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uint16_t* q, long q_sb,
-                                                       long q_sh, const uint16_t* k, const uint16_t* v,
-                                                       float* out, int length, int t_dec, int mode,
-                                                       int stats_slot) {
-  const int bh = blockIdx.x;
-  const int bb = bh / d.Hq, h = bh % d.Hq, g = h / d.G;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ HeadShared sh;
-  extern __shared__ __align__(16) unsigned char dyn[];
-  const size_t region0 = (kBitmapLdsWords * 4 > 8 * d.K) ? kBitmapLdsWords * 4 : 8 * d.K;
-  uint32_t* bm = reinterpret_cast<uint32_t*>(dyn);
-  int32_t* s_sel = reinterpret_cast<int32_t*>(dyn);
-  float* s_selsc = reinterpret_cast<float*>(dyn + 4 * static_cast<size_t>(d.K));
-  int32_t* s_cand = reinterpret_cast<int32_t*>(dyn + region0);
-  float* s_sc = reinterpret_cast<float*>(dyn + region0 + 4 * static_cast<size_t>(d.cand_cap));
-
-  // ---- one round of loads: query, FIFO state, every ring slot's q_bar and support size ----
-  const int fifo_head = b.fifo[2 * bh];
-  const int count = b.fifo[2 * bh + 1];
-  const int part = tid & 15;
-  float4 ent[2][2];
-  if (mode == kModeDecode) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = min(i * (kHeadThreads / 16) + (tid >> 4), d.C - 1);
-      const float* e = b.cache_qbar + (static_cast<long>(bh) * d.C + c) * kHeadDim + 8 * part;
-      ent[i][0] = *reinterpret_cast<const float4*>(e);
-      ent[i][1] = *reinterpret_cast<const float4*>(e + 4);
-    }
-    const int len_c = b.cache_len[static_cast<long>(bh) * d.C + min(tid, d.C - 1)];
-    if (tid < d.C) sh.len[tid] = len_c;
-  }
-  if (wave == 0) {
-    const uint32_t w2 = *reinterpret_cast<const uint32_t*>(q + bb * q_sb + h * q_sh + 2 * lane);
-    const double x0 = bf16_lo(w2), x1 = bf16_hi(w2);
-    const double nrm = sqrt(wave_sum_f64(x0 * x0 + x1 * x1));
-    float qb0 = 0.f, qb1 = 0.f;
-    if (nrm > 0.0) {
-      qb0 = static_cast<float>(x0 / nrm);
-      qb1 = static_cast<float>(x1 / nrm);
-    }
-    sh.q[2 * lane] = static_cast<float>(x0);
-    sh.q[2 * lane + 1] = static_cast<float>(x1);
-    sh.qbar[2 * lane] = qb0;
-    sh.qbar[2 * lane + 1] = qb1;
-    *reinterpret_cast<float2*>(b.qbar + static_cast<long>(bh) * kHeadDim + 2 * lane) = make_float2(qb0, qb1);
-  }
-  __syncthreads();
-
-  bool exact = true, refresh = false;
-  double rho_max = -INFINITY;
-  int n_ret = 0;
-  if (mode == kModeDecode) {
-    refresh = d.Tr > 0 && (t_dec % d.Tr) == 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = i * (kHeadThreads / 16) + (tid >> 4);
-      const float* t = sh.qbar + 8 * part;
-      double s = 0.0;
-      s = fma(static_cast<double>(t[0]), static_cast<double>(ent[i][0].x), s);
-      s = fma(static_cast<double>(t[1]), static_cast<double>(ent[i][0].y), s);
-      s = fma(static_cast<double>(t[2]), static_cast<double>(ent[i][0].z), s);
-      s = fma(static_cast<double>(t[3]), static_cast<double>(ent[i][0].w), s);
-      s = fma(static_cast<double>(t[4]), static_cast<double>(ent[i][1].x), s);
-      s = fma(static_cast<double>(t[5]), static_cast<double>(ent[i][1].y), s);
-      s = fma(static_cast<double>(t[6]), static_cast<double>(ent[i][1].z), s);
-      s = fma(static_cast<double>(t[7]), static_cast<double>(ent[i][1].w), s);
-      s = row_sum(s);
-      if (part == 0 && c < d.C) sh.rho[c] = s;
-    }
-    __syncthreads();
-    // FIFO position p (0 = oldest) lives in ring slot (oldest + p) mod C.
-    // Wave 0, lane p holds position p; R rounds of a wave argmax pick the
-    // most similar entries, ties to the lowest position (the older entry).
-    const int oldest = (fifo_head - count + d.C) % d.C;
-    if (wave == 0) {
-      int slot = oldest + lane;
-      if (slot >= d.C) slot -= d.C;
-      double v = (lane < count) ? sh.rho[min(slot, d.C - 1)] : -INFINITY;
-      const int rounds = min(d.R, count);
-      for (int r = 0; r < rounds; ++r) {
-        const double m = wave_max_f64(v);
-        const uint64_t tie = __ballot(lane < count && v == m);
-        const int win = __ffsll(static_cast<unsigned long long>(tie)) - 1;
-        if (r == 0) sh.d0 = m;
-        if (lane == win) {
-          b.ret[bh * d.R + r] = lane;
-          b.retslot[bh * d.R + r] = slot;
-          sh.rslot[r] = slot;
-          v = -INFINITY;
-        }
-      }
-    }
-    n_ret = min(d.R, count);
-    __syncthreads();
-    if (count > 0) rho_max = sh.d0;
-    exact = refresh || count == 0 || rho_max < d.tau;
-  }
-  if (tid >= n_ret && tid < d.R) {
-    b.ret[bh * d.R + tid] = -1;
-    b.retslot[bh * d.R + tid] = -1;
-  }
-  if (tid == 0) {
-    b.path[bh] = exact ? 1 : 0;
-    b.rho[bh] = rho_max;
-    if (stats_slot >= 0) {
-      const long o = static_cast<long>(stats_slot) * d.B * d.Hq + bh;
-      b.st_path[o] = static_cast<uint8_t>((exact ? 1 : 0) | (refresh ? 2 : 0));
-      b.st_rho[o] = rho_max;
-      if (exact) b.st_m[o] = 0;
-    }
-  }
-  if (exact) {
-    if (tid == 0) b.m[bh] = 0;
-    uint4* hz = reinterpret_cast<uint4*>(b.hist + static_cast<long>(bh) * kHistSeg * kNumBins);
-    for (int i = tid; i < kHistSeg * kNumBins / 4; i += blockDim.x) hz[i] = make_uint4(0u, 0u, 0u, 0u);
-    return;
-  }
-
-  // ---- candidate union (Eqs. 8-9) ----
-  // Support entries below the window go through an LDS bitmap over token
-  // positions (windows of 262144) and come out ascending and de-duplicated;
-  // the window [max(0, L-W), L) holds the largest positions and is appended
-  // after them (support entries inside it are already covered).
-  const int wlo = max(0, length - d.W);
-  int M = 0;
-  for (int base = 0; base < wlo; base += kBitmapWords * 32) {
-    const int nbits = min(kBitmapWords * 32, wlo - base);
-    const int nwords = (nbits + 31) >> 5;
-    bitmap_clear(bm);
-    __syncthreads();
-    for (int j0 = 0; j0 < d.K; j0 += blockDim.x) {
-      const int j = j0 + tid;
-      for (int r0 = 0; r0 < n_ret; r0 += 4) {
-        int x[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          // clamped entry: always a valid address, discarded when out of range
-          const int r = min(r0 + u, n_ret - 1);
-          const int slot = sh.rslot[r];
-          x[u] = b.cache_supp[(static_cast<long>(bh) * d.C + slot) * d.K + min(j, d.K - 1)];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = r0 + u;
-          const int y = x[u] - base;
-          if (r < n_ret && j < sh.len[sh.rslot[min(r, n_ret - 1)]] && y >= 0 && y < nbits) bitmap_set(bm, y);
-        }
-      }
-    }
-    __syncthreads();
-    M += bitmap_emit(bm, nwords, base, s_cand + M, sh.tmp);
-    __syncthreads();
-  }
-  for (int x = wlo + tid; x < length; x += blockDim.x) s_cand[M + (x - wlo)] = x;
-  M += length - wlo;
-  __syncthreads();
-  for (int i = tid; i < M; i += blockDim.x) b.cand[static_cast<long>(bh) * d.cand_cap + i] = s_cand[i];
-  if (tid == 0) {
-    b.m[bh] = M;
-    if (stats_slot >= 0) b.st_m[static_cast<long>(stats_slot) * d.B * d.Hq + bh] = M;
-  }
-
-  // ---- candidate scores (Eq. 10) ----
-  const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
-  {
-    const int rg = tid >> 4, rpr = blockDim.x >> 4;
-    float qf[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[e] = sh.q[8 * part + e];
-    constexpr int U = 20;
-    for (int r0 = 0; r0 < M; r0 += rpr * U) {
-      uint4 kv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = min(r0 + u * rpr + rg, M - 1);
-        kv[u] = *reinterpret_cast<const uint4*>(kb + static_cast<long>(s_cand[i]) * kHeadDim + 8 * part);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = r0 + u * rpr + rg;
-        float s = qf[0] * bf16_lo(kv[u].x);
-        s = fmaf(qf[1], bf16_hi(kv[u].x), s);
-        s = fmaf(qf[2], bf16_lo(kv[u].y), s);
-        s = fmaf(qf[3], bf16_hi(kv[u].y), s);
-        s = fmaf(qf[4], bf16_lo(kv[u].z), s);
-        s = fmaf(qf[5], bf16_hi(kv[u].z), s);
-        s = fmaf(qf[6], bf16_lo(kv[u].w), s);
-        s = fmaf(qf[7], bf16_hi(kv[u].w), s);
-        s = row_sum(s);
-        if (part == 0 && i < M) s_sc[i] = s;
-      }
-    }
-  }
-  __syncthreads();
-  float mx = kNegInf;
-  for (int i = tid; i < M; i += blockDim.x) {
-    mx = fmaxf(mx, s_sc[i]);
-    b.cscore[static_cast<long>(bh) * d.cand_cap + i] = s_sc[i];
-  }
-  mx = block_max_f32(mx, reinterpret_cast<float*>(sh.tmp));
-
-  // ---- rerank (Eq. 11) ----
-  int n;
-  if (M <= d.K) {
-    for (int i = tid; i < M; i += blockDim.x) {
-      s_sel[i] = s_cand[i];
-      s_selsc[i] = s_sc[i];
-    }
-    n = M;
-    __syncthreads();
-  } else {
-    int need;
-    uint32_t mask;
-    const uint32_t T = radix_kth(s_sc, M, d.K, sh, &mask, &need);
-    n = select_in_order(s_cand, s_sc, M, T, mask, need, s_sel, s_selsc, sh);
-  }
-  for (int i = tid; i < n; i += blockDim.x) {
-    b.sel[static_cast<long>(bh) * d.K + i] = s_sel[i];
-    b.selsc[static_cast<long>(bh) * d.K + i] = s_selsc[i];
-  }
-  if (tid == 0) b.sellen[bh] = n;
-
-  // ---- softmax-V (Eq. 12) and cache update ----
-  const uint16_t* vb = v + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
-  attend(s_sel, s_selsc, n, mx, vb, out + static_cast<long>(bh) * kHeadDim, sh);
-  cache_push(d, b, bh, sh.qbar, s_sel, n);
-}
-
-// ---------------------------------------------------------------------------
-// Full-history scores (Eq. 4, unscaled) for every exact head, GQA-grouped:
-// the rows of one KV head are split evenly over `wpg` work groups; each
-// streams its rows exactly once and scores them for all query heads of the
-// group with MFMA 16x16x32 bf16 tiles (A = 16 key rows x 32 dims, B = 32 dims
-// x 16 query heads, fp32 accumulation). The loads of the next 256 rows are in
-// flight while the current ones are scored (two register buffers; rows past
-// the end are clamped to a valid row and masked). Scores go to the workspace
-// and into a per-head histogram of the top 10 bits of their ordered keys
-// (LDS, flushed with global atomics into one of kHistSeg copies chosen by the
-// work group); the collect kernel finds the Top-K boundary from it. Work
-// groups whose KV group has no exact head return at once.
-// ---------------------------------------------------------------------------
 namespace {
 constexpr int kQkUnroll = 4;  // 16-row tiles per wave per stage: 256 rows per work group
 
@@ -770,73 +552,487 @@ __device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4]
     }
   }
 }
+
 }  // namespace
 
-__global__ __launch_bounds__(256) void k_exact_qk(Dims d, Bufs b, const uint16_t* q, long q_sb, long q_sh,
-                                                  const uint16_t* k, int length, int wpg) {
-  const int bg = blockIdx.x / wpg, part = blockIdx.x % wpg;
-  const int bb = bg / d.Hkv, g = bg % d.Hkv;
+// ---------------------------------------------------------------------------
+// K1, one work group per query head: recall, path decision and the whole
+// reuse path.
+//
+// Recall (Eqs. 5-7): q_bar = fp32(x / ||x||) with fp64 sum of squares, sqrt
+// and divide; rho = fp64 dot of the fp32 q_bar values for every ring slot
+// (16 threads per slot, all slots loaded at once); R_t = the R largest rho
+// over the held entries, ranked by counting in parallel over all waves (ties:
+// older entry); rho_max. Path (Eq. 13): exact if refresh, empty cache or
+// rho_max < tau. Exact heads clear their score histogram and stop.
+//
+// Reuse heads, same work group:
+//   union (Eqs. 8-9): retrieved supports and the window [max(0, L-W), L) set
+//     bits of an LDS bitmap over token positions (windows of 262144), read
+//     back in ascending order -> A_t, M_t;
+//   scores (Eq. 10): q . k_i for i in A_t straight from the KV cache, 16 lanes
+//     per key row, 20 rows in flight per thread, fp32 accumulation of exact
+//     bf16 products;
+//   rerank (Eq. 11): radix select of the K-th largest, kept in candidate
+//     (= ascending index) order, ties to the lower index;
+//   softmax-V (Eq. 12) and the cache update.
+//
+// In kModeExact (no cache: the exact Top-K baseline and the cache
+// initialisation) every head is exact.
+//
+// LDS (dynamic): region0 = bitmap window (34 KiB), later S_hat and its scores
+// (K each); then A_t and its scores (cand_cap each).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uint16_t* q, long q_sb,
+                                                       long q_sh, const uint16_t* k, const uint16_t* v, float* out,
+                                                       int length, int t_dec, int mode, int stats_slot) {
+  const int bh = blockIdx.x;
+  const int bb = bh / d.Hq, h = bh % d.Hq, g = h / d.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ HeadShared sh;
+  __shared__ int s_rank[8][64];
+  extern __shared__ __align__(16) unsigned char dyn[];
+  const size_t region0 = (kBitmapLdsWords * 4 > 8 * d.K) ? kBitmapLdsWords * 4 : 8 * d.K;
+  uint32_t* bm = reinterpret_cast<uint32_t*>(dyn);
+  int32_t* s_sel = reinterpret_cast<int32_t*>(dyn);
+  float* s_selsc = reinterpret_cast<float*>(dyn + 4 * static_cast<size_t>(d.K));
+  int32_t* s_cand = reinterpret_cast<int32_t*>(dyn + region0);
+  float* s_sc = reinterpret_cast<float*>(dyn + region0 + 4 * static_cast<size_t>(d.cand_cap));
+
+  // ---- one round of loads: query, FIFO state, every ring slot's q_bar and support size ----
+  const int fifo_head = b.fifo[2 * bh];
+  const int count = b.fifo[2 * bh + 1];
+  const int part = tid & 15;
+  float4 ent[2][2];
+  if (mode == kModeDecode) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = min(i * (kHeadThreads / 16) + (tid >> 4), d.C - 1);
+      const float* e = b.cache_qbar + (static_cast<long>(bh) * d.C + c) * kHeadDim + 8 * part;
+      ent[i][0] = *reinterpret_cast<const float4*>(e);
+      ent[i][1] = *reinterpret_cast<const float4*>(e + 4);
+    }
+    const int len_c = b.cache_len[static_cast<long>(bh) * d.C + min(tid, d.C - 1)];
+    if (tid < d.C) sh.len[tid] = len_c;
+  }
+  if (wave == 0) {
+    const uint32_t w2 = *reinterpret_cast<const uint32_t*>(q + bb * q_sb + h * q_sh + 2 * lane);
+    const double x0 = bf16_lo(w2), x1 = bf16_hi(w2);
+    const double nrm = sqrt(wave_sum_f64(x0 * x0 + x1 * x1));
+    float qb0 = 0.f, qb1 = 0.f;
+    if (nrm > 0.0) {
+      qb0 = static_cast<float>(x0 / nrm);
+      qb1 = static_cast<float>(x1 / nrm);
+    }
+    sh.qbar[2 * lane] = qb0;
+    sh.qbar[2 * lane + 1] = qb1;
+    *reinterpret_cast<float2*>(b.qbar + static_cast<long>(bh) * kHeadDim + 2 * lane) = make_float2(qb0, qb1);
+  }
+  if (mode == kModeDecode) bitmap_clear(bm);  // first bitmap window, while the loads are in flight
+  __syncthreads();
+
+  bool exact = true, refresh = false;
+  double rho_max = -INFINITY;
+  int n_ret = 0;
+  const int oldest = (fifo_head - count + d.C) % d.C;
+  if (mode == kModeDecode) {
+    refresh = d.Tr > 0 && (t_dec % d.Tr) == 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = i * (kHeadThreads / 16) + (tid >> 4);
+      const float* t = sh.qbar + 8 * part;
+      double s = 0.0;
+      s = fma(static_cast<double>(t[0]), static_cast<double>(ent[i][0].x), s);
+      s = fma(static_cast<double>(t[1]), static_cast<double>(ent[i][0].y), s);
+      s = fma(static_cast<double>(t[2]), static_cast<double>(ent[i][0].z), s);
+      s = fma(static_cast<double>(t[3]), static_cast<double>(ent[i][0].w), s);
+      s = fma(static_cast<double>(t[4]), static_cast<double>(ent[i][1].x), s);
+      s = fma(static_cast<double>(t[5]), static_cast<double>(ent[i][1].y), s);
+      s = fma(static_cast<double>(t[6]), static_cast<double>(ent[i][1].z), s);
+      s = fma(static_cast<double>(t[7]), static_cast<double>(ent[i][1].w), s);
+      s = row_sum(s);
+      // FIFO position p (0 = oldest) lives in ring slot (oldest + p) mod C
+      if (part == 0 && c < d.C) {
+        int p = c - oldest;
+        if (p < 0) p += d.C;
+        sh.rho[p] = s;
+      }
+    }
+    __syncthreads();
+    // Rank of FIFO position p under (rho desc, position asc), counted in
+    // parallel: wave w compares every position with positions w, w+8, ...
+    {
+      const int p = lane;
+      const double v = (p < count) ? sh.rho[p] : -INFINITY;
+      int r = 0;
+      for (int p2 = wave; p2 < count; p2 += kHeadThreads / 64) {
+        const double u = sh.rho[p2];
+        r += (u > v) || (u == v && p2 < p);
+      }
+      s_rank[wave][p] = r;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int rank = 0;
+#pragma unroll
+      for (int w = 0; w < kHeadThreads / 64; ++w) rank += s_rank[w][lane];
+      if (lane < count && rank < d.R) {
+        int slot = oldest + lane;
+        if (slot >= d.C) slot -= d.C;
+        b.ret[bh * d.R + rank] = lane;
+        b.retslot[bh * d.R + rank] = slot;
+        sh.rslot[rank] = slot;
+        if (rank == 0) sh.d0 = sh.rho[lane];
+      }
+    }
+    n_ret = min(d.R, count);
+    __syncthreads();
+    if (count > 0) rho_max = sh.d0;
+    exact = refresh || count == 0 || rho_max < d.tau;
+  }
+  if (tid >= n_ret && tid < d.R) {
+    b.ret[bh * d.R + tid] = -1;
+    b.retslot[bh * d.R + tid] = -1;
+  }
+  if (tid == 0) {
+    b.path[bh] = exact ? 1 : 0;
+    b.rho[bh] = rho_max;
+    if (stats_slot >= 0) {
+      const long o = static_cast<long>(stats_slot) * d.B * d.Hq + bh;
+      b.st_path[o] = static_cast<uint8_t>((exact ? 1 : 0) | (refresh ? 2 : 0));
+      b.st_rho[o] = rho_max;
+      if (exact) b.st_m[o] = 0;
+    }
+  }
+  if (exact) {
+    // the full-history pass histograms this head's scores: clear its copies
+    if (tid == 0) b.m[bh] = 0;
+    uint4* hz = reinterpret_cast<uint4*>(b.hist + static_cast<long>(bh) * kHistSeg * kNumBins);
+    for (int i = tid; i < kHistSeg * kNumBins / 4; i += blockDim.x) hz[i] = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
+
+  // ---- candidate union (Eqs. 8-9) ----
+  // Support entries below the window go through the LDS bitmap and come out
+  // ascending and de-duplicated; the window [max(0, L-W), L) holds the
+  // largest positions and is appended after them (support entries inside it
+  // are already covered).
+  const int wlo = max(0, length - d.W);
+  int M = 0;
+  for (int base = 0; base < wlo; base += kBitmapWords * 32) {
+    const int nbits = min(kBitmapWords * 32, wlo - base);
+    const int nwords = (nbits + 31) >> 5;
+    if (base > 0) {
+      bitmap_clear(bm);
+      __syncthreads();
+    }
+    for (int j0 = 0; j0 < d.K; j0 += blockDim.x) {
+      const int j = j0 + tid;
+      for (int r0 = 0; r0 < n_ret; r0 += 4) {
+        int x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          // clamped entry: always a valid address, discarded when out of range
+          const int r = min(r0 + u, n_ret - 1);
+          x[u] = b.cache_supp[(static_cast<long>(bh) * d.C + sh.rslot[r]) * d.K + min(j, d.K - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = r0 + u;
+          const int y = x[u] - base;
+          if (r < n_ret && j < sh.len[sh.rslot[min(r, n_ret - 1)]] && y >= 0 && y < nbits) bitmap_set(bm, y);
+        }
+      }
+    }
+    __syncthreads();
+    if (nwords <= 8 * kHeadThreads) M += bitmap_emit<8>(bm, nwords, base, s_cand + M, sh.tmp);
+    else M += bitmap_emit<kSliceWords>(bm, nwords, base, s_cand + M, sh.tmp);
+    __syncthreads();
+  }
+  for (int x = wlo + tid; x < length; x += blockDim.x) s_cand[M + (x - wlo)] = x;
+  M += length - wlo;
+  __syncthreads();
+  for (int i = tid; i < M; i += blockDim.x) b.cand[static_cast<long>(bh) * d.cand_cap + i] = s_cand[i];
+  if (tid == 0) {
+    b.m[bh] = M;
+    if (stats_slot >= 0) b.st_m[static_cast<long>(stats_slot) * d.B * d.Hq + bh] = M;
+  }
+
+  // ---- candidate scores (Eq. 10) ----
+  const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
+  {
+    // 16 lanes per key row (16 bytes each), 20 rows in flight per thread,
+    // fp32 accumulation of exact bf16 products
+    const int part = tid & 15, rg = tid >> 4, rpr = blockDim.x >> 4;
+    const uint4 qw = *reinterpret_cast<const uint4*>(q + bb * q_sb + h * q_sh + 8 * part);
+    const float qf[8] = {bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y),
+                         bf16_lo(qw.z), bf16_hi(qw.z), bf16_lo(qw.w), bf16_hi(qw.w)};
+    constexpr int U = 20;
+    for (int r0 = 0; r0 < M; r0 += rpr * U) {
+      uint4 kv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = min(r0 + u * rpr + rg, M - 1);
+        kv[u] = *reinterpret_cast<const uint4*>(kb + static_cast<long>(s_cand[i]) * kHeadDim + 8 * part);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = r0 + u * rpr + rg;
+        float sc = qf[0] * bf16_lo(kv[u].x);
+        sc = fmaf(qf[1], bf16_hi(kv[u].x), sc);
+        sc = fmaf(qf[2], bf16_lo(kv[u].y), sc);
+        sc = fmaf(qf[3], bf16_hi(kv[u].y), sc);
+        sc = fmaf(qf[4], bf16_lo(kv[u].z), sc);
+        sc = fmaf(qf[5], bf16_hi(kv[u].z), sc);
+        sc = fmaf(qf[6], bf16_lo(kv[u].w), sc);
+        sc = fmaf(qf[7], bf16_hi(kv[u].w), sc);
+        sc = row_sum(sc);
+        if (part == 0 && i < M) s_sc[i] = sc;
+      }
+    }
+  }
+  __syncthreads();
+  float mx = kNegInf;
+  for (int i = tid; i < M; i += blockDim.x) mx = fmaxf(mx, s_sc[i]);
+  mx = block_max_f32(mx, reinterpret_cast<float*>(sh.tmp));
+
+  // ---- rerank (Eq. 11) ----
+  int n;
+  if (M <= d.K) {
+    for (int i = tid; i < M; i += blockDim.x) {
+      s_sel[i] = s_cand[i];
+      s_selsc[i] = s_sc[i];
+    }
+    n = M;
+    __syncthreads();
+  } else {
+    int need;
+    uint32_t mask;
+    const uint32_t T = radix_kth(s_sc, M, d.K, sh, &mask, &need);
+    n = select_in_order(s_cand, s_sc, M, T, mask, need, s_sel, s_selsc, sh);
+  }
+
+  // ---- reuse path: softmax-V (Eq. 12) and cache update ----
+  for (int i = tid; i < n; i += blockDim.x) {
+    b.sel[static_cast<long>(bh) * d.K + i] = s_sel[i];
+    b.selsc[static_cast<long>(bh) * d.K + i] = s_selsc[i];
+  }
+  if (tid == 0) b.sellen[bh] = n;
+  const uint16_t* vb = v + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
+  attend(s_sel, s_selsc, n, mx, vb, out + static_cast<long>(bh) * kHeadDim, nullptr, sh);
+  cache_push(d, b, bh, sh.qbar, s_sel, n);
+}
+
+// ---------------------------------------------------------------------------
+// K2, full-history scores (Eq. 4, unscaled) of every exact head, GQA-grouped.
+// The KV groups holding at least one exact head are listed in order; their
+// rows, concatenated, are split evenly over the whole grid (at 16-row
+// boundaries inside a group), so that one falling-back group uses every work
+// group. Each work group streams its rows exactly once and scores them for
+// all query heads of the group with MFMA 16x16x32 bf16 tiles (A = 16 key rows
+// x 32 dims, B = 32 dims x 16 query heads, fp32 accumulation). The loads of
+// the next 256 rows are in flight while the current ones are scored (two
+// register buffers; rows past the end are clamped to a valid row and
+// masked). Scores of exact heads go to the workspace and into a per-head
+// histogram of the top 10 bits of their ordered keys (LDS, flushed with
+// global atomics into one of kHistSeg copies chosen by the work group); the
+// Top-K kernel finds its boundary from it.
+// ---------------------------------------------------------------------------
+constexpr int kScoreThreads = 256;
+constexpr int kMaxExactGroups = 1024;  // KV groups (batch x KV heads) the row split can list
+
+__global__ __launch_bounds__(kScoreThreads) void k_score(Dims d, Bufs b, const uint16_t* q, long q_sb, long q_sh,
+                                                         const uint16_t* k, int length) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, kq = lane >> 4;
-  const int h = g * d.G + j;
-  const bool hv = (j < d.G) && b.path[bb * d.Hq + h];
-  if (__ballot(hv) == 0) return;  // same answer in every wave
-  const int row0 = static_cast<int>((static_cast<long>(part) * length / wpg) & ~15L);
-  const int rend = (part == wpg - 1) ? length : static_cast<int>((static_cast<long>(part + 1) * length / wpg) & ~15L);
-  if (row0 >= rend) return;
-  extern __shared__ uint32_t s_hist[];  // [G, kNumBins]
-  bf16x8 bq[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (hv) u = *reinterpret_cast<const uint4*>(q + bb * q_sb + h * q_sh + 8 * kq + 32 * s);
-    bq[s] = as_bf16x8(u);
+  const int NG = d.B * d.Hkv, nW = gridDim.x;
+  __shared__ int s_eg[kMaxExactGroups];
+  __shared__ int s_tmp[8];
+  extern __shared__ __align__(16) uint32_t s_hist[];  // [G, kNumBins]
+
+  // ordered list of the KV groups holding an exact head
+  int ne;
+  {
+    const int per = (NG + kScoreThreads - 1) / kScoreThreads;
+    const int g0 = min(static_cast<int>(threadIdx.x) * per, NG), g1 = min(g0 + per, NG);
+    int flags = 0, cnt = 0;
+    for (int bg = g0; bg < g1; ++bg) {
+      const int bb = bg / d.Hkv, g = bg % d.Hkv;
+      int any = 0;
+      for (int jj = 0; jj < d.G; ++jj) any |= b.path[bb * d.Hq + g * d.G + jj];
+      flags |= (any != 0) << (bg - g0);
+      cnt += any != 0;
+    }
+    int o = block_exclusive_scan(cnt, &ne, s_tmp);
+    for (int bg = g0; bg < g1; ++bg)
+      if (flags >> (bg - g0) & 1) s_eg[o++] = bg;
   }
-  const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
-  QkTiles ta, tb;
-  qk_load(ta, kb, row0, rend, wave, j, kq);
-  for (int i = threadIdx.x; i < d.G * kNumBins; i += blockDim.x) s_hist[i] = 0u;
   __syncthreads();
-  float* srow = b.score + static_cast<long>(bb * d.Hq + h) * d.score_stride;
-  uint32_t* hrow = s_hist + j * kNumBins;
+  if (ne == 0) return;
+
+  // this work group's share of the concatenated exact rows: split point w ->
+  // (list position e, row r), r rounded down to a 16-row boundary
+  const long T = static_cast<long>(ne) * length;
+  auto split = [&](int ww, int& e, int& r) {
+    const long x = static_cast<long>(ww) * T / nW;
+    e = static_cast<int>(x / length);
+    r = e < ne ? static_cast<int>(x % length) & ~15 : 0;
+  };
+  int e, r, e1, r1;
+  split(blockIdx.x, e, r);
+  split(blockIdx.x + 1, e1, r1);
   constexpr int kStage = 64 * kQkUnroll;  // rows per stage
-  for (int t0 = row0; t0 < rend; t0 += 2 * kStage) {
-    qk_load(tb, kb, t0 + kStage, rend, wave, j, kq);
-    qk_score(ta, bq, t0, rend, wave, kq, hv, srow, hrow);
-    if (t0 + kStage >= rend) break;
-    qk_load(ta, kb, t0 + 2 * kStage, rend, wave, j, kq);
-    qk_score(tb, bq, t0 + kStage, rend, wave, kq, hv, srow, hrow);
-  }
-  __syncthreads();
-  uint32_t* ghist = b.hist + static_cast<long>(bb * d.Hq + g * d.G) * kHistSeg * kNumBins +
-                    (blockIdx.x % kHistSeg) * kNumBins;
-  for (int i = threadIdx.x; i < d.G * kNumBins; i += blockDim.x) {
-    const uint32_t c = s_hist[i];
-    if (c) atomicAdd(&ghist[(i / kNumBins) * kHistSeg * kNumBins + (i % kNumBins)], c);
+  for (; e < e1 || (e == e1 && r < r1); ++e, r = 0) {
+    const int row0 = r, rend = e == e1 ? r1 : length;
+    if (row0 >= rend) continue;
+    const int bg = s_eg[e];
+    const int bb = bg / d.Hkv, g = bg % d.Hkv;
+    const int h = g * d.G + j;
+    const bool hv = (j < d.G) && b.path[bb * d.Hq + h];
+    bf16x8 bq[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (hv) u = *reinterpret_cast<const uint4*>(q + bb * q_sb + h * q_sh + 8 * kq + 32 * s);
+      bq[s] = as_bf16x8(u);
+    }
+    const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
+    QkTiles ta, tb;
+    qk_load(ta, kb, row0, rend, wave, j, kq);
+    __syncthreads();  // the previous segment's histogram flush is done
+    for (int i = threadIdx.x; i < d.G * kNumBins; i += blockDim.x) s_hist[i] = 0u;
+    __syncthreads();
+    float* srow = b.score + static_cast<long>(bb * d.Hq + h) * d.score_stride;
+    uint32_t* hrow = s_hist + j * kNumBins;
+    for (int t0 = row0; t0 < rend; t0 += 2 * kStage) {
+      qk_load(tb, kb, t0 + kStage, rend, wave, j, kq);
+      qk_score(ta, bq, t0, rend, wave, kq, hv, srow, hrow);
+      if (t0 + kStage >= rend) break;
+      qk_load(ta, kb, t0 + 2 * kStage, rend, wave, j, kq);
+      qk_score(tb, bq, t0 + kStage, rend, wave, kq, hv, srow, hrow);
+    }
+    __syncthreads();
+    uint32_t* ghist = b.hist + static_cast<long>(bb * d.Hq + g * d.G) * kHistSeg * kNumBins +
+                      (blockIdx.x % kHistSeg) * kNumBins;
+    for (int i = threadIdx.x; i < d.G * kNumBins; i += blockDim.x) {
+      const uint32_t c = s_hist[i];
+      if (c) atomicAdd(&ghist[(i / kNumBins) * kHistSeg * kNumBins + (i % kNumBins)], c);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Global Top-K (Eq. 1), step 1, for exact heads. Every work group takes a
-// chunk of 4096 scores of one head, finds the boundary bin from the
+// Composite keys of the exact Top-K: ordered score << 32 | ~index, so that a
+// larger key is a higher score, then a lower index; all keys are distinct.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t comp_key(float s, uint32_t idx) {
+  return (static_cast<uint64_t>(order_key(s)) << 32) | static_cast<uint64_t>(0xffffffffu - idx);
+}
+
+// The score half of a composite key back to the score's bits.
+__device__ __forceinline__ uint32_t key_score_bits(uint64_t u) {
+  const uint32_t ok = static_cast<uint32_t>(u >> 32);
+  return (ok & 0x80000000u) ? (ok & 0x7fffffffu) : ~ok;
+}
+
+// ---------------------------------------------------------------------------
+// Shared end of both exact finishes: the n chosen (index, score bits) pairs
+// are put in ascending index order by their rank in an LDS bitmap over the
+// positions (prefix popcount), giving S_t and its scores; the values are
+// aggregated (Eq. 12) and (q_bar_t, S_t) is pushed when `push`. Every thread
+// of the block must call it.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh, const uint2* chosen, int n,
+                                            int length, const uint16_t* v, float* out, int32_t* sel_out, int push,
+                                            HeadShared& sh, uint32_t* bm, int32_t* wpre, int32_t* s_sel,
+                                            float* s_selsc) {
+  const int tid = threadIdx.x;
+  const int bb = bh / d.Hq, g = (bh % d.Hq) / d.G;
+
+  // ascending order: rank of each chosen index = popcount of the set bits below it
+  int base_out = 0;
+  for (int base = 0; base < length; base += kBitmapWords * 32) {
+    const int nbits = min(kBitmapWords * 32, length - base);
+    bitmap_clear(bm);
+    __syncthreads();
+    for (int i = tid; i < n; i += blockDim.x) {
+      const int x = static_cast<int>(chosen[i].x) - base;
+      if (x >= 0 && x < nbits) bitmap_set(bm, x);
+    }
+    __syncthreads();
+    // word prefix counts: fixed 16-word slice per thread (same padded layout)
+    {
+      const int w0 = tid * kSliceWords;
+      const uint32_t* p = bm + tid * (kSliceWords + 1);
+      uint32_t w[kSliceWords];
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < kSliceWords; ++i) {
+        w[i] = p[i];
+        cnt += __popc(w[i]);
+      }
+      int wtot;
+      int run = block_exclusive_scan(cnt, &wtot, sh.tmp);
+      int* q = wpre + tid * (kSliceWords + 1);
+#pragma unroll
+      for (int i = 0; i < kSliceWords; ++i) {
+        q[i] = run;
+        run += __popc(w[i]);
+      }
+      (void)w0;
+      sh.i2 = wtot;  // read after the barrier below
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += blockDim.x) {
+      const uint2 e = chosen[i];
+      const int x = static_cast<int>(e.x) - base;
+      if (x >= 0 && x < nbits) {
+        const int w = x >> 5;
+        const int pos = base_out + wpre[bm_at(w)] + __popc(bm[bm_at(w)] & ((1u << (x & 31)) - 1u));
+        s_sel[pos] = static_cast<int32_t>(e.x);
+        s_selsc[pos] = __uint_as_float(e.y);
+      }
+    }
+    base_out += sh.i2;
+    __syncthreads();
+  }
+  float mx = kNegInf;
+  for (int i = tid; i < n; i += blockDim.x) {
+    mx = fmaxf(mx, s_selsc[i]);
+    b.sel[static_cast<long>(bh) * d.K + i] = s_sel[i];
+    b.selsc[static_cast<long>(bh) * d.K + i] = s_selsc[i];
+  }
+  mx = block_max_f32(mx, reinterpret_cast<float*>(sh.tmp));
+  if (tid == 0) b.sellen[bh] = n;
+  if (sel_out != nullptr)
+    for (int i = tid; i < d.K; i += blockDim.x) sel_out[static_cast<long>(bh) * d.K + i] = i < n ? s_sel[i] : -1;
+  if (v != nullptr && out != nullptr) {
+    const uint16_t* vb = v + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
+    attend(s_sel, s_selsc, n, mx, vb, out + static_cast<long>(bh) * kHeadDim, nullptr, sh);
+  }
+  if (push) {
+    for (int t = tid; t < kHeadDim; t += blockDim.x) sh.qbar[t] = b.qbar[static_cast<long>(bh) * kHeadDim + t];
+    __syncthreads();
+    cache_push(d, b, bh, sh.qbar, s_sel, n);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K3, global Top-K (Eq. 1), step 1, for exact heads. Every work group takes a
+// chunk of kCollectChunk scores of one head, finds the boundary bin from the
 // histogram (the bin holding the K-th largest score) and classifies its
 // scores: entries in higher bins ("above", fewer than K in all) and entries
 // in the boundary bin are written, as (index, score bits), to the chunk's own
 // region of the hit buffer (boundary from the front, above from the back) in
 // position order, with the two counts. No global atomics.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_collect(Dims d, Bufs b, int length) {
-  const int bh = blockIdx.x;
-  if (!b.path[bh]) return;
-  const int chunk = blockIdx.y;
+__device__ __forceinline__ void collect_chunk(const Dims& d, const Bufs& b, int bh, int chunk, int length, int* tmp,
+                                              int* s_b1) {
   const int c0 = chunk * kCollectChunk;
-  if (c0 >= length) return;
   const int clen = min(kCollectChunk, length - c0);
-  __shared__ int tmp[8];
-  __shared__ int s_b1;
   const int keff = min(d.K, length);
   const float* srow = b.score + static_cast<long>(bh) * d.score_stride;
-  constexpr int kPerThread = kCollectChunk / 256;
+  constexpr int kPerThread = kCollectChunk / kHeadThreads;
   const int i0 = c0 + threadIdx.x * kPerThread;
   float v[kPerThread];
   if (i0 + kPerThread <= length) {
@@ -852,38 +1048,36 @@ __global__ __launch_bounds__(256) void k_collect(Dims d, Bufs b, int length) {
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u) v[u] = (i0 + u < length) ? srow[i0 + u] : 0.f;
   }
-  // this thread's 4 bins, in descending order, summed over the histogram copies
+  // this thread's 2 bins, in descending order, summed over the histogram copies
   const uint32_t* hist = b.hist + static_cast<long>(bh) * kHistSeg * kNumBins;
-  constexpr int kPer = kNumBins / 256;
-  static_assert(kPer == 4, "4 bins per thread");
-  uint4 hs[kHistSeg];
+  constexpr int kPer = kNumBins / kHeadThreads;
+  static_assert(kPer == 2, "2 bins per thread");
+  uint2 hs[kHistSeg];
 #pragma unroll
   for (int sgm = 0; sgm < kHistSeg; ++sgm)
-    hs[sgm] = *reinterpret_cast<const uint4*>(hist + sgm * kNumBins + kNumBins - 4 * (threadIdx.x + 1));
-  int c[kPer] = {0, 0, 0, 0};
+    hs[sgm] = *reinterpret_cast<const uint2*>(hist + sgm * kNumBins + kNumBins - kPer * (threadIdx.x + 1));
+  int c[kPer] = {0, 0};
 #pragma unroll
   for (int sgm = 0; sgm < kHistSeg; ++sgm) {
-    c[0] += hs[sgm].w;
-    c[1] += hs[sgm].z;
-    c[2] += hs[sgm].y;
-    c[3] += hs[sgm].x;
+    c[0] += hs[sgm].y;
+    c[1] += hs[sgm].x;
   }
-  const int csum = c[0] + c[1] + c[2] + c[3];
-  if (threadIdx.x == 0) s_b1 = 0;
+  const int csum = c[0] + c[1];
+  if (threadIdx.x == 0) *s_b1 = 0;
   int tot;
   const int ex = block_exclusive_scan(csum, &tot, tmp);
   if (ex < keff && ex + csum >= keff) {
     int run = ex;
     for (int i = 0; i < kPer; ++i) {
       if (run + c[i] >= keff) {
-        s_b1 = kNumBins - 1 - (kPer * threadIdx.x + i);
+        *s_b1 = kNumBins - 1 - (kPer * threadIdx.x + i);
         break;
       }
       run += c[i];
     }
   }
   __syncthreads();
-  const uint32_t b1 = static_cast<uint32_t>(s_b1);
+  const uint32_t b1 = static_cast<uint32_t>(*s_b1);
   int nu = 0, nbd = 0;
 #pragma unroll
   for (int u = 0; u < kPerThread; ++u) {
@@ -907,25 +1101,28 @@ __global__ __launch_bounds__(256) void k_collect(Dims d, Bufs b, int length) {
   if (threadIdx.x == 0) b.ccnt[static_cast<long>(bh) * d.n_chunks + chunk] = make_int2(tot >> 16, tot & 0xffff);
 }
 
-// ---------------------------------------------------------------------------
-// Global Top-K, step 2, for exact heads, then softmax-V and the cache update.
-// The chunks' "above" entries (all selected) and boundary entries are
-// gathered with their scores into LDS. Of the boundary entries the `need`
-// best under (score desc, index asc) are kept: a radix select over 64-bit
-// keys (ordered score << 32 | ~index) with per-wave histograms, in LDS when
-// the boundary holds at most 4096 entries, else read from the hit buffer.
-// The K selected indices are put in ascending order by their rank in an LDS
-// bitmap (prefix popcount), giving S_t and its scores; the values are
-// aggregated (Eq. 12) and (q_bar_t, S_t) is pushed. One work group per head.
-//
-// LDS (dynamic): A = boundary keys, later word prefix counts (32 KiB);
-// B = bitmap window (32 KiB); C = selected (index, score) pairs, unordered
-// (K); D = S_t indices and scores, ordered (K each); E = chunk offsets.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t comp_key(float s, uint32_t idx) {
-  return (static_cast<uint64_t>(order_key(s)) << 32) | static_cast<uint64_t>(0xffffffffu - idx);
+// One work group per (head, chunk); reuse heads return at once.
+__global__ __launch_bounds__(kHeadThreads) void k_collect(Dims d, Bufs b, int length, int nch) {
+  __shared__ int tmp[8];
+  __shared__ int s_b1;
+  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;
+  if (!b.path[bh]) return;
+  collect_chunk(d, b, bh, chunk, length, tmp, &s_b1);
 }
 
+// ---------------------------------------------------------------------------
+// K4, global Top-K, step 2, for exact heads, then softmax-V and the cache
+// update. The chunks' "above" entries (all selected) and boundary entries are
+// gathered with their scores into LDS. Of the boundary entries the `need`
+// best under (score desc, index asc) are kept: a radix select over the
+// composite keys with per-wave histograms, in LDS when the boundary holds at
+// most kBoundaryLds entries, else read from the hit buffer. One work group
+// per head.
+//
+// LDS (dynamic): A = boundary keys, later word prefix counts (34 KiB);
+// B = bitmap window (34 KiB); C = selected (index, score) pairs, unordered
+// (K); D = S_t indices and scores, ordered (K each); E = chunk offsets.
+// ---------------------------------------------------------------------------
 // Boundary entry g of a head: chunk found by binary search over the offsets.
 __device__ __forceinline__ uint2 boundary_entry(const uint2* hits_row, const int* boff, int nch, int g) {
   int lo = 0, hi = nch;  // boff[lo] <= g < boff[hi]
@@ -1047,7 +1244,8 @@ __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const u
     ncand = sh.i2;
   }
   // boundary entries whose masked key is >= prefix are exactly the kept ones
-  for (int i = tid; i < nb; i += blockDim.x) {
+  for (int i0 = 0; i0 < nb; i0 += blockDim.x) {
+    const int i = min(i0 + tid, nb - 1);  // clamped: a repeated entry is never taken twice (t below)
     uint2 e;
     uint64_t u;
     if (in_lds) {
@@ -1057,86 +1255,16 @@ __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const u
       e = boundary_entry(hits_row, boff, nch, i);
       u = comp_key(__uint_as_float(e.y), e.x);
     }
-    if ((u & mask) >= prefix) {
-      const int o = atomicAdd(&sh.i3, 1);
-      if (na + o < d.K) {
-        // the score half of the key holds the ordered score; map it back
-        const uint32_t ok = static_cast<uint32_t>(u >> 32);
-        const uint32_t bits = (ok & 0x80000000u) ? (ok & 0x7fffffffu) : ~ok;
-        chosen[na + o] = make_uint2(e.x, bits);
-      }
-    }
+    const bool t = i0 + tid < nb && (u & mask) >= prefix;
+    const int o = wave_slot(t, &sh.i3);
+    if (t && na + o < d.K) chosen[na + o] = make_uint2(e.x, key_score_bits(u));
   }
   __syncthreads();
   const int n = min(na + sh.i3, keff);
-
-  // ascending order: rank of each chosen index = popcount of the set bits below it
-  int base_out = 0;
-  for (int base = 0; base < length; base += kBitmapWords * 32) {
-    const int nbits = min(kBitmapWords * 32, length - base);
-    const int nwords = (nbits + 31) >> 5;
-    bitmap_clear(bm);
-    __syncthreads();
-    for (int i = tid; i < n; i += blockDim.x) {
-      const int x = static_cast<int>(chosen[i].x) - base;
-      if (x >= 0 && x < nbits) bitmap_set(bm, x);
-    }
-    __syncthreads();
-    // word prefix counts: fixed 16-word slice per thread (same padded layout)
-    {
-      const int w0 = tid * kSliceWords;
-      const uint32_t* p = bm + tid * (kSliceWords + 1);
-      uint32_t w[kSliceWords];
-      int cnt = 0;
-#pragma unroll
-      for (int i = 0; i < kSliceWords; ++i) {
-        w[i] = p[i];
-        cnt += __popc(w[i]);
-      }
-      int wtot;
-      int run = block_exclusive_scan(cnt, &wtot, sh.tmp);
-      int* q = wpre + tid * (kSliceWords + 1);
-#pragma unroll
-      for (int i = 0; i < kSliceWords; ++i) {
-        q[i] = run;
-        run += __popc(w[i]);
-      }
-      (void)w0;
-      sh.i2 = wtot;  // read after the barrier below
-    }
-    __syncthreads();
-    for (int i = tid; i < n; i += blockDim.x) {
-      const uint2 e = chosen[i];
-      const int x = static_cast<int>(e.x) - base;
-      if (x >= 0 && x < nbits) {
-        const int w = x >> 5;
-        const int pos = base_out + wpre[bm_at(w)] + __popc(bm[bm_at(w)] & ((1u << (x & 31)) - 1u));
-        s_sel[pos] = static_cast<int32_t>(e.x);
-        s_selsc[pos] = __uint_as_float(e.y);
-      }
-    }
-    base_out += sh.i2;
-    __syncthreads();
-  }
-  float mx = kNegInf;
-  for (int i = tid; i < n; i += blockDim.x) {
-    mx = fmaxf(mx, s_selsc[i]);
-    b.sel[static_cast<long>(bh) * d.K + i] = s_sel[i];
-    b.selsc[static_cast<long>(bh) * d.K + i] = s_selsc[i];
-  }
-  mx = block_max_f32(mx, reinterpret_cast<float*>(sh.tmp));
-  if (tid == 0) b.sellen[bh] = n;
-  if (sel_out != nullptr)
-    for (int i = tid; i < d.K; i += blockDim.x) sel_out[static_cast<long>(bh) * d.K + i] = i < n ? s_sel[i] : -1;
-  if (v != nullptr && out != nullptr) {
-    const uint16_t* vb = v + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
-    attend(s_sel, s_selsc, n, mx, vb, out + static_cast<long>(bh) * kHeadDim, sh);
-  }
-  if (push) {
-    for (int t = tid; t < kHeadDim; t += blockDim.x) sh.qbar[t] = b.qbar[static_cast<long>(bh) * kHeadDim + t];
-    __syncthreads();
-    cache_push(d, b, bh, sh.qbar, s_sel, n);
-  }
+  finish_tail(d, b, bh, chosen, n, length, v, out, sel_out, push, sh, bm, wpre, s_sel, s_selsc);
+  (void)h;
+  (void)bb;
+  (void)g;
 }
 
 // ---------------------------------------------------------------------------
@@ -1147,13 +1275,16 @@ hipError_t configure_kernels(const Dims& d) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(head_lds_bytes(d)));
   if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(score_lds_bytes(d)));
+  if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_finish), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(finish_lds_bytes(d)));
   return e;
 }
 
 const char* kernel_name(int id) {
-  static const char* names[kNumKernels] = {"k_head", "k_exact_qk", "k_collect", "k_finish", "k_reset"};
+  static const char* names[kNumKernels] = {"k_head", "k_score", "k_collect", "k_finish", "k_reset"};
   return (id >= 0 && id < kNumKernels) ? names[id] : "";
 }
 
@@ -1163,27 +1294,24 @@ hipError_t launch_reset(const Dims& d, const Bufs& b, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_head(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
-                       const uint16_t* k, const uint16_t* v, float* out, int length, int t_dec, int mode,
-                       int stats_slot, hipStream_t s) {
-  hipLaunchKernelGGL(k_head, dim3(d.B * d.Hq), dim3(kHeadThreads), head_lds_bytes(d), s, d, b, q, q_sb, q_sh,
-                     k, v, out, length, t_dec, mode, stats_slot);
+hipError_t launch_head(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh, const uint16_t* k,
+                       const uint16_t* v, float* out, int length, int t_dec, int mode, int stats_slot,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(k_head, dim3(d.B * d.Hq), dim3(kHeadThreads), head_lds_bytes(d), s, d, b, q, q_sb, q_sh, k, v,
+                     out, length, t_dec, mode, stats_slot);
   return hipGetLastError();
 }
 
-hipError_t launch_exact_qk(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
-                           const uint16_t* k, int length, hipStream_t s) {
-  const int groups = d.B * d.Hkv;
-  int wpg = (kExactWGTarget + groups - 1) / groups;
-  wpg = std::max(1, std::min(wpg, (length + kExactMinRows - 1) / kExactMinRows));
-  hipLaunchKernelGGL(k_exact_qk, dim3(groups * wpg), dim3(256), d.G * kNumBins * sizeof(uint32_t), s, d, b,
-                     q, q_sb, q_sh, k, length, wpg);
+hipError_t launch_score(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
+                        const uint16_t* k, int length, hipStream_t s) {
+  hipLaunchKernelGGL(k_score, dim3(score_grid(d, length)), dim3(kScoreThreads), score_lds_bytes(d), s, d, b, q,
+                     q_sb, q_sh, k, length);
   return hipGetLastError();
 }
 
 hipError_t launch_collect(const Dims& d, const Bufs& b, int length, hipStream_t s) {
-  const int ny = (length + kCollectChunk - 1) / kCollectChunk;
-  hipLaunchKernelGGL(k_collect, dim3(d.B * d.Hq, ny), dim3(256), 0, s, d, b, length);
+  const int nch = (length + kCollectChunk - 1) / kCollectChunk;
+  hipLaunchKernelGGL(k_collect, dim3(d.B * d.Hq * nch), dim3(kHeadThreads), 0, s, d, b, length, nch);
   return hipGetLastError();
 }
 
