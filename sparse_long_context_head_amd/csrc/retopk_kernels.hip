@@ -37,6 +37,7 @@ namespace retopk {
 namespace {
 
 constexpr float kNegInf = -INFINITY;
+constexpr float kPosInf = INFINITY;
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
 
 // Order-preserving map of a float32 to uint32 (larger float, larger key).
@@ -49,6 +50,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// acc + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs (v_dot2, fp32 accumulation).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+}
 
 // ---- cross-lane primitives on DPP row operations (no LDS traffic) ----
 // A DPP "row" is 16 consecutive lanes. Lanes whose source is out of range
@@ -181,6 +188,26 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* tmp)
   return before + incl - v;
 }
 
+// Block-wide minimum and maximum of one float per thread (tmp: 2 * waves floats).
+__device__ __forceinline__ void block_minmax_f32(float lo, float hi, float* tmp, float* mn, float* mx) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  hi = wave_max_f32(hi);
+  lo = -wave_max_f32(-lo);
+  if (lane == 0) {
+    tmp[2 * wave] = lo;
+    tmp[2 * wave + 1] = hi;
+  }
+  __syncthreads();
+  float a = kPosInf, b = kNegInf;
+  for (int w = 0; w < nw; ++w) {
+    a = fminf(a, tmp[2 * w]);
+    b = fmaxf(b, tmp[2 * w + 1]);
+  }
+  __syncthreads();
+  *mn = a;
+  *mx = b;
+}
+
 __device__ __forceinline__ float block_max_f32(float v, float* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   v = wave_max_f32(v);
@@ -217,23 +244,24 @@ __device__ __forceinline__ void bitmap_clear_n(uint32_t* bm, int nwords) {
 
 // Emit, in ascending order, the positions base + bit of every set bit of an
 // LDS bitmap window of `nwords` words to out[0 ..). Returns the number emitted
-// (the same value in every thread). Each thread takes Per consecutive words
-// (Per = 8 covers windows of up to 4096 words with every thread busy).
-// Every thread of the block must call it.
-template <int Per>
+// (the same value in every thread). The words are split evenly over the
+// block: thread t takes words [t*per, (t+1)*per) with per = ceil(nwords /
+// blockDim) <= kSliceWords. Every thread of the block must call it.
 __device__ __forceinline__ int bitmap_emit(const uint32_t* bm, int nwords, int base, int32_t* out, int* tmp) {
-  uint32_t w[Per];
-  const int w0 = threadIdx.x * Per;
+  const int per = (nwords + blockDim.x - 1) / blockDim.x;
+  uint32_t w[kSliceWords];
+  const int w0 = threadIdx.x * per;
   int cnt = 0;
 #pragma unroll
-  for (int i = 0; i < Per; ++i) {
-    w[i] = (w0 + i < nwords) ? bm[bm_at(w0 + i)] : 0u;
+  for (int i = 0; i < kSliceWords; ++i) {
+    w[i] = (i < per && w0 + i < nwords) ? bm[bm_at(w0 + i)] : 0u;
     cnt += __popc(w[i]);
   }
   int total;
   int off = block_exclusive_scan(cnt, &total, tmp);
 #pragma unroll
-  for (int i = 0; i < Per; ++i) {
+  for (int i = 0; i < kSliceWords; ++i) {
+    if (i >= per) break;  // uniform
     uint32_t bits = w[i];
     while (bits) {
       const int b = __ffs(bits) - 1;
@@ -242,6 +270,14 @@ __device__ __forceinline__ int bitmap_emit(const uint32_t* bm, int nwords, int b
     }
   }
   return total;
+}
+
+// First dynamic-LDS region of the head kernel: the bitmap window, later S_hat
+// with its scores (8K bytes) and one flag byte per candidate.
+__host__ __device__ inline size_t head_region0(const Dims& d) {
+  const size_t sel = 8 * static_cast<size_t>(d.K) + static_cast<size_t>(d.cand_cap);
+  const size_t bm = static_cast<size_t>(kBitmapLdsWords) * 4;
+  return ((bm > sel ? bm : sel) + 15) / 16 * 16;
 }
 
 // Shared scratch of the per-head kernels (static LDS).
@@ -253,7 +289,7 @@ struct HeadShared {
   int rslot[64];                       // ring slots of the retrieved entries, best first
   __align__(16) int whist[kHeadThreads / 64][256];   // one radix histogram per wave
   int tmp[16];
-  float red[kHeadThreads / 64][kHeadDim + 4];
+  __align__(16) float red[kHeadThreads / 16][kHeadDim + 4];  // one row per 16-lane row group
   int i0, i1, i2, i3;
   double d0;
 };
@@ -386,18 +422,136 @@ __device__ __forceinline__ int select_in_order(const int32_t* idx, const float* 
   return (tot & 0xffff) + min(tot >> 16, need);
 }
 
+// Rerank (Eq. 11) of M > K candidates in LDS, first pass on scores binned
+// linearly between their minimum mn and maximum mx (mx > mn): the bin of a
+// score is monotone in the score, so every bin above the one holding the
+// K-th largest is kept whole. When only some entries of that boundary bin are
+// kept (at most 64 of them), one wave ranks them exactly by (score desc,
+// index asc) and flags the kept ones. The kept entries are written in
+// candidate order (ascending index) to out_idx / out_sc; returns K, or -1
+// (nothing written) when the boundary bin is too crowded, for the caller's
+// order-key radix select. flag: M bytes of LDS scratch. Every thread must
+// call it.
+__device__ __forceinline__ int rerank_linear(const int32_t* idx, const float* sc, int M, int K, float mn, float mx,
+                                             int32_t* out_idx, float* out_sc, uint8_t* flag, HeadShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float scale = 2048.f / (mx - mn);
+  auto bin_of = [&](float v) { return min(2047, static_cast<int>((v - mn) * scale)); };
+  int* bins = &sh.whist[0][0];  // 2048 bins
+  reinterpret_cast<int4*>(bins)[tid] = make_int4(0, 0, 0, 0);
+  if (tid == 0) sh.i3 = 0;
+  __syncthreads();
+  for (int i = tid; i < M; i += blockDim.x) atomicAdd(&bins[bin_of(sc[i])], 1);
+  __syncthreads();
+  {
+    const int4 h = reinterpret_cast<const int4*>(bins)[511 - tid];  // bins 2047-4t .. 2044-4t
+    const int c[4] = {h.w, h.z, h.y, h.x};
+    const int s4 = c[0] + c[1] + c[2] + c[3];
+    int tot;
+    int run = block_exclusive_scan(s4, &tot, sh.tmp);
+    if (run < K && run + s4 >= K) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (run + c[j] >= K) {
+          sh.i0 = 2047 - 4 * tid - j;
+          sh.i1 = K - run;
+          sh.i2 = c[j];
+          break;
+        }
+        run += c[j];
+      }
+    }
+    __syncthreads();
+  }
+  const int b1 = sh.i0, need = sh.i1, cnt = sh.i2;
+  if (need < cnt) {
+    if (cnt > 64) return -1;  // uniform
+    // the boundary bin's entries, listed by one wave-aggregated pass
+    for (int i0 = 0; i0 < M; i0 += blockDim.x) {
+      const int i = i0 + tid;
+      const bool in = i < M && bin_of(sc[min(i, M - 1)]) == b1;
+      const int o = wave_slot(in, &sh.i3);
+      if (in) sh.rslot[o] = i;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int p = sh.rslot[min(lane, cnt - 1)];
+      const float v = sc[p];
+      const int x = idx[p];
+      int rank = 0;
+      for (int j = 0; j < cnt; ++j) {
+        const float u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+        const int y = __builtin_amdgcn_readlane(x, j);
+        rank += (u > v) || (u == v && y < x);
+      }
+      if (lane < cnt) flag[p] = rank < need ? 1 : 0;
+    }
+    __syncthreads();
+  }
+  // kept: bin > b1, or bin == b1 and (all of the bin kept, or flagged)
+  const int per = (M + blockDim.x - 1) / blockDim.x;
+  const int i0 = tid * per, i1 = min(i0 + per, M);
+  auto kept = [&](int i) {
+    const int bn = bin_of(sc[i]);
+    return bn > b1 || (bn == b1 && (need == cnt || flag[i] != 0));
+  };
+  int k = 0;
+  for (int i = i0; i < i1; ++i) k += kept(i);
+  int tot;
+  int o = block_exclusive_scan(k, &tot, sh.tmp);
+  for (int i = i0; i < i1; ++i) {
+    if (kept(i)) {
+      out_idx[o] = idx[i];
+      out_sc[o] = sc[i];
+      ++o;
+    }
+  }
+  __syncthreads();
+  return tot;
+}
+
+// End of softmax-V: every thread holds the weighted sums of 8 value dims
+// (lane & 15 picks the dims) over its rows and, in lane & 15 == 0, the sum of
+// their weights. Each 16-lane row group stores one row of sh.red; then 128
+// threads add the rows of one dim each (conflict-free LDS columns) and write
+// out (see attend). Every thread of the block must call it.
+__device__ __forceinline__ void attend_reduce(float (&acc)[8], float z, float* out, float* out_z, HeadShared& sh) {
+  const int sub = threadIdx.x & 15, rg = threadIdx.x >> 4, nrg = blockDim.x >> 4;
+  float4* r = reinterpret_cast<float4*>(&sh.red[rg][8 * sub]);
+  r[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  r[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if (sub == 0) sh.red[rg][kHeadDim] = z;
+  __syncthreads();
+  if (out != nullptr && threadIdx.x < kHeadDim) {
+    float a = 0.f, zz = 0.f;
+    for (int g2 = 0; g2 < nrg; ++g2) {
+      a += sh.red[g2][threadIdx.x];
+      zz += sh.red[g2][kHeadDim];
+    }
+    if (out_z == nullptr) {
+      out[threadIdx.x] = a / zz;
+    } else {
+      out[threadIdx.x] = a;
+      if (threadIdx.x == 0) *out_z = zz;
+    }
+  }
+  __syncthreads();
+}
+
 // Sparse softmax-V (Eq. 12) over n selected rows (indices and unscaled
-// scores in LDS; mx = the maximum over the whole support): 16 lanes per
-// value row (16 bytes each), 16 row loads in flight per thread. With out_z
-// NULL it writes the normalised output out[0 .. 127]; otherwise the
-// unnormalised sums sum_i exp((s_i - mx)/sqrt(d)) v_i to out[0 .. 127] and
-// sum_i exp((s_i - mx)/sqrt(d)) to *out_z, so that disjoint slices of one
-// support can be merged by adding them. Nothing is written when out is NULL.
-// Every thread of the block must call it.
-__device__ __forceinline__ void attend(const int32_t* sel, const float* sc, int n, float mx, const uint16_t* vb, float* out,
+// scores in LDS; mx = the maximum over the whole support). The scores are
+// first replaced in place by their weights exp((s - mx) / sqrt(d)), one
+// thread per row; then 16 lanes per value row (16 bytes each), 16 row loads
+// in flight per thread. With out_z NULL it writes the normalised output
+// out[0 .. 127]; otherwise the unnormalised sums to out[0 .. 127] and the sum
+// of the weights to *out_z, so that disjoint slices of one support can be
+// merged by adding them. Nothing is written when out is NULL. Every thread of
+// the block must call it.
+__device__ __forceinline__ void attend(const int32_t* sel, float* sc, int n, float mx, const uint16_t* vb, float* out,
                                        float* out_z, HeadShared& sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int sub = threadIdx.x & 15, rg = threadIdx.x >> 4, rpr = blockDim.x >> 4;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) sc[i] = expf((sc[i] - mx) * kInvSqrtD);
+  __syncthreads();
   constexpr int U = 16;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float z = 0.f;
@@ -413,7 +567,7 @@ __device__ __forceinline__ void attend(const int32_t* sel, const float* sc, int 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = r0 + u * rpr + rg;
-      p[u] = (i < n) ? expf((sc[min(i, n - 1)] - mx) * kInvSqrtD) : 0.f;
+      p[u] = (i < n) ? sc[min(i, n - 1)] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -428,33 +582,7 @@ __device__ __forceinline__ void attend(const int32_t* sel, const float* sc, int 
       if (sub == 0) z += p[u];
     }
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    acc[e] += __shfl_xor(acc[e], 16);
-    acc[e] += __shfl_xor(acc[e], 32);
-  }
-  z += __shfl_xor(z, 16);
-  z += __shfl_xor(z, 32);
-  if (lane < 16) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sh.red[wave][8 * sub + e] = acc[e];
-    if (lane == 0) sh.red[wave][kHeadDim] = z;
-  }
-  __syncthreads();
-  if (out != nullptr && threadIdx.x < kHeadDim) {
-    float a = 0.f, zz = 0.f;
-    for (int w = 0; w < nw; ++w) {
-      a += sh.red[w][threadIdx.x];
-      zz += sh.red[w][kHeadDim];
-    }
-    if (out_z == nullptr) {
-      out[threadIdx.x] = a / zz;
-    } else {
-      out[threadIdx.x] = a;
-      if (threadIdx.x == 0) *out_z = zz;
-    }
-  }
-  __syncthreads();
+  attend_reduce(acc, z, out, out_z, sh);
 }
 
 // Push (q_bar_t, S_hat_t) into the head's FIFO (Query-support cache
@@ -480,8 +608,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 }  // namespace
 
 size_t head_lds_bytes(const Dims& d) {
-  const size_t region0 = std::max<size_t>(kBitmapLdsWords * 4, 8 * static_cast<size_t>(d.K));
-  return region0 + 8 * static_cast<size_t>(d.cand_cap);
+  return head_region0(d) + 8 * static_cast<size_t>(d.cand_cap);
 }
 
 size_t score_lds_bytes(const Dims& d) { return static_cast<size_t>(d.G) * kNumBins * 4; }
@@ -571,9 +698,11 @@ __device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4]
 //     bits of an LDS bitmap over token positions (windows of 262144), read
 //     back in ascending order -> A_t, M_t;
 //   scores (Eq. 10): q . k_i for i in A_t straight from the KV cache, 16 lanes
-//     per key row, 20 rows in flight per thread, fp32 accumulation of exact
-//     bf16 products;
-//   rerank (Eq. 11): radix select of the K-th largest, kept in candidate
+//     per key row, 20 rows in flight per thread, bf16 pair products with fp32
+//     accumulation;
+//   rerank (Eq. 11): a pass over scores binned linearly between their minimum
+//     and maximum finds the bin of the K-th largest, whose entries are ranked
+//     exactly (else a radix select on the ordered keys); kept in candidate
 //     (= ascending index) order, ties to the lower index;
 //   softmax-V (Eq. 12) and the cache update.
 //
@@ -581,8 +710,11 @@ __device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4]
 // initialisation) every head is exact.
 //
 // LDS (dynamic): region0 = bitmap window (34 KiB), later S_hat and its scores
-// (K each); then A_t and its scores (cand_cap each).
+// (K each) and one flag byte per candidate; then A_t and its scores
+// (cand_cap each).
 // ---------------------------------------------------------------------------
+constexpr int kCandU = 20;  // candidate rows per 16-lane group in flight: 640 per round
+
 __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uint16_t* q, long q_sb,
                                                        long q_sh, const uint16_t* k, const uint16_t* v, float* out,
                                                        int length, int t_dec, int mode, int stats_slot) {
@@ -592,7 +724,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
   __shared__ HeadShared sh;
   __shared__ int s_rank[8][64];
   extern __shared__ __align__(16) unsigned char dyn[];
-  const size_t region0 = (kBitmapLdsWords * 4 > 8 * d.K) ? kBitmapLdsWords * 4 : 8 * d.K;
+  const size_t region0 = head_region0(d);
   uint32_t* bm = reinterpret_cast<uint32_t*>(dyn);
   int32_t* s_sel = reinterpret_cast<int32_t*>(dyn);
   float* s_selsc = reinterpret_cast<float*>(dyn + 4 * static_cast<size_t>(d.K));
@@ -745,8 +877,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
       }
     }
     __syncthreads();
-    if (nwords <= 8 * kHeadThreads) M += bitmap_emit<8>(bm, nwords, base, s_cand + M, sh.tmp);
-    else M += bitmap_emit<kSliceWords>(bm, nwords, base, s_cand + M, sh.tmp);
+    M += bitmap_emit(bm, nwords, base, s_cand + M, sh.tmp);
     __syncthreads();
   }
   for (int x = wlo + tid; x < length; x += blockDim.x) s_cand[M + (x - wlo)] = x;
@@ -760,43 +891,44 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
 
   // ---- candidate scores (Eq. 10) ----
   const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
+  const uint16_t* vb = v + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
+  const int rg = tid >> 4, rpr = blockDim.x >> 4;
   {
-    // 16 lanes per key row (16 bytes each), 20 rows in flight per thread,
-    // fp32 accumulation of exact bf16 products
-    const int part = tid & 15, rg = tid >> 4, rpr = blockDim.x >> 4;
+    // 16 lanes per key row (16 bytes each), kCandU rows in flight per thread,
+    // bf16 pair products accumulated in fp32 (dot2)
     const uint4 qw = *reinterpret_cast<const uint4*>(q + bb * q_sb + h * q_sh + 8 * part);
-    const float qf[8] = {bf16_lo(qw.x), bf16_hi(qw.x), bf16_lo(qw.y), bf16_hi(qw.y),
-                         bf16_lo(qw.z), bf16_hi(qw.z), bf16_lo(qw.w), bf16_hi(qw.w)};
-    constexpr int U = 20;
+    constexpr int U = kCandU;
     for (int r0 = 0; r0 < M; r0 += rpr * U) {
       uint4 kv[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = min(r0 + u * rpr + rg, M - 1);
-        kv[u] = *reinterpret_cast<const uint4*>(kb + static_cast<long>(s_cand[i]) * kHeadDim + 8 * part);
+        const long row = static_cast<long>(s_cand[i]) * kHeadDim + 8 * part;
+        kv[u] = *reinterpret_cast<const uint4*>(kb + row);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = r0 + u * rpr + rg;
-        float sc = qf[0] * bf16_lo(kv[u].x);
-        sc = fmaf(qf[1], bf16_hi(kv[u].x), sc);
-        sc = fmaf(qf[2], bf16_lo(kv[u].y), sc);
-        sc = fmaf(qf[3], bf16_hi(kv[u].y), sc);
-        sc = fmaf(qf[4], bf16_lo(kv[u].z), sc);
-        sc = fmaf(qf[5], bf16_hi(kv[u].z), sc);
-        sc = fmaf(qf[6], bf16_lo(kv[u].w), sc);
-        sc = fmaf(qf[7], bf16_hi(kv[u].w), sc);
+        float sc = dot2_bf16(kv[u].x, qw.x, 0.f);
+        sc = dot2_bf16(kv[u].y, qw.y, sc);
+        sc = dot2_bf16(kv[u].z, qw.z, sc);
+        sc = dot2_bf16(kv[u].w, qw.w, sc);
         sc = row_sum(sc);
         if (part == 0 && i < M) s_sc[i] = sc;
       }
     }
   }
   __syncthreads();
-  float mx = kNegInf;
-  for (int i = tid; i < M; i += blockDim.x) mx = fmaxf(mx, s_sc[i]);
-  mx = block_max_f32(mx, reinterpret_cast<float*>(sh.tmp));
+  float mx = kNegInf, mn = kPosInf;
+  for (int i = tid; i < M; i += blockDim.x) {
+    mx = fmaxf(mx, s_sc[i]);
+    mn = fminf(mn, s_sc[i]);
+  }
+  block_minmax_f32(mn, mx, reinterpret_cast<float*>(sh.tmp), &mn, &mx);
 
   // ---- rerank (Eq. 11) ----
+  // LDS after S_hat and its scores in region0: boundary flags of the linear rerank
+  uint8_t* flag = reinterpret_cast<uint8_t*>(dyn + 8 * static_cast<size_t>(d.K));
   int n;
   if (M <= d.K) {
     for (int i = tid; i < M; i += blockDim.x) {
@@ -806,10 +938,13 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
     n = M;
     __syncthreads();
   } else {
-    int need;
-    uint32_t mask;
-    const uint32_t T = radix_kth(s_sc, M, d.K, sh, &mask, &need);
-    n = select_in_order(s_cand, s_sc, M, T, mask, need, s_sel, s_selsc, sh);
+    n = (mx > mn) ? rerank_linear(s_cand, s_sc, M, d.K, mn, mx, s_sel, s_selsc, flag, sh) : -1;
+    if (n < 0) {
+      int need;
+      uint32_t mask;
+      const uint32_t T = radix_kth(s_sc, M, d.K, sh, &mask, &need);
+      n = select_in_order(s_cand, s_sc, M, T, mask, need, s_sel, s_selsc, sh);
+    }
   }
 
   // ---- reuse path: softmax-V (Eq. 12) and cache update ----
@@ -818,7 +953,6 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
     b.selsc[static_cast<long>(bh) * d.K + i] = s_selsc[i];
   }
   if (tid == 0) b.sellen[bh] = n;
-  const uint16_t* vb = v + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
   attend(s_sel, s_selsc, n, mx, vb, out + static_cast<long>(bh) * kHeadDim, nullptr, sh);
   cache_push(d, b, bh, sh.qbar, s_sel, n);
 }
