@@ -40,6 +40,12 @@ constexpr float kNegInf = -INFINITY;
 constexpr float kPosInf = INFINITY;
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
 
+// Barrier for data shared through LDS only: this wave's LDS operations are
+// complete, then s_barrier. Unlike __syncthreads() it does not wait for the
+// wave's outstanding global loads and stores (which no other wave of the
+// work group reads), so global traffic stays in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Order-preserving map of a float32 to uint32 (larger float, larger key).
 // Negative zero is folded into positive zero so that the two compare equal.
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -176,14 +182,14 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* tmp)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int incl = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   int before = 0, tot = 0;
   for (int w = 0; w < nw; ++w) {
     const int x = tmp[w];
     if (w < wave) before += x;
     tot += x;
   }
-  __syncthreads();
+  lds_barrier();
   *total = tot;
   return before + incl - v;
 }
@@ -197,13 +203,13 @@ __device__ __forceinline__ void block_minmax_f32(float lo, float hi, float* tmp,
     tmp[2 * wave] = lo;
     tmp[2 * wave + 1] = hi;
   }
-  __syncthreads();
+  lds_barrier();
   float a = kPosInf, b = kNegInf;
   for (int w = 0; w < nw; ++w) {
     a = fminf(a, tmp[2 * w]);
     b = fmaxf(b, tmp[2 * w + 1]);
   }
-  __syncthreads();
+  lds_barrier();
   *mn = a;
   *mx = b;
 }
@@ -212,10 +218,10 @@ __device__ __forceinline__ float block_max_f32(float v, float* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   v = wave_max_f32(v);
   if (lane == 0) tmp[wave] = v;
-  __syncthreads();
+  lds_barrier();
   float m = kNegInf;
   for (int w = 0; w < nw; ++w) m = fmaxf(m, tmp[w]);
-  __syncthreads();
+  lds_barrier();
   return m;
 }
 
@@ -343,9 +349,9 @@ __device__ __forceinline__ uint32_t radix_kth(const float* sc, int n, int k, Hea
   const int wave = threadIdx.x >> 6;
   int* bins = &sh.whist[0][0];  // 2048 bins for the first pass
   reinterpret_cast<int4*>(bins)[threadIdx.x] = make_int4(0, 0, 0, 0);
-  __syncthreads();
+  lds_barrier();
   for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&bins[order_key(sc[i]) >> 21], 1);
-  __syncthreads();
+  lds_barrier();
   {
     const int4 h = reinterpret_cast<const int4*>(bins)[511 - threadIdx.x];  // bins 2047-4t .. 2044-4t
     const int c[4] = {h.w, h.z, h.y, h.x};
@@ -364,7 +370,7 @@ __device__ __forceinline__ uint32_t radix_kth(const float* sc, int n, int k, Hea
         run += c[j];
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   uint32_t prefix = static_cast<uint32_t>(sh.i0) << 21, mask = 0x7FFu << 21;
   int rem = sh.i1, ncand = sh.i2;
@@ -373,14 +379,14 @@ __device__ __forceinline__ uint32_t radix_kth(const float* sc, int n, int k, Hea
     const int shift = shifts[p];
     const uint32_t dmask = shift == 0 ? 31u : 255u;
     clear_whist(sh);
-    __syncthreads();
+    lds_barrier();
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
       const uint32_t u = order_key(sc[i]);
       if ((u & mask) == prefix) atomicAdd(&sh.whist[wave][(u >> shift) & dmask], 1);
     }
-    __syncthreads();
+    lds_barrier();
     pick_digit(sh, rem);
-    __syncthreads();
+    lds_barrier();
     prefix |= static_cast<uint32_t>(sh.i0) << shift;
     mask |= dmask << shift;
     rem = sh.i1;
@@ -418,7 +424,7 @@ __device__ __forceinline__ int select_in_order(const int32_t* idx, const float* 
     }
     e += (u == T);
   }
-  __syncthreads();
+  lds_barrier();
   return (tot & 0xffff) + min(tot >> 16, need);
 }
 
@@ -440,9 +446,9 @@ __device__ __forceinline__ int rerank_linear(const int32_t* idx, const float* sc
   int* bins = &sh.whist[0][0];  // 2048 bins
   reinterpret_cast<int4*>(bins)[tid] = make_int4(0, 0, 0, 0);
   if (tid == 0) sh.i3 = 0;
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i < M; i += blockDim.x) atomicAdd(&bins[bin_of(sc[i])], 1);
-  __syncthreads();
+  lds_barrier();
   {
     const int4 h = reinterpret_cast<const int4*>(bins)[511 - tid];  // bins 2047-4t .. 2044-4t
     const int c[4] = {h.w, h.z, h.y, h.x};
@@ -461,7 +467,7 @@ __device__ __forceinline__ int rerank_linear(const int32_t* idx, const float* sc
         run += c[j];
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   const int b1 = sh.i0, need = sh.i1, cnt = sh.i2;
   if (need < cnt) {
@@ -473,7 +479,7 @@ __device__ __forceinline__ int rerank_linear(const int32_t* idx, const float* sc
       const int o = wave_slot(in, &sh.i3);
       if (in) sh.rslot[o] = i;
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
       const int p = sh.rslot[min(lane, cnt - 1)];
       const float v = sc[p];
@@ -486,7 +492,7 @@ __device__ __forceinline__ int rerank_linear(const int32_t* idx, const float* sc
       }
       if (lane < cnt) flag[p] = rank < need ? 1 : 0;
     }
-    __syncthreads();
+    lds_barrier();
   }
   // kept: bin > b1, or bin == b1 and (all of the bin kept, or flagged)
   const int per = (M + blockDim.x - 1) / blockDim.x;
@@ -506,7 +512,7 @@ __device__ __forceinline__ int rerank_linear(const int32_t* idx, const float* sc
       ++o;
     }
   }
-  __syncthreads();
+  lds_barrier();
   return tot;
 }
 
@@ -521,7 +527,7 @@ __device__ __forceinline__ void attend_reduce(float (&acc)[8], float z, float* o
   r[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
   r[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   if (sub == 0) sh.red[rg][kHeadDim] = z;
-  __syncthreads();
+  lds_barrier();
   if (out != nullptr && threadIdx.x < kHeadDim) {
     float a = 0.f, zz = 0.f;
     for (int g2 = 0; g2 < nrg; ++g2) {
@@ -535,7 +541,7 @@ __device__ __forceinline__ void attend_reduce(float (&acc)[8], float z, float* o
       if (threadIdx.x == 0) *out_z = zz;
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Sparse softmax-V (Eq. 12) over n selected rows (indices and unscaled
@@ -551,7 +557,7 @@ __device__ __forceinline__ void attend(const int32_t* sel, float* sc, int n, flo
                                        float* out_z, HeadShared& sh) {
   const int sub = threadIdx.x & 15, rg = threadIdx.x >> 4, rpr = blockDim.x >> 4;
   for (int i = threadIdx.x; i < n; i += blockDim.x) sc[i] = expf((sc[i] - mx) * kInvSqrtD);
-  __syncthreads();
+  lds_barrier();
   constexpr int U = 16;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float z = 0.f;
@@ -587,9 +593,10 @@ __device__ __forceinline__ void attend(const int32_t* sel, float* sc, int n, flo
 
 // Push (q_bar_t, S_hat_t) into the head's FIFO (Query-support cache
 // paragraph: after either path; the oldest entry is overwritten when full).
-__device__ __forceinline__ void cache_push(const Dims& d, const Bufs& b, int bh, const float* qbar, const int32_t* sel, int n) {
-  const int slot = b.fifo[2 * bh];
-  const int count = b.fifo[2 * bh + 1];
+// slot / count: the FIFO state read at the start of the kernel (the caller's
+// threads must not re-read it here, since thread 0 updates it).
+__device__ __forceinline__ void cache_push(const Dims& d, const Bufs& b, int bh, int slot, int count, const float* qbar,
+                                           const int32_t* sel, int n) {
   const long e = static_cast<long>(bh) * d.C + slot;
   for (int t = threadIdx.x; t < kHeadDim; t += blockDim.x) b.cache_qbar[e * kHeadDim + t] = qbar[t];
   for (int i = threadIdx.x; i < n; i += blockDim.x) b.cache_supp[e * d.K + i] = sel[i];
@@ -761,7 +768,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
     *reinterpret_cast<float2*>(b.qbar + static_cast<long>(bh) * kHeadDim + 2 * lane) = make_float2(qb0, qb1);
   }
   if (mode == kModeDecode) bitmap_clear(bm);  // first bitmap window, while the loads are in flight
-  __syncthreads();
+  lds_barrier();
 
   bool exact = true, refresh = false;
   double rho_max = -INFINITY;
@@ -790,7 +797,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
         sh.rho[p] = s;
       }
     }
-    __syncthreads();
+    lds_barrier();
     // Rank of FIFO position p under (rho desc, position asc), counted in
     // parallel: wave w compares every position with positions w, w+8, ...
     {
@@ -803,7 +810,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
       }
       s_rank[wave][p] = r;
     }
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
       int rank = 0;
 #pragma unroll
@@ -818,7 +825,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
       }
     }
     n_ret = min(d.R, count);
-    __syncthreads();
+    lds_barrier();
     if (count > 0) rho_max = sh.d0;
     exact = refresh || count == 0 || rho_max < d.tau;
   }
@@ -856,7 +863,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
     const int nwords = (nbits + 31) >> 5;
     if (base > 0) {
       bitmap_clear(bm);
-      __syncthreads();
+      lds_barrier();
     }
     for (int j0 = 0; j0 < d.K; j0 += blockDim.x) {
       const int j = j0 + tid;
@@ -876,13 +883,13 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     M += bitmap_emit(bm, nwords, base, s_cand + M, sh.tmp);
-    __syncthreads();
+    lds_barrier();
   }
   for (int x = wlo + tid; x < length; x += blockDim.x) s_cand[M + (x - wlo)] = x;
   M += length - wlo;
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i < M; i += blockDim.x) b.cand[static_cast<long>(bh) * d.cand_cap + i] = s_cand[i];
   if (tid == 0) {
     b.m[bh] = M;
@@ -918,7 +925,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   float mx = kNegInf, mn = kPosInf;
   for (int i = tid; i < M; i += blockDim.x) {
     mx = fmaxf(mx, s_sc[i]);
@@ -936,7 +943,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
       s_selsc[i] = s_sc[i];
     }
     n = M;
-    __syncthreads();
+    lds_barrier();
   } else {
     n = (mx > mn) ? rerank_linear(s_cand, s_sc, M, d.K, mn, mx, s_sel, s_selsc, flag, sh) : -1;
     if (n < 0) {
@@ -954,7 +961,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
   }
   if (tid == 0) b.sellen[bh] = n;
   attend(s_sel, s_selsc, n, mx, vb, out + static_cast<long>(bh) * kHeadDim, nullptr, sh);
-  cache_push(d, b, bh, sh.qbar, s_sel, n);
+  cache_push(d, b, bh, fifo_head, count, sh.qbar, s_sel, n);
 }
 
 // ---------------------------------------------------------------------------
@@ -1001,7 +1008,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(Dims d, Bufs b, const u
     for (int bg = g0; bg < g1; ++bg)
       if (flags >> (bg - g0) & 1) s_eg[o++] = bg;
   }
-  __syncthreads();
+  lds_barrier();
   if (ne == 0) return;
 
   // this work group's share of the concatenated exact rows: split point w ->
@@ -1033,9 +1040,9 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(Dims d, Bufs b, const u
     const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
     QkTiles ta, tb;
     qk_load(ta, kb, row0, rend, wave, j, kq);
-    __syncthreads();  // the previous segment's histogram flush is done
+    lds_barrier();  // the previous segment's histogram flush is done
     for (int i = threadIdx.x; i < d.G * kNumBins; i += blockDim.x) s_hist[i] = 0u;
-    __syncthreads();
+    lds_barrier();
     float* srow = b.score + static_cast<long>(bb * d.Hq + h) * d.score_stride;
     uint32_t* hrow = s_hist + j * kNumBins;
     for (int t0 = row0; t0 < rend; t0 += 2 * kStage) {
@@ -1045,7 +1052,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(Dims d, Bufs b, const u
       qk_load(ta, kb, t0 + 2 * kStage, rend, wave, j, kq);
       qk_score(tb, bq, t0 + kStage, rend, wave, kq, hv, srow, hrow);
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t* ghist = b.hist + static_cast<long>(bb * d.Hq + g * d.G) * kHistSeg * kNumBins +
                       (blockIdx.x % kHistSeg) * kNumBins;
     for (int i = threadIdx.x; i < d.G * kNumBins; i += blockDim.x) {
@@ -1078,8 +1085,8 @@ __device__ __forceinline__ uint32_t key_score_bits(uint64_t u) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh, const uint2* chosen, int n,
                                             int length, const uint16_t* v, float* out, int32_t* sel_out, int push,
-                                            HeadShared& sh, uint32_t* bm, int32_t* wpre, int32_t* s_sel,
-                                            float* s_selsc) {
+                                            int fifo_slot, int fifo_count, HeadShared& sh, uint32_t* bm,
+                                            int32_t* wpre, int32_t* s_sel, float* s_selsc) {
   const int tid = threadIdx.x;
   const int bb = bh / d.Hq, g = (bh % d.Hq) / d.G;
 
@@ -1088,12 +1095,12 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh
   for (int base = 0; base < length; base += kBitmapWords * 32) {
     const int nbits = min(kBitmapWords * 32, length - base);
     bitmap_clear(bm);
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < n; i += blockDim.x) {
       const int x = static_cast<int>(chosen[i].x) - base;
       if (x >= 0 && x < nbits) bitmap_set(bm, x);
     }
-    __syncthreads();
+    lds_barrier();
     // word prefix counts: fixed 16-word slice per thread (same padded layout)
     {
       const int w0 = tid * kSliceWords;
@@ -1116,7 +1123,7 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh
       (void)w0;
       sh.i2 = wtot;  // read after the barrier below
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < n; i += blockDim.x) {
       const uint2 e = chosen[i];
       const int x = static_cast<int>(e.x) - base;
@@ -1128,7 +1135,7 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh
       }
     }
     base_out += sh.i2;
-    __syncthreads();
+    lds_barrier();
   }
   float mx = kNegInf;
   for (int i = tid; i < n; i += blockDim.x) {
@@ -1146,8 +1153,8 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh
   }
   if (push) {
     for (int t = tid; t < kHeadDim; t += blockDim.x) sh.qbar[t] = b.qbar[static_cast<long>(bh) * kHeadDim + t];
-    __syncthreads();
-    cache_push(d, b, bh, sh.qbar, s_sel, n);
+    lds_barrier();
+    cache_push(d, b, bh, fifo_slot, fifo_count, sh.qbar, s_sel, n);
   }
 }
 
@@ -1210,7 +1217,7 @@ __device__ __forceinline__ void collect_chunk(const Dims& d, const Bufs& b, int 
       run += c[i];
     }
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t b1 = static_cast<uint32_t>(*s_b1);
   int nu = 0, nbd = 0;
 #pragma unroll
@@ -1270,6 +1277,7 @@ __device__ __forceinline__ uint2 boundary_entry(const uint2* hits_row, const int
 __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const uint16_t* v, float* out,
                                                          int32_t* sel_out, int length, int push) {
   const int bh = blockIdx.x;
+  const int fifo_slot = b.fifo[2 * bh], fifo_count = b.fifo[2 * bh + 1];  // before the push updates them
   if (!b.path[bh]) return;
   const int bb = bh / d.Hq, h = bh % d.Hq, g = h / d.G;
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -1314,7 +1322,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const u
       aoff[nch] = ta;
       boff[nch] = tb;
     }
-    __syncthreads();
+    lds_barrier();
   }
   const int na = min(aoff[nch], keff);
   const int nb = boff[nch];
@@ -1350,7 +1358,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const u
     }
   }
   if (tid == 0) sh.i3 = 0;
-  __syncthreads();
+  lds_barrier();
 
   // radix select of the `need` best boundary entries
   uint64_t prefix = 0ull, mask = 0ull;
@@ -1358,7 +1366,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const u
   int ncand = nb;
   for (int shift = 56; shift >= 0 && ncand > need; shift -= 8) {
     clear_whist(sh);
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < nb; i += blockDim.x) {
       uint64_t u;
       if (in_lds) {
@@ -1369,9 +1377,9 @@ __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const u
       }
       if ((u & mask) == prefix) atomicAdd(&sh.whist[wave][(u >> shift) & 255ull], 1);
     }
-    __syncthreads();
+    lds_barrier();
     pick_digit(sh, need);
-    __syncthreads();
+    lds_barrier();
     prefix |= static_cast<uint64_t>(sh.i0) << shift;
     mask |= 255ull << shift;
     need = sh.i1;
@@ -1393,9 +1401,10 @@ __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const u
     const int o = wave_slot(t, &sh.i3);
     if (t && na + o < d.K) chosen[na + o] = make_uint2(e.x, key_score_bits(u));
   }
-  __syncthreads();
+  lds_barrier();
   const int n = min(na + sh.i3, keff);
-  finish_tail(d, b, bh, chosen, n, length, v, out, sel_out, push, sh, bm, wpre, s_sel, s_selsc);
+  finish_tail(d, b, bh, chosen, n, length, v, out, sel_out, push, fifo_slot, fifo_count, sh, bm, wpre, s_sel,
+              s_selsc);
   (void)h;
   (void)bb;
   (void)g;
