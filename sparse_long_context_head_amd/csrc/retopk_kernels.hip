@@ -214,6 +214,33 @@ __device__ __forceinline__ void block_minmax_f32(float lo, float hi, float* tmp,
   *mx = b;
 }
 
+// Two block-wide exclusive prefix sums at once (one pair of barriers). tmp:
+// 2 * blockDim.x / 64 ints.
+__device__ __forceinline__ void block_exclusive_scan2(int a, int b, int* ea, int* eb, int* ta, int* tb, int* tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+  if (lane == 63) {
+    tmp[2 * wave] = ia;
+    tmp[2 * wave + 1] = ib;
+  }
+  lds_barrier();
+  int pa = 0, pb = 0, sa = 0, sb = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int xa = tmp[2 * w], xb = tmp[2 * w + 1];
+    if (w < wave) {
+      pa += xa;
+      pb += xb;
+    }
+    sa += xa;
+    sb += xb;
+  }
+  lds_barrier();
+  *ea = pa + ia - a;
+  *eb = pb + ib - b;
+  *ta = sa;
+  *tb = sb;
+}
+
 __device__ __forceinline__ float block_max_f32(float v, float* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   v = wave_max_f32(v);
@@ -294,7 +321,7 @@ struct HeadShared {
   int len[64];                         // support size of each ring slot
   int rslot[64];                       // ring slots of the retrieved entries, best first
   __align__(16) int whist[kHeadThreads / 64][256];   // one radix histogram per wave
-  int tmp[16];
+  int tmp[32];
   __align__(16) float red[kHeadThreads / 16][kHeadDim + 4];  // one row per 16-lane row group
   int i0, i1, i2, i3;
   double d0;
@@ -331,6 +358,32 @@ __device__ __forceinline__ void pick_digit(HeadShared& sh, int rem) {
       run += c[j];
     }
   }
+}
+
+// From a 2048-bin histogram in sh.whist, the bin holding the rem-th largest
+// (bins scanned from 2047 down): sh.i0 = bin, sh.i1 = rank within it, sh.i2 =
+// its count. Every thread of a 512-thread block must call it; ends with a
+// barrier.
+__device__ __forceinline__ void pick_bin2048(HeadShared& sh, int rem) {
+  const int* bins = &sh.whist[0][0];
+  const int4 h = reinterpret_cast<const int4*>(bins)[511 - threadIdx.x];  // bins 2047-4t .. 2044-4t
+  const int c[4] = {h.w, h.z, h.y, h.x};
+  const int s4 = c[0] + c[1] + c[2] + c[3];
+  int tot;
+  int run = block_exclusive_scan(s4, &tot, sh.tmp);
+  if (run < rem && run + s4 >= rem) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (run + c[j] >= rem) {
+        sh.i0 = 2047 - 4 * static_cast<int>(threadIdx.x) - j;
+        sh.i1 = rem - run;
+        sh.i2 = c[j];
+        break;
+      }
+      run += c[j];
+    }
+  }
+  lds_barrier();
 }
 
 __device__ __forceinline__ void clear_whist(HeadShared& sh) {
@@ -1094,33 +1147,33 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh
   int base_out = 0;
   for (int base = 0; base < length; base += kBitmapWords * 32) {
     const int nbits = min(kBitmapWords * 32, length - base);
-    bitmap_clear(bm);
+    const int nwords = (nbits + 31) >> 5;
+    bitmap_clear_n(bm, nwords);
     lds_barrier();
     for (int i = tid; i < n; i += blockDim.x) {
       const int x = static_cast<int>(chosen[i].x) - base;
       if (x >= 0 && x < nbits) bitmap_set(bm, x);
     }
     lds_barrier();
-    // word prefix counts: fixed 16-word slice per thread (same padded layout)
+    // word prefix counts, the words split evenly over the block
     {
-      const int w0 = tid * kSliceWords;
-      const uint32_t* p = bm + tid * (kSliceWords + 1);
+      const int per = (nwords + blockDim.x - 1) / blockDim.x;  // <= kSliceWords
+      const int w0 = tid * per;
       uint32_t w[kSliceWords];
       int cnt = 0;
 #pragma unroll
       for (int i = 0; i < kSliceWords; ++i) {
-        w[i] = p[i];
+        w[i] = (i < per && w0 + i < nwords) ? bm[bm_at(w0 + i)] : 0u;
         cnt += __popc(w[i]);
       }
       int wtot;
       int run = block_exclusive_scan(cnt, &wtot, sh.tmp);
-      int* q = wpre + tid * (kSliceWords + 1);
 #pragma unroll
       for (int i = 0; i < kSliceWords; ++i) {
-        q[i] = run;
+        if (i >= per) break;  // uniform
+        if (w0 + i < nwords) wpre[bm_at(w0 + i)] = run;
         run += __popc(w[i]);
       }
-      (void)w0;
       sh.i2 = wtot;  // read after the barrier below
     }
     lds_barrier();
@@ -1164,11 +1217,11 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh
 // histogram (the bin holding the K-th largest score) and classifies its
 // scores: entries in higher bins ("above", fewer than K in all) and entries
 // in the boundary bin are written, as (index, score bits), to the chunk's own
-// region of the hit buffer (boundary from the front, above from the back) in
-// position order, with the two counts. No global atomics.
+// region of the hit buffer (boundary from the front, above from the back),
+// with the two counts. No global atomics.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void collect_chunk(const Dims& d, const Bufs& b, int bh, int chunk, int length, int* tmp,
-                                              int* s_b1) {
+                                              int* s_b1, int* s_cnt) {
   const int c0 = chunk * kCollectChunk;
   const int clen = min(kCollectChunk, length - c0);
   const int keff = min(d.K, length);
@@ -1204,7 +1257,11 @@ __device__ __forceinline__ void collect_chunk(const Dims& d, const Bufs& b, int 
     c[1] += hs[sgm].x;
   }
   const int csum = c[0] + c[1];
-  if (threadIdx.x == 0) *s_b1 = 0;
+  if (threadIdx.x == 0) {
+    *s_b1 = 0;
+    s_cnt[0] = 0;
+    s_cnt[1] = 0;
+  }
   int tot;
   const int ex = block_exclusive_scan(csum, &tot, tmp);
   if (ex < keff && ex + csum >= keff) {
@@ -1219,36 +1276,36 @@ __device__ __forceinline__ void collect_chunk(const Dims& d, const Bufs& b, int 
   }
   lds_barrier();
   const uint32_t b1 = static_cast<uint32_t>(*s_b1);
-  int nu = 0, nbd = 0;
+  // one pass: above-bin entries from the back of the region, boundary-bin
+  // entries from the front, slots from wave-aggregated LDS counters (the
+  // order inside a region is free: the finish resolves by composite key and
+  // sorts by index)
+  uint2* region = b.hits + static_cast<long>(bh) * d.max_len + c0;
 #pragma unroll
   for (int u = 0; u < kPerThread; ++u) {
     const bool valid = i0 + u < length;
     const uint32_t bin = order_key(v[u]) >> kHistShift;
-    nu += valid && bin > b1;
-    nbd += valid && bin == b1;
+    const bool up = valid && bin > b1;
+    const bool bd = valid && bin == b1;
+    if (__ballot(up || bd) == 0ull) continue;
+    const uint2 e = make_uint2(static_cast<uint32_t>(i0 + u), __float_as_uint(v[u]));
+    const int ou = wave_slot(up, &s_cnt[0]);
+    if (up) region[clen - 1 - ou] = e;
+    const int ob = wave_slot(bd, &s_cnt[1]);
+    if (bd) region[ob] = e;
   }
-  const int pre = block_exclusive_scan((nu << 16) | nbd, &tot, tmp);
-  int ou = pre >> 16, ob = pre & 0xffff;
-  uint2* region = b.hits + static_cast<long>(bh) * d.max_len + c0;
-#pragma unroll
-  for (int u = 0; u < kPerThread; ++u) {
-    if (i0 + u < length) {
-      const uint32_t bin = order_key(v[u]) >> kHistShift;
-      const uint2 e = make_uint2(static_cast<uint32_t>(i0 + u), __float_as_uint(v[u]));
-      if (bin > b1) region[clen - 1 - (ou++)] = e;
-      else if (bin == b1) region[ob++] = e;
-    }
-  }
-  if (threadIdx.x == 0) b.ccnt[static_cast<long>(bh) * d.n_chunks + chunk] = make_int2(tot >> 16, tot & 0xffff);
+  lds_barrier();
+  if (threadIdx.x == 0) b.ccnt[static_cast<long>(bh) * d.n_chunks + chunk] = make_int2(s_cnt[0], s_cnt[1]);
 }
 
 // One work group per (head, chunk); reuse heads return at once.
 __global__ __launch_bounds__(kHeadThreads) void k_collect(Dims d, Bufs b, int length, int nch) {
   __shared__ int tmp[8];
   __shared__ int s_b1;
+  __shared__ int s_cnt[2];
   const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;
   if (!b.path[bh]) return;
-  collect_chunk(d, b, bh, chunk, length, tmp, &s_b1);
+  collect_chunk(d, b, bh, chunk, length, tmp, &s_b1, s_cnt);
 }
 
 // ---------------------------------------------------------------------------
@@ -1277,10 +1334,18 @@ __device__ __forceinline__ uint2 boundary_entry(const uint2* hits_row, const int
 __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const uint16_t* v, float* out,
                                                          int32_t* sel_out, int length, int push) {
   const int bh = blockIdx.x;
-  const int fifo_slot = b.fifo[2 * bh], fifo_count = b.fifo[2 * bh + 1];  // before the push updates them
+  const int tid = threadIdx.x;
+  const int nch = (length + kCollectChunk - 1) / kCollectChunk;
+  const int2* ccnt = b.ccnt + static_cast<long>(bh) * d.n_chunks;
+  // one round of loads: FIFO state (before the push updates it), path flag
+  // and this thread's chunk counts
+  const int per = (nch + blockDim.x - 1) / blockDim.x;  // <= 2 (n_chunks <= 1024)
+  const int c0 = min(tid * per, nch), c1 = min(c0 + per, nch);
+  int2 cc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) cc[i] = c0 + i < c1 ? ccnt[c0 + i] : make_int2(0, 0);
+  const int fifo_slot = b.fifo[2 * bh], fifo_count = b.fifo[2 * bh + 1];
   if (!b.path[bh]) return;
-  const int bb = bh / d.Hq, h = bh % d.Hq, g = h / d.G;
-  const int tid = threadIdx.x, wave = tid >> 6;
   __shared__ HeadShared sh;
   extern __shared__ __align__(16) unsigned char dyn[];
   constexpr size_t kRegion = kBitmapLdsWords * 4;                            // >= 4096 64-bit keys
@@ -1294,33 +1359,22 @@ __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const u
   int* aoff = reinterpret_cast<int*>(dyn + 2 * kRegion + 16 * static_cast<size_t>(d.K));           // E
   int* boff = aoff + d.n_chunks + 1;
   const int keff = min(d.K, length);
-  const int nch = (length + kCollectChunk - 1) / kCollectChunk;
   const uint2* hits_row = b.hits + static_cast<long>(bh) * d.max_len;
-  const int2* ccnt = b.ccnt + static_cast<long>(bh) * d.n_chunks;
 
   // chunk offsets of the above and boundary lists
   {
-    const int per = (nch + blockDim.x - 1) / blockDim.x;
-    const int c0 = tid * per, c1 = min(c0 + per, nch);
-    int sa = 0, sb = 0;
-    for (int c = c0; c < c1; ++c) {
-      const int2 cc = ccnt[c];
-      sa += cc.x;
-      sb += cc.y;
-    }
-    int ta, tb;
-    int oa = block_exclusive_scan(sa, &ta, sh.tmp);
-    int ob = block_exclusive_scan(sb, &tb, sh.tmp);
-    for (int c = c0; c < c1; ++c) {
-      const int2 cc = ccnt[c];
-      aoff[c] = oa;
-      boff[c] = ob;
-      oa += cc.x;
-      ob += cc.y;
+    int oa, ob, ta, tb;
+    block_exclusive_scan2(cc[0].x + cc[1].x, cc[0].y + cc[1].y, &oa, &ob, &ta, &tb, sh.tmp);
+    for (int i = 0; i < 2 && c0 + i < c1; ++i) {
+      aoff[c0 + i] = oa;
+      boff[c0 + i] = ob;
+      oa += cc[i].x;
+      ob += cc[i].y;
     }
     if (tid == 0) {
       aoff[nch] = ta;
       boff[nch] = tb;
+      sh.i3 = 0;
     }
     lds_barrier();
   }
@@ -1328,13 +1382,14 @@ __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const u
   const int nb = boff[nch];
   const bool in_lds = nb <= kBoundaryLds;
 
-  // gather: above entries into C, boundary keys into A
+  // gather: above entries into C, boundary keys into A (8 entries per thread per round)
   {
+    constexpr int U = 8;
     const int tot = na + (in_lds ? nb : 0);
-    for (int f0 = 0; f0 < tot; f0 += blockDim.x * 4) {
-      uint2 e[4];
+    for (int f0 = 0; f0 < tot; f0 += blockDim.x * U) {
+      uint2 e[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int f = f0 + u * blockDim.x + tid;
         e[u] = make_uint2(0u, 0u);
         if (f < na) {
@@ -1350,64 +1405,60 @@ __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const u
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int f = f0 + u * blockDim.x + tid;
         if (f < na) chosen[f] = e[u];
         else if (f < tot) keys[f - na] = comp_key(__uint_as_float(e[u].y), e[u].x);
       }
     }
   }
-  if (tid == 0) sh.i3 = 0;
   lds_barrier();
 
-  // radix select of the `need` best boundary entries
-  uint64_t prefix = 0ull, mask = 0ull;
+  // Radix select of the `need` best boundary entries. They share the top 10
+  // bits of their keys (the boundary bin), so the digits start below them:
+  // 11 bits at a time, 2048 LDS bins.
   int need = keff - na;
   int ncand = nb;
-  for (int shift = 56; shift >= 0 && ncand > need; shift -= 8) {
-    clear_whist(sh);
+  auto bkey = [&](int i) -> uint64_t {
+    if (in_lds) return keys[i];
+    const uint2 e = boundary_entry(hits_row, boff, nch, i);
+    return comp_key(__uint_as_float(e.y), e.x);
+  };
+  uint64_t mask = 0x3FFull << 54, prefix = 0ull;
+  if (nb > 0) prefix = bkey(0) & mask;
+  int* bins = &sh.whist[0][0];
+  // digits: bits 53-43, 42-32 (score), 31-21, 20-10, 9-0 (index)
+  for (int shift = 43; ncand > need && need > 0; shift = shift >= 11 ? shift - 11 : 0) {
+    const uint64_t dmask = shift == 0 ? 0x3FFull : 0x7FFull;
+    reinterpret_cast<int4*>(bins)[tid] = make_int4(0, 0, 0, 0);
     lds_barrier();
     for (int i = tid; i < nb; i += blockDim.x) {
-      uint64_t u;
-      if (in_lds) {
-        u = keys[i];
-      } else {
-        const uint2 e = boundary_entry(hits_row, boff, nch, i);
-        u = comp_key(__uint_as_float(e.y), e.x);
-      }
-      if ((u & mask) == prefix) atomicAdd(&sh.whist[wave][(u >> shift) & 255ull], 1);
+      const uint64_t u = bkey(i);
+      if ((u & mask) == prefix) atomicAdd(&bins[(u >> shift) & dmask], 1);
     }
     lds_barrier();
-    pick_digit(sh, need);
-    lds_barrier();
+    pick_bin2048(sh, need);
     prefix |= static_cast<uint64_t>(sh.i0) << shift;
-    mask |= 255ull << shift;
+    mask |= dmask << shift;
     need = sh.i1;
     ncand = sh.i2;
+    if (shift == 0) break;
   }
   // boundary entries whose masked key is >= prefix are exactly the kept ones
-  for (int i0 = 0; i0 < nb; i0 += blockDim.x) {
-    const int i = min(i0 + tid, nb - 1);  // clamped: a repeated entry is never taken twice (t below)
-    uint2 e;
-    uint64_t u;
-    if (in_lds) {
-      u = keys[i];
-      e = make_uint2(0xffffffffu - static_cast<uint32_t>(u & 0xffffffffull), 0u);
-    } else {
-      e = boundary_entry(hits_row, boff, nch, i);
-      u = comp_key(__uint_as_float(e.y), e.x);
+  if (keff - na > 0) {
+    for (int i0 = 0; i0 < nb; i0 += blockDim.x) {
+      const int i = min(i0 + tid, nb - 1);  // clamped: a repeated entry is never taken twice (t below)
+      const uint64_t u = bkey(i);
+      const bool t = i0 + tid < nb && (u & mask) >= prefix;
+      const int o = wave_slot(t, &sh.i3);
+      if (t && na + o < d.K)
+        chosen[na + o] = make_uint2(0xffffffffu - static_cast<uint32_t>(u & 0xffffffffull), key_score_bits(u));
     }
-    const bool t = i0 + tid < nb && (u & mask) >= prefix;
-    const int o = wave_slot(t, &sh.i3);
-    if (t && na + o < d.K) chosen[na + o] = make_uint2(e.x, key_score_bits(u));
   }
   lds_barrier();
   const int n = min(na + sh.i3, keff);
   finish_tail(d, b, bh, chosen, n, length, v, out, sel_out, push, fifo_slot, fifo_count, sh, bm, wpre, s_sel,
               s_selsc);
-  (void)h;
-  (void)bb;
-  (void)g;
 }
 
 // ---------------------------------------------------------------------------
