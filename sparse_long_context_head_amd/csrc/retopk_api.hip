@@ -219,6 +219,8 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   A(&b.hist, BH * kHistSeg * kNumBins);
   A(&b.hits, BH * d.max_len);
   A(&b.ccnt, BH * d.n_chunks);
+  A(&b.bnd, BH * 4);
+  A(&b.bkeys, BH * d.max_len);
   A(&b.sel, BH * d.K);
   A(&b.selsc, BH * d.K);
   A(&b.sellen, BH);

@@ -19,11 +19,11 @@ constexpr int kStatsCap = 4096;      // decode steps kept in the statistics ring
 constexpr int kExactWGTarget = 512;  // work groups of the full-history score kernel (2 per CU)
 constexpr int kExactMinRows = 1024;  // ... with about this many key rows each, at least
 constexpr int kHistSeg = 8;          // copies of each head's histogram (spreads the atomics)
-constexpr int kCollectChunk = 16384; // scores per work group of the threshold/collect step
-constexpr int kBoundaryLds = 4096;   // boundary entries resolved in LDS (32 KiB of 64-bit keys)
+constexpr int kBoundaryLds = 4096;   // boundary-bin candidates resolved in LDS (32 KiB of 64-bit keys)
+constexpr int kCollectChunk = 16384; // positions per work group of the collect step
 constexpr int kHeadThreads = 512;    // threads of the per-head kernels
 constexpr int kBitmapWords = 8192;   // LDS bitmap window: 262144 token positions (32 KiB)
-constexpr int kLdsLimit = 160 * 1024 - 20 * 1024;  // dynamic LDS a per-head kernel may use
+constexpr int kLdsLimit = 128 * 1024;  // dynamic LDS a per-head kernel may use (static LDS <= 32 KiB)
 constexpr int kMaxCand = 16384;      // R*K + W limit (candidate keys kept in LDS for reranking)
 
 // Problem dimensions, passed by value to every kernel.
@@ -54,10 +54,12 @@ struct Bufs {
   int32_t* cand;           // [BH, cand_cap]  A_t ascending
   float* score;            // [BH, score_stride]  full-history q.k
   uint32_t* hist;          // [BH, kHistSeg, kNumBins]  histogram of ordered score keys
-  uint2* hits;             // [BH, max_len] per score chunk of kCollectChunk positions: the
-                           //   boundary-bin entries from the front, the entries above it from
-                           //   the back; each entry is (index, score bits)
-  int2* ccnt;              // [BH, n_chunks] (above count, boundary count) of each chunk
+  uint2* hits;             // [BH, max_len] survivors (scores in the boundary bin or above) as
+                           //   (position, score bits), each chunk of kCollectChunk positions
+                           //   in its own region, in ascending position order
+  int32_t* ccnt;           // [BH, n_chunks] survivors per chunk
+  int32_t* bnd;            // [BH, 4] boundary bin, count above it, count in it
+  uint64_t* bkeys;         // [BH, max_len] boundary-bin composite keys when more than kBoundaryLds
   int32_t* sel;            // [BH, K]   S_hat_t ascending
   float* selsc;            // [BH, K]   q.k of S_hat_t
   int32_t* sellen;         // [BH]
@@ -95,7 +97,7 @@ hipError_t launch_head(const Dims& d, const Bufs& b, const uint16_t* q, long q_s
 // Full-history scores and histogram of exact heads.
 hipError_t launch_score(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
                         const uint16_t* k, int length, hipStream_t s);
-// Exact heads, global Top-K step 1: threshold bin and collection.
+// Exact heads, global Top-K step 1: boundary bin and survivors.
 hipError_t launch_collect(const Dims& d, const Bufs& b, int length, hipStream_t s);
 // Exact heads, global Top-K step 2, softmax-V (skipped when v or out is NULL),
 // S_t to sel_out (when not NULL) and the cache update (when push).

@@ -15,10 +15,11 @@
 //   k_score    full-history scores (Eq. 4) and a score histogram of every
 //              exact head, GQA-grouped on MFMA, the rows of the exact KV groups
 //              spread over the whole grid;
-//   k_collect  global Top-K (Eq. 1) step 1: threshold bin and collection,
-//              many work groups per exact head;
-//   k_finish   global Top-K step 2, softmax-V and the cache update, one work
-//              group per exact head.
+//   k_collect  global Top-K (Eq. 1) step 1: the boundary bin of the score
+//              histogram and the scores in it or above it, in position
+//              order, many work groups per exact head;
+//   k_finish   global Top-K step 2 (a radix select inside the boundary bin),
+//              softmax-V and the cache update, one work group per exact head.
 //
 // The exact Top-K baseline and the cache initialisation are the same four
 // kernels with every head marked exact. The path flag stays on the device:
@@ -269,12 +270,6 @@ __device__ __forceinline__ void bitmap_clear(uint32_t* bm) {
 
 __device__ __forceinline__ void bitmap_set(uint32_t* bm, int x) { atomicOr(&bm[bm_at(x >> 5)], 1u << (x & 31)); }
 
-// Clear the words 0 .. nwords-1 (nwords >= 1) of a bitmap window, any block size.
-__device__ __forceinline__ void bitmap_clear_n(uint32_t* bm, int nwords) {
-  const int n = bm_at(nwords - 1) + 1;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) bm[i] = 0u;
-}
-
 // Emit, in ascending order, the positions base + bit of every set bit of an
 // LDS bitmap window of `nwords` words to out[0 ..). Returns the number emitted
 // (the same value in every thread). The words are split evenly over the
@@ -326,6 +321,8 @@ struct HeadShared {
   int i0, i1, i2, i3;
   double d0;
 };
+// the per-head kernels add at most 2 KiB of their own to it; LDS is 160 KiB per work group
+static_assert(sizeof(HeadShared) + 2048 + kLdsLimit <= 160 * 1024, "static + dynamic LDS of a per-head kernel");
 
 // Wave 0 turns the per-wave histograms into the digit holding the rem-th
 // largest key (digits scanned from 255 down): sh.i0 = digit, sh.i1 = rank
@@ -674,8 +671,8 @@ size_t head_lds_bytes(const Dims& d) {
 size_t score_lds_bytes(const Dims& d) { return static_cast<size_t>(d.G) * kNumBins * 4; }
 
 size_t finish_lds_bytes(const Dims& d) {
-  return static_cast<size_t>(kBitmapLdsWords) * 4 * 2 + 16 * static_cast<size_t>(d.K) +
-         8 * (static_cast<size_t>(d.n_chunks) + 1);
+  return 8 * static_cast<size_t>(kBoundaryLds) + (4 * (static_cast<size_t>(d.n_chunks) + 1) + 15) / 16 * 16 +
+         8 * static_cast<size_t>(d.K);
 }
 
 int score_grid(const Dims& d, int length) {
@@ -1130,66 +1127,15 @@ __device__ __forceinline__ uint32_t key_score_bits(uint64_t u) {
 }
 
 // ---------------------------------------------------------------------------
-// Shared end of both exact finishes: the n chosen (index, score bits) pairs
-// are put in ascending index order by their rank in an LDS bitmap over the
-// positions (prefix popcount), giving S_t and its scores; the values are
-// aggregated (Eq. 12) and (q_bar_t, S_t) is pushed when `push`. Every thread
-// of the block must call it.
+// Shared end of the exact finish: S_t (n indices, ascending) and their scores
+// are in LDS. Writes them out, aggregates the values (Eq. 12) and pushes
+// (q_bar_t, S_t) when `push`. Every thread of the block must call it.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh, const uint2* chosen, int n,
-                                            int length, const uint16_t* v, float* out, int32_t* sel_out, int push,
-                                            int fifo_slot, int fifo_count, HeadShared& sh, uint32_t* bm,
-                                            int32_t* wpre, int32_t* s_sel, float* s_selsc) {
+__device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh, int n, const uint16_t* v, float* out,
+                                            int32_t* sel_out, int push, int fifo_slot, int fifo_count, HeadShared& sh,
+                                            const int32_t* s_sel, float* s_selsc) {
   const int tid = threadIdx.x;
   const int bb = bh / d.Hq, g = (bh % d.Hq) / d.G;
-
-  // ascending order: rank of each chosen index = popcount of the set bits below it
-  int base_out = 0;
-  for (int base = 0; base < length; base += kBitmapWords * 32) {
-    const int nbits = min(kBitmapWords * 32, length - base);
-    const int nwords = (nbits + 31) >> 5;
-    bitmap_clear_n(bm, nwords);
-    lds_barrier();
-    for (int i = tid; i < n; i += blockDim.x) {
-      const int x = static_cast<int>(chosen[i].x) - base;
-      if (x >= 0 && x < nbits) bitmap_set(bm, x);
-    }
-    lds_barrier();
-    // word prefix counts, the words split evenly over the block
-    {
-      const int per = (nwords + blockDim.x - 1) / blockDim.x;  // <= kSliceWords
-      const int w0 = tid * per;
-      uint32_t w[kSliceWords];
-      int cnt = 0;
-#pragma unroll
-      for (int i = 0; i < kSliceWords; ++i) {
-        w[i] = (i < per && w0 + i < nwords) ? bm[bm_at(w0 + i)] : 0u;
-        cnt += __popc(w[i]);
-      }
-      int wtot;
-      int run = block_exclusive_scan(cnt, &wtot, sh.tmp);
-#pragma unroll
-      for (int i = 0; i < kSliceWords; ++i) {
-        if (i >= per) break;  // uniform
-        if (w0 + i < nwords) wpre[bm_at(w0 + i)] = run;
-        run += __popc(w[i]);
-      }
-      sh.i2 = wtot;  // read after the barrier below
-    }
-    lds_barrier();
-    for (int i = tid; i < n; i += blockDim.x) {
-      const uint2 e = chosen[i];
-      const int x = static_cast<int>(e.x) - base;
-      if (x >= 0 && x < nbits) {
-        const int w = x >> 5;
-        const int pos = base_out + wpre[bm_at(w)] + __popc(bm[bm_at(w)] & ((1u << (x & 31)) - 1u));
-        s_sel[pos] = static_cast<int32_t>(e.x);
-        s_selsc[pos] = __uint_as_float(e.y);
-      }
-    }
-    base_out += sh.i2;
-    lds_barrier();
-  }
   float mx = kNegInf;
   for (int i = tid; i < n; i += blockDim.x) {
     mx = fmaxf(mx, s_selsc[i]);
@@ -1212,227 +1158,248 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh
 }
 
 // ---------------------------------------------------------------------------
-// K3, global Top-K (Eq. 1), step 1, for exact heads. Every work group takes a
-// chunk of kCollectChunk scores of one head, finds the boundary bin from the
-// histogram (the bin holding the K-th largest score) and classifies its
-// scores: entries in higher bins ("above", fewer than K in all) and entries
-// in the boundary bin are written, as (index, score bits), to the chunk's own
-// region of the hit buffer (boundary from the front, above from the back),
-// with the two counts. No global atomics.
+// K3, global Top-K (Eq. 1), step 1, for exact heads. One work group per (head,
+// chunk of kCollectChunk positions); reuse heads return at once. Every work
+// group finds the boundary bin b1 (the bin holding the K-th largest score)
+// from the head's histogram copies, then writes the chunk's "survivors"
+// (scores in b1 or above) as (position, score bits), in ascending position
+// order, to the chunk's region of the hit buffer, and their count. Wave w
+// owns rows 32w .. 32w+31 of 64 positions (lane l holds position 64r + l), so
+// a ballot is a row's survivors and mbcnt gives each one's slot: no atomics.
+// The work group of chunk 0 also records (b1, the count above b1, the count
+// in b1).
+//
+// The survivor test (ordered key >= b1 << 22, i.e. bin >= b1, with -0.0 and
+// +0.0 sharing the key of +0.0) is one compare per score: for b1 > 512 the
+// signed compare of the raw bits with those of the smallest float of bin b1
+// (positive; negative scores and -0.0 fail it), else the float compare with
+// the smallest float of bin b1 (0.0 for b1 = 512, a negative float below it,
+// -inf for bins 0 and 1, which hold only NaN patterns).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void collect_chunk(const Dims& d, const Bufs& b, int bh, int chunk, int length, int* tmp,
-                                              int* s_b1, int* s_cnt) {
-  const int c0 = chunk * kCollectChunk;
-  const int clen = min(kCollectChunk, length - c0);
+constexpr int kCollectRows = kCollectChunk / kHeadThreads;  // rows of 64 positions per wave
+static_assert(kCollectRows * 64 * (kHeadThreads / 64) == kCollectChunk, "collect chunk layout");
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// Both passes over a wave's rows; kInt selects the survivor compare.
+template <bool kInt>
+__device__ __forceinline__ void collect_rows(const float (&x)[kCollectRows], int p0, int length, int ti, float tf,
+                                             uint2* region, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  auto survives = [&](int u) {
+    return (p0 + 64 * u < length) & (kInt ? __float_as_int(x[u]) >= ti : x[u] >= tf);
+  };
+  // pass 1: this wave's survivor count; wave bases
+  int wc = 0;
+#pragma unroll
+  for (int u = 0; u < kCollectRows; ++u) wc += __popcll(__ballot(survives(u)));
+  if (lane == 0) tmp[wave] = wc;
+  lds_barrier();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kHeadThreads / 64; ++w) {
+    const int t = tmp[w];
+    base += w < wave ? t : 0;
+    tot += t;
+  }
+  *total = tot;
+  // pass 2: every survivor to its slot, in position order
+#pragma unroll
+  for (int u = 0; u < kCollectRows; ++u) {
+    const bool s = survives(u);
+    const uint64_t m = __ballot(s);
+    if (s) region[base + lanes_below(m)] = make_uint2(static_cast<uint32_t>(p0 + 64 * u), __float_as_uint(x[u]));
+    base += __popcll(m);
+  }
+}
+
+__global__ __launch_bounds__(kHeadThreads) void k_collect(Dims d, Bufs b, int length, int nch) {
+  __shared__ int tmp[16];
+  __shared__ int s_bd[3];
+  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;
+  if (!b.path[bh]) return;
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int keff = min(d.K, length);
   const float* srow = b.score + static_cast<long>(bh) * d.score_stride;
-  constexpr int kPerThread = kCollectChunk / kHeadThreads;
-  const int i0 = c0 + threadIdx.x * kPerThread;
-  float v[kPerThread];
-  if (i0 + kPerThread <= length) {
-#pragma unroll
-    for (int u = 0; u < kPerThread; u += 4) {
-      const float4 f = *reinterpret_cast<const float4*>(srow + i0 + u);
-      v[u] = f.x;
-      v[u + 1] = f.y;
-      v[u + 2] = f.z;
-      v[u + 3] = f.w;
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < kPerThread; ++u) v[u] = (i0 + u < length) ? srow[i0 + u] : 0.f;
-  }
-  // this thread's 2 bins, in descending order, summed over the histogram copies
   const uint32_t* hist = b.hist + static_cast<long>(bh) * kHistSeg * kNumBins;
-  constexpr int kPer = kNumBins / kHeadThreads;
-  static_assert(kPer == 2, "2 bins per thread");
+  const int c0 = chunk * kCollectChunk;
+  const int p0 = c0 + wave * kCollectRows * 64 + (tid & 63);  // position of row u: p0 + 64 u
+  // one round of loads: this wave's rows and this thread's two bins (1023-2t,
+  // 1022-2t) of every histogram copy
+  float x[kCollectRows];
+#pragma unroll
+  for (int u = 0; u < kCollectRows; ++u) x[u] = srow[min(p0 + 64 * u, length - 1)];  // clamped, masked below
   uint2 hs[kHistSeg];
 #pragma unroll
   for (int sgm = 0; sgm < kHistSeg; ++sgm)
-    hs[sgm] = *reinterpret_cast<const uint2*>(hist + sgm * kNumBins + kNumBins - kPer * (threadIdx.x + 1));
-  int c[kPer] = {0, 0};
+    hs[sgm] = *reinterpret_cast<const uint2*>(hist + sgm * kNumBins + kNumBins - 2 * (tid + 1));
+  int ca = 0, cb = 0;
 #pragma unroll
   for (int sgm = 0; sgm < kHistSeg; ++sgm) {
-    c[0] += hs[sgm].y;
-    c[1] += hs[sgm].x;
+    ca += hs[sgm].y;
+    cb += hs[sgm].x;
   }
-  const int csum = c[0] + c[1];
-  if (threadIdx.x == 0) {
-    *s_b1 = 0;
-    s_cnt[0] = 0;
-    s_cnt[1] = 0;
+  if (tid == 0) {  // defined even if the counts fell short of keff (ordered by the scan's barriers)
+    s_bd[0] = 0;
+    s_bd[1] = 0;
+    s_bd[2] = 0;
   }
   int tot;
-  const int ex = block_exclusive_scan(csum, &tot, tmp);
-  if (ex < keff && ex + csum >= keff) {
-    int run = ex;
-    for (int i = 0; i < kPer; ++i) {
-      if (run + c[i] >= keff) {
-        *s_b1 = kNumBins - 1 - (kPer * threadIdx.x + i);
-        break;
-      }
-      run += c[i];
-    }
+  const int ex = block_exclusive_scan(ca + cb, &tot, tmp);
+  if (ex < keff && ex + ca + cb >= keff) {
+    const bool first = ex + ca >= keff;
+    s_bd[0] = kNumBins - 1 - 2 * tid - (first ? 0 : 1);
+    s_bd[1] = first ? ex : ex + ca;
+    s_bd[2] = first ? ca : cb;
   }
   lds_barrier();
-  const uint32_t b1 = static_cast<uint32_t>(*s_b1);
-  // one pass: above-bin entries from the back of the region, boundary-bin
-  // entries from the front, slots from wave-aggregated LDS counters (the
-  // order inside a region is free: the finish resolves by composite key and
-  // sorts by index)
+  const int b1 = s_bd[0];
+  const uint32_t k0 = static_cast<uint32_t>(b1) << kHistShift;
   uint2* region = b.hits + static_cast<long>(bh) * d.max_len + c0;
-#pragma unroll
-  for (int u = 0; u < kPerThread; ++u) {
-    const bool valid = i0 + u < length;
-    const uint32_t bin = order_key(v[u]) >> kHistShift;
-    const bool up = valid && bin > b1;
-    const bool bd = valid && bin == b1;
-    if (__ballot(up || bd) == 0ull) continue;
-    const uint2 e = make_uint2(static_cast<uint32_t>(i0 + u), __float_as_uint(v[u]));
-    const int ou = wave_slot(up, &s_cnt[0]);
-    if (up) region[clen - 1 - ou] = e;
-    const int ob = wave_slot(bd, &s_cnt[1]);
-    if (bd) region[ob] = e;
+  int total;
+  if (b1 > kNumBins / 2) {
+    collect_rows<true>(x, p0, length, static_cast<int>(k0 & 0x7fffffffu), 0.f, region, tmp + 8, &total);
+  } else {
+    const float tf = b1 == kNumBins / 2 ? 0.f : (b1 >= 2 ? __uint_as_float(~k0) : kNegInf);
+    collect_rows<false>(x, p0, length, 0, tf, region, tmp + 8, &total);
   }
-  lds_barrier();
-  if (threadIdx.x == 0) b.ccnt[static_cast<long>(bh) * d.n_chunks + chunk] = make_int2(s_cnt[0], s_cnt[1]);
-}
-
-// One work group per (head, chunk); reuse heads return at once.
-__global__ __launch_bounds__(kHeadThreads) void k_collect(Dims d, Bufs b, int length, int nch) {
-  __shared__ int tmp[8];
-  __shared__ int s_b1;
-  __shared__ int s_cnt[2];
-  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;
-  if (!b.path[bh]) return;
-  collect_chunk(d, b, bh, chunk, length, tmp, &s_b1, s_cnt);
+  if (tid == 0) {
+    b.ccnt[static_cast<long>(bh) * d.n_chunks + chunk] = total;
+    if (chunk == 0) *reinterpret_cast<int4*>(b.bnd + 4 * bh) = make_int4(b1, s_bd[1], s_bd[2], 0);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// K4, global Top-K, step 2, for exact heads, then softmax-V and the cache
-// update. The chunks' "above" entries (all selected) and boundary entries are
-// gathered with their scores into LDS. Of the boundary entries the `need`
-// best under (score desc, index asc) are kept: a radix select over the
-// composite keys with per-wave histograms, in LDS when the boundary holds at
-// most kBoundaryLds entries, else read from the hit buffer. One work group
-// per head.
+// K4, global Top-K, step 2, for exact heads, softmax-V and the cache update.
+// One work group per head; reuse heads return at once.
+//  1. The chunks' survivor counts give each chunk's offset in the head's
+//     survivor list (ascending positions: the chunks are in order).
+//  2. Each thread takes kSU consecutive survivors and classifies them: above
+//     b1 (all kept) or in b1 (candidates). The candidates' composite keys
+//     (score desc, index asc) are compacted (LDS, else the global spill row)
+//     and a radix select over the bits below their shared top 10 keeps the
+//     `need` = keff - (count above b1) best.
+//  3. A block scan over "kept" flags writes S_t in ascending index order.
 //
-// LDS (dynamic): A = boundary keys, later word prefix counts (34 KiB);
-// B = bitmap window (34 KiB); C = selected (index, score) pairs, unordered
-// (K); D = S_t indices and scores, ordered (K each); E = chunk offsets.
+// LDS (dynamic): candidate keys (kBoundaryLds), chunk offsets (n_chunks + 1),
+// S_t and its scores (K each).
 // ---------------------------------------------------------------------------
-// Boundary entry g of a head: chunk found by binary search over the offsets.
-__device__ __forceinline__ uint2 boundary_entry(const uint2* hits_row, const int* boff, int nch, int g) {
-  int lo = 0, hi = nch;  // boff[lo] <= g < boff[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (boff[mid] <= g) lo = mid; else hi = mid;
-  }
-  return hits_row[static_cast<long>(lo) * kCollectChunk + (g - boff[lo])];
-}
+constexpr int kSU = 8;  // survivors per thread per round
 
 __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const uint16_t* v, float* out,
                                                          int32_t* sel_out, int length, int push) {
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int nch = (length + kCollectChunk - 1) / kCollectChunk;
-  const int2* ccnt = b.ccnt + static_cast<long>(bh) * d.n_chunks;
-  // one round of loads: FIFO state (before the push updates it), path flag
-  // and this thread's chunk counts
-  const int per = (nch + blockDim.x - 1) / blockDim.x;  // <= 2 (n_chunks <= 1024)
-  const int c0 = min(tid * per, nch), c1 = min(c0 + per, nch);
-  int2 cc[2];
+  // one round of loads: this thread's chunk counts, the boundary record, the
+  // FIFO state (before the push updates it) and the path flag
+  const int per = (nch + kHeadThreads - 1) / kHeadThreads;  // <= 2 (n_chunks <= 1024)
+  const int q0 = min(tid * per, nch), q1 = min(q0 + per, nch);
+  const int32_t* ccnt = b.ccnt + static_cast<long>(bh) * d.n_chunks;
+  int cc[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) cc[i] = c0 + i < c1 ? ccnt[c0 + i] : make_int2(0, 0);
+  for (int i = 0; i < 2; ++i) cc[i] = q0 + i < q1 ? ccnt[q0 + i] : 0;
+  const int4 bd = *reinterpret_cast<const int4*>(b.bnd + 4 * bh);
   const int fifo_slot = b.fifo[2 * bh], fifo_count = b.fifo[2 * bh + 1];
   if (!b.path[bh]) return;
   __shared__ HeadShared sh;
   extern __shared__ __align__(16) unsigned char dyn[];
-  constexpr size_t kRegion = kBitmapLdsWords * 4;                            // >= 4096 64-bit keys
-  static_assert(kRegion >= kBoundaryLds * 8, "boundary keys fit region A");
-  uint64_t* keys = reinterpret_cast<uint64_t*>(dyn);                         // A
-  int32_t* wpre = reinterpret_cast<int32_t*>(dyn);                           // A, later
-  uint32_t* bm = reinterpret_cast<uint32_t*>(dyn + kRegion);                 // B
-  uint2* chosen = reinterpret_cast<uint2*>(dyn + 2 * kRegion);               // C
-  int32_t* s_sel = reinterpret_cast<int32_t*>(dyn + 2 * kRegion + 8 * static_cast<size_t>(d.K));  // D
-  float* s_selsc = reinterpret_cast<float*>(dyn + 2 * kRegion + 12 * static_cast<size_t>(d.K));
-  int* aoff = reinterpret_cast<int*>(dyn + 2 * kRegion + 16 * static_cast<size_t>(d.K));           // E
-  int* boff = aoff + d.n_chunks + 1;
+  uint64_t* lkeys = reinterpret_cast<uint64_t*>(dyn);
+  int* aoff = reinterpret_cast<int*>(dyn + 8 * kBoundaryLds);
+  const size_t off_c = 8 * kBoundaryLds + (4 * (static_cast<size_t>(d.n_chunks) + 1) + 15) / 16 * 16;
+  int32_t* s_sel = reinterpret_cast<int32_t*>(dyn + off_c);
+  float* s_selsc = reinterpret_cast<float*>(dyn + off_c + 4 * static_cast<size_t>(d.K));
   const int keff = min(d.K, length);
+  // (clamped: consistent scores and histogram never need it, but every index below stays in its row)
+  const int b1 = bd.x, n_above = min(max(bd.y, 0), keff - 1), n_bd = min(max(bd.z, 0), length);
+  const bool keys_lds = n_bd <= kBoundaryLds;
+  uint64_t* gkeys = b.bkeys + static_cast<long>(bh) * d.max_len;
   const uint2* hits_row = b.hits + static_cast<long>(bh) * d.max_len;
 
-  // chunk offsets of the above and boundary lists
+  // ---- 1. chunk offsets ----
   {
-    int oa, ob, ta, tb;
-    block_exclusive_scan2(cc[0].x + cc[1].x, cc[0].y + cc[1].y, &oa, &ob, &ta, &tb, sh.tmp);
-    for (int i = 0; i < 2 && c0 + i < c1; ++i) {
-      aoff[c0 + i] = oa;
-      boff[c0 + i] = ob;
-      oa += cc[i].x;
-      ob += cc[i].y;
+    int tot;
+    int o = block_exclusive_scan(cc[0] + cc[1], &tot, sh.tmp);
+    for (int i = 0; i < 2 && q0 + i < q1; ++i) {
+      aoff[q0 + i] = o;
+      o += cc[i];
     }
-    if (tid == 0) {
-      aoff[nch] = ta;
-      boff[nch] = tb;
-      sh.i3 = 0;
-    }
+    if (tid == 0) aoff[nch] = tot;
     lds_barrier();
   }
-  const int na = min(aoff[nch], keff);
-  const int nb = boff[nch];
-  const bool in_lds = nb <= kBoundaryLds;
+  const int ns = aoff[nch];
 
-  // gather: above entries into C, boundary keys into A (8 entries per thread per round)
-  {
-    constexpr int U = 8;
-    const int tot = na + (in_lds ? nb : 0);
-    for (int f0 = 0; f0 < tot; f0 += blockDim.x * U) {
-      uint2 e[U];
+  // ---- 2. classification, candidate keys, radix select ----
+  const int nrounds = (ns + kHeadThreads * kSU - 1) / (kHeadThreads * kSU);
+  int pos[kSU];
+  uint32_t sb[kSU];
+  auto load_round = [&](int rd) {
+    const int i0 = rd * kHeadThreads * kSU + tid * kSU;
+    uint2 e[kSU];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int f = f0 + u * blockDim.x + tid;
-        e[u] = make_uint2(0u, 0u);
-        if (f < na) {
-          int lo = 0, hi = nch;
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (aoff[mid] <= f) lo = mid; else hi = mid;
+    for (int u = 0; u < kSU; ++u) {
+      const int i = i0 + u;
+      e[u] = make_uint2(0xffffffffu, 0u);
+      if (i < ns) {
+        int lo = 0, hi = nch;  // the last chunk whose offset is <= i
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (aoff[mid] <= i) lo = mid; else hi = mid;
+        }
+        e[u] = hits_row[static_cast<long>(lo) * kCollectChunk + (i - aoff[lo])];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSU; ++u) {
+      pos[u] = static_cast<int>(e[u].x);  // -1 past the end
+      sb[u] = e[u].y;
+    }
+  };
+  auto bin_of = [&](int u) { return static_cast<int>(order_key(__uint_as_float(sb[u])) >> kHistShift); };
+  auto in_b1 = [&](int u) { return (pos[u] >= 0) & (bin_of(u) == b1); };
+  auto above = [&](int u) { return (pos[u] >= 0) & (bin_of(u) > b1); };
+
+  // candidate keys, compacted in position order
+  {
+    int krun = 0;
+    for (int rd = 0; rd < nrounds; ++rd) {
+      load_round(rd);
+      int c = 0;
+#pragma unroll
+      for (int u = 0; u < kSU; ++u) c += in_b1(u);
+      int tot;
+      int o = krun + block_exclusive_scan(c, &tot, sh.tmp);
+#pragma unroll
+      for (int u = 0; u < kSU; ++u) {
+        if (in_b1(u)) {
+          const uint64_t key = comp_key(__uint_as_float(sb[u]), static_cast<uint32_t>(pos[u]));
+          if (o < n_bd) {
+            if (keys_lds) lkeys[o] = key;
+            else gkeys[o] = key;
           }
-          const int clen = min(kCollectChunk, length - lo * kCollectChunk);
-          e[u] = hits_row[static_cast<long>(lo) * kCollectChunk + clen - 1 - (f - aoff[lo])];
-        } else if (f < tot) {
-          e[u] = boundary_entry(hits_row, boff, nch, f - na);
+          ++o;
         }
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int f = f0 + u * blockDim.x + tid;
-        if (f < na) chosen[f] = e[u];
-        else if (f < tot) keys[f - na] = comp_key(__uint_as_float(e[u].y), e[u].x);
-      }
+      krun += tot;
     }
   }
   lds_barrier();
-
-  // Radix select of the `need` best boundary entries. They share the top 10
-  // bits of their keys (the boundary bin), so the digits start below them:
-  // 11 bits at a time, 2048 LDS bins.
-  int need = keff - na;
-  int ncand = nb;
-  auto bkey = [&](int i) -> uint64_t {
-    if (in_lds) return keys[i];
-    const uint2 e = boundary_entry(hits_row, boff, nch, i);
-    return comp_key(__uint_as_float(e.y), e.x);
-  };
-  uint64_t mask = 0x3FFull << 54, prefix = 0ull;
-  if (nb > 0) prefix = bkey(0) & mask;
+  // Radix select of the `need` best candidates. Their composite keys share
+  // the top 10 bits (the bin b1), so the digits start below them, 11 bits at
+  // a time: bits 53-43, 42-32 (score), 31-21, 20-10, 9-0 (index).
+  int need = keff - n_above;
+  int ncand = n_bd;
+  auto bkey = [&](int i) -> uint64_t { return keys_lds ? lkeys[i] : gkeys[i]; };
+  uint64_t mask = 0x3FFull << 54, prefix = static_cast<uint64_t>(b1) << 54;
   int* bins = &sh.whist[0][0];
-  // digits: bits 53-43, 42-32 (score), 31-21, 20-10, 9-0 (index)
   for (int shift = 43; ncand > need && need > 0; shift = shift >= 11 ? shift - 11 : 0) {
     const uint64_t dmask = shift == 0 ? 0x3FFull : 0x7FFull;
     reinterpret_cast<int4*>(bins)[tid] = make_int4(0, 0, 0, 0);
     lds_barrier();
-    for (int i = tid; i < nb; i += blockDim.x) {
+    for (int i = tid; i < n_bd; i += blockDim.x) {
       const uint64_t u = bkey(i);
       if ((u & mask) == prefix) atomicAdd(&bins[(u >> shift) & dmask], 1);
     }
@@ -1444,21 +1411,36 @@ __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const u
     ncand = sh.i2;
     if (shift == 0) break;
   }
-  // boundary entries whose masked key is >= prefix are exactly the kept ones
-  if (keff - na > 0) {
-    for (int i0 = 0; i0 < nb; i0 += blockDim.x) {
-      const int i = min(i0 + tid, nb - 1);  // clamped: a repeated entry is never taken twice (t below)
-      const uint64_t u = bkey(i);
-      const bool t = i0 + tid < nb && (u & mask) >= prefix;
-      const int o = wave_slot(t, &sh.i3);
-      if (t && na + o < d.K)
-        chosen[na + o] = make_uint2(0xffffffffu - static_cast<uint32_t>(u & 0xffffffffull), key_score_bits(u));
+
+  // ---- 3. S_t in ascending index order: survivors above b1 and the kept candidates ----
+  int n = 0;
+  for (int rd = 0; rd < nrounds; ++rd) {
+    if (nrounds > 1) load_round(rd);  // one round: still in registers
+    bool keep[kSU];
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < kSU; ++u) {
+      keep[u] = above(u) |
+                (in_b1(u) & ((comp_key(__uint_as_float(sb[u]), static_cast<uint32_t>(pos[u])) & mask) >= prefix));
+      c += keep[u];
     }
+    int tot;
+    int o = n + block_exclusive_scan(c, &tot, sh.tmp);
+#pragma unroll
+    for (int u = 0; u < kSU; ++u) {
+      if (keep[u]) {
+        if (o < d.K) {
+          s_sel[o] = pos[u];
+          s_selsc[o] = __uint_as_float(sb[u]);
+        }
+        ++o;
+      }
+    }
+    n += tot;
   }
+  n = min(n, keff);
   lds_barrier();
-  const int n = min(na + sh.i3, keff);
-  finish_tail(d, b, bh, chosen, n, length, v, out, sel_out, push, fifo_slot, fifo_count, sh, bm, wpre, s_sel,
-              s_selsc);
+  finish_tail(d, b, bh, n, v, out, sel_out, push, fifo_slot, fifo_count, sh, s_sel, s_selsc);
 }
 
 // ---------------------------------------------------------------------------
