@@ -65,8 +65,12 @@ def parse():
     ap.add_argument("--summarize-traffic", metavar="DIR", default=None,
                     help="turn rocprofv3 counter runs under DIR (<leg>_<COUNTER>/ and "
                          "copy_<COUNTER>/) into profiles/traffic.json and exit")
+    ap.add_argument("--summarize-kernels", metavar="DIR", default=None,
+                    help="turn rocprofv3 --kernel-trace --stats runs (DIR/prof_<leg>/) into "
+                         "profiles/kernels_<workload>.md and exit")
     ap.add_argument("--last", type=int, default=64,
-                    help="with --summarize-traffic: dispatches per kernel to average (the last ones)")
+                    help="with --summarize-traffic / --summarize-kernels: dispatches per kernel to "
+                         "average (the last ones, i.e. the timed steps)")
     return ap.parse_args()
 
 
@@ -154,6 +158,67 @@ def summarize_traffic(root, last, workload):
     print(f"copy scale {scale}; wrote {path}")
 
 
+PROFILE_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_{leg} -o {leg} --output-format csv -- "
+               "python3 bench.py --only {leg} --steps {steps} --warmup 64 --no-cpu-baseline --no-breakdown")
+LEG_TITLES = {"natural": "natural ReTopK decode steps (the metric's step)",
+              "exact": "Exact Top-K baseline (retopk_exact_topk_attn, every head exact)",
+              "reuse": "forced reuse (tau = -2, T_r = 0)"}
+
+
+def summarize_kernels(root, last, workload):
+    """Per-kernel durations of the timed dispatches (the last `last` of each
+    library kernel) from rocprofv3 kernel traces, plus the whole-run --stats
+    rows; written to profiles/kernels_<workload>.md."""
+    import csv
+    lines = [f"# Kernel durations, {workload}: rocprofv3 --kernel-trace --stats", "",
+             "Each leg is one run of the command below on one MI355X (from the repository root, after "
+             "`cd /tmp && export TMPDIR=/tmp`, with absolute paths). The first table of a leg averages "
+             f"the last {last} dispatches of each library kernel, which are the timed decode steps; "
+             "the second is rocprofv3's own --stats summary of the whole run (it also counts the cache "
+             "initialisation and warm-up dispatches). Summarised by "
+             f"`python3 bench.py --summarize-kernels gpurun_out --last {last}`.", ""]
+    for leg in ("natural", "exact", "reuse"):
+        d = os.path.join(root, f"prof_{leg}")
+        trace = os.path.join(d, f"{leg}_kernel_trace.csv")
+        stats = os.path.join(d, f"{leg}_kernel_stats.csv")
+        if not os.path.exists(trace):
+            continue
+        with open(trace) as f:
+            rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+        per = {}
+        for r in rows:
+            name = r["Kernel_Name"].split("(")[0].split("::")[-1].strip()
+            per.setdefault(name, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+        lines += [f"## {leg}: {LEG_TITLES[leg]}", "", "```", PROFILE_CMD.format(leg=leg, steps=last), "```", "",
+                  f"Timed dispatches (last {last} of each kernel):", "",
+                  "| kernel | dispatches | avg µs | median µs | min µs | max µs |", "|---|---|---|---|---|---|"]
+        for name in sorted(k for k in per if k.startswith("k_") and k != "k_reset"):
+            dur = np.array([(e - s) / 1000.0 for s, e in per[name][-last:]])
+            lines.append(f"| {name} | {len(dur)} | {dur.mean():.2f} | {np.median(dur):.2f} | {dur.min():.2f} | "
+                         f"{dur.max():.2f} |")
+        if "k_head" in per:
+            st = np.array([s for s, _ in per["k_head"][-last:]], dtype=np.float64)
+            gap = np.diff(st) / 1000.0
+            lines += ["", f"Step period under the tracer (k_head start to the next k_head start): median "
+                          f"{np.median(gap):.2f} µs, mean {gap.mean():.2f} µs (the tracer serialises "
+                          "dispatches, so this is longer than the untraced step)."]
+        if os.path.exists(stats):
+            with open(stats) as f:
+                srows = list(csv.DictReader(f))
+            lines += ["", "rocprofv3 --stats (whole run):", "",
+                      "| kernel | calls | avg µs | min µs | max µs | total % |", "|---|---|---|---|---|---|"]
+            for r in srows:
+                name = r["Name"].split("(")[0].split("::")[-1].strip()
+                lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1000:.2f} | "
+                             f"{float(r['MinNs']) / 1000:.2f} | {float(r['MaxNs']) / 1000:.2f} | "
+                             f"{float(r['Percentage']):.1f} |")
+        lines.append("")
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"wrote {path}")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     with open(os.path.join(ROOT, "sparse_long_context_head_amd", "csrc", "retopk_kernels.hip"), "rb") as f:
@@ -180,6 +245,9 @@ def main():
     args = parse()
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic, args.last, args.workload)
+        return
+    if args.summarize_kernels:
+        summarize_kernels(args.summarize_kernels, args.last, args.workload)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path has no "
