@@ -362,8 +362,8 @@ def main():
         are not. k_head: every head's query and C cached normalised queries; a
         reusing head's R supports, M_t key rows, min(K, M_t) value rows, its
         output and cache entry. k_score: every key row of a KV group holding
-        an exact head. k_collect: nothing (it reads and writes workspaces).
-        k_finish: an exact head's K value rows, output and cache entry."""
+        an exact head. k_tail: an exact head's K value rows, output and cache
+        entry."""
         d, K, C, R = wl.head_dim, wl.top_k, wl.cache_cap, wl.top_r
         T = path.shape[0]
         exact = (path & 1) == 1
@@ -375,8 +375,7 @@ def main():
             "k_head": (2 * d + 4 * C * d
                        + reuse * (4 * R * K + ROW_BYTES * (m + n) + 4 * d + entry)).sum(),
             "k_score": gex.sum() * ROW_BYTES * length,
-            "k_collect": 0.0,
-            "k_finish": (exact * (ROW_BYTES * min(K, length) + 4 * d + entry)).sum(),
+            "k_tail": (exact * (ROW_BYTES * min(K, length) + 4 * d + entry)).sum(),
         }
         return {k: float(v) / T for k, v in per.items()}
 

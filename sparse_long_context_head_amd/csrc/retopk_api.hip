@@ -220,6 +220,7 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   A(&b.hits, BH * d.max_len);
   A(&b.ccnt, BH * d.n_chunks);
   A(&b.bnd, BH * 4);
+  A(&b.tailcnt, BH);
   A(&b.bkeys, BH * d.max_len);
   A(&b.sel, BH * d.K);
   A(&b.selsc, BH * d.K);
@@ -271,9 +272,8 @@ retopk_status retopk_init_from_prefill(retopk_handle* h, const uint16_t* q_tail,
       return launch_head(d, b, qi, q_sb, q_sh, nullptr, nullptr, nullptr, len, 0, kModeExact, -1, s);
     });
     if (st == RETOPK_OK) st = h->run(kKScore, s, [&] { return launch_score(d, b, qi, q_sb, q_sh, k, len, s); });
-    if (st == RETOPK_OK) st = h->run(kKCollect, s, [&] { return launch_collect(d, b, len, s); });
     if (st == RETOPK_OK)
-      st = h->run(kKFinish, s, [&] { return launch_finish(d, b, nullptr, nullptr, nullptr, len, 1, s); });
+      st = h->run(kKTail, s, [&] { return launch_tail(d, b, nullptr, nullptr, nullptr, len, 1, s); });
   }
   return st;
 }
@@ -299,8 +299,7 @@ retopk_status retopk_decode_step(retopk_handle* h, const uint16_t* q, const uint
     return launch_head(d, b, q, q_sb, q_sh, k, v, out, length, t_dec, kModeDecode, slot, s);
   });
   if (st == RETOPK_OK) st = h->run(kKScore, s, [&] { return launch_score(d, b, q, q_sb, q_sh, k, length, s); });
-  if (st == RETOPK_OK) st = h->run(kKCollect, s, [&] { return launch_collect(d, b, length, s); });
-  if (st == RETOPK_OK) st = h->run(kKFinish, s, [&] { return launch_finish(d, b, v, out, nullptr, length, 1, s); });
+  if (st == RETOPK_OK) st = h->run(kKTail, s, [&] { return launch_tail(d, b, v, out, nullptr, length, 1, s); });
   return st;
 }
 
@@ -324,8 +323,7 @@ retopk_status retopk_exact_topk_attn(retopk_handle* h, const uint16_t* q, const 
     return launch_head(d, b, q, q_sb, q_sh, nullptr, nullptr, nullptr, length, 0, kModeExact, -1, s);
   });
   if (st == RETOPK_OK) st = h->run(kKScore, s, [&] { return launch_score(d, b, q, q_sb, q_sh, k, length, s); });
-  if (st == RETOPK_OK) st = h->run(kKCollect, s, [&] { return launch_collect(d, b, length, s); });
-  if (st == RETOPK_OK) st = h->run(kKFinish, s, [&] { return launch_finish(d, b, v, out, sel_out, length, 0, s); });
+  if (st == RETOPK_OK) st = h->run(kKTail, s, [&] { return launch_tail(d, b, v, out, sel_out, length, 0, s); });
   return st;
 }
 

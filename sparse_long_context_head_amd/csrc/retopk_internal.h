@@ -59,6 +59,7 @@ struct Bufs {
                            //   in its own region, in ascending position order
   int32_t* ccnt;           // [BH, n_chunks] survivors per chunk
   int32_t* bnd;            // [BH, 4] boundary bin, count above it, count in it
+  int32_t* tailcnt;        // [BH] collect work groups done (zero between calls)
   uint64_t* bkeys;         // [BH, max_len] boundary-bin composite keys when more than kBoundaryLds
   int32_t* sel;            // [BH, K]   S_hat_t ascending
   float* selsc;            // [BH, K]   q.k of S_hat_t
@@ -69,7 +70,7 @@ struct Bufs {
   int32_t* st_m;           // [kStatsCap, BH]
 };
 
-enum KernelId : int { kKHead = 0, kKScore, kKCollect, kKFinish, kKReset, kNumKernels };
+enum KernelId : int { kKHead = 0, kKScore, kKTail, kKReset, kNumKernels };
 
 const char* kernel_name(int id);
 
@@ -82,7 +83,7 @@ int score_grid(const Dims& d, int length);
 
 // Launch helpers (retopk_kernels.hip). Each returns the hipError_t of the
 // launch. A decode step, the exact Top-K baseline and the cache
-// initialisation are each head -> score -> collect -> finish on one stream.
+// initialisation are each head -> score -> tail on one stream.
 enum HeadMode : int { kModeDecode = 0, kModeExact = 1 };
 
 // Raise the dynamic-LDS limit of the kernels to what `d` needs.
@@ -97,11 +98,9 @@ hipError_t launch_head(const Dims& d, const Bufs& b, const uint16_t* q, long q_s
 // Full-history scores and histogram of exact heads.
 hipError_t launch_score(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
                         const uint16_t* k, int length, hipStream_t s);
-// Exact heads, global Top-K step 1: boundary bin and survivors.
-hipError_t launch_collect(const Dims& d, const Bufs& b, int length, hipStream_t s);
-// Exact heads, global Top-K step 2, softmax-V (skipped when v or out is NULL),
+// Exact heads: global Top-K, softmax-V (skipped when v or out is NULL),
 // S_t to sel_out (when not NULL) and the cache update (when push).
-hipError_t launch_finish(const Dims& d, const Bufs& b, const uint16_t* v, float* out, int32_t* sel_out,
-                         int length, int push, hipStream_t s);
+hipError_t launch_tail(const Dims& d, const Bufs& b, const uint16_t* v, float* out, int32_t* sel_out, int length,
+                       int push, hipStream_t s);
 
 }  // namespace retopk

@@ -2,10 +2,11 @@
 //
 // Method: "Recall Before You Rank: Similarity-Guided Top-K Reuse for
 // Efficient Long-Context Attention", Methodology section. A decode step is
-// four launches on one stream; a kernel boundary is the only point where
-// data passes between work groups (an in-kernel handoff across work groups
-// costs more than a launch on this part, because a device-scope release or
-// acquire writes back or invalidates a whole L2):
+// three launches on one stream. Data passes between work groups at kernel
+// boundaries, and once inside k_tail, where the last collect work group of an
+// exact head takes over its survivors (a device-scope release or acquire
+// writes back or invalidates a whole L2, so such hand-offs are kept to the
+// exact heads, where they replace a launch):
 //
 //   k_head     one work group per query head: recall (Eqs. 5-7) and the path
 //              rule (Eq. 13); a reuse head runs its whole path in the same
@@ -15,13 +16,13 @@
 //   k_score    full-history scores (Eq. 4) and a score histogram of every
 //              exact head, GQA-grouped on MFMA, the rows of the exact KV groups
 //              spread over the whole grid;
-//   k_collect  global Top-K (Eq. 1) step 1: the boundary bin of the score
-//              histogram and the scores in it or above it, in position
-//              order, many work groups per exact head;
-//   k_finish   global Top-K step 2 (a radix select inside the boundary bin),
-//              softmax-V and the cache update, one work group per exact head.
+//   k_tail     global Top-K (Eq. 1): many work groups per exact head collect
+//              the scores in the histogram's boundary bin or above it, in
+//              position order; the last one of a head to finish collecting
+//              selects inside the boundary bin, then runs softmax-V and the
+//              cache update.
 //
-// The exact Top-K baseline and the cache initialisation are the same four
+// The exact Top-K baseline and the cache initialisation are the same three
 // kernels with every head marked exact. The path flag stays on the device:
 // each kernel reads it and work of the other path returns at once, so the
 // host never waits. Every phase issues its global loads before consuming
@@ -1158,8 +1159,8 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh
 }
 
 // ---------------------------------------------------------------------------
-// K3, global Top-K (Eq. 1), step 1, for exact heads. One work group per (head,
-// chunk of kCollectChunk positions); reuse heads return at once. Every work
+// Global Top-K (Eq. 1), step 1 (collect), one work group per (exact head,
+// chunk of kCollectChunk positions). Every work
 // group finds the boundary bin b1 (the bin holding the K-th largest score)
 // from the head's histogram copies, then writes the chunk's "survivors"
 // (scores in b1 or above) as (position, score bits), in ascending position
@@ -1182,6 +1183,26 @@ static_assert(kCollectRows * 64 * (kHeadThreads / 64) == kCollectChunk, "collect
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// Data handed from one work group to another inside k_tail goes through
+// device-scope (sc1) stores and loads, which are coherent across the XCDs'
+// L2s on their own; the hand-off then needs only the stores to be complete
+// before the counter is bumped, not a whole-L2 write-back and invalidate.
+__device__ __forceinline__ void store_shared(uint2* p, uint2 v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                     (static_cast<unsigned long long>(v.y) << 32) | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_shared(int32_t* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint2 load_shared(const uint2* p) {
+  const unsigned long long u = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint2(static_cast<uint32_t>(u), static_cast<uint32_t>(u >> 32));
+}
+__device__ __forceinline__ int load_shared(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Both passes over a wave's rows; kInt selects the survivor compare.
@@ -1211,16 +1232,16 @@ __device__ __forceinline__ void collect_rows(const float (&x)[kCollectRows], int
   for (int u = 0; u < kCollectRows; ++u) {
     const bool s = survives(u);
     const uint64_t m = __ballot(s);
-    if (s) region[base + lanes_below(m)] = make_uint2(static_cast<uint32_t>(p0 + 64 * u), __float_as_uint(x[u]));
+    if (s)
+      store_shared(region + base + lanes_below(m),
+                   make_uint2(static_cast<uint32_t>(p0 + 64 * u), __float_as_uint(x[u])));
     base += __popcll(m);
   }
 }
 
-__global__ __launch_bounds__(kHeadThreads) void k_collect(Dims d, Bufs b, int length, int nch) {
-  __shared__ int tmp[16];
-  __shared__ int s_bd[3];
-  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;
-  if (!b.path[bh]) return;
+// tmp: 16 ints, s_bd: 3 ints of LDS. Every thread of the block must call it.
+__device__ __forceinline__ void collect_phase(const Dims& d, const Bufs& b, int bh, int chunk, int length, int* tmp,
+                                              int* s_bd) {
   const int tid = threadIdx.x, wave = tid >> 6;
   const int keff = min(d.K, length);
   const float* srow = b.score + static_cast<long>(bh) * d.score_stride;
@@ -1267,14 +1288,18 @@ __global__ __launch_bounds__(kHeadThreads) void k_collect(Dims d, Bufs b, int le
     collect_rows<false>(x, p0, length, 0, tf, region, tmp + 8, &total);
   }
   if (tid == 0) {
-    b.ccnt[static_cast<long>(bh) * d.n_chunks + chunk] = total;
-    if (chunk == 0) *reinterpret_cast<int4*>(b.bnd + 4 * bh) = make_int4(b1, s_bd[1], s_bd[2], 0);
+    store_shared(b.ccnt + static_cast<long>(bh) * d.n_chunks + chunk, total);
+    if (chunk == 0) {
+      store_shared(b.bnd + 4 * bh, b1);
+      store_shared(b.bnd + 4 * bh + 1, s_bd[1]);
+      store_shared(b.bnd + 4 * bh + 2, s_bd[2]);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// K4, global Top-K, step 2, for exact heads, softmax-V and the cache update.
-// One work group per head; reuse heads return at once.
+// Global Top-K, step 2 (finish), softmax-V and the cache update, run by the
+// last collect work group of an exact head.
 //  1. The chunks' survivor counts give each chunk's offset in the head's
 //     survivor list (ascending positions: the chunks are in order).
 //  2. Each thread takes kSU consecutive survivors and classifies them: above
@@ -1289,24 +1314,22 @@ __global__ __launch_bounds__(kHeadThreads) void k_collect(Dims d, Bufs b, int le
 // ---------------------------------------------------------------------------
 constexpr int kSU = 8;  // survivors per thread per round
 
-__global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const uint16_t* v, float* out,
-                                                         int32_t* sel_out, int length, int push) {
-  const int bh = blockIdx.x;
+// fifo_slot / fifo_count: the FIFO state read before any push. Every thread of
+// the block must call it.
+__device__ __forceinline__ void finish_phase(const Dims& d, const Bufs& b, int bh, const uint16_t* v, float* out,
+                                             int32_t* sel_out, int length, int push, int fifo_slot, int fifo_count,
+                                             HeadShared& sh, unsigned char* dyn) {
   const int tid = threadIdx.x;
   const int nch = (length + kCollectChunk - 1) / kCollectChunk;
-  // one round of loads: this thread's chunk counts, the boundary record, the
-  // FIFO state (before the push updates it) and the path flag
+  // one round of loads: this thread's chunk counts and the boundary record
   const int per = (nch + kHeadThreads - 1) / kHeadThreads;  // <= 2 (n_chunks <= 1024)
   const int q0 = min(tid * per, nch), q1 = min(q0 + per, nch);
   const int32_t* ccnt = b.ccnt + static_cast<long>(bh) * d.n_chunks;
   int cc[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) cc[i] = q0 + i < q1 ? ccnt[q0 + i] : 0;
-  const int4 bd = *reinterpret_cast<const int4*>(b.bnd + 4 * bh);
-  const int fifo_slot = b.fifo[2 * bh], fifo_count = b.fifo[2 * bh + 1];
-  if (!b.path[bh]) return;
-  __shared__ HeadShared sh;
-  extern __shared__ __align__(16) unsigned char dyn[];
+  for (int i = 0; i < 2; ++i) cc[i] = q0 + i < q1 ? load_shared(ccnt + q0 + i) : 0;
+  const int4 bd = make_int4(load_shared(b.bnd + 4 * bh), load_shared(b.bnd + 4 * bh + 1),
+                            load_shared(b.bnd + 4 * bh + 2), 0);
   uint64_t* lkeys = reinterpret_cast<uint64_t*>(dyn);
   int* aoff = reinterpret_cast<int*>(dyn + 8 * kBoundaryLds);
   const size_t off_c = 8 * kBoundaryLds + (4 * (static_cast<size_t>(d.n_chunks) + 1) + 15) / 16 * 16;
@@ -1349,7 +1372,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const u
           const int mid = (lo + hi) >> 1;
           if (aoff[mid] <= i) lo = mid; else hi = mid;
         }
-        e[u] = hits_row[static_cast<long>(lo) * kCollectChunk + (i - aoff[lo])];
+        e[u] = load_shared(hits_row + static_cast<long>(lo) * kCollectChunk + (i - aoff[lo]));
       }
     }
 #pragma unroll
@@ -1444,6 +1467,36 @@ __global__ __launch_bounds__(kHeadThreads) void k_finish(Dims d, Bufs b, const u
 }
 
 // ---------------------------------------------------------------------------
+// K3, the exact heads' global Top-K, softmax-V and cache update in one launch:
+// one work group per (head, chunk); reuse heads return at once. Each work group
+// collects its chunk's survivors with device-scope stores, waits until they
+// are complete and counts itself in on the head's counter; the work group that
+// arrives last reads every chunk's survivors with device-scope loads, finishes
+// the head and resets the counter for the next call. No wave waits on another
+// work group.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kHeadThreads) void k_tail(Dims d, Bufs b, const uint16_t* v, float* out,
+                                                       int32_t* sel_out, int length, int push, int nch) {
+  __shared__ int tmp[16];
+  __shared__ int s_bd[3];
+  __shared__ int s_last;
+  __shared__ HeadShared sh;
+  extern __shared__ __align__(16) unsigned char dyn[];
+  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;
+  const int fifo_slot = b.fifo[2 * bh], fifo_count = b.fifo[2 * bh + 1];  // written only by the finish below
+  if (!b.path[bh]) return;
+  collect_phase(d, b, bh, chunk, length, tmp, s_bd);
+  __syncthreads();  // every wave's (device-scope) survivor and count stores are complete
+  if (threadIdx.x == 0) {
+    s_last = atomicAdd(&b.tailcnt[bh], 1) == nch - 1;
+    if (s_last) b.tailcnt[bh] = 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  finish_phase(d, b, bh, v, out, sel_out, length, push, fifo_slot, fifo_count, sh, dyn);
+}
+
+// ---------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------
 hipError_t configure_kernels(const Dims& d) {
@@ -1454,13 +1507,13 @@ hipError_t configure_kernels(const Dims& d) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(score_lds_bytes(d)));
   if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_finish), hipFuncAttributeMaxDynamicSharedMemorySize,
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tail), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(finish_lds_bytes(d)));
   return e;
 }
 
 const char* kernel_name(int id) {
-  static const char* names[kNumKernels] = {"k_head", "k_score", "k_collect", "k_finish", "k_reset"};
+  static const char* names[kNumKernels] = {"k_head", "k_score", "k_tail", "k_reset"};
   return (id >= 0 && id < kNumKernels) ? names[id] : "";
 }
 
@@ -1485,16 +1538,11 @@ hipError_t launch_score(const Dims& d, const Bufs& b, const uint16_t* q, long q_
   return hipGetLastError();
 }
 
-hipError_t launch_collect(const Dims& d, const Bufs& b, int length, hipStream_t s) {
+hipError_t launch_tail(const Dims& d, const Bufs& b, const uint16_t* v, float* out, int32_t* sel_out, int length,
+                       int push, hipStream_t s) {
   const int nch = (length + kCollectChunk - 1) / kCollectChunk;
-  hipLaunchKernelGGL(k_collect, dim3(d.B * d.Hq * nch), dim3(kHeadThreads), 0, s, d, b, length, nch);
-  return hipGetLastError();
-}
-
-hipError_t launch_finish(const Dims& d, const Bufs& b, const uint16_t* v, float* out, int32_t* sel_out,
-                         int length, int push, hipStream_t s) {
-  hipLaunchKernelGGL(k_finish, dim3(d.B * d.Hq), dim3(kHeadThreads), finish_lds_bytes(d), s, d, b, v, out,
-                     sel_out, length, push);
+  hipLaunchKernelGGL(k_tail, dim3(d.B * d.Hq * nch), dim3(kHeadThreads), finish_lds_bytes(d), s, d, b, v, out,
+                     sel_out, length, push, nch);
   return hipGetLastError();
 }
 
