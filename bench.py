@@ -196,10 +196,10 @@ def summarize_kernels(root, last, workload):
             dur = np.array([(e - s) / 1000.0 for s, e in per[name][-last:]])
             lines.append(f"| {name} | {len(dur)} | {dur.mean():.2f} | {np.median(dur):.2f} | {dur.min():.2f} | "
                          f"{dur.max():.2f} |")
-        if "k_head" in per:
-            st = np.array([s for s, _ in per["k_head"][-last:]], dtype=np.float64)
+        if "k_step" in per:
+            st = np.array([s for s, _ in per["k_step"][-last:]], dtype=np.float64)
             gap = np.diff(st) / 1000.0
-            lines += ["", f"Step period under the tracer (k_head start to the next k_head start): median "
+            lines += ["", f"Step period under the tracer (k_step start to the next k_step start): median "
                           f"{np.median(gap):.2f} µs, mean {gap.mean():.2f} µs (the tracer serialises "
                           "dispatches, so this is longer than the untraced step)."]
         if os.path.exists(stats):
@@ -359,11 +359,10 @@ def main():
         the statistics ring). Only what the method must move is counted:
         queries, the q_bar cache, the retrieved supports, key and value rows,
         outputs and cache entries; candidate, score and histogram workspaces
-        are not. k_head: every head's query and C cached normalised queries; a
+        are not. k_step: every head's query and C cached normalised queries; a
         reusing head's R supports, M_t key rows, min(K, M_t) value rows, its
-        output and cache entry. k_score: every key row of a KV group holding
-        an exact head. k_tail: an exact head's K value rows, output and cache
-        entry."""
+        output and cache entry; every key row of a KV group holding an exact
+        head. k_tail: an exact head's K value rows, output and cache entry."""
         d, K, C, R = wl.head_dim, wl.top_k, wl.cache_cap, wl.top_r
         T = path.shape[0]
         exact = (path & 1) == 1
@@ -372,9 +371,9 @@ def main():
         n = np.minimum(K, m)
         entry = 4 * d + 4 * K
         per = {
-            "k_head": (2 * d + 4 * C * d
-                       + reuse * (4 * R * K + ROW_BYTES * (m + n) + 4 * d + entry)).sum(),
-            "k_score": gex.sum() * ROW_BYTES * length,
+            "k_step": (2 * d + 4 * C * d
+                       + reuse * (4 * R * K + ROW_BYTES * (m + n) + 4 * d + entry)).sum()
+                      + gex.sum() * ROW_BYTES * length,
             "k_tail": (exact * (ROW_BYTES * min(K, length) + 4 * d + entry)).sum(),
         }
         return {k: float(v) / T for k, v in per.items()}
@@ -462,12 +461,13 @@ def main():
             result["kernels_exact"] = kb
             for layer in ex:
                 layer.close()
-            # the score kernel on all-exact steps: every KV group's key rows once
-            kq = kb.get("k_score")
+            # the head + score kernel on all-exact steps: every KV group's key rows
+            # once and every head's query (exact heads skip recall)
+            kq = kb.get("k_step")
             if kq:
                 alg = ROW_BYTES * mean_len * wl.batch * wl.n_kv_heads \
                     + 2 * wl.batch * wl.n_q_heads * wl.head_dim
-                result["roofline_exact_score"] = roofline("k_score", alg, kq["us_per_launch"],
+                result["roofline_exact_score"] = roofline("k_step", alg, kq["us_per_launch"],
                                                           "exact")
         if "value" in result:
             result["speedup_vs_exact"] = round(us_ex / result["value"], 3)

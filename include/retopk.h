@@ -190,6 +190,14 @@ const char* retopk_kernel_name(int32_t id);
 /* Bytes of device memory the handle holds. */
 size_t retopk_device_bytes(const retopk_handle* h);
 
+/* Sticky device error word of the handle: 0 when every call since the last
+ * read completed its work; 1 when a score work group of some call gave up
+ * waiting (several milliseconds) for the path decisions of that call's head
+ * work groups, in which case that call's exact heads were not scored and its
+ * results are not valid. Synchronises the device, writes the word to *word
+ * and clears it. */
+retopk_status retopk_read_device_error(retopk_handle* h, int32_t* word);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,7 @@ _SIGNATURES = {
     "retopk_kernel_count": (_I32, []),
     "retopk_kernel_name": (ctypes.c_char_p, [_I32]),
     "retopk_device_bytes": (ctypes.c_size_t, [_P]),
+    "retopk_read_device_error": (ctypes.c_int, [_P, _P]),
 }
 
 _lib = None
@@ -260,6 +261,12 @@ def retopk_read_kernel_times(h: Handle) -> dict:
 
 def retopk_device_bytes(h: Handle) -> int:
     return int(load_library().retopk_device_bytes(h.ptr))
+
+
+def retopk_read_device_error(h: Handle) -> int:
+    word = np.zeros(1, np.int32)
+    _check(load_library().retopk_read_device_error(h.ptr, _ptr(word)))
+    return int(word[0])
 
 
 def bf16_tensor(bits: np.ndarray, device="cuda"):

@@ -59,6 +59,12 @@ struct retopk_handle {
   std::vector<hipEvent_t> events;   // pairs (start, stop)
   std::vector<int> event_kernel;    // kernel id of each recorded pair
   int timed = 0;                    // pairs recorded since the last read
+  int call_flag = 0;                // tag of the last k_step's decision flags (even; the buffer starts at 0)
+
+  int next_call_flag() {
+    call_flag = call_flag + 2 < (1 << 30) ? call_flag + 2 : 2;
+    return call_flag;
+  }
 
   template <typename T>
   hipError_t alloc(T** ptr, size_t count) {
@@ -128,6 +134,17 @@ const char* retopk_kernel_name(int32_t id) { return kernel_name(id); }
 
 size_t retopk_device_bytes(const retopk_handle* h) { return h ? h->bytes : 0; }
 
+retopk_status retopk_read_device_error(retopk_handle* h, int32_t* word) {
+  if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_read_device_error: NULL handle");
+  if (word == nullptr) return fail(RETOPK_INVALID_ARG, "retopk_read_device_error: NULL output");
+  DeviceGuard guard(h->device);
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(word, h->b.err, sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemset(h->b.err, 0, sizeof(int32_t));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  return e == hipSuccess ? RETOPK_OK : hip_fail(e, "retopk_read_device_error");
+}
+
 retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   if (out == nullptr) return fail(RETOPK_INVALID_ARG, "retopk_create: out is NULL");
   *out = nullptr;
@@ -176,6 +193,9 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(RETOPK_NO_DEVICE, "retopk_create: hipGetDevice failed");
+  int n_cu = 0;
+  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+    return fail(RETOPK_NO_DEVICE, "retopk_create: cannot read the compute unit count");
 
   auto* h = new (std::nothrow) retopk_handle();
   if (h == nullptr) return fail(RETOPK_HIP_ERROR, "retopk_create: out of host memory");
@@ -195,6 +215,7 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   d.Tr = p.refresh_every;
   d.cand_cap = static_cast<int>(cand);
   d.n_chunks = (p.max_len + kCollectChunk - 1) / kCollectChunk;
+  d.n_cu = n_cu;
   d.tau = p.tau;
 
   Bufs& b = h->b;
@@ -221,6 +242,8 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   A(&b.ccnt, BH * d.n_chunks);
   A(&b.bnd, BH * 4);
   A(&b.tailcnt, BH);
+  A(&b.dec, BH);
+  A(&b.err, 1);
   A(&b.bkeys, BH * d.max_len);
   A(&b.sel, BH * d.K);
   A(&b.selsc, BH * d.K);
@@ -268,10 +291,10 @@ retopk_status retopk_init_from_prefill(retopk_handle* h, const uint16_t* q_tail,
   for (int i = 0; i < n0 && st == RETOPK_OK; ++i) {
     const int len = prompt_len - n0 + i + 1;  // causal: keys 0 .. p
     const uint16_t* qi = q_tail + static_cast<long>(i) * kHeadDim;
-    st = h->run(kKHead, s, [&] {
-      return launch_head(d, b, qi, q_sb, q_sh, nullptr, nullptr, nullptr, len, 0, kModeExact, -1, s);
+    const int flag = h->next_call_flag();
+    st = h->run(kKStep, s, [&] {
+      return launch_step(d, b, qi, q_sb, q_sh, k, nullptr, nullptr, len, 0, kModeExact, -1, flag, s);
     });
-    if (st == RETOPK_OK) st = h->run(kKScore, s, [&] { return launch_score(d, b, qi, q_sb, q_sh, k, len, s); });
     if (st == RETOPK_OK)
       st = h->run(kKTail, s, [&] { return launch_tail(d, b, nullptr, nullptr, nullptr, len, 1, s); });
   }
@@ -295,10 +318,10 @@ retopk_status retopk_decode_step(retopk_handle* h, const uint16_t* q, const uint
   auto s = static_cast<hipStream_t>(stream);
   const int slot = h->stats ? (t_dec - 1) % kStatsCap : -1;
   const long q_sb = static_cast<long>(d.Hq) * kHeadDim, q_sh = kHeadDim;
-  retopk_status st = h->run(kKHead, s, [&] {
-    return launch_head(d, b, q, q_sb, q_sh, k, v, out, length, t_dec, kModeDecode, slot, s);
+  const int flag = h->next_call_flag();
+  retopk_status st = h->run(kKStep, s, [&] {
+    return launch_step(d, b, q, q_sb, q_sh, k, v, out, length, t_dec, kModeDecode, slot, flag, s);
   });
-  if (st == RETOPK_OK) st = h->run(kKScore, s, [&] { return launch_score(d, b, q, q_sb, q_sh, k, length, s); });
   if (st == RETOPK_OK) st = h->run(kKTail, s, [&] { return launch_tail(d, b, v, out, nullptr, length, 1, s); });
   return st;
 }
@@ -319,10 +342,10 @@ retopk_status retopk_exact_topk_attn(retopk_handle* h, const uint16_t* q, const 
   const Bufs& b = h->b;
   auto s = static_cast<hipStream_t>(stream);
   const long q_sb = static_cast<long>(d.Hq) * kHeadDim, q_sh = kHeadDim;
-  retopk_status st = h->run(kKHead, s, [&] {
-    return launch_head(d, b, q, q_sb, q_sh, nullptr, nullptr, nullptr, length, 0, kModeExact, -1, s);
+  const int flag = h->next_call_flag();
+  retopk_status st = h->run(kKStep, s, [&] {
+    return launch_step(d, b, q, q_sb, q_sh, k, nullptr, nullptr, length, 0, kModeExact, -1, flag, s);
   });
-  if (st == RETOPK_OK) st = h->run(kKScore, s, [&] { return launch_score(d, b, q, q_sb, q_sh, k, length, s); });
   if (st == RETOPK_OK) st = h->run(kKTail, s, [&] { return launch_tail(d, b, v, out, sel_out, length, 0, s); });
   return st;
 }

@@ -16,14 +16,13 @@ constexpr int kHistBits = 10;        // first-level histogram: top 10 bits of th
 constexpr int kNumBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
 constexpr int kStatsCap = 4096;      // decode steps kept in the statistics ring
-constexpr int kExactWGTarget = 512;  // work groups of the full-history score kernel (2 per CU)
-constexpr int kExactMinRows = 1024;  // ... with about this many key rows each, at least
+constexpr int kExactMinRows = 2048;  // key rows per score work group of the full-history pass, at least
 constexpr int kHistSeg = 8;          // copies of each head's histogram (spreads the atomics)
 constexpr int kBoundaryLds = 4096;   // boundary-bin candidates resolved in LDS (32 KiB of 64-bit keys)
 constexpr int kCollectChunk = 16384; // positions per work group of the collect step
 constexpr int kHeadThreads = 512;    // threads of the per-head kernels
 constexpr int kBitmapWords = 8192;   // LDS bitmap window: 262144 token positions (32 KiB)
-constexpr int kLdsLimit = 128 * 1024;  // dynamic LDS a per-head kernel may use (static LDS <= 32 KiB)
+constexpr int kLdsLimit = 124 * 1024;  // dynamic LDS a per-head kernel may use (static LDS <= 36 KiB)
 constexpr int kMaxCand = 16384;      // R*K + W limit (candidate keys kept in LDS for reranking)
 
 // Problem dimensions, passed by value to every kernel.
@@ -34,6 +33,7 @@ struct Dims {
   int K, C, W, R, Tr;
   int cand_cap;            // R*K + W
   int n_chunks;            // ceil(max_len / kCollectChunk)
+  int n_cu;                // compute units of the device
   double tau;
 };
 
@@ -60,6 +60,9 @@ struct Bufs {
   int32_t* ccnt;           // [BH, n_chunks] survivors per chunk
   int32_t* bnd;            // [BH, 4] boundary bin, count above it, count in it
   int32_t* tailcnt;        // [BH] collect work groups done (zero between calls)
+                           // (hist is zero between calls too: the tail clears an exact head's copies)
+  int32_t* dec;            // [BH] path decision of the current call: call flag | exact
+  int32_t* err;            // [1]  sticky device error word (1: a score work group timed out)
   uint64_t* bkeys;         // [BH, max_len] boundary-bin composite keys when more than kBoundaryLds
   int32_t* sel;            // [BH, K]   S_hat_t ascending
   float* selsc;            // [BH, K]   q.k of S_hat_t
@@ -70,34 +73,34 @@ struct Bufs {
   int32_t* st_m;           // [kStatsCap, BH]
 };
 
-enum KernelId : int { kKHead = 0, kKScore, kKTail, kKReset, kNumKernels };
+enum KernelId : int { kKStep = 0, kKTail, kKReset, kNumKernels };
 
 const char* kernel_name(int id);
 
 // Dynamic LDS of the kernels for the given dimensions.
 size_t head_lds_bytes(const Dims& d);
 size_t score_lds_bytes(const Dims& d);
+size_t step_lds_bytes(const Dims& d);
 size_t finish_lds_bytes(const Dims& d);
 // Grid of the full-history score kernel at this length.
 int score_grid(const Dims& d, int length);
 
 // Launch helpers (retopk_kernels.hip). Each returns the hipError_t of the
 // launch. A decode step, the exact Top-K baseline and the cache
-// initialisation are each head -> score -> tail on one stream.
+// initialisation are each step -> tail on one stream.
 enum HeadMode : int { kModeDecode = 0, kModeExact = 1 };
 
 // Raise the dynamic-LDS limit of the kernels to what `d` needs.
 hipError_t configure_kernels(const Dims& d);
 hipError_t launch_reset(const Dims& d, const Bufs& b, hipStream_t s);
 // Recall, path decision and the reuse path of reuse heads (k, v, out are
-// used by reuse heads only). In kModeExact every head is marked exact (no
-// recall).
-hipError_t launch_head(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh, const uint16_t* k,
-                       const uint16_t* v, float* out, int length, int t_dec, int mode, int stats_slot,
+// used by reuse heads only; in kModeExact every head is marked exact, with no
+// recall), and the full-history scores and histogram of exact heads.
+// call_flag: an even number, different from the previous call's, that tags
+// this call's decision flags.
+hipError_t launch_step(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh, const uint16_t* k,
+                       const uint16_t* v, float* out, int length, int t_dec, int mode, int stats_slot, int call_flag,
                        hipStream_t s);
-// Full-history scores and histogram of exact heads.
-hipError_t launch_score(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
-                        const uint16_t* k, int length, hipStream_t s);
 // Exact heads: global Top-K, softmax-V (skipped when v or out is NULL),
 // S_t to sel_out (when not NULL) and the cache update (when push).
 hipError_t launch_tail(const Dims& d, const Bufs& b, const uint16_t* v, float* out, int32_t* sel_out, int length,

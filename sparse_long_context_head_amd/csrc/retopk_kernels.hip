@@ -671,16 +671,23 @@ size_t head_lds_bytes(const Dims& d) {
 
 size_t score_lds_bytes(const Dims& d) { return static_cast<size_t>(d.G) * kNumBins * 4; }
 
+size_t step_lds_bytes(const Dims& d) { return std::max(head_lds_bytes(d), score_lds_bytes(d)); }
+
 size_t finish_lds_bytes(const Dims& d) {
   return 8 * static_cast<size_t>(kBoundaryLds) + (4 * (static_cast<size_t>(d.n_chunks) + 1) + 15) / 16 * 16 +
          8 * static_cast<size_t>(d.K);
 }
 
 int score_grid(const Dims& d, int length) {
+  // one 512-thread work group per CU beside the head work groups (all resident
+  // at once, so none starts late), but at least half the CUs
+  const long cap = std::max(d.n_cu - d.B * d.Hq, d.n_cu / 2);
   const long groups = static_cast<long>(d.B) * d.Hkv;
   const long want = groups * ((length + kExactMinRows - 1) / kExactMinRows);
-  return static_cast<int>(std::max(1L, std::min<long>(kExactWGTarget, want)));
+  return static_cast<int>(std::max(1L, std::min(cap, want)));
 }
+// static LDS of k_step: the head role's shared state and rank table, the score role's group list
+static_assert(sizeof(HeadShared) + 2048 + 4 * 1024 + 64 + kLdsLimit <= 160 * 1024, "k_step LDS");
 
 // ---------------------------------------------------------------------------
 // Reset the FIFO bookkeeping before cache initialisation. One thread per head.
@@ -693,27 +700,49 @@ __global__ void k_reset(Dims d, Bufs b) {
 }
 
 namespace {
-constexpr int kQkUnroll = 4;  // 16-row tiles per wave per stage: 256 rows per work group
+// Data handed from one work group to another inside a launch goes through
+// device-scope (sc1) stores and loads, which are coherent across the XCDs'
+// L2s on their own (as are the device-scope atomics): a hand-off then needs
+// only the stores to be complete before the flag or counter that publishes
+// them, not a whole-L2 write-back and invalidate.
+__device__ __forceinline__ void store_shared(uint2* p, uint2 v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                     (static_cast<unsigned long long>(v.y) << 32) | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_shared(int32_t* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint2 load_shared(const uint2* p) {
+  const unsigned long long u = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint2(static_cast<uint32_t>(u), static_cast<uint32_t>(u >> 32));
+}
+__device__ __forceinline__ int load_shared(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kQkUnroll = 4;  // 16-row tiles per wave per stage: 512 rows per 8-wave work group
 
 struct QkTiles {
   uint4 a[kQkUnroll][4];
 };
 
-__device__ __forceinline__ void qk_load(QkTiles& t, const uint16_t* kb, int t0, int rend, int wave, int j, int kq) {
+__device__ __forceinline__ void qk_load(QkTiles& t, const uint16_t* kb, int t0, int rend, int wave, int nw, int j,
+                                        int kq) {
 #pragma unroll
   for (int u = 0; u < kQkUnroll; ++u) {
-    const int r = min(t0 + (u * 4 + wave) * 16 + j, rend - 1);
+    const int r = min(t0 + (u * nw + wave) * 16 + j, rend - 1);
     const uint16_t* row = kb + static_cast<long>(r) * kHeadDim + 8 * kq;
 #pragma unroll
     for (int s = 0; s < 4; ++s) t.a[u][s] = *reinterpret_cast<const uint4*>(row + 32 * s);
   }
 }
 
-__device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4], int t0, int rend, int wave, int kq,
-                                         bool hv, float* srow, uint32_t* hrow) {
+__device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4], int t0, int rend, int wave, int nw,
+                                         int kq, bool hv, float* srow, uint32_t* hrow) {
 #pragma unroll
   for (int u = 0; u < kQkUnroll; ++u) {
-    const int rbase = t0 + (u * 4 + wave) * 16;
+    const int rbase = t0 + (u * nw + wave) * 16;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -773,10 +802,9 @@ __device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4]
 // ---------------------------------------------------------------------------
 constexpr int kCandU = 20;  // candidate rows per 16-lane group in flight: 640 per round
 
-__global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uint16_t* q, long q_sb,
-                                                       long q_sh, const uint16_t* k, const uint16_t* v, float* out,
-                                                       int length, int t_dec, int mode, int stats_slot) {
-  const int bh = blockIdx.x;
+__device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
+                                          const uint16_t* k, const uint16_t* v, float* out, int length, int t_dec,
+                                          int mode, int stats_slot, int call_flag, int bh) {
   const int bb = bh / d.Hq, h = bh % d.Hq, g = h / d.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ HeadShared sh;
@@ -894,11 +922,11 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
       if (exact) b.st_m[o] = 0;
     }
   }
+  // publish the decision to the score work groups (an exact head's histogram
+  // copies are zero: the previous call's tail cleared them after use)
+  if (tid == 0) store_shared(b.dec + bh, call_flag | (exact ? 1 : 0));
   if (exact) {
-    // the full-history pass histograms this head's scores: clear its copies
     if (tid == 0) b.m[bh] = 0;
-    uint4* hz = reinterpret_cast<uint4*>(b.hist + static_cast<long>(bh) * kHistSeg * kNumBins);
-    for (int i = tid; i < kHistSeg * kNumBins / 4; i += blockDim.x) hz[i] = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
 
@@ -1030,34 +1058,56 @@ __global__ __launch_bounds__(kHeadThreads) void k_head(Dims d, Bufs b, const uin
 // global atomics into one of kHistSeg copies chosen by the work group); the
 // Top-K kernel finds its boundary from it.
 // ---------------------------------------------------------------------------
-constexpr int kScoreThreads = 256;
 constexpr int kMaxExactGroups = 1024;  // KV groups (batch x KV heads) the row split can list
+constexpr int kPollSleep = 8;          // s_sleep between polls of the decision flags (about 0.2 us)
+constexpr int kPollRounds = 20000;     // then give up (several ms): the error word is set, no scores
 
-__global__ __launch_bounds__(kScoreThreads) void k_score(Dims d, Bufs b, const uint16_t* q, long q_sb, long q_sh,
-                                                         const uint16_t* k, int length) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// w: this score work group's index among the nW of them.
+__device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
+                                           const uint16_t* k, int length, int call_flag, int w, int nW) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int j = lane & 15, kq = lane >> 4;
-  const int NG = d.B * d.Hkv, nW = gridDim.x;
-  __shared__ int s_eg[kMaxExactGroups];
+  const int NG = d.B * d.Hkv, BH = d.B * d.Hq;
+  __shared__ int s_eg[kMaxExactGroups];  // listed group | its exact heads << 16 (bit jj: head jj of the group)
   __shared__ int s_tmp[8];
   extern __shared__ __align__(16) uint32_t s_hist[];  // [G, kNumBins]
+
+  // every head's decision of this call, published by the head work groups
+  // (lower block indices, so already running); bounded wait
+  {
+    int done = 0;
+    for (int it = 0; it < kPollRounds; ++it) {
+      int mine = 1;
+      for (int i = threadIdx.x; i < BH; i += blockDim.x) mine &= (load_shared(b.dec + i) | 1) == (call_flag | 1);
+      done = __syncthreads_and(mine);
+      if (done) break;
+      __builtin_amdgcn_s_sleep(kPollSleep);
+    }
+    if (!done) {
+      if (threadIdx.x == 0) store_shared(b.err, 1);
+      return;
+    }
+  }
 
   // ordered list of the KV groups holding an exact head
   int ne;
   {
-    const int per = (NG + kScoreThreads - 1) / kScoreThreads;
+    const int per = (NG + blockDim.x - 1) / blockDim.x;
     const int g0 = min(static_cast<int>(threadIdx.x) * per, NG), g1 = min(g0 + per, NG);
-    int flags = 0, cnt = 0;
+    int cnt = 0;
     for (int bg = g0; bg < g1; ++bg) {
       const int bb = bg / d.Hkv, g = bg % d.Hkv;
-      int any = 0;
-      for (int jj = 0; jj < d.G; ++jj) any |= b.path[bb * d.Hq + g * d.G + jj];
-      flags |= (any != 0) << (bg - g0);
-      cnt += any != 0;
+      int m = 0;
+      for (int jj = 0; jj < d.G; ++jj) m |= (load_shared(b.dec + bb * d.Hq + g * d.G + jj) & 1) << jj;
+      cnt += m != 0;
     }
     int o = block_exclusive_scan(cnt, &ne, s_tmp);
-    for (int bg = g0; bg < g1; ++bg)
-      if (flags >> (bg - g0) & 1) s_eg[o++] = bg;
+    for (int bg = g0; bg < g1; ++bg) {
+      const int bb = bg / d.Hkv, g = bg % d.Hkv;
+      int m = 0;
+      for (int jj = 0; jj < d.G; ++jj) m |= (load_shared(b.dec + bb * d.Hq + g * d.G + jj) & 1) << jj;
+      if (m != 0) s_eg[o++] = bg | (m << 16);
+    }
   }
   lds_barrier();
   if (ne == 0) return;
@@ -1071,16 +1121,16 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(Dims d, Bufs b, const u
     r = e < ne ? static_cast<int>(x % length) & ~15 : 0;
   };
   int e, r, e1, r1;
-  split(blockIdx.x, e, r);
-  split(blockIdx.x + 1, e1, r1);
-  constexpr int kStage = 64 * kQkUnroll;  // rows per stage
+  split(w, e, r);
+  split(w + 1, e1, r1);
+  const int kStage = 16 * kQkUnroll * nw;  // rows per stage
   for (; e < e1 || (e == e1 && r < r1); ++e, r = 0) {
     const int row0 = r, rend = e == e1 ? r1 : length;
     if (row0 >= rend) continue;
-    const int bg = s_eg[e];
+    const int bg = s_eg[e] & 0xffff;
     const int bb = bg / d.Hkv, g = bg % d.Hkv;
     const int h = g * d.G + j;
-    const bool hv = (j < d.G) && b.path[bb * d.Hq + h];
+    const bool hv = (j < d.G) && ((static_cast<unsigned>(s_eg[e]) >> (16 + j)) & 1u);
     bf16x8 bq[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -1090,27 +1140,45 @@ __global__ __launch_bounds__(kScoreThreads) void k_score(Dims d, Bufs b, const u
     }
     const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
     QkTiles ta, tb;
-    qk_load(ta, kb, row0, rend, wave, j, kq);
+    qk_load(ta, kb, row0, rend, wave, nw, j, kq);
     lds_barrier();  // the previous segment's histogram flush is done
     for (int i = threadIdx.x; i < d.G * kNumBins; i += blockDim.x) s_hist[i] = 0u;
     lds_barrier();
     float* srow = b.score + static_cast<long>(bb * d.Hq + h) * d.score_stride;
     uint32_t* hrow = s_hist + j * kNumBins;
     for (int t0 = row0; t0 < rend; t0 += 2 * kStage) {
-      qk_load(tb, kb, t0 + kStage, rend, wave, j, kq);
-      qk_score(ta, bq, t0, rend, wave, kq, hv, srow, hrow);
+      qk_load(tb, kb, t0 + kStage, rend, wave, nw, j, kq);
+      qk_score(ta, bq, t0, rend, wave, nw, kq, hv, srow, hrow);
       if (t0 + kStage >= rend) break;
-      qk_load(ta, kb, t0 + 2 * kStage, rend, wave, j, kq);
-      qk_score(tb, bq, t0 + kStage, rend, wave, kq, hv, srow, hrow);
+      qk_load(ta, kb, t0 + 2 * kStage, rend, wave, nw, j, kq);
+      qk_score(tb, bq, t0 + kStage, rend, wave, nw, kq, hv, srow, hrow);
     }
     lds_barrier();
     uint32_t* ghist = b.hist + static_cast<long>(bb * d.Hq + g * d.G) * kHistSeg * kNumBins +
-                      (blockIdx.x % kHistSeg) * kNumBins;
+                      (w % kHistSeg) * kNumBins;
     for (int i = threadIdx.x; i < d.G * kNumBins; i += blockDim.x) {
       const uint32_t c = s_hist[i];
       if (c) atomicAdd(&ghist[(i / kNumBins) * kHistSeg * kNumBins + (i % kNumBins)], c);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// K1: the head work groups (block index < B*Hq) and after them the score work
+// groups, in one launch. A head work group publishes its path decision (and,
+// for an exact head, its cleared histogram) through a device-scope flag
+// tagged with this call; the score work groups wait for every flag of the
+// call (bounded), then stream the rows of the KV groups holding an exact
+// head. A reuse-only step thus costs no launch of its own for the score pass.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, Bufs b, const uint16_t* q, long q_sb, long q_sh,
+                                                       const uint16_t* k, const uint16_t* v, float* out, int length,
+                                                       int t_dec, int mode, int stats_slot, int call_flag) {
+  const int BH = d.B * d.Hq;
+  if (static_cast<int>(blockIdx.x) < BH)
+    head_role(d, b, q, q_sb, q_sh, k, v, out, length, t_dec, mode, stats_slot, call_flag, blockIdx.x);
+  else
+    score_role(d, b, q, q_sb, q_sh, k, length, call_flag, blockIdx.x - BH, gridDim.x - BH);
 }
 
 // ---------------------------------------------------------------------------
@@ -1183,26 +1251,6 @@ static_assert(kCollectRows * 64 * (kHeadThreads / 64) == kCollectChunk, "collect
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-}
-
-// Data handed from one work group to another inside k_tail goes through
-// device-scope (sc1) stores and loads, which are coherent across the XCDs'
-// L2s on their own; the hand-off then needs only the stores to be complete
-// before the counter is bumped, not a whole-L2 write-back and invalidate.
-__device__ __forceinline__ void store_shared(uint2* p, uint2 v) {
-  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
-                     (static_cast<unsigned long long>(v.y) << 32) | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_shared(int32_t* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint2 load_shared(const uint2* p) {
-  const unsigned long long u = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-  return make_uint2(static_cast<uint32_t>(u), static_cast<uint32_t>(u >> 32));
-}
-__device__ __forceinline__ int load_shared(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Both passes over a wave's rows; kInt selects the survivor compare.
@@ -1493,6 +1541,12 @@ __global__ __launch_bounds__(kHeadThreads) void k_tail(Dims d, Bufs b, const uin
   }
   __syncthreads();
   if (!s_last) return;
+  {
+    // every collect work group of the head has read its histogram copies:
+    // clear them for the next call's score pass
+    uint4* hz = reinterpret_cast<uint4*>(b.hist + static_cast<long>(bh) * kHistSeg * kNumBins);
+    for (int i = threadIdx.x; i < kHistSeg * kNumBins / 4; i += blockDim.x) hz[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
   finish_phase(d, b, bh, v, out, sel_out, length, push, fifo_slot, fifo_count, sh, dyn);
 }
 
@@ -1500,12 +1554,9 @@ __global__ __launch_bounds__(kHeadThreads) void k_tail(Dims d, Bufs b, const uin
 // Launch helpers
 // ---------------------------------------------------------------------------
 hipError_t configure_kernels(const Dims& d) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_head),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_step),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(head_lds_bytes(d)));
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(score_lds_bytes(d)));
+                                     static_cast<int>(step_lds_bytes(d)));
   if (e == hipSuccess)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tail), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(finish_lds_bytes(d)));
@@ -1513,7 +1564,7 @@ hipError_t configure_kernels(const Dims& d) {
 }
 
 const char* kernel_name(int id) {
-  static const char* names[kNumKernels] = {"k_head", "k_score", "k_tail", "k_reset"};
+  static const char* names[kNumKernels] = {"k_step", "k_tail", "k_reset"};
   return (id >= 0 && id < kNumKernels) ? names[id] : "";
 }
 
@@ -1523,18 +1574,11 @@ hipError_t launch_reset(const Dims& d, const Bufs& b, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_head(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh, const uint16_t* k,
-                       const uint16_t* v, float* out, int length, int t_dec, int mode, int stats_slot,
+hipError_t launch_step(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh, const uint16_t* k,
+                       const uint16_t* v, float* out, int length, int t_dec, int mode, int stats_slot, int call_flag,
                        hipStream_t s) {
-  hipLaunchKernelGGL(k_head, dim3(d.B * d.Hq), dim3(kHeadThreads), head_lds_bytes(d), s, d, b, q, q_sb, q_sh, k, v,
-                     out, length, t_dec, mode, stats_slot);
-  return hipGetLastError();
-}
-
-hipError_t launch_score(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
-                        const uint16_t* k, int length, hipStream_t s) {
-  hipLaunchKernelGGL(k_score, dim3(score_grid(d, length)), dim3(kScoreThreads), score_lds_bytes(d), s, d, b, q,
-                     q_sb, q_sh, k, length);
+  hipLaunchKernelGGL(k_step, dim3(d.B * d.Hq + score_grid(d, length)), dim3(kHeadThreads), step_lds_bytes(d), s, d,
+                     b, q, q_sb, q_sh, k, v, out, length, t_dec, mode, stats_slot, call_flag);
   return hipGetLastError();
 }
 

@@ -82,6 +82,12 @@ def compare_init(layer, orc, odata, prompt_len, sl, swaps):
                               odata["k"][b, g], where, swaps)
 
 
+def close_checked(layer):
+    """Every call completed its work (no score work group gave up waiting), then free."""
+    assert _B().retopk_read_device_error(layer.handle) == 0
+    layer.close()
+
+
 def run_lockstep(name, n_steps, sub=None, override=None, check_init=True, wl_kw=None):
     """Run n_steps decode steps; before each, the oracle adopts the GPU's cache."""
     torch = _torch()
@@ -138,7 +144,7 @@ def run_lockstep(name, n_steps, sub=None, override=None, check_init=True, wl_kw=
     log(f"[lockstep] {name}: exact head-steps {int(paths.sum())}/{paths.size}, "
         f"M_t mean {np.mean(ms) if ms else 0:.1f} max {max(ms) if ms else 0}, "
         f"swaps {len(swaps)}, max out err {max(errs):.2e}")
-    layer.close()
+    close_checked(layer)
     return dict(paths=paths, swaps=swaps, max_err=max(errs), ms=ms)
 
 
@@ -177,7 +183,7 @@ def run_exact(name, lengths, top_k=None, sub=None, wl_kw=None, q_override=None):
                 gs = check_support(s[b, h, :keff], osel, q[b, h], data["k"][b, g], where, swaps)
                 assert info["path"][b, h] == 1
                 check_output(o[b, h], gs, data["v"][b, g, s[b, h, :keff]], wl.head_dim, where)
-    layer.close()
+    close_checked(layer)
     return swaps
 
 
@@ -211,7 +217,7 @@ def test_exact_integer_ties():
         for h in range(Hq):
             osel, _ = O.exact_topk_support(q[0, h], k[0, h // 4], length, K)
             assert np.array_equal(s[0, h, :min(K, length)], osel), f"L={length} h={h}"
-    layer.close()
+    close_checked(layer)
 
 
 def test_exact_degenerate_all_equal():
@@ -232,7 +238,7 @@ def test_exact_degenerate_all_equal():
     assert np.array_equal(sel.cpu().numpy()[0, 0], np.arange(K))
     ref = O.bf16_to_f64(v[0, 0, :K]).mean(0)
     np.testing.assert_allclose(out.cpu().numpy()[0, 0], ref, rtol=1e-4, atol=1e-5)
-    layer.close()
+    close_checked(layer)
 
 
 # ---------------------------------------------------------------------------
@@ -303,7 +309,7 @@ def test_decode_free_running_tiny():
             break
         matched = t
     log(f"[free-running] tiny: identical for {matched} of {wl.decode_steps} steps")
-    layer.close()
+    close_checked(layer)
 
 
 def test_determinism_and_resume():
@@ -340,7 +346,7 @@ def test_determinism_and_resume():
     assert np.array_equal(oa2.view(np.uint32), oc2.view(np.uint32))
     assert all(np.array_equal(x, y) for x, y in zip(c.read_state(), sa))
     for layer in (a, b, c):
-        layer.close()
+        close_checked(layer)
 
 
 def test_stats_ring_matches_step_info():
@@ -362,7 +368,7 @@ def test_stats_ring_matches_step_info():
         assert np.all(((path[i] >> 1) & 1) == (1 if t % 5 == 0 else 0))
         assert np.array_equal(rho[i], info["rho_max"])
         assert np.array_equal(m[i], np.where(info["path"] == 1, 0, info["n_cand"]))
-    layer.close()
+    close_checked(layer)
 
 
 # ---------------------------------------------------------------------------
