@@ -359,10 +359,11 @@ def main():
         the statistics ring). Only what the method must move is counted:
         queries, the q_bar cache, the retrieved supports, key and value rows,
         outputs and cache entries; candidate, score and histogram workspaces
-        are not. k_step: every head's query and C cached normalised queries; a
-        reusing head's R supports, M_t key rows, min(K, M_t) value rows, its
-        output and cache entry; every key row of a KV group holding an exact
-        head. k_tail: an exact head's K value rows, output and cache entry."""
+        are not. k_step (the whole step): every head's query and C cached
+        normalised queries; a reusing head's R supports, M_t key rows,
+        min(K, M_t) value rows, its output and cache entry; every key row of
+        a KV group holding an exact head; an exact head's K value rows, output
+        and cache entry."""
         d, K, C, R = wl.head_dim, wl.top_k, wl.cache_cap, wl.top_r
         T = path.shape[0]
         exact = (path & 1) == 1
@@ -372,9 +373,9 @@ def main():
         entry = 4 * d + 4 * K
         per = {
             "k_step": (2 * d + 4 * C * d
-                       + reuse * (4 * R * K + ROW_BYTES * (m + n) + 4 * d + entry)).sum()
+                       + reuse * (4 * R * K + ROW_BYTES * (m + n) + 4 * d + entry)
+                       + exact * (ROW_BYTES * min(K, length) + 4 * d + entry)).sum()
                       + gex.sum() * ROW_BYTES * length,
-            "k_tail": (exact * (ROW_BYTES * min(K, length) + 4 * d + entry)).sum(),
         }
         return {k: float(v) / T for k, v in per.items()}
 
@@ -461,14 +462,11 @@ def main():
             result["kernels_exact"] = kb
             for layer in ex:
                 layer.close()
-            # the head + score kernel on all-exact steps: every KV group's key rows
-            # once and every head's query (exact heads skip recall)
+            # the step kernel on all-exact steps: every KV group's key rows once, the
+            # selected value rows (union per group), q in and out
             kq = kb.get("k_step")
             if kq:
-                alg = ROW_BYTES * mean_len * wl.batch * wl.n_kv_heads \
-                    + 2 * wl.batch * wl.n_q_heads * wl.head_dim
-                result["roofline_exact_score"] = roofline("k_step", alg, kq["us_per_launch"],
-                                                          "exact")
+                result["roofline_exact"] = roofline("k_step", step_alg, kq["us_per_launch"], "exact")
         if "value" in result:
             result["speedup_vs_exact"] = round(us_ex / result["value"], 3)
 

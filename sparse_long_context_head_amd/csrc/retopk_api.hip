@@ -59,11 +59,14 @@ struct retopk_handle {
   std::vector<hipEvent_t> events;   // pairs (start, stop)
   std::vector<int> event_kernel;    // kernel id of each recorded pair
   int timed = 0;                    // pairs recorded since the last read
-  int call_flag = 0;                // tag of the last k_step's decision flags (even; the buffer starts at 0)
+  int call_seq = 0;                 // sequence number of the last k_step launch
 
+  // Tag of the next launch's decision flags: 2 * seq, seq counting 1, 2, ... mod
+  // 2^29 (an even modulus, so bit 1, which selects the scored-row counters,
+  // alternates from call to call, and no tag repeats the previous one).
   int next_call_flag() {
-    call_flag = call_flag + 2 < (1 << 30) ? call_flag + 2 : 2;
-    return call_flag;
+    call_seq = (call_seq + 1) & ((1 << 29) - 1);
+    return 2 * call_seq;
   }
 
   template <typename T>
@@ -244,6 +247,7 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   A(&b.tailcnt, BH);
   A(&b.dec, BH);
   A(&b.err, 1);
+  A(&b.scored, 2 * static_cast<size_t>(d.B) * d.Hkv);
   A(&b.bkeys, BH * d.max_len);
   A(&b.sel, BH * d.K);
   A(&b.selsc, BH * d.K);
@@ -293,10 +297,8 @@ retopk_status retopk_init_from_prefill(retopk_handle* h, const uint16_t* q_tail,
     const uint16_t* qi = q_tail + static_cast<long>(i) * kHeadDim;
     const int flag = h->next_call_flag();
     st = h->run(kKStep, s, [&] {
-      return launch_step(d, b, qi, q_sb, q_sh, k, nullptr, nullptr, len, 0, kModeExact, -1, flag, s);
+      return launch_step(d, b, qi, q_sb, q_sh, k, nullptr, nullptr, nullptr, len, 0, kModeExact, -1, 1, flag, s);
     });
-    if (st == RETOPK_OK)
-      st = h->run(kKTail, s, [&] { return launch_tail(d, b, nullptr, nullptr, nullptr, len, 1, s); });
   }
   return st;
 }
@@ -320,9 +322,8 @@ retopk_status retopk_decode_step(retopk_handle* h, const uint16_t* q, const uint
   const long q_sb = static_cast<long>(d.Hq) * kHeadDim, q_sh = kHeadDim;
   const int flag = h->next_call_flag();
   retopk_status st = h->run(kKStep, s, [&] {
-    return launch_step(d, b, q, q_sb, q_sh, k, v, out, length, t_dec, kModeDecode, slot, flag, s);
+    return launch_step(d, b, q, q_sb, q_sh, k, v, out, nullptr, length, t_dec, kModeDecode, slot, 1, flag, s);
   });
-  if (st == RETOPK_OK) st = h->run(kKTail, s, [&] { return launch_tail(d, b, v, out, nullptr, length, 1, s); });
   return st;
 }
 
@@ -344,9 +345,8 @@ retopk_status retopk_exact_topk_attn(retopk_handle* h, const uint16_t* q, const 
   const long q_sb = static_cast<long>(d.Hq) * kHeadDim, q_sh = kHeadDim;
   const int flag = h->next_call_flag();
   retopk_status st = h->run(kKStep, s, [&] {
-    return launch_step(d, b, q, q_sb, q_sh, k, nullptr, nullptr, length, 0, kModeExact, -1, flag, s);
+    return launch_step(d, b, q, q_sb, q_sh, k, v, out, sel_out, length, 0, kModeExact, -1, 0, flag, s);
   });
-  if (st == RETOPK_OK) st = h->run(kKTail, s, [&] { return launch_tail(d, b, v, out, sel_out, length, 0, s); });
   return st;
 }
 

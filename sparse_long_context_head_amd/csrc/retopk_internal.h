@@ -62,7 +62,8 @@ struct Bufs {
   int32_t* tailcnt;        // [BH] collect work groups done (zero between calls)
                            // (hist is zero between calls too: the tail clears an exact head's copies)
   int32_t* dec;            // [BH] path decision of the current call: call flag | exact
-  int32_t* err;            // [1]  sticky device error word (1: a score work group timed out)
+  int32_t* err;            // [1]  sticky device error word (1: a wait of the step kernel timed out)
+  int32_t* scored;         // [2, B*Hkv] key rows scored this call per KV group (call parity selects the half)
   uint64_t* bkeys;         // [BH, max_len] boundary-bin composite keys when more than kBoundaryLds
   int32_t* sel;            // [BH, K]   S_hat_t ascending
   float* selsc;            // [BH, K]   q.k of S_hat_t
@@ -73,7 +74,7 @@ struct Bufs {
   int32_t* st_m;           // [kStatsCap, BH]
 };
 
-enum KernelId : int { kKStep = 0, kKTail, kKReset, kNumKernels };
+enum KernelId : int { kKStep = 0, kKReset, kNumKernels };
 
 const char* kernel_name(int id);
 
@@ -87,23 +88,21 @@ int score_grid(const Dims& d, int length);
 
 // Launch helpers (retopk_kernels.hip). Each returns the hipError_t of the
 // launch. A decode step, the exact Top-K baseline and the cache
-// initialisation are each step -> tail on one stream.
+// initialisation are each one k_step launch per call on one stream.
 enum HeadMode : int { kModeDecode = 0, kModeExact = 1 };
 
 // Raise the dynamic-LDS limit of the kernels to what `d` needs.
 hipError_t configure_kernels(const Dims& d);
 hipError_t launch_reset(const Dims& d, const Bufs& b, hipStream_t s);
-// Recall, path decision and the reuse path of reuse heads (k, v, out are
-// used by reuse heads only; in kModeExact every head is marked exact, with no
-// recall), and the full-history scores and histogram of exact heads.
-// call_flag: an even number, different from the previous call's, that tags
-// this call's decision flags.
+// The whole call in one launch: recall, path decision and the reuse path of
+// reuse heads (k, v, out are used by reuse heads only; in kModeExact every
+// head is marked exact, with no recall), the full-history scores and
+// histogram of exact heads, and their global Top-K, softmax-V (skipped when v
+// or out is NULL), S_t to sel_out (when not NULL) and cache update (when
+// push). call_flag: an even number, different from the previous call's, that
+// tags this call's decision flags; its bit 1 selects the half of `scored`.
 hipError_t launch_step(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh, const uint16_t* k,
-                       const uint16_t* v, float* out, int length, int t_dec, int mode, int stats_slot, int call_flag,
-                       hipStream_t s);
-// Exact heads: global Top-K, softmax-V (skipped when v or out is NULL),
-// S_t to sel_out (when not NULL) and the cache update (when push).
-hipError_t launch_tail(const Dims& d, const Bufs& b, const uint16_t* v, float* out, int32_t* sel_out, int length,
-                       int push, hipStream_t s);
+                       const uint16_t* v, float* out, int32_t* sel_out, int length, int t_dec, int mode,
+                       int stats_slot, int push, int call_flag, hipStream_t s);
 
 }  // namespace retopk

@@ -1,31 +1,32 @@
 // ReTopK decode-step kernels for CDNA4 (gfx950, wave64).
 //
 // Method: "Recall Before You Rank: Similarity-Guided Top-K Reuse for
-// Efficient Long-Context Attention", Methodology section. A decode step is
-// three launches on one stream. Data passes between work groups at kernel
-// boundaries, and once inside k_tail, where the last collect work group of an
-// exact head takes over its survivors (a device-scope release or acquire
-// writes back or invalidates a whole L2, so such hand-offs are kept to the
-// exact heads, where they replace a launch):
+// Efficient Long-Context Attention", Methodology section. A decode step (or an
+// exact call) is one launch of k_step, whose work groups take three roles by
+// block index:
 //
-//   k_head     one work group per query head: recall (Eqs. 5-7) and the path
-//              rule (Eq. 13); a reuse head runs its whole path in the same
-//              work group: candidate union (Eqs. 8-9), candidate scores
-//              (Eq. 10), rerank (Eq. 11), softmax-V (Eq. 12) and the cache
-//              update;
-//   k_score    full-history scores (Eq. 4) and a score histogram of every
-//              exact head, GQA-grouped on MFMA, the rows of the exact KV groups
-//              spread over the whole grid;
-//   k_tail     global Top-K (Eq. 1): many work groups per exact head collect
-//              the scores in the histogram's boundary bin or above it, in
-//              position order; the last one of a head to finish collecting
-//              selects inside the boundary bin, then runs softmax-V and the
-//              cache update.
+//   head   one per query head: recall (Eqs. 5-7) and the path rule (Eq. 13),
+//          published at once through a device-scope flag tagged with the call;
+//          a reuse head then runs its whole path in the same work group:
+//          candidate union (Eqs. 8-9), candidate scores (Eq. 10), rerank
+//          (Eq. 11), softmax-V (Eq. 12) and the cache update;
+//   score  full-history scores (Eq. 4) and a score histogram of every exact
+//          head, GQA-grouped on MFMA, the rows of the exact KV groups spread
+//          over all score work groups; each adds the rows it scored to its KV
+//          group's counter;
+//   tail   one per (query head, chunk of positions): for an exact head, once
+//          its KV group is fully scored, the scores in the histogram's
+//          boundary bin or above it, in position order (global Top-K, Eq. 1,
+//          step 1); the last one of a head selects inside the boundary bin,
+//          then runs softmax-V and the cache update.
 //
-// The exact Top-K baseline and the cache initialisation are the same three
-// kernels with every head marked exact. The path flag stays on the device:
-// each kernel reads it and work of the other path returns at once, so the
-// host never waits. Every phase issues its global loads before consuming
+// Data passes between work groups only through device-scope (sc1) stores and
+// loads and device-scope atomics, which are coherent across the XCDs' L2s on
+// their own: no whole-L2 write-back or invalidate is needed (those cost more
+// than a launch on this part). Every wait is on work groups of lower block
+// index, which the dispatcher has started first, and is bounded in time.
+// Reuse heads need no full-history work at all, and the host never waits on
+// the path decision. Every phase issues its global loads before consuming
 // them, so a phase costs about one memory round trip rather than one per loop
 // iteration.
 
@@ -671,7 +672,9 @@ size_t head_lds_bytes(const Dims& d) {
 
 size_t score_lds_bytes(const Dims& d) { return static_cast<size_t>(d.G) * kNumBins * 4; }
 
-size_t step_lds_bytes(const Dims& d) { return std::max(head_lds_bytes(d), score_lds_bytes(d)); }
+size_t step_lds_bytes(const Dims& d) {
+  return std::max({head_lds_bytes(d), score_lds_bytes(d), finish_lds_bytes(d)});
+}
 
 size_t finish_lds_bytes(const Dims& d) {
   return 8 * static_cast<size_t>(kBoundaryLds) + (4 * (static_cast<size_t>(d.n_chunks) + 1) + 15) / 16 * 16 +
@@ -720,6 +723,38 @@ __device__ __forceinline__ uint2 load_shared(const uint2* p) {
 __device__ __forceinline__ int load_shared(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ float load_shared(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_shared(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// two consecutive floats (8-byte aligned) as one device-scope store
+__device__ __forceinline__ void store_shared2(float* p, float a, float b) {
+  store_shared(reinterpret_cast<uint2*>(p), make_uint2(__float_as_uint(a), __float_as_uint(b)));
+}
+
+constexpr int kPollSleep = 8;                 // s_sleep between polls of a flag (about 0.2 us)
+constexpr long long kWaitTicks = 20000000;    // give up a wait after 200 ms (s_memrealtime is 100 MHz)
+
+// Thread 0 polls *p until ok(value) or the time limit; every thread gets the
+// last value read (through *s_val) and whether it was ok. A timeout sets the
+// device error word. Every thread of the block must call it.
+template <typename Ok>
+__device__ __forceinline__ bool wait_flag(const int32_t* p, Ok ok, int* s_val, int32_t* err) {
+  if (threadIdx.x == 0) {
+    const long long t0 = __builtin_amdgcn_s_memrealtime();
+    int v = load_shared(p);
+    while (!ok(v) && __builtin_amdgcn_s_memrealtime() - t0 < kWaitTicks) {
+      __builtin_amdgcn_s_sleep(kPollSleep);
+      v = load_shared(p);
+    }
+    if (!ok(v)) store_shared(err, 1);
+    *s_val = v;
+  }
+  lds_barrier();
+  return ok(*s_val);
+}
 
 constexpr int kQkUnroll = 4;  // 16-row tiles per wave per stage: 512 rows per 8-wave work group
 
@@ -739,7 +774,7 @@ __device__ __forceinline__ void qk_load(QkTiles& t, const uint16_t* kb, int t0, 
 }
 
 __device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4], int t0, int rend, int wave, int nw,
-                                         int kq, bool hv, float* srow, uint32_t* hrow) {
+                                         int kq, bool hv, bool sc1, float* srow, uint32_t* hrow) {
 #pragma unroll
   for (int u = 0; u < kQkUnroll; ++u) {
     const int rbase = t0 + (u * nw + wave) * 16;
@@ -750,15 +785,22 @@ __device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4]
     // lane holds query head j for rows rbase + 4*kq + 0..3
     if (hv) {
       const int r = rbase + 4 * kq;
+      // sc1: the tail role reads the scores in this launch (device-scope stores)
       if (r + 3 < rend) {
-        *reinterpret_cast<float4*>(srow + r) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        if (sc1) {
+          store_shared2(srow + r, acc[0], acc[1]);
+          store_shared2(srow + r + 2, acc[2], acc[3]);
+        } else {
+          *reinterpret_cast<float4*>(srow + r) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) atomicAdd(&hrow[order_key(acc[e]) >> kHistShift], 1u);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (r + e < rend) {
-            srow[r + e] = acc[e];
+            if (sc1) store_shared(srow + r + e, acc[e]);
+            else srow[r + e] = acc[e];
             atomicAdd(&hrow[order_key(acc[e]) >> kHistShift], 1u);
           }
         }
@@ -804,10 +846,9 @@ constexpr int kCandU = 20;  // candidate rows per 16-lane group in flight: 640 p
 
 __device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
                                           const uint16_t* k, const uint16_t* v, float* out, int length, int t_dec,
-                                          int mode, int stats_slot, int call_flag, int bh) {
+                                          int mode, int stats_slot, int call_flag, int bh, HeadShared& sh) {
   const int bb = bh / d.Hq, h = bh % d.Hq, g = h / d.G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ HeadShared sh;
   __shared__ int s_rank[8][64];
   extern __shared__ __align__(16) unsigned char dyn[];
   const size_t region0 = head_region0(d);
@@ -844,7 +885,7 @@ __device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const ui
     }
     sh.qbar[2 * lane] = qb0;
     sh.qbar[2 * lane + 1] = qb1;
-    *reinterpret_cast<float2*>(b.qbar + static_cast<long>(bh) * kHeadDim + 2 * lane) = make_float2(qb0, qb1);
+    store_shared2(b.qbar + static_cast<long>(bh) * kHeadDim + 2 * lane, qb0, qb1);  // read by the tail role
   }
   if (mode == kModeDecode) bitmap_clear(bm);  // first bitmap window, while the loads are in flight
   lds_barrier();
@@ -922,9 +963,13 @@ __device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const ui
       if (exact) b.st_m[o] = 0;
     }
   }
-  // publish the decision to the score work groups (an exact head's histogram
-  // copies are zero: the previous call's tail cleared them after use)
-  if (tid == 0) store_shared(b.dec + bh, call_flag | (exact ? 1 : 0));
+  // publish the decision to the score and tail work groups (an exact head's
+  // histogram copies are zero: the previous call's tail cleared them after
+  // use); zero the next call's scored-row counter of group bh
+  if (tid == 0) {
+    store_shared(b.dec + bh, call_flag | (exact ? 1 : 0));
+    if (bh < d.B * d.Hkv) b.scored[((call_flag >> 1) & 1 ^ 1) * d.B * d.Hkv + bh] = 0;
+  }
   if (exact) {
     if (tid == 0) b.m[bh] = 0;
     return;
@@ -1059,12 +1104,15 @@ __device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const ui
 // Top-K kernel finds its boundary from it.
 // ---------------------------------------------------------------------------
 constexpr int kMaxExactGroups = 1024;  // KV groups (batch x KV heads) the row split can list
-constexpr int kPollSleep = 8;          // s_sleep between polls of the decision flags (about 0.2 us)
-constexpr int kPollRounds = 20000;     // then give up (several ms): the error word is set, no scores
+constexpr int kPollRounds = 20000;     // polls of the decision flags before giving up (several ms)
 
 // w: this score work group's index among the nW of them.
+// all_exact: every head of the call is exact (no flags to wait for); fused:
+// the tail work groups run in the same launch (scores go out through
+// device-scope stores and the scored-row counters are kept).
 __device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
-                                           const uint16_t* k, int length, int call_flag, int w, int nW) {
+                                           const uint16_t* k, int length, int call_flag, int w, int nW,
+                                           bool all_exact, bool fused) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int j = lane & 15, kq = lane >> 4;
   const int NG = d.B * d.Hkv, BH = d.B * d.Hq;
@@ -1074,7 +1122,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const u
 
   // every head's decision of this call, published by the head work groups
   // (lower block indices, so already running); bounded wait
-  {
+  if (!all_exact) {
     int done = 0;
     for (int it = 0; it < kPollRounds; ++it) {
       int mine = 1;
@@ -1097,15 +1145,15 @@ __device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const u
     int cnt = 0;
     for (int bg = g0; bg < g1; ++bg) {
       const int bb = bg / d.Hkv, g = bg % d.Hkv;
-      int m = 0;
-      for (int jj = 0; jj < d.G; ++jj) m |= (load_shared(b.dec + bb * d.Hq + g * d.G + jj) & 1) << jj;
+      int m = all_exact ? (1 << d.G) - 1 : 0;
+      for (int jj = 0; !all_exact && jj < d.G; ++jj) m |= (load_shared(b.dec + bb * d.Hq + g * d.G + jj) & 1) << jj;
       cnt += m != 0;
     }
     int o = block_exclusive_scan(cnt, &ne, s_tmp);
     for (int bg = g0; bg < g1; ++bg) {
       const int bb = bg / d.Hkv, g = bg % d.Hkv;
-      int m = 0;
-      for (int jj = 0; jj < d.G; ++jj) m |= (load_shared(b.dec + bb * d.Hq + g * d.G + jj) & 1) << jj;
+      int m = all_exact ? (1 << d.G) - 1 : 0;
+      for (int jj = 0; !all_exact && jj < d.G; ++jj) m |= (load_shared(b.dec + bb * d.Hq + g * d.G + jj) & 1) << jj;
       if (m != 0) s_eg[o++] = bg | (m << 16);
     }
   }
@@ -1148,10 +1196,10 @@ __device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const u
     uint32_t* hrow = s_hist + j * kNumBins;
     for (int t0 = row0; t0 < rend; t0 += 2 * kStage) {
       qk_load(tb, kb, t0 + kStage, rend, wave, nw, j, kq);
-      qk_score(ta, bq, t0, rend, wave, nw, kq, hv, srow, hrow);
+      qk_score(ta, bq, t0, rend, wave, nw, kq, hv, fused, srow, hrow);
       if (t0 + kStage >= rend) break;
       qk_load(ta, kb, t0 + 2 * kStage, rend, wave, nw, j, kq);
-      qk_score(tb, bq, t0 + kStage, rend, wave, nw, kq, hv, srow, hrow);
+      qk_score(tb, bq, t0 + kStage, rend, wave, nw, kq, hv, fused, srow, hrow);
     }
     lds_barrier();
     uint32_t* ghist = b.hist + static_cast<long>(bb * d.Hq + g * d.G) * kHistSeg * kNumBins +
@@ -1160,25 +1208,11 @@ __device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const u
       const uint32_t c = s_hist[i];
       if (c) atomicAdd(&ghist[(i / kNumBins) * kHistSeg * kNumBins + (i % kNumBins)], c);
     }
+    if (fused) {
+      __syncthreads();  // every wave's scores and histogram adds of the segment are complete
+      if (threadIdx.x == 0) atomicAdd(&b.scored[((call_flag >> 1) & 1) * NG + bg], rend - row0);
+    }
   }
-}
-
-// ---------------------------------------------------------------------------
-// K1: the head work groups (block index < B*Hq) and after them the score work
-// groups, in one launch. A head work group publishes its path decision (and,
-// for an exact head, its cleared histogram) through a device-scope flag
-// tagged with this call; the score work groups wait for every flag of the
-// call (bounded), then stream the rows of the KV groups holding an exact
-// head. A reuse-only step thus costs no launch of its own for the score pass.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, Bufs b, const uint16_t* q, long q_sb, long q_sh,
-                                                       const uint16_t* k, const uint16_t* v, float* out, int length,
-                                                       int t_dec, int mode, int stats_slot, int call_flag) {
-  const int BH = d.B * d.Hq;
-  if (static_cast<int>(blockIdx.x) < BH)
-    head_role(d, b, q, q_sb, q_sh, k, v, out, length, t_dec, mode, stats_slot, call_flag, blockIdx.x);
-  else
-    score_role(d, b, q, q_sb, q_sh, k, length, call_flag, blockIdx.x - BH, gridDim.x - BH);
 }
 
 // ---------------------------------------------------------------------------
@@ -1220,7 +1254,7 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh
     attend(s_sel, s_selsc, n, mx, vb, out + static_cast<long>(bh) * kHeadDim, nullptr, sh);
   }
   if (push) {
-    for (int t = tid; t < kHeadDim; t += blockDim.x) sh.qbar[t] = b.qbar[static_cast<long>(bh) * kHeadDim + t];
+    for (int t = tid; t < kHeadDim; t += blockDim.x) sh.qbar[t] = load_shared(b.qbar + static_cast<long>(bh) * kHeadDim + t);
     lds_barrier();
     cache_push(d, b, bh, fifo_slot, fifo_count, sh.qbar, s_sel, n);
   }
@@ -1300,11 +1334,11 @@ __device__ __forceinline__ void collect_phase(const Dims& d, const Bufs& b, int 
   // 1022-2t) of every histogram copy
   float x[kCollectRows];
 #pragma unroll
-  for (int u = 0; u < kCollectRows; ++u) x[u] = srow[min(p0 + 64 * u, length - 1)];  // clamped, masked below
+  for (int u = 0; u < kCollectRows; ++u) x[u] = load_shared(srow + min(p0 + 64 * u, length - 1));  // clamped, masked below
   uint2 hs[kHistSeg];
 #pragma unroll
   for (int sgm = 0; sgm < kHistSeg; ++sgm)
-    hs[sgm] = *reinterpret_cast<const uint2*>(hist + sgm * kNumBins + kNumBins - 2 * (tid + 1));
+    hs[sgm] = load_shared(reinterpret_cast<const uint2*>(hist + sgm * kNumBins + kNumBins - 2 * (tid + 1)));
   int ca = 0, cb = 0;
 #pragma unroll
   for (int sgm = 0; sgm < kHistSeg; ++sgm) {
@@ -1523,16 +1557,27 @@ __device__ __forceinline__ void finish_phase(const Dims& d, const Bufs& b, int b
 // the head and resets the counter for the next call. No wave waits on another
 // work group.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kHeadThreads) void k_tail(Dims d, Bufs b, const uint16_t* v, float* out,
-                                                       int32_t* sel_out, int length, int push, int nch) {
+// fused: the score work groups run in the same launch (wait for the KV
+// group's scored-row counter); else they ran in an earlier launch.
+__device__ __forceinline__ void tail_role(const Dims& d, const Bufs& b, const uint16_t* v, float* out, int32_t* sel_out,
+                                          int length, int push, int call_flag, int tw, int nch, bool fused,
+                                          HeadShared& sh) {
   __shared__ int tmp[16];
   __shared__ int s_bd[3];
   __shared__ int s_last;
-  __shared__ HeadShared sh;
+  __shared__ int s_val;
   extern __shared__ __align__(16) unsigned char dyn[];
-  const int bh = blockIdx.x / nch, chunk = blockIdx.x % nch;
-  const int fifo_slot = b.fifo[2 * bh], fifo_count = b.fifo[2 * bh + 1];  // written only by the finish below
-  if (!b.path[bh]) return;
+  const int bh = tw / nch, chunk = tw % nch;
+  const int NG = d.B * d.Hkv;
+  // this head's FIFO state: only the finish below pushes for an exact head
+  const int fifo_slot = b.fifo[2 * bh], fifo_count = b.fifo[2 * bh + 1];
+  // this call's decision for the head, then (exact) its KV group fully scored
+  if (!wait_flag(b.dec + bh, [&](int x) { return (x | 1) == (call_flag | 1); }, &s_val, b.err)) return;
+  if (!(s_val & 1)) return;
+  const int bg = (bh / d.Hq) * d.Hkv + (bh % d.Hq) / d.G;
+  if (fused &&
+      !wait_flag(b.scored + ((call_flag >> 1) & 1) * NG + bg, [&](int x) { return x >= length; }, &s_val, b.err))
+    return;
   collect_phase(d, b, bh, chunk, length, tmp, s_bd);
   __syncthreads();  // every wave's (device-scope) survivor and count stores are complete
   if (threadIdx.x == 0) {
@@ -1551,20 +1596,45 @@ __global__ __launch_bounds__(kHeadThreads) void k_tail(Dims d, Bufs b, const uin
 }
 
 // ---------------------------------------------------------------------------
+// A decode step (or an exact call) over the work-group index space
+//   [0, BH)                     head work groups (query heads);
+//   [BH, BH + NS)               score work groups;
+//   [BH + NS, BH + NS + BH*nch) tail work groups (query head, chunk),
+// launched whole (a decode step: `fused`) or as [0, BH + NS) then the rest
+// (calls with every head exact, where the first part is long and a launch
+// boundary is cheaper than device-scope traffic and polling): block b is index
+// base + b. Every wait is on work groups of lower index (dispatched first, or
+// in an earlier launch) and is bounded in time; a timeout sets the device
+// error word.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, Bufs b, const uint16_t* q, long q_sb, long q_sh,
+                                                       const uint16_t* k, const uint16_t* v, float* out,
+                                                       int32_t* sel_out, int length, int t_dec, int mode,
+                                                       int stats_slot, int push, int call_flag, int n_score, int base,
+                                                       int fused) {
+  __shared__ HeadShared sh;
+  const int BH = d.B * d.Hq;
+  const int w = base + static_cast<int>(blockIdx.x);
+  if (w < BH) {
+    head_role(d, b, q, q_sb, q_sh, k, v, out, length, t_dec, mode, stats_slot, call_flag, w, sh);
+  } else if (w < BH + n_score) {
+    score_role(d, b, q, q_sb, q_sh, k, length, call_flag, w - BH, n_score, mode == kModeExact, fused != 0);
+  } else {
+    const int nch = (length + kCollectChunk - 1) / kCollectChunk;
+    tail_role(d, b, v, out, sel_out, length, push, call_flag, w - BH - n_score, nch, fused != 0, sh);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launch helpers
 // ---------------------------------------------------------------------------
 hipError_t configure_kernels(const Dims& d) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_step),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(step_lds_bytes(d)));
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_tail), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(finish_lds_bytes(d)));
-  return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_step), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             static_cast<int>(step_lds_bytes(d)));
 }
 
 const char* kernel_name(int id) {
-  static const char* names[kNumKernels] = {"k_step", "k_tail", "k_reset"};
+  static const char* names[kNumKernels] = {"k_step", "k_reset"};
   return (id >= 0 && id < kNumKernels) ? names[id] : "";
 }
 
@@ -1575,18 +1645,23 @@ hipError_t launch_reset(const Dims& d, const Bufs& b, hipStream_t s) {
 }
 
 hipError_t launch_step(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh, const uint16_t* k,
-                       const uint16_t* v, float* out, int length, int t_dec, int mode, int stats_slot, int call_flag,
-                       hipStream_t s) {
-  hipLaunchKernelGGL(k_step, dim3(d.B * d.Hq + score_grid(d, length)), dim3(kHeadThreads), step_lds_bytes(d), s, d,
-                     b, q, q_sb, q_sh, k, v, out, length, t_dec, mode, stats_slot, call_flag);
-  return hipGetLastError();
-}
-
-hipError_t launch_tail(const Dims& d, const Bufs& b, const uint16_t* v, float* out, int32_t* sel_out, int length,
-                       int push, hipStream_t s) {
+                       const uint16_t* v, float* out, int32_t* sel_out, int length, int t_dec, int mode,
+                       int stats_slot, int push, int call_flag, hipStream_t s) {
+  const int n_score = score_grid(d, length);
   const int nch = (length + kCollectChunk - 1) / kCollectChunk;
-  hipLaunchKernelGGL(k_tail, dim3(d.B * d.Hq * nch), dim3(kHeadThreads), finish_lds_bytes(d), s, d, b, v, out,
-                     sel_out, length, push, nch);
+  const int BH = d.B * d.Hq;
+  if (mode == kModeDecode) {
+    hipLaunchKernelGGL(k_step, dim3(BH + n_score + BH * nch), dim3(kHeadThreads), step_lds_bytes(d), s, d, b, q,
+                       q_sb, q_sh, k, v, out, sel_out, length, t_dec, mode, stats_slot, push, call_flag, n_score, 0,
+                       1);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_step, dim3(BH + n_score), dim3(kHeadThreads), step_lds_bytes(d), s, d, b, q, q_sb, q_sh, k, v,
+                     out, sel_out, length, t_dec, mode, stats_slot, push, call_flag, n_score, 0, 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_step, dim3(BH * nch), dim3(kHeadThreads), step_lds_bytes(d), s, d, b, q, q_sb, q_sh, k, v, out,
+                     sel_out, length, t_dec, mode, stats_slot, push, call_flag, n_score, BH + n_score, 0);
   return hipGetLastError();
 }
 
