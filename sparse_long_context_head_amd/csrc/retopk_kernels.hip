@@ -690,7 +690,7 @@ int score_grid(const Dims& d, int length) {
   return static_cast<int>(std::max(1L, std::min(cap, want)));
 }
 // static LDS of k_step: the head role's shared state and rank table, the score role's group list
-static_assert(sizeof(HeadShared) + 2048 + 4 * 1024 + 64 + kLdsLimit <= 160 * 1024, "k_step LDS");
+static_assert(sizeof(HeadShared) + 2048 + 4 * 1024 + 2048 + 128 + kLdsLimit <= 160 * 1024, "k_step LDS");
 
 // ---------------------------------------------------------------------------
 // Reset the FIFO bookkeeping before cache initialisation. One thread per head.
@@ -874,6 +874,7 @@ __device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const ui
     const int len_c = b.cache_len[static_cast<long>(bh) * d.C + min(tid, d.C - 1)];
     if (tid < d.C) sh.len[tid] = len_c;
   }
+
   if (wave == 0) {
     const uint32_t w2 = *reinterpret_cast<const uint32_t*>(q + bb * q_sb + h * q_sh + 2 * lane);
     const double x0 = bf16_lo(w2), x1 = bf16_hi(w2);
@@ -918,6 +919,11 @@ __device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const ui
       }
     }
     lds_barrier();
+    // the path rule needs only rho_max: publish the decision before ranking
+    if (wave == 0) {
+      const double mxr = wave_max_f64(lane < count ? sh.rho[lane] : -INFINITY);
+      if (lane == 0) store_shared(b.dec + bh, call_flag | ((refresh || count == 0 || mxr < d.tau) ? 1 : 0));
+    }
     // Rank of FIFO position p under (rho desc, position asc), counted in
     // parallel: wave w compares every position with positions w, w+8, ...
     {
@@ -963,11 +969,12 @@ __device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const ui
       if (exact) b.st_m[o] = 0;
     }
   }
-  // publish the decision to the score and tail work groups (an exact head's
-  // histogram copies are zero: the previous call's tail cleared them after
-  // use); zero the next call's scored-row counter of group bh
+  // publish the decision to the score and tail work groups (decode mode did
+  // so above; an exact head's histogram copies are zero: the previous call's
+  // tail cleared them after use); zero the next call's scored-row counter of
+  // group bh
   if (tid == 0) {
-    store_shared(b.dec + bh, call_flag | (exact ? 1 : 0));
+    if (mode != kModeDecode) store_shared(b.dec + bh, call_flag | (exact ? 1 : 0));
     if (bh < d.B * d.Hkv) b.scored[((call_flag >> 1) & 1 ^ 1) * d.B * d.Hkv + bh] = 0;
   }
   if (exact) {
@@ -1118,6 +1125,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const u
   const int NG = d.B * d.Hkv, BH = d.B * d.Hq;
   __shared__ int s_eg[kMaxExactGroups];  // listed group | its exact heads << 16 (bit jj: head jj of the group)
   __shared__ int s_tmp[8];
+  __shared__ uint32_t s_ex[kMaxExactGroups * kMaxGroup / 32];  // exact bit of every head
   extern __shared__ __align__(16) uint32_t s_hist[];  // [G, kNumBins]
 
   // every head's decision of this call, published by the head work groups
@@ -1125,8 +1133,14 @@ __device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const u
   if (!all_exact) {
     int done = 0;
     for (int it = 0; it < kPollRounds; ++it) {
+      for (int i = threadIdx.x; i < (BH + 31) / 32; i += blockDim.x) s_ex[i] = 0u;
+      lds_barrier();
       int mine = 1;
-      for (int i = threadIdx.x; i < BH; i += blockDim.x) mine &= (load_shared(b.dec + i) | 1) == (call_flag | 1);
+      for (int i = threadIdx.x; i < BH; i += blockDim.x) {
+        const int x = load_shared(b.dec + i);
+        mine &= (x | 1) == (call_flag | 1);
+        if (x & 1) atomicOr(&s_ex[i >> 5], 1u << (i & 31));
+      }
       done = __syncthreads_and(mine);
       if (done) break;
       __builtin_amdgcn_s_sleep(kPollSleep);
@@ -1146,14 +1160,20 @@ __device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const u
     for (int bg = g0; bg < g1; ++bg) {
       const int bb = bg / d.Hkv, g = bg % d.Hkv;
       int m = all_exact ? (1 << d.G) - 1 : 0;
-      for (int jj = 0; !all_exact && jj < d.G; ++jj) m |= (load_shared(b.dec + bb * d.Hq + g * d.G + jj) & 1) << jj;
+      for (int jj = 0; !all_exact && jj < d.G; ++jj) {
+        const int hh = bb * d.Hq + g * d.G + jj;
+        m |= ((s_ex[hh >> 5] >> (hh & 31)) & 1) << jj;
+      }
       cnt += m != 0;
     }
     int o = block_exclusive_scan(cnt, &ne, s_tmp);
     for (int bg = g0; bg < g1; ++bg) {
       const int bb = bg / d.Hkv, g = bg % d.Hkv;
       int m = all_exact ? (1 << d.G) - 1 : 0;
-      for (int jj = 0; !all_exact && jj < d.G; ++jj) m |= (load_shared(b.dec + bb * d.Hq + g * d.G + jj) & 1) << jj;
+      for (int jj = 0; !all_exact && jj < d.G; ++jj) {
+        const int hh = bb * d.Hq + g * d.G + jj;
+        m |= ((s_ex[hh >> 5] >> (hh & 31)) & 1) << jj;
+      }
       if (m != 0) s_eg[o++] = bg | (m << 16);
     }
   }
@@ -1189,8 +1209,11 @@ __device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const u
     const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
     QkTiles ta, tb;
     qk_load(ta, kb, row0, rend, wave, nw, j, kq);
+    const unsigned emask = static_cast<unsigned>(s_eg[e]) >> 16;
     lds_barrier();  // the previous segment's histogram flush is done
-    for (int i = threadIdx.x; i < d.G * kNumBins; i += blockDim.x) s_hist[i] = 0u;
+    for (int jj = 0; jj < d.G; ++jj)
+      if ((emask >> jj) & 1)
+        for (int i = threadIdx.x; i < kNumBins; i += blockDim.x) s_hist[jj * kNumBins + i] = 0u;
     lds_barrier();
     float* srow = b.score + static_cast<long>(bb * d.Hq + h) * d.score_stride;
     uint32_t* hrow = s_hist + j * kNumBins;
@@ -1204,9 +1227,12 @@ __device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const u
     lds_barrier();
     uint32_t* ghist = b.hist + static_cast<long>(bb * d.Hq + g * d.G) * kHistSeg * kNumBins +
                       (w % kHistSeg) * kNumBins;
-    for (int i = threadIdx.x; i < d.G * kNumBins; i += blockDim.x) {
-      const uint32_t c = s_hist[i];
-      if (c) atomicAdd(&ghist[(i / kNumBins) * kHistSeg * kNumBins + (i % kNumBins)], c);
+    for (int jj = 0; jj < d.G; ++jj) {
+      if (!((emask >> jj) & 1)) continue;
+      for (int i = threadIdx.x; i < kNumBins; i += blockDim.x) {
+        const uint32_t c = s_hist[jj * kNumBins + i];
+        if (c) atomicAdd(&ghist[jj * kHistSeg * kNumBins + i], c);
+      }
     }
     if (fused) {
       __syncthreads();  // every wave's scores and histogram adds of the segment are complete
@@ -1234,9 +1260,10 @@ __device__ __forceinline__ uint32_t key_score_bits(uint64_t u) {
 // are in LDS. Writes them out, aggregates the values (Eq. 12) and pushes
 // (q_bar_t, S_t) when `push`. Every thread of the block must call it.
 // ---------------------------------------------------------------------------
+// qv: element threadIdx.x of q_bar_t (threads < 128), loaded early by the caller.
 __device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh, int n, const uint16_t* v, float* out,
                                             int32_t* sel_out, int push, int fifo_slot, int fifo_count, HeadShared& sh,
-                                            const int32_t* s_sel, float* s_selsc) {
+                                            const int32_t* s_sel, float* s_selsc, float qv) {
   const int tid = threadIdx.x;
   const int bb = bh / d.Hq, g = (bh % d.Hq) / d.G;
   float mx = kNegInf;
@@ -1254,7 +1281,7 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh
     attend(s_sel, s_selsc, n, mx, vb, out + static_cast<long>(bh) * kHeadDim, nullptr, sh);
   }
   if (push) {
-    for (int t = tid; t < kHeadDim; t += blockDim.x) sh.qbar[t] = load_shared(b.qbar + static_cast<long>(bh) * kHeadDim + t);
+    if (tid < kHeadDim) sh.qbar[tid] = qv;
     lds_barrier();
     cache_push(d, b, bh, fifo_slot, fifo_count, sh.qbar, s_sel, n);
   }
@@ -1403,7 +1430,9 @@ __device__ __forceinline__ void finish_phase(const Dims& d, const Bufs& b, int b
                                              HeadShared& sh, unsigned char* dyn) {
   const int tid = threadIdx.x;
   const int nch = (length + kCollectChunk - 1) / kCollectChunk;
-  // one round of loads: this thread's chunk counts and the boundary record
+  // one round of loads: this thread's chunk counts, the boundary record and
+  // (for the push) q_bar_t
+  const float qv = push && tid < kHeadDim ? load_shared(b.qbar + static_cast<long>(bh) * kHeadDim + tid) : 0.f;
   const int per = (nch + kHeadThreads - 1) / kHeadThreads;  // <= 2 (n_chunks <= 1024)
   const int q0 = min(tid * per, nch), q1 = min(q0 + per, nch);
   const int32_t* ccnt = b.ccnt + static_cast<long>(bh) * d.n_chunks;
@@ -1545,7 +1574,7 @@ __device__ __forceinline__ void finish_phase(const Dims& d, const Bufs& b, int b
   }
   n = min(n, keff);
   lds_barrier();
-  finish_tail(d, b, bh, n, v, out, sel_out, push, fifo_slot, fifo_count, sh, s_sel, s_selsc);
+  finish_tail(d, b, bh, n, v, out, sel_out, push, fifo_slot, fifo_count, sh, s_sel, s_selsc, qv);
 }
 
 // ---------------------------------------------------------------------------
