@@ -104,16 +104,28 @@ def _counter_rows(path):
     return rows
 
 
-def _per_dispatch(rows, counter):
-    """{kernel short name: [counter value per dispatch, in dispatch order]} (KiB)."""
+def _per_dispatch(rows, counter, last=None):
+    """{(kernel short name, grid size): [counter value per dispatch, in dispatch
+    order]} (KiB). A call that launches one kernel twice with different grids
+    (the exact calls) shows up as two keys. With `last`, only each kernel's
+    timed window is kept: its last `last` calls, i.e. its last
+    last * (grids among its last `last` dispatches) dispatches."""
     per = {}
     for r in rows:
         if r.get("Counter_Name") != counter:
             continue
         name = r["Kernel_Name"].split("(")[0].split("::")[-1].strip()
-        per.setdefault(name, {}).setdefault(int(r["Dispatch_Id"]), 0.0)
-        per[name][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
-    return {k: [v[i] for i in sorted(v)] for k, v in per.items()}
+        per.setdefault(name, {}).setdefault(int(r["Dispatch_Id"]), [int(r.get("Grid_Size") or 0), 0.0])
+        per[name][int(r["Dispatch_Id"])][1] += float(r["Counter_Value"])
+    out = {}
+    for name, dd in per.items():
+        ds = [dd[i] for i in sorted(dd)]
+        if last is not None:
+            ngrid = len({g for g, _ in ds[-last:]})
+            ds = ds[-last * ngrid:]
+        for g, v in ds:
+            out.setdefault((name, g), []).append(v)
+    return out
 
 
 def summarize_traffic(root, last, workload):
@@ -123,7 +135,7 @@ def summarize_traffic(root, last, workload):
     scale = {}
     for c in TRAFFIC_COUNTERS:
         per = _per_dispatch(_counter_rows(os.path.join(root, f"copy_{c}")), c)
-        vals = [v for k, vs in per.items() if "copy" in k.lower() for v in vs
+        vals = [v for k, vs in per.items() if "copy" in k[0].lower() for v in vs
                 if v * 1024 > COPY_BYTES / 2]
         if not vals:
             raise SystemExit(f"no copy dispatch with {c} under {root}/copy_{c}")
@@ -134,24 +146,42 @@ def summarize_traffic(root, last, workload):
         for c in TRAFFIC_COUNTERS:
             d = os.path.join(root, f"{leg}_{c}")
             if os.path.isdir(d):
-                got[c] = _per_dispatch(_counter_rows(d), c)
+                got[c] = _per_dispatch(_counter_rows(d), c, last)
         if len(got) != len(TRAFFIC_COUNTERS):
             continue
-        for kern in sorted(got["FETCH_SIZE"]):
-            if not kern.startswith("k_") or kern not in got["WRITE_SIZE"]:
+        # per kernel: the launches of one call (one per grid size) summed
+        names = sorted({k[0] for k in got["FETCH_SIZE"] if k[0].startswith("k_")})
+        for kern in names:
+            parts, fb, wb, nd = [], 0.0, 0.0, 0
+            for key in sorted(k for k in got["FETCH_SIZE"] if k[0] == kern):
+                if key not in got["WRITE_SIZE"]:
+                    continue
+                f = got["FETCH_SIZE"][key]
+                w = got["WRITE_SIZE"][key]
+                pf = float(np.mean(f)) * 1024 * scale["FETCH_SIZE"]
+                pw = float(np.mean(w)) * 1024 * scale["WRITE_SIZE"]
+                parts.append({"grid_threads": key[1], "dispatches": len(f), "fetch_bytes": int(pf),
+                              "write_bytes": int(pw)})
+                fb, wb, nd = fb + pf, wb + pw, nd + len(f)
+            if not parts:
                 continue
-            f = got["FETCH_SIZE"][kern][-last:]
-            w = got["WRITE_SIZE"][kern][-last:]
-            fb = float(np.mean(f)) * 1024 * scale["FETCH_SIZE"]
-            wb = float(np.mean(w)) * 1024 * scale["WRITE_SIZE"]
-            out.append({"kernel": kern, "workload": workload, "leg": leg, "dispatches": len(f),
+            out.append({"kernel": kern, "workload": workload, "leg": leg, "dispatches": nd,
                         "fetch_bytes_per_launch": int(fb), "write_bytes_per_launch": int(wb),
-                        "hbm_bytes_per_launch": int(fb + wb),
+                        "hbm_bytes_per_launch": int(fb + wb), "launches_per_call": parts,
                         "copy_scale": {c: round(scale[c], 4) for c in TRAFFIC_COUNTERS},
                         "kernel_source_sha": kernel_source_hash()})
+    doc = {"commands": [
+        "(on one MI355X, from the repository root after `cd /tmp && export TMPDIR=/tmp`, absolute paths)",
+        "rocprofv3 --pmc <C> --output-format csv -d gpurun_out/pmc/copy_<C> -o pmc -- python3 bench.py "
+        "--copy-calibration",
+        "rocprofv3 --pmc <C> --output-format csv -d gpurun_out/pmc/<LEG>_<C> -o pmc -- python3 bench.py "
+        "--only <LEG> --steps 2048 --warmup 64 --no-cpu-baseline --no-breakdown",
+        "for C in FETCH_SIZE WRITE_SIZE, LEG in natural exact reuse; then",
+        f"python3 bench.py --summarize-traffic gpurun_out/pmc --last {last}"],
+        "rows": out}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as fh:
-        json.dump(out, fh, indent=1)
+        json.dump(doc, fh, indent=1)
     for r in out:
         print(f"{r['leg']:8s} {r['kernel']:12s} fetch {r['fetch_bytes_per_launch'] / 1e6:9.3f} MB "
               f"write {r['write_bytes_per_launch'] / 1e6:8.3f} MB per launch")
@@ -185,23 +215,35 @@ def summarize_kernels(root, last, workload):
             continue
         with open(trace) as f:
             rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
-        per = {}
+        # the timed window: the last `last` calls of each kernel (a call may launch
+        # it more than once, with different grids), then one row per grid
+        by_name = {}
         for r in rows:
             name = r["Kernel_Name"].split("(")[0].split("::")[-1].strip()
-            per.setdefault(name, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+            by_name.setdefault(name, []).append(
+                (int(r.get("Grid_Size_X") or 0), int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+        per = {}
+        for name, ds in by_name.items():
+            grids = {g for g, _, _ in ds[-last:]}
+            for g, a, e in ds[-last * len(grids):]:
+                per.setdefault((name, g), []).append((a, e))
         lines += [f"## {leg}: {LEG_TITLES[leg]}", "", "```", PROFILE_CMD.format(leg=leg, steps=last), "```", "",
-                  f"Timed dispatches (last {last} of each kernel):", "",
-                  "| kernel | dispatches | avg µs | median µs | min µs | max µs |", "|---|---|---|---|---|---|"]
-        for name in sorted(k for k in per if k.startswith("k_") and k != "k_reset"):
-            dur = np.array([(e - s) / 1000.0 for s, e in per[name][-last:]])
-            lines.append(f"| {name} | {len(dur)} | {dur.mean():.2f} | {np.median(dur):.2f} | {dur.min():.2f} | "
-                         f"{dur.max():.2f} |")
-        if "k_step" in per:
-            st = np.array([s for s, _ in per["k_step"][-last:]], dtype=np.float64)
+                  f"Timed dispatches (last {last} of each kernel and grid; a call that launches the kernel "
+                  "twice, with different grids, has one row per launch):", "",
+                  "| kernel | grid (threads) | dispatches | avg µs | median µs | min µs | max µs |",
+                  "|---|---|---|---|---|---|---|"]
+        for key in sorted(k for k in per if k[0].startswith("k_") and k[0] != "k_reset"):
+            dur = np.array([(e - s) / 1000.0 for s, e in per[key][-last:]])
+            lines.append(f"| {key[0]} | {key[1]} | {len(dur)} | {dur.mean():.2f} | {np.median(dur):.2f} | "
+                         f"{dur.min():.2f} | {dur.max():.2f} |")
+        steps = [k for k in per if k[0] == "k_step"]
+        if steps:
+            step_key = min(steps, key=lambda k: min(s for s, _ in per[k][-last:]))  # a call's first launch
+            st = np.array([s for s, _ in per[step_key][-last:]], dtype=np.float64)
             gap = np.diff(st) / 1000.0
             lines += ["", f"Step period under the tracer (k_step start to the next k_step start): median "
-                          f"{np.median(gap):.2f} µs, mean {gap.mean():.2f} µs (the tracer serialises "
-                          "dispatches, so this is longer than the untraced step)."]
+                          f"{np.median(gap):.2f} µs, mean {gap.mean():.2f} µs (under the tracer; the untraced "
+                          "step time is the bench line's value)."]
         if os.path.exists(stats):
             with open(stats) as f:
                 srows = list(csv.DictReader(f))
@@ -233,7 +275,8 @@ def load_traffic(kernel, workload, leg):
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rows = json.load(f)
+        doc = json.load(f)
+    rows = doc["rows"] if isinstance(doc, dict) else doc
     for r in rows:
         if r.get("kernel") == kernel and r.get("workload") == workload and \
                 r.get("leg") == leg and r.get("kernel_source_sha") == kernel_source_hash():
