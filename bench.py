@@ -11,15 +11,16 @@ resident in HBM before the timed region; nothing is allocated inside it.
 
 Prints one JSON line: the metric is microseconds per decode step per layer
 (lower is better) on the 128K-context, K = 512 GQA layer, with the exact
-Top-K baseline, a forced-reuse run, the path mix, a per-kernel breakdown, the
-roofline of the kernel with the largest share of the step (and of every
-kernel of the step), of the score kernel on all-exact steps, whole-step
-rooflines of the exact and the forced-reuse steps, and the CPU oracle
-baseline.
+Top-K baseline, a forced-reuse run, the path mix, the roofline of the step
+kernel (a decode step is one launch of it) over the timed steps, the same on
+exact calls, whole-step rooflines of the exact and the forced-reuse steps,
+event-bracketed per-launch times, and the CPU oracle baseline.
 
-Counter support: --copy-calibration runs plain copies of known size, and
+Counter support: --copy-calibration runs plain copies of known size,
 --summarize-traffic turns rocprofv3 FETCH_SIZE / WRITE_SIZE runs into the
-per-launch HBM bytes that the roofline objects report as "traffic".
+per-call HBM bytes that the roofline objects report as "traffic", and
+--summarize-kernels turns rocprofv3 kernel traces into the committed
+duration tables.
 """
 from __future__ import annotations
 
@@ -422,12 +423,12 @@ def main():
         }
         return {k: float(v) / T for k, v in per.items()}
 
-    def roofline(kernel, alg, us_launch, leg):
-        gbs = alg / (us_launch * 1e-6) / 1e9
+    def roofline(kernel, alg, us, leg, per="launch"):
+        gbs = alg / (us * 1e-6) / 1e9
         return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                 "traffic": load_traffic(kernel, wl.name, leg),
-                "algorithmic_bytes_per_launch": int(alg), "us_per_launch": us_launch}
+                f"algorithmic_bytes_per_{per}": int(alg), f"us_per_{per}": round(us, 3)}
 
     # --- natural ReTopK step (the headline value) ---------------------------
     if args.only in (None, "natural"):
@@ -451,26 +452,18 @@ def main():
                     "p50": int(np.percentile(mr, 50)) if mr.size else None,
                     "p90": int(np.percentile(mr, 90)) if mr.size else None,
                     "max": int(mr.max()) if mr.size else None}}
+        # A decode step is one launch of k_step, so the timed region's per-step
+        # time (HIP events on the launch stream) is its average launch duration;
+        # the algorithmic bytes are averaged over the same timed steps.
+        mean_len = L0 + (args.warmup + args.steps / 2) / nl
+        result["roofline"] = roofline("k_step", kernel_bytes(path, m, mean_len)["k_step"], us, "natural")
         for layer in nat:
             layer.close()
         if not args.no_breakdown:
+            # per-launch times with an event pair around every launch (each pair
+            # adds a dispatch gap, so these run longer than the timed step)
             nat = make_layers()
-            kb = kernel_breakdown(nat)
-            result["kernels_natural"] = kb
-            # roofline of every kernel of the step; the headline one is the
-            # kernel with the largest share of the step time
-            path_b, m_b = timed_paths(nat)
-            mean_len = L0 + (args.warmup + args.steps / 2) / nl
-            alg = kernel_bytes(path_b, m_b, mean_len)
-            rl = {kn: roofline(kn, alg[kn], kb[kn]["us_per_launch"], "natural")
-                  for kn in alg if kn in kb}
-            if rl:
-                dom = max(rl, key=lambda kn: kb[kn]["us_per_step"])
-                result["roofline"] = rl[dom]
-                result["rooflines_natural"] = {kn: {k: r[k] for k in ("achieved", "frac", "traffic",
-                                                                      "algorithmic_bytes_per_launch",
-                                                                      "us_per_launch")}
-                                               for kn, r in rl.items()}
+            result["kernels_natural"] = kernel_breakdown(nat)
             for layer in nat:
                 layer.close()
 
@@ -497,19 +490,16 @@ def main():
                                          "frac": round(gbs / HBM_PEAK_GBS, 4),
                                          "algorithmic_bytes_per_step": int(step_alg),
                                          "unique_v_rows": int(v_rows)}
+        # an exact call is two launches of k_step (head and score work groups,
+        # then the tail), timed together per call
+        result["roofline_exact"] = roofline("k_step", step_alg, us_ex, "exact", per="call")
         for layer in ex:
             layer.close()
         if not args.no_breakdown:
             ex = make_layers()
-            kb = kernel_breakdown(ex, exact=True)
-            result["kernels_exact"] = kb
+            result["kernels_exact"] = kernel_breakdown(ex, exact=True)
             for layer in ex:
                 layer.close()
-            # the step kernel on all-exact steps: every KV group's key rows once, the
-            # selected value rows (union per group), q in and out
-            kq = kb.get("k_step")
-            if kq:
-                result["roofline_exact"] = roofline("k_step", step_alg, kq["us_per_launch"], "exact")
         if "value" in result:
             result["speedup_vs_exact"] = round(us_ex / result["value"], 3)
 
