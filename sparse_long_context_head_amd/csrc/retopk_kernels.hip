@@ -272,6 +272,27 @@ __device__ __forceinline__ void bitmap_clear(uint32_t* bm) {
 
 __device__ __forceinline__ void bitmap_set(uint32_t* bm, int x) { atomicOr(&bm[bm_at(x >> 5)], 1u << (x & 31)); }
 
+// Emit, in ascending order, the positions base + 32 * w + bit of every set bit
+// of words [w0, w1) of an LDS bitmap window, one byte (8 positions) per
+// thread: for dense stretches, where a thread owning whole words would emit
+// hundreds of bits one after another. w1 - w0 <= blockDim / 4. Returns the
+// number emitted (the same value in every thread). Every thread of the block
+// must call it.
+__device__ __forceinline__ int bitmap_emit_bytes(const uint32_t* bm, int w0, int w1, int base, int32_t* out,
+                                                 int* tmp) {
+  const int t = threadIdx.x, w = w0 + (t >> 2);
+  const uint32_t byte = w < w1 ? (bm[bm_at(w)] >> (8 * (t & 3))) & 0xffu : 0u;
+  int total;
+  int off = block_exclusive_scan(__popc(byte), &total, tmp);
+  uint32_t bits = byte;
+  while (bits) {
+    const int b = __ffs(bits) - 1;
+    out[off++] = base + w * 32 + 8 * (t & 3) + b;
+    bits &= bits - 1;
+  }
+  return total;
+}
+
 // Emit, in ascending order, the positions base + bit of every set bit of an
 // LDS bitmap window of `nwords` words to out[0 ..). Returns the number emitted
 // (the same value in every thread). The words are split evenly over the
@@ -843,6 +864,7 @@ __device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4]
 // (cand_cap each).
 // ---------------------------------------------------------------------------
 constexpr int kCandU = 20;  // candidate rows per 16-lane group in flight: 640 per round
+constexpr int kDenseWords = kHeadThreads / 4;  // bitmap words emitted a byte per thread (4096 positions)
 
 __device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
                                           const uint16_t* k, const uint16_t* v, float* out, int length, int t_dec,
@@ -1015,7 +1037,13 @@ __device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const ui
       }
     }
     lds_barrier();
-    M += bitmap_emit(bm, nwords, base, s_cand + M, sh.tmp);
+    // Positions just below the window are dense (recent decode positions carry
+    // forward from support to support): the last kDenseWords words of the
+    // window's bitmap go out a byte per thread, the rest a slice of words per
+    // thread.
+    const int wsplit = max(0, nwords - kDenseWords);
+    M += bitmap_emit(bm, wsplit, base, s_cand + M, sh.tmp);
+    M += bitmap_emit_bytes(bm, wsplit, nwords, base, s_cand + M, sh.tmp);
     lds_barrier();
   }
   for (int x = wlo + tid; x < length; x += blockDim.x) s_cand[M + (x - wlo)] = x;
