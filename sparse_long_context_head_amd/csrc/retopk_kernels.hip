@@ -273,24 +273,47 @@ __device__ __forceinline__ void bitmap_clear(uint32_t* bm) {
 __device__ __forceinline__ void bitmap_set(uint32_t* bm, int x) { atomicOr(&bm[bm_at(x >> 5)], 1u << (x & 31)); }
 
 // Emit, in ascending order, the positions base + 32 * w + bit of every set bit
-// of words [w0, w1) of an LDS bitmap window, one byte (8 positions) per
-// thread: for dense stretches, where a thread owning whole words would emit
-// hundreds of bits one after another. w1 - w0 <= blockDim / 4. Returns the
-// number emitted (the same value in every thread). Every thread of the block
-// must call it.
-__device__ __forceinline__ int bitmap_emit_bytes(const uint32_t* bm, int w0, int w1, int base, int32_t* out,
+// of words [0, nwords) of an LDS bitmap window. Words [0, wsplit) are taken a
+// slice of per = ceil(wsplit / blockDim) <= kSliceWords words per thread;
+// words [wsplit, nwords) (at most blockDim / 4) a byte (8 positions) per
+// thread, for dense stretches, where a thread owning whole words would emit
+// hundreds of bits one after another. One two-value block scan places both.
+// Returns the number emitted (the same value in every thread). Every thread of
+// the block must call it.
+__device__ __forceinline__ int bitmap_emit_split(const uint32_t* bm, int wsplit, int nwords, int base, int32_t* out,
                                                  int* tmp) {
-  const int t = threadIdx.x, w = w0 + (t >> 2);
-  const uint32_t byte = w < w1 ? (bm[bm_at(w)] >> (8 * (t & 3))) & 0xffu : 0u;
-  int total;
-  int off = block_exclusive_scan(__popc(byte), &total, tmp);
+  const int t = threadIdx.x;
+  const int per = (wsplit + blockDim.x - 1) / blockDim.x;
+  uint32_t w[kSliceWords];
+  const int w0 = t * per;
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < kSliceWords; ++i) {
+    w[i] = (i < per && w0 + i < wsplit) ? bm[bm_at(w0 + i)] : 0u;
+    cnt += __popc(w[i]);
+  }
+  const int wd = wsplit + (t >> 2);
+  const uint32_t byte = wd < nwords ? (bm[bm_at(wd)] >> (8 * (t & 3))) & 0xffu : 0u;
+  int off, offd, tot, totd;
+  block_exclusive_scan2(cnt, __popc(byte), &off, &offd, &tot, &totd, tmp);
+#pragma unroll
+  for (int i = 0; i < kSliceWords; ++i) {
+    if (i >= per) break;  // uniform
+    uint32_t bits = w[i];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      out[off++] = base + (w0 + i) * 32 + b;
+      bits &= bits - 1;
+    }
+  }
+  offd += tot;
   uint32_t bits = byte;
   while (bits) {
     const int b = __ffs(bits) - 1;
-    out[off++] = base + w * 32 + 8 * (t & 3) + b;
+    out[offd++] = base + wd * 32 + 8 * (t & 3) + b;
     bits &= bits - 1;
   }
-  return total;
+  return tot + totd;
 }
 
 // Emit, in ascending order, the positions base + bit of every set bit of an
@@ -1041,9 +1064,7 @@ __device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const ui
     // forward from support to support): the last kDenseWords words of the
     // window's bitmap go out a byte per thread, the rest a slice of words per
     // thread.
-    const int wsplit = max(0, nwords - kDenseWords);
-    M += bitmap_emit(bm, wsplit, base, s_cand + M, sh.tmp);
-    M += bitmap_emit_bytes(bm, wsplit, nwords, base, s_cand + M, sh.tmp);
+    M += bitmap_emit_split(bm, max(0, nwords - kDenseWords), nwords, base, s_cand + M, sh.tmp);
     lds_barrier();
   }
   for (int x = wlo + tid; x < length; x += blockDim.x) s_cand[M + (x - wlo)] = x;
