@@ -886,7 +886,34 @@ __device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4]
 // (K each) and one flag byte per candidate; then A_t and its scores
 // (cand_cap each).
 // ---------------------------------------------------------------------------
-constexpr int kCandU = 20;  // candidate rows per 16-lane group in flight: 640 per round
+constexpr int kCandU = 20;     // candidate rows per 16-lane group in flight: 640 per round
+constexpr int kCandWide = 28;  // ... for 641 .. 896 candidates: one round of 896
+
+// Candidate scores (Eq. 10): 16 lanes per key row (16 bytes each), U rows in
+// flight per 16-lane group, bf16 pair products accumulated in fp32 (dot2).
+// Every thread of the block must call it.
+template <int U>
+__device__ __forceinline__ void cand_scores(const uint16_t* kb, const int32_t* s_cand, int M, uint4 qw, int rg,
+                                            int rpr, int part, float* s_sc) {
+  for (int r0 = 0; r0 < M; r0 += rpr * U) {
+    uint4 kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = min(r0 + u * rpr + rg, M - 1);  // clamped: a valid row, its score is not stored
+      kv[u] = *reinterpret_cast<const uint4*>(kb + static_cast<long>(s_cand[i]) * kHeadDim + 8 * part);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = r0 + u * rpr + rg;
+      float sc = dot2_bf16(kv[u].x, qw.x, 0.f);
+      sc = dot2_bf16(kv[u].y, qw.y, sc);
+      sc = dot2_bf16(kv[u].z, qw.z, sc);
+      sc = dot2_bf16(kv[u].w, qw.w, sc);
+      sc = row_sum(sc);
+      if (part == 0 && i < M) s_sc[i] = sc;
+    }
+  }
+}
 constexpr int kDenseWords = kHeadThreads / 4;  // bitmap words emitted a byte per thread (4096 positions)
 
 __device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
@@ -1081,29 +1108,14 @@ __device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const ui
   const uint16_t* vb = v + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
   const int rg = tid >> 4, rpr = blockDim.x >> 4;
   {
-    // 16 lanes per key row (16 bytes each), kCandU rows in flight per thread,
-    // bf16 pair products accumulated in fp32 (dot2)
+    // kCandU rows in flight per 16-lane group; a wider round for candidate
+    // sets that one such round misses only by a little, so that they do not
+    // pay a second dependent round trip
     const uint4 qw = *reinterpret_cast<const uint4*>(q + bb * q_sb + h * q_sh + 8 * part);
-    constexpr int U = kCandU;
-    for (int r0 = 0; r0 < M; r0 += rpr * U) {
-      uint4 kv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = min(r0 + u * rpr + rg, M - 1);
-        const long row = static_cast<long>(s_cand[i]) * kHeadDim + 8 * part;
-        kv[u] = *reinterpret_cast<const uint4*>(kb + row);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = r0 + u * rpr + rg;
-        float sc = dot2_bf16(kv[u].x, qw.x, 0.f);
-        sc = dot2_bf16(kv[u].y, qw.y, sc);
-        sc = dot2_bf16(kv[u].z, qw.z, sc);
-        sc = dot2_bf16(kv[u].w, qw.w, sc);
-        sc = row_sum(sc);
-        if (part == 0 && i < M) s_sc[i] = sc;
-      }
-    }
+    if (M > rpr * kCandU && M <= rpr * kCandWide)
+      cand_scores<kCandWide>(kb, s_cand, M, qw, rg, rpr, part, s_sc);
+    else
+      cand_scores<kCandU>(kb, s_cand, M, qw, rg, rpr, part, s_sc);
   }
   lds_barrier();
   float mx = kNegInf, mn = kPosInf;
