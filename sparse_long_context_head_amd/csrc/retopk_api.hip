@@ -178,7 +178,7 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
     probe.K = p.top_k;
     probe.G = p.n_q_heads / p.n_kv_heads;
     probe.cand_cap = static_cast<int>(cand);
-    probe.n_chunks = (p.max_len + kCollectChunk - 1) / kCollectChunk;
+    probe.n_cu = kHeadThreads;  // the most score work groups a call has
     if (head_lds_bytes(probe) > static_cast<size_t>(kLdsLimit) ||
         finish_lds_bytes(probe) > static_cast<size_t>(kLdsLimit) ||
         score_lds_bytes(probe) > static_cast<size_t>(kLdsLimit))
@@ -217,7 +217,6 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   d.R = p.top_r;
   d.Tr = p.refresh_every;
   d.cand_cap = static_cast<int>(cand);
-  d.n_chunks = (p.max_len + kCollectChunk - 1) / kCollectChunk;
   d.n_cu = n_cu;
   d.tau = p.tau;
 
@@ -240,14 +239,12 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   A(&b.m, BH);
   A(&b.cand, BH * d.cand_cap);
   A(&b.score, BH * d.score_stride);
-  A(&b.hist, BH * kHistSeg * kNumBins);
+  A(&b.hist, BH * 2 * kNumBins);
   A(&b.hits, BH * d.max_len);
-  A(&b.ccnt, BH * d.n_chunks);
-  A(&b.bnd, BH * 4);
-  A(&b.tailcnt, BH);
+  A(&b.ccnt, BH * d.n_cu);
   A(&b.dec, BH);
   A(&b.err, 1);
-  A(&b.scored, 2 * static_cast<size_t>(d.B) * d.Hkv);
+  A(&b.wdone, 2 * static_cast<size_t>(d.n_cu));
   A(&b.bkeys, BH * d.max_len);
   A(&b.sel, BH * d.K);
   A(&b.selsc, BH * d.K);

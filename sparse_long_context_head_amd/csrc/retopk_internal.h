@@ -17,9 +17,7 @@ constexpr int kNumBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
 constexpr int kStatsCap = 4096;      // decode steps kept in the statistics ring
 constexpr int kExactMinRows = 2048;  // key rows per score work group of the full-history pass, at least
-constexpr int kHistSeg = 8;          // copies of each head's histogram (spreads the atomics)
 constexpr int kBoundaryLds = 4096;   // boundary-bin candidates resolved in LDS (32 KiB of 64-bit keys)
-constexpr int kCollectChunk = 16384; // positions per work group of the collect step
 constexpr int kHeadThreads = 512;    // threads of the per-head kernels
 constexpr int kBitmapWords = 8192;   // LDS bitmap window: 262144 token positions (32 KiB)
 constexpr int kLdsLimit = 124 * 1024;  // dynamic LDS a per-head kernel may use (static LDS <= 36 KiB)
@@ -32,7 +30,6 @@ struct Dims {
   int score_stride;        // row stride of the full-history score workspace (max_len rounded to 16)
   int K, C, W, R, Tr;
   int cand_cap;            // R*K + W
-  int n_chunks;            // ceil(max_len / kCollectChunk)
   int n_cu;                // compute units of the device
   double tau;
 };
@@ -53,17 +50,15 @@ struct Bufs {
   int32_t* m;              // [BH]      M_t
   int32_t* cand;           // [BH, cand_cap]  A_t ascending
   float* score;            // [BH, score_stride]  full-history q.k
-  uint32_t* hist;          // [BH, kHistSeg, kNumBins]  histogram of ordered score keys
+  uint32_t* hist;          // [BH, 2, kNumBins]  histogram of ordered score keys, a half per call parity
   uint2* hits;             // [BH, max_len] survivors (scores in the boundary bin or above) as
-                           //   (position, score bits), each chunk of kCollectChunk positions
-                           //   in its own region, in ascending position order
-  int32_t* ccnt;           // [BH, n_chunks] survivors per chunk
-  int32_t* bnd;            // [BH, 4] boundary bin, count above it, count in it
-  int32_t* tailcnt;        // [BH] collect work groups done (zero between calls)
-                           // (hist is zero between calls too: the tail clears an exact head's copies)
+                           //   (position, score bits); a score work group's segment [row0, rend)
+                           //   writes its own in ascending position order from row0 on
+  int32_t* ccnt;           // [BH, n_cu] survivors per score work group's segment
   int32_t* dec;            // [BH] path decision of the current call: call flag | exact
   int32_t* err;            // [1]  sticky device error word (1: a wait of the step kernel timed out)
-  int32_t* scored;         // [2, B*Hkv] key rows scored this call per KV group (call parity selects the half)
+  int32_t* wdone;          // [2, n_cu] per score work group, the call flag once its scores and histogram
+                           //   adds are out (row 0), once its survivors are out (row 1)
   uint64_t* bkeys;         // [BH, max_len] boundary-bin composite keys when more than kBoundaryLds
   int32_t* sel;            // [BH, K]   S_hat_t ascending
   float* selsc;            // [BH, K]   q.k of S_hat_t
@@ -83,8 +78,11 @@ size_t head_lds_bytes(const Dims& d);
 size_t score_lds_bytes(const Dims& d);
 size_t step_lds_bytes(const Dims& d);
 size_t finish_lds_bytes(const Dims& d);
-// Grid of the full-history score kernel at this length.
+// Score work groups of a call at this length.
 int score_grid(const Dims& d, int length);
+// Rows per query head of LDS a score work group keeps its scores in (0: they
+// go to the score workspace).
+int score_keep_rows(const Dims& d, int length, int n_score);
 
 // Launch helpers (retopk_kernels.hip). Each returns the hipError_t of the
 // launch. A decode step, the exact Top-K baseline and the cache

@@ -704,6 +704,7 @@ __device__ __forceinline__ void cache_push(const Dims& d, const Bufs& b, int bh,
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) float lds_float;  // a float in LDS (ds_* accesses)
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -716,25 +717,42 @@ size_t head_lds_bytes(const Dims& d) {
 
 size_t score_lds_bytes(const Dims& d) { return static_cast<size_t>(d.G) * kNumBins * 4; }
 
+// Every launch takes kLdsLimit: one 512-thread work group per CU is resident
+// anyway (registers), and a score work group keeps its scores in what its
+// histograms leave free.
 size_t step_lds_bytes(const Dims& d) {
-  return std::max({head_lds_bytes(d), score_lds_bytes(d), finish_lds_bytes(d)});
+  return std::max({head_lds_bytes(d), score_lds_bytes(d), finish_lds_bytes(d), static_cast<size_t>(kLdsLimit)});
 }
 
 size_t finish_lds_bytes(const Dims& d) {
-  return 8 * static_cast<size_t>(kBoundaryLds) + (4 * (static_cast<size_t>(d.n_chunks) + 1) + 15) / 16 * 16 +
+  const size_t nw = static_cast<size_t>(std::min(d.n_cu, kHeadThreads));
+  return 8 * static_cast<size_t>(kBoundaryLds) + 4 * ((nw + 4) / 4 * 4 + (nw + 3) / 4 * 4) +
          8 * static_cast<size_t>(d.K);
 }
 
 int score_grid(const Dims& d, int length) {
   // one 512-thread work group per CU beside the head work groups (all resident
-  // at once, so none starts late), but at least half the CUs
-  const long cap = std::max(d.n_cu - d.B * d.Hq, d.n_cu / 2);
+  // at once, so none starts late), but at least half the CUs; at most one
+  // per thread of a work group (the finish reads one segment per thread)
+  const long cap = std::min<long>(std::max(d.n_cu - d.B * d.Hq, d.n_cu / 2), kHeadThreads);
   const long groups = static_cast<long>(d.B) * d.Hkv;
   const long want = groups * ((length + kExactMinRows - 1) / kExactMinRows);
   return static_cast<int>(std::max(1L, std::min(cap, want)));
 }
-// static LDS of k_step: the head role's shared state and rank table, the score role's group list
-static_assert(sizeof(HeadShared) + 2048 + 4 * 1024 + 2048 + 128 + kLdsLimit <= 160 * 1024, "k_step LDS");
+
+int score_keep_rows(const Dims& d, int length, int n_score) {
+  // the largest share a score work group can get (every KV group exact), its
+  // segments each starting at a 16-row boundary of LDS
+  const long T = static_cast<long>(d.B) * d.Hkv * length;
+  const long rows = (T + n_score - 1) / n_score + 16;
+  const long segs = (rows + length - 1) / length + 1;
+  const long keep = (rows + 16 * segs + 15) / 16 * 16;
+  const long bytes = static_cast<long>(d.G) * kNumBins * 4 + static_cast<long>(d.G) * (keep + 4) * 4;
+  return bytes <= kLdsLimit ? static_cast<int>(keep) : 0;
+}
+// static LDS of k_step: the head role's shared state and rank table, the score
+// role's group list and exact bits, the survivor pass's boundaries
+static_assert(sizeof(HeadShared) + 2048 + 4 * 1024 + 2048 + 512 + kLdsLimit <= 160 * 1024, "k_step LDS");
 
 // ---------------------------------------------------------------------------
 // Reset the FIFO bookkeeping before cache initialisation. One thread per head.
@@ -817,8 +835,11 @@ __device__ __forceinline__ void qk_load(QkTiles& t, const uint16_t* kb, int t0, 
   }
 }
 
+// Row r goes to ldst[r + off] (to_lds) or gdst[r + off]: two typed pointers,
+// so that each store is a plain LDS or global store.
 __device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4], int t0, int rend, int wave, int nw,
-                                         int kq, bool hv, bool sc1, float* srow, uint32_t* hrow) {
+                                         int kq, bool hv, bool to_lds, lds_float* ldst, float* gdst, int off,
+                                         uint32_t* hrow) {
 #pragma unroll
   for (int u = 0; u < kQkUnroll; ++u) {
     const int rbase = t0 + (u * nw + wave) * 16;
@@ -829,22 +850,21 @@ __device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4]
     // lane holds query head j for rows rbase + 4*kq + 0..3
     if (hv) {
       const int r = rbase + 4 * kq;
-      // sc1: the tail role reads the scores in this launch (device-scope stores)
       if (r + 3 < rend) {
-        if (sc1) {
-          store_shared2(srow + r, acc[0], acc[1]);
-          store_shared2(srow + r + 2, acc[2], acc[3]);
-        } else {
-          *reinterpret_cast<float4*>(srow + r) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        }
+        if (to_lds)
+          *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(ldst + r + off) = acc;
+        else
+          *reinterpret_cast<f32x4*>(gdst + r + off) = acc;
 #pragma unroll
         for (int e = 0; e < 4; ++e) atomicAdd(&hrow[order_key(acc[e]) >> kHistShift], 1u);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (r + e < rend) {
-            if (sc1) store_shared(srow + r + e, acc[e]);
-            else srow[r + e] = acc[e];
+            if (to_lds)
+              ldst[r + e + off] = acc[e];
+            else
+              gdst[r + e + off] = acc[e];
             atomicAdd(&hrow[order_key(acc[e]) >> kHistShift], 1u);
           }
         }
@@ -1041,14 +1061,9 @@ __device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const ui
       if (exact) b.st_m[o] = 0;
     }
   }
-  // publish the decision to the score and tail work groups (decode mode did
-  // so above; an exact head's histogram copies are zero: the previous call's
-  // tail cleared them after use); zero the next call's scored-row counter of
-  // group bh
-  if (tid == 0) {
-    if (mode != kModeDecode) store_shared(b.dec + bh, call_flag | (exact ? 1 : 0));
-    if (bh < d.B * d.Hkv) b.scored[((call_flag >> 1) & 1 ^ 1) * d.B * d.Hkv + bh] = 0;
-  }
+  // publish the decision to the score work groups (decode mode did so above;
+  // the histogram half of this call was cleared during the previous one)
+  if (tid == 0 && mode != kModeDecode) store_shared(b.dec + bh, call_flag | (exact ? 1 : 0));
   if (exact) {
     if (tid == 0) b.m[bh] = 0;
     return;
@@ -1157,37 +1172,430 @@ __device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const ui
 }
 
 // ---------------------------------------------------------------------------
-// K2, full-history scores (Eq. 4, unscaled) of every exact head, GQA-grouped.
-// The KV groups holding at least one exact head are listed in order; their
-// rows, concatenated, are split evenly over the whole grid (at 16-row
-// boundaries inside a group), so that one falling-back group uses every work
-// group. Each work group streams its rows exactly once and scores them for
-// all query heads of the group with MFMA 16x16x32 bf16 tiles (A = 16 key rows
-// x 32 dims, B = 32 dims x 16 query heads, fp32 accumulation). The loads of
-// the next 256 rows are in flight while the current ones are scored (two
-// register buffers; rows past the end are clamped to a valid row and
-// masked). Scores of exact heads go to the workspace and into a per-head
-// histogram of the top 10 bits of their ordered keys (LDS, flushed with
-// global atomics into one of kHistSeg copies chosen by the work group); the
-// Top-K kernel finds its boundary from it.
+// Composite keys of the exact Top-K: ordered score << 32 | ~index, so that a
+// larger key is a higher score, then a lower index; all keys are distinct.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t comp_key(float s, uint32_t idx) {
+  return (static_cast<uint64_t>(order_key(s)) << 32) | static_cast<uint64_t>(0xffffffffu - idx);
+}
+
+// The score half of a composite key back to the score's bits.
+__device__ __forceinline__ uint32_t key_score_bits(uint64_t u) {
+  const uint32_t ok = static_cast<uint32_t>(u >> 32);
+  return (ok & 0x80000000u) ? (ok & 0x7fffffffu) : ~ok;
+}
+
+// ---------------------------------------------------------------------------
+// Shared end of the exact finish: S_t (n indices, ascending) and their scores
+// are in LDS. Writes them out, aggregates the values (Eq. 12) and pushes
+// (q_bar_t, S_t) when `push`. Every thread of the block must call it.
+// ---------------------------------------------------------------------------
+// qv: element threadIdx.x of q_bar_t (threads < 128), loaded early by the caller.
+__device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh, int n, const uint16_t* v, float* out,
+                                            int32_t* sel_out, int push, int fifo_slot, int fifo_count, HeadShared& sh,
+                                            const int32_t* s_sel, float* s_selsc, float qv) {
+  const int tid = threadIdx.x;
+  const int bb = bh / d.Hq, g = (bh % d.Hq) / d.G;
+  float mx = kNegInf;
+  for (int i = tid; i < n; i += blockDim.x) {
+    mx = fmaxf(mx, s_selsc[i]);
+    b.sel[static_cast<long>(bh) * d.K + i] = s_sel[i];
+    b.selsc[static_cast<long>(bh) * d.K + i] = s_selsc[i];
+  }
+  mx = block_max_f32(mx, reinterpret_cast<float*>(sh.tmp));
+  if (tid == 0) b.sellen[bh] = n;
+  if (sel_out != nullptr)
+    for (int i = tid; i < d.K; i += blockDim.x) sel_out[static_cast<long>(bh) * d.K + i] = i < n ? s_sel[i] : -1;
+  if (v != nullptr && out != nullptr) {
+    const uint16_t* vb = v + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
+    attend(s_sel, s_selsc, n, mx, vb, out + static_cast<long>(bh) * kHeadDim, nullptr, sh);
+  }
+  if (push) {
+    if (tid < kHeadDim) sh.qbar[tid] = qv;
+    lds_barrier();
+    cache_push(d, b, bh, fifo_slot, fifo_count, sh.qbar, s_sel, n);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The exact heads of a call, GQA-grouped: full-history scores (Eq. 4,
+// unscaled), Global Top-K (Eq. 1), softmax-V (Eq. 12) and the cache update,
+// all run by the score work groups.
+//
+// Rows: the KV groups holding at least one exact head are listed in order;
+// their rows, concatenated (T = ne * L of them), are split evenly over the nW
+// score work groups: work group w owns [x_w, x_{w+1}), x_w = floor(w T / nW).
+// Inside a group a work group's rows start at a 16-row boundary; its rows of
+// one group are a segment [row0, rend).
+//
+// Phase 1, scores: every segment is streamed once and scored for all query
+//   heads of its group with MFMA 16x16x32 bf16 tiles (A = 16 key rows x 32
+//   dims, B = 32 dims x 16 query heads, fp32 accumulation), the loads of the
+//   next 512 rows in flight while the current ones are scored. The scores of
+//   exact heads stay in LDS when a work group's share fits (else they go to
+//   the score workspace) and are counted in a per-head histogram of the top
+//   10 bits of their ordered keys (LDS, then added into the call's half of
+//   the global one). The work group then sets its scored flag (the call
+//   flag, device scope).
+// Phase 2, survivors: once the group of a segment is fully scored (the scored
+//   flag of every work group with rows in it is the call's), one wave
+//   per exact head reads the head's histogram, finds the bin b1 holding the
+//   K-th largest score, and writes the segment's positions and scores in bin
+//   b1 or above, in ascending position order, to the segment's own region of
+//   the head's survivor row (starting at row0), and their count; the work
+//   group then sets its survivor flag.
+// Phase 3, finish: exact head m (of n_ex) of group e belongs to the work group
+//   whose rows hold x = e L + floor((2m + 1) L / (2 n_ex)). That work group
+//   finds b1 and the counts above and in it from the histogram, waits for
+//   the survivor flags of the group's work groups, selects the K best survivors
+//   (radix select over the key bits below bin b1), writes S_t, aggregates the
+//   values and pushes (q_bar_t, S_t).
+//
+// A head's histogram has a half per call parity: a call fills one while the
+// score work groups clear the other (used by the previous call) for the next.
+// A phase waits only for earlier phases, which never wait for later ones, and
+// every wait is bounded in time (a timeout sets the device error word and the
+// work group gives up the call). Head work groups never wait, so score work
+// groups not yet resident get a CU as the head work groups end.
 // ---------------------------------------------------------------------------
 constexpr int kMaxExactGroups = 1024;  // KV groups (batch x KV heads) the row split can list
 constexpr int kPollRounds = 20000;     // polls of the decision flags before giving up (several ms)
 
-// w: this score work group's index among the nW of them.
-// all_exact: every head of the call is exact (no flags to wait for); fused:
-// the tail work groups run in the same launch (scores go out through
-// device-scope stores and the scored-row counters are kept).
+// Where work group ww's share starts: list position e and row r (rounded
+// down to 16 inside the group; e == ne, r == 0 at the end).
+__device__ __forceinline__ void split_at(long T, int nW, int length, int ne, int ww, int& e, int& r) {
+  const long x = static_cast<long>(ww) * T / nW;
+  e = static_cast<int>(x / length);
+  r = e < ne ? static_cast<int>(x % length) & ~15 : 0;
+}
+
+// Rows [lo, hi) of group e in work group ww's share (empty when lo >= hi).
+__device__ __forceinline__ void seg_rows(long T, int nW, int length, int ne, int ww, int e, int& lo, int& hi) {
+  int ea, ra, eb, rb;
+  split_at(T, nW, length, ne, ww, ea, ra);
+  split_at(T, nW, length, ne, ww + 1, eb, rb);
+  lo = ea < e ? 0 : (ea == e ? ra : length);
+  hi = eb > e ? length : (eb == e ? rb : 0);
+}
+
+// Lanes below this one with their bit set in m.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// Wait until flags[ww] == call_flag for every work group ww with rows in list
+// group e (one thread per work group; bounded in time, a timeout sets the
+// device error word). Every thread of the block must call it.
+__device__ __forceinline__ bool wait_group(const int32_t* flags, long T, int nW, int length, int ne, int e,
+                                           int call_flag, int32_t* err, int* s_go) {
+  const int tid = threadIdx.x;
+  bool chk = false;
+  if (tid < nW) {
+    int lo, hi;
+    seg_rows(T, nW, length, ne, tid, e, lo, hi);
+    chk = lo < hi;
+  }
+  const long long t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    const bool ok = !chk || load_shared(flags + tid) == call_flag;
+    if (__syncthreads_and(ok)) return true;
+    if (tid == 0) *s_go = __builtin_amdgcn_s_memrealtime() - t0 >= kWaitTicks ? -1 : 0;
+    lds_barrier();
+    if (*s_go < 0) {
+      if (tid == 0) store_shared(err, 1);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(kPollSleep);
+  }
+}
+
+// Index of the m-th set bit of mask (m < popcount(mask)).
+__device__ __forceinline__ int nth_bit(unsigned mask, int m) {
+  for (int i = 0; i < m; ++i) mask &= mask - 1;
+  return __ffs(mask) - 1;
+}
+
+// One wave: the bin b1 holding the keff-th largest key of a histogram
+// (kNumBins counters, read with device-scope loads), the count above b1 and
+// the count in b1 ({0, 0, 0} if the counts fall short of keff). Lane l holds
+// the 16 bins below kNumBins - 16 l. Every lane of the wave must call it.
+__device__ __forceinline__ int3 wave_boundary(const uint32_t* hist, int keff) {
+  const int lane = threadIdx.x & 63;
+  const int lo = kNumBins - 16 * (lane + 1);
+  uint32_t c[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint2 v = load_shared(reinterpret_cast<const uint2*>(hist + lo + 2 * i));
+    c[2 * i] = v.x;
+    c[2 * i + 1] = v.y;
+  }
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tot += static_cast<int>(c[i]);
+  const int incl = wave_incl_scan(tot);  // counts of this lane's bins and all above
+  int run = incl - tot;
+  int3 r = make_int3(0, 0, 0);
+  const bool here = run < keff && incl >= keff;
+  if (here) {
+    bool found = false;
+#pragma unroll
+    for (int i = 15; i >= 0; --i) {
+      if (!found && run + static_cast<int>(c[i]) >= keff) {
+        r = make_int3(lo + i, run, static_cast<int>(c[i]));
+        found = true;
+      }
+      run += static_cast<int>(c[i]);
+    }
+  }
+  const uint64_t m = __ballot(here);
+  if (m == 0) return make_int3(0, 0, 0);
+  const int src = __ffsll(static_cast<long long>(m)) - 1;
+  return make_int3(__builtin_amdgcn_readlane(r.x, src), __builtin_amdgcn_readlane(r.y, src),
+                   __builtin_amdgcn_readlane(r.z, src));
+}
+
+// Phase 2 for one segment [row0, rend) of KV group (bb, g), whose rows are all
+// scored: the survivors of every exact head jj of the group (bit jj of
+// emask), one wave per head: b1 from the head's histogram, then 64 rows per
+// ballot in position order with a running count (kEmitU ballots' worth of
+// scores read at once). Scores from LDS (kLds: head jj's row row0 + i at
+// sc[jj * stride + i]) or from the score workspace. Every thread of the block
+// must call it.
+constexpr int kEmitU = 8;
+
+template <bool kLds>
+__device__ __forceinline__ void emit_segment(const Dims& d, const Bufs& b, int bb, int g, unsigned emask, int row0,
+                                             int rend, int length, int w, int par, const float* sc, int stride) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int G = d.G;
+  const int h0 = bb * d.Hq + g * G;  // query head of jj = 0
+  const int nrows = rend - row0;
+  for (int jj = wave; jj < G; jj += nw) {
+    if (!((emask >> jj) & 1u)) continue;
+    const int b1 = wave_boundary(b.hist + (static_cast<long>(h0 + jj) * 2 + par) * kNumBins, min(d.K, length)).x;
+    const float* srow = kLds ? sc + jj * stride : b.score + static_cast<long>(h0 + jj) * d.score_stride + row0;
+    uint2* region = b.hits + static_cast<long>(h0 + jj) * d.max_len + row0;
+    int run = 0;
+    for (int c0 = 0; c0 < nrows; c0 += 64 * kEmitU) {
+      float x[kEmitU];
+#pragma unroll
+      for (int u = 0; u < kEmitU; ++u) x[u] = srow[min(c0 + 64 * u + lane, nrows - 1)];  // clamped, masked below
+#pragma unroll
+      for (int u = 0; u < kEmitU; ++u) {
+        const int i = c0 + 64 * u + lane;
+        const bool sv = (i < nrows) & (static_cast<int>(order_key(x[u]) >> kHistShift) >= b1);
+        const uint64_t m = __ballot(sv);
+        if (sv)
+          store_shared(region + run + lanes_below(m), make_uint2(static_cast<uint32_t>(row0 + i), __float_as_uint(x[u])));
+        run += __popcll(m);
+      }
+    }
+    if (lane == 0) store_shared(b.ccnt + static_cast<long>(h0 + jj) * d.n_cu + w, run);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase 4 (finish) for head bh of list group e, run by the work group the head
+// belongs to.
+//  1. The survivor counts of the group's segments give each segment's offset
+//     in the head's survivor list (ascending positions: the segments are in
+//     order).
+//  2. Each thread takes kSU consecutive survivors and classifies them: above
+//     b1 (all kept) or in b1 (candidates). The candidates' composite keys
+//     (score desc, index asc) are compacted (LDS, else the global spill row)
+//     and a radix select over the bits below their shared top 10 keeps the
+//     `need` = keff - (count above b1) best.
+//  3. A block scan over "kept" flags writes S_t in ascending index order.
+//
+// LDS (dynamic): candidate keys (kBoundaryLds), segment offsets (nW + 1) and
+// first rows (nW), S_t and its scores (K each).
+// ---------------------------------------------------------------------------
+constexpr int kSU = 8;  // survivors per thread per round
+
+// Every thread of the block must call it.
+// bd: (b1, count above b1, count in b1).
+__device__ __forceinline__ void finish_phase(const Dims& d, const Bufs& b, int bh, const uint16_t* v, float* out,
+                                             int32_t* sel_out, int length, int push, long T, int nW, int ne, int e,
+                                             int3 bd, HeadShared& sh, unsigned char* dyn) {
+  const int tid = threadIdx.x;
+  // one round of loads: this thread's segment count, the FIFO state and (for
+  // the push) q_bar_t
+  const float qv = push && tid < kHeadDim ? load_shared(b.qbar + static_cast<long>(bh) * kHeadDim + tid) : 0.f;
+  int slo = 0, shi = 0;
+  if (tid < nW) seg_rows(T, nW, length, ne, tid, e, slo, shi);
+  const int cc = (tid < nW && slo < shi) ? load_shared(b.ccnt + static_cast<long>(bh) * d.n_cu + tid) : 0;
+  const int fifo_slot = b.fifo[2 * bh], fifo_count = b.fifo[2 * bh + 1];
+  uint64_t* lkeys = reinterpret_cast<uint64_t*>(dyn);
+  int* aoff = reinterpret_cast<int*>(dyn + 8 * kBoundaryLds);
+  int* srow0 = aoff + (nW + 4) / 4 * 4;
+  const size_t off_c = 8 * kBoundaryLds + 4 * static_cast<size_t>((nW + 4) / 4 * 4 + (nW + 3) / 4 * 4);
+  int32_t* s_sel = reinterpret_cast<int32_t*>(dyn + off_c);
+  float* s_selsc = reinterpret_cast<float*>(dyn + off_c + 4 * static_cast<size_t>(d.K));
+  const int keff = min(d.K, length);
+  // (clamped: consistent scores and histogram never need it, but every index below stays in its row)
+  const int b1 = bd.x, n_above = min(max(bd.y, 0), keff - 1), n_bd = min(max(bd.z, 0), length);
+  const bool keys_lds = n_bd <= kBoundaryLds;
+  uint64_t* gkeys = b.bkeys + static_cast<long>(bh) * d.max_len;
+  const uint2* hits_row = b.hits + static_cast<long>(bh) * d.max_len;
+
+  // ---- 1. segment offsets ----
+  {
+    int tot;
+    const int o = block_exclusive_scan(cc, &tot, sh.tmp);
+    if (tid < nW) {
+      aoff[tid] = o;
+      srow0[tid] = slo;
+    }
+    if (tid == 0) aoff[nW] = tot;
+    lds_barrier();
+  }
+  const int ns = aoff[nW];
+
+  // ---- 2. classification, candidate keys, radix select ----
+  const int nrounds = (ns + kHeadThreads * kSU - 1) / (kHeadThreads * kSU);
+  int pos[kSU];
+  uint32_t sb[kSU];
+  auto load_round = [&](int rd) {
+    const int i0 = rd * kHeadThreads * kSU + tid * kSU;
+    // the segment holding survivor i0 (the last whose offset is <= i0), then
+    // forward from there for the following ones
+    int sg = 0;
+    if (i0 < ns) {
+      int hi = nW;
+      while (hi - sg > 1) {
+        const int mid = (sg + hi) >> 1;
+        if (aoff[mid] <= i0) sg = mid; else hi = mid;
+      }
+    }
+    uint2 e[kSU];
+#pragma unroll
+    for (int u = 0; u < kSU; ++u) {
+      const int i = i0 + u;
+      e[u] = make_uint2(0xffffffffu, 0u);
+      if (i < ns) {
+        while (aoff[sg + 1] <= i) ++sg;  // aoff[nW] = ns > i ends it
+        e[u] = load_shared(hits_row + srow0[sg] + (i - aoff[sg]));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSU; ++u) {
+      pos[u] = static_cast<int>(e[u].x);  // -1 past the end
+      sb[u] = e[u].y;
+    }
+  };
+  auto bin_of = [&](int u) { return static_cast<int>(order_key(__uint_as_float(sb[u])) >> kHistShift); };
+  auto in_b1 = [&](int u) { return (pos[u] >= 0) & (bin_of(u) == b1); };
+  auto above = [&](int u) { return (pos[u] >= 0) & (bin_of(u) > b1); };
+
+  // candidate keys, compacted in position order
+  {
+    int krun = 0;
+    for (int rd = 0; rd < nrounds; ++rd) {
+      load_round(rd);
+      int c = 0;
+#pragma unroll
+      for (int u = 0; u < kSU; ++u) c += in_b1(u);
+      int tot;
+      int o = krun + block_exclusive_scan(c, &tot, sh.tmp);
+#pragma unroll
+      for (int u = 0; u < kSU; ++u) {
+        if (in_b1(u)) {
+          const uint64_t key = comp_key(__uint_as_float(sb[u]), static_cast<uint32_t>(pos[u]));
+          if (o < n_bd) {
+            if (keys_lds) lkeys[o] = key;
+            else gkeys[o] = key;
+          }
+          ++o;
+        }
+      }
+      krun += tot;
+    }
+  }
+  lds_barrier();
+  // Radix select of the `need` best candidates. Their composite keys share
+  // the top 10 bits (the bin b1), so the digits start below them, 11 bits at
+  // a time: bits 53-43, 42-32 (score), 31-21, 20-10, 9-0 (index).
+  int need = keff - n_above;
+  int ncand = n_bd;
+  uint64_t mask = 0x3FFull << 54, prefix = static_cast<uint64_t>(b1) << 54;
+  int* bins = &sh.whist[0][0];
+  for (int shift = 43; ncand > need && need > 0; shift = shift >= 11 ? shift - 11 : 0) {
+    const uint64_t dmask = shift == 0 ? 0x3FFull : 0x7FFull;
+    reinterpret_cast<int4*>(bins)[tid] = make_int4(0, 0, 0, 0);
+    lds_barrier();
+    if (keys_lds) {
+      for (int i = tid; i < n_bd; i += blockDim.x) {
+        const uint64_t u = lkeys[i];
+        if ((u & mask) == prefix) atomicAdd(&bins[(u >> shift) & dmask], 1);
+      }
+    } else {
+      for (int i = tid; i < n_bd; i += blockDim.x) {
+        const uint64_t u = gkeys[i];
+        if ((u & mask) == prefix) atomicAdd(&bins[(u >> shift) & dmask], 1);
+      }
+    }
+    lds_barrier();
+    pick_bin2048(sh, need);
+    prefix |= static_cast<uint64_t>(sh.i0) << shift;
+    mask |= dmask << shift;
+    need = sh.i1;
+    ncand = sh.i2;
+    if (shift == 0) break;
+  }
+
+  // ---- 3. S_t in ascending index order: survivors above b1 and the kept candidates ----
+  int n = 0;
+  for (int rd = 0; rd < nrounds; ++rd) {
+    if (nrounds > 1) load_round(rd);  // one round: still in registers
+    bool keep[kSU];
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < kSU; ++u) {
+      keep[u] = above(u) |
+                (in_b1(u) & ((comp_key(__uint_as_float(sb[u]), static_cast<uint32_t>(pos[u])) & mask) >= prefix));
+      c += keep[u];
+    }
+    int tot;
+    int o = n + block_exclusive_scan(c, &tot, sh.tmp);
+#pragma unroll
+    for (int u = 0; u < kSU; ++u) {
+      if (keep[u]) {
+        if (o < d.K) {
+          s_sel[o] = pos[u];
+          s_selsc[o] = __uint_as_float(sb[u]);
+        }
+        ++o;
+      }
+    }
+    n += tot;
+  }
+  n = min(n, keff);
+  lds_barrier();
+  finish_tail(d, b, bh, n, v, out, sel_out, push, fifo_slot, fifo_count, sh, s_sel, s_selsc, qv);
+}
+
+// w: this score work group's index among the nW of them. all_exact: every
+// head of the call is exact (no flags to wait for). keep: rows per head of
+// LDS for the scores of phase 1 (a multiple of 16; 0: they go to the score
+// workspace).
 __device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
-                                           const uint16_t* k, int length, int call_flag, int w, int nW,
-                                           bool all_exact, bool fused) {
+                                           const uint16_t* k, const uint16_t* v, float* out, int32_t* sel_out,
+                                           int length, int push, int call_flag, int w, int nW, bool all_exact,
+                                           int keep, HeadShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int j = lane & 15, kq = lane >> 4;
   const int NG = d.B * d.Hkv, BH = d.B * d.Hq;
+  const int par = (call_flag >> 1) & 1;
   __shared__ int s_eg[kMaxExactGroups];  // listed group | its exact heads << 16 (bit jj: head jj of the group)
   __shared__ int s_tmp[8];
   __shared__ uint32_t s_ex[kMaxExactGroups * kMaxGroup / 32];  // exact bit of every head
-  extern __shared__ __align__(16) uint32_t s_hist[];  // [G, kNumBins]
+  extern __shared__ __align__(16) unsigned char dyn[];
+  // LDS: histograms [G, kNumBins] (phase 1), then the kept scores
+  // [G, keep + 4] (phase 1 -> 3); phase 4 reuses all of it
+  uint32_t* s_hist = reinterpret_cast<uint32_t*>(dyn);
+  const int stride = keep + 4;
+  float* s_sc = reinterpret_cast<float*>(dyn + static_cast<size_t>(d.G) * kNumBins * 4);
 
   // every head's decision of this call, published by the head work groups
   // (lower block indices, so already running); bounded wait
@@ -1239,21 +1647,20 @@ __device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const u
     }
   }
   lds_barrier();
+  // clear the other half of a slice of the heads' histograms for the next call
+  for (int hh = static_cast<int>(static_cast<long>(w) * BH / nW); hh < static_cast<int>(static_cast<long>(w + 1) * BH / nW);
+       ++hh) {
+    uint4* hz = reinterpret_cast<uint4*>(b.hist + (static_cast<long>(hh) * 2 + (par ^ 1)) * kNumBins);
+    for (int i = threadIdx.x; i < kNumBins / 4; i += blockDim.x) hz[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
   if (ne == 0) return;
-
-  // this work group's share of the concatenated exact rows: split point w ->
-  // (list position e, row r), r rounded down to a 16-row boundary
   const long T = static_cast<long>(ne) * length;
-  auto split = [&](int ww, int& e, int& r) {
-    const long x = static_cast<long>(ww) * T / nW;
-    e = static_cast<int>(x / length);
-    r = e < ne ? static_cast<int>(x % length) & ~15 : 0;
-  };
-  int e, r, e1, r1;
-  split(w, e, r);
-  split(w + 1, e1, r1);
-  const int kStage = 16 * kQkUnroll * nw;  // rows per stage
-  for (; e < e1 || (e == e1 && r < r1); ++e, r = 0) {
+  int e0, r0, e1, r1;
+  split_at(T, nW, length, ne, w, e0, r0);
+  split_at(T, nW, length, ne, w + 1, e1, r1);
+
+  // ---- phase 1: scores and histograms ----
+  for (int e = e0, r = r0, lb = 0; e < e1 || (e == e1 && r < r1); ++e, r = 0) {
     const int row0 = r, rend = e == e1 ? r1 : length;
     if (row0 >= rend) continue;
     const int bg = s_eg[e] & 0xffff;
@@ -1276,443 +1683,107 @@ __device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const u
       if ((emask >> jj) & 1)
         for (int i = threadIdx.x; i < kNumBins; i += blockDim.x) s_hist[jj * kNumBins + i] = 0u;
     lds_barrier();
-    float* srow = b.score + static_cast<long>(bb * d.Hq + h) * d.score_stride;
+    // row r of the segment goes to LDS row lb + (r - row0) of head j, or to
+    // the workspace row
+    const bool to_lds = keep > 0;
+    lds_float* ldst = (lds_float*)(s_sc + (j < d.G ? j : 0) * stride);  // (address-space cast)
+    float* gdst = b.score + static_cast<long>(bb * d.Hq + h) * d.score_stride;
+    const int off = to_lds ? lb - row0 : 0;
     uint32_t* hrow = s_hist + j * kNumBins;
+    const int kStage = 16 * kQkUnroll * nw;  // rows per stage
     for (int t0 = row0; t0 < rend; t0 += 2 * kStage) {
       qk_load(tb, kb, t0 + kStage, rend, wave, nw, j, kq);
-      qk_score(ta, bq, t0, rend, wave, nw, kq, hv, fused, srow, hrow);
+      qk_score(ta, bq, t0, rend, wave, nw, kq, hv, to_lds, ldst, gdst, off, hrow);
       if (t0 + kStage >= rend) break;
       qk_load(ta, kb, t0 + 2 * kStage, rend, wave, nw, j, kq);
-      qk_score(tb, bq, t0 + kStage, rend, wave, nw, kq, hv, fused, srow, hrow);
+      qk_score(tb, bq, t0 + kStage, rend, wave, nw, kq, hv, to_lds, ldst, gdst, off, hrow);
     }
     lds_barrier();
-    uint32_t* ghist = b.hist + static_cast<long>(bb * d.Hq + g * d.G) * kHistSeg * kNumBins +
-                      (w % kHistSeg) * kNumBins;
     for (int jj = 0; jj < d.G; ++jj) {
       if (!((emask >> jj) & 1)) continue;
+      uint32_t* ghist = b.hist + (static_cast<long>(bb * d.Hq + g * d.G + jj) * 2 + par) * kNumBins;
       for (int i = threadIdx.x; i < kNumBins; i += blockDim.x) {
         const uint32_t c = s_hist[jj * kNumBins + i];
-        if (c) atomicAdd(&ghist[jj * kHistSeg * kNumBins + i], c);
+        if (c) atomicAdd(&ghist[i], c);
       }
     }
-    if (fused) {
-      __syncthreads();  // every wave's scores and histogram adds of the segment are complete
-      if (threadIdx.x == 0) atomicAdd(&b.scored[((call_flag >> 1) & 1) * NG + bg], rend - row0);
-    }
+    lb += (rend - row0 + 15) & ~15;
   }
-}
+  __syncthreads();  // every wave's histogram adds are complete
+  if (threadIdx.x == 0) store_shared(b.wdone + w, call_flag);
 
-// ---------------------------------------------------------------------------
-// Composite keys of the exact Top-K: ordered score << 32 | ~index, so that a
-// larger key is a higher score, then a lower index; all keys are distinct.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t comp_key(float s, uint32_t idx) {
-  return (static_cast<uint64_t>(order_key(s)) << 32) | static_cast<uint64_t>(0xffffffffu - idx);
-}
-
-// The score half of a composite key back to the score's bits.
-__device__ __forceinline__ uint32_t key_score_bits(uint64_t u) {
-  const uint32_t ok = static_cast<uint32_t>(u >> 32);
-  return (ok & 0x80000000u) ? (ok & 0x7fffffffu) : ~ok;
-}
-
-// ---------------------------------------------------------------------------
-// Shared end of the exact finish: S_t (n indices, ascending) and their scores
-// are in LDS. Writes them out, aggregates the values (Eq. 12) and pushes
-// (q_bar_t, S_t) when `push`. Every thread of the block must call it.
-// ---------------------------------------------------------------------------
-// qv: element threadIdx.x of q_bar_t (threads < 128), loaded early by the caller.
-__device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh, int n, const uint16_t* v, float* out,
-                                            int32_t* sel_out, int push, int fifo_slot, int fifo_count, HeadShared& sh,
-                                            const int32_t* s_sel, float* s_selsc, float qv) {
-  const int tid = threadIdx.x;
-  const int bb = bh / d.Hq, g = (bh % d.Hq) / d.G;
-  float mx = kNegInf;
-  for (int i = tid; i < n; i += blockDim.x) {
-    mx = fmaxf(mx, s_selsc[i]);
-    b.sel[static_cast<long>(bh) * d.K + i] = s_sel[i];
-    b.selsc[static_cast<long>(bh) * d.K + i] = s_selsc[i];
-  }
-  mx = block_max_f32(mx, reinterpret_cast<float*>(sh.tmp));
-  if (tid == 0) b.sellen[bh] = n;
-  if (sel_out != nullptr)
-    for (int i = tid; i < d.K; i += blockDim.x) sel_out[static_cast<long>(bh) * d.K + i] = i < n ? s_sel[i] : -1;
-  if (v != nullptr && out != nullptr) {
-    const uint16_t* vb = v + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
-    attend(s_sel, s_selsc, n, mx, vb, out + static_cast<long>(bh) * kHeadDim, nullptr, sh);
-  }
-  if (push) {
-    if (tid < kHeadDim) sh.qbar[tid] = qv;
-    lds_barrier();
-    cache_push(d, b, bh, fifo_slot, fifo_count, sh.qbar, s_sel, n);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Global Top-K (Eq. 1), step 1 (collect), one work group per (exact head,
-// chunk of kCollectChunk positions). Every work
-// group finds the boundary bin b1 (the bin holding the K-th largest score)
-// from the head's histogram copies, then writes the chunk's "survivors"
-// (scores in b1 or above) as (position, score bits), in ascending position
-// order, to the chunk's region of the hit buffer, and their count. Wave w
-// owns rows 32w .. 32w+31 of 64 positions (lane l holds position 64r + l), so
-// a ballot is a row's survivors and mbcnt gives each one's slot: no atomics.
-// The work group of chunk 0 also records (b1, the count above b1, the count
-// in b1).
-//
-// The survivor test (ordered key >= b1 << 22, i.e. bin >= b1, with -0.0 and
-// +0.0 sharing the key of +0.0) is one compare per score: for b1 > 512 the
-// signed compare of the raw bits with those of the smallest float of bin b1
-// (positive; negative scores and -0.0 fail it), else the float compare with
-// the smallest float of bin b1 (0.0 for b1 = 512, a negative float below it,
-// -inf for bins 0 and 1, which hold only NaN patterns).
-// ---------------------------------------------------------------------------
-constexpr int kCollectRows = kCollectChunk / kHeadThreads;  // rows of 64 positions per wave
-static_assert(kCollectRows * 64 * (kHeadThreads / 64) == kCollectChunk, "collect chunk layout");
-
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-}
-
-// Both passes over a wave's rows; kInt selects the survivor compare.
-template <bool kInt>
-__device__ __forceinline__ void collect_rows(const float (&x)[kCollectRows], int p0, int length, int ti, float tf,
-                                             uint2* region, int* tmp, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  auto survives = [&](int u) {
-    return (p0 + 64 * u < length) & (kInt ? __float_as_int(x[u]) >= ti : x[u] >= tf);
+  // the heads this work group finishes: head m of group e when x_m (see
+  // above) falls in [xa, xb)
+  const long xa = static_cast<long>(w) * T / nW, xb = static_cast<long>(w + 1) * T / nW;
+  const int ea = static_cast<int>(xa / length), eb = xb > xa ? static_cast<int>((xb - 1) / length) : ea - 1;
+  auto owned = [&](int e, int m, int nex) {
+    const long xm = static_cast<long>(e) * length + (static_cast<long>(2 * m + 1) * length) / (2 * nex);
+    return xa <= xm && xm < xb;
   };
-  // pass 1: this wave's survivor count; wave bases
-  int wc = 0;
-#pragma unroll
-  for (int u = 0; u < kCollectRows; ++u) wc += __popcll(__ballot(survives(u)));
-  if (lane == 0) tmp[wave] = wc;
-  lds_barrier();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kHeadThreads / 64; ++w) {
-    const int t = tmp[w];
-    base += w < wave ? t : 0;
-    tot += t;
-  }
-  *total = tot;
-  // pass 2: every survivor to its slot, in position order
-#pragma unroll
-  for (int u = 0; u < kCollectRows; ++u) {
-    const bool s = survives(u);
-    const uint64_t m = __ballot(s);
-    if (s)
-      store_shared(region + base + lanes_below(m),
-                   make_uint2(static_cast<uint32_t>(p0 + 64 * u), __float_as_uint(x[u])));
-    base += __popcll(m);
-  }
-}
 
-// tmp: 16 ints, s_bd: 3 ints of LDS. Every thread of the block must call it.
-__device__ __forceinline__ void collect_phase(const Dims& d, const Bufs& b, int bh, int chunk, int length, int* tmp,
-                                              int* s_bd) {
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const int keff = min(d.K, length);
-  const float* srow = b.score + static_cast<long>(bh) * d.score_stride;
-  const uint32_t* hist = b.hist + static_cast<long>(bh) * kHistSeg * kNumBins;
-  const int c0 = chunk * kCollectChunk;
-  const int p0 = c0 + wave * kCollectRows * 64 + (tid & 63);  // position of row u: p0 + 64 u
-  // one round of loads: this wave's rows and this thread's two bins (1023-2t,
-  // 1022-2t) of every histogram copy
-  float x[kCollectRows];
-#pragma unroll
-  for (int u = 0; u < kCollectRows; ++u) x[u] = load_shared(srow + min(p0 + 64 * u, length - 1));  // clamped, masked below
-  uint2 hs[kHistSeg];
-#pragma unroll
-  for (int sgm = 0; sgm < kHistSeg; ++sgm)
-    hs[sgm] = load_shared(reinterpret_cast<const uint2*>(hist + sgm * kNumBins + kNumBins - 2 * (tid + 1)));
-  int ca = 0, cb = 0;
-#pragma unroll
-  for (int sgm = 0; sgm < kHistSeg; ++sgm) {
-    ca += hs[sgm].y;
-    cb += hs[sgm].x;
+  // ---- phase 2: survivors of every segment ----
+  for (int e = e0, r = r0, lb = 0; e < e1 || (e == e1 && r < r1); ++e, r = 0) {
+    const int row0 = r, rend = e == e1 ? r1 : length;
+    if (row0 >= rend) continue;
+    const int bg = s_eg[e] & 0xffff;
+    if (!wait_group(b.wdone, T, nW, length, ne, e, call_flag, b.err, &sh.i3)) return;
+    if (keep > 0)
+      emit_segment<true>(d, b, bg / d.Hkv, bg % d.Hkv, static_cast<unsigned>(s_eg[e]) >> 16, row0, rend, length, w,
+                         par, s_sc + lb, stride);
+    else
+      emit_segment<false>(d, b, bg / d.Hkv, bg % d.Hkv, static_cast<unsigned>(s_eg[e]) >> 16, row0, rend, length, w,
+                          par, nullptr, stride);
+    lb += (rend - row0 + 15) & ~15;
   }
-  if (tid == 0) {  // defined even if the counts fell short of keff (ordered by the scan's barriers)
-    s_bd[0] = 0;
-    s_bd[1] = 0;
-    s_bd[2] = 0;
-  }
-  int tot;
-  const int ex = block_exclusive_scan(ca + cb, &tot, tmp);
-  if (ex < keff && ex + ca + cb >= keff) {
-    const bool first = ex + ca >= keff;
-    s_bd[0] = kNumBins - 1 - 2 * tid - (first ? 0 : 1);
-    s_bd[1] = first ? ex : ex + ca;
-    s_bd[2] = first ? ca : cb;
-  }
-  lds_barrier();
-  const int b1 = s_bd[0];
-  const uint32_t k0 = static_cast<uint32_t>(b1) << kHistShift;
-  uint2* region = b.hits + static_cast<long>(bh) * d.max_len + c0;
-  int total;
-  if (b1 > kNumBins / 2) {
-    collect_rows<true>(x, p0, length, static_cast<int>(k0 & 0x7fffffffu), 0.f, region, tmp + 8, &total);
-  } else {
-    const float tf = b1 == kNumBins / 2 ? 0.f : (b1 >= 2 ? __uint_as_float(~k0) : kNegInf);
-    collect_rows<false>(x, p0, length, 0, tf, region, tmp + 8, &total);
-  }
-  if (tid == 0) {
-    store_shared(b.ccnt + static_cast<long>(bh) * d.n_chunks + chunk, total);
-    if (chunk == 0) {
-      store_shared(b.bnd + 4 * bh, b1);
-      store_shared(b.bnd + 4 * bh + 1, s_bd[1]);
-      store_shared(b.bnd + 4 * bh + 2, s_bd[2]);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Global Top-K, step 2 (finish), softmax-V and the cache update, run by the
-// last collect work group of an exact head.
-//  1. The chunks' survivor counts give each chunk's offset in the head's
-//     survivor list (ascending positions: the chunks are in order).
-//  2. Each thread takes kSU consecutive survivors and classifies them: above
-//     b1 (all kept) or in b1 (candidates). The candidates' composite keys
-//     (score desc, index asc) are compacted (LDS, else the global spill row)
-//     and a radix select over the bits below their shared top 10 keeps the
-//     `need` = keff - (count above b1) best.
-//  3. A block scan over "kept" flags writes S_t in ascending index order.
-//
-// LDS (dynamic): candidate keys (kBoundaryLds), chunk offsets (n_chunks + 1),
-// S_t and its scores (K each).
-// ---------------------------------------------------------------------------
-constexpr int kSU = 8;  // survivors per thread per round
-
-// fifo_slot / fifo_count: the FIFO state read before any push. Every thread of
-// the block must call it.
-__device__ __forceinline__ void finish_phase(const Dims& d, const Bufs& b, int bh, const uint16_t* v, float* out,
-                                             int32_t* sel_out, int length, int push, int fifo_slot, int fifo_count,
-                                             HeadShared& sh, unsigned char* dyn) {
-  const int tid = threadIdx.x;
-  const int nch = (length + kCollectChunk - 1) / kCollectChunk;
-  // one round of loads: this thread's chunk counts, the boundary record and
-  // (for the push) q_bar_t
-  const float qv = push && tid < kHeadDim ? load_shared(b.qbar + static_cast<long>(bh) * kHeadDim + tid) : 0.f;
-  const int per = (nch + kHeadThreads - 1) / kHeadThreads;  // <= 2 (n_chunks <= 1024)
-  const int q0 = min(tid * per, nch), q1 = min(q0 + per, nch);
-  const int32_t* ccnt = b.ccnt + static_cast<long>(bh) * d.n_chunks;
-  int cc[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) cc[i] = q0 + i < q1 ? load_shared(ccnt + q0 + i) : 0;
-  const int4 bd = make_int4(load_shared(b.bnd + 4 * bh), load_shared(b.bnd + 4 * bh + 1),
-                            load_shared(b.bnd + 4 * bh + 2), 0);
-  uint64_t* lkeys = reinterpret_cast<uint64_t*>(dyn);
-  int* aoff = reinterpret_cast<int*>(dyn + 8 * kBoundaryLds);
-  const size_t off_c = 8 * kBoundaryLds + (4 * (static_cast<size_t>(d.n_chunks) + 1) + 15) / 16 * 16;
-  int32_t* s_sel = reinterpret_cast<int32_t*>(dyn + off_c);
-  float* s_selsc = reinterpret_cast<float*>(dyn + off_c + 4 * static_cast<size_t>(d.K));
-  const int keff = min(d.K, length);
-  // (clamped: consistent scores and histogram never need it, but every index below stays in its row)
-  const int b1 = bd.x, n_above = min(max(bd.y, 0), keff - 1), n_bd = min(max(bd.z, 0), length);
-  const bool keys_lds = n_bd <= kBoundaryLds;
-  uint64_t* gkeys = b.bkeys + static_cast<long>(bh) * d.max_len;
-  const uint2* hits_row = b.hits + static_cast<long>(bh) * d.max_len;
-
-  // ---- 1. chunk offsets ----
-  {
-    int tot;
-    int o = block_exclusive_scan(cc[0] + cc[1], &tot, sh.tmp);
-    for (int i = 0; i < 2 && q0 + i < q1; ++i) {
-      aoff[q0 + i] = o;
-      o += cc[i];
-    }
-    if (tid == 0) aoff[nch] = tot;
-    lds_barrier();
-  }
-  const int ns = aoff[nch];
-
-  // ---- 2. classification, candidate keys, radix select ----
-  const int nrounds = (ns + kHeadThreads * kSU - 1) / (kHeadThreads * kSU);
-  int pos[kSU];
-  uint32_t sb[kSU];
-  auto load_round = [&](int rd) {
-    const int i0 = rd * kHeadThreads * kSU + tid * kSU;
-    uint2 e[kSU];
-#pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      const int i = i0 + u;
-      e[u] = make_uint2(0xffffffffu, 0u);
-      if (i < ns) {
-        int lo = 0, hi = nch;  // the last chunk whose offset is <= i
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (aoff[mid] <= i) lo = mid; else hi = mid;
-        }
-        e[u] = load_shared(hits_row + static_cast<long>(lo) * kCollectChunk + (i - aoff[lo]));
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      pos[u] = static_cast<int>(e[u].x);  // -1 past the end
-      sb[u] = e[u].y;
-    }
-  };
-  auto bin_of = [&](int u) { return static_cast<int>(order_key(__uint_as_float(sb[u])) >> kHistShift); };
-  auto in_b1 = [&](int u) { return (pos[u] >= 0) & (bin_of(u) == b1); };
-  auto above = [&](int u) { return (pos[u] >= 0) & (bin_of(u) > b1); };
-
-  // candidate keys, compacted in position order
-  {
-    int krun = 0;
-    for (int rd = 0; rd < nrounds; ++rd) {
-      load_round(rd);
-      int c = 0;
-#pragma unroll
-      for (int u = 0; u < kSU; ++u) c += in_b1(u);
-      int tot;
-      int o = krun + block_exclusive_scan(c, &tot, sh.tmp);
-#pragma unroll
-      for (int u = 0; u < kSU; ++u) {
-        if (in_b1(u)) {
-          const uint64_t key = comp_key(__uint_as_float(sb[u]), static_cast<uint32_t>(pos[u]));
-          if (o < n_bd) {
-            if (keys_lds) lkeys[o] = key;
-            else gkeys[o] = key;
-          }
-          ++o;
-        }
-      }
-      krun += tot;
-    }
-  }
-  lds_barrier();
-  // Radix select of the `need` best candidates. Their composite keys share
-  // the top 10 bits (the bin b1), so the digits start below them, 11 bits at
-  // a time: bits 53-43, 42-32 (score), 31-21, 20-10, 9-0 (index).
-  int need = keff - n_above;
-  int ncand = n_bd;
-  auto bkey = [&](int i) -> uint64_t { return keys_lds ? lkeys[i] : gkeys[i]; };
-  uint64_t mask = 0x3FFull << 54, prefix = static_cast<uint64_t>(b1) << 54;
-  int* bins = &sh.whist[0][0];
-  for (int shift = 43; ncand > need && need > 0; shift = shift >= 11 ? shift - 11 : 0) {
-    const uint64_t dmask = shift == 0 ? 0x3FFull : 0x7FFull;
-    reinterpret_cast<int4*>(bins)[tid] = make_int4(0, 0, 0, 0);
-    lds_barrier();
-    for (int i = tid; i < n_bd; i += blockDim.x) {
-      const uint64_t u = bkey(i);
-      if ((u & mask) == prefix) atomicAdd(&bins[(u >> shift) & dmask], 1);
-    }
-    lds_barrier();
-    pick_bin2048(sh, need);
-    prefix |= static_cast<uint64_t>(sh.i0) << shift;
-    mask |= dmask << shift;
-    need = sh.i1;
-    ncand = sh.i2;
-    if (shift == 0) break;
-  }
-
-  // ---- 3. S_t in ascending index order: survivors above b1 and the kept candidates ----
-  int n = 0;
-  for (int rd = 0; rd < nrounds; ++rd) {
-    if (nrounds > 1) load_round(rd);  // one round: still in registers
-    bool keep[kSU];
-    int c = 0;
-#pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      keep[u] = above(u) |
-                (in_b1(u) & ((comp_key(__uint_as_float(sb[u]), static_cast<uint32_t>(pos[u])) & mask) >= prefix));
-      c += keep[u];
-    }
-    int tot;
-    int o = n + block_exclusive_scan(c, &tot, sh.tmp);
-#pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      if (keep[u]) {
-        if (o < d.K) {
-          s_sel[o] = pos[u];
-          s_selsc[o] = __uint_as_float(sb[u]);
-        }
-        ++o;
-      }
-    }
-    n += tot;
-  }
-  n = min(n, keff);
-  lds_barrier();
-  finish_tail(d, b, bh, n, v, out, sel_out, push, fifo_slot, fifo_count, sh, s_sel, s_selsc, qv);
-}
-
-// ---------------------------------------------------------------------------
-// K3, the exact heads' global Top-K, softmax-V and cache update in one launch:
-// one work group per (head, chunk); reuse heads return at once. Each work group
-// collects its chunk's survivors with device-scope stores, waits until they
-// are complete and counts itself in on the head's counter; the work group that
-// arrives last reads every chunk's survivors with device-scope loads, finishes
-// the head and resets the counter for the next call. No wave waits on another
-// work group.
-// ---------------------------------------------------------------------------
-// fused: the score work groups run in the same launch (wait for the KV
-// group's scored-row counter); else they ran in an earlier launch.
-__device__ __forceinline__ void tail_role(const Dims& d, const Bufs& b, const uint16_t* v, float* out, int32_t* sel_out,
-                                          int length, int push, int call_flag, int tw, int nch, bool fused,
-                                          HeadShared& sh) {
-  __shared__ int tmp[16];
-  __shared__ int s_bd[3];
-  __shared__ int s_last;
-  __shared__ int s_val;
-  extern __shared__ __align__(16) unsigned char dyn[];
-  const int bh = tw / nch, chunk = tw % nch;
-  const int NG = d.B * d.Hkv;
-  // this head's FIFO state: only the finish below pushes for an exact head
-  const int fifo_slot = b.fifo[2 * bh], fifo_count = b.fifo[2 * bh + 1];
-  // this call's decision for the head, then (exact) its KV group fully scored
-  if (!wait_flag(b.dec + bh, [&](int x) { return (x | 1) == (call_flag | 1); }, &s_val, b.err)) return;
-  if (!(s_val & 1)) return;
-  const int bg = (bh / d.Hq) * d.Hkv + (bh % d.Hq) / d.G;
-  if (fused &&
-      !wait_flag(b.scored + ((call_flag >> 1) & 1) * NG + bg, [&](int x) { return x >= length; }, &s_val, b.err))
-    return;
-  collect_phase(d, b, bh, chunk, length, tmp, s_bd);
   __syncthreads();  // every wave's (device-scope) survivor and count stores are complete
-  if (threadIdx.x == 0) {
-    s_last = atomicAdd(&b.tailcnt[bh], 1) == nch - 1;
-    if (s_last) b.tailcnt[bh] = 0;
+  if (threadIdx.x == 0) store_shared(b.wdone + d.n_cu + w, call_flag);
+
+  // ---- phase 3: finish the owned heads ----
+  for (int e = ea; e <= eb; ++e) {
+    const int bg = s_eg[e] & 0xffff;
+    const unsigned emask = static_cast<unsigned>(s_eg[e]) >> 16;
+    const int nex = __popc(emask);
+    for (int m = 0; m < nex; ++m) {
+      if (!owned(e, m, nex)) continue;
+      const int bh = (bg / d.Hkv) * d.Hq + (bg % d.Hkv) * d.G + nth_bit(emask, m);
+      // the head's boundary (its group is fully scored once this work group's
+      // own segments have passed phase 2; else wait for that here)
+      if (!wait_group(b.wdone, T, nW, length, ne, e, call_flag, b.err, &sh.i3)) return;
+      if ((threadIdx.x >> 6) == 0) {
+        const int3 bd = wave_boundary(b.hist + (static_cast<long>(bh) * 2 + par) * kNumBins, min(d.K, length));
+        if (threadIdx.x == 0) {
+          sh.i0 = bd.x;
+          sh.i1 = bd.y;
+          sh.i2 = bd.z;
+        }
+      }
+      if (!wait_group(b.wdone + d.n_cu, T, nW, length, ne, e, call_flag, b.err, &sh.i3)) return;
+      const int3 bd = make_int3(sh.i0, sh.i1, sh.i2);
+      lds_barrier();  // (the finish reuses sh.i0 ..)
+      finish_phase(d, b, bh, v, out, sel_out, length, push, T, nW, ne, e, bd, sh, dyn);
+      lds_barrier();  // the next finish reuses the LDS
+    }
   }
-  __syncthreads();
-  if (!s_last) return;
-  {
-    // every collect work group of the head has read its histogram copies:
-    // clear them for the next call's score pass
-    uint4* hz = reinterpret_cast<uint4*>(b.hist + static_cast<long>(bh) * kHistSeg * kNumBins);
-    for (int i = threadIdx.x; i < kHistSeg * kNumBins / 4; i += blockDim.x) hz[i] = make_uint4(0u, 0u, 0u, 0u);
-  }
-  finish_phase(d, b, bh, v, out, sel_out, length, push, fifo_slot, fifo_count, sh, dyn);
 }
 
 // ---------------------------------------------------------------------------
-// A decode step (or an exact call) over the work-group index space
-//   [0, BH)                     head work groups (query heads);
-//   [BH, BH + NS)               score work groups;
-//   [BH + NS, BH + NS + BH*nch) tail work groups (query head, chunk),
-// launched whole (a decode step: `fused`) or as [0, BH + NS) then the rest
-// (calls with every head exact, where the first part is long and a launch
-// boundary is cheaper than device-scope traffic and polling): block b is index
-// base + b. Every wait is on work groups of lower index (dispatched first, or
-// in an earlier launch) and is bounded in time; a timeout sets the device
-// error word.
+// A decode step (or an exact call), one launch over the work-group index space
+//   [0, BH)        head work groups (query heads);
+//   [BH, BH + NS)  score work groups (also the exact heads' Top-K and finish).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, Bufs b, const uint16_t* q, long q_sb, long q_sh,
                                                        const uint16_t* k, const uint16_t* v, float* out,
                                                        int32_t* sel_out, int length, int t_dec, int mode,
-                                                       int stats_slot, int push, int call_flag, int n_score, int base,
-                                                       int fused) {
+                                                       int stats_slot, int push, int call_flag, int n_score,
+                                                       int keep) {
   __shared__ HeadShared sh;
   const int BH = d.B * d.Hq;
-  const int w = base + static_cast<int>(blockIdx.x);
-  if (w < BH) {
+  const int w = static_cast<int>(blockIdx.x);
+  if (w < BH)
     head_role(d, b, q, q_sb, q_sh, k, v, out, length, t_dec, mode, stats_slot, call_flag, w, sh);
-  } else if (w < BH + n_score) {
-    score_role(d, b, q, q_sb, q_sh, k, length, call_flag, w - BH, n_score, mode == kModeExact, fused != 0);
-  } else {
-    const int nch = (length + kCollectChunk - 1) / kCollectChunk;
-    tail_role(d, b, v, out, sel_out, length, push, call_flag, w - BH - n_score, nch, fused != 0, sh);
-  }
+  else
+    score_role(d, b, q, q_sb, q_sh, k, v, out, sel_out, length, push, call_flag, w - BH, n_score,
+               mode == kModeExact, keep, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1738,20 +1809,9 @@ hipError_t launch_step(const Dims& d, const Bufs& b, const uint16_t* q, long q_s
                        const uint16_t* v, float* out, int32_t* sel_out, int length, int t_dec, int mode,
                        int stats_slot, int push, int call_flag, hipStream_t s) {
   const int n_score = score_grid(d, length);
-  const int nch = (length + kCollectChunk - 1) / kCollectChunk;
-  const int BH = d.B * d.Hq;
-  if (mode == kModeDecode) {
-    hipLaunchKernelGGL(k_step, dim3(BH + n_score + BH * nch), dim3(kHeadThreads), step_lds_bytes(d), s, d, b, q,
-                       q_sb, q_sh, k, v, out, sel_out, length, t_dec, mode, stats_slot, push, call_flag, n_score, 0,
-                       1);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL(k_step, dim3(BH + n_score), dim3(kHeadThreads), step_lds_bytes(d), s, d, b, q, q_sb, q_sh, k, v,
-                     out, sel_out, length, t_dec, mode, stats_slot, push, call_flag, n_score, 0, 0);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_step, dim3(BH * nch), dim3(kHeadThreads), step_lds_bytes(d), s, d, b, q, q_sb, q_sh, k, v, out,
-                     sel_out, length, t_dec, mode, stats_slot, push, call_flag, n_score, BH + n_score, 0);
+  hipLaunchKernelGGL(k_step, dim3(d.B * d.Hq + n_score), dim3(kHeadThreads), step_lds_bytes(d), s, d, b, q, q_sb,
+                     q_sh, k, v, out, sel_out, length, t_dec, mode, stats_slot, push, call_flag, n_score,
+                     score_keep_rows(d, length, n_score));
   return hipGetLastError();
 }
 
