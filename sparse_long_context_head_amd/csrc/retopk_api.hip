@@ -252,6 +252,8 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   A(&b.st_path, BH * kStatsCap);
   A(&b.st_rho, BH * kStatsCap);
   A(&b.st_m, BH * kStatsCap);
+  A(&b.self, 1);
+  if (e == hipSuccess) e = hipMemcpy(b.self, &b, sizeof(Bufs), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = configure_kernels(d);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {

@@ -67,6 +67,7 @@ struct Bufs {
   uint8_t* st_path;        // [kStatsCap, BH]
   double* st_rho;          // [kStatsCap, BH]
   int32_t* st_m;           // [kStatsCap, BH]
+  Bufs* self;              // device copy of this table (what the step kernel is given)
 };
 
 enum KernelId : int { kKStep = 0, kKReset, kNumKernels };

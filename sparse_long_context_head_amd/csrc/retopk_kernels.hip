@@ -1771,19 +1771,24 @@ __device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const u
 //   [0, BH)        head work groups (query heads);
 //   [BH, BH + NS)  score work groups (also the exact heads' Top-K and finish).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, Bufs b, const uint16_t* q, long q_sb, long q_sh,
+__global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, const Bufs* __restrict__ bp, const uint16_t* q, long q_sb, long q_sh,
                                                        const uint16_t* k, const uint16_t* v, float* out,
                                                        int32_t* sel_out, int length, int t_dec, int mode,
                                                        int stats_slot, int push, int call_flag, int n_score,
                                                        int keep) {
   __shared__ HeadShared sh;
+  // The buffer table is not held in the kernel's argument registers: the head
+  // role reads it where it needs it, the score role (many barriers, which
+  // would make it read the table again) takes its own copy once.
   const int BH = d.B * d.Hq;
   const int w = static_cast<int>(blockIdx.x);
-  if (w < BH)
-    head_role(d, b, q, q_sb, q_sh, k, v, out, length, t_dec, mode, stats_slot, call_flag, w, sh);
-  else
+  if (w < BH) {
+    head_role(d, *bp, q, q_sb, q_sh, k, v, out, length, t_dec, mode, stats_slot, call_flag, w, sh);
+  } else {
+    const Bufs b = *bp;
     score_role(d, b, q, q_sb, q_sh, k, v, out, sel_out, length, push, call_flag, w - BH, n_score,
                mode == kModeExact, keep, sh);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1809,7 +1814,7 @@ hipError_t launch_step(const Dims& d, const Bufs& b, const uint16_t* q, long q_s
                        const uint16_t* v, float* out, int32_t* sel_out, int length, int t_dec, int mode,
                        int stats_slot, int push, int call_flag, hipStream_t s) {
   const int n_score = score_grid(d, length);
-  hipLaunchKernelGGL(k_step, dim3(d.B * d.Hq + n_score), dim3(kHeadThreads), step_lds_bytes(d), s, d, b, q, q_sb,
+  hipLaunchKernelGGL(k_step, dim3(d.B * d.Hq + n_score), dim3(kHeadThreads), step_lds_bytes(d), s, d, b.self, q, q_sb,
                      q_sh, k, v, out, sel_out, length, t_dec, mode, stats_slot, push, call_flag, n_score,
                      score_keep_rows(d, length, n_score));
   return hipGetLastError();
