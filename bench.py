@@ -107,8 +107,8 @@ def _counter_rows(path):
 
 def _per_dispatch(rows, counter, last=None):
     """{(kernel short name, grid size): [counter value per dispatch, in dispatch
-    order]} (KiB). A call that launches one kernel twice with different grids
-    (the exact calls) shows up as two keys. With `last`, only each kernel's
+    order]} (KiB). A call that launches one kernel more than once with
+    different grids shows up as several keys. With `last`, only each kernel's
     timed window is kept: its last `last` calls, i.e. its last
     last * (grids among its last `last` dispatches) dispatches."""
     per = {}
@@ -490,8 +490,7 @@ def main():
                                          "frac": round(gbs / HBM_PEAK_GBS, 4),
                                          "algorithmic_bytes_per_step": int(step_alg),
                                          "unique_v_rows": int(v_rows)}
-        # an exact call is two launches of k_step (head and score work groups,
-        # then the tail), timed together per call
+        # an exact call is one launch of k_step, timed per call
         result["roofline_exact"] = roofline("k_step", step_alg, us_ex, "exact", per="call")
         for layer in ex:
             layer.close()
