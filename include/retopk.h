@@ -191,9 +191,10 @@ const char* retopk_kernel_name(int32_t id);
 size_t retopk_device_bytes(const retopk_handle* h);
 
 /* Sticky device error word of the handle: 0 when every call since the last
- * read completed its work; 1 when a score work group of some call gave up
- * waiting (several milliseconds) for the path decisions of that call's head
- * work groups, in which case that call's exact heads were not scored and its
+ * read completed its work; 1 when a work group of some call gave up one of
+ * its bounded waits inside the step (for the path decisions of the call's
+ * head work groups, or for other work groups' scores or survivors of an exact
+ * KV group), in which case that call's exact heads were not finished and its
  * results are not valid. Synchronises the device, writes the word to *word
  * and clears it. */
 retopk_status retopk_read_device_error(retopk_handle* h, int32_t* word);

@@ -2,7 +2,7 @@
 //
 // Method: "Recall Before You Rank: Similarity-Guided Top-K Reuse for
 // Efficient Long-Context Attention", Methodology section. A decode step (or an
-// exact call) is one launch of k_step, whose work groups take three roles by
+// exact call) is one launch of k_step, whose work groups take two roles by
 // block index:
 //
 //   head   one per query head: recall (Eqs. 5-7) and the path rule (Eq. 13),
@@ -12,21 +12,19 @@
 //          (Eq. 11), softmax-V (Eq. 12) and the cache update;
 //   score  full-history scores (Eq. 4) and a score histogram of every exact
 //          head, GQA-grouped on MFMA, the rows of the exact KV groups spread
-//          over all score work groups; each adds the rows it scored to its KV
-//          group's counter;
-//   tail   one per (query head, chunk of positions): for an exact head, once
-//          its KV group is fully scored, the scores in the histogram's
-//          boundary bin or above it, in position order (global Top-K, Eq. 1,
-//          step 1); the last one of a head selects inside the boundary bin,
-//          then runs softmax-V and the cache update.
+//          over all score work groups and kept in LDS; then the scores in the
+//          histogram's boundary bin or above, per segment in position order,
+//          and, in the work group each exact head is assigned to, the
+//          selection inside the boundary bin (global Top-K, Eq. 1),
+//          softmax-V and the cache update.
 //
 // Data passes between work groups only through device-scope (sc1) stores and
 // loads and device-scope atomics, which are coherent across the XCDs' L2s on
 // their own: no whole-L2 write-back or invalidate is needed (those cost more
-// than a launch on this part). Every wait is on work groups of lower block
-// index, which the dispatcher has started first, and is bounded in time.
-// Reuse heads need no full-history work at all, and the host never waits on
-// the path decision. Every phase issues its global loads before consuming
+// than a launch on this part). Head work groups never wait; a score work group
+// waits only for earlier phases of the others, and every wait is bounded in
+// time. Reuse heads need no full-history work at all, and the host never waits
+// on the path decision. Every phase issues its global loads before consuming
 // them, so a phase costs about one memory round trip rather than one per loop
 // iteration.
 
