@@ -26,6 +26,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -263,9 +264,16 @@ def summarize_kernels(root, last, workload):
 
 
 def kernel_source_hash():
+    """Hash of the kernels' code (the kernel source and the internal header),
+    with comments and whitespace removed: counters taken on one version stay
+    valid across comment-only edits."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "sparse_long_context_head_amd", "csrc", "retopk_kernels.hip"), "rb") as f:
-        h.update(f.read())
+    for name in ("retopk_kernels.hip", "retopk_internal.h"):
+        with open(os.path.join(ROOT, "sparse_long_context_head_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
