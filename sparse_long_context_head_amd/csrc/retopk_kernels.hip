@@ -37,6 +37,49 @@ namespace retopk {
 
 namespace {
 
+// The buffer table as the kernels see it: the same layout, every pointer in
+// the global address space, so that accesses through it compile to global
+// (not flat) instructions once the table is read from device memory.
+// (the host pass, which only parses device code, sees plain pointers)
+#if defined(__HIP_DEVICE_COMPILE__)
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+#else
+template <typename T>
+using gptr = T*;
+#endif
+
+struct BufsDev {
+  gptr<float> cache_qbar;
+  gptr<int32_t> cache_supp;
+  gptr<int32_t> cache_len;
+  gptr<int32_t> fifo;
+  gptr<float> qbar;
+  gptr<int32_t> path;
+  gptr<double> rho;
+  gptr<int32_t> ret;
+  gptr<int32_t> retslot;
+  gptr<int32_t> m;
+  gptr<int32_t> cand;
+  gptr<float> score;
+  gptr<uint32_t> hist;
+  gptr<uint2> hits;
+  gptr<int32_t> ccnt;
+  gptr<int32_t> dec;
+  gptr<int32_t> err;
+  gptr<int32_t> wdone;
+  gptr<uint64_t> bkeys;
+  gptr<int32_t> sel;
+  gptr<float> selsc;
+  gptr<int32_t> sellen;
+  gptr<uint8_t> st_path;
+  gptr<double> st_rho;
+  gptr<int32_t> st_m;
+  Bufs* self;
+};
+static_assert(sizeof(BufsDev) == sizeof(Bufs), "device view of the buffer table");
+
+
 constexpr float kNegInf = -INFINITY;
 constexpr float kPosInf = INFINITY;
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
@@ -689,7 +732,7 @@ __device__ __forceinline__ void attend(const int32_t* sel, float* sc, int n, flo
 // paragraph: after either path; the oldest entry is overwritten when full).
 // slot / count: the FIFO state read at the start of the kernel (the caller's
 // threads must not re-read it here, since thread 0 updates it).
-__device__ __forceinline__ void cache_push(const Dims& d, const Bufs& b, int bh, int slot, int count, const float* qbar,
+__device__ __forceinline__ void cache_push(const Dims& d, const BufsDev& b, int bh, int slot, int count, const float* qbar,
                                            const int32_t* sel, int n) {
   const long e = static_cast<long>(bh) * d.C + slot;
   for (int t = threadIdx.x; t < kHeadDim; t += blockDim.x) b.cache_qbar[e * kHeadDim + t] = qbar[t];
@@ -934,7 +977,7 @@ __device__ __forceinline__ void cand_scores(const uint16_t* kb, const int32_t* s
 }
 constexpr int kDenseWords = kHeadThreads / 4;  // bitmap words emitted a byte per thread (4096 positions)
 
-__device__ __forceinline__ void head_role(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
+__device__ __forceinline__ void head_role(const Dims& d, const BufsDev& b, const uint16_t* q, long q_sb, long q_sh,
                                           const uint16_t* k, const uint16_t* v, float* out, int length, int t_dec,
                                           int mode, int stats_slot, int call_flag, int bh, HeadShared& sh) {
   const int bb = bh / d.Hq, h = bh % d.Hq, g = h / d.G;
@@ -1189,7 +1232,7 @@ __device__ __forceinline__ uint32_t key_score_bits(uint64_t u) {
 // (q_bar_t, S_t) when `push`. Every thread of the block must call it.
 // ---------------------------------------------------------------------------
 // qv: element threadIdx.x of q_bar_t (threads < 128), loaded early by the caller.
-__device__ __forceinline__ void finish_tail(const Dims& d, const Bufs& b, int bh, int n, const uint16_t* v, float* out,
+__device__ __forceinline__ void finish_tail(const Dims& d, const BufsDev& b, int bh, int n, const uint16_t* v, float* out,
                                             int32_t* sel_out, int push, int fifo_slot, int fifo_count, HeadShared& sh,
                                             const int32_t* s_sel, float* s_selsc, float qv) {
   const int tid = threadIdx.x;
@@ -1363,7 +1406,7 @@ __device__ __forceinline__ int3 wave_boundary(const uint32_t* hist, int keff) {
 constexpr int kEmitU = 8;
 
 template <bool kLds>
-__device__ __forceinline__ void emit_segment(const Dims& d, const Bufs& b, int bb, int g, unsigned emask, int row0,
+__device__ __forceinline__ void emit_segment(const Dims& d, const BufsDev& b, int bb, int g, unsigned emask, int row0,
                                              int rend, int length, int w, int par, const float* sc, int stride) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int G = d.G;
@@ -1413,7 +1456,7 @@ constexpr int kSU = 8;  // survivors per thread per round
 
 // Every thread of the block must call it.
 // bd: (b1, count above b1, count in b1).
-__device__ __forceinline__ void finish_phase(const Dims& d, const Bufs& b, int bh, const uint16_t* v, float* out,
+__device__ __forceinline__ void finish_phase(const Dims& d, const BufsDev& b, int bh, const uint16_t* v, float* out,
                                              int32_t* sel_out, int length, int push, long T, int nW, int ne, int e,
                                              int3 bd, HeadShared& sh, unsigned char* dyn) {
   const int tid = threadIdx.x;
@@ -1577,7 +1620,7 @@ __device__ __forceinline__ void finish_phase(const Dims& d, const Bufs& b, int b
 // head of the call is exact (no flags to wait for). keep: rows per head of
 // LDS for the scores of phase 1 (a multiple of 16; 0: they go to the score
 // workspace).
-__device__ __forceinline__ void score_role(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh,
+__device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, const uint16_t* q, long q_sb, long q_sh,
                                            const uint16_t* k, const uint16_t* v, float* out, int32_t* sel_out,
                                            int length, int push, int call_flag, int w, int nW, bool all_exact,
                                            int keep, HeadShared& sh) {
@@ -1775,15 +1818,15 @@ __global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, const Bufs* __res
                                                        int stats_slot, int push, int call_flag, int n_score,
                                                        int keep) {
   __shared__ HeadShared sh;
-  // The buffer table is not held in the kernel's argument registers: the head
-  // role reads it where it needs it, the score role (many barriers, which
-  // would make it read the table again) takes its own copy once.
+  // The buffer table is not held in the kernel's argument registers, which
+  // would keep it live through both roles: each role reads its own copy.
   const int BH = d.B * d.Hq;
   const int w = static_cast<int>(blockIdx.x);
   if (w < BH) {
-    head_role(d, *bp, q, q_sb, q_sh, k, v, out, length, t_dec, mode, stats_slot, call_flag, w, sh);
+    head_role(d, *reinterpret_cast<const BufsDev*>(bp), q, q_sb, q_sh, k, v, out, length, t_dec, mode, stats_slot,
+              call_flag, w, sh);
   } else {
-    const Bufs b = *bp;
+    const BufsDev b = *reinterpret_cast<const BufsDev*>(bp);
     score_role(d, b, q, q_sb, q_sh, k, v, out, sel_out, length, push, call_flag, w - BH, n_score,
                mode == kModeExact, keep, sh);
   }
