@@ -1415,6 +1415,10 @@ __device__ __forceinline__ void emit_segment(const Dims& d, const BufsDev& b, in
   for (int jj = wave; jj < G; jj += nw) {
     if (!((emask >> jj) & 1u)) continue;
     const int b1 = wave_boundary(b.hist + (static_cast<long>(h0 + jj) * 2 + par) * kNumBins, min(d.K, length)).x;
+    // bin(x) >= b1 as one unsigned compare: s ^ ((s >> 31) | 2^31) orders the
+    // raw bits like order_key except that -0.0 lands just below +0.0, which
+    // only matters at b1 = 512 and is covered by lowering that threshold by one
+    const uint32_t k0 = b1 == kNumBins / 2 ? 0x7fffffffu : static_cast<uint32_t>(b1) << kHistShift;
     const float* srow = kLds ? sc + jj * stride : b.score + static_cast<long>(h0 + jj) * d.score_stride + row0;
     uint2* region = b.hits + static_cast<long>(h0 + jj) * d.max_len + row0;
     int run = 0;
@@ -1425,7 +1429,8 @@ __device__ __forceinline__ void emit_segment(const Dims& d, const BufsDev& b, in
 #pragma unroll
       for (int u = 0; u < kEmitU; ++u) {
         const int i = c0 + 64 * u + lane;
-        const bool sv = (i < nrows) & (static_cast<int>(order_key(x[u]) >> kHistShift) >= b1);
+        const int sb = __float_as_int(x[u]);
+        const bool sv = (i < nrows) & ((static_cast<uint32_t>(sb) ^ (static_cast<uint32_t>(sb >> 31) | 0x80000000u)) >= k0);
         const uint64_t m = __ballot(sv);
         if (sv)
           store_shared(region + run + lanes_below(m), make_uint2(static_cast<uint32_t>(row0 + i), __float_as_uint(x[u])));
