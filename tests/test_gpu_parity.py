@@ -197,6 +197,16 @@ def test_exact_gqa16k():
     run_exact("gqa16k", [300, 512, 513, 5000, 16385, 16640])
 
 
+def test_exact_more_groups_than_score_work_groups():
+    """40 batch rows x 4 KV heads x 2 query heads, K=64: 160 KV groups over at
+    most 128 score work groups, so one work group scores and writes survivors
+    for segments of several KV groups and finishes several heads; with 320
+    head work groups the launch also holds more work groups than the GPU has
+    CUs, and the score work groups start as head work groups end."""
+    run_exact("tiny", [1200, 700, 65, 64, 5],
+              wl_kw=dict(batch=40, n_q_heads=8, n_kv_heads=4, prompt_len=1200, decode_steps=4))
+
+
 def test_exact_integer_ties():
     """Integer-valued keys and queries make fp32 scores exact, so equal scores
     are real ties: the lower index must win, with no near-tie allowance."""
