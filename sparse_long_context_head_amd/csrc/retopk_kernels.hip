@@ -357,36 +357,6 @@ __device__ __forceinline__ int bitmap_emit_split(const uint32_t* bm, int wsplit,
   return tot + totd;
 }
 
-// Emit, in ascending order, the positions base + bit of every set bit of an
-// LDS bitmap window of `nwords` words to out[0 ..). Returns the number emitted
-// (the same value in every thread). The words are split evenly over the
-// block: thread t takes words [t*per, (t+1)*per) with per = ceil(nwords /
-// blockDim) <= kSliceWords. Every thread of the block must call it.
-__device__ __forceinline__ int bitmap_emit(const uint32_t* bm, int nwords, int base, int32_t* out, int* tmp) {
-  const int per = (nwords + blockDim.x - 1) / blockDim.x;
-  uint32_t w[kSliceWords];
-  const int w0 = threadIdx.x * per;
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < kSliceWords; ++i) {
-    w[i] = (i < per && w0 + i < nwords) ? bm[bm_at(w0 + i)] : 0u;
-    cnt += __popc(w[i]);
-  }
-  int total;
-  int off = block_exclusive_scan(cnt, &total, tmp);
-#pragma unroll
-  for (int i = 0; i < kSliceWords; ++i) {
-    if (i >= per) break;  // uniform
-    uint32_t bits = w[i];
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      out[off++] = base + (w0 + i) * 32 + b;
-      bits &= bits - 1;
-    }
-  }
-  return total;
-}
-
 // First dynamic-LDS region of the head kernel: the bitmap window, later S_hat
 // with its scores (8K bytes) and one flag byte per candidate.
 __host__ __device__ inline size_t head_region0(const Dims& d) {
@@ -840,25 +810,6 @@ __device__ __forceinline__ void store_shared2(float* p, float a, float b) {
 constexpr int kPollSleep = 8;                 // s_sleep between polls of a flag (about 0.2 us)
 constexpr long long kWaitTicks = 20000000;    // give up a wait after 200 ms (s_memrealtime is 100 MHz)
 
-// Thread 0 polls *p until ok(value) or the time limit; every thread gets the
-// last value read (through *s_val) and whether it was ok. A timeout sets the
-// device error word. Every thread of the block must call it.
-template <typename Ok>
-__device__ __forceinline__ bool wait_flag(const int32_t* p, Ok ok, int* s_val, int32_t* err) {
-  if (threadIdx.x == 0) {
-    const long long t0 = __builtin_amdgcn_s_memrealtime();
-    int v = load_shared(p);
-    while (!ok(v) && __builtin_amdgcn_s_memrealtime() - t0 < kWaitTicks) {
-      __builtin_amdgcn_s_sleep(kPollSleep);
-      v = load_shared(p);
-    }
-    if (!ok(v)) store_shared(err, 1);
-    *s_val = v;
-  }
-  lds_barrier();
-  return ok(*s_val);
-}
-
 constexpr int kQkUnroll = 4;  // 16-row tiles per wave per stage: 512 rows per 8-wave work group
 
 struct QkTiles {
@@ -1218,12 +1169,6 @@ __device__ __forceinline__ void head_role(const Dims& d, const BufsDev& b, const
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint64_t comp_key(float s, uint32_t idx) {
   return (static_cast<uint64_t>(order_key(s)) << 32) | static_cast<uint64_t>(0xffffffffu - idx);
-}
-
-// The score half of a composite key back to the score's bits.
-__device__ __forceinline__ uint32_t key_score_bits(uint64_t u) {
-  const uint32_t ok = static_cast<uint32_t>(u >> 32);
-  return (ok & 0x80000000u) ? (ok & 0x7fffffffu) : ~ok;
 }
 
 // ---------------------------------------------------------------------------
