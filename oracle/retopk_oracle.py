@@ -21,6 +21,8 @@ written from its Methodology section, in the paper's order and notation:
   candidate scores e_hat ......... Eq. (10)
   reranked support S_hat_t ....... Eq. (11)
   sparse softmax-V output ........ Eq. (12)
+  dense attention (comparison) ... Eq. (4) over all keys, then Eq. (12);
+                                   Table 1 "Full Attention", Figure 9
   fallback / refresh path P_t .... Reliable Reuse via Fallback and Refresh, Eq. (13)
   cache update after both paths .. same subsection, closing sentence
   cache initialisation ........... Query-support cache paragraph (final C prompt
@@ -176,6 +178,28 @@ def exact_topk_attention(q_bits, k_bits, v_bits, length: int, k: int):
             row.append(sel)
         sel_all.append(row)
     return out, sel_all
+
+
+def dense_attention(q_bits, k_bits, v_bits, length: int):
+    """Full (dense) softmax attention over every cached key, the "Full
+    Attention" column set beside Exact Top-K (Experimental Results, Table 1;
+    Kernel efficiency analysis, Figure 9): the scores of Eq. (4) for all
+    i < length and Eq. (12)'s softmax-value aggregation with the support taken
+    as all of them.
+
+    q_bits [B, Hq, d]; k_bits, v_bits [B, Hkv, >=length, d] (rows >= length are
+    not read). Returns out [B, Hq, d] float64.
+    """
+    bsz, hq, d = q_bits.shape
+    hkv = k_bits.shape[1]
+    out = np.zeros((bsz, hq, d))
+    for b in range(bsz):
+        for h in range(hq):
+            kv_head = h * hkv // hq
+            every = k_bits[b, kv_head, :length]
+            out[b, h] = sparse_softmax_v(qk_scores(q_bits[b, h], every),
+                                         bf16_to_f64(v_bits[b, kv_head, :length]), d)
+    return out
 
 
 # ----------------------------------------------------------------------------

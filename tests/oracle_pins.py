@@ -403,8 +403,47 @@ def pin_gqa_mapping(o):
             np.testing.assert_allclose(rec.out[0, h], ref, rtol=1e-10, atol=1e-12)
 
 
+def pin_dense_attention(o):
+    """Dense attention over every cached key (Table 1's "Full Attention").
+
+    Closed forms: one key gives its value row; a zero query gives equal weights,
+    hence the mean of the value rows. Brute force on a GQA problem (4 query
+    heads over 2 KV heads, rows past `length` filled with large values that
+    must not be read). K >= L: equals Exact Top-K attention.
+    """
+    rng = np.random.default_rng(21)
+    d = 16
+    q = bits(rng.standard_normal((2, 4, d)))
+    k = bits(rng.standard_normal((2, 2, 12, d)))
+    v = bits(rng.standard_normal((2, 2, 12, d)))
+    out1 = o.dense_attention(q, k, v, 1)
+    for b in range(2):
+        for h in range(4):
+            np.testing.assert_array_equal(out1[b, h], as_float(v[b, h // 2, 0]))
+    zero = np.zeros_like(q)
+    out0 = o.dense_attention(zero, k, v, 7)
+    for b in range(2):
+        for h in range(4):
+            mean = [math.fsum(as_float(v[b, h // 2, :7])[:, c]) / 7 for c in range(d)]
+            np.testing.assert_allclose(out0[b, h], mean, rtol=1e-12, atol=1e-14)
+    length = 9
+    k2 = k.copy()
+    v2 = v.copy()
+    k2[:, :, length:] = bits(np.full((2, 2, 12 - length, d), 40.0))
+    v2[:, :, length:] = bits(np.full((2, 2, 12 - length, d), 1000.0))
+    out = o.dense_attention(q, k2, v2, length)
+    for b in range(2):
+        for h in range(4):
+            g = h // 2
+            s = [brute_dot(as_float(q[b, h]), as_float(k2[b, g, i])) for i in range(length)]
+            ref = brute_attention(s, as_float(v2[b, g, :length]), d)
+            np.testing.assert_allclose(out[b, h], ref, rtol=1e-10, atol=1e-12)
+    ex, _ = o.exact_topk_attention(q, k2, v2, length, length)
+    np.testing.assert_allclose(out, ex, rtol=1e-12, atol=1e-14)
+
+
 ALL_PINS = [pin_bf16_decode, pin_normalize, pin_top_k, pin_top_r, pin_window_and_union,
             pin_dense_special_case, pin_softmax_properties, pin_split_merge, pin_micro_example,
             pin_forced_exact, pin_forced_reuse_and_candidates, pin_refresh_schedule,
             pin_fallback_threshold, pin_window_covers_history, pin_fifo, pin_init,
-            pin_gqa_mapping]
+            pin_gqa_mapping, pin_dense_attention]

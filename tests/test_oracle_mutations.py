@@ -45,6 +45,11 @@ MUTATIONS = [
     ("rerank_uses_wrong_query", "cand_s = qk_scores(q_bits[b, h], k_bits[b, g, cand])",
      "cand_s = qk_scores(q_bits[b, (h + 1) % hq], k_bits[b, g, cand])"),
     ("bf16_decode_shift_15", "astype(np.uint32) << np.uint32(16)", "astype(np.uint32) << np.uint32(15)"),
+    ("dense_drops_newest_key", "every = k_bits[b, kv_head, :length]",
+     "every = k_bits[b, kv_head, :length - 1]"),
+    ("dense_gqa_interleaved", "kv_head = h * hkv // hq", "kv_head = h % hkv"),
+    ("dense_reads_past_length", "bf16_to_f64(v_bits[b, kv_head, :length]), d)",
+     "bf16_to_f64(v_bits[b, kv_head, 1:length + 1]), d)"),
     ("recall_uses_raw_query", "rho = cosine_recall(qbar, [e[0] for e in entries])",
      "rho = cosine_recall(bf16_to_f64(q_bits[b, h]), [e[0] for e in entries])"),
 ]
