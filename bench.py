@@ -11,10 +11,12 @@ resident in HBM before the timed region; nothing is allocated inside it.
 
 Prints one JSON line: the metric is microseconds per decode step per layer
 (lower is better) on the 128K-context, K = 512 GQA layer, with the exact
-Top-K baseline, a forced-reuse run, the path mix, the roofline of the step
-kernel (a decode step is one launch of it) over the timed steps, the same on
-exact calls, whole-step rooflines of the exact and the forced-reuse steps,
-event-bracketed per-launch times, and the CPU oracle baseline.
+Top-K baseline, a forced-reuse run, dense softmax attention over every key
+(the paper's "Full Attention" comparison column), the path mix, the roofline
+of the step kernel (a decode step is one launch of it) over the timed steps,
+the same on exact calls and on dense calls, whole-step rooflines of the exact
+and the forced-reuse steps, event-bracketed per-launch times, and the CPU
+oracle baseline.
 
 Counter support: --copy-calibration runs plain copies of known size,
 --summarize-traffic turns rocprofv3 FETCH_SIZE / WRITE_SIZE runs into the
@@ -56,7 +58,7 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="rotated layers (0: enough to exceed 1 GiB of KV)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["natural", "exact", "reuse"], default=None,
+    ap.add_argument("--only", choices=list(LEGS), default=None,
                     help="run one timed leg only (for profiler runs)")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the per-kernel event-timed pass (counter runs: the last --steps "
@@ -76,6 +78,7 @@ def parse():
     return ap.parse_args()
 
 
+LEGS = ("natural", "exact", "reuse", "dense")
 COPY_BYTES = 256 << 20
 COPY_REPS = 8
 TRAFFIC_COUNTERS = ("FETCH_SIZE", "WRITE_SIZE")
@@ -143,7 +146,7 @@ def summarize_traffic(root, last, workload):
             raise SystemExit(f"no copy dispatch with {c} under {root}/copy_{c}")
         scale[c] = COPY_BYTES / (1024.0 * float(np.median(vals)))
     out = []
-    for leg in ("natural", "exact", "reuse"):
+    for leg in LEGS:
         got = {}
         for c in TRAFFIC_COUNTERS:
             d = os.path.join(root, f"{leg}_{c}")
@@ -178,7 +181,7 @@ def summarize_traffic(root, last, workload):
         "--copy-calibration",
         "rocprofv3 --pmc <C> --output-format csv -d gpurun_out/pmc/<LEG>_<C> -o pmc -- python3 bench.py "
         "--only <LEG> --steps 2048 --warmup 64 --no-cpu-baseline --no-breakdown",
-        "for C in FETCH_SIZE WRITE_SIZE, LEG in natural exact reuse; then",
+        "for C in FETCH_SIZE WRITE_SIZE, LEG in natural exact reuse dense; then",
         f"python3 bench.py --summarize-traffic gpurun_out/pmc --last {last}"],
         "rows": out}
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -194,7 +197,8 @@ PROFILE_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_{leg} -o {le
                "python3 bench.py --only {leg} --steps {steps} --warmup 64 --no-cpu-baseline --no-breakdown")
 LEG_TITLES = {"natural": "natural ReTopK decode steps (the metric's step)",
               "exact": "Exact Top-K baseline (retopk_exact_topk_attn, every head exact)",
-              "reuse": "forced reuse (tau = -2, T_r = 0)"}
+              "reuse": "forced reuse (tau = -2, T_r = 0)",
+              "dense": "dense softmax attention over every key (retopk_dense_attn)"}
 
 
 def summarize_kernels(root, last, workload):
@@ -209,7 +213,7 @@ def summarize_kernels(root, last, workload):
              "the second is rocprofv3's own --stats summary of the whole run (it also counts the cache "
              "initialisation and warm-up dispatches). Summarised by "
              f"`python3 bench.py --summarize-kernels gpurun_out --last {last}`.", ""]
-    for leg in ("natural", "exact", "reuse"):
+    for leg in LEGS:
         d = os.path.join(root, f"prof_{leg}")
         trace = os.path.join(d, f"{leg}_kernel_trace.csv")
         stats = os.path.join(d, f"{leg}_kernel_stats.csv")
@@ -268,7 +272,7 @@ def kernel_source_hash():
     with comments and whitespace removed: counters taken on one version stay
     valid across comment-only edits."""
     h = hashlib.sha256()
-    for name in ("retopk_kernels.hip", "retopk_internal.h"):
+    for name in ("retopk_kernels.hip", "retopk_dense.hip", "retopk_internal.h"):
         with open(os.path.join(ROOT, "sparse_long_context_head_amd", "csrc", name)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -336,10 +340,11 @@ def main():
     out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def make_layers(**override):
+    def make_layers(init=True, **override):
         layers = [B.ReTopKLayer.from_workload(wl, **override) for _ in range(nl)]
         for l in range(nl):
-            layers[l].init_from_prefill(q_tail, ks[l], L0, stream)
+            if init:
+                layers[l].init_from_prefill(q_tail, ks[l], L0, stream)
         torch.cuda.synchronize()
         return layers
 
@@ -350,7 +355,9 @@ def main():
     def run(layers, s0, n, exact=False):
         for s in range(s0, s0 + n):
             l, pos = schedule(s)
-            if exact:
+            if exact == "dense":
+                layers[l].dense_attn(q_dec[pos - 1], ks[l], vs[l], L0 + pos, out, stream)
+            elif exact:
                 layers[l].exact_topk_attn(q_dec[pos - 1], ks[l], vs[l], L0 + pos, out, None, stream)
             else:
                 layers[l].decode_step(q_dec[pos - 1], ks[l], vs[l], L0 + pos, pos, out, stream)
@@ -533,6 +540,30 @@ def main():
                 layer.close()
         if "exact_topk_us_per_step" in result:
             result["speedup_reuse_vs_exact"] = round(result["exact_topk_us_per_step"] / us_ru, 3)
+
+    # --- dense attention over every key (comparison column) -----------------
+    if args.only in (None, "dense"):
+        de = make_layers(init=False)
+        us_de = timed(de, exact="dense")
+        result["dense_attn_us_per_step"] = round(us_de, 3)
+        log(f"dense attention: {us_de:.2f} us/step/layer")
+        mean_len = L0 + (args.warmup + args.steps / 2) / nl
+        # every key and value row of every KV group once, q in and out
+        dense_alg = 2 * ROW_BYTES * mean_len * wl.batch * wl.n_kv_heads \
+            + wl.batch * wl.n_q_heads * wl.head_dim * (2 + 4)
+        # a dense call is k_dense (the row slices) then k_dense_merge, timed per call
+        result["roofline_dense"] = roofline("k_dense", dense_alg, us_de, "dense", per="call")
+        for layer in de:
+            layer.close()
+        if not args.no_breakdown:
+            de = make_layers(init=False)
+            result["kernels_dense"] = kernel_breakdown(de, exact="dense")
+            for layer in de:
+                layer.close()
+        if "value" in result:
+            result["speedup_vs_dense"] = round(us_de / result["value"], 3)
+        if "exact_topk_us_per_step" in result:
+            result["dense_vs_exact"] = round(result["exact_topk_us_per_step"] / us_de, 3)
 
     # --- CPU oracle baseline ------------------------------------------------
     if not args.no_cpu_baseline and args.only in (None, "natural"):

@@ -135,6 +135,25 @@ retopk_status retopk_exact_topk_attn(retopk_handle* h, const uint16_t* q, const 
                                      const uint16_t* v, int32_t length, float* out,
                                      int32_t* sel_out, void* stream);
 
+/* Dense softmax attention over every cached key, for comparison with the
+ * sparse paths: the "Full Attention" column of the ReTopK paper's Table 1
+ * (Experimental Results) and Figure 9 (Kernel efficiency analysis). For every
+ * (b, h): e_i = q.k_i / sqrt(D) for all i < length (Eq. 4) and
+ * out = sum_i softmax(e)_i v_i (Eq. 12 with every position as the support).
+ * The row range is split into slices per KV group; the slices' partial
+ * results (maximum, weight sum, weighted value sum) are merged as disjoint
+ * partial softmax results are (RetrievalAttention reading notes, Method,
+ * CPU-GPU two-path computation). Uses the handle's dimensions and its
+ * partials workspace; the query-support cache is neither read nor changed.
+ * q [B, Hq, D], k and v [B, Hkv, Lmax, D] bf16 (rows 0 .. length-1 are read),
+ * out [B, Hq, D] float32. Needs Hq / Hkv <= 8. Two launches on `stream`
+ * (slices, then merge); asynchronous, no allocation.
+ * Errors: RETOPK_INVALID_ARG for a NULL or misaligned tensor,
+ * RETOPK_OUT_OF_RANGE for length outside 1 .. Lmax or more than 8 query heads
+ * per KV head, RETOPK_HIP_ERROR when a launch fails. */
+retopk_status retopk_dense_attn(retopk_handle* h, const uint16_t* q, const uint16_t* k,
+                                const uint16_t* v, int32_t length, float* out, void* stream);
+
 /* Copy the caches to host buffers, entries oldest first; unused slots zero.
  *   qbar      float32 [B, Hq, C, D]   normalised queries
  *   supp      int32   [B, Hq, C, K]   supports (ascending), padded with 0

@@ -47,6 +47,7 @@ _SIGNATURES = {
     "retopk_init_from_prefill": (ctypes.c_int, [_P, _P, _P, _I32, _P]),
     "retopk_decode_step": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _P, _P]),
     "retopk_exact_topk_attn": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _P]),
+    "retopk_dense_attn": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P]),
     "retopk_read_state": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "retopk_write_state": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "retopk_read_step_info": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -187,6 +188,17 @@ def retopk_exact_topk_attn(h: Handle, q, k, v, length: int, out, sel_out=None, s
                                                  _stream(stream, q.device)))
 
 
+def retopk_dense_attn(h: Handle, q, k, v, length: int, out, stream=None):
+    p = h.params
+    _check_tensor("q", q, (p["batch"], p["n_q_heads"], p["head_dim"]), _BF16)
+    kv_shape = (p["batch"], p["n_kv_heads"], p["max_len"], p["head_dim"])
+    _check_tensor("k", k, kv_shape, _BF16)
+    _check_tensor("v", v, kv_shape, _BF16)
+    _check_tensor("out", out, (p["batch"], p["n_q_heads"], p["head_dim"]), ("float32",))
+    _check(load_library().retopk_dense_attn(h.ptr, _ptr(q), _ptr(k), _ptr(v), length, _ptr(out),
+                                            _stream(stream, q.device)))
+
+
 def retopk_read_state(h: Handle):
     """Return (qbar [B,Hq,C,D] f32, supp [B,Hq,C,K] i32, supp_len [B,Hq,C] i32, count [B,Hq] i32)."""
     p = h.params
@@ -309,6 +321,9 @@ class ReTopKLayer:
 
     def exact_topk_attn(self, q, k, v, length, out, sel_out=None, stream=None):
         retopk_exact_topk_attn(self.handle, q, k, v, length, out, sel_out, stream)
+
+    def dense_attn(self, q, k, v, length, out, stream=None):
+        retopk_dense_attn(self.handle, q, k, v, length, out, stream)
 
     def read_state(self):
         return retopk_read_state(self.handle)

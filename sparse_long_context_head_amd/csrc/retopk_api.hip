@@ -60,6 +60,7 @@ struct retopk_handle {
   std::vector<int> event_kernel;    // kernel id of each recorded pair
   int timed = 0;                    // pairs recorded since the last read
   int call_seq = 0;                 // sequence number of the last k_step launch
+  float* dense_part = nullptr;      // dense attention's row-slice partials [B*Hq, dense_max_split, kDensePart]
 
   // Tag of the next launch's decision flags: 2 * seq, seq counting 1, 2, ... mod
   // 2^29 (an even modulus, so bit 1, which selects the scored-row counters,
@@ -253,6 +254,7 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   A(&b.st_rho, BH * kStatsCap);
   A(&b.st_m, BH * kStatsCap);
   A(&b.self, 1);
+  A(&h->dense_part, BH * static_cast<size_t>(dense_max_split(d)) * kDensePart);
   if (e == hipSuccess) e = hipMemcpy(b.self, &b, sizeof(Bufs), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = configure_kernels(d);
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -347,6 +349,24 @@ retopk_status retopk_exact_topk_attn(retopk_handle* h, const uint16_t* q, const 
     return launch_step(d, b, q, q_sb, q_sh, k, v, out, sel_out, length, 0, kModeExact, -1, 0, flag, s);
   });
   return st;
+}
+
+retopk_status retopk_dense_attn(retopk_handle* h, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                int32_t length, float* out, void* stream) {
+  if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_dense_attn: NULL handle");
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(RETOPK_INVALID_ARG, "retopk_dense_attn: NULL tensor");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 4))
+    return fail(RETOPK_INVALID_ARG, "retopk_dense_attn: misaligned tensor");
+  if (length < 1 || length > h->d.max_len)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_dense_attn: length must be in 1 .. max_len");
+  if (h->d.G > kDenseMaxGroup)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_dense_attn: at most 8 query heads per KV head");
+  DeviceGuard guard(h->device);
+  auto s = static_cast<hipStream_t>(stream);
+  retopk_status st = h->run(kKDense, s, [&] { return launch_dense(h->d, q, k, v, out, length, h->dense_part, s, 0); });
+  if (st != RETOPK_OK) return st;
+  return h->run(kKDenseMerge, s, [&] { return launch_dense(h->d, q, k, v, out, length, h->dense_part, s, 1); });
 }
 
 retopk_status retopk_read_state(retopk_handle* h, float* qbar, int32_t* supp, int32_t* supp_len,

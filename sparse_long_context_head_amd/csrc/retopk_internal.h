@@ -22,6 +22,8 @@ constexpr int kHeadThreads = 512;    // threads of the per-head kernels
 constexpr int kBitmapWords = 8192;   // LDS bitmap window: 262144 token positions (32 KiB)
 constexpr int kLdsLimit = 124 * 1024;  // dynamic LDS a per-head kernel may use (static LDS <= 36 KiB)
 constexpr int kMaxCand = 16384;      // R*K + W limit (candidate keys kept in LDS for reranking)
+constexpr int kDenseMaxGroup = 8;    // query heads per KV head the dense-attention kernel handles
+constexpr int kDensePart = 132;      // floats per (query head, row slice) partial: 128 sums, m, Z, 2 pad
 
 // Problem dimensions, passed by value to every kernel.
 struct Dims {
@@ -70,7 +72,7 @@ struct Bufs {
   Bufs* self;              // device copy of this table (what the step kernel is given)
 };
 
-enum KernelId : int { kKStep = 0, kKReset, kNumKernels };
+enum KernelId : int { kKStep = 0, kKReset, kKDense, kKDenseMerge, kNumKernels };
 
 const char* kernel_name(int id);
 
@@ -104,4 +106,13 @@ hipError_t launch_step(const Dims& d, const Bufs& b, const uint16_t* q, long q_s
                        const uint16_t* v, float* out, int32_t* sel_out, int length, int t_dec, int mode,
                        int stats_slot, int push, int call_flag, hipStream_t s);
 
+// Dense softmax attention (retopk_dense.hip): row slices per KV group of a
+// call at this length, and the most any length gives (the partials workspace
+// holds B * Hq * dense_max_split(d) * kDensePart floats).
+int dense_max_split(const Dims& d);
+void dense_split(const Dims& d, int length, int* n_split, int* rows);
+// phase 0: the slices' partial results (k_dense); phase 1: their merge into
+// out (k_dense_merge). Both on stream s, one launch each.
+hipError_t launch_dense(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v, float* out,
+                        int length, float* part, hipStream_t s, int phase);
 }  // namespace retopk

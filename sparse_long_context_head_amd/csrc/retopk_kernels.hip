@@ -1791,7 +1791,7 @@ hipError_t configure_kernels(const Dims& d) {
 }
 
 const char* kernel_name(int id) {
-  static const char* names[kNumKernels] = {"k_step", "k_reset"};
+  static const char* names[kNumKernels] = {"k_step", "k_reset", "k_dense", "k_dense_merge"};
   return (id >= 0 && id < kNumKernels) ? names[id] : "";
 }
 

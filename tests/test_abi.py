@@ -46,7 +46,7 @@ def test_status_strings_and_kernel_names():
     assert lib.retopk_status_string(0) == b"ok"
     assert lib.retopk_status_string(2) == b"argument out of range"
     names = binding.retopk_kernel_names()
-    assert {"k_step"} <= set(names)
+    assert {"k_step", "k_dense", "k_dense_merge"} <= set(names)
     assert len(names) == lib.retopk_kernel_count()
 
 
@@ -82,6 +82,7 @@ def test_null_handle_calls_fail_cleanly():
     _, lib = _lib()
     assert lib.retopk_decode_step(None, None, None, None, 10, 1, None, None) == 4
     assert lib.retopk_exact_topk_attn(None, None, None, None, 10, None, None, None) == 4
+    assert lib.retopk_dense_attn(None, None, None, None, 10, None, None) == 4
     assert lib.retopk_init_from_prefill(None, None, None, 10, None) == 4
     assert lib.retopk_read_state(None, None, None, None, None) == 4
     assert lib.retopk_set_timing(None, 1) == 4
