@@ -109,6 +109,11 @@ def _counter_rows(path):
     return rows
 
 
+def _short_name(full):
+    """Kernel name without namespaces or arguments: "ns::(anonymous namespace)::k(int, ...)" -> "k"."""
+    return full.replace("(anonymous namespace)::", "").split("(")[0].split("::")[-1].strip()
+
+
 def _per_dispatch(rows, counter, last=None):
     """{(kernel short name, grid size): [counter value per dispatch, in dispatch
     order]} (KiB). A call that launches one kernel more than once with
@@ -119,7 +124,7 @@ def _per_dispatch(rows, counter, last=None):
     for r in rows:
         if r.get("Counter_Name") != counter:
             continue
-        name = r["Kernel_Name"].split("(")[0].split("::")[-1].strip()
+        name = _short_name(r["Kernel_Name"])
         per.setdefault(name, {}).setdefault(int(r["Dispatch_Id"]), [int(r.get("Grid_Size") or 0), 0.0])
         per[name][int(r["Dispatch_Id"])][1] += float(r["Counter_Value"])
     out = {}
@@ -193,15 +198,16 @@ def summarize_traffic(root, last, workload):
     print(f"copy scale {scale}; wrote {path}")
 
 
-PROFILE_CMD = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof_{leg} -o {leg} --output-format csv -- "
-               "python3 bench.py --only {leg} --steps {steps} --warmup 64 --no-cpu-baseline --no-breakdown")
+PROFILE_CMD = ("rocprofv3 --kernel-trace --stats -d {root}/prof_{leg} -o {leg} --output-format csv -- "
+               "python3 bench.py{wl} --only {leg} --steps {steps} --warmup {warmup} --no-cpu-baseline "
+               "--no-breakdown")
 LEG_TITLES = {"natural": "natural ReTopK decode steps (the metric's step)",
               "exact": "Exact Top-K baseline (retopk_exact_topk_attn, every head exact)",
               "reuse": "forced reuse (tau = -2, T_r = 0)",
               "dense": "dense softmax attention over every key (retopk_dense_attn)"}
 
 
-def summarize_kernels(root, last, workload):
+def summarize_kernels(root, last, workload, warmup=64):
     """Per-kernel durations of the timed dispatches (the last `last` of each
     library kernel) from rocprofv3 kernel traces, plus the whole-run --stats
     rows; written to profiles/kernels_<workload>.md."""
@@ -225,7 +231,7 @@ def summarize_kernels(root, last, workload):
         # it more than once, with different grids), then one row per grid
         by_name = {}
         for r in rows:
-            name = r["Kernel_Name"].split("(")[0].split("::")[-1].strip()
+            name = _short_name(r["Kernel_Name"])
             by_name.setdefault(name, []).append(
                 (int(r.get("Grid_Size_X") or 0), int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
         per = {}
@@ -233,7 +239,9 @@ def summarize_kernels(root, last, workload):
             grids = {g for g, _, _ in ds[-last:]}
             for g, a, e in ds[-last * len(grids):]:
                 per.setdefault((name, g), []).append((a, e))
-        lines += [f"## {leg}: {LEG_TITLES[leg]}", "", "```", PROFILE_CMD.format(leg=leg, steps=last), "```", "",
+        lines += [f"## {leg}: {LEG_TITLES[leg]}", "", "```", PROFILE_CMD.format(
+                      leg=leg, steps=last, root=root.rstrip("/"), warmup=warmup,
+                      wl="" if workload == "headline128k" else f" --workload {workload}"), "```", "",
                   f"Timed dispatches (last {last} of each kernel and grid; a call that launches the kernel "
                   "twice, with different grids, has one row per launch):", "",
                   "| kernel | grid (threads) | dispatches | avg µs | median µs | min µs | max µs |",
@@ -256,7 +264,7 @@ def summarize_kernels(root, last, workload):
             lines += ["", "rocprofv3 --stats (whole run):", "",
                       "| kernel | calls | avg µs | min µs | max µs | total % |", "|---|---|---|---|---|---|"]
             for r in srows:
-                name = r["Name"].split("(")[0].split("::")[-1].strip()
+                name = _short_name(r["Name"])
                 lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1000:.2f} | "
                              f"{float(r['MinNs']) / 1000:.2f} | {float(r['MaxNs']) / 1000:.2f} | "
                              f"{float(r['Percentage']):.1f} |")
@@ -303,7 +311,7 @@ def main():
         summarize_traffic(args.summarize_traffic, args.last, args.workload)
         return
     if args.summarize_kernels:
-        summarize_kernels(args.summarize_kernels, args.last, args.workload)
+        summarize_kernels(args.summarize_kernels, args.last, args.workload, args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path has no "
