@@ -95,6 +95,9 @@ WORKLOADS = {
                               n_kv_heads=4, prompt_len=131072, decode_steps=256, top_k=2048,
                               n_heavy=64, **{**_BASE, "tau": 0.99, "refresh_every": 32,
                                              "query_rho": 0.5}),
+    # One-layer scaling: the headline layer at 1M context (K + V = 2.1 GB per layer).
+    "scale1m": Workload(name="scale1m", config_id=7, batch=1, n_q_heads=28, n_kv_heads=4,
+                        prompt_len=1 << 20, decode_steps=256, top_k=512, n_heavy=64, **_BASE),
 }
 
 

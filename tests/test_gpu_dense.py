@@ -122,3 +122,10 @@ def test_dense_headline_128k():
     """L0 = 131072, 28/4 heads: every head at the first decode length."""
     wl = WORKLOADS["headline128k"].replace(decode_steps=8)
     _run(wl, generate(wl), [131072 + 1])
+
+
+@pytest.mark.slow
+def test_dense_scale_1m():
+    """L0 = 1,048,576: the heads of KV group 1 at the first decode length."""
+    wl = WORKLOADS["scale1m"].replace(decode_steps=8)
+    _run(wl, generate(wl), [(1 << 20) + 1], heads=[(0, h) for h in range(7, 14)])

@@ -400,3 +400,14 @@ def test_stress_128k_b8_sampled():
     """Batch 8 at L0 = 131072 with K = 2048 and tau = 0.99 (mostly exact): one
     sampled (batch row, KV group), 3 lockstep steps without the init check."""
     run_lockstep("stress128k_b8", 3, sub=(5, 2), check_init=False, wl_kw=dict(decode_steps=8))
+
+
+@pytest.mark.slow
+def test_scale_1m_sampled():
+    """L0 = 1,048,576 (one-layer scaling): KV group 2 in lockstep for 4 steps
+    with a refresh every 2 steps (the cache from the GPU's initialisation); the
+    reuse steps' unions span four LDS bitmap windows of 262,144 positions. Then
+    the Exact Top-K baseline on KV group 0."""
+    run_lockstep("scale1m", 4, sub=(0, 2), override=dict(refresh_every=2), check_init=False,
+                 wl_kw=dict(decode_steps=8))
+    run_exact("scale1m", [(1 << 20) + 3], sub=(0, 0), wl_kw=dict(decode_steps=8))
