@@ -58,8 +58,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="rotated layers (0: enough to exceed 1 GiB of KV)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=list(LEGS), default=None,
+    ap.add_argument("--only", choices=list(LEGS) + ["fidelity"], default=None,
                     help="run one timed leg only (for profiler runs)")
+    ap.add_argument("--fidelity-steps", type=int, default=32,
+                    help="decode steps of the support-fidelity leg (0 skips it)")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the per-kernel event-timed pass (counter runs: the last --steps "
                          "dispatches of each kernel are then the timed steps)")
@@ -79,6 +81,7 @@ def parse():
 
 
 LEGS = ("natural", "exact", "reuse", "dense")
+RHO_BINS = (0.85, 0.875, 0.9, 0.925, 0.95)
 COPY_BYTES = 256 << 20
 COPY_REPS = 8
 TRAFFIC_COUNTERS = ("FETCH_SIZE", "WRITE_SIZE")
@@ -573,12 +576,99 @@ def main():
         if "exact_topk_us_per_step" in result:
             result["dense_vs_exact"] = round(result["exact_topk_us_per_step"] / us_de, 3)
 
+    # --- support fidelity against Exact Top-K (quality, not timed) ----------
+    if args.only in (None, "fidelity") and args.fidelity_steps > 0:
+        result["fidelity"] = support_fidelity(wl, data, q_tail, q_dec, ks[0], vs[0], out, stream,
+                                              min(args.fidelity_steps, wl.decode_steps))
+
     # --- CPU oracle baseline ------------------------------------------------
     if not args.no_cpu_baseline and args.only in (None, "natural"):
         result["cpu_baseline"] = cpu_baseline(wl, data, init_state, args.cpu_seconds)
     if "value" not in result:
         result["value"] = None
     print(json.dumps(result), flush=True)
+
+
+def _cos(a, b):
+    na, nb = float(np.linalg.norm(a)), float(np.linalg.norm(b))
+    return float(a @ b) / (na * nb) if na > 0 and nb > 0 else 1.0
+
+
+def support_fidelity(wl, data, q_tail, q_dec, k, v, out, stream, n_steps):
+    """Attention-support fidelity of the natural ReTopK path against Exact
+    Top-K on one layer (Experimental Results, Attention-support fidelity,
+    Figures 5-6): for every head-step, the Exact Top-K support recall
+    |S_hat & S| / |S|, the retained attention mass (full-attention softmax mass
+    on S_hat over that on S), the cosine of the two renormalised attention
+    distributions over positions, and the cosine of the two head outputs. S_hat
+    and both outputs come from the library (a decode step, then the stateless
+    Exact Top-K call on the same query); the full-attention weights are
+    computed here in float64 from the bf16 keys. Summarised over all
+    head-steps, over reuse-path ones, and by rho_max."""
+    import torch
+
+    from sparse_long_context_head_amd import binding as B
+    G, d, L0 = wl.n_q_heads // wl.n_kv_heads, wl.head_dim, wl.prompt_len
+    dev = out.device
+    layer = B.ReTopKLayer.from_workload(wl)
+    layer.init_from_prefill(q_tail, k, L0, stream)
+    out_x = torch.empty_like(out)
+    sel = torch.empty((wl.batch, wl.n_q_heads, wl.top_k), dtype=torch.int32, device=dev)
+    dec = lambda a: (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    kf_all = {(b, g): dec(data["k"][b, g, :L0 + n_steps])
+              for b in range(wl.batch) for g in range(wl.n_kv_heads)}
+    rows = []
+    for t in range(1, n_steps + 1):
+        L = L0 + t
+        layer.decode_step(q_dec[t - 1], k, v, L, t, out, stream)
+        info = layer.step_info()
+        o_r = out.cpu().numpy().astype(np.float64)
+        layer.exact_topk_attn(q_dec[t - 1], k, v, L, out_x, sel, stream)
+        o_x = out_x.cpu().numpy().astype(np.float64)
+        s_x = sel.cpu().numpy()
+        for b in range(wl.batch):
+            for g in range(wl.n_kv_heads):
+                kf = kf_all[b, g][:L]
+                for h in range(g * G, (g + 1) * G):
+                    e = kf @ dec(data["q_dec"][t - 1, b, h]) / math.sqrt(d)
+                    a = np.exp(e - e.max())
+                    S = s_x[b, h, :min(wl.top_k, L)]
+                    Sh = info["sel"][b, h, :info["sel_len"][b, h]]
+                    pS = np.zeros(L)
+                    pS[S] = a[S] / a[S].sum()
+                    pH = np.zeros(L)
+                    pH[Sh] = a[Sh] / a[Sh].sum()
+                    rows.append((int(info["path"][b, h]), float(info["rho_max"][b, h]),
+                                 t,
+                                 len(np.intersect1d(S, Sh)) / len(S), float(a[Sh].sum() / a[S].sum()),
+                                 _cos(pS, pH), _cos(o_r[b, h], o_x[b, h])))
+    # columns: path, rho_max, step, recall, retained mass, attention cosine, output cosine
+    layer.close()
+    r = np.array(rows)
+
+    def summary(m):
+        if not m.any():
+            return None
+        return {"head_steps": int(m.sum()), "support_recall": round(float(r[m, 3].mean()), 4),
+                "retained_mass": round(float(r[m, 4].mean()), 5),
+                "attention_cosine": round(float(r[m, 5].mean()), 5),
+                "output_cosine": round(float(r[m, 6].mean()), 6)}
+
+    reuse = r[:, 0] == 0
+    edges = (-np.inf,) + RHO_BINS + (np.inf,)
+    by = []
+    for lo, hi in zip(edges[:-1], edges[1:]):
+        m = reuse & (r[:, 1] >= lo) & (r[:, 1] < hi)
+        if m.any():
+            by.append({"rho_max": [None if np.isinf(lo) else lo, None if np.isinf(hi) else hi], **summary(m)})
+    # the cache starts from exact supports; reuse steps only re-rank earlier
+    # supports and the recent window, so recall against the current query's
+    # Exact Top-K support is shown per decode step as well
+    by_step = {str(t): summary(r[:, 2] == t) for t in (1, 2, 4, 8, 16, 32, 64, 128, 256) if t <= n_steps}
+    log(f"fidelity over {len(rows)} head-steps: recall {r[:, 3].mean():.3f}, mass {r[:, 4].mean():.4f}, "
+        f"output cosine {r[:, 6].mean():.5f}")
+    return {"decode_steps": n_steps, "all": summary(np.ones(len(r), bool)), "reuse": summary(reuse),
+            "reuse_by_rho_max": by, "by_decode_step": by_step}
 
 
 def cpu_baseline(wl, data, init_state, budget_s):
