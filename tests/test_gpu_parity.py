@@ -207,6 +207,19 @@ def test_exact_more_groups_than_score_work_groups():
               wl_kw=dict(batch=40, n_q_heads=8, n_kv_heads=4, prompt_len=1200, decode_steps=4))
 
 
+def test_exact_sixteen_heads_per_group():
+    """16 query heads on one KV head, every column of the MFMA score tile used."""
+    run_exact("tiny", [5000, 4097, 129, 128, 127], top_k=128,
+              wl_kw=dict(n_q_heads=16, n_kv_heads=1, prompt_len=5000, decode_steps=4))
+
+
+def test_exact_large_top_k():
+    """K = 4096 (R = 2 keeps R K + W within the candidate limit): the finish's
+    support, the boundary bin and the softmax-V span many rounds."""
+    run_exact("tiny", [20000, 4097, 4096, 4095, 9000], top_k=4096,
+              wl_kw=dict(prompt_len=20000, decode_steps=4, top_r=2))
+
+
 def test_exact_integer_ties():
     """Integer-valued keys and queries make fp32 scores exact, so equal scores
     are real ties: the lower index must win, with no near-tie allowance."""
@@ -284,6 +297,18 @@ def test_decode_tiny_window_covers_history():
 def test_decode_small_cache_no_window():
     """C = R = 1 and W = 0 (the ablation without the recent-token guard)."""
     run_lockstep("tiny", 30, override=dict(cache_cap=1, top_r=1, window=0))
+
+
+def test_decode_sixteen_heads_lockstep():
+    """16 query heads on one KV head, a refresh every 4 steps."""
+    run_lockstep("tiny", 8, override=dict(refresh_every=4),
+                 wl_kw=dict(n_q_heads=16, n_kv_heads=1, prompt_len=3000, decode_steps=8))
+
+
+def test_decode_largest_cache():
+    """C = 64 (the largest cache) and R = 8: recall ranks 64 entries, the union
+    merges 8 supports."""
+    run_lockstep("tiny", 12, wl_kw=dict(cache_cap=64, top_r=8, decode_steps=12))
 
 
 def test_decode_gqa16k_lockstep():
