@@ -81,8 +81,8 @@ size_t head_lds_bytes(const Dims& d);
 size_t score_lds_bytes(const Dims& d);
 size_t step_lds_bytes(const Dims& d);
 size_t finish_lds_bytes(const Dims& d);
-// Score work groups of a call at this length.
-int score_grid(const Dims& d, int length);
+// Score work groups of a call at this length and mode (HeadMode).
+int score_grid(const Dims& d, int length, int mode);
 // Rows per query head of LDS a score work group keeps its scores in (0: they
 // go to the score workspace).
 int score_keep_rows(const Dims& d, int length, int n_score);
