@@ -61,6 +61,7 @@ struct retopk_handle {
   int timed = 0;                    // pairs recorded since the last read
   int call_seq = 0;                 // sequence number of the last k_step launch
   float* dense_part = nullptr;      // dense attention's row-slice partials [B*Hq, dense_max_split, kDensePart]
+  int32_t* hint_host = nullptr;     // pinned, device-mapped word behind Bufs::hint
 
   // Tag of the next launch's decision flags: 2 * seq, seq counting 1, 2, ... mod
   // 2^29 (an even modulus, so bit 1, which selects the scored-row counters,
@@ -85,6 +86,8 @@ struct retopk_handle {
   void release() {
     for (void* a : allocs) (void)hipFree(a);
     allocs.clear();
+    if (hint_host != nullptr) (void)hipHostFree(hint_host);
+    hint_host = nullptr;
     for (hipEvent_t e : events) (void)hipEventDestroy(e);
     events.clear();
   }
@@ -253,6 +256,11 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   A(&b.st_path, BH * kStatsCap);
   A(&b.st_rho, BH * kStatsCap);
   A(&b.st_m, BH * kStatsCap);
+  if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&h->hint_host), 64, hipHostMallocMapped);
+  if (e == hipSuccess) {
+    *h->hint_host = 0;
+    e = hipHostGetDevicePointer(reinterpret_cast<void**>(&b.hint), h->hint_host, 0);
+  }
   A(&b.self, 1);
   A(&h->dense_part, BH * static_cast<size_t>(dense_max_split(d)) * kDensePart);
   if (e == hipSuccess) e = hipMemcpy(b.self, &b, sizeof(Bufs), hipMemcpyHostToDevice);
@@ -298,7 +306,8 @@ retopk_status retopk_init_from_prefill(retopk_handle* h, const uint16_t* q_tail,
     const uint16_t* qi = q_tail + static_cast<long>(i) * kHeadDim;
     const int flag = h->next_call_flag();
     st = h->run(kKStep, s, [&] {
-      return launch_step(d, b, qi, q_sb, q_sh, k, nullptr, nullptr, nullptr, len, 0, kModeExact, -1, 1, flag, s);
+      return launch_step(d, b, qi, q_sb, q_sh, k, nullptr, nullptr, nullptr, len, 0, kModeExact, -1, 1, flag, false,
+                         s);
     });
   }
   return st;
@@ -322,8 +331,12 @@ retopk_status retopk_decode_step(retopk_handle* h, const uint16_t* q, const uint
   const int slot = h->stats ? (t_dec - 1) % kStatsCap : -1;
   const long q_sb = static_cast<long>(d.Hq) * kHeadDim, q_sh = kHeadDim;
   const int flag = h->next_call_flag();
+  // exact KV groups of a recent step, written by the device into host-mapped
+  // memory (possibly stale; it only sizes the launch)
+  const int recent_exact = *static_cast<volatile int32_t*>(h->hint_host);
+  const bool wide = 2 * recent_exact >= d.B * d.Hkv;
   retopk_status st = h->run(kKStep, s, [&] {
-    return launch_step(d, b, q, q_sb, q_sh, k, v, out, nullptr, length, t_dec, kModeDecode, slot, 1, flag, s);
+    return launch_step(d, b, q, q_sb, q_sh, k, v, out, nullptr, length, t_dec, kModeDecode, slot, 1, flag, wide, s);
   });
   return st;
 }
@@ -346,7 +359,7 @@ retopk_status retopk_exact_topk_attn(retopk_handle* h, const uint16_t* q, const 
   const long q_sb = static_cast<long>(d.Hq) * kHeadDim, q_sh = kHeadDim;
   const int flag = h->next_call_flag();
   retopk_status st = h->run(kKStep, s, [&] {
-    return launch_step(d, b, q, q_sb, q_sh, k, v, out, sel_out, length, 0, kModeExact, -1, 0, flag, s);
+    return launch_step(d, b, q, q_sb, q_sh, k, v, out, sel_out, length, 0, kModeExact, -1, 0, flag, false, s);
   });
   return st;
 }

@@ -69,6 +69,8 @@ struct Bufs {
   uint8_t* st_path;        // [kStatsCap, BH]
   double* st_rho;          // [kStatsCap, BH]
   int32_t* st_m;           // [kStatsCap, BH]
+  int32_t* hint;           // [1] host-mapped: exact KV groups of the latest decode step (sizes the next
+                           //   launch; read by the host without synchronising)
   Bufs* self;              // device copy of this table (what the step kernel is given)
 };
 
@@ -81,8 +83,9 @@ size_t head_lds_bytes(const Dims& d);
 size_t score_lds_bytes(const Dims& d);
 size_t step_lds_bytes(const Dims& d);
 size_t finish_lds_bytes(const Dims& d);
-// Score work groups of a call at this length and mode (HeadMode).
-int score_grid(const Dims& d, int length, int mode);
+// Score work groups of a call at this length and mode (HeadMode); wide: the
+// call is expected to hold exact heads in at least half the KV groups.
+int score_grid(const Dims& d, int length, int mode, bool wide);
 // Rows per query head of LDS a score work group keeps its scores in (0: they
 // go to the score workspace).
 int score_keep_rows(const Dims& d, int length, int n_score);
@@ -104,7 +107,7 @@ hipError_t launch_reset(const Dims& d, const Bufs& b, hipStream_t s);
 // tags this call's decision flags; its bit 1 selects the half of `scored`.
 hipError_t launch_step(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh, const uint16_t* k,
                        const uint16_t* v, float* out, int32_t* sel_out, int length, int t_dec, int mode,
-                       int stats_slot, int push, int call_flag, hipStream_t s);
+                       int stats_slot, int push, int call_flag, bool wide, hipStream_t s);
 
 // Dense softmax attention (retopk_dense.hip): row slices per KV group of a
 // call at this length, and the most any length gives (the partials workspace

@@ -75,6 +75,7 @@ struct BufsDev {
   gptr<uint8_t> st_path;
   gptr<double> st_rho;
   gptr<int32_t> st_m;
+  gptr<int32_t> hint;
   Bufs* self;
 };
 static_assert(sizeof(BufsDev) == sizeof(Bufs), "device view of the buffer table");
@@ -741,18 +742,20 @@ size_t finish_lds_bytes(const Dims& d) {
          8 * static_cast<size_t>(d.K);
 }
 
-int score_grid(const Dims& d, int length, int mode) {
+int score_grid(const Dims& d, int length, int mode, bool wide) {
   // One 512-thread work group per CU beside the head work groups, so that all
   // are resident at once and none starts late (a reuse head's work group holds
   // its CU for the whole reuse path), but at least half the CUs. Exact calls
-  // with many heads take every CU instead: their head work groups only publish
-  // the decision and leave, and half the CUs cannot stream the keys at the
-  // HBM rate (with few heads the late starters cost more than they add). At
-  // most one per thread of a work group (the finish reads one segment per
-  // thread), and never more than the CUs, so that all score work groups,
-  // which wait for one another, can be resident together.
+  // with many heads, and decode steps expected to be mostly exact, take every
+  // CU instead: their head work groups only publish the decision and leave,
+  // and half the CUs cannot stream the keys at the HBM rate (with few heads
+  // the late starters cost more than they add). At most one per thread of a
+  // work group (the finish reads one segment per thread), and never more than
+  // the CUs, so that all score work groups, which wait for one another, can be
+  // resident together.
   const long bh = static_cast<long>(d.B) * d.Hq;
-  const long free_cu = mode == kModeExact && bh >= d.n_cu / 8 ? d.n_cu : std::max<long>(d.n_cu - bh, d.n_cu / 2);
+  const bool all_cu = (mode == kModeExact || wide) && bh >= d.n_cu / 8;
+  const long free_cu = all_cu ? d.n_cu : std::max<long>(d.n_cu - bh, d.n_cu / 2);
   const long cap = std::min<long>(free_cu, kHeadThreads);
   const long groups = static_cast<long>(d.B) * d.Hkv;
   const long want = groups * ((length + kExactMinRows - 1) / kExactMinRows);
@@ -1635,6 +1638,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
       cnt += m != 0;
     }
     int o = block_exclusive_scan(cnt, &ne, s_tmp);
+    if (!all_exact && w == 0 && threadIdx.x == 0) b.hint[0] = ne;  // (host-mapped; sizes later launches)
     for (int bg = g0; bg < g1; ++bg) {
       const int bb = bg / d.Hkv, g = bg % d.Hkv;
       int m = all_exact ? (1 << d.G) - 1 : 0;
@@ -1811,8 +1815,8 @@ hipError_t launch_reset(const Dims& d, const Bufs& b, hipStream_t s) {
 
 hipError_t launch_step(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh, const uint16_t* k,
                        const uint16_t* v, float* out, int32_t* sel_out, int length, int t_dec, int mode,
-                       int stats_slot, int push, int call_flag, hipStream_t s) {
-  const int n_score = score_grid(d, length, mode);
+                       int stats_slot, int push, int call_flag, bool wide, hipStream_t s) {
+  const int n_score = score_grid(d, length, mode, wide);
   hipLaunchKernelGGL(k_step, dim3(d.B * d.Hq + n_score), dim3(kHeadThreads), step_lds_bytes(d), s, d, b.self, q, q_sb,
                      q_sh, k, v, out, sel_out, length, t_dec, mode, stats_slot, push, call_flag, n_score,
                      score_keep_rows(d, length, n_score));
