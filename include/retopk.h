@@ -96,8 +96,10 @@ const char* retopk_last_error(void);
 
 /* Create a handle on the current HIP device: validates *params and allocates
  * the per-head query-support caches (empty) and every workspace at worst-case
- * size (R*K + W candidates, Lmax scores per head). Synchronous. On success
- * *out receives the handle; on failure *out is set to NULL. */
+ * size (R*K + W candidates, Lmax scores per head), plus one pinned,
+ * device-mapped host word through which decode steps report their exact KV
+ * groups to size later launches. Synchronous. On success *out receives the
+ * handle; on failure *out is set to NULL. */
 retopk_status retopk_create(const retopk_params* params, retopk_handle** out);
 
 /* Free the handle and all its device memory (synchronises the device first).
