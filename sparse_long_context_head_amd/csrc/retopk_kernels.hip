@@ -1356,10 +1356,12 @@ __device__ __forceinline__ int3 wave_boundary(const uint32_t* hist, int keff) {
 // scored: the survivors of every exact head jj of the group (bit jj of
 // emask), one wave per head: b1 from the head's histogram, then 64 rows per
 // ballot in position order with a running count (kEmitU ballots' worth of
-// scores read at once). Scores from LDS (kLds: head jj's row row0 + i at
-// sc[jj * stride + i]) or from the score workspace. Every thread of the block
-// must call it.
+// scores read at once from LDS, kEmitUGlobal from the score workspace, whose
+// round trips are far longer). Scores from LDS (kLds: head jj's row row0 + i
+// at sc[jj * stride + i]) or from the score workspace. Every thread of the
+// block must call it.
 constexpr int kEmitU = 8;
+constexpr int kEmitUGlobal = 32;
 
 template <bool kLds>
 __device__ __forceinline__ void emit_segment(const Dims& d, const BufsDev& b, int bb, int g, unsigned emask, int row0,
@@ -1378,12 +1380,13 @@ __device__ __forceinline__ void emit_segment(const Dims& d, const BufsDev& b, in
     const float* srow = kLds ? sc + jj * stride : b.score + static_cast<long>(h0 + jj) * d.score_stride + row0;
     uint2* region = b.hits + static_cast<long>(h0 + jj) * d.max_len + row0;
     int run = 0;
-    for (int c0 = 0; c0 < nrows; c0 += 64 * kEmitU) {
-      float x[kEmitU];
+    constexpr int U = kLds ? kEmitU : kEmitUGlobal;
+    for (int c0 = 0; c0 < nrows; c0 += 64 * U) {
+      float x[U];
 #pragma unroll
-      for (int u = 0; u < kEmitU; ++u) x[u] = srow[min(c0 + 64 * u + lane, nrows - 1)];  // clamped, masked below
+      for (int u = 0; u < U; ++u) x[u] = srow[min(c0 + 64 * u + lane, nrows - 1)];  // clamped, masked below
 #pragma unroll
-      for (int u = 0; u < kEmitU; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int i = c0 + 64 * u + lane;
         const int sb = __float_as_int(x[u]);
         const bool sv = (i < nrows) & ((static_cast<uint32_t>(sb) ^ (static_cast<uint32_t>(sb >> 31) | 0x80000000u)) >= k0);
