@@ -50,7 +50,7 @@ struct DTiles {
   uint4 v[kDVRows];  // value row t0 + (tid >> 4) + 32 i, dims 8 (tid & 15) .. + 8
 };
 
-struct DShared {
+struct __align__(16) DShared {  // (16-byte rows of p are read as float4)
   float p[kDStage][kDenseMaxGroup];       // the stage's weights, [row][head]
   float wmax[kDWaves][16];                // per wave and head: the stage's maximum score
   float wz[kDWaves][16];                  // per wave and head: the stage's weight sum
