@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=64, help="untimed layer-steps before timing")
     ap.add_argument("--workload", default="headline128k")
     ap.add_argument("--layers", type=int, default=0, help="rotated layers (0: enough to exceed 1 GiB of KV)")
+    for flag, typ in (("top-k", int), ("top-r", int), ("window", int), ("cache-cap", int), ("tau", float),
+                      ("refresh-every", int)):
+        ap.add_argument(f"--{flag}", type=typ, default=None,
+                        help=f"override the workload's {flag.replace('-', '_')} (sensitivity runs)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=list(LEGS) + ["fidelity"], default=None,
@@ -329,6 +333,10 @@ def main():
     from sparse_long_context_head_amd.workload import WORKLOADS, generate
 
     wl = WORKLOADS[args.workload]
+    over = {k: getattr(args, k) for k in ("top_k", "top_r", "window", "cache_cap", "tau", "refresh_every")
+            if getattr(args, k) is not None}
+    if over:
+        wl = wl.replace(**over)
     kv_bytes = 2 * wl.batch * wl.n_kv_heads * wl.max_len * ROW_BYTES
     nl = args.layers or max(1, math.ceil((1 << 30) / kv_bytes))
     n_pos = math.ceil((args.warmup + args.steps) / nl)
