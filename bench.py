@@ -189,12 +189,13 @@ def summarize_traffic(root, last, workload):
                         "kernel_source_sha": kernel_source_hash()})
     doc = {"commands": [
         "(on one MI355X, from the repository root after `cd /tmp && export TMPDIR=/tmp`, absolute paths)",
-        "rocprofv3 --pmc <C> --output-format csv -d gpurun_out/pmc/copy_<C> -o pmc -- python3 bench.py "
+        "(<DIR>: any output directory)",
+        "rocprofv3 --pmc <C> --output-format csv -d <DIR>/copy_<C> -o pmc -- python3 bench.py "
         "--copy-calibration",
-        "rocprofv3 --pmc <C> --output-format csv -d gpurun_out/pmc/<LEG>_<C> -o pmc -- python3 bench.py "
+        "rocprofv3 --pmc <C> --output-format csv -d <DIR>/<LEG>_<C> -o pmc -- python3 bench.py "
         "--only <LEG> --steps 2048 --warmup 64 --no-cpu-baseline --no-breakdown",
         "for C in FETCH_SIZE WRITE_SIZE, LEG in natural exact reuse dense; then",
-        f"python3 bench.py --summarize-traffic gpurun_out/pmc --last {last}"],
+        f"python3 bench.py --summarize-traffic <DIR> --last {last}"],
         "rows": out}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as fh:
@@ -225,7 +226,8 @@ def summarize_kernels(root, last, workload, warmup=64):
              f"the last {last} dispatches of each library kernel, which are the timed decode steps; "
              "the second is rocprofv3's own --stats summary of the whole run (it also counts the cache "
              "initialisation and warm-up dispatches). Summarised by "
-             f"`python3 bench.py --summarize-kernels gpurun_out --last {last}`.", ""]
+             f"`python3 bench.py --summarize-kernels <DIR> --last {last}`, <DIR> being the "
+             "directory the commands wrote to.", ""]
     for leg in LEGS:
         d = os.path.join(root, f"prof_{leg}")
         trace = os.path.join(d, f"{leg}_kernel_trace.csv")
@@ -247,7 +249,7 @@ def summarize_kernels(root, last, workload, warmup=64):
             for g, a, e in ds[-last * len(grids):]:
                 per.setdefault((name, g), []).append((a, e))
         lines += [f"## {leg}: {LEG_TITLES[leg]}", "", "```", PROFILE_CMD.format(
-                      leg=leg, steps=last, root=root.rstrip("/"), warmup=warmup,
+                      leg=leg, steps=last, root="<DIR>", warmup=warmup,
                       wl="" if workload == "headline128k" else f" --workload {workload}"), "```", "",
                   f"Timed dispatches (last {last} of each kernel and grid; a call that launches the kernel "
                   "twice, with different grids, has one row per launch):", "",
