@@ -153,7 +153,7 @@ def summarize_traffic(root, last, workload):
     for c in TRAFFIC_COUNTERS:
         per = _per_dispatch(_counter_rows(os.path.join(root, f"copy_{c}")), c)
         vals = [v for k, vs in per.items() if "copy" in k[0].lower() for v in vs
-                if v * 1024 > COPY_BYTES / 2]
+                if v * 1024 > COPY_BYTES / 4]  # the copies, not small copy dispatches
         if not vals:
             raise SystemExit(f"no copy dispatch with {c} under {root}/copy_{c}")
         scale[c] = COPY_BYTES / (1024.0 * float(np.median(vals)))
