@@ -421,6 +421,17 @@ def test_headline_128k_sampled():
 
 
 @pytest.mark.slow
+def test_gqa64k_b4_sampled():
+    """Batch 4 at L0 = 65536 (every score work group keeps its scores in the
+    workspace, and exact calls take every CU): batch row 2, KV group 1 in
+    lockstep for 4 steps with a refresh at step 2, then the Exact Top-K baseline
+    on batch row 3, KV group 0."""
+    run_lockstep("gqa64k_b4", 4, sub=(2, 1), override=dict(refresh_every=2), check_init=False,
+                 wl_kw=dict(decode_steps=8))
+    run_exact("gqa64k_b4", [65536 + 2], sub=(3, 0), wl_kw=dict(decode_steps=8))
+
+
+@pytest.mark.slow
 def test_stress_128k_b8_sampled():
     """Batch 8 at L0 = 131072 with K = 2048 and tau = 0.99 (mostly exact): one
     sampled (batch row, KV group), 3 lockstep steps without the init check."""
