@@ -16,7 +16,7 @@ constexpr int kHistBits = 10;        // first-level histogram: top 10 bits of th
 constexpr int kNumBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
 constexpr int kStatsCap = 4096;      // decode steps kept in the statistics ring
-constexpr int kExactMinRows = 2048;  // key rows per score work group of the full-history pass, at least
+constexpr int kExactMinRows = 512;   // key rows per score work group of the full-history pass, at least
 constexpr int kBoundaryLds = 4096;   // boundary-bin candidates resolved in LDS (32 KiB of 64-bit keys)
 constexpr int kHeadThreads = 512;    // threads of the per-head kernels
 constexpr int kBitmapWords = 8192;   // LDS bitmap window: 262144 token positions (32 KiB)
