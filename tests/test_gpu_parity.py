@@ -421,6 +421,16 @@ def test_headline_128k_sampled():
 
 
 @pytest.mark.slow
+def test_headline_128k_longer_lockstep():
+    """L0 = 131072: KV group 2 in lockstep for 40 steps with a refresh every 16
+    (the cache from the GPU's initialisation), so that the cache turns over
+    more than once at full size."""
+    r = run_lockstep("headline128k", 40, sub=(0, 2), override=dict(refresh_every=16), check_init=False,
+                     wl_kw=dict(decode_steps=48))
+    assert r["paths"].sum() >= 2 * 7  # two refreshes at least
+
+
+@pytest.mark.slow
 def test_gqa64k_b4_sampled():
     """Batch 4 at L0 = 65536 (every score work group keeps its scores in the
     workspace, and exact calls take every CU): batch row 2, KV group 1 in
