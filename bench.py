@@ -394,6 +394,26 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / args.steps * 1000.0  # us per layer-step
 
+    def step_percentiles(layers, exact=False):
+        """Per-step times from an event pair around every timed step (each pair
+        adds a dispatch gap, so these run a little longer than the timed mean).
+        A GPU sleep queued first keeps the device busy while the host enqueues
+        the steps, so that host submission time does not enter the pairs."""
+        run(layers, 0, args.warmup, exact)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda._sleep(int(2.4e9 * 60e-6 * args.steps))  # about 60 us of host time per step
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            run(layers, args.warmup + i, 1, exact)
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) * 1000.0 for a, b in ev])
+        return {"p50": round(float(np.percentile(t, 50)), 3), "p90": round(float(np.percentile(t, 90)), 3),
+                "p99": round(float(np.percentile(t, 99)), 3), "max": round(float(t.max()), 3),
+                "mean": round(float(t.mean()), 3)}
+
     def kernel_breakdown(layers, exact=False):
         run(layers, 0, args.warmup, exact)
         torch.cuda.synchronize()
@@ -500,6 +520,10 @@ def main():
             # adds a dispatch gap, so these run longer than the timed step)
             nat = make_layers()
             result["kernels_natural"] = kernel_breakdown(nat)
+            for layer in nat:
+                layer.close()
+            nat = make_layers()
+            result["natural_step_us_percentiles"] = step_percentiles(nat)
             for layer in nat:
                 layer.close()
 
