@@ -818,7 +818,7 @@ __device__ __forceinline__ void store_shared2(float* p, float a, float b) {
   store_shared(reinterpret_cast<uint2*>(p), make_uint2(__float_as_uint(a), __float_as_uint(b)));
 }
 
-constexpr int kPollSleep = 8;                 // s_sleep between polls of a flag (about 0.2 us)
+constexpr int kPollSleep = 16;                // s_sleep between polls of a flag (about 0.4 us)
 constexpr long long kWaitTicks = 20000000;    // give up a wait after 200 ms (s_memrealtime is 100 MHz)
 
 constexpr int kQkUnroll = 4;  // 16-row tiles per wave per stage: 512 rows per 8-wave work group
