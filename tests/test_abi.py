@@ -90,3 +90,14 @@ def test_null_handle_calls_fail_cleanly():
     lib.retopk_destroy(None)
     out = ctypes.c_void_p()
     assert lib.retopk_create(None, ctypes.byref(out)) == 1 and out.value is None
+
+
+def test_header_compiles_as_c_and_cxx():
+    import shutil
+    import subprocess
+    for cc, lang in (("gcc", "c"), ("g++", "c++")):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not available")
+        r = subprocess.run([cc, "-fsyntax-only", "-Wall", "-Wextra", "-Werror", "-x", lang, HEADER],
+                           capture_output=True, text=True, timeout=60)
+        assert r.returncode == 0, r.stderr
