@@ -615,6 +615,26 @@ def main():
         result["fidelity"] = support_fidelity(wl, data, q_tail, q_dec, ks[0], vs[0], out, stream,
                                               min(args.fidelity_steps, wl.decode_steps))
 
+    # --- a plain streaming read for reference (torch's sum over 1 GiB) ---------
+    if args.only is None:
+        buf = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            buf.sum()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(10):
+            buf.sum()
+        b.record(stream)
+        torch.cuda.synchronize()
+        gbs = (1 << 30) * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+        result["stream_read_gbs"] = round(gbs, 1)
+        for key in ("roofline", "roofline_exact", "roofline_dense"):
+            if key in result:
+                result[key]["frac_of_stream_read"] = round(result[key]["achieved"] / gbs, 4)
+        del buf
+
     # --- CPU oracle baseline ------------------------------------------------
     if not args.no_cpu_baseline and args.only in (None, "natural"):
         result["cpu_baseline"] = cpu_baseline(wl, data, init_state, args.cpu_seconds)
