@@ -910,7 +910,7 @@ __device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4]
 // (cand_cap each).
 // ---------------------------------------------------------------------------
 constexpr int kCandU = 18;     // candidate rows per 16-lane group in flight: 576 per round
-constexpr int kCandWide = 28;  // ... for 577 .. 896 candidates: one round of 896
+constexpr int kCandWide = 24;  // ... for 577 .. 768 candidates: one round of 768
 
 // Candidate scores (Eq. 10): 16 lanes per key row (16 bytes each), U rows in
 // flight per 16-lane group, bf16 pair products accumulated in fp32 (dot2).
