@@ -45,6 +45,9 @@ Readings taken where the paper is silent:
     and every query head keeps its own cache;
   * refresh applies to all heads at once; the similarity fallback is per head;
   * supports are stored in ascending token order;
+  * a stored support entry that is not a visible key at step t (>= L_t; only a
+    restored snapshot can hold one) is not a candidate; a reuse head with no
+    candidate at all (W = 0) has an empty support and the zero output;
   * softmax is evaluated with the maximum subtracted (identical in exact
     arithmetic to Eq. (12));
   * prompt entry p of the cache holds the causal Exact Top-K support of prompt
@@ -118,11 +121,15 @@ def recent_window(length: int, window: int) -> np.ndarray:
 def candidate_set(supports, retrieved, length: int, window: int) -> np.ndarray:
     """A_t = Unique(union of the retrieved supports and the window) (Eq. (9)).
 
-    Returned sorted ascending; M_t is its length.
+    Only keys visible at this step can be candidates: a stored support entry
+    >= length (possible only in a cache restored from a snapshot, since a
+    cache written by decoding holds earlier steps' supports of shorter
+    lengths) is left out, as the scores of Eq. (10) range over the keys
+    currently available. Returned sorted ascending; M_t is its length.
     """
     pool: set[int] = set()
     for c in retrieved:
-        pool.update(int(i) for i in supports[c])
+        pool.update(int(i) for i in supports[c] if int(i) < length)
     pool.update(int(i) for i in recent_window(length, window))
     return np.array(sorted(pool), dtype=np.int64)
 
@@ -146,7 +153,13 @@ def top_k(indices: np.ndarray, scores: np.ndarray, k: int) -> np.ndarray:
 
 
 def sparse_softmax_v(scores: np.ndarray, v_rows: np.ndarray, head_dim: int) -> np.ndarray:
-    """o = sum_i softmax(e)_i v_i over the selected entries, e = s / sqrt(d) (Eq. (12))."""
+    """o = sum_i softmax(e)_i v_i over the selected entries, e = s / sqrt(d) (Eq. (12)).
+
+    An empty support (a reuse head left with no candidate, possible only with
+    W = 0) gives the zero vector: the sum of Eq. (12) has no terms.
+    """
+    if len(scores) == 0:
+        return np.zeros(head_dim)
     e = np.asarray(scores, dtype=np.float64) / math.sqrt(head_dim)
     w = np.exp(e - np.max(e))
     return (w @ np.asarray(v_rows, dtype=np.float64)) / np.sum(w)

@@ -442,8 +442,72 @@ def pin_dense_attention(o):
     np.testing.assert_allclose(out, ex, rtol=1e-12, atol=1e-14)
 
 
+def pin_state_snapshot(o):
+    """Cache snapshots (the library's read/write-state layout): a hand-built
+    state with fewer than C entries and ragged supports round-trips unchanged,
+    and one step from it follows Eqs. (6)-(9) and the FIFO rule by hand.
+
+    Head 0 holds 2 of C = 4 entries, head 1 holds 3, one of them with an empty
+    support; head 0's older support names key 12, which is not visible at
+    length 10 and so cannot be a candidate. With W = 0, head 1's retrieved
+    supports leave it no visible candidate: its support is empty and its
+    output the zero vector (Eq. (12) has no terms).
+    """
+    d, C, K = 4, 4, 3
+    e = np.eye(d, dtype=np.float32)
+    qbar = np.zeros((1, 2, C, d), np.float32)
+    supp = np.zeros((1, 2, C, K), np.int32)
+    slen = np.zeros((1, 2, C), np.int32)
+    count = np.array([[2, 3]], np.int32)
+    qbar[0, 0, 0], supp[0, 0, 0, :3], slen[0, 0, 0] = e[0], [1, 5, 12], 3   # oldest
+    qbar[0, 0, 1], supp[0, 0, 1, :2], slen[0, 0, 1] = e[1], [0, 2], 2
+    qbar[0, 1, 0], supp[0, 1, 0, :1], slen[0, 1, 0] = e[2], [11], 1
+    qbar[0, 1, 1], slen[0, 1, 1] = e[3], 0
+    qbar[0, 1, 2], supp[0, 1, 2, :2], slen[0, 1, 2] = e[1], [10, 13], 2
+    orc = o.ReTopKOracle(batch=1, n_q_heads=2, n_kv_heads=1, head_dim=d, top_k=K,
+                         cache_cap=C, window=0, top_r=2, refresh_every=0, tau=-2.0)
+    orc.set_state(qbar, supp, slen, count)
+    for got, want in zip(orc.get_state(), (qbar, supp, slen, count)):
+        assert got.dtype == want.dtype and np.array_equal(got, want)
+    # keys: key i has a single nonzero coordinate, so every score is read off by hand
+    length = 10
+    kf = np.zeros((1, 1, 14, d), np.float32)
+    vf = np.zeros((1, 1, 14, d), np.float32)
+    for i in range(14):
+        kf[0, 0, i, i % d] = float(i + 1)
+        vf[0, 0, i] = [i, -i, 2 * i, 1.0]
+    # query head 0 = (3, 1, 0, 0): rho = 3/sqrt(10) with e0 (oldest), 1/sqrt(10) with e1
+    # query head 1 = (0, 2, 1, 0): rho = 1/sqrt(5) (e2), 0 (e3), 2/sqrt(5) (e1)
+    qf = np.array([[[3, 1, 0, 0], [0, 2, 1, 0]]], np.float32)
+    rec = orc.step(bits(qf), bits(kf), bits(vf), length, 1)
+    assert list(rec.retrieved[0][0]) == [0, 1]
+    assert list(rec.retrieved[0][1]) == [2, 0]
+    assert abs(rec.rho_max[0, 0] - float(np.float32(3 / math.sqrt(10)))) < 1e-7
+    # head 0: {1, 5, 12} U {0, 2}, key 12 not visible -> {0, 1, 2, 5}
+    assert list(rec.candidates[0][0]) == [0, 1, 2, 5]
+    # scores q.k_i: key i has value i+1 at coordinate i mod 4
+    sc = {i: [3.0, 1.0, 0.0, 0.0][i % d] * (i + 1) for i in (0, 1, 2, 5)}
+    assert sc == {0: 3.0, 1: 2.0, 2: 0.0, 5: 6.0}
+    assert list(rec.support[0][0]) == [0, 1, 5]
+    w = np.exp(np.array([3.0, 2.0, 6.0]) / 2.0)
+    want0 = (w[:, None] * np.array([vf[0, 0, i] for i in (0, 1, 5)], np.float64)).sum(0) / w.sum()
+    np.testing.assert_allclose(rec.out[0, 0], want0, rtol=1e-12)
+    # head 1: {10, 13} U {11}, none visible at length 10, W = 0 -> empty
+    assert rec.n_cand[0, 1] == 0 and len(rec.support[0][1]) == 0
+    assert np.array_equal(rec.out[0, 1], np.zeros(d))
+    after = orc.get_state()
+    assert list(after[3][0]) == [3, 4]
+    # FIFO: old entries keep their order, the new one is last
+    assert np.array_equal(after[0][0, 0, :2], qbar[0, 0, :2])
+    assert list(after[1][0, 0, 2, :3]) == [0, 1, 5] and after[2][0, 0, 2] == 3
+    assert np.array_equal(after[0][0, 1, :3], qbar[0, 1, :3])
+    assert after[2][0, 1, 3] == 0 and list(after[2][0, 1, :3]) == [1, 0, 2]
+    qb1 = np.array([0, 2, 1, 0], np.float64) / math.sqrt(5)
+    assert np.array_equal(after[0][0, 1, 3], qb1.astype(np.float32))
+
+
 ALL_PINS = [pin_bf16_decode, pin_normalize, pin_top_k, pin_top_r, pin_window_and_union,
             pin_dense_special_case, pin_softmax_properties, pin_split_merge, pin_micro_example,
             pin_forced_exact, pin_forced_reuse_and_candidates, pin_refresh_schedule,
             pin_fallback_threshold, pin_window_covers_history, pin_fifo, pin_init,
-            pin_gqa_mapping, pin_dense_attention]
+            pin_gqa_mapping, pin_dense_attention, pin_state_snapshot]

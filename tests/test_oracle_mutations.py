@@ -50,6 +50,13 @@ MUTATIONS = [
     ("dense_gqa_interleaved", "kv_head = h * hkv // hq", "kv_head = h % hkv"),
     ("dense_reads_past_length", "bf16_to_f64(v_bits[b, kv_head, :length]), d)",
      "bf16_to_f64(v_bits[b, kv_head, 1:length + 1]), d)"),
+    ("snapshot_newest_first", "for i, (qb, s) in enumerate(entries):",
+     "for i, (qb, s) in enumerate(reversed(entries)):"),
+    ("snapshot_ignores_support_len", "supp[b, h, i, : supp_len[b, h, i]]", "supp[b, h, i, :]"),
+    ("snapshot_drops_last_entry", "for i in range(n)]", "for i in range(max(n - 1, 0))]"),
+    ("candidates_keep_invisible_keys", "for i in supports[c] if int(i) < length)", "for i in supports[c])"),
+    ("empty_support_not_zero", "if len(scores) == 0:\n        return np.zeros(head_dim)",
+     "if len(scores) == 0:\n        return np.full(head_dim, np.nan)"),
     ("recall_uses_raw_query", "rho = cosine_recall(qbar, [e[0] for e in entries])",
      "rho = cosine_recall(bf16_to_f64(q_bits[b, h]), [e[0] for e in entries])"),
 ]
