@@ -168,7 +168,13 @@ retopk_status retopk_read_state(retopk_handle* h, float* qbar, int32_t* supp,
 
 /* Replace the caches from host buffers in the retopk_read_state layout
  * (resume from a snapshot). Each count must be 0 .. C, each supp_len 0 .. K,
- * and each support entry 0 .. Lmax-1. Synchronous. */
+ * and each support entry 0 .. Lmax-1. Synchronous.
+ * A later decode step at visible length L ignores stored support entries
+ * >= L (those keys are not visible yet, so they cannot be candidates; a
+ * library-written cache never holds any, since L never decreases). When a
+ * reuse head is left with no candidate at all (W = 0 and nothing visible
+ * in the retrieved supports), its support is empty, its output the zero
+ * vector, and the pushed entry has support size 0. */
 retopk_status retopk_write_state(retopk_handle* h, const float* qbar, const int32_t* supp,
                                  const int32_t* supp_len, const int32_t* count);
 
@@ -207,6 +213,16 @@ retopk_status retopk_read_kernel_times(retopk_handle* h, int32_t n, double* tota
                                        int64_t* launches);
 int32_t retopk_kernel_count(void);
 const char* retopk_kernel_name(int32_t id);
+
+/* Measurement aid, not part of the method: one kernel that reads `bytes`
+ * bytes of device memory at `buf` once, as fast as it can, and computes
+ * nothing else (the measured streaming-read ceiling beside which the
+ * attention kernels' HBM rates are reported). buf must be 16-byte aligned and
+ * bytes a multiple of 16; sink is one device uint32 the kernel may write.
+ * Uses the current device; asynchronous on `stream`. Errors:
+ * RETOPK_INVALID_ARG for a NULL or misaligned pointer or a bad size,
+ * RETOPK_HIP_ERROR when the launch fails. */
+retopk_status retopk_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 /* Bytes of device memory the handle holds. */
 size_t retopk_device_bytes(const retopk_handle* h);

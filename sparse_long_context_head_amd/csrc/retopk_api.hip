@@ -382,6 +382,19 @@ retopk_status retopk_dense_attn(retopk_handle* h, const uint16_t* q, const uint1
   return h->run(kKDenseMerge, s, [&] { return launch_dense(h->d, q, k, v, out, length, h->dense_part, s, 1); });
 }
 
+retopk_status retopk_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (buf == nullptr || sink == nullptr) return fail(RETOPK_INVALID_ARG, "retopk_stream_read: NULL pointer");
+  if (!aligned(buf, 16) || bytes % 16 != 0 || !aligned(sink, 4))
+    return fail(RETOPK_INVALID_ARG, "retopk_stream_read: buf must be 16-byte aligned, bytes a multiple of 16");
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+    return fail(RETOPK_NO_DEVICE, "retopk_stream_read: no usable device");
+  if (bytes == 0) return RETOPK_OK;
+  const hipError_t e = launch_stream_read(buf, bytes, sink, n_cu, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RETOPK_OK : hip_fail(e, "retopk_stream_read");
+}
+
 retopk_status retopk_read_state(retopk_handle* h, float* qbar, int32_t* supp, int32_t* supp_len,
                                 int32_t* count) {
   if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_read_state: NULL handle");
@@ -431,7 +444,7 @@ retopk_status retopk_write_state(retopk_handle* h, const float* qbar, const int3
     for (int i = 0; i < n; ++i) {
       const size_t e = bh * C + i;
       const int len = supp_len[e];
-      if (len < 1 || len > d.K) return fail(RETOPK_OUT_OF_RANGE, "retopk_write_state: supp_len out of range");
+      if (len < 0 || len > d.K) return fail(RETOPK_OUT_OF_RANGE, "retopk_write_state: supp_len out of range");
       for (int j = 0; j < len; ++j) {
         const int x = supp[e * K + j];
         if (x < 0 || x >= d.max_len) return fail(RETOPK_OUT_OF_RANGE, "retopk_write_state: support index out of range");

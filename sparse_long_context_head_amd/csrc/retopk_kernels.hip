@@ -91,6 +91,14 @@ constexpr float kInvSqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
 // work group reads), so global traffic stays in flight across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Wait until this wave's global stores, atomics and loads have completed
+// (vmcnt counts all of them on gfx9-family parts). A work group publishes data
+// to other work groups by having every wave that wrote a part of it execute
+// this before the barrier that precedes the flag store: s_barrier alone (and
+// __syncthreads(), which compiles to it with an LDS wait only) lets a wave
+// arrive with stores still in flight, so the flag could become visible first.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Order-preserving map of a float32 to uint32 (larger float, larger key).
 // Negative zero is folded into positive zero so that the two compare equal.
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -643,7 +651,7 @@ __device__ __forceinline__ void attend_reduce(float (&acc)[8], float z, float* o
       zz += sh.red[g2][kHeadDim];
     }
     if (out_z == nullptr) {
-      out[threadIdx.x] = a / zz;
+      out[threadIdx.x] = zz > 0.f ? a / zz : 0.f;  // an empty support gives the zero vector
     } else {
       out[threadIdx.x] = a;
       if (threadIdx.x == 0) *out_z = zz;
@@ -1017,6 +1025,7 @@ __device__ __forceinline__ void head_role(const Dims& d, const BufsDev& b, const
     // the path rule needs only rho_max: publish the decision before ranking
     if (wave == 0) {
       const double mxr = wave_max_f64(lane < count ? sh.rho[lane] : -INFINITY);
+      wait_vmem();  // this wave's q_bar stores are complete before the flag that publishes them
       if (lane == 0) store_shared(b.dec + bh, call_flag | ((refresh || count == 0 || mxr < d.tau) ? 1 : 0));
     }
     // Rank of FIFO position p under (rho desc, position asc), counted in
@@ -1066,7 +1075,10 @@ __device__ __forceinline__ void head_role(const Dims& d, const BufsDev& b, const
   }
   // publish the decision to the score work groups (decode mode did so above;
   // the histogram half of this call was cleared during the previous one)
-  if (tid == 0 && mode != kModeDecode) store_shared(b.dec + bh, call_flag | (exact ? 1 : 0));
+  if (mode != kModeDecode && wave == 0) {
+    wait_vmem();  // wave 0's q_bar stores are complete before the flag
+    if (tid == 0) store_shared(b.dec + bh, call_flag | (exact ? 1 : 0));
+  }
   if (exact) {
     if (tid == 0) b.m[bh] = 0;
     return;
@@ -1602,6 +1614,14 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
   const int stride = keep + 4;
   float* s_sc = reinterpret_cast<float*>(dyn + static_cast<size_t>(d.G) * kNumBins * 4);
 
+  // clear the other half of a slice of the heads' histograms for the next call
+  // (first, so that a call that gives up below still leaves it clear)
+  for (int hh = static_cast<int>(static_cast<long>(w) * BH / nW); hh < static_cast<int>(static_cast<long>(w + 1) * BH / nW);
+       ++hh) {
+    uint4* hz = reinterpret_cast<uint4*>(b.hist + (static_cast<long>(hh) * 2 + (par ^ 1)) * kNumBins);
+    for (int i = threadIdx.x; i < kNumBins / 4; i += blockDim.x) hz[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+
   // every head's decision of this call, published by the head work groups
   // (lower block indices, so already running); bounded wait
   if (!all_exact) {
@@ -1653,12 +1673,6 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
     }
   }
   lds_barrier();
-  // clear the other half of a slice of the heads' histograms for the next call
-  for (int hh = static_cast<int>(static_cast<long>(w) * BH / nW); hh < static_cast<int>(static_cast<long>(w + 1) * BH / nW);
-       ++hh) {
-    uint4* hz = reinterpret_cast<uint4*>(b.hist + (static_cast<long>(hh) * 2 + (par ^ 1)) * kNumBins);
-    for (int i = threadIdx.x; i < kNumBins / 4; i += blockDim.x) hz[i] = make_uint4(0u, 0u, 0u, 0u);
-  }
   if (ne == 0) return;
   const long T = static_cast<long>(ne) * length;
   int e0, r0, e1, r1;
@@ -1715,7 +1729,8 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
     }
     lb += (rend - row0 + 15) & ~15;
   }
-  __syncthreads();  // every wave's histogram adds are complete
+  wait_vmem();      // this wave's histogram adds (and workspace scores) have completed ...
+  __syncthreads();  // ... in every wave, before the flag that publishes them
   if (threadIdx.x == 0) store_shared(b.wdone + w, call_flag);
 
   // the heads this work group finishes: head m of group e when x_m (see
@@ -1741,7 +1756,8 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
                           par, nullptr, stride);
     lb += (rend - row0 + 15) & ~15;
   }
-  __syncthreads();  // every wave's (device-scope) survivor and count stores are complete
+  wait_vmem();      // this wave's survivor and count stores have completed ...
+  __syncthreads();  // ... in every wave, before the flag that publishes them
   if (threadIdx.x == 0) store_shared(b.wdone + d.n_cu + w, call_flag);
 
   // ---- phase 3: finish the owned heads ----

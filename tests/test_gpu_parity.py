@@ -88,12 +88,13 @@ def close_checked(layer):
     layer.close()
 
 
-def run_lockstep(name, n_steps, sub=None, override=None, check_init=True, wl_kw=None):
-    """Run n_steps decode steps; before each, the oracle adopts the GPU's cache."""
+def run_lockstep(name, n_steps, sub=None, override=None, check_init=True, wl_kw=None, given=None):
+    """Run n_steps decode steps; before each, the oracle adopts the GPU's cache.
+    `given` = (workload, data) replaces the seeded workload's inputs."""
     torch = _torch()
     B = _B()
     override = dict(override or {})
-    wl, data = data_for(name, **(wl_kw or {}))
+    wl, data = given if given is not None else data_for(name, **(wl_kw or {}))
     n0 = min(override.get("cache_cap", wl.cache_cap), wl.prompt_len)
     if n0 != data["q_tail"].shape[2]:
         data = {**data, "q_tail": np.ascontiguousarray(data["q_tail"][:, :, -n0:])}
@@ -110,9 +111,16 @@ def run_lockstep(name, n_steps, sub=None, override=None, check_init=True, wl_kw=
     swaps, errs = [], []
     log(f"[lockstep] {name} sub={sub} override={override} steps={n_steps}")
     layer.init_from_prefill(dev["q_tail"], dev["k"], L0)
-    if check_init:
+    if check_init is True:
         orc.init_from_prefill(odata["q_tail"], odata["k"], L0)
         compare_init(layer, orc, odata, L0, sl, swaps)
+    elif check_init:
+        # the initialisation compared on one (batch row, KV group) only
+        ib, ig = check_init
+        iorc, _ = _oracle_for(wl, (ib, ig), override)
+        idata = sub_problem(data, ib, ig, G)
+        iorc.init_from_prefill(idata["q_tail"], idata["k"], L0)
+        compare_init(layer, iorc, idata, L0, (slice(ib, ib + 1), slice(ig * G, (ig + 1) * G)), swaps)
     out = torch.empty((wl.batch, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
     paths, ms = [], []
     heads = [(b, h) for b in range(orc.batch) for h in range(orc.hq)]
@@ -319,6 +327,107 @@ def test_decode_gqa32k_batch4_lockstep():
     run_lockstep("gqa32k_b4", 6, wl_kw=dict(decode_steps=8), override=dict(refresh_every=3))
 
 
+def integer_tie_data(seed, prompt_len=3000, steps=6, hq=8, hkv=2, cache_cap=8, nonzero=3,
+                     zero_query_step=None, zero_heads=()):
+    """Keys with entries in {-1, 0, 1} and queries with `nonzero` entries of
+    +-1: every score is a small integer, exact in fp32, so a reuse head's
+    candidates share few distinct scores and the one holding the K-th largest
+    is shared by more than 64 of them (the rerank's radix-select fallback),
+    with real ties decided by the lower index. Optionally the query of one
+    decode step is zero for some heads: all its candidate scores are equal."""
+    rng = np.random.default_rng(seed)
+    k = f32_to_bf16_bits(rng.integers(-1, 2, size=(1, hkv, prompt_len + steps, 128)).astype(np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((1, hkv, prompt_len + steps, 128)).astype(np.float32))
+    q = np.zeros((1, hq, cache_cap + steps, 128), np.float32)
+    for h in range(hq):
+        for n in range(cache_cap + steps):
+            dims = rng.choice(128, nonzero, replace=False)
+            q[0, h, n, dims] = rng.choice([-1.0, 1.0], nonzero)
+    if zero_query_step is not None:
+        q[0, list(zero_heads), cache_cap + zero_query_step - 1] = 0.0
+    q = f32_to_bf16_bits(q)
+    wl = WORKLOADS["tiny"].replace(name="integer_ties", n_q_heads=hq, n_kv_heads=hkv, prompt_len=prompt_len,
+                                   decode_steps=steps, top_k=100, cache_cap=cache_cap, window=16, top_r=4,
+                                   tau=-2.0, refresh_every=0)
+    data = dict(k=k, v=v, q_tail=np.ascontiguousarray(q[:, :, :cache_cap]),
+                q_dec=np.ascontiguousarray(q[:, :, cache_cap:].transpose(2, 0, 1, 3)))
+    return wl, data
+
+
+def _boundary_crowding(wl, data, steps):
+    """Per reuse head-step of the oracle's trajectory: (M_t, candidates sharing
+    the K-th score, of which the support keeps `need`)."""
+    orc = O.ReTopKOracle.from_workload(wl)
+    orc.init_from_prefill(data["q_tail"], data["k"], wl.prompt_len)
+    rows = []
+    for t in range(1, steps + 1):
+        rec = orc.step(data["q_dec"][t - 1], data["k"], data["v"], wl.prompt_len + t, t)
+        for h in range(wl.n_q_heads):
+            cand = rec.candidates[0][h]
+            s = O.qk_scores(data["q_dec"][t - 1][0, h], data["k"][0, h * wl.n_kv_heads // wl.n_q_heads, cand])
+            kth = np.sort(s)[::-1][wl.top_k - 1]
+            rows.append((len(cand), int((s == kth).sum()), wl.top_k - int((s > kth).sum())))
+    return rows
+
+
+def test_decode_reuse_rerank_integer_ties():
+    """Forced reuse on integer-valued scores: the K-th largest candidate score
+    is shared by more than 64 candidates at every head-step (checked on the
+    oracle's trajectory first), so the rerank takes its radix-select fallback;
+    real ties must go to the lower index, with no near-tie allowance."""
+    wl, data = integer_tie_data(31)
+    rows = _boundary_crowding(wl, data, wl.decode_steps)
+    assert all(m > wl.top_k and cnt > 64 and need < cnt for m, cnt, need in rows), rows
+    r = run_lockstep("integer_ties", wl.decode_steps, given=(wl, data))
+    assert not r["paths"].any()
+    assert not r["swaps"], f"integer scores leave no near-tie: {r['swaps'][:3]}"
+
+
+def test_decode_reuse_zero_query_all_scores_equal():
+    """Forced reuse where step 3's query is zero for heads 0-3: every candidate
+    score is 0 (minimum = maximum), so the rerank goes straight to the radix
+    select and keeps the K lowest candidate indices; the zero q_bar enters the
+    cache and step 4 recalls against it (rho = 0)."""
+    wl, data = integer_tie_data(32, zero_query_step=3, zero_heads=(0, 1, 2, 3))
+    r = run_lockstep("integer_ties", wl.decode_steps, given=(wl, data))
+    assert not r["paths"].any() and not r["swaps"]
+
+
+def test_decode_empty_candidate_set():
+    """W = 0 and a restored cache whose supports name only keys past the
+    visible length: the reuse heads have no candidate, an empty support and
+    the zero output; the entry pushed has support size 0 (restored again
+    below, which write_state accepts)."""
+    torch = _torch()
+    B = _B()
+    wl, data = data_for("tiny")
+    wl = wl.replace(window=0)
+    dev = upload(data)
+    L = wl.prompt_len + 1
+    layer = B.ReTopKLayer.from_workload(wl, window=0, tau=-2.0, refresh_every=0)
+    orc = O.ReTopKOracle.from_workload(wl, window=0, tau=-2.0, refresh_every=0)
+    C, K = wl.cache_cap, wl.top_k
+    qbar = np.zeros((1, 1, C, 128), np.float32)
+    qbar[0, 0, :, 0] = 1.0
+    supp = np.zeros((1, 1, C, K), np.int32)
+    supp[0, 0, :, :3] = [L, L + 5, wl.max_len - 1]
+    slen = np.full((1, 1, C), 3, np.int32)
+    count = np.array([[C]], np.int32)
+    layer.write_state(qbar, supp, slen, count)
+    out = torch.full((1, 1, 128), 7.0, dtype=torch.float32, device="cuda")
+    orc.set_state(*layer.read_state())
+    layer.decode_step(dev["q_dec"][0], dev["k"], dev["v"], L, 1, out)
+    rec = orc.step(data["q_dec"][0], data["k"], data["v"], L, 1)
+    info = layer.step_info()
+    assert rec.n_cand[0, 0] == 0 and len(rec.support[0][0]) == 0
+    assert info["path"][0, 0] == 0 and info["n_cand"][0, 0] == 0 and info["sel_len"][0, 0] == 0
+    assert np.array_equal(out.cpu().numpy(), np.zeros((1, 1, 128), np.float32))
+    st = layer.read_state()
+    assert st[3][0, 0] == C and st[2][0, 0, C - 1] == 0
+    layer.write_state(*st)
+    close_checked(layer)
+
+
 def test_decode_free_running_tiny():
     """Without re-synchronisation the GPU trajectory matches the oracle's until
     the first near-tie swap (if any)."""
@@ -407,20 +516,25 @@ def test_stats_ring_matches_step_info():
 
 
 # ---------------------------------------------------------------------------
-# Full-size configurations, sampled
+# Full-size configurations: every head for a few steps, then longer sampled runs
 # ---------------------------------------------------------------------------
 
 @pytest.mark.slow
-def test_headline_128k_sampled():
-    """L0 = 131072, 28/4 heads, K = 512: the oracle follows KV group 1 in
-    lockstep (init included) for 6 steps with a refresh at step 3."""
-    run_lockstep("headline128k", 6, sub=(0, 1), override=dict(refresh_every=3),
-                 wl_kw=dict(decode_steps=16))
-    swaps = run_exact("headline128k", [131072 + 5], sub=(0, 3), wl_kw=dict(decode_steps=16))
-    log(f"[exact] headline group 3: swaps {len(swaps)}")
+@pytest.mark.timeout(900)
+def test_headline_128k_every_head():
+    """L0 = 131072, 28/4 heads, K = 512, in the launch configuration the bench
+    times: every query head in lockstep for 6 steps with a refresh at step 3
+    (the initialisation compared on KV group 1), then the Exact Top-K baseline
+    on every head."""
+    r = run_lockstep("headline128k", 6, override=dict(refresh_every=3), wl_kw=dict(decode_steps=16),
+                     check_init=(0, 1))
+    assert r["paths"][2].all()
+    swaps = run_exact("headline128k", [131072 + 5], wl_kw=dict(decode_steps=16))
+    log(f"[exact] headline every head: swaps {len(swaps)}")
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_headline_128k_longer_lockstep():
     """L0 = 131072: KV group 2 in lockstep for 40 steps with a refresh every 16
     (the cache from the GPU's initialisation), so that the cache turns over
@@ -431,29 +545,57 @@ def test_headline_128k_longer_lockstep():
 
 
 @pytest.mark.slow
-def test_gqa64k_b4_sampled():
-    """Batch 4 at L0 = 65536 (every score work group keeps its scores in the
-    workspace, and exact calls take every CU): batch row 2, KV group 1 in
-    lockstep for 4 steps with a refresh at step 2, then the Exact Top-K baseline
-    on batch row 3, KV group 0."""
-    run_lockstep("gqa64k_b4", 4, sub=(2, 1), override=dict(refresh_every=2), check_init=False,
-                 wl_kw=dict(decode_steps=8))
-    run_exact("gqa64k_b4", [65536 + 2], sub=(3, 0), wl_kw=dict(decode_steps=8))
+@pytest.mark.timeout(900)
+def test_headline_128k_forced_reuse_k1024():
+    """K = 1024 at 128K (the pages' cross-model budget): every head forced onto
+    the reuse path (tau = -2, T_r = 0) for 4 lockstep steps, R K + W = 4128
+    candidates at most."""
+    r = run_lockstep("headline128k", 4, override=dict(top_k=1024, tau=-2.0, refresh_every=0),
+                     check_init=False, wl_kw=dict(decode_steps=8))
+    assert not r["paths"].any()
+    assert max(r["ms"]) > 1024
 
 
 @pytest.mark.slow
-def test_stress_128k_b8_sampled():
-    """Batch 8 at L0 = 131072 with K = 2048 and tau = 0.99 (mostly exact): one
-    sampled (batch row, KV group), 3 lockstep steps without the init check."""
-    run_lockstep("stress128k_b8", 3, sub=(5, 2), check_init=False, wl_kw=dict(decode_steps=8))
+@pytest.mark.timeout(900)
+def test_gqa64k_b4_every_head():
+    """Batch 4 at L0 = 65536 (scores in the workspace, exact calls on every
+    CU): all 112 query heads in lockstep for 4 steps with a refresh at step 2,
+    then the Exact Top-K baseline on every head."""
+    run_lockstep("gqa64k_b4", 4, override=dict(refresh_every=2), check_init=False, wl_kw=dict(decode_steps=8))
+    run_exact("gqa64k_b4", [65536 + 2], wl_kw=dict(decode_steps=8))
 
 
 @pytest.mark.slow
-def test_scale_1m_sampled():
-    """L0 = 1,048,576 (one-layer scaling): KV group 2 in lockstep for 4 steps
+@pytest.mark.timeout(900)
+def test_stress_128k_b8_every_head():
+    """Batch 8 at L0 = 131072 with K = 2048 and tau = 0.99 (mostly exact): all
+    224 query heads in lockstep for 3 steps, then the Exact Top-K baseline on
+    every head."""
+    r = run_lockstep("stress128k_b8", 3, check_init=False, wl_kw=dict(decode_steps=8))
+    assert r["paths"].mean() > 0.9
+    run_exact("stress128k_b8", [131072 + 3], wl_kw=dict(decode_steps=8))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_stress_shape_forced_reuse_k2048():
+    """The stress layer's largest reuse layout: one batch row at L0 = 131072,
+    K = 2048, every head forced onto the reuse path (tau = -2, T_r = 0) for 4
+    lockstep steps; R K + W = 8224 candidates at most (low query similarity
+    keeps the retrieved supports apart, so the union is large)."""
+    r = run_lockstep("stress128k_b8", 4, override=dict(tau=-2.0, refresh_every=0), check_init=False,
+                     wl_kw=dict(batch=1, decode_steps=8))
+    assert not r["paths"].any()
+    assert max(r["ms"]) > 4096
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_scale_1m_every_head():
+    """L0 = 1,048,576 (one-layer scaling): every head in lockstep for 4 steps
     with a refresh every 2 steps (the cache from the GPU's initialisation); the
-    reuse steps' unions span four LDS bitmap windows of 262,144 positions. Then
-    the Exact Top-K baseline on KV group 0."""
-    run_lockstep("scale1m", 4, sub=(0, 2), override=dict(refresh_every=2), check_init=False,
-                 wl_kw=dict(decode_steps=8))
-    run_exact("scale1m", [(1 << 20) + 3], sub=(0, 0), wl_kw=dict(decode_steps=8))
+    reuse steps' unions span four LDS bitmap windows of 262,144 positions.
+    Then the Exact Top-K baseline on every head."""
+    run_lockstep("scale1m", 4, override=dict(refresh_every=2), check_init=False, wl_kw=dict(decode_steps=8))
+    run_exact("scale1m", [(1 << 20) + 3], wl_kw=dict(decode_steps=8))
