@@ -59,6 +59,7 @@ _SIGNATURES = {
     "retopk_kernel_name": (ctypes.c_char_p, [_I32]),
     "retopk_device_bytes": (ctypes.c_size_t, [_P]),
     "retopk_read_device_error": (ctypes.c_int, [_P, _P]),
+    "retopk_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
 }
 
 _lib = None
@@ -279,6 +280,14 @@ def retopk_read_device_error(h: Handle) -> int:
     word = np.zeros(1, np.int32)
     _check(load_library().retopk_read_device_error(h.ptr, _ptr(word)))
     return int(word[0])
+
+
+def retopk_stream_read(buf, sink, stream=None):
+    """One plain streaming read of the whole device tensor `buf` (measurement aid)."""
+    if not buf.is_cuda or not sink.is_cuda:
+        raise ValueError("buf and sink must be device tensors")
+    _check(load_library().retopk_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                             _stream(stream, buf.device)))
 
 
 def bf16_tensor(bits: np.ndarray, device="cuda"):

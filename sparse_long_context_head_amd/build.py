@@ -12,7 +12,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["retopk_kernels.hip", "retopk_dense.hip", "retopk_api.hip"]
+SOURCES = ["retopk_kernels.hip", "retopk_dense.hip", "retopk_probe.hip", "retopk_api.hip"]
 LIB = os.path.join(PKG, "libretopk.so")
 
 FLAGS = [

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 
@@ -118,4 +119,7 @@ void dense_split(const Dims& d, int length, int* n_split, int* rows);
 // out (k_dense_merge). Both on stream s, one launch each.
 hipError_t launch_dense(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v, float* out,
                         int length, float* part, hipStream_t s, int phase);
+
+// Plain streaming read of `bytes` (a multiple of 16) at buf (retopk_probe.hip).
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int n_cu, hipStream_t s);
 }  // namespace retopk

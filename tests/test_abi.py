@@ -87,6 +87,9 @@ def test_null_handle_calls_fail_cleanly():
     assert lib.retopk_read_state(None, None, None, None, None) == 4
     assert lib.retopk_set_timing(None, 1) == 4
     assert b"NULL handle" in lib.retopk_last_error()
+    # the streaming-read probe checks its arguments before touching a device
+    assert lib.retopk_stream_read(None, 16, None, None) == 1
+    assert b"NULL pointer" in lib.retopk_last_error()
     lib.retopk_destroy(None)
     out = ctypes.c_void_p()
     assert lib.retopk_create(None, ctypes.byref(out)) == 1 and out.value is None

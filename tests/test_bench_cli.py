@@ -60,6 +60,10 @@ def test_traffic_scaled_by_the_copy(tmp_path, monkeypatch):
     k = "retopk::k_step(int)"
     _write_counters(tmp_path / "exact_FETCH_SIZE", "FETCH_SIZE", [(i, k, 1000, 100.0) for i in range(1, 5)])
     _write_counters(tmp_path / "exact_WRITE_SIZE", "WRITE_SIZE", [(i, k, 1000, 10.0) for i in range(1, 5)])
+    # the counter run's own result line: its timed window and algorithmic bytes
+    (tmp_path / "exact_FETCH_SIZE.json").write_text(json.dumps(
+        {"steps": 4, "warmup": 2, "config": {"rotated_layers": 3},
+         "roofline_exact": {"algorithmic_bytes_per_call": 200000}}))
     out = tmp_path / "repo"
     (out / "profiles").mkdir(parents=True)
     monkeypatch.setattr(bench, "ROOT", str(out))
@@ -70,5 +74,29 @@ def test_traffic_scaled_by_the_copy(tmp_path, monkeypatch):
     assert row["kernel"] == "k_step" and row["leg"] == "exact" and row["dispatches"] == 4
     assert row["fetch_bytes_per_launch"] == 2 * 100 * 1024
     assert row["write_bytes_per_launch"] == 10 * 1024
-    assert bench.load_traffic("k_step", "w", "exact") == 210 * 1024
-    assert bench.load_traffic("k_step", "w", "natural") is None
+    win = {"steps": 4, "warmup": 2, "layers": 3}
+    assert row["window"] == win and row["algorithmic_bytes_per_launch"] == 200000
+    # traffic only for a run over the same window; else the other window's row beside it
+    assert bench.load_traffic("k_step", "w", "exact", win) == (210 * 1024, None)
+    t, other = bench.load_traffic("k_step", "w", "exact", {**win, "steps": 20})
+    assert t is None and other == {"window": win, "hbm_bytes_per_launch": 210 * 1024,
+                                   "algorithmic_bytes_per_launch": 200000}
+    assert bench.load_traffic("k_step", "w", "natural", win) == (None, None)
+    # a later summary over another window keeps this row
+    (tmp_path / "exact_FETCH_SIZE.json").write_text(json.dumps(
+        {"steps": 20, "warmup": 5, "config": {"rotated_layers": 3},
+         "roofline_exact": {"algorithmic_bytes_per_call": 200001}}))
+    bench.summarize_traffic(str(tmp_path), 4, "w")
+    doc = json.load(open(out / "profiles" / "traffic.json"))
+    assert sorted(r["window"]["steps"] for r in doc["rows"]) == [4, 20]
+
+
+def test_layer_offsets_spread_over_the_decode():
+    # 25 layer-steps over 4 layers: layer 0 runs 7 positions, the others 6
+    counts = [len(range(l, 25, 4)) for l in range(4)]
+    offs = bench.layer_offsets(counts, 512)
+    assert offs[0] == 0 and offs[-1] + counts[-1] == 512 and offs == sorted(offs)
+    assert bench.layer_offsets([516] * 4, 516) == [0, 0, 0, 0]
+    assert bench.layer_offsets([7], 512) == [0]
+    offs = bench.layer_offsets([3] * 32, 256)
+    assert offs[0] == 0 and offs[-1] + 3 == 256 and offs == sorted(offs)
