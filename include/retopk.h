@@ -156,6 +156,29 @@ retopk_status retopk_exact_topk_attn(retopk_handle* h, const uint16_t* q, const 
 retopk_status retopk_dense_attn(retopk_handle* h, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, int32_t length, float* out, void* stream);
 
+/* retopk_dense_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * handle, no allocation of any kind. The shapes are given per call (head
+ * dimension 128); q, k, v and out are as for retopk_dense_attn, and so is the
+ * result, from the same kernels. The row slices' partial results go to a
+ * scratch array of 4 MiB that the library holds in device memory on every GPU
+ * it runs on until the process ends; a call needs
+ * batch * n_q_heads * ceil(CUs / (batch * n_kv_heads)) * 528 bytes of it
+ * (0.9 MiB for 28 query heads over 4 KV heads at batch 1 on 256 CUs) and is
+ * refused with RETOPK_OUT_OF_RANGE, before any device work, when that exceeds
+ * 4 MiB. Every call on one GPU shares that GPU's array: calls that overlap on
+ * one GPU (other streams, other threads) race and give wrong results; a call
+ * leaves nothing in it that a later call relies on. Uses the current device;
+ * two launches on `stream`, asynchronous.
+ * Errors: RETOPK_INVALID_ARG for a NULL or misaligned tensor or inconsistent
+ * head counts, RETOPK_OUT_OF_RANGE for sizes outside the limits above,
+ * RETOPK_NO_DEVICE without a usable GPU, RETOPK_HIP_ERROR when a launch
+ * fails. */
+retopk_status retopk_dense_attn_noalloc(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                        int32_t max_len, const uint16_t* q, const uint16_t* k,
+                                        const uint16_t* v, int32_t length, float* out,
+                                        void* stream);
+
 /* Copy the caches to host buffers, entries oldest first; unused slots zero.
  *   qbar      float32 [B, Hq, C, D]   normalised queries
  *   supp      int32   [B, Hq, C, K]   supports (ascending), padded with 0

@@ -60,6 +60,7 @@ _SIGNATURES = {
     "retopk_device_bytes": (ctypes.c_size_t, [_P]),
     "retopk_read_device_error": (ctypes.c_int, [_P, _P]),
     "retopk_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
+    "retopk_dense_attn_noalloc": (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P, _P]),
 }
 
 _lib = None
@@ -280,6 +281,18 @@ def retopk_read_device_error(h: Handle) -> int:
     word = np.zeros(1, np.int32)
     _check(load_library().retopk_read_device_error(h.ptr, _ptr(word)))
     return int(word[0])
+
+
+def retopk_dense_attn_noalloc(q, k, v, length: int, out, stream=None):
+    """Dense attention without a handle or any allocation (shapes from the tensors)."""
+    b, hq, d = q.shape
+    hkv, max_len = k.shape[1], k.shape[2]
+    _check_tensor("q", q, (b, hq, d), _BF16)
+    _check_tensor("k", k, (b, hkv, max_len, d), _BF16)
+    _check_tensor("v", v, (b, hkv, max_len, d), _BF16)
+    _check_tensor("out", out, (b, hq, d), ("float32",))
+    _check(load_library().retopk_dense_attn_noalloc(b, hq, hkv, max_len, _ptr(q), _ptr(k), _ptr(v), length,
+                                                    _ptr(out), _stream(stream, q.device)))
 
 
 def retopk_stream_read(buf, sink, stream=None):

@@ -382,6 +382,48 @@ retopk_status retopk_dense_attn(retopk_handle* h, const uint16_t* q, const uint1
   return h->run(kKDenseMerge, s, [&] { return launch_dense(h->d, q, k, v, out, length, h->dense_part, s, 1); });
 }
 
+retopk_status retopk_dense_attn_noalloc(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t max_len,
+                                        const uint16_t* q, const uint16_t* k, const uint16_t* v, int32_t length,
+                                        float* out, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(RETOPK_INVALID_ARG, "retopk_dense_attn_noalloc: NULL tensor");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 4))
+    return fail(RETOPK_INVALID_ARG, "retopk_dense_attn_noalloc: misaligned tensor");
+  if (batch < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads != 0)
+    return fail(RETOPK_INVALID_ARG, "retopk_dense_attn_noalloc: batch and head counts must be >= 1, "
+                                    "n_q_heads a multiple of n_kv_heads");
+  if (n_q_heads / n_kv_heads > kDenseMaxGroup)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_dense_attn_noalloc: at most 8 query heads per KV head");
+  if (max_len < 1 || max_len > (1 << 24) || length < 1 || length > max_len)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_dense_attn_noalloc: need 1 <= length <= max_len <= 2^24");
+  if (static_cast<long long>(batch) * n_kv_heads > 1024)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_dense_attn_noalloc: batch * n_kv_heads must be <= 1024");
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1) {
+    (void)hipGetLastError();
+    return fail(RETOPK_NO_DEVICE, "retopk_dense_attn_noalloc: no usable device");
+  }
+  Dims d{};
+  d.B = batch;
+  d.Hq = n_q_heads;
+  d.Hkv = n_kv_heads;
+  d.G = n_q_heads / n_kv_heads;
+  d.max_len = max_len;
+  d.n_cu = n_cu;
+  const size_t need = static_cast<size_t>(batch) * n_q_heads * dense_max_split(d) * kDensePart;
+  if (need > kNoAllocScratchFloats)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_dense_attn_noalloc: needs " + std::to_string(need * 4) +
+                                         " bytes of scratch, more than its 4 MiB");
+  float* part = nullptr;
+  hipError_t e = dense_scratch(&part);
+  if (e != hipSuccess) return hip_fail(e, "retopk_dense_attn_noalloc: scratch address");
+  auto s = static_cast<hipStream_t>(stream);
+  e = launch_dense(d, q, k, v, out, length, part, s, 0);
+  if (e == hipSuccess) e = launch_dense(d, q, k, v, out, length, part, s, 1);
+  return e == hipSuccess ? RETOPK_OK : hip_fail(e, "retopk_dense_attn_noalloc");
+}
+
 retopk_status retopk_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (buf == nullptr || sink == nullptr) return fail(RETOPK_INVALID_ARG, "retopk_stream_read: NULL pointer");
   if (!aligned(buf, 16) || bytes % 16 != 0 || !aligned(sink, 4))

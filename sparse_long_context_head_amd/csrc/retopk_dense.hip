@@ -25,6 +25,15 @@
 
 #include "retopk_internal.h"
 
+#include <mutex>
+
+// Scratch of the entry point that allocates nothing (retopk_dense_attn_noalloc):
+// the row slices' partial results, reserved in device memory on every GPU the
+// library runs on, from load time until the process ends. Host code never
+// passes this name to a kernel (on the host it does not denote the device
+// address); it takes the address hipGetSymbolAddress returns per device.
+static __device__ __align__(256) float scratch[retopk::kNoAllocScratchFloats];
+
 namespace retopk {
 namespace {
 
@@ -289,6 +298,24 @@ void dense_split(const Dims& d, int length, int* n_split, int* rows) {
   const int r = ((length + ns - 1) / ns + 15) / 16 * 16;
   *rows = r;
   *n_split = (length + r - 1) / r;
+}
+
+hipError_t dense_scratch(float** ptr) {
+  static std::mutex mu;
+  static float* per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // this device's copy of the array
+    if (e != hipSuccess) return e;
+    per_device[dev] = static_cast<float*>(p);
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_dense(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v, float* out,

@@ -114,6 +114,12 @@ hipError_t launch_step(const Dims& d, const Bufs& b, const uint16_t* q, long q_s
 // call at this length, and the most any length gives (the partials workspace
 // holds B * Hq * dense_max_split(d) * kDensePart floats).
 int dense_max_split(const Dims& d);
+// The static scratch of the no-allocation dense entry point: 4 MiB of floats
+// (the partials of B * Hq * dense_max_split(d) slices must fit), and this
+// device's address of it (looked up once per device with that device current).
+constexpr size_t kNoAllocScratchFloats = (static_cast<size_t>(4) << 20) / 4;
+constexpr int kMaxDevices = 64;
+hipError_t dense_scratch(float** ptr);
 void dense_split(const Dims& d, int length, int* n_split, int* rows);
 // phase 0: the slices' partial results (k_dense); phase 1: their merge into
 // out (k_dense_merge). Both on stream s, one launch each.
