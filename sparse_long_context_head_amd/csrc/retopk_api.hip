@@ -235,7 +235,6 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   A(&b.cache_supp, BH * d.C * d.K);
   A(&b.cache_len, BH * d.C);
   A(&b.fifo, BH * 2);
-  A(&b.qbar, BH * D);
   A(&b.path, BH);
   A(&b.rho, BH);
   A(&b.ret, BH * d.R);

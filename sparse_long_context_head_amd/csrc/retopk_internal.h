@@ -45,7 +45,6 @@ struct Bufs {
   int32_t* cache_len;      // [BH, C]
   int32_t* fifo;           // [BH, 2]: next slot to write, entries held
   // per-step workspaces
-  float* qbar;             // [BH, D]   normalised current query
   int32_t* path;           // [BH]      1 exact, 0 reuse
   double* rho;             // [BH]      rho_max
   int32_t* ret;            // [BH, R]   retrieved FIFO positions, -1 pad

@@ -54,7 +54,6 @@ struct BufsDev {
   gptr<int32_t> cache_supp;
   gptr<int32_t> cache_len;
   gptr<int32_t> fifo;
-  gptr<float> qbar;
   gptr<int32_t> path;
   gptr<double> rho;
   gptr<int32_t> ret;
@@ -79,6 +78,16 @@ struct BufsDev {
   Bufs* self;
 };
 static_assert(sizeof(BufsDev) == sizeof(Bufs), "device view of the buffer table");
+
+// The table as the head role reads it: in the constant address space, since
+// it does not change while a kernel runs, so that its fields are read with
+// scalar loads through the scalar cache (one round trip for the whole table,
+// see prefetch_table) rather than vector loads that the compiler serialises.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __attribute__((address_space(4))) const BufsDev ConstBufs;
+#else
+typedef const BufsDev ConstBufs;
+#endif
 
 
 constexpr float kNegInf = -INFINITY;
@@ -707,11 +716,28 @@ __device__ __forceinline__ void attend(const int32_t* sel, float* sc, int n, flo
   attend_reduce(acc, z, out, out_z, sh);
 }
 
+// q_bar = x / ||x|| (Eqs. 5-6) of one bf16 query row, by one wave: w2 holds
+// elements 2l and 2l+1 in lane l, which gets their normalised values. Sum of
+// squares, square root and division in fp64, one rounding to fp32; the zero
+// query gives 0. The head and the score work groups both call it, so both
+// get the same bits without a hand-off.
+__device__ __forceinline__ void normalize_row(uint32_t w2, float& qb0, float& qb1) {
+  const double x0 = bf16_lo(w2), x1 = bf16_hi(w2);
+  const double nrm = sqrt(wave_sum_f64(x0 * x0 + x1 * x1));
+  qb0 = 0.f;
+  qb1 = 0.f;
+  if (nrm > 0.0) {
+    qb0 = static_cast<float>(x0 / nrm);
+    qb1 = static_cast<float>(x1 / nrm);
+  }
+}
+
 // Push (q_bar_t, S_hat_t) into the head's FIFO (Query-support cache
 // paragraph: after either path; the oldest entry is overwritten when full).
 // slot / count: the FIFO state read at the start of the kernel (the caller's
 // threads must not re-read it here, since thread 0 updates it).
-__device__ __forceinline__ void cache_push(const Dims& d, const BufsDev& b, int bh, int slot, int count, const float* qbar,
+template <typename Table>
+__device__ __forceinline__ void cache_push(const Dims& d, Table& b, int bh, int slot, int count, const float* qbar,
                                            const int32_t* sel, int n) {
   const long e = static_cast<long>(bh) * d.C + slot;
   for (int t = threadIdx.x; t < kHeadDim; t += blockDim.x) b.cache_qbar[e * kHeadDim + t] = qbar[t];
@@ -947,7 +973,33 @@ __device__ __forceinline__ void cand_scores(const uint16_t* kb, const int32_t* s
 }
 constexpr int kDenseWords = kHeadThreads / 4;  // bitmap words emitted a byte per thread (4096 positions)
 
-__device__ __forceinline__ void head_role(const Dims& d, const BufsDev& b, const uint16_t* q, long q_sb, long q_sh,
+// Bring all four 64-byte lines of the buffer table into the scalar cache at
+// once. The head role reads its pointers from the table where it needs them,
+// and the first read of each line after a launch would otherwise wait a
+// memory round trip of its own in the middle of a phase. (The loads complete
+// inside the block, so their unused results are safe.)
+__device__ __forceinline__ void prefetch_table(const void* t) {
+  uint32_t a, b2, c, e;
+  asm volatile(
+      "s_load_dword %0, %4, 0x0\n\ts_load_dword %1, %4, 0x40\n\ts_load_dword %2, %4, 0x80\n\t"
+      "s_load_dword %3, %4, 0xc0\n\ts_waitcnt lgkmcnt(0)"
+      : "=s"(a), "=s"(b2), "=s"(c), "=s"(e)
+      : "s"(t)
+      : "memory");
+}
+static_assert(sizeof(Bufs) > 0xc0 && sizeof(Bufs) <= 0x100, "the buffer table spans four 64-byte lines");
+
+// A uniform int read with a scalar load (constant address space): only for
+// words no work group of the running launch writes before the read.
+__device__ __forceinline__ int scalar_read(gptr<int32_t> p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return *(__attribute__((address_space(4))) const int32_t*)(reinterpret_cast<uintptr_t>(p));
+#else
+  return *p;
+#endif
+}
+
+__device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uint16_t* q, long q_sb, long q_sh,
                                           const uint16_t* k, const uint16_t* v, float* out, int length, int t_dec,
                                           int mode, int stats_slot, int call_flag, int bh, HeadShared& sh) {
   const int bb = bh / d.Hq, h = bh % d.Hq, g = h / d.G;
@@ -962,36 +1014,34 @@ __device__ __forceinline__ void head_role(const Dims& d, const BufsDev& b, const
   float* s_sc = reinterpret_cast<float*>(dyn + region0 + 4 * static_cast<size_t>(d.cand_cap));
 
   // ---- one round of loads: query, FIFO state, every ring slot's q_bar and support size ----
-  const int fifo_head = b.fifo[2 * bh];
-  const int count = b.fifo[2 * bh + 1];
+  // (all requested before any of them is used, so that they cost one round trip)
   const int part = tid & 15;
+  const uint32_t qw2 = wave == 0 ? *reinterpret_cast<const uint32_t*>(q + bb * q_sb + h * q_sh + 2 * lane) : 0u;
+  prefetch_table(&b);
+  // The FIFO state through the scalar cache: written only by earlier launches
+  // (this launch's push comes after this read), so the scalar load is safe.
+  const int fifo_head = scalar_read(b.fifo + 2 * bh);
+  const int count = scalar_read(b.fifo + 2 * bh + 1);
+  // (also in the exact mode, which does not use them: a branch here made the
+  // compiler consume the loads inside it, before the rest were requested)
   float4 ent[2][2];
-  if (mode == kModeDecode) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = min(i * (kHeadThreads / 16) + (tid >> 4), d.C - 1);
-      const float* e = b.cache_qbar + (static_cast<long>(bh) * d.C + c) * kHeadDim + 8 * part;
-      ent[i][0] = *reinterpret_cast<const float4*>(e);
-      ent[i][1] = *reinterpret_cast<const float4*>(e + 4);
-    }
-    const int len_c = b.cache_len[static_cast<long>(bh) * d.C + min(tid, d.C - 1)];
-    if (tid < d.C) sh.len[tid] = len_c;
+  for (int i = 0; i < 2; ++i) {
+    const int c = min(i * (kHeadThreads / 16) + (tid >> 4), d.C - 1);
+    const float* e = b.cache_qbar + (static_cast<long>(bh) * d.C + c) * kHeadDim + 8 * part;
+    ent[i][0] = *reinterpret_cast<const float4*>(e);
+    ent[i][1] = *reinterpret_cast<const float4*>(e + 4);
   }
+  const int len_c = b.cache_len[static_cast<long>(bh) * d.C + min(tid, d.C - 1)];
 
   if (wave == 0) {
-    const uint32_t w2 = *reinterpret_cast<const uint32_t*>(q + bb * q_sb + h * q_sh + 2 * lane);
-    const double x0 = bf16_lo(w2), x1 = bf16_hi(w2);
-    const double nrm = sqrt(wave_sum_f64(x0 * x0 + x1 * x1));
-    float qb0 = 0.f, qb1 = 0.f;
-    if (nrm > 0.0) {
-      qb0 = static_cast<float>(x0 / nrm);
-      qb1 = static_cast<float>(x1 / nrm);
-    }
+    float qb0, qb1;
+    normalize_row(qw2, qb0, qb1);
     sh.qbar[2 * lane] = qb0;
     sh.qbar[2 * lane + 1] = qb1;
-    store_shared2(b.qbar + static_cast<long>(bh) * kHeadDim + 2 * lane, qb0, qb1);  // read by the tail role
   }
   if (mode == kModeDecode) bitmap_clear(bm);  // first bitmap window, while the loads are in flight
+  if (mode == kModeDecode && tid < d.C) sh.len[tid] = len_c;
   lds_barrier();
 
   bool exact = true, refresh = false;
@@ -1025,7 +1075,6 @@ __device__ __forceinline__ void head_role(const Dims& d, const BufsDev& b, const
     // the path rule needs only rho_max: publish the decision before ranking
     if (wave == 0) {
       const double mxr = wave_max_f64(lane < count ? sh.rho[lane] : -INFINITY);
-      wait_vmem();  // this wave's q_bar stores are complete before the flag that publishes them
       if (lane == 0) store_shared(b.dec + bh, call_flag | ((refresh || count == 0 || mxr < d.tau) ? 1 : 0));
     }
     // Rank of FIFO position p under (rho desc, position asc), counted in
@@ -1075,10 +1124,7 @@ __device__ __forceinline__ void head_role(const Dims& d, const BufsDev& b, const
   }
   // publish the decision to the score work groups (decode mode did so above;
   // the histogram half of this call was cleared during the previous one)
-  if (mode != kModeDecode && wave == 0) {
-    wait_vmem();  // wave 0's q_bar stores are complete before the flag
-    if (tid == 0) store_shared(b.dec + bh, call_flag | (exact ? 1 : 0));
-  }
+  if (tid == 0 && mode != kModeDecode) store_shared(b.dec + bh, call_flag | (exact ? 1 : 0));
   if (exact) {
     if (tid == 0) b.m[bh] = 0;
     return;
@@ -1199,10 +1245,10 @@ __device__ __forceinline__ uint64_t comp_key(float s, uint32_t idx) {
 // are in LDS. Writes them out, aggregates the values (Eq. 12) and pushes
 // (q_bar_t, S_t) when `push`. Every thread of the block must call it.
 // ---------------------------------------------------------------------------
-// qv: element threadIdx.x of q_bar_t (threads < 128), loaded early by the caller.
+// qb0 / qb1: elements 2 lane and 2 lane + 1 of q_bar_t in wave 0 (normalize_row).
 __device__ __forceinline__ void finish_tail(const Dims& d, const BufsDev& b, int bh, int n, const uint16_t* v, float* out,
                                             int32_t* sel_out, int push, int fifo_slot, int fifo_count, HeadShared& sh,
-                                            const int32_t* s_sel, float* s_selsc, float qv) {
+                                            const int32_t* s_sel, float* s_selsc, float qb0, float qb1) {
   const int tid = threadIdx.x;
   const int bb = bh / d.Hq, g = (bh % d.Hq) / d.G;
   float mx = kNegInf;
@@ -1220,7 +1266,10 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const BufsDev& b, int
     attend(s_sel, s_selsc, n, mx, vb, out + static_cast<long>(bh) * kHeadDim, nullptr, sh);
   }
   if (push) {
-    if (tid < kHeadDim) sh.qbar[tid] = qv;
+    if (tid < 64) {
+      sh.qbar[2 * tid] = qb0;
+      sh.qbar[2 * tid + 1] = qb1;
+    }
     lds_barrier();
     cache_push(d, b, bh, fifo_slot, fifo_count, sh.qbar, s_sel, n);
   }
@@ -1432,13 +1481,18 @@ constexpr int kSU = 8;  // survivors per thread per round
 
 // Every thread of the block must call it.
 // bd: (b1, count above b1, count in b1).
-__device__ __forceinline__ void finish_phase(const Dims& d, const BufsDev& b, int bh, const uint16_t* v, float* out,
+__device__ __forceinline__ void finish_phase(const Dims& d, const BufsDev& b, int bh, const uint16_t* q, long q_sb,
+                                             long q_sh, const uint16_t* v, float* out,
                                              int32_t* sel_out, int length, int push, long T, int nW, int ne, int e,
                                              int3 bd, HeadShared& sh, unsigned char* dyn) {
   const int tid = threadIdx.x;
   // one round of loads: this thread's segment count, the FIFO state and (for
   // the push) q_bar_t
-  const float qv = push && tid < kHeadDim ? load_shared(b.qbar + static_cast<long>(bh) * kHeadDim + tid) : 0.f;
+  // q_bar_t for the push, normalised here from the query (the same bits as the
+  // head work group's, with normalize_row; the word is loaded in this round)
+  const uint32_t qw2 = push && tid < 64 ? *reinterpret_cast<const uint32_t*>(q + (bh / d.Hq) * q_sb +
+                                                                               (bh % d.Hq) * q_sh + 2 * tid)
+                                        : 0u;
   int slo = 0, shi = 0;
   if (tid < nW) seg_rows(T, nW, length, ne, tid, e, slo, shi);
   const int cc = (tid < nW && slo < shi) ? load_shared(b.ccnt + static_cast<long>(bh) * d.n_cu + tid) : 0;
@@ -1468,6 +1522,8 @@ __device__ __forceinline__ void finish_phase(const Dims& d, const BufsDev& b, in
     lds_barrier();
   }
   const int ns = aoff[nW];
+  float qb0 = 0.f, qb1 = 0.f;
+  if (push && tid < 64) normalize_row(qw2, qb0, qb1);
 
   // ---- 2. classification, candidate keys, radix select ----
   const int nrounds = (ns + kHeadThreads * kSU - 1) / (kHeadThreads * kSU);
@@ -1589,7 +1645,7 @@ __device__ __forceinline__ void finish_phase(const Dims& d, const BufsDev& b, in
   }
   n = min(n, keff);
   lds_barrier();
-  finish_tail(d, b, bh, n, v, out, sel_out, push, fifo_slot, fifo_count, sh, s_sel, s_selsc, qv);
+  finish_tail(d, b, bh, n, v, out, sel_out, push, fifo_slot, fifo_count, sh, s_sel, s_selsc, qb0, qb1);
 }
 
 // w: this score work group's index among the nW of them. all_exact: every
@@ -1782,7 +1838,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
       if (!wait_group(b.wdone + d.n_cu, T, nW, length, ne, e, call_flag, b.err, &sh.i3)) return;
       const int3 bd = make_int3(sh.i0, sh.i1, sh.i2);
       lds_barrier();  // (the finish reuses sh.i0 ..)
-      finish_phase(d, b, bh, v, out, sel_out, length, push, T, nW, ne, e, bd, sh, dyn);
+      finish_phase(d, b, bh, q, q_sb, q_sh, v, out, sel_out, length, push, T, nW, ne, e, bd, sh, dyn);
       lds_barrier();  // the next finish reuses the LDS
     }
   }
@@ -1804,7 +1860,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, const Bufs* __res
   const int BH = d.B * d.Hq;
   const int w = static_cast<int>(blockIdx.x);
   if (w < BH) {
-    head_role(d, *reinterpret_cast<const BufsDev*>(bp), q, q_sb, q_sh, k, v, out, length, t_dec, mode, stats_slot,
+    head_role(d, *(ConstBufs*)(reinterpret_cast<uintptr_t>(bp)), q, q_sb, q_sh, k, v, out, length, t_dec, mode, stats_slot,
               call_flag, w, sh);
   } else {
     const BufsDev b = *reinterpret_cast<const BufsDev*>(bp);
