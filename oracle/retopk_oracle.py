@@ -16,6 +16,7 @@ written from its Methodology section, in the paper's order and notation:
   query-support FIFO cache B_t ... Recall-Before-Rerank Selection, Eq. (5)
   cosine recall rho_{t,c} ........ Eq. (6)
   TopR retrieval and rho_max ..... Eq. (7)
+  recent-R retrieval (ablation) .. Experiments, component ablation, Table 3
   recent window L_t .............. Eq. (8)
   candidate set A_t, M_t ......... Eq. (9)
   candidate scores e_hat ......... Eq. (10)
@@ -44,6 +45,9 @@ Readings taken where the paper is silent:
   * query head h reads KV head floor(h * Hkv / Hq) (contiguous GQA groups),
     and every query head keeps its own cache;
   * refresh applies to all heads at once; the similarity fallback is per head;
+  * recent-R retrieval (ablation): the R newest entries, newest first, and
+    rho_max over them only (under which the exact-path rate rises, as the
+    ablation reports);
   * supports are stored in ascending token order;
   * a stored support entry that is not a visible key at step t (>= L_t; only a
     restored snapshot can hold one) is not a candidate; a reuse head with no
@@ -111,6 +115,20 @@ def top_r(rho: list[float], r: int):
     order = sorted(range(len(rho)), key=lambda c: (-rho[c], c))
     rho_max = max(rho) if rho else -math.inf
     return order[: min(r, len(rho))], rho_max
+
+
+def recent_r(rho: list[float], r: int):
+    """The recent-R retrieval of the component ablation (Experiments,
+    "Hyperparameter sensitivity and component ablation", Table 3), in place of
+    Eq. (7): R_t = the min(R, |B_t|) newest entries, newest first, whatever
+    their similarity. rho_max is taken over those entries only, the reading
+    under which this ablation changes the exact-path rate, as the paper
+    reports (11.6% -> 16.7%); with none, -inf.
+    """
+    n = len(rho)
+    chosen = [n - 1 - i for i in range(min(r, n))]
+    rho_max = max(rho[c] for c in chosen) if chosen else -math.inf
+    return chosen, rho_max
 
 
 def recent_window(length: int, window: int) -> np.ndarray:
@@ -243,12 +261,15 @@ class ReTopKOracle:
     """
 
     def __init__(self, batch, n_q_heads, n_kv_heads, head_dim, top_k, cache_cap,
-                 window, top_r, refresh_every, tau):
+                 window, top_r, refresh_every, tau, retrieval="similarity"):
         if n_q_heads % n_kv_heads:
             raise ValueError("query heads must be a multiple of KV heads")
         self.batch, self.hq, self.hkv, self.d = batch, n_q_heads, n_kv_heads, head_dim
         self.k, self.c, self.w, self.r = top_k, cache_cap, window, top_r
         self.refresh_every, self.tau = refresh_every, float(tau)
+        if retrieval not in ("similarity", "recent"):
+            raise ValueError("retrieval is 'similarity' (Eq. (7)) or 'recent' (ablation)")
+        self.retrieval = retrieval
         self.cache = [[[] for _ in range(n_q_heads)] for _ in range(batch)]
 
     @classmethod
@@ -304,7 +325,10 @@ class ReTopKOracle:
                 entries = self.cache[b][h]
                 qbar = normalize_query(q_bits[b, h])
                 rho = cosine_recall(qbar, [e[0] for e in entries])
-                retrieved, rho_max = top_r(rho, self.r)
+                if self.retrieval == "similarity":
+                    retrieved, rho_max = top_r(rho, self.r)
+                else:
+                    retrieved, rho_max = recent_r(rho, self.r)
                 exact = refresh or rho_max < self.tau
                 if exact:
                     sel, sel_s = exact_topk_support(q_bits[b, h], k_bits[b, g], length, self.k)

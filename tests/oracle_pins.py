@@ -506,8 +506,76 @@ def pin_state_snapshot(o):
     assert np.array_equal(after[0][0, 1, 3], qb1.astype(np.float32))
 
 
+def pin_recent_r(o):
+    """Recent-R retrieval (component ablation, Table 3): the R newest entries,
+    newest first, and rho_max over them only. Hand-worked: four cached unit
+    vectors, the oldest identical to the query; similarity-guided retrieval
+    takes it (rho_max = 1, reuse at tau = 0.9), recent-R with R = 2 takes the
+    two newest (rho_max = 0.6, exact path). Then brute force over a tiny
+    forced-reuse run: the candidate set is the window plus the supports of the
+    R newest entries."""
+    d = 4
+    e = np.eye(d, dtype=np.float32)
+    other = np.array([0.6, 0.8, 0, 0], np.float32)      # cosine 0.6 with e0
+    entries = [e[0], e[2], other, e[1]]                  # oldest first
+    supports = [[1, 2], [3], [4, 5], [6]]
+    qbar = np.zeros((1, 1, 4, d), np.float32)
+    supp = np.zeros((1, 1, 4, 2), np.int32)
+    slen = np.zeros((1, 1, 4), np.int32)
+    for i, (q_, s_) in enumerate(zip(entries, supports)):
+        qbar[0, 0, i] = q_
+        supp[0, 0, i, :len(s_)] = s_
+        slen[0, 0, i] = len(s_)
+    kf = np.zeros((1, 1, 10, d), np.float32)
+    vf = np.zeros((1, 1, 10, d), np.float32)
+    for i in range(10):
+        kf[0, 0, i, i % d] = 1.0 + i
+        vf[0, 0, i] = [i, 1.0, -i, 2.0]
+    q = bits(np.array([[[5.0, 0, 0, 0]]], np.float32))
+    for retrieval, want_ret, want_rho, want_path in (("similarity", [0, 2], 1.0, o.REUSE),
+                                                     ("recent", [3, 2], 0.6, o.EXACT)):
+        orc = o.ReTopKOracle(batch=1, n_q_heads=1, n_kv_heads=1, head_dim=d, top_k=2, cache_cap=4,
+                             window=1, top_r=2, refresh_every=0, tau=0.9, retrieval=retrieval)
+        orc.set_state(qbar, supp, slen, np.array([[4]], np.int32))
+        rec = orc.step(q, bits(kf), bits(vf), 10, 1)
+        assert list(rec.retrieved[0][0]) == want_ret, (retrieval, rec.retrieved)
+        assert abs(rec.rho_max[0, 0] - want_rho) < 1e-7, (retrieval, rec.rho_max)
+        assert rec.path[0, 0] == want_path, retrieval
+    # forced reuse (tau = -2): A_t = window U supports of the two newest entries
+    orc = o.ReTopKOracle(batch=1, n_q_heads=1, n_kv_heads=1, head_dim=d, top_k=2, cache_cap=4,
+                         window=1, top_r=2, refresh_every=0, tau=-2.0, retrieval="recent")
+    orc.set_state(qbar, supp, slen, np.array([[4]], np.int32))
+    rec = orc.step(q, bits(kf), bits(vf), 10, 1)
+    assert list(rec.candidates[0][0]) == [4, 5, 6, 9]
+    # scores: key i has i + 1 at coordinate i mod 4; q = 5 e0 -> only keys 4 (25.0) count
+    assert list(rec.support[0][0]) == [4, 5]   # 25 > 0 = 0 = 0, the tie to the lower index
+    # empty cache: nothing retrieved, rho_max = -inf, exact
+    orc = o.ReTopKOracle(batch=1, n_q_heads=1, n_kv_heads=1, head_dim=d, top_k=2, cache_cap=4,
+                         window=1, top_r=2, refresh_every=0, tau=-2.0, retrieval="recent")
+    rec = orc.step(q, bits(kf), bits(vf), 10, 1)
+    assert rec.retrieved[0][0] == [] and rec.rho_max[0, 0] == -math.inf and rec.path[0, 0] == o.EXACT
+    # brute force on a tiny run: the retrieved entries are the newest, and
+    # fewer than R entries are all taken
+    orc, p, k, v, q2, l0 = _run(o, 15, tau=-2.0, retrieval="recent", cache_cap=3, top_r=2)
+    for t in range(1, 6):
+        before = [[(x[0].copy(), list(x[1])) for x in orc.cache[0][h]] for h in range(p["n_q_heads"])]
+        rec = orc.step(q2[40 + t - 1], k, v, l0 + t, t)
+        for h in range(p["n_q_heads"]):
+            n = len(before[h])
+            assert list(rec.retrieved[0][h]) == [n - 1 - i for i in range(min(2, n))]
+            qf = as_float(q2[40 + t - 1, 0, h])
+            nq = math.sqrt(math.fsum(x * x for x in qf))
+            qb = [float(np.float32(x / nq)) for x in qf]
+            rho = [brute_dot(qb, before[h][c][0]) for c in rec.retrieved[0][h]]
+            assert abs(rec.rho_max[0, h] - max(rho)) < 1e-12
+            pool = set(range(max(0, l0 + t - p["window"]), l0 + t))
+            for c in rec.retrieved[0][h]:
+                pool |= set(before[h][c][1])
+            assert list(rec.candidates[0][h]) == sorted(pool)
+
+
 ALL_PINS = [pin_bf16_decode, pin_normalize, pin_top_k, pin_top_r, pin_window_and_union,
             pin_dense_special_case, pin_softmax_properties, pin_split_merge, pin_micro_example,
             pin_forced_exact, pin_forced_reuse_and_candidates, pin_refresh_schedule,
             pin_fallback_threshold, pin_window_covers_history, pin_fifo, pin_init,
-            pin_gqa_mapping, pin_dense_attention, pin_state_snapshot]
+            pin_gqa_mapping, pin_dense_attention, pin_state_snapshot, pin_recent_r]

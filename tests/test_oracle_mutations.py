@@ -57,6 +57,11 @@ MUTATIONS = [
     ("candidates_keep_invisible_keys", "for i in supports[c] if int(i) < length)", "for i in supports[c])"),
     ("empty_support_not_zero", "if len(scores) == 0:\n        return np.zeros(head_dim)",
      "if len(scores) == 0:\n        return np.full(head_dim, np.nan)"),
+    ("recent_r_oldest_first", "chosen = [n - 1 - i for i in range(min(r, n))]",
+     "chosen = [i for i in range(min(r, n))]"),
+    ("recent_r_rho_over_all", "rho_max = max(rho[c] for c in chosen) if chosen else -math.inf",
+     "rho_max = max(rho) if chosen else -math.inf"),
+    ("recent_r_ignored", "if self.retrieval == \"similarity\":", "if True:"),
     ("recall_uses_raw_query", "rho = cosine_recall(qbar, [e[0] for e in entries])",
      "rho = cosine_recall(bf16_to_f64(q_bits[b, h]), [e[0] for e in entries])"),
 ]
