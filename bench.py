@@ -60,9 +60,11 @@ def parse():
                       ("refresh-every", int)):
         ap.add_argument(f"--{flag}", type=typ, default=None,
                         help=f"override the workload's {flag.replace('-', '_')} (sensitivity runs)")
+    ap.add_argument("--retrieval", choices=("similarity", "recent"), default=None,
+                    help="retrieval of the natural leg: similarity-guided (the method) or recent-R (ablation)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=list(LEGS) + ["fidelity", "stream"], default=None,
+    ap.add_argument("--only", choices=list(LEGS) + ["fidelity", "stream", "ablation"], default=None,
                     help="run one timed leg only (for profiler runs)")
     ap.add_argument("--fidelity-steps", type=int, default=32,
                     help="decode steps of the support-fidelity leg (0 skips it)")
@@ -414,6 +416,7 @@ def main():
             if getattr(args, k) is not None}
     if over:
         wl = wl.replace(**over)
+    retrieval = args.retrieval or "similarity"
     kv_bytes = 2 * wl.batch * wl.n_kv_heads * wl.max_len * ROW_BYTES
     nl = args.layers or max(1, math.ceil((1 << 30) / kv_bytes))
     n_pos = math.ceil((args.warmup + args.steps) / nl)
@@ -442,6 +445,7 @@ def main():
         """Handles with initialised caches, each advanced through its offset's
         decode steps (untimed setup: the cache state a layer has at that point
         of the decode)."""
+        override = {"retrieval": retrieval, **override}
         layers = [B.ReTopKLayer.from_workload(wl, **override) for _ in range(nl)]
         for l in range(nl):
             if init:
@@ -528,7 +532,7 @@ def main():
               "config": {"workload": wl.name, "batch": wl.batch, "n_q_heads": wl.n_q_heads,
                          "n_kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
                          "prompt_len": L0, "top_k": wl.top_k, "cache_cap": wl.cache_cap,
-                         "window": wl.window, "top_r": wl.top_r, "tau": wl.tau,
+                         "window": wl.window, "top_r": wl.top_r, "tau": wl.tau, "retrieval": retrieval,
                          "refresh_every": wl.refresh_every, "rotated_layers": nl,
                          "decode_positions": n_pos, "layer_offsets": offsets,
                          "timed_positions": {str(l_): [min(ps), max(ps)] for l_, ps in sorted(timed_pos.items())},
@@ -583,6 +587,21 @@ def main():
             r["traffic_other_window"] = other
         return r
 
+    def path_mix(path, m):
+        exact = (path & 1) == 1
+        refresh = (path & 2) == 2
+        gexact = exact.reshape(exact.shape[0], wl.batch, wl.n_kv_heads, G).any(-1)
+        mr = m[~exact]
+        return {
+            "head_steps": int(exact.size), "reuse": round(float((~exact).mean()), 5),
+            "exact_fallback": round(float((exact & ~refresh).mean()), 5),
+            "exact_refresh": round(float(refresh.mean()), 5),
+            "kv_group_steps_with_exact": round(float(gexact.mean()), 5),
+            "M_t": {"mean": round(float(mr.mean()), 1) if mr.size else None,
+                    "p50": int(np.percentile(mr, 50)) if mr.size else None,
+                    "p90": int(np.percentile(mr, 90)) if mr.size else None,
+                    "max": int(mr.max()) if mr.size else None}}
+
     # --- natural ReTopK step (the headline value) ---------------------------
     if args.only in (None, "natural"):
         nat = make_layers()
@@ -592,19 +611,7 @@ def main():
         result["ms_per_step"] = round(us / 1000.0, 6)
         log(f"natural ReTopK: {us:.2f} us/step/layer")
         path, m, lens = timed_paths(nat)
-        exact = (path & 1) == 1
-        refresh = (path & 2) == 2
-        gexact = exact.reshape(exact.shape[0], wl.batch, wl.n_kv_heads, G).any(-1)
-        mr = m[~exact]
-        result["path_mix"] = {
-            "head_steps": int(exact.size), "reuse": round(float((~exact).mean()), 5),
-            "exact_fallback": round(float((exact & ~refresh).mean()), 5),
-            "exact_refresh": round(float(refresh.mean()), 5),
-            "kv_group_steps_with_exact": round(float(gexact.mean()), 5),
-            "M_t": {"mean": round(float(mr.mean()), 1) if mr.size else None,
-                    "p50": int(np.percentile(mr, 50)) if mr.size else None,
-                    "p90": int(np.percentile(mr, 90)) if mr.size else None,
-                    "max": int(mr.max()) if mr.size else None}}
+        result["path_mix"] = path_mix(path, m)
         # A decode step is one launch of k_step, so the timed region's per-step
         # time (HIP events on the launch stream) is its average launch duration;
         # the algorithmic bytes are averaged over the same timed steps.
@@ -710,6 +717,25 @@ def main():
             result["speedup_vs_dense"] = round(us_de / result["value"], 3)
         if "exact_topk_us_per_step" in result:
             result["dense_vs_exact"] = round(result["exact_topk_us_per_step"] / us_de, 3)
+
+    # --- retrieval ablation: similarity-guided against recent-R --------------
+    # (Experiments, component ablation, Table 3: the exact-path rate and the
+    # mean candidate count of each, here over the natural leg's timed window)
+    if args.only in (None, "ablation"):
+        abl = {}
+        for mode in ("similarity", "recent"):
+            lay = make_layers(retrieval=mode)
+            us_m = timed(lay)
+            pth, mm, _ = timed_paths(lay)
+            check_device_error(B, lay, f"ablation ({mode})")
+            for layer in lay:
+                layer.close()
+            pm = path_mix(pth, mm)
+            abl[mode] = {"us_per_step": round(us_m, 3), "exact_path_rate": round(1.0 - pm["reuse"], 5),
+                         "exact_fallback": pm["exact_fallback"], "M_t_mean": pm["M_t"]["mean"]}
+            log(f"retrieval {mode}: {us_m:.2f} us/step, exact-path rate {1.0 - pm['reuse']:.4f}, "
+                f"M_t mean {pm['M_t']['mean']}")
+        result["retrieval_ablation"] = abl
 
     # --- support fidelity against Exact Top-K (quality, not timed) ----------
     if args.only in (None, "fidelity") and args.fidelity_steps > 0:

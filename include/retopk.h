@@ -84,7 +84,15 @@ typedef struct retopk_params {
   int32_t refresh_every;  /* T_r >= 0; 0 disables scheduled refresh (Eq. 13)     */
   double  tau;            /* similarity threshold: rho_max < tau takes the exact
                              path (Eq. 13); compared against rho in float64      */
+  int32_t retrieval;      /* RETOPK_RETRIEVE_SIMILAR (0, the method): R_t = the R
+                             entries most similar to q_t (Eq. 7), rho_max over
+                             all entries; RETOPK_RETRIEVE_RECENT (1, the component
+                             ablation of the Experiments' Table 3): R_t = the R
+                             newest entries, newest first, and rho_max over them
+                             only                                                */
 } retopk_params;
+
+enum { RETOPK_RETRIEVE_SIMILAR = 0, RETOPK_RETRIEVE_RECENT = 1 };
 
 typedef struct retopk_handle retopk_handle;
 

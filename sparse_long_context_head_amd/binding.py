@@ -33,7 +33,10 @@ class RetopkParams(ctypes.Structure):
                 ("max_len", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("cache_cap", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("top_r", ctypes.c_int32), ("refresh_every", ctypes.c_int32),
-                ("tau", ctypes.c_double)]
+                ("tau", ctypes.c_double), ("retrieval", ctypes.c_int32)]
+
+
+RETRIEVAL = {"similarity": 0, "recent": 1}
 
 
 # Exported symbols and their C signatures (restype, argtypes).
@@ -139,12 +142,14 @@ _BF16 = ("bfloat16", "int16", "uint16")
 
 
 def retopk_create(batch, n_q_heads, n_kv_heads, head_dim, max_len, top_k, cache_cap, window,
-                  top_r, refresh_every, tau) -> Handle:
+                  top_r, refresh_every, tau, retrieval="similarity") -> Handle:
+    """retrieval: "similarity" (Eq. 7) or "recent" (the ablation's recent-R)."""
     lib = load_library()
     params = dict(batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, head_dim=head_dim,
                   max_len=max_len, top_k=top_k, cache_cap=cache_cap, window=window,
                   top_r=top_r, refresh_every=refresh_every, tau=float(tau))
-    p = RetopkParams(**params)
+    p = RetopkParams(**params, retrieval=RETRIEVAL[retrieval])
+    params["retrieval"] = retrieval
     out = _P()
     _check(lib.retopk_create(ctypes.byref(p), ctypes.byref(out)))
     return Handle(out.value, params)

@@ -174,6 +174,8 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
     return fail(RETOPK_OUT_OF_RANGE, "retopk_create: top_r must be in 1 .. cache_cap");
   if (p.refresh_every < 0) return fail(RETOPK_OUT_OF_RANGE, "retopk_create: refresh_every must be >= 0");
   if (std::isnan(p.tau)) return fail(RETOPK_INVALID_ARG, "retopk_create: tau is NaN");
+  if (p.retrieval != RETOPK_RETRIEVE_SIMILAR && p.retrieval != RETOPK_RETRIEVE_RECENT)
+    return fail(RETOPK_INVALID_ARG, "retopk_create: retrieval must be RETOPK_RETRIEVE_SIMILAR or _RECENT");
   const long long cand = static_cast<long long>(p.top_r) * p.top_k + p.window;
   if (cand > kMaxCand)
     return fail(RETOPK_OUT_OF_RANGE, "retopk_create: top_r * top_k + window must be <= 16384");
@@ -222,6 +224,7 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   d.Tr = p.refresh_every;
   d.cand_cap = static_cast<int>(cand);
   d.n_cu = n_cu;
+  d.recent = p.retrieval == RETOPK_RETRIEVE_RECENT ? 1 : 0;
   d.tau = p.tau;
 
   Bufs& b = h->b;

@@ -34,6 +34,7 @@ struct Dims {
   int K, C, W, R, Tr;
   int cand_cap;            // R*K + W
   int n_cu;                // compute units of the device
+  int recent;              // 1: recent-R retrieval (the R newest entries, rho_max over them)
   double tau;
 };
 

@@ -1073,9 +1073,14 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
     }
     lds_barrier();
     // the path rule needs only rho_max: publish the decision before ranking
+    // (recent-R retrieval: rho_max over the R newest entries only)
     if (wave == 0) {
-      const double mxr = wave_max_f64(lane < count ? sh.rho[lane] : -INFINITY);
-      if (lane == 0) store_shared(b.dec + bh, call_flag | ((refresh || count == 0 || mxr < d.tau) ? 1 : 0));
+      const int lo = d.recent ? max(0, count - d.R) : 0;
+      const double mxr = wave_max_f64(lane < count && lane >= lo ? sh.rho[lane] : -INFINITY);
+      if (lane == 0) {
+        store_shared(b.dec + bh, call_flag | ((refresh || count == 0 || mxr < d.tau) ? 1 : 0));
+        if (d.recent) sh.d0 = mxr;
+      }
     }
     // Rank of FIFO position p under (rho desc, position asc), counted in
     // parallel: wave w compares every position with positions w, w+8, ...
@@ -1094,13 +1099,14 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
       int rank = 0;
 #pragma unroll
       for (int w = 0; w < kHeadThreads / 64; ++w) rank += s_rank[w][lane];
+      if (d.recent) rank = count - 1 - lane;  // the newest first
       if (lane < count && rank < d.R) {
         int slot = oldest + lane;
         if (slot >= d.C) slot -= d.C;
         b.ret[bh * d.R + rank] = lane;
         b.retslot[bh * d.R + rank] = slot;
         sh.rslot[rank] = slot;
-        if (rank == 0) sh.d0 = sh.rho[lane];
+        if (rank == 0 && !d.recent) sh.d0 = sh.rho[lane];
       }
     }
     n_ret = min(d.R, count);

@@ -68,6 +68,15 @@ def test_create_rejects_bad_params(change, status):
     assert e.value.status == status
 
 
+def test_create_rejects_unknown_retrieval():
+    import ctypes
+    binding, lib = _lib()
+    p = binding.RetopkParams(**{k: v for k, v in GOOD.items()}, retrieval=2)
+    out = ctypes.c_void_p()
+    assert lib.retopk_create(ctypes.byref(p), ctypes.byref(out)) == 1 and out.value is None
+    assert b"retrieval" in lib.retopk_last_error()
+
+
 def test_create_without_gpu_reports_no_device():
     import torch
     if torch.cuda.is_available():

@@ -428,6 +428,39 @@ def test_decode_empty_candidate_set():
     close_checked(layer)
 
 
+def test_decode_tiny_recent_r():
+    """Recent-R retrieval (the component ablation): the R newest entries and
+    rho_max over them, in lockstep with the oracle, a refresh every 8 steps."""
+    r = run_lockstep("tiny", 24, override=dict(retrieval="recent", refresh_every=8))
+    assert r["paths"][7].all()
+
+
+def periodic_query_data(seed, period=8, noise=0.3, steps=24):
+    """Queries cycling through `period` random directions (plus noise): the
+    entries most similar to q_t are `period` steps old, while the R < period
+    newest point elsewhere, so the two retrievals decide differently."""
+    wl = WORKLOADS["tiny"].replace(name="periodic", decode_steps=steps, prompt_len=3000)
+    data = dict(generate(wl))
+    rng = np.random.default_rng(seed)
+    base = rng.standard_normal((period, 128))
+    n0 = data["q_tail"].shape[2]
+    qs = np.stack([base[n % period] + noise * rng.standard_normal(128) for n in range(n0 + steps)])
+    q = f32_to_bf16_bits(qs.astype(np.float32))
+    data["q_tail"] = np.ascontiguousarray(q[:n0][None, None])
+    data["q_dec"] = np.ascontiguousarray(q[n0:][:, None, None])
+    return wl, data
+
+
+def test_decode_periodic_queries_both_retrievals():
+    """Similarity-guided retrieval finds the same-direction entries (rho_max
+    about 0.9: reuse); recent-R sees only the newest, unrelated ones (rho_max
+    near 0: the exact path). Both in lockstep with the oracle."""
+    wl, data = periodic_query_data(41)
+    sim = run_lockstep("periodic", wl.decode_steps, given=(wl, data))
+    rec = run_lockstep("periodic", wl.decode_steps, given=(wl, data), override=dict(retrieval="recent"))
+    assert sim["paths"].mean() < 0.2 and rec["paths"].mean() > 0.8, (sim["paths"].mean(), rec["paths"].mean())
+
+
 def test_decode_free_running_tiny():
     """Without re-synchronisation the GPU trajectory matches the oracle's until
     the first near-tie swap (if any)."""
