@@ -64,7 +64,9 @@ def parse():
                     help="retrieval of the natural leg: similarity-guided (the method) or recent-R (ablation)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=list(LEGS) + ["fidelity", "stream", "ablation"], default=None,
+    ap.add_argument("--token-layers", type=int, default=28,
+                    help="layers of the graph-replayed decode token leg (0 skips it)")
+    ap.add_argument("--only", choices=list(LEGS) + ["fidelity", "stream", "ablation", "token"], default=None,
                     help="run one timed leg only (for profiler runs)")
     ap.add_argument("--fidelity-steps", type=int, default=32,
                     help="decode steps of the support-fidelity leg (0 skips it)")
@@ -737,6 +739,12 @@ def main():
                 f"M_t mean {pm['M_t']['mean']}")
         result["retrieval_ablation"] = abl
 
+    # --- one decode token over many layers: eager calls against a graph replay
+    # (Experiments, Kernel efficiency analysis, Table 4: ms/token over the 28
+    # layers, workspaces reused across layers)
+    if args.only in (None, "token") and args.token_layers > 0:
+        result["token"] = token_leg(B, torch, wl, data, k0, v0, q_tail, q_dec, dev, args, L0)
+
     # --- support fidelity against Exact Top-K (quality, not timed) ----------
     if args.only in (None, "fidelity") and args.fidelity_steps > 0:
         result["fidelity"] = support_fidelity(wl, data, q_tail, q_dec, ks[0], vs[0], out, stream,
@@ -760,6 +768,79 @@ def main():
         with open(args.json_out, "w") as fh:
             fh.write(line + "\n")
     print(line, flush=True)
+
+
+def token_leg(B, torch, wl, data, k0, v0, q_tail, q_dec, dev, args, L0):
+    """Decode tokens over n layers that share one set of workspaces (a
+    retopk_group): each layer has its own KV buffers (copies of the
+    workload's) and caches. Eager: retopk_decode_step of every layer per token.
+    Graph: one retopk_group_replay per token (the captured position update
+    and all layers' steps), after copying the token's query into the captured
+    query buffer (timed with it). Both from the initialised caches, over the
+    same decode positions (warm-up tokens first); HIP events on the stream and
+    the host's enqueue time per token."""
+    n = args.token_layers
+    tokens = max(8, min(args.steps, 64))
+    warm = 2
+    if warm + tokens > wl.decode_steps:
+        tokens = wl.decode_steps - warm
+    stream = torch.cuda.Stream(device=dev)
+    ks = [k0] + [k0.clone() for _ in range(n - 1)]
+    vs = [v0] + [v0.clone() for _ in range(n - 1)]
+    shape = (wl.batch, wl.n_q_heads, wl.head_dim)
+    outs = [torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(n)]
+    qbuf = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    grp = B.ReTopKGroup.from_workload(wl, n)
+
+    def init():
+        with torch.cuda.stream(stream):
+            for l in range(n):
+                grp.layers[l].init_from_prefill(q_tail, ks[l], L0, stream)
+        stream.synchronize()
+
+    def timed(step_fn):
+        for t in range(1, warm + 1):
+            step_fn(t)
+        stream.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        h0 = time.perf_counter()
+        for t in range(warm + 1, warm + tokens + 1):
+            step_fn(t)
+        host = (time.perf_counter() - h0) / tokens * 1e6
+        b.record(stream)
+        stream.synchronize()
+        return a.elapsed_time(b) / tokens, host
+
+    def eager_token(t):
+        for l in range(n):
+            grp.layers[l].decode_step(q_dec[t - 1], ks[l], vs[l], L0 + t, t, outs[l], stream)
+
+    init()
+    ms_e, host_e = timed(eager_token)
+    check_device_error(B, grp.layers[:1], "token (eager)")
+    init()
+    grp.capture([qbuf] * n, ks, vs, outs, stream)
+    grp.set_position(L0 + 1, 1)
+
+    def graph_token(t):
+        with torch.cuda.stream(stream):
+            qbuf.copy_(q_dec[t - 1])
+        grp.replay(stream)
+
+    ms_g, host_g = timed(graph_token)
+    check_device_error(B, grp.layers[:1], "token (graph)")
+    ws_bytes = grp.device_bytes()
+    grp.close()
+    del ks, vs
+    log(f"token over {n} layers: eager {ms_e:.3f} ms, graph {ms_g:.3f} ms (host {host_e:.0f} / {host_g:.0f} us)")
+    return {"layers": n, "tokens": tokens, "warmup_tokens": warm,
+            "eager_ms_per_token": round(ms_e, 4), "graph_ms_per_token": round(ms_g, 4),
+            "eager_us_per_layer_step": round(ms_e * 1000 / n, 3),
+            "graph_us_per_layer_step": round(ms_g * 1000 / n, 3),
+            "eager_host_us_per_token": round(host_e, 1), "graph_host_us_per_token": round(host_g, 1),
+            "group_device_bytes": ws_bytes}
 
 
 def stream_read(B, torch, dev, stream):

@@ -164,6 +164,64 @@ retopk_status retopk_exact_topk_attn(retopk_handle* h, const uint16_t* q, const 
 retopk_status retopk_dense_attn(retopk_handle* h, const uint16_t* q, const uint16_t* k,
                                 const uint16_t* v, int32_t length, float* out, void* stream);
 
+/* ---- Several layers: shared workspaces and a graph-replayed decode token ----
+ *
+ * A decoder runs one decode step per attention layer for every token; the
+ * ReTopK paper measures its kernels over the 28 layers of a token and lists
+ * per-layer workspace reuse among its kernel stages (Experiments, Kernel
+ * efficiency analysis, Table 4). A group holds n_layers handles (one per
+ * layer: its own query-support caches and statistics ring) that share ONE set
+ * of per-call workspaces (scores, histograms, survivors, candidates, flags),
+ * so a layer's memory beyond its caches is not repeated n_layers times. The
+ * layers' calls must then be serialised on one stream (they share the
+ * workspaces); the per-call outputs that retopk_read_step_info returns are
+ * those of the group's most recent call, on whichever layer; the device error
+ * word is the group's. Every per-handle entry point works on a layer handle
+ * (retopk_group_layer); retopk_destroy ignores layer handles. */
+typedef struct retopk_group retopk_group;
+
+/* Create n_layers (1 .. 1024) layers with the parameters *params on the
+ * current device, caches empty. Synchronous. *out is NULL on failure. */
+retopk_status retopk_group_create(const retopk_params* params, int32_t n_layers, retopk_group** out);
+
+/* Free the group, its layers, workspaces and graph (synchronises the device).
+ * A NULL group is ignored. */
+void retopk_group_destroy(retopk_group* g);
+
+/* The handle of layer `layer` (0 .. n_layers-1), owned by the group; NULL when
+ * out of range. */
+retopk_handle* retopk_group_layer(retopk_group* g, int32_t layer);
+
+/* Bytes of device memory the group holds (all layers and the shared workspaces). */
+size_t retopk_group_device_bytes(const retopk_group* g);
+
+/* Capture one decode token as a HIP graph owned by the group: a one-thread
+ * kernel that moves the group's device position words on by one token
+ * (length + 1, t_dec + 1, call sequence + n_layers), then retopk_decode_step
+ * of every layer l in order on q[l], k[l], v[l] -> out[l] (arrays of n_layers
+ * device pointers, shapes as for retopk_decode_step), each reading its visible
+ * length, decode step and call flag from those words instead of from
+ * arguments, so that one graph serves every token. Launches are sized for
+ * length = max_len. The pointers are fixed in the graph: the caller writes each
+ * token's queries (and the new key and value rows) into the same buffers before
+ * a replay. `stream` must be a created stream (not NULL); nothing runs during
+ * capture. A new capture replaces the previous graph. */
+retopk_status retopk_group_capture(retopk_group* g, const uint16_t* const* q, const uint16_t* const* k,
+                                   const uint16_t* const* v, float* const* out, void* stream);
+
+/* Position of the next replayed token: visible length `length` (1 .. max_len)
+ * and decode step t_dec (>= 1). Host-side only; applied by the next replay. */
+retopk_status retopk_group_set_position(retopk_group* g, int32_t length, int32_t t_dec);
+
+/* Replay the captured token on `stream` (one graph launch, plus a one-thread
+ * kernel that sets the position words first when the position was just set or
+ * eager calls ran on the group since the last replay), then advance the
+ * position by one. The same results as retopk_decode_step of every layer in
+ * order at that position. Errors: RETOPK_INVALID_ARG when nothing was captured
+ * or no position was set; RETOPK_OUT_OF_RANGE when the length would exceed
+ * max_len; RETOPK_HIP_ERROR when a launch fails. */
+retopk_status retopk_group_replay(retopk_group* g, void* stream);
+
 /* retopk_dense_attn for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): no
  * handle, no allocation of any kind. The shapes are given per call (head

@@ -64,6 +64,13 @@ _SIGNATURES = {
     "retopk_read_device_error": (ctypes.c_int, [_P, _P]),
     "retopk_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
     "retopk_dense_attn_noalloc": (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P, _P]),
+    "retopk_group_create": (ctypes.c_int, [ctypes.POINTER(RetopkParams), _I32, ctypes.POINTER(_P)]),
+    "retopk_group_destroy": (None, [_P]),
+    "retopk_group_layer": (_P, [_P, _I32]),
+    "retopk_group_device_bytes": (ctypes.c_size_t, [_P]),
+    "retopk_group_capture": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
+    "retopk_group_set_position": (ctypes.c_int, [_P, _I32, _I32]),
+    "retopk_group_replay": (ctypes.c_int, [_P, _P]),
 }
 
 _lib = None
@@ -300,6 +307,80 @@ def retopk_dense_attn_noalloc(q, k, v, length: int, out, stream=None):
                                                     _ptr(out), _stream(stream, q.device)))
 
 
+class ReTopKGroup:
+    """n layers sharing one set of per-call workspaces (retopk_group_*), with
+    a graph-replayed decode token. layers[l] is a ReTopKLayer view of layer l
+    (owned by the group)."""
+
+    def __init__(self, n_layers, retrieval="similarity", **params):
+        lib = load_library()
+        self.params = dict(params, tau=float(params["tau"]))
+        p = RetopkParams(**self.params, retrieval=RETRIEVAL[retrieval])
+        self.params["retrieval"] = retrieval
+        out = _P()
+        _check(lib.retopk_group_create(ctypes.byref(p), n_layers, ctypes.byref(out)))
+        self.ptr = out.value
+        self.layers = []
+        for l in range(n_layers):
+            layer = ReTopKLayer.__new__(ReTopKLayer)
+            layer.handle = Handle(lib.retopk_group_layer(self.ptr, l), self.params)
+            layer.params = self.params
+            layer.owned = False
+            self.layers.append(layer)
+        self._keep = None
+
+    @classmethod
+    def from_workload(cls, wl, n_layers, max_len=None, **override):
+        p = dict(batch=wl.batch, n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads,
+                 head_dim=wl.head_dim, max_len=max_len or wl.max_len, top_k=wl.top_k,
+                 cache_cap=wl.cache_cap, window=wl.window, top_r=wl.top_r,
+                 refresh_every=wl.refresh_every, tau=wl.tau)
+        p.update(override)
+        return cls(n_layers, **p)
+
+    def device_bytes(self):
+        return int(load_library().retopk_group_device_bytes(self.ptr))
+
+    def capture(self, qs, ks, vs, outs, stream):
+        """Capture one token over all layers (lists of device tensors, one per
+        layer; the tensors must stay alive while the graph is used)."""
+        n = len(self.layers)
+        p = self.params
+        for name, ts, shape in (("q", qs, (p["batch"], p["n_q_heads"], p["head_dim"])),
+                                ("k", ks, (p["batch"], p["n_kv_heads"], p["max_len"], p["head_dim"])),
+                                ("v", vs, (p["batch"], p["n_kv_heads"], p["max_len"], p["head_dim"]))):
+            if len(ts) != n:
+                raise ValueError(f"{name}: one tensor per layer")
+            for t in ts:
+                _check_tensor(name, t, shape, _BF16)
+        for t in outs:
+            _check_tensor("out", t, (p["batch"], p["n_q_heads"], p["head_dim"]), ("float32",))
+        arr = lambda ts: (ctypes.c_void_p * n)(*[t.data_ptr() for t in ts])
+        a = [arr(qs), arr(ks), arr(vs), arr(outs)]
+        _check(load_library().retopk_group_capture(self.ptr, *[ctypes.cast(x, ctypes.c_void_p) for x in a],
+                                                   _stream(stream)))
+        self._keep = (list(qs), list(ks), list(vs), list(outs))
+
+    def set_position(self, length, t_dec):
+        _check(load_library().retopk_group_set_position(self.ptr, length, t_dec))
+
+    def replay(self, stream):
+        _check(load_library().retopk_group_replay(self.ptr, _stream(stream)))
+
+    def close(self):
+        if self.ptr:
+            load_library().retopk_group_destroy(self.ptr)
+            self.ptr = 0
+            for layer in self.layers:
+                layer.handle.ptr = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def retopk_stream_read(buf, sink, stream=None):
     """One plain streaming read of the whole device tensor `buf` (measurement aid)."""
     if not buf.is_cuda or not sink.is_cuda:
@@ -321,6 +402,7 @@ class ReTopKLayer:
     def __init__(self, **params):
         self.handle = retopk_create(**params)
         self.params = self.handle.params
+        self.owned = True
 
     @classmethod
     def from_workload(cls, wl, max_len=None, **override):
@@ -332,7 +414,8 @@ class ReTopKLayer:
         return cls(**p)
 
     def close(self):
-        retopk_destroy(self.handle)
+        if getattr(self, "owned", True):
+            retopk_destroy(self.handle)
 
     def __del__(self):
         try:

@@ -47,29 +47,14 @@ class DeviceGuard {
 
 }  // namespace
 
-struct retopk_handle {
-  retopk_params p{};
-  Dims d{};
-  Bufs b{};
-  int device = 0;
-  std::vector<void*> allocs;
-  size_t bytes = 0;
-  bool stats = true;
-  bool timing = false;
-  std::vector<hipEvent_t> events;   // pairs (start, stop)
-  std::vector<int> event_kernel;    // kernel id of each recorded pair
-  int timed = 0;                    // pairs recorded since the last read
-  int call_seq = 0;                 // sequence number of the last k_step launch
-  float* dense_part = nullptr;      // dense attention's row-slice partials [B*Hq, dense_max_split, kDensePart]
-  int32_t* hint_host = nullptr;     // pinned, device-mapped word behind Bufs::hint
+namespace {
 
-  // Tag of the next launch's decision flags: 2 * seq, seq counting 1, 2, ... mod
-  // 2^29 (an even modulus, so bit 1, which selects the scored-row counters,
-  // alternates from call to call, and no tag repeats the previous one).
-  int next_call_flag() {
-    call_seq = (call_seq + 1) & ((1 << 29) - 1);
-    return 2 * call_seq;
-  }
+constexpr int kMaxGroupLayers = 1024;
+
+// Device allocations of one owner, zero-filled, freed together.
+struct Allocs {
+  std::vector<void*> ptrs;
+  size_t bytes = 0;
 
   template <typename T>
   hipError_t alloc(T** ptr, size_t count) {
@@ -77,17 +62,125 @@ struct retopk_handle {
     void* raw = nullptr;
     hipError_t e = hipMalloc(&raw, n > 0 ? n : 16);
     if (e != hipSuccess) return e;
-    allocs.push_back(raw);
+    ptrs.push_back(raw);
     bytes += n;
     *ptr = static_cast<T*>(raw);
     return hipMemset(raw, 0, n > 0 ? n : 16);
   }
-
   void release() {
-    for (void* a : allocs) (void)hipFree(a);
-    allocs.clear();
+    for (void* a : ptrs) (void)hipFree(a);
+    ptrs.clear();
+    bytes = 0;
+  }
+};
+
+// The per-call workspaces of k_step (everything in Bufs but a layer's cache
+// and statistics ring), the dense partials, the launch-hint word, the control
+// words of graph-replayed steps and the call sequence. A handle owns one, or
+// the layers of a group share one (calls on them are serialised on one stream).
+struct Workspace {
+  Allocs mem;
+  Bufs b{};                         // the shared fields filled, the per-layer ones NULL
+  float* dense_part = nullptr;      // dense attention's row-slice partials [B*Hq, dense_max_split, kDensePart]
+  int32_t* hint_host = nullptr;     // pinned, device-mapped word behind Bufs::hint
+  int32_t* ctl = nullptr;           // {length, t_dec, seq, pad}: position of graph-replayed steps
+  int call_seq = 0;                 // sequence number of the last k_step launch on the workspace
+
+  // Tag of the next launch's decision flags: 2 * seq, seq counting 1, 2, ... mod
+  // 2^29 (an even modulus, so bit 1, which selects the histogram half,
+  // alternates from call to call, and no tag repeats the previous one).
+  int next_call_flag() {
+    call_seq = (call_seq + 1) & kSeqMask;
+    return 2 * call_seq;
+  }
+
+  hipError_t create(const Dims& d) {
+    const size_t BH = static_cast<size_t>(d.B) * d.Hq;
+    hipError_t e = hipSuccess;
+    auto A = [&](auto** ptr, size_t n) {
+      if (e == hipSuccess) e = mem.alloc(ptr, n);
+    };
+    A(&b.path, BH);
+    A(&b.rho, BH);
+    A(&b.ret, BH * d.R);
+    A(&b.retslot, BH * d.R);
+    A(&b.m, BH);
+    A(&b.cand, BH * d.cand_cap);
+    A(&b.score, BH * d.score_stride);
+    A(&b.hist, BH * 2 * kNumBins);
+    A(&b.hits, BH * d.max_len);
+    A(&b.ccnt, BH * d.n_cu);
+    A(&b.dec, BH);
+    A(&b.err, 1);
+    A(&b.wdone, 2 * static_cast<size_t>(d.n_cu));
+    A(&b.bkeys, BH * d.max_len);
+    A(&b.sel, BH * d.K);
+    A(&b.selsc, BH * d.K);
+    A(&b.sellen, BH);
+    A(&dense_part, BH * static_cast<size_t>(dense_max_split(d)) * kDensePart);
+    A(&ctl, 4);
+    if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&hint_host), 64, hipHostMallocMapped);
+    if (e == hipSuccess) {
+      *hint_host = 0;
+      e = hipHostGetDevicePointer(reinterpret_cast<void**>(&b.hint), hint_host, 0);
+    }
+    return e;
+  }
+  void release() {
+    mem.release();
     if (hint_host != nullptr) (void)hipHostFree(hint_host);
     hint_host = nullptr;
+  }
+};
+
+}  // namespace
+
+struct retopk_group;
+
+struct retopk_handle {
+  retopk_params p{};
+  Dims d{};
+  Bufs b{};
+  int device = 0;
+  Allocs mem;                       // this layer's cache, statistics ring and table copy
+  Workspace own;                    // the workspace of a stand-alone handle
+  Workspace* ws = &own;             // the workspace in use (a group's, for its layers)
+  retopk_group* group = nullptr;    // the owning group, or NULL
+  bool stats = true;
+  bool timing = false;
+  std::vector<hipEvent_t> events;   // pairs (start, stop)
+  std::vector<int> event_kernel;    // kernel id of each recorded pair
+  int timed = 0;                    // pairs recorded since the last read
+
+  int next_call_flag() { return ws->next_call_flag(); }
+
+  // This layer's own buffers, and its table (the workspace's fields beside
+  // them) copied to the device.
+  hipError_t create_layer() {
+    const size_t BH = static_cast<size_t>(d.B) * d.Hq, D = kHeadDim;
+    Bufs t = ws->b;
+    hipError_t e = hipSuccess;
+    auto A = [&](auto** ptr, size_t n) {
+      if (e == hipSuccess) e = mem.alloc(ptr, n);
+    };
+    A(&t.cache_qbar, BH * d.C * D);
+    A(&t.cache_supp, BH * d.C * d.K);
+    A(&t.cache_len, BH * d.C);
+    A(&t.fifo, BH * 2);
+    A(&t.st_path, BH * kStatsCap);
+    A(&t.st_rho, BH * kStatsCap);
+    A(&t.st_m, BH * kStatsCap);
+    A(&t.self, 1);
+    if (e == hipSuccess) e = hipMemcpy(t.self, &t, sizeof(Bufs), hipMemcpyHostToDevice);
+    b = t;
+    return e;
+  }
+
+  size_t bytes() const { return mem.bytes + (group == nullptr ? own.mem.bytes : 0); }
+
+  void release() {
+    mem.release();
+    own.release();
     for (hipEvent_t e : events) (void)hipEventDestroy(e);
     events.clear();
   }
@@ -119,6 +212,112 @@ struct retopk_handle {
   }
 };
 
+// Layers sharing one workspace, and the HIP graph of one decode token over
+// all of them.
+struct retopk_group {
+  retopk_params p{};
+  Dims d{};
+  int device = 0;
+  Workspace ws;
+  std::vector<retopk_handle*> layers;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  int next_len = 0, next_tdec = 0;  // position of the next replayed token (0: not set)
+  bool ctl_stale = true;            // the control words need setting before the next replay
+  int seq_at_replay = -1;           // the workspace's call sequence after the last replay
+
+  void release() {
+    if (exec != nullptr) (void)hipGraphExecDestroy(exec);
+    if (graph != nullptr) (void)hipGraphDestroy(graph);
+    exec = nullptr;
+    graph = nullptr;
+    for (retopk_handle* h : layers) {
+      h->release();
+      delete h;
+    }
+    layers.clear();
+    ws.release();
+  }
+};
+
+namespace {
+
+// Argument checks shared by retopk_create and retopk_group_create.
+retopk_status check_params(const retopk_params& p, const char* who) {
+  const std::string w(who);
+  if (p.batch < 1 || p.n_q_heads < 1 || p.n_kv_heads < 1)
+    return fail(RETOPK_INVALID_ARG, w + ": batch and head counts must be >= 1");
+  if (p.n_q_heads % p.n_kv_heads != 0)
+    return fail(RETOPK_INVALID_ARG, w + ": n_q_heads must be a multiple of n_kv_heads");
+  if (p.n_q_heads / p.n_kv_heads > kMaxGroup)
+    return fail(RETOPK_INVALID_ARG, w + ": at most 16 query heads per KV head");
+  if (p.head_dim != kHeadDim) return fail(RETOPK_INVALID_ARG, w + ": head_dim must be 128");
+  if (p.max_len < 1 || p.max_len > (1 << 24))
+    return fail(RETOPK_OUT_OF_RANGE, w + ": max_len must be in 1 .. 2^24");
+  if (p.top_k < 1 || p.top_k > 8192) return fail(RETOPK_OUT_OF_RANGE, w + ": top_k must be in 1 .. 8192");
+  if (p.cache_cap < 1 || p.cache_cap > 64)
+    return fail(RETOPK_OUT_OF_RANGE, w + ": cache_cap must be in 1 .. 64");
+  if (p.window < 0) return fail(RETOPK_OUT_OF_RANGE, w + ": window must be >= 0");
+  if (p.top_r < 1 || p.top_r > p.cache_cap)
+    return fail(RETOPK_OUT_OF_RANGE, w + ": top_r must be in 1 .. cache_cap");
+  if (p.refresh_every < 0) return fail(RETOPK_OUT_OF_RANGE, w + ": refresh_every must be >= 0");
+  if (std::isnan(p.tau)) return fail(RETOPK_INVALID_ARG, w + ": tau is NaN");
+  if (p.retrieval != RETOPK_RETRIEVE_SIMILAR && p.retrieval != RETOPK_RETRIEVE_RECENT)
+    return fail(RETOPK_INVALID_ARG, w + ": retrieval must be RETOPK_RETRIEVE_SIMILAR or _RECENT");
+  const long long cand = static_cast<long long>(p.top_r) * p.top_k + p.window;
+  if (cand > kMaxCand) return fail(RETOPK_OUT_OF_RANGE, w + ": top_r * top_k + window must be <= 16384");
+  {
+    Dims probe{};
+    probe.K = p.top_k;
+    probe.G = p.n_q_heads / p.n_kv_heads;
+    probe.cand_cap = static_cast<int>(cand);
+    probe.n_cu = kHeadThreads;  // the most score work groups a call has
+    if (head_lds_bytes(probe) > static_cast<size_t>(kLdsLimit) ||
+        finish_lds_bytes(probe) > static_cast<size_t>(kLdsLimit) ||
+        score_lds_bytes(probe) > static_cast<size_t>(kLdsLimit))
+      return fail(RETOPK_OUT_OF_RANGE, w + ": top_k / top_r / window need more LDS than a work group has");
+  }
+  const long long bh = static_cast<long long>(p.batch) * p.n_q_heads;
+  if (bh > (1 << 20)) return fail(RETOPK_OUT_OF_RANGE, w + ": batch * n_q_heads too large");
+  if (static_cast<long long>(p.batch) * p.n_kv_heads > 1024)
+    return fail(RETOPK_OUT_OF_RANGE, w + ": batch * n_kv_heads must be <= 1024");
+  return RETOPK_OK;
+}
+
+retopk_status current_device(int* dev, int* n_cu, const char* who) {
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return fail(RETOPK_NO_DEVICE, std::string(who) + ": no HIP device visible");
+  }
+  if (hipGetDevice(dev) != hipSuccess) return fail(RETOPK_NO_DEVICE, std::string(who) + ": hipGetDevice failed");
+  if (hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, *dev) != hipSuccess || *n_cu < 1)
+    return fail(RETOPK_NO_DEVICE, std::string(who) + ": cannot read the compute unit count");
+  return RETOPK_OK;
+}
+
+Dims make_dims(const retopk_params& p, int n_cu) {
+  Dims d{};
+  d.B = p.batch;
+  d.Hq = p.n_q_heads;
+  d.Hkv = p.n_kv_heads;
+  d.G = p.n_q_heads / p.n_kv_heads;
+  d.max_len = p.max_len;
+  d.score_stride = (p.max_len + 15) / 16 * 16;
+  d.K = p.top_k;
+  d.C = p.cache_cap;
+  d.W = p.window;
+  d.R = p.top_r;
+  d.Tr = p.refresh_every;
+  d.cand_cap = p.top_r * p.top_k + p.window;
+  d.n_cu = n_cu;
+  d.recent = p.retrieval == RETOPK_RETRIEVE_RECENT ? 1 : 0;
+  d.tau = p.tau;
+  return d;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* retopk_status_string(retopk_status s) {
@@ -139,7 +338,7 @@ int32_t retopk_kernel_count(void) { return kNumKernels; }
 
 const char* retopk_kernel_name(int32_t id) { return kernel_name(id); }
 
-size_t retopk_device_bytes(const retopk_handle* h) { return h ? h->bytes : 0; }
+size_t retopk_device_bytes(const retopk_handle* h) { return h ? h->bytes() : 0; }
 
 retopk_status retopk_read_device_error(retopk_handle* h, int32_t* word) {
   if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_read_device_error: NULL handle");
@@ -156,117 +355,19 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
   if (out == nullptr) return fail(RETOPK_INVALID_ARG, "retopk_create: out is NULL");
   *out = nullptr;
   if (params == nullptr) return fail(RETOPK_INVALID_ARG, "retopk_create: params is NULL");
-  const retopk_params& p = *params;
-  if (p.batch < 1 || p.n_q_heads < 1 || p.n_kv_heads < 1)
-    return fail(RETOPK_INVALID_ARG, "retopk_create: batch and head counts must be >= 1");
-  if (p.n_q_heads % p.n_kv_heads != 0)
-    return fail(RETOPK_INVALID_ARG, "retopk_create: n_q_heads must be a multiple of n_kv_heads");
-  if (p.n_q_heads / p.n_kv_heads > kMaxGroup)
-    return fail(RETOPK_INVALID_ARG, "retopk_create: at most 16 query heads per KV head");
-  if (p.head_dim != kHeadDim) return fail(RETOPK_INVALID_ARG, "retopk_create: head_dim must be 128");
-  if (p.max_len < 1 || p.max_len > (1 << 24))
-    return fail(RETOPK_OUT_OF_RANGE, "retopk_create: max_len must be in 1 .. 2^24");
-  if (p.top_k < 1 || p.top_k > 8192) return fail(RETOPK_OUT_OF_RANGE, "retopk_create: top_k must be in 1 .. 8192");
-  if (p.cache_cap < 1 || p.cache_cap > 64)
-    return fail(RETOPK_OUT_OF_RANGE, "retopk_create: cache_cap must be in 1 .. 64");
-  if (p.window < 0) return fail(RETOPK_OUT_OF_RANGE, "retopk_create: window must be >= 0");
-  if (p.top_r < 1 || p.top_r > p.cache_cap)
-    return fail(RETOPK_OUT_OF_RANGE, "retopk_create: top_r must be in 1 .. cache_cap");
-  if (p.refresh_every < 0) return fail(RETOPK_OUT_OF_RANGE, "retopk_create: refresh_every must be >= 0");
-  if (std::isnan(p.tau)) return fail(RETOPK_INVALID_ARG, "retopk_create: tau is NaN");
-  if (p.retrieval != RETOPK_RETRIEVE_SIMILAR && p.retrieval != RETOPK_RETRIEVE_RECENT)
-    return fail(RETOPK_INVALID_ARG, "retopk_create: retrieval must be RETOPK_RETRIEVE_SIMILAR or _RECENT");
-  const long long cand = static_cast<long long>(p.top_r) * p.top_k + p.window;
-  if (cand > kMaxCand)
-    return fail(RETOPK_OUT_OF_RANGE, "retopk_create: top_r * top_k + window must be <= 16384");
-  {
-    Dims probe{};
-    probe.K = p.top_k;
-    probe.G = p.n_q_heads / p.n_kv_heads;
-    probe.cand_cap = static_cast<int>(cand);
-    probe.n_cu = kHeadThreads;  // the most score work groups a call has
-    if (head_lds_bytes(probe) > static_cast<size_t>(kLdsLimit) ||
-        finish_lds_bytes(probe) > static_cast<size_t>(kLdsLimit) ||
-        score_lds_bytes(probe) > static_cast<size_t>(kLdsLimit))
-      return fail(RETOPK_OUT_OF_RANGE, "retopk_create: top_k / top_r / window need more LDS than a work group has");
-  }
-  const long long bh = static_cast<long long>(p.batch) * p.n_q_heads;
-  if (bh > (1 << 20)) return fail(RETOPK_OUT_OF_RANGE, "retopk_create: batch * n_q_heads too large");
-  if (static_cast<long long>(p.batch) * p.n_kv_heads > 1024)
-    return fail(RETOPK_OUT_OF_RANGE, "retopk_create: batch * n_kv_heads must be <= 1024");
-
-  int ndev = 0;
-  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
-    (void)hipGetLastError();
-    return fail(RETOPK_NO_DEVICE, "retopk_create: no HIP device visible");
-  }
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(RETOPK_NO_DEVICE, "retopk_create: hipGetDevice failed");
-  int n_cu = 0;
-  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
-    return fail(RETOPK_NO_DEVICE, "retopk_create: cannot read the compute unit count");
-
+  retopk_status st = check_params(*params, "retopk_create");
+  if (st != RETOPK_OK) return st;
+  int dev = 0, n_cu = 0;
+  st = current_device(&dev, &n_cu, "retopk_create");
+  if (st != RETOPK_OK) return st;
   auto* h = new (std::nothrow) retopk_handle();
   if (h == nullptr) return fail(RETOPK_HIP_ERROR, "retopk_create: out of host memory");
-  h->p = p;
+  h->p = *params;
   h->device = dev;
-  Dims& d = h->d;
-  d.B = p.batch;
-  d.Hq = p.n_q_heads;
-  d.Hkv = p.n_kv_heads;
-  d.G = p.n_q_heads / p.n_kv_heads;
-  d.max_len = p.max_len;
-  d.score_stride = (p.max_len + 15) / 16 * 16;
-  d.K = p.top_k;
-  d.C = p.cache_cap;
-  d.W = p.window;
-  d.R = p.top_r;
-  d.Tr = p.refresh_every;
-  d.cand_cap = static_cast<int>(cand);
-  d.n_cu = n_cu;
-  d.recent = p.retrieval == RETOPK_RETRIEVE_RECENT ? 1 : 0;
-  d.tau = p.tau;
-
-  Bufs& b = h->b;
-  const size_t BH = static_cast<size_t>(bh);
-  const size_t D = kHeadDim;
-  hipError_t e = hipSuccess;
-  auto A = [&](auto** ptr, size_t n) {
-    if (e == hipSuccess) e = h->alloc(ptr, n);
-  };
-  A(&b.cache_qbar, BH * d.C * D);
-  A(&b.cache_supp, BH * d.C * d.K);
-  A(&b.cache_len, BH * d.C);
-  A(&b.fifo, BH * 2);
-  A(&b.path, BH);
-  A(&b.rho, BH);
-  A(&b.ret, BH * d.R);
-  A(&b.retslot, BH * d.R);
-  A(&b.m, BH);
-  A(&b.cand, BH * d.cand_cap);
-  A(&b.score, BH * d.score_stride);
-  A(&b.hist, BH * 2 * kNumBins);
-  A(&b.hits, BH * d.max_len);
-  A(&b.ccnt, BH * d.n_cu);
-  A(&b.dec, BH);
-  A(&b.err, 1);
-  A(&b.wdone, 2 * static_cast<size_t>(d.n_cu));
-  A(&b.bkeys, BH * d.max_len);
-  A(&b.sel, BH * d.K);
-  A(&b.selsc, BH * d.K);
-  A(&b.sellen, BH);
-  A(&b.st_path, BH * kStatsCap);
-  A(&b.st_rho, BH * kStatsCap);
-  A(&b.st_m, BH * kStatsCap);
-  if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&h->hint_host), 64, hipHostMallocMapped);
-  if (e == hipSuccess) {
-    *h->hint_host = 0;
-    e = hipHostGetDevicePointer(reinterpret_cast<void**>(&b.hint), h->hint_host, 0);
-  }
-  A(&b.self, 1);
-  A(&h->dense_part, BH * static_cast<size_t>(dense_max_split(d)) * kDensePart);
-  if (e == hipSuccess) e = hipMemcpy(b.self, &b, sizeof(Bufs), hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = configure_kernels(d);
+  h->d = make_dims(*params, n_cu);
+  hipError_t e = h->own.create(h->d);
+  if (e == hipSuccess) e = h->create_layer();
+  if (e == hipSuccess) e = configure_kernels(h->d);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     h->release();
@@ -278,13 +379,162 @@ retopk_status retopk_create(const retopk_params* params, retopk_handle** out) {
 }
 
 void retopk_destroy(retopk_handle* h) {
-  if (h == nullptr) return;
+  if (h == nullptr || h->group != nullptr) return;  // a group's layers go with the group
   {
     DeviceGuard guard(h->device);
     (void)hipDeviceSynchronize();
     h->release();
   }
   delete h;
+}
+
+retopk_status retopk_group_create(const retopk_params* params, int32_t n_layers, retopk_group** out) {
+  if (out == nullptr) return fail(RETOPK_INVALID_ARG, "retopk_group_create: out is NULL");
+  *out = nullptr;
+  if (params == nullptr) return fail(RETOPK_INVALID_ARG, "retopk_group_create: params is NULL");
+  if (n_layers < 1 || n_layers > kMaxGroupLayers)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_group_create: n_layers must be in 1 .. 1024");
+  retopk_status st = check_params(*params, "retopk_group_create");
+  if (st != RETOPK_OK) return st;
+  int dev = 0, n_cu = 0;
+  st = current_device(&dev, &n_cu, "retopk_group_create");
+  if (st != RETOPK_OK) return st;
+  auto* g = new (std::nothrow) retopk_group();
+  if (g == nullptr) return fail(RETOPK_HIP_ERROR, "retopk_group_create: out of host memory");
+  g->p = *params;
+  g->device = dev;
+  g->d = make_dims(*params, n_cu);
+  hipError_t e = g->ws.create(g->d);
+  for (int l = 0; l < n_layers && e == hipSuccess; ++l) {
+    auto* h = new (std::nothrow) retopk_handle();
+    if (h == nullptr) {
+      e = hipErrorOutOfMemory;
+      break;
+    }
+    h->p = *params;
+    h->device = dev;
+    h->d = g->d;
+    h->ws = &g->ws;
+    h->group = g;
+    g->layers.push_back(h);
+    e = h->create_layer();
+  }
+  if (e == hipSuccess) e = configure_kernels(g->d);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    g->release();
+    delete g;
+    return hip_fail(e, "retopk_group_create: device allocation");
+  }
+  *out = g;
+  return RETOPK_OK;
+}
+
+void retopk_group_destroy(retopk_group* g) {
+  if (g == nullptr) return;
+  {
+    DeviceGuard guard(g->device);
+    (void)hipDeviceSynchronize();
+    g->release();
+  }
+  delete g;
+}
+
+retopk_handle* retopk_group_layer(retopk_group* g, int32_t layer) {
+  if (g == nullptr || layer < 0 || layer >= static_cast<int32_t>(g->layers.size())) return nullptr;
+  return g->layers[layer];
+}
+
+size_t retopk_group_device_bytes(const retopk_group* g) {
+  if (g == nullptr) return 0;
+  size_t n = g->ws.mem.bytes;
+  for (const retopk_handle* h : g->layers) n += h->mem.bytes;
+  return n;
+}
+
+retopk_status retopk_group_set_position(retopk_group* g, int32_t length, int32_t t_dec) {
+  if (g == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_group_set_position: NULL group");
+  if (length < 1 || length > g->d.max_len)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_group_set_position: length must be in 1 .. max_len");
+  if (t_dec < 1) return fail(RETOPK_OUT_OF_RANGE, "retopk_group_set_position: t_dec must be >= 1");
+  g->next_len = length;
+  g->next_tdec = t_dec;
+  g->ctl_stale = true;
+  return RETOPK_OK;
+}
+
+retopk_status retopk_group_capture(retopk_group* g, const uint16_t* const* q, const uint16_t* const* k,
+                                   const uint16_t* const* v, float* const* out, void* stream) {
+  if (g == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_group_capture: NULL group");
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(RETOPK_INVALID_ARG, "retopk_group_capture: NULL pointer array");
+  if (stream == nullptr) return fail(RETOPK_INVALID_ARG, "retopk_group_capture: needs a created stream (not NULL)");
+  const int n = static_cast<int>(g->layers.size());
+  for (int l = 0; l < n; ++l) {
+    if (q[l] == nullptr || k[l] == nullptr || v[l] == nullptr || out[l] == nullptr)
+      return fail(RETOPK_INVALID_ARG, "retopk_group_capture: NULL tensor");
+    if (!aligned(q[l], 16) || !aligned(k[l], 16) || !aligned(v[l], 16) || !aligned(out[l], 4))
+      return fail(RETOPK_INVALID_ARG, "retopk_group_capture: misaligned tensor");
+  }
+  DeviceGuard guard(g->device);
+  auto s = static_cast<hipStream_t>(stream);
+  const Dims& d = g->d;
+  const long q_sb = static_cast<long>(d.Hq) * kHeadDim, q_sh = kHeadDim;
+  const bool wide = 2 * *static_cast<volatile int32_t*>(g->ws.hint_host) >= d.B * d.Hkv;
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return hip_fail(e, "retopk_group_capture: hipStreamBeginCapture");
+  hipError_t le = launch_advance(g->ws.ctl, n, s);
+  for (int l = 0; l < n && le == hipSuccess; ++l) {
+    const retopk_handle* h = g->layers[l];
+    // sized for the longest length a replay can have; the position and the
+    // call flag are read from the control words
+    le = launch_step(d, h->b, q[l], q_sb, q_sh, k[l], v[l], out[l], nullptr, d.max_len, 0, kModeDecode,
+                     h->stats ? 0 : -1, 1, 0, wide, s, g->ws.ctl, l);
+  }
+  e = hipStreamEndCapture(s, &graph);
+  if (le != hipSuccess) {
+    if (graph != nullptr) (void)hipGraphDestroy(graph);
+    return hip_fail(le, "retopk_group_capture: launch");
+  }
+  if (e != hipSuccess) return hip_fail(e, "retopk_group_capture: hipStreamEndCapture");
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return hip_fail(e, "retopk_group_capture: hipGraphInstantiate");
+  }
+  if (g->exec != nullptr) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph != nullptr) (void)hipGraphDestroy(g->graph);
+  g->graph = graph;
+  g->exec = exec;
+  return RETOPK_OK;
+}
+
+retopk_status retopk_group_replay(retopk_group* g, void* stream) {
+  if (g == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_group_replay: NULL group");
+  if (g->exec == nullptr) return fail(RETOPK_INVALID_ARG, "retopk_group_replay: nothing captured");
+  if (g->next_len < 1) return fail(RETOPK_INVALID_ARG, "retopk_group_replay: no position set");
+  if (g->next_len > g->d.max_len)
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_group_replay: the next token's length exceeds max_len");
+  DeviceGuard guard(g->device);
+  auto s = static_cast<hipStream_t>(stream);
+  const int n = static_cast<int>(g->layers.size());
+  hipError_t e = hipSuccess;
+  if (g->ctl_stale || g->ws.call_seq != g->seq_at_replay) {
+    // the words the replay's k_advance moves on to this token's position and to
+    // the call sequence an eager call would take next
+    e = launch_set_position(g->ws.ctl, g->next_len - 1, g->next_tdec - 1, g->ws.call_seq + 1 - n, s);
+    if (e != hipSuccess) return hip_fail(e, "retopk_group_replay: control words");
+  }
+  e = hipGraphLaunch(g->exec, s);
+  if (e != hipSuccess) return hip_fail(e, "retopk_group_replay: hipGraphLaunch");
+  g->ws.call_seq = (g->ws.call_seq + n) & kSeqMask;
+  g->seq_at_replay = g->ws.call_seq;
+  g->ctl_stale = false;
+  g->next_len += 1;
+  g->next_tdec += 1;
+  return RETOPK_OK;
 }
 
 retopk_status retopk_init_from_prefill(retopk_handle* h, const uint16_t* q_tail, const uint16_t* k,
@@ -309,7 +559,7 @@ retopk_status retopk_init_from_prefill(retopk_handle* h, const uint16_t* q_tail,
     const int flag = h->next_call_flag();
     st = h->run(kKStep, s, [&] {
       return launch_step(d, b, qi, q_sb, q_sh, k, nullptr, nullptr, nullptr, len, 0, kModeExact, -1, 1, flag, false,
-                         s);
+                         s, nullptr, 0);
     });
   }
   return st;
@@ -335,10 +585,11 @@ retopk_status retopk_decode_step(retopk_handle* h, const uint16_t* q, const uint
   const int flag = h->next_call_flag();
   // exact KV groups of a recent step, written by the device into host-mapped
   // memory (possibly stale; it only sizes the launch)
-  const int recent_exact = *static_cast<volatile int32_t*>(h->hint_host);
+  const int recent_exact = *static_cast<volatile int32_t*>(h->ws->hint_host);
   const bool wide = 2 * recent_exact >= d.B * d.Hkv;
   retopk_status st = h->run(kKStep, s, [&] {
-    return launch_step(d, b, q, q_sb, q_sh, k, v, out, nullptr, length, t_dec, kModeDecode, slot, 1, flag, wide, s);
+    return launch_step(d, b, q, q_sb, q_sh, k, v, out, nullptr, length, t_dec, kModeDecode, slot, 1, flag, wide, s,
+                       nullptr, 0);
   });
   return st;
 }
@@ -361,7 +612,8 @@ retopk_status retopk_exact_topk_attn(retopk_handle* h, const uint16_t* q, const 
   const long q_sb = static_cast<long>(d.Hq) * kHeadDim, q_sh = kHeadDim;
   const int flag = h->next_call_flag();
   retopk_status st = h->run(kKStep, s, [&] {
-    return launch_step(d, b, q, q_sb, q_sh, k, v, out, sel_out, length, 0, kModeExact, -1, 0, flag, false, s);
+    return launch_step(d, b, q, q_sb, q_sh, k, v, out, sel_out, length, 0, kModeExact, -1, 0, flag, false, s,
+                       nullptr, 0);
   });
   return st;
 }
@@ -379,9 +631,9 @@ retopk_status retopk_dense_attn(retopk_handle* h, const uint16_t* q, const uint1
     return fail(RETOPK_OUT_OF_RANGE, "retopk_dense_attn: at most 8 query heads per KV head");
   DeviceGuard guard(h->device);
   auto s = static_cast<hipStream_t>(stream);
-  retopk_status st = h->run(kKDense, s, [&] { return launch_dense(h->d, q, k, v, out, length, h->dense_part, s, 0); });
+  retopk_status st = h->run(kKDense, s, [&] { return launch_dense(h->d, q, k, v, out, length, h->ws->dense_part, s, 0); });
   if (st != RETOPK_OK) return st;
-  return h->run(kKDenseMerge, s, [&] { return launch_dense(h->d, q, k, v, out, length, h->dense_part, s, 1); });
+  return h->run(kKDenseMerge, s, [&] { return launch_dense(h->d, q, k, v, out, length, h->ws->dense_part, s, 1); });
 }
 
 retopk_status retopk_dense_attn_noalloc(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t max_len,

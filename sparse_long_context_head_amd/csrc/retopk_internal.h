@@ -75,7 +75,7 @@ struct Bufs {
   Bufs* self;              // device copy of this table (what the step kernel is given)
 };
 
-enum KernelId : int { kKStep = 0, kKReset, kKDense, kKDenseMerge, kNumKernels };
+enum KernelId : int { kKStep = 0, kKReset, kKDense, kKDenseMerge, kKAdvance, kNumKernels };
 
 const char* kernel_name(int id);
 
@@ -106,9 +106,17 @@ hipError_t launch_reset(const Dims& d, const Bufs& b, hipStream_t s);
 // or out is NULL), S_t to sel_out (when not NULL) and cache update (when
 // push). call_flag: an even number, different from the previous call's, that
 // tags this call's decision flags; its bit 1 selects the half of `scored`.
+// ctl: NULL for a step whose length, t_dec and call flag are the arguments;
+// else the device control words {length, t_dec, seq} of graph-replayed steps
+// (length then sizes the launch: the longest of the replays), the call flag
+// being 2 * ((seq + layer) & kSeqMask) and stats_slot >= 0 meaning "record".
 hipError_t launch_step(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh, const uint16_t* k,
                        const uint16_t* v, float* out, int32_t* sel_out, int length, int t_dec, int mode,
-                       int stats_slot, int push, int call_flag, bool wide, hipStream_t s);
+                       int stats_slot, int push, int call_flag, bool wide, hipStream_t s, const int32_t* ctl,
+                       int layer);
+constexpr int kSeqMask = (1 << 29) - 1;  // call sequence numbers, mod 2^29 (the call flag is twice one)
+hipError_t launch_advance(int32_t* ctl, int n_layers, hipStream_t s);
+hipError_t launch_set_position(int32_t* ctl, int length, int t_dec, int seq, hipStream_t s);
 
 // Dense softmax attention (retopk_dense.hip): row slices per KV group of a
 // call at this length, and the most any length gives (the partials workspace

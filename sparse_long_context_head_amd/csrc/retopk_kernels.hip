@@ -991,12 +991,15 @@ static_assert(sizeof(Bufs) > 0xc0 && sizeof(Bufs) <= 0x100, "the buffer table sp
 
 // A uniform int read with a scalar load (constant address space): only for
 // words no work group of the running launch writes before the read.
-__device__ __forceinline__ int scalar_read(gptr<int32_t> p) {
+__device__ __forceinline__ int scalar_read_ptr(const int32_t* p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   return *(__attribute__((address_space(4))) const int32_t*)(reinterpret_cast<uintptr_t>(p));
 #else
   return *p;
 #endif
+}
+__device__ __forceinline__ int scalar_read(gptr<int32_t> p) {
+  return scalar_read_ptr(reinterpret_cast<const int32_t*>(reinterpret_cast<uintptr_t>(p)));
 }
 
 __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uint16_t* q, long q_sb, long q_sh,
@@ -1859,8 +1862,19 @@ __global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, const Bufs* __res
                                                        const uint16_t* k, const uint16_t* v, float* out,
                                                        int32_t* sel_out, int length, int t_dec, int mode,
                                                        int stats_slot, int push, int call_flag, int n_score,
-                                                       int keep) {
+                                                       int keep, const int32_t* ctl, int layer) {
   __shared__ HeadShared sh;
+  if (ctl != nullptr) {
+    // A step replayed from a graph: the position and the call's sequence
+    // number come from the control words that k_advance moved on at the head
+    // of the replay (an earlier launch on the stream); this layer's call is
+    // `layer` steps after the replay's first.
+    length = scalar_read_ptr(ctl);
+    t_dec = scalar_read_ptr(ctl + 1);
+    const int seq = (scalar_read_ptr(ctl + 2) + layer) & kSeqMask;
+    call_flag = 2 * seq;
+    if (stats_slot >= 0) stats_slot = (t_dec - 1) % kStatsCap;
+  }
   // The buffer table is not held in the kernel's argument registers, which
   // would keep it live through both roles: each role reads its own copy.
   const int BH = d.B * d.Hq;
@@ -1884,7 +1898,7 @@ hipError_t configure_kernels(const Dims& d) {
 }
 
 const char* kernel_name(int id) {
-  static const char* names[kNumKernels] = {"k_step", "k_reset", "k_dense", "k_dense_merge"};
+  static const char* names[kNumKernels] = {"k_step", "k_reset", "k_dense", "k_dense_merge", "k_advance"};
   return (id >= 0 && id < kNumKernels) ? names[id] : "";
 }
 
@@ -1896,11 +1910,41 @@ hipError_t launch_reset(const Dims& d, const Bufs& b, hipStream_t s) {
 
 hipError_t launch_step(const Dims& d, const Bufs& b, const uint16_t* q, long q_sb, long q_sh, const uint16_t* k,
                        const uint16_t* v, float* out, int32_t* sel_out, int length, int t_dec, int mode,
-                       int stats_slot, int push, int call_flag, bool wide, hipStream_t s) {
+                       int stats_slot, int push, int call_flag, bool wide, hipStream_t s, const int32_t* ctl,
+                       int layer) {
+  // (a replayed step is sized for `length`, the longest of its replays)
   const int n_score = score_grid(d, length, mode, wide);
   hipLaunchKernelGGL(k_step, dim3(d.B * d.Hq + n_score), dim3(kHeadThreads), step_lds_bytes(d), s, d, b.self, q, q_sb,
                      q_sh, k, v, out, sel_out, length, t_dec, mode, stats_slot, push, call_flag, n_score,
-                     score_keep_rows(d, length, n_score));
+                     score_keep_rows(d, length, n_score), ctl, layer);
+  return hipGetLastError();
+}
+
+// The control words of graph-replayed steps: {length, t_dec, seq}. k_advance
+// moves them on by one token (n_layers calls); k_set_position sets them.
+__global__ void k_advance(int32_t* ctl, int n_layers) {
+  if (threadIdx.x == 0) {
+    ctl[0] += 1;
+    ctl[1] += 1;
+    ctl[2] = (ctl[2] + n_layers) & kSeqMask;
+  }
+}
+
+__global__ void k_set_position(int32_t* ctl, int length, int t_dec, int seq) {
+  if (threadIdx.x == 0) {
+    ctl[0] = length;
+    ctl[1] = t_dec;
+    ctl[2] = seq & kSeqMask;
+  }
+}
+
+hipError_t launch_advance(int32_t* ctl, int n_layers, hipStream_t s) {
+  hipLaunchKernelGGL(k_advance, dim3(1), dim3(64), 0, s, ctl, n_layers);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_position(int32_t* ctl, int length, int t_dec, int seq, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_position, dim3(1), dim3(64), 0, s, ctl, length, t_dec, seq);
   return hipGetLastError();
 }
 
