@@ -21,7 +21,8 @@ the AR recursion runs unrounded in float64. Arrays are returned as raw uint16
 bf16 bit patterns.
 
 Draw order per sequence (numpy PCG64, ``default_rng(seed)``):
-  1. K  float64 normals, shape [Hkv, L0 + T, d]
+  1. K  float64 normals, shape [Hkv, L0 + T, d] (for multi-GB arrays drawn in
+     chunks of rows, the same normals in the same order; see _sequence_chunked)
   2. heavy rows: for each KV head, ``choice(L0, n_heavy, replace=False)``
   3. V  float64 normals, shape [Hkv, L0 + T, d]
   4. query innovations, shape [Hq, n0 + T, d]
@@ -98,6 +99,9 @@ WORKLOADS = {
     # One-layer scaling: the headline layer at 1M context (K + V = 2.1 GB per layer).
     "scale1m": Workload(name="scale1m", config_id=7, batch=1, n_q_heads=28, n_kv_heads=4,
                         prompt_len=1 << 20, decode_steps=256, top_k=512, n_heavy=64, **_BASE),
+    # ... and at 4M (K + V = 8.6 GB per layer; drawn in chunks, see _sequence_chunked).
+    "scale4m": Workload(name="scale4m", config_id=8, batch=1, n_q_heads=28, n_kv_heads=4,
+                        prompt_len=1 << 22, decode_steps=128, top_k=512, n_heavy=64, **_BASE),
 }
 
 
@@ -108,16 +112,52 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return rounded.astype(np.uint16)
 
 
+# Key/value arrays of more elements than this are drawn in chunks of rows (the
+# same normals in the same order) to bound host memory; their heavy rows are
+# then scaled from the float32-rounded draws (a second rounding the smaller
+# workloads do not have).
+_CHUNKED_ABOVE = 1 << 31
+_CHUNK_ROWS = 1 << 18
+
+
+def _sequence_chunked(w: Workload, rng):
+    hkv, d = w.n_kv_heads, w.head_dim
+    n_rows = w.prompt_len + w.decode_steps
+    k32 = np.empty((hkv, n_rows, d), np.float32)
+    for g in range(hkv):
+        for r0 in range(0, n_rows, _CHUNK_ROWS):
+            r1 = min(n_rows, r0 + _CHUNK_ROWS)
+            k32[g, r0:r1] = rng.standard_normal((r1 - r0, d))
+    if w.n_heavy:
+        for g in range(hkv):
+            rows = rng.choice(w.prompt_len, w.n_heavy, replace=False)
+            k32[g, rows, :] *= np.float32(3.0)
+    k = f32_to_bf16_bits(k32)
+    del k32
+    v = np.empty((hkv, n_rows, d), np.uint16)
+    for g in range(hkv):
+        for r0 in range(0, n_rows, _CHUNK_ROWS):
+            r1 = min(n_rows, r0 + _CHUNK_ROWS)
+            v[g, r0:r1] = f32_to_bf16_bits(rng.standard_normal((r1 - r0, d)).astype(np.float32))
+    return k, v
+
+
 def _sequence(w: Workload, seed: int):
     rng = np.random.default_rng(seed)
     hkv, hq, d = w.n_kv_heads, w.n_q_heads, w.head_dim
     n_rows = w.prompt_len + w.decode_steps
-    k = rng.standard_normal((hkv, n_rows, d))
-    if w.n_heavy:
-        for g in range(hkv):
-            rows = rng.choice(w.prompt_len, w.n_heavy, replace=False)
-            k[g, rows, :] *= 3.0
-    v = rng.standard_normal((hkv, n_rows, d))
+    to16 = lambda a: f32_to_bf16_bits(a.astype(np.float32))
+    if hkv * n_rows * d > _CHUNKED_ABOVE:
+        k16, v16 = _sequence_chunked(w, rng)
+    else:
+        k = rng.standard_normal((hkv, n_rows, d))
+        if w.n_heavy:
+            for g in range(hkv):
+                rows = rng.choice(w.prompt_len, w.n_heavy, replace=False)
+                k[g, rows, :] *= 3.0
+        v = rng.standard_normal((hkv, n_rows, d))
+        k16, v16 = to16(k), to16(v)
+        del k, v
     n_q = w.n_prompt_queries + w.decode_steps
     eps = rng.standard_normal((hq, n_q, d))
     q = np.empty_like(eps)
@@ -125,8 +165,7 @@ def _sequence(w: Workload, seed: int):
     s = math.sqrt(1.0 - w.query_rho * w.query_rho)
     for n in range(1, n_q):
         q[:, n] = w.query_rho * q[:, n - 1] + s * eps[:, n]
-    to16 = lambda a: f32_to_bf16_bits(a.astype(np.float32))
-    return to16(k), to16(v), to16(q)
+    return k16, v16, to16(q)
 
 
 def generate(w: Workload, seed_base: int | None = None):

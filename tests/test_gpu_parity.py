@@ -632,3 +632,16 @@ def test_scale_1m_every_head():
     Then the Exact Top-K baseline on every head."""
     run_lockstep("scale1m", 4, override=dict(refresh_every=2), check_init=False, wl_kw=dict(decode_steps=8))
     run_exact("scale1m", [(1 << 20) + 3], wl_kw=dict(decode_steps=8))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_scale_4m_sampled():
+    """L0 = 4,194,304 (K and V of the layer 8.6 GB; scores, survivors and
+    boundary keys in their workspaces): KV group 1 in lockstep for 4 steps
+    with a refresh every 2 steps (the cache from the GPU's initialisation), the
+    reuse unions spanning 16 LDS bitmap windows of 262,144 positions; then the
+    Exact Top-K baseline on KV group 3."""
+    run_lockstep("scale4m", 4, sub=(0, 1), override=dict(refresh_every=2), check_init=False,
+                 wl_kw=dict(decode_steps=8))
+    run_exact("scale4m", [(1 << 22) + 3], sub=(0, 3), wl_kw=dict(decode_steps=8))
