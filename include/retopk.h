@@ -257,7 +257,8 @@ retopk_status retopk_read_state(retopk_handle* h, float* qbar, int32_t* supp,
 
 /* Replace the caches from host buffers in the retopk_read_state layout
  * (resume from a snapshot). Each count must be 0 .. C, each supp_len 0 .. K,
- * and each support entry 0 .. Lmax-1. Synchronous.
+ * each support strictly ascending (RETOPK_INVALID_ARG otherwise) with entries
+ * 0 .. Lmax-1 (RETOPK_OUT_OF_RANGE otherwise). Synchronous.
  * A later decode step at visible length L ignores stored support entries
  * >= L (those keys are not visible yet, so they cannot be candidates; a
  * library-written cache never holds any, since L never decreases). When a

@@ -744,6 +744,8 @@ retopk_status retopk_write_state(retopk_handle* h, const float* qbar, const int3
       for (int j = 0; j < len; ++j) {
         const int x = supp[e * K + j];
         if (x < 0 || x >= d.max_len) return fail(RETOPK_OUT_OF_RANGE, "retopk_write_state: support index out of range");
+        if (j > 0 && x <= rs[e * K + j - 1])
+          return fail(RETOPK_INVALID_ARG, "retopk_write_state: a support is not strictly ascending");
         rs[e * K + j] = x;
       }
       rl[e] = len;

@@ -390,6 +390,7 @@ struct HeadShared {
   double rho[64];                      // rho of each held entry, by FIFO position
   int len[64];                         // support size of each ring slot
   int rslot[64];                       // ring slots of the retrieved entries, best first
+  int moff[65];                        // merged union: start of each retrieved list's part below the window
   __align__(16) int whist[kHeadThreads / 64][256];   // one radix histogram per wave
   int tmp[32];
   __align__(16) float red[kHeadThreads / 16][kHeadDim + 4];  // one row per 16-lane row group
@@ -972,6 +973,144 @@ __device__ __forceinline__ void cand_scores(const uint16_t* kb, const int32_t* s
   }
 }
 constexpr int kDenseWords = kHeadThreads / 4;  // bitmap words emitted a byte per thread (4096 positions)
+constexpr int kMergeR = 8;                      // retrieved lists the merged union takes
+constexpr int kMergeE = 4;                      // entries per thread: R K <= 4 * 512
+
+// Candidate union (Eqs. 8-9) below the window by merging the retrieved
+// supports, each held in ascending order (the cache's canonical form): its
+// cost depends on R K, not on the context length (one LDS bitmap window
+// covers 262144 positions; longer contexts would need a sweep per window).
+// The n_ret <= kMergeR lists are staged in LDS (lists, K ints each) and cut
+// at the first entry >= wlo (the window [wlo, L) is appended after; entries
+// past the visible length lie beyond it too). Each thread takes up to kMergeE
+// consecutive entries and finds, for each entry x and each list, the number
+// of that list's entries below x: all these searches advance together, one
+// power-of-two step per round. An entry is kept unless a lower-numbered list
+// holds x; its place in the output is the sum over the lists of the kept
+// entries below x (a prefix count of the kept flags, pre). Writes the
+// distinct positions ascending to out and returns their number. Requires
+// n_ret * K <= kMergeE * 512. Every thread of the block must call it.
+__device__ __forceinline__ int union_merge(const Dims& d, ConstBufs& b, int bh, int n_ret, int wlo, int32_t* out,
+                                           int* lists, int* pre, HeadShared& sh) {
+  const int tid = threadIdx.x;
+  for (int j0 = 0; j0 < d.K; j0 += blockDim.x) {
+    const int j = j0 + tid;
+    for (int r0 = 0; r0 < n_ret; r0 += 4) {
+      int x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = min(r0 + u, n_ret - 1);  // clamped: a valid address, not stored when out of range
+        x[u] = b.cache_supp[(static_cast<long>(bh) * d.C + sh.rslot[r]) * d.K + min(j, d.K - 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = r0 + u;
+        if (r < n_ret && j < sh.len[sh.rslot[min(r, n_ret - 1)]]) lists[r * d.K + j] = x[u];
+      }
+    }
+  }
+  lds_barrier();
+  // list r (lane r of wave 0): its entries below wlo, then their offsets
+  if (tid < 64) {
+    const int len = tid < n_ret ? sh.len[sh.rslot[tid]] : 0;
+    const int* L = lists + min(tid, n_ret - 1) * d.K;
+    int cut = 0;
+    for (int st = kHeadThreads * kMergeE; st > 0; st >>= 1) {
+      const int c = cut + st;
+      const int x = L[max(min(c, len) - 1, 0)];
+      cut = (c <= len && x < wlo) ? c : cut;
+    }
+    const int incl = wave_incl_scan(cut);
+    if (tid < n_ret) sh.moff[tid + 1] = incl;
+    if (tid == 0) sh.moff[0] = 0;
+  }
+  lds_barrier();
+  int nmax = 0;
+  for (int r = 0; r < n_ret; ++r) nmax = max(nmax, sh.moff[r + 1] - sh.moff[r]);
+  const int F = sh.moff[n_ret];
+  const int f0 = min(tid * kMergeE, F);
+  int xe[kMergeE], re[kMergeE];
+  {
+    int r = 0;
+#pragma unroll
+    for (int e = 0; e < kMergeE; ++e) {
+      const int f = min(f0 + e, max(F - 1, 0));
+      while (r + 1 < n_ret && sh.moff[r + 1] <= f) ++r;
+      re[e] = r;
+      xe[e] = F > 0 ? lists[r * d.K + (f - sh.moff[r])] : 0;
+    }
+  }
+  // lb[e][r2]: entries of list r2 below xe[e]
+  int lb[kMergeE][kMergeR];
+#pragma unroll
+  for (int e = 0; e < kMergeE; ++e)
+#pragma unroll
+    for (int r2 = 0; r2 < kMergeR; ++r2) lb[e][r2] = 0;
+  int step = 1;
+  while (step * 2 <= nmax) step *= 2;
+  int nl[kMergeR];
+#pragma unroll
+  for (int r2 = 0; r2 < kMergeR; ++r2) nl[r2] = r2 < n_ret ? sh.moff[r2 + 1] - sh.moff[r2] : 0;
+  // (every read is issued unconditionally at a clamped, valid index, so that
+  // a round's reads are all in flight together)
+  for (; step > 0; step >>= 1) {
+    int v[kMergeE][kMergeR];
+#pragma unroll
+    for (int r2 = 0; r2 < kMergeR; ++r2) {
+      if (r2 >= n_ret) break;  // uniform
+#pragma unroll
+      for (int e = 0; e < kMergeE; ++e)
+        v[e][r2] = lists[r2 * d.K + max(min(lb[e][r2] + step, nl[r2]) - 1, 0)];
+    }
+#pragma unroll
+    for (int r2 = 0; r2 < kMergeR; ++r2) {
+      if (r2 >= n_ret) break;
+#pragma unroll
+      for (int e = 0; e < kMergeE; ++e)
+        lb[e][r2] = (lb[e][r2] + step <= nl[r2] && v[e][r2] < xe[e]) ? lb[e][r2] + step : lb[e][r2];
+    }
+  }
+  uint32_t keep = 0u;
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < kMergeE; ++e) {
+    bool dup = f0 + e >= F;
+#pragma unroll
+    for (int r2 = 0; r2 < kMergeR - 1; ++r2) {
+      if (r2 >= n_ret - 1) break;  // (the last list is never below another)
+      const int at = lists[r2 * d.K + min(lb[e][r2], max(nl[r2] - 1, 0))];
+      dup = dup || (r2 < re[e] && lb[e][r2] < nl[r2] && at == xe[e]);
+    }
+    if (!dup) {
+      keep |= 1u << e;
+      ++cnt;
+    }
+  }
+  int total;
+  int run = block_exclusive_scan(cnt, &total, sh.tmp);
+#pragma unroll
+  for (int e = 0; e < kMergeE; ++e) {
+    if (f0 + e < F) pre[f0 + e] = run;
+    run += (keep >> e) & 1u;
+  }
+  if (tid == 0) pre[F] = total;
+  lds_barrier();
+#pragma unroll
+  for (int e = 0; e < kMergeE; ++e) {
+    if (!((keep >> e) & 1u)) continue;
+    int pos = 0;
+#pragma unroll
+    for (int r2 = 0; r2 < kMergeR; ++r2) {
+      if (r2 >= n_ret) break;
+      const int o2 = sh.moff[r2];
+      // (an entry's own list: lb is its index there, as the list is ascending)
+      pos += pre[o2 + lb[e][r2]] - pre[o2];
+    }
+    out[pos] = xe[e];
+  }
+  lds_barrier();
+  return total;
+}
 
 // Bring all four 64-byte lines of the buffer table into the scalar cache at
 // once. The head role reads its pointers from the table where it needs them,
@@ -1146,7 +1285,11 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
   // are already covered).
   const int wlo = max(0, length - d.W);
   int M = 0;
-  for (int base = 0; base < wlo; base += kBitmapWords * 32) {
+  // positions beyond one bitmap window: merge the sorted supports instead of
+  // sweeping window after window
+  const bool merged = wlo > kBitmapWords * 32 && n_ret <= kMergeR && n_ret * d.K <= kMergeE * kHeadThreads;
+  if (merged) M = union_merge(d, b, bh, n_ret, wlo, s_cand, reinterpret_cast<int*>(s_sc), reinterpret_cast<int*>(dyn), sh);
+  for (int base = 0; !merged && base < wlo; base += kBitmapWords * 32) {
     const int nbits = min(kBitmapWords * 32, wlo - base);
     const int nwords = (nbits + 31) >> 5;
     if (base > 0) {
