@@ -84,6 +84,8 @@ def parse():
                          "profiles/kernels_<workload>.md and exit")
     ap.add_argument("--json-out", metavar="FILE", default=None,
                     help="also write the result line to FILE (counter runs keep it beside their counters)")
+    ap.add_argument("--profile-tag", default="",
+                    help="with --summarize-kernels: suffix of the summary's file name (e.g. _20steps)")
     ap.add_argument("--last", type=int, default=64,
                     help="with --summarize-traffic / --summarize-kernels: dispatches per kernel to "
                          "average (the last ones, i.e. the timed steps)")
@@ -251,7 +253,7 @@ LEG_TITLES = {"natural": "natural ReTopK decode steps (the metric's step)",
               "dense": "dense softmax attention over every key (retopk_dense_attn)"}
 
 
-def summarize_kernels(root, last, workload, warmup=64):
+def summarize_kernels(root, last, workload, warmup=64, tag=""):
     """Per-kernel durations of the timed dispatches (the last `last` of each
     library kernel) from rocprofv3 kernel traces, plus the whole-run --stats
     rows; written to profiles/kernels_<workload>.md."""
@@ -314,7 +316,7 @@ def summarize_kernels(root, last, workload, warmup=64):
                              f"{float(r['MinNs']) / 1000:.2f} | {float(r['MaxNs']) / 1000:.2f} | "
                              f"{float(r['Percentage']):.1f} |")
         lines.append("")
-    path = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}{tag}.md")
     with open(path, "w") as fh:
         fh.write("\n".join(lines))
     print(f"wrote {path}")
@@ -399,7 +401,7 @@ def main():
         summarize_traffic(args.summarize_traffic, args.last, args.workload)
         return
     if args.summarize_kernels:
-        summarize_kernels(args.summarize_kernels, args.last, args.workload, args.warmup)
+        summarize_kernels(args.summarize_kernels, args.last, args.workload, args.warmup, args.profile_tag)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path has no "
