@@ -66,7 +66,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--token-layers", type=int, default=28,
                     help="layers of the graph-replayed decode token leg (0 skips it)")
-    ap.add_argument("--only", choices=list(LEGS) + ["fidelity", "stream", "ablation", "token"], default=None,
+    ap.add_argument("--only", choices=list(LEGS) + ["fidelity", "stream", "scoreab", "ablation", "token"],
+                    default=None,
                     help="run one timed leg only (for profiler runs)")
     ap.add_argument("--fidelity-steps", type=int, default=32,
                     help="decode steps of the support-fidelity leg (0 skips it)")
@@ -760,6 +761,10 @@ def main():
             if key in result:
                 result[key]["frac_of_stream_read"] = round(result[key]["achieved"] / gbs, 4)
 
+    # --- the score pass on matrix cores against the vector ALUs --------------
+    if args.only in (None, "scoreab"):
+        result["score_unit_ab"] = score_unit_ab(B, torch, ks[0], q_dec, stream)
+
     # --- CPU oracle baseline ------------------------------------------------
     if not args.no_cpu_baseline and args.only in (None, "natural"):
         result["cpu_baseline"] = cpu_baseline(wl, data, init_state, args.cpu_seconds)
@@ -869,6 +874,39 @@ def stream_read(B, torch, dev, stream):
     del buf
     return {"kernel": "k_stream_read", "bytes": 1 << 30, "us_per_launch": round(best * 1000, 2),
             "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def score_unit_ab(B, torch, k, q_dec, stream):
+    """The full-history score pass of one call (7 query heads per KV head,
+    every key row of batch entry 0) as the library's score probe runs it on
+    MFMA and on the vector ALUs: best of three batches of ten launches each,
+    alternating, HIP events on the launch stream."""
+    rows = k[0].reshape(-1, 128)
+    q = q_dec[0, 0, :7].contiguous()
+    sink = torch.zeros(1, dtype=torch.float32, device=k.device)
+    best = {1: None, 0: None}
+    for _ in range(3):
+        B.retopk_score_probe(1, rows, q, sink, stream)
+        B.retopk_score_probe(0, rows, q, sink, stream)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for mode in (1, 0):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(10):
+                B.retopk_score_probe(mode, rows, q, sink, stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / 10
+            best[mode] = ms if best[mode] is None else min(best[mode], ms)
+    nbytes = rows.shape[0] * 256
+    res = {"rows": int(rows.shape[0]), "bytes": nbytes, "query_heads": 7}
+    for mode, name in ((1, "mfma"), (0, "valu")):
+        res[f"{name}_us"] = round(best[mode] * 1000, 2)
+        res[f"{name}_gbs"] = round(nbytes / (best[mode] * 1e-3) / 1e9, 1)
+    log(f"score pass A/B: MFMA {res['mfma_us']} us, VALU {res['valu_us']} us over {res['rows']} rows")
+    return res
 
 
 def _cos(a, b):

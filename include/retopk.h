@@ -45,6 +45,19 @@
  *   itself appear at the next synchronising call. A handle must be used from
  *   one host thread and one stream at a time; calls that overlap on one
  *   handle race.
+ * Co-residency. retopk_decode_step, retopk_exact_topk_attn and
+ *   retopk_init_from_prefill are each one kernel launch whose work groups hand
+ *   results to one another through device memory: the work groups of an
+ *   exact KV group wait for each other's scores and survivors. The grid is
+ *   sized so that all of them fit on the device at once (at most one
+ *   work group per compute unit besides the head work groups, which never
+ *   wait), which holds when nothing else runs on the GPU during the call.
+ *   Work on other streams or from other processes that holds compute units
+ *   meanwhile can keep some work groups from starting; every wait is bounded
+ *   (about 200 ms), so the call still ends, but then its exact heads are not
+ *   finished, their outputs and cache entries are not valid and the sticky
+ *   device error word is set (retopk_read_device_error). Callers that must
+ *   share the GPU check that word after the steps they need to trust.
  * Errors. Every entry point returns a retopk_status. Arguments are checked
  *   before any device work is enqueued; on error nothing is enqueued and the
  *   handle's state is unchanged. retopk_last_error() gives a message for the
@@ -313,6 +326,21 @@ const char* retopk_kernel_name(int32_t id);
  * RETOPK_INVALID_ARG for a NULL or misaligned pointer or a bad size,
  * RETOPK_HIP_ERROR when the launch fails. */
 retopk_status retopk_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
+/* Measurement aid, not part of the method: the full-history score pass of
+ * one KV group, q.k of 7 query heads (q: 7 rows of 128 bf16) against n_rows
+ * key rows (k: [n_rows, 128] bf16, row-major), written once on the matrix
+ * cores (use_mfma = 1: 16x16x32 bf16 MFMA tiles) and once on the vector ALUs
+ * (use_mfma = 0: bf16 pair dot products), with the same row streaming and
+ * grid (one work group per compute unit); the scores are reduced to a
+ * running maximum and not stored. Times the choice of unit for the scoring
+ * inner loop of retopk_exact_topk_attn. sink is one device float the kernel
+ * may write. Uses the current device; asynchronous on `stream`. Errors:
+ * RETOPK_INVALID_ARG for a NULL or misaligned pointer or use_mfma not 0/1,
+ * RETOPK_OUT_OF_RANGE for n_rows outside 1 .. 2^30, RETOPK_HIP_ERROR when the launch
+ * fails. */
+retopk_status retopk_score_probe(int32_t use_mfma, const uint16_t* k, int64_t n_rows, const uint16_t* q,
+                                 float* sink, void* stream);
 
 /* Bytes of device memory the handle holds. */
 size_t retopk_device_bytes(const retopk_handle* h);

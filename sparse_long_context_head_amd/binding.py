@@ -63,6 +63,7 @@ _SIGNATURES = {
     "retopk_device_bytes": (ctypes.c_size_t, [_P]),
     "retopk_read_device_error": (ctypes.c_int, [_P, _P]),
     "retopk_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
+    "retopk_score_probe": (ctypes.c_int, [ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P]),
     "retopk_dense_attn_noalloc": (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P, _P]),
     "retopk_group_create": (ctypes.c_int, [ctypes.POINTER(RetopkParams), _I32, ctypes.POINTER(_P)]),
     "retopk_group_destroy": (None, [_P]),
@@ -387,6 +388,21 @@ def retopk_stream_read(buf, sink, stream=None):
         raise ValueError("buf and sink must be device tensors")
     _check(load_library().retopk_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                              _stream(stream, buf.device)))
+
+
+def retopk_score_probe(use_mfma, k, q, sink, stream=None):
+    """One score pass of 7 query heads (q [7, 128] bf16) over every row of
+    k [n, 128] bf16, on MFMA or on the vector ALUs (measurement aid)."""
+    if not (k.is_cuda and q.is_cuda and sink.is_cuda):
+        raise ValueError("k, q and sink must be device tensors")
+    if k.dim() != 2 or k.shape[1] != 128 or tuple(q.shape) != (7, 128):
+        raise ValueError("k must be [n, 128] and q [7, 128]")
+    if k.dtype != q.dtype or k.element_size() != 2 or sink.dtype.itemsize != 4:
+        raise ValueError("k and q must be 2-byte (bf16) tensors, sink a 4-byte one")
+    if not (k.is_contiguous() and q.is_contiguous()):
+        raise ValueError("k and q must be contiguous")
+    _check(load_library().retopk_score_probe(int(use_mfma), _ptr(k), k.shape[0], _ptr(q), _ptr(sink),
+                                             _stream(stream, k.device)))
 
 
 def bf16_tensor(bits: np.ndarray, device="cuda"):

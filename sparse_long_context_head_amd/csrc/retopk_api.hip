@@ -691,6 +691,24 @@ retopk_status retopk_stream_read(const void* buf, size_t bytes, uint32_t* sink, 
   return e == hipSuccess ? RETOPK_OK : hip_fail(e, "retopk_stream_read");
 }
 
+retopk_status retopk_score_probe(int32_t use_mfma, const uint16_t* k, int64_t n_rows, const uint16_t* q,
+                                float* sink, void* stream) {
+  if (k == nullptr || q == nullptr || sink == nullptr)
+    return fail(RETOPK_INVALID_ARG, "retopk_score_probe: NULL pointer");
+  if (use_mfma != 0 && use_mfma != 1) return fail(RETOPK_INVALID_ARG, "retopk_score_probe: use_mfma must be 0 or 1");
+  if (n_rows < 1 || n_rows > (int64_t(1) << 30))
+    return fail(RETOPK_OUT_OF_RANGE, "retopk_score_probe: n_rows out of range");
+  if (!aligned(k, 16) || !aligned(q, 16) || !aligned(sink, 4))
+    return fail(RETOPK_INVALID_ARG, "retopk_score_probe: k and q must be 16-byte aligned");
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+    return fail(RETOPK_NO_DEVICE, "retopk_score_probe: no usable device");
+  const hipError_t e = launch_score_probe(use_mfma, k, static_cast<long>(n_rows), q, sink, n_cu,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? RETOPK_OK : hip_fail(e, "retopk_score_probe");
+}
+
 retopk_status retopk_read_state(retopk_handle* h, float* qbar, int32_t* supp, int32_t* supp_len,
                                 int32_t* count) {
   if (h == nullptr) return fail(RETOPK_NOT_INITIALIZED, "retopk_read_state: NULL handle");

@@ -136,4 +136,8 @@ hipError_t launch_dense(const Dims& d, const uint16_t* q, const uint16_t* k, con
 
 // Plain streaming read of `bytes` (a multiple of 16) at buf (retopk_probe.hip).
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int n_cu, hipStream_t s);
+// Score pass of 7 query heads over n_rows key rows, on MFMA (use_mfma) or on
+// the vector ALUs (retopk_probe.hip); q holds 7 rows of kHeadDim bf16.
+hipError_t launch_score_probe(int use_mfma, const uint16_t* k, long n_rows, const uint16_t* q, float* sink, int n_cu,
+                              hipStream_t s);
 }  // namespace retopk

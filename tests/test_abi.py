@@ -99,6 +99,8 @@ def test_null_handle_calls_fail_cleanly():
     # the streaming-read probe checks its arguments before touching a device
     assert lib.retopk_stream_read(None, 16, None, None) == 1
     assert b"NULL pointer" in lib.retopk_last_error()
+    assert lib.retopk_score_probe(1, None, 16, None, None, None) == 1
+    assert b"NULL pointer" in lib.retopk_last_error()
     lib.retopk_destroy(None)
     out = ctypes.c_void_p()
     assert lib.retopk_create(None, ctypes.byref(out)) == 1 and out.value is None
