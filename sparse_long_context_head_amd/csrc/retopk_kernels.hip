@@ -929,7 +929,7 @@ __device__ __forceinline__ void qk_score(const QkTiles& t, const bf16x8 (&bq)[4]
 //     bits of an LDS bitmap over token positions (windows of 262144), read
 //     back in ascending order -> A_t, M_t;
 //   scores (Eq. 10): q . k_i for i in A_t straight from the KV cache, 16 lanes
-//     per key row, 20 rows in flight per thread, bf16 pair products with fp32
+//     per key row, 18 rows in flight per 16-lane group, bf16 pair products with fp32
 //     accumulation;
 //   rerank (Eq. 11): a pass over scores binned linearly between their minimum
 //     and maximum finds the bin of the K-th largest, whose entries are ranked

@@ -52,7 +52,8 @@ hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int
 // on the vector ALUs. Each work group of 8 waves takes a contiguous slice of
 // rows; a wave reads 16-row tiles (a lane holds 16 bytes of four 64-byte
 // column chunks of one row), two register stages of 4 tiles per wave in
-// flight. The matrix form multiplies each tile by the queries in a
+// flight (scheduling barriers keep the compiler from sinking the next stage's
+// loads down to their use, which it otherwise does in the matrix form). The matrix form multiplies each tile by the queries in a
 // 16x16x32 bf16 MFMA (query heads as the 16 columns, 7 used); the vector form
 // keeps each lane's 32 query dimensions per head in registers and takes 16
 // bf16 pair dot products per head and row, then sums the four lanes of a row
@@ -116,9 +117,11 @@ __global__ __launch_bounds__(kQThreads) void k_score_probe(const uint16_t* __res
     q_stage_load(ta, k, row0, rend, wave, j, kq);
     for (int t0 = row0; t0 < rend; t0 += 2 * kQRowsPerStage) {
       q_stage_load(tb, k, t0 + kQRowsPerStage, rend, wave, j, kq);
+      __builtin_amdgcn_sched_barrier(0);  // the next stage's loads stay ahead of this stage's math
       score(ta);
       if (t0 + kQRowsPerStage >= rend) break;
       q_stage_load(ta, k, t0 + 2 * kQRowsPerStage, rend, wave, j, kq);
+      __builtin_amdgcn_sched_barrier(0);
       score(tb);
     }
   } else {
@@ -159,9 +162,11 @@ __global__ __launch_bounds__(kQThreads) void k_score_probe(const uint16_t* __res
     q_stage_load(ta, k, row0, rend, wave, j, kq);
     for (int t0 = row0; t0 < rend; t0 += 2 * kQRowsPerStage) {
       q_stage_load(tb, k, t0 + kQRowsPerStage, rend, wave, j, kq);
+      __builtin_amdgcn_sched_barrier(0);  // the next stage's loads stay ahead of this stage's math
       score(ta);
       if (t0 + kQRowsPerStage >= rend) break;
       q_stage_load(ta, k, t0 + 2 * kQRowsPerStage, rend, wave, j, kq);
+      __builtin_amdgcn_sched_barrier(0);
       score(tb);
     }
   }
