@@ -777,6 +777,9 @@ size_t finish_lds_bytes(const Dims& d) {
          8 * static_cast<size_t>(d.K);
 }
 
+constexpr long kLongShare = 8192;  // key rows per score work group from which exact calls take every CU
+constexpr int kKbDecodeLen = 1 << 21;  // visible keys from which decode steps use the K-best variant
+
 int score_grid(const Dims& d, int length, int mode, bool wide) {
   // One 512-thread work group per CU beside the head work groups, so that all
   // are resident at once and none starts late (a reuse head's work group holds
@@ -789,7 +792,10 @@ int score_grid(const Dims& d, int length, int mode, bool wide) {
   // the CUs, so that all score work groups, which wait for one another, can be
   // resident together.
   const long bh = static_cast<long>(d.B) * d.Hq;
-  const bool all_cu = (mode == kModeExact || wide) && bh >= d.n_cu / 8;
+  // (an exact call whose share per work group is long: the head work groups'
+  // CUs are free within a few us, and the scan then gains their bandwidth)
+  const long share = static_cast<long>(d.B) * d.Hkv * length / std::max<long>(1, d.n_cu - bh);
+  const bool all_cu = ((mode == kModeExact || wide) && bh >= d.n_cu / 8) || (mode == kModeExact && share >= kLongShare);
   const long free_cu = all_cu ? d.n_cu : std::max<long>(d.n_cu - bh, d.n_cu / 2);
   const long cap = std::min<long>(free_cu, kHeadThreads);
   const long groups = static_cast<long>(d.B) * d.Hkv;
@@ -1614,6 +1620,466 @@ __device__ __forceinline__ void emit_segment(const Dims& d, const BufsDev& b, in
 }
 
 // ---------------------------------------------------------------------------
+// Long histories: per-segment K-best lists instead of stored scores.
+//
+// When a score work group's share of rows does not fit its LDS as scores, it
+// keeps, per exact head of each of its segments, only the entries that can
+// still be among the segment's K best: a key outside its own segment's K best
+// cannot be among the K best of the whole history (the segment alone holds K
+// better ones). Entries are (score bits, row) in LDS, admitted when their
+// composite key (ordered score << 32 | ~row: higher score first, then lower
+// row; all keys distinct) reaches the head's admission threshold. Each stage's
+// admitted entries are placed in row order (a scan of per-tile counts), so a
+// list is always sorted by row. When a head's list could overflow during the
+// next stage, one wave cuts it (in place, in order) to the entries at or above
+// a new threshold that keeps at least its K best: a 256-bin histogram of the
+// 8 key bits just below the keys' common prefix, refined 8 bits further while
+// the kept count would still leave no room. At the end of a segment each list
+// is cut to at most the next power of two >= K entries and moved to that
+// stride, and only its entries enter the call's score histogram: the K best
+// of the union of all lists are the K best of the history, so the boundary
+// bin b1, the counts above and in it, and the survivors (list entries in b1
+// or above, already in position order) are those of the full history.
+// ---------------------------------------------------------------------------
+constexpr int kKbSlack = 1024;   // list room beyond K: the next stage's arrivals never overflow it
+constexpr int kKbCutSlack = 64;  // a cut during the scan keeps at most K + this many entries
+// Rows per score work group from which the lists beat stored scores (below,
+// the stored scores' write and re-read cost less than the lists' per-stage
+// ordering, cuts and histogram)
+constexpr long kKbMinShare = 8192;
+constexpr int kKbMaxSeg = 2;    // segments per work group the lists are kept for (else stored scores)
+constexpr int kKbTc = 16 * kQkUnroll * (kHeadThreads / kWave) / 4;  // (tile, row quad) slots per head and stage
+
+__device__ __forceinline__ uint64_t kb_key(uint2 e) {
+  return (static_cast<uint64_t>(order_key(__uint_as_float(e.x))) << 32) | static_cast<uint64_t>(0xffffffffu - e.y);
+}
+
+__host__ __device__ inline int kb_stride(int K) {
+  int p = 1;
+  while (p < K) p <<= 1;
+  return p;
+}
+
+// Dynamic LDS of the K-best path: two stages' tile counts, then the lists.
+__host__ __device__ inline long kb_tc_bytes(const Dims& d) { return (8L * d.G * kKbTc + 15) / 16 * 16; }
+
+// Entries per head of segment si's working list (after the finished lists of
+// segments 0 .. si-1).
+__host__ __device__ inline int kb_cap(const Dims& d, int si) {
+  const long list_bytes = 8L * d.G * kb_stride(d.K);
+  return static_cast<int>((kLdsLimit - kb_tc_bytes(d) - si * list_bytes) / (8L * d.G));
+}
+
+// Whether a work group with nseg non-empty segments keeps K-best lists: each
+// segment's working list holds K + kKbSlack entries per head, and the
+// histogram of the last one fits after the finished lists.
+__host__ __device__ inline bool kb_fits(const Dims& d, int nseg) {
+  if (nseg < 1 || nseg > kKbMaxSeg) return false;
+  for (int si = 0; si < nseg; ++si)
+    if (kb_cap(d, si) < d.K + kKbSlack) return false;
+  return kb_tc_bytes(d) + static_cast<long>(nseg) * 8L * d.G * kb_stride(d.K) + 4L * d.G * kNumBins <= kLdsLimit;
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t y = static_cast<uint64_t>(__shfl_xor(static_cast<long long>(x), o));
+    x = y < x ? y : x;
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t y = static_cast<uint64_t>(__shfl_xor(static_cast<long long>(x), o));
+    x = y > x ? y : x;
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = min(x, static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), o)));
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = max(x, static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), o)));
+  return x;
+}
+
+// The cut below on the scores' ordered keys alone (32 bits), which is what
+// separates entries unless scores tie: entries with equal scores are kept or
+// dropped together. Returns false, with buf untouched, when ties leave more
+// than `limit` entries at the finest score resolution (the caller then cuts on
+// the full composite keys); else cuts, sets *theta (a composite-key
+// threshold) and *n_out.
+__device__ __forceinline__ bool kb_cut32(uint2* buf, int n, int k, int limit, int* bins, uint64_t* theta,
+                                         int* n_out) {
+  const int lane = threadIdx.x & 63;
+  constexpr int U = 8;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int c0 = 0; c0 < n; c0 += 64 * U) {
+    uint32_t x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = buf[min(c0 + 64 * u + lane, n - 1)].x;  // (clamped repeats change nothing)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t ok = order_key(__uint_as_float(x[u]));
+      lo = min(lo, ok);
+      hi = max(hi, ok);
+    }
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lo == hi) return false;
+  const int hb = 31 - __clz(static_cast<int>(lo ^ hi));
+  int shift = max(hb - 7, 0), width = min(hb + 1, 8);
+  uint32_t mask = hb >= 31 ? 0u : ~0u << (hb + 1);
+  uint32_t pre = lo & mask;
+  int need = k, kept = 0;
+  for (;;) {
+    const uint32_t dm = (1u << width) - 1u;
+    reinterpret_cast<int4*>(bins)[lane] = make_int4(0, 0, 0, 0);
+    for (int c0 = 0; c0 < n; c0 += 64 * U) {
+      uint32_t x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = buf[min(c0 + 64 * u + lane, n - 1)].x;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t ok = order_key(__uint_as_float(x[u]));
+        if (c0 + 64 * u + lane < n && (ok & mask) == pre) atomicAdd(&bins[(ok >> shift) & dm], 1);
+      }
+    }
+    const int4 h = reinterpret_cast<const int4*>(bins)[63 - lane];
+    const int c[4] = {h.w, h.z, h.y, h.x};
+    const int s4 = c[0] + c[1] + c[2] + c[3];
+    const int incl = wave_incl_scan(s4);
+    int run = incl - s4;
+    int dg = -1, above = 0, cnt = 0;
+    if (run < need && incl >= need) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (dg < 0 && run + c[j] >= need) {
+          dg = 255 - 4 * lane - j;
+          above = run;
+          cnt = c[j];
+        }
+        run += c[j];
+      }
+    }
+    const uint64_t m = __ballot(dg >= 0);
+    const int src = m ? __ffsll(static_cast<long long>(m)) - 1 : 0;
+    dg = __builtin_amdgcn_readlane(dg, src);
+    above = __builtin_amdgcn_readlane(above, src);
+    cnt = __builtin_amdgcn_readlane(cnt, src);
+    if (dg < 0) return false;  // (cannot happen: the window's entries always cover need)
+    pre |= static_cast<uint32_t>(dg) << shift;
+    mask |= dm << shift;
+    kept += above;
+    need -= above;
+    if (kept + cnt <= limit) break;
+    if (shift == 0) return false;
+    width = min(shift, 8);
+    shift -= width;
+  }
+  int run = 0;
+  for (int c0 = 0; c0 < n; c0 += 64 * U) {
+    uint2 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = buf[min(c0 + 64 * u + lane, n - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool kp = (c0 + 64 * u + lane < n) && (order_key(__uint_as_float(x[u].x)) & mask) >= pre;
+      const uint64_t b = __ballot(kp);
+      if (kp) buf[run + lanes_below(b)] = x[u];
+      run += __popcll(b);
+    }
+  }
+  *n_out = run;
+  *theta = static_cast<uint64_t>(pre) << 32;
+  return true;
+}
+
+// The cut of a list: on the scores, else on the composite keys.
+__device__ __forceinline__ uint64_t kb_cut_list(uint2* buf, int n, int k, int limit, int* bins, int* n_out);
+
+// One wave: cut buf[0, n) (n > limit >= k, keys distinct) in place and in
+// order to the entries whose key reaches a threshold that keeps at least the
+// k largest and at most `limit` of them; returns the threshold and the kept
+// count (*n_out). bins: 256 ints of this wave's own LDS.
+__device__ __forceinline__ uint64_t kb_cut(uint2* buf, int n, int k, int limit, int* bins, int* n_out) {
+  const int lane = threadIdx.x & 63;
+  constexpr int U = 8;
+  uint64_t lo = ~0ull, hi = 0ull;
+  for (int c0 = 0; c0 < n; c0 += 64 * U) {
+    uint2 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = buf[min(c0 + 64 * u + lane, n - 1)];  // (clamped repeats change nothing)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t key = kb_key(x[u]);
+      lo = key < lo ? key : lo;
+      hi = key > hi ? key : hi;
+    }
+  }
+  lo = wave_min_u64(lo);
+  hi = wave_max_u64(hi);
+  // the first digit: the 8 bits whose top one is the highest bit where keys differ
+  const int hb = 63 - __clzll(static_cast<long long>(lo ^ hi));
+  int shift = max(hb - 7, 0), width = min(hb + 1, 8);
+  uint64_t mask = hb >= 63 ? 0ull : ~0ull << (hb + 1);
+  uint64_t pre = lo & mask;
+  int need = k, kept = 0;
+  for (;;) {
+    const uint64_t dm = (1ull << width) - 1;
+    reinterpret_cast<int4*>(bins)[lane] = make_int4(0, 0, 0, 0);
+    for (int c0 = 0; c0 < n; c0 += 64 * U) {
+      uint2 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = buf[min(c0 + 64 * u + lane, n - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t key = kb_key(x[u]);
+        if (c0 + 64 * u + lane < n && (key & mask) == pre) atomicAdd(&bins[(key >> shift) & dm], 1);
+      }
+    }
+    // lane l owns digits 255-4l .. 252-4l (digits above dm are empty)
+    const int4 h = reinterpret_cast<const int4*>(bins)[63 - lane];
+    const int c[4] = {h.w, h.z, h.y, h.x};
+    const int s4 = c[0] + c[1] + c[2] + c[3];
+    const int incl = wave_incl_scan(s4);
+    int run = incl - s4;
+    int dg = -1, above = 0, cnt = 0;
+    if (run < need && incl >= need) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (dg < 0 && run + c[j] >= need) {
+          dg = 255 - 4 * lane - j;
+          above = run;
+          cnt = c[j];
+        }
+        run += c[j];
+      }
+    }
+    const uint64_t m = __ballot(dg >= 0);
+    const int src = m ? __ffsll(static_cast<long long>(m)) - 1 : 0;
+    dg = __builtin_amdgcn_readlane(dg, src);
+    above = __builtin_amdgcn_readlane(above, src);
+    cnt = __builtin_amdgcn_readlane(cnt, src);
+    if (dg < 0) break;  // (cannot happen: the window's entries always cover need)
+    pre |= static_cast<uint64_t>(dg) << shift;
+    mask |= dm << shift;
+    kept += above;
+    need -= above;
+    if (kept + cnt <= limit || shift == 0) break;
+    width = min(shift, 8);
+    shift -= width;
+  }
+  int run = 0;
+  for (int c0 = 0; c0 < n; c0 += 64 * U) {
+    uint2 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = buf[min(c0 + 64 * u + lane, n - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool kp = (c0 + 64 * u + lane < n) && (kb_key(x[u]) & mask) >= pre;
+      const uint64_t b = __ballot(kp);
+      if (kp) buf[run + lanes_below(b)] = x[u];
+      run += __popcll(b);
+    }
+  }
+  *n_out = run;
+  return pre;
+}
+
+__device__ __forceinline__ uint64_t kb_cut_list(uint2* buf, int n, int k, int limit, int* bins, int* n_out) {
+  uint64_t th;
+  if (kb_cut32(buf, n, k, limit, bins, &th, n_out)) return th;
+  return kb_cut(buf, n, k, limit, bins, n_out);
+}
+
+// One stage of scores (as qk_score) into the K-best lists, in row order:
+//  1. every lane with an exact head j counts, per tile, its four rows whose
+//     keys reach theta and writes the count to the stage's slot table;
+//  2. a wave per head scans the head's table (slot order = row order) into
+//     list positions and moves the head's length on;
+//  3. the lanes write their entries;
+//  4. when a head's list could overflow during the next stage, its wave cuts
+//     it and raises its threshold.
+// tc: this stage's table (the other one serves the neighbouring stages, so
+// no barrier is needed between step 3 of one stage and step 1 of the next).
+// Every thread of the block must call it.
+__device__ __forceinline__ void qk_score_kb(const Dims& d, const QkTiles& t, const bf16x8 (&bq)[4], int t0, int rend,
+                                            int wave, int nw, int j, int kq, bool hv, uint64_t& theta, uint2* lists,
+                                            int cap, int* tc, int* s_n, uint64_t* s_theta, int* s_full,
+                                            unsigned emask, HeadShared& sh) {
+  const int lane = threadIdx.x & 63;
+  float sc[kQkUnroll][4];
+  unsigned pass = 0u;
+#pragma unroll
+  for (int u = 0; u < kQkUnroll; ++u) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.a[u][s]), bq[s], acc, 0, 0, 0);
+    const int r = t0 + (u * nw + wave) * 16 + 4 * kq;
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sc[u][e] = acc[e];
+      const uint64_t ck = (static_cast<uint64_t>(order_key(acc[e])) << 32) |
+                          static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(r + e));
+      const bool pe = hv & (r + e < rend) & (ck >= theta);
+      pass |= static_cast<unsigned>(pe) << (4 * u + e);
+      c += pe;
+    }
+    if (hv) tc[j * kKbTc + (u * nw + wave) * 4 + kq] = c;
+  }
+  lds_barrier();
+  const int room = cap - 16 * kQkUnroll * nw;  // a stage adds at most one entry per row
+  for (int jj = wave; jj < d.G; jj += nw) {
+    if (!((emask >> jj) & 1u)) continue;
+    int* row = tc + jj * kKbTc;
+    const int a = row[2 * lane], b2 = row[2 * lane + 1];
+    const int incl = wave_incl_scan(a + b2);
+    const int base = s_n[jj];
+    const int ex = base + incl - a - b2;
+    row[2 * lane] = ex;
+    row[2 * lane + 1] = ex + a;
+    const int n = base + __builtin_amdgcn_readlane(incl, 63);
+    if (lane == 0) {
+      s_n[jj] = n;
+      s_full[jj] = n > room;
+    }
+  }
+  lds_barrier();
+  if (hv && pass) {
+    uint2* buf = lists + static_cast<long>(j) * cap;
+#pragma unroll
+    for (int u = 0; u < kQkUnroll; ++u) {
+      if (!((pass >> (4 * u)) & 0xfu)) continue;
+      int slot = tc[j * kKbTc + (u * nw + wave) * 4 + kq];
+      const int r = t0 + (u * nw + wave) * 16 + 4 * kq;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((pass >> (4 * u + e)) & 1u) {
+          if (slot < cap) buf[slot] = make_uint2(__float_as_uint(sc[u][e]), static_cast<uint32_t>(r + e));
+          ++slot;
+        }
+      }
+    }
+  }
+  bool any = false;
+  for (int jj = 0; jj < d.G; ++jj) any |= s_full[jj] != 0;  // (set before the last barrier; uniform)
+  if (any) {
+    lds_barrier();  // the entries are in
+    for (int jj = wave; jj < d.G; jj += nw) {
+      if (!s_full[jj]) continue;
+      const int n = min(s_n[jj], cap);
+      int kept;
+      const uint64_t th =
+          kb_cut_list(lists + static_cast<long>(jj) * cap, n, d.K, d.K + kKbCutSlack, &sh.whist[wave][0], &kept);
+      if (lane == 0) {
+        s_theta[jj] = th;
+        s_n[jj] = kept;
+        s_full[jj] = 0;
+      }
+    }
+    lds_barrier();
+  }
+  theta = s_theta[j < d.G ? j : 0];
+}
+
+// End of a segment's scan: cut each list to at most kp entries (keeping its
+// K best), move the lists to stride kp (padded with row 0xffffffff), record
+// their lengths, and add their histograms (LDS first) into the call's half of
+// the heads' global histograms. Every thread of the block must call it.
+__device__ __forceinline__ void kb_close(const Dims& d, const BufsDev& b, int bb, int g, unsigned emask, int par,
+                                         uint2* lists, int cap, int kp, int* s_n, int* kcnt, HeadShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  lds_barrier();
+  for (int jj = wave; jj < d.G; jj += nw) {
+    int n = min(s_n[jj], cap);
+    if (n > kp) kb_cut_list(lists + static_cast<long>(jj) * cap, n, d.K, kp, &sh.whist[wave][0], &n);
+    if (lane == 0) kcnt[jj] = n;
+  }
+  lds_barrier();
+  // move: read a chunk into registers, then write it (a destination never
+  // lies past its own source, nor in the source of a later chunk)
+  const int total = d.G * kp;
+  for (int base = 0; base < total; base += 8 * kHeadThreads) {
+    uint2 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int xi = base + u * kHeadThreads + tid;
+      const int jj = xi / kp, i = xi - jj * kp;
+      x[u] = make_uint2(0u, 0xffffffffu);
+      if (xi < total && i < kcnt[jj]) x[u] = lists[static_cast<long>(jj) * cap + i];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int xi = base + u * kHeadThreads + tid;
+      if (xi < total) lists[xi] = x[u];
+    }
+    lds_barrier();
+  }
+  // histograms of the lists (LDS after them), then their non-zero bins
+  uint32_t* hist = reinterpret_cast<uint32_t*>(lists + total);
+  for (int i = tid; i < d.G * kNumBins; i += blockDim.x) hist[i] = 0u;
+  lds_barrier();
+  for (int xi = tid; xi < total; xi += blockDim.x) {
+    const int jj = xi / kp, i = xi - jj * kp;
+    if (i < kcnt[jj]) atomicAdd(&hist[jj * kNumBins + (order_key(__uint_as_float(lists[xi].x)) >> kHistShift)], 1u);
+  }
+  lds_barrier();
+  for (int jj = 0; jj < d.G; ++jj) {
+    if (!((emask >> jj) & 1)) continue;
+    uint32_t* ghist = b.hist + (static_cast<long>(bb * d.Hq + g * d.G + jj) * 2 + par) * kNumBins;
+    for (int i = tid; i < kNumBins; i += blockDim.x) {
+      const uint32_t c = hist[jj * kNumBins + i];
+      if (c) atomicAdd(&ghist[i], c);
+    }
+  }
+}
+
+// Phase 2 from a list (sorted by row): as emit_segment, reading (score, row) entries.
+__device__ __forceinline__ void emit_kb(const Dims& d, const BufsDev& b, int bb, int g, unsigned emask, int row0,
+                                        int length, int w, int par, const uint2* lists, int kp,
+                                        const int* kcnt) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int G = d.G;
+  const int h0 = bb * d.Hq + g * G;
+  for (int jj = wave; jj < G; jj += nw) {
+    if (!((emask >> jj) & 1u)) continue;
+    const int b1 = wave_boundary(b.hist + (static_cast<long>(h0 + jj) * 2 + par) * kNumBins, min(d.K, length)).x;
+    const uint32_t k0 = b1 == kNumBins / 2 ? 0x7fffffffu : static_cast<uint32_t>(b1) << kHistShift;
+    const uint2* list = lists + static_cast<long>(jj) * kp;
+    uint2* region = b.hits + static_cast<long>(h0 + jj) * d.max_len + row0;
+    const int n = kcnt[jj];
+    int run = 0;
+    for (int c0 = 0; c0 < n; c0 += 64 * kEmitU) {
+      uint2 x[kEmitU];
+#pragma unroll
+      for (int u = 0; u < kEmitU; ++u) x[u] = list[min(c0 + 64 * u + lane, max(n - 1, 0))];
+#pragma unroll
+      for (int u = 0; u < kEmitU; ++u) {
+        const int i = c0 + 64 * u + lane;
+        const int sb = static_cast<int>(x[u].x);
+        const bool sv = (i < n) & ((static_cast<uint32_t>(sb) ^ (static_cast<uint32_t>(sb >> 31) | 0x80000000u)) >= k0);
+        const uint64_t m = __ballot(sv);
+        if (sv) store_shared(region + run + lanes_below(m), make_uint2(x[u].y, x[u].x));
+        run += __popcll(m);
+      }
+    }
+    if (lane == 0) store_shared(b.ccnt + static_cast<long>(h0 + jj) * d.n_cu + w, run);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Phase 4 (finish) for head bh of list group e, run by the work group the head
 // belongs to.
 //  1. The survivor counts of the group's segments give each segment's offset
@@ -1803,7 +2269,8 @@ __device__ __forceinline__ void finish_phase(const Dims& d, const BufsDev& b, in
 // w: this score work group's index among the nW of them. all_exact: every
 // head of the call is exact (no flags to wait for). keep: rows per head of
 // LDS for the scores of phase 1 (a multiple of 16; 0: they go to the score
-// workspace).
+// workspace, or, with kLong, into K-best lists where those fit).
+template <bool kLong>
 __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, const uint16_t* q, long q_sb, long q_sh,
                                            const uint16_t* k, const uint16_t* v, float* out, int32_t* sel_out,
                                            int length, int push, int call_flag, int w, int nW, bool all_exact,
@@ -1815,6 +2282,10 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
   __shared__ int s_eg[kMaxExactGroups];  // listed group | its exact heads << 16 (bit jj: head jj of the group)
   __shared__ int s_tmp[8];
   __shared__ uint32_t s_ex[kMaxExactGroups * kMaxGroup / 32];  // exact bit of every head
+  __shared__ int s_kbn[kMaxGroup];                  // K-best lists: entries per head (current segment)
+  __shared__ uint64_t s_kbtheta[kMaxGroup];         // ... admission threshold per head
+  __shared__ int s_kbfull[kMaxGroup];               // ... list to be cut after this stage
+  __shared__ int s_kbcnt[kKbMaxSeg][kMaxGroup];     // ... final length per segment and head
   extern __shared__ __align__(16) unsigned char dyn[];
   // LDS: histograms [G, kNumBins] (phase 1), then the kept scores
   // [G, keep + 4] (phase 1 -> 3); phase 4 reuses all of it
@@ -1886,9 +2357,60 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
   int e0, r0, e1, r1;
   split_at(T, nW, length, ne, w, e0, r0);
   split_at(T, nW, length, ne, w + 1, e1, r1);
+  // long histories: K-best lists when this work group's segments allow them
+  bool use_kb = false;
+  int nseg = 0;
+  if constexpr (kLong) {
+    for (int e = e0, r = r0; e < e1 || (e == e1 && r < r1); ++e, r = 0) nseg += r < (e == e1 ? r1 : length);
+    use_kb = T >= kKbMinShare * nW && kb_fits(d, nseg);
+  }
+  const int kp = kb_stride(d.K);
 
   // ---- phase 1: scores and histograms ----
-  for (int e = e0, r = r0, lb = 0; e < e1 || (e == e1 && r < r1); ++e, r = 0) {
+  if constexpr (kLong) {
+    for (int e = e0, r = r0, si = 0; use_kb && (e < e1 || (e == e1 && r < r1)); ++e, r = 0) {
+      const int row0 = r, rend = e == e1 ? r1 : length;
+      if (row0 >= rend) continue;
+      const int bg = s_eg[e] & 0xffff;
+      const int bb = bg / d.Hkv, g = bg % d.Hkv;
+      const int h = g * d.G + j;
+      const unsigned emask = static_cast<unsigned>(s_eg[e]) >> 16;
+      const bool hv = (j < d.G) && ((emask >> j) & 1u);
+      bf16x8 bq[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint4 u = make_uint4(0u, 0u, 0u, 0u);
+        if (hv) u = *reinterpret_cast<const uint4*>(q + bb * q_sb + h * q_sh + 8 * kq + 32 * s);
+        bq[s] = as_bf16x8(u);
+      }
+      const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
+      QkTiles ta, tb;
+      qk_load(ta, kb, row0, rend, wave, nw, j, kq);
+      const int cap = kb_cap(d, si);
+      int* tc = reinterpret_cast<int*>(dyn);  // two stages' slot tables
+      uint2* lists = reinterpret_cast<uint2*>(dyn + kb_tc_bytes(d)) + static_cast<long>(si) * d.G * kp;
+      if (threadIdx.x < d.G) {
+        s_kbn[threadIdx.x] = 0;
+        s_kbtheta[threadIdx.x] = 0ull;
+        s_kbfull[threadIdx.x] = 0;
+      }
+      lds_barrier();  // (also: the previous segment's histogram is read out)
+      uint64_t theta = 0ull;
+      const int kStage = 16 * kQkUnroll * nw;  // rows per stage
+      for (int t0 = row0; t0 < rend; t0 += 2 * kStage) {
+        qk_load(tb, kb, t0 + kStage, rend, wave, nw, j, kq);
+        qk_score_kb(d, ta, bq, t0, rend, wave, nw, j, kq, hv, theta, lists, cap, tc, s_kbn, s_kbtheta, s_kbfull,
+                    emask, sh);
+        if (t0 + kStage >= rend) break;
+        qk_load(ta, kb, t0 + 2 * kStage, rend, wave, nw, j, kq);
+        qk_score_kb(d, tb, bq, t0 + kStage, rend, wave, nw, j, kq, hv, theta, lists, cap, tc + d.G * kKbTc, s_kbn,
+                    s_kbtheta, s_kbfull, emask, sh);
+      }
+      kb_close(d, b, bb, g, emask, par, lists, cap, kp, s_kbn, s_kbcnt[si], sh);
+      ++si;
+    }
+  }
+  for (int e = e0, r = r0, lb = 0; !use_kb && (e < e1 || (e == e1 && r < r1)); ++e, r = 0) {
     const int row0 = r, rend = e == e1 ? r1 : length;
     if (row0 >= rend) continue;
     const int bg = s_eg[e] & 0xffff;
@@ -1951,12 +2473,17 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
   };
 
   // ---- phase 2: survivors of every segment ----
-  for (int e = e0, r = r0, lb = 0; e < e1 || (e == e1 && r < r1); ++e, r = 0) {
+  for (int e = e0, r = r0, lb = 0, si = 0; e < e1 || (e == e1 && r < r1); ++e, r = 0) {
     const int row0 = r, rend = e == e1 ? r1 : length;
     if (row0 >= rend) continue;
     const int bg = s_eg[e] & 0xffff;
     if (!wait_group(b.wdone, T, nW, length, ne, e, call_flag, b.err, &sh.i3)) return;
-    if (keep > 0)
+    if (use_kb) {
+      emit_kb(d, b, bg / d.Hkv, bg % d.Hkv, static_cast<unsigned>(s_eg[e]) >> 16, row0, length, w, par,
+              reinterpret_cast<const uint2*>(dyn + kb_tc_bytes(d)) + static_cast<long>(si) * d.G * kp, kp,
+              s_kbcnt[si]);
+      ++si;
+    } else if (keep > 0)
       emit_segment<true>(d, b, bg / d.Hkv, bg % d.Hkv, static_cast<unsigned>(s_eg[e]) >> 16, row0, rend, length, w,
                          par, s_sc + lb, stride);
     else
@@ -2001,6 +2528,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
 //   [0, BH)        head work groups (query heads);
 //   [BH, BH + NS)  score work groups (also the exact heads' Top-K and finish).
 // ---------------------------------------------------------------------------
+template <bool kLong>
 __global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, const Bufs* __restrict__ bp, const uint16_t* q, long q_sb, long q_sh,
                                                        const uint16_t* k, const uint16_t* v, float* out,
                                                        int32_t* sel_out, int length, int t_dec, int mode,
@@ -2027,8 +2555,8 @@ __global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, const Bufs* __res
               call_flag, w, sh);
   } else {
     const BufsDev b = *reinterpret_cast<const BufsDev*>(bp);
-    score_role(d, b, q, q_sb, q_sh, k, v, out, sel_out, length, push, call_flag, w - BH, n_score,
-               mode == kModeExact, keep, sh);
+    score_role<kLong>(d, b, q, q_sb, q_sh, k, v, out, sel_out, length, push, call_flag, w - BH, n_score,
+                      mode == kModeExact, keep, sh);
   }
 }
 
@@ -2036,8 +2564,13 @@ __global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, const Bufs* __res
 // Launch helpers
 // ---------------------------------------------------------------------------
 hipError_t configure_kernels(const Dims& d) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_step), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             static_cast<int>(step_lds_bytes(d)));
+  const int lds = static_cast<int>(step_lds_bytes(d));
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_step<false>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_step<true>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            lds);
+  return e;
 }
 
 const char* kernel_name(int id) {
@@ -2057,9 +2590,19 @@ hipError_t launch_step(const Dims& d, const Bufs& b, const uint16_t* q, long q_s
                        int layer) {
   // (a replayed step is sized for `length`, the longest of its replays)
   const int n_score = score_grid(d, length, mode, wide);
-  hipLaunchKernelGGL(k_step, dim3(d.B * d.Hq + n_score), dim3(kHeadThreads), step_lds_bytes(d), s, d, b.self, q, q_sb,
-                     q_sh, k, v, out, sel_out, length, t_dec, mode, stats_slot, push, call_flag, n_score,
-                     score_keep_rows(d, length, n_score), ctl, layer);
+  const int keep = score_keep_rows(d, length, n_score);
+  // Scores that do not fit the score work groups' LDS: the variant with K-best
+  // lists, for calls expected to be mostly exact. Its larger score role costs
+  // the head role about 1 us of register spills, so decode steps take it only
+  // from kKbDecodeLen keys on, where its refresh steps save more than that.
+  if (keep == 0 && (mode == kModeExact || wide || length >= kKbDecodeLen))
+    hipLaunchKernelGGL(k_step<true>, dim3(d.B * d.Hq + n_score), dim3(kHeadThreads), step_lds_bytes(d), s, d, b.self,
+                       q, q_sb, q_sh, k, v, out, sel_out, length, t_dec, mode, stats_slot, push, call_flag, n_score,
+                       keep, ctl, layer);
+  else
+    hipLaunchKernelGGL(k_step<false>, dim3(d.B * d.Hq + n_score), dim3(kHeadThreads), step_lds_bytes(d), s, d,
+                       b.self, q, q_sb, q_sh, k, v, out, sel_out, length, t_dec, mode, stats_slot, push, call_flag,
+                       n_score, keep, ctl, layer);
   return hipGetLastError();
 }
 

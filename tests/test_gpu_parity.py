@@ -272,6 +272,50 @@ def test_exact_degenerate_all_equal():
     close_checked(layer)
 
 
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_exact_long_history_integer_ties_and_all_equal():
+    """Histories whose scores do not fit the score work groups' LDS: 28 query
+    heads over 4 KV heads at 600,000 and 530,001 keys (more than 8,192 rows
+    per score work group: per-segment K-best lists) and at 230,000 keys
+    (about 4,000 rows: scores stored to and re-read from the workspace).
+    Integer-valued keys and queries make every score exact with many ties,
+    which must be broken by the lower index with no near-tie allowance; a zero
+    query makes every score equal (the K lowest indices; the lists then cut on
+    their rows, and the boundary bin holds far more keys than the LDS)."""
+    torch = _torch()
+    B = _B()
+    rng = np.random.default_rng(31)
+    L, Hq, Hkv, D, K = 600_000, 28, 4, 128, 512
+    G = Hq // Hkv
+    k = f32_to_bf16_bits(rng.integers(-2, 3, size=(1, Hkv, L, D), dtype=np.int8).astype(np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((1, Hkv, L, D), dtype=np.float32))
+    q = f32_to_bf16_bits(rng.integers(-1, 2, size=(1, Hq, D), dtype=np.int8).astype(np.float32))
+    layer = B.ReTopKLayer(batch=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, max_len=L, top_k=K,
+                          cache_cap=4, window=4, top_r=2, refresh_every=0, tau=0.5)
+    out = torch.empty((1, Hq, D), dtype=torch.float32, device="cuda")
+    sel = torch.empty((1, Hq, K), dtype=torch.int32, device="cuda")
+    kd, vd = B.bf16_tensor(k), B.bf16_tensor(v)
+    heads = list(range(G, 2 * G)) + [0, Hq - 1]
+    for length in (L, 530_001, 230_000):
+        log(f"[long ties] length {length}")
+        layer.exact_topk_attn(B.bf16_tensor(q), kd, vd, length, out, sel)
+        s, o = sel.cpu().numpy(), out.cpu().numpy()
+        for h in heads:
+            osel, osc = O.exact_topk_support(q[0, h], k[0, h // G], length, K)
+            assert np.array_equal(s[0, h], osel), f"L={length} h={h}"
+            check_output(o[0, h], osc, v[0, h // G, osel], D, f"L={length} h={h}")
+    for length in (L, 230_000):
+        log(f"[long ties] zero query, length {length}")
+        layer.exact_topk_attn(B.bf16_tensor(np.zeros((1, Hq, D), np.uint16)), kd, vd, length, out, sel)
+        s, o = sel.cpu().numpy(), out.cpu().numpy()
+        for h in range(Hq):
+            assert np.array_equal(s[0, h], np.arange(K)), f"zero query L={length} h={h}"
+            ref = O.bf16_to_f64(v[0, h // G, :K]).mean(0)
+            np.testing.assert_allclose(o[0, h], ref, rtol=1e-4, atol=1e-5)
+    close_checked(layer)
+
+
 # ---------------------------------------------------------------------------
 # Decode steps
 # ---------------------------------------------------------------------------
