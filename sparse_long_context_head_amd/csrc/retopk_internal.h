@@ -18,7 +18,7 @@ constexpr int kNumBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
 constexpr int kStatsCap = 4096;      // decode steps kept in the statistics ring
 constexpr int kExactMinRows = 512;   // key rows per score work group of the full-history pass, at least
-constexpr int kBoundaryLds = 4096;   // boundary-bin candidates resolved in LDS (32 KiB of 64-bit keys)
+constexpr int kBoundaryLds = 4096;   // boundary-bin candidates resolved in LDS, at least (32 KiB of 64-bit keys)
 constexpr int kHeadThreads = 512;    // threads of the per-head kernels
 constexpr int kBitmapWords = 8192;   // LDS bitmap window: 262144 token positions (32 KiB)
 constexpr int kLdsLimit = 124 * 1024;  // dynamic LDS a per-head kernel may use (static LDS <= 36 KiB)
@@ -62,7 +62,7 @@ struct Bufs {
   int32_t* err;            // [1]  sticky device error word (1: a wait of the step kernel timed out)
   int32_t* wdone;          // [2, n_cu] per score work group, the call flag once its scores and histogram
                            //   adds are out (row 0), once its survivors are out (row 1)
-  uint64_t* bkeys;         // [BH, max_len] boundary-bin composite keys when more than kBoundaryLds
+  uint64_t* bkeys;         // [BH, max_len] boundary-bin composite keys when more than the LDS holds
   int32_t* sel;            // [BH, K]   S_hat_t ascending
   float* selsc;            // [BH, K]   q.k of S_hat_t
   int32_t* sellen;         // [BH]

@@ -1626,33 +1626,38 @@ __device__ __forceinline__ void emit_segment(const Dims& d, const BufsDev& b, in
 // keeps, per exact head of each of its segments, only the entries that can
 // still be among the segment's K best: a key outside its own segment's K best
 // cannot be among the K best of the whole history (the segment alone holds K
-// better ones). Entries are (score bits, row) in LDS, admitted when their
-// composite key (ordered score << 32 | ~row: higher score first, then lower
-// row; all keys distinct) reaches the head's admission threshold. Each stage's
-// admitted entries are placed in row order (a scan of per-tile counts), so a
-// list is always sorted by row. When a head's list could overflow during the
-// next stage, one wave cuts it (in place, in order) to the entries at or above
-// a new threshold that keeps at least its K best: a 256-bin histogram of the
-// 8 key bits just below the keys' common prefix, refined 8 bits further while
-// the kept count would still leave no room. At the end of a segment each list
-// is cut to at most the next power of two >= K entries and moved to that
-// stride, and only its entries enter the call's score histogram: the K best
-// of the union of all lists are the K best of the history, so the boundary
-// bin b1, the counts above and in it, and the survivors (list entries in b1
-// or above, already in position order) are those of the full history.
+// better ones). Entries are (ordered score key, row) in LDS, admitted when
+// their composite key (ordered score << 32 | ~row: higher score first, then
+// lower row; all keys distinct) reaches the head's admission threshold. Each
+// stage's admitted entries are placed in row order (a scan of per-tile
+// counts), so a list is always sorted by row. When a head's list could
+// overflow during the next stage, one wave cuts it (in place, in order) to the
+// entries at or above a new threshold that keeps at least its K best: a
+// 256-bin histogram of the 8 score-key bits below the common prefix of the
+// list's key range (tracked per head as entries are admitted), refined 8 bits
+// at a time; on the full composite keys only when scores tie. At the end of a
+// segment, the lists of a work group's first segment (of two) are cut to the
+// next power of two >= K entries and moved to that stride; only the lists'
+// entries enter the call's score histogram: the K best of the union of all
+// lists are the K best of the history, so the boundary bin b1, the counts
+// above and in it, and the survivors (list entries in b1 or above, already in
+// position order) are those of the full history.
 // ---------------------------------------------------------------------------
 constexpr int kKbSlack = 1024;   // list room beyond K: the next stage's arrivals never overflow it
 constexpr int kKbCutSlack = 64;  // a cut during the scan keeps at most K + this many entries
+constexpr int kKbMaxSeg = 2;     // segments per work group the lists are kept for (else stored scores)
+constexpr int kKbTc = 16 * kQkUnroll * (kHeadThreads / kWave) / 4;  // (tile, row quad) slots per head and stage
 // Rows per score work group from which the lists beat stored scores (below,
 // the stored scores' write and re-read cost less than the lists' per-stage
-// ordering, cuts and histogram)
+// ordering and cuts)
 constexpr long kKbMinShare = 8192;
-constexpr int kKbMaxSeg = 2;    // segments per work group the lists are kept for (else stored scores)
-constexpr int kKbTc = 16 * kQkUnroll * (kHeadThreads / kWave) / 4;  // (tile, row quad) slots per head and stage
 
 __device__ __forceinline__ uint64_t kb_key(uint2 e) {
-  return (static_cast<uint64_t>(order_key(__uint_as_float(e.x))) << 32) | static_cast<uint64_t>(0xffffffffu - e.y);
+  return (static_cast<uint64_t>(e.x) << 32) | static_cast<uint64_t>(0xffffffffu - e.y);
 }
+
+// The float bits of an ordered score key (negative zero comes back as +0).
+__device__ __forceinline__ uint32_t okey_bits(uint32_t k) { return (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k; }
 
 __host__ __device__ inline int kb_stride(int K) {
   int p = 1;
@@ -1664,20 +1669,19 @@ __host__ __device__ inline int kb_stride(int K) {
 __host__ __device__ inline long kb_tc_bytes(const Dims& d) { return (8L * d.G * kKbTc + 15) / 16 * 16; }
 
 // Entries per head of segment si's working list (after the finished lists of
-// segments 0 .. si-1).
+// segments 0 .. si-1, at stride kb_stride(K)).
 __host__ __device__ inline int kb_cap(const Dims& d, int si) {
   const long list_bytes = 8L * d.G * kb_stride(d.K);
   return static_cast<int>((kLdsLimit - kb_tc_bytes(d) - si * list_bytes) / (8L * d.G));
 }
 
 // Whether a work group with nseg non-empty segments keeps K-best lists: each
-// segment's working list holds K + kKbSlack entries per head, and the
-// histogram of the last one fits after the finished lists.
+// segment's working list holds K + kKbSlack entries per head.
 __host__ __device__ inline bool kb_fits(const Dims& d, int nseg) {
   if (nseg < 1 || nseg > kKbMaxSeg) return false;
   for (int si = 0; si < nseg; ++si)
     if (kb_cap(d, si) < d.K + kKbSlack) return false;
-  return kb_tc_bytes(d) + static_cast<long>(nseg) * 8L * d.G * kb_stride(d.K) + 4L * d.G * kNumBins <= kLdsLimit;
+  return true;
 }
 
 __device__ __forceinline__ uint64_t wave_min_u64(uint64_t x) {
@@ -1698,43 +1702,50 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
   return x;
 }
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x = min(x, static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), o)));
-  return x;
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x = max(x, static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), o)));
-  return x;
-}
-
-// The cut below on the scores' ordered keys alone (32 bits), which is what
-// separates entries unless scores tie: entries with equal scores are kept or
-// dropped together. Returns false, with buf untouched, when ties leave more
-// than `limit` entries at the finest score resolution (the caller then cuts on
-// the full composite keys); else cuts, sets *theta (a composite-key
-// threshold) and *n_out.
-__device__ __forceinline__ bool kb_cut32(uint2* buf, int n, int k, int limit, int* bins, uint64_t* theta,
-                                         int* n_out) {
+// One wave: the digit holding the need-th largest of a 256-bin histogram
+// (bins scanned from 255 down): returns false if the bins hold fewer; else
+// *dg, the count above it (*above) and in it (*cnt).
+__device__ __forceinline__ bool kb_pick(const int* bins, int need, int* dg_out, int* above_out, int* cnt_out) {
   const int lane = threadIdx.x & 63;
-  constexpr int U = 8;
-  uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int c0 = 0; c0 < n; c0 += 64 * U) {
-    uint32_t x[U];
+  const int4 h = reinterpret_cast<const int4*>(bins)[63 - lane];  // lane l: digits 255-4l .. 252-4l
+  const int c[4] = {h.w, h.z, h.y, h.x};
+  const int s4 = c[0] + c[1] + c[2] + c[3];
+  const int incl = wave_incl_scan(s4);
+  int run = incl - s4;
+  int dg = -1, above = 0, cnt = 0;
+  if (run < need && incl >= need) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = buf[min(c0 + 64 * u + lane, n - 1)].x;  // (clamped repeats change nothing)
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t ok = order_key(__uint_as_float(x[u]));
-      lo = min(lo, ok);
-      hi = max(hi, ok);
+    for (int j = 0; j < 4; ++j) {
+      if (dg < 0 && run + c[j] >= need) {
+        dg = 255 - 4 * lane - j;
+        above = run;
+        cnt = c[j];
+      }
+      run += c[j];
     }
   }
-  lo = wave_min_u32(lo);
-  hi = wave_max_u32(hi);
-  if (lo == hi) return false;
+  const uint64_t m = __ballot(dg >= 0);
+  if (m == 0) return false;
+  const int src = __ffsll(static_cast<long long>(m)) - 1;
+  *dg_out = __builtin_amdgcn_readlane(dg, src);
+  *above_out = __builtin_amdgcn_readlane(above, src);
+  *cnt_out = __builtin_amdgcn_readlane(cnt, src);
+  return true;
+}
+
+// One wave: cut buf[0, n) (n > limit >= k) in place and in order to the
+// entries whose score key is at least a threshold that keeps at least the k
+// largest and at most `limit` of them. lo, hi bound the list's score keys.
+// Entries with equal scores are kept or dropped together: returns false, with
+// buf untouched, when ties leave more than `limit` entries at the finest
+// score resolution; else sets *theta (as a composite-key threshold) and
+// *n_out. bins: 256 ints of this wave's own LDS.
+__device__ __forceinline__ bool kb_cut32(uint2* buf, int n, int k, int limit, uint32_t lo, uint32_t hi, int* bins,
+                                         uint64_t* theta, int* n_out) {
+  const int lane = threadIdx.x & 63;
+  constexpr int U = 8;
+  if (lo >= hi) return false;
+  // the first digit: the 8 bits whose top one is the highest bit where lo and hi differ
   const int hb = 31 - __clz(static_cast<int>(lo ^ hi));
   int shift = max(hb - 7, 0), width = min(hb + 1, 8);
   uint32_t mask = hb >= 31 ? 0u : ~0u << (hb + 1);
@@ -1746,36 +1757,13 @@ __device__ __forceinline__ bool kb_cut32(uint2* buf, int n, int k, int limit, in
     for (int c0 = 0; c0 < n; c0 += 64 * U) {
       uint32_t x[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) x[u] = buf[min(c0 + 64 * u + lane, n - 1)].x;
+      for (int u = 0; u < U; ++u) x[u] = buf[min(c0 + 64 * u + lane, n - 1)].x;  // (clamped, masked below)
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t ok = order_key(__uint_as_float(x[u]));
-        if (c0 + 64 * u + lane < n && (ok & mask) == pre) atomicAdd(&bins[(ok >> shift) & dm], 1);
-      }
+      for (int u = 0; u < U; ++u)
+        if (c0 + 64 * u + lane < n && (x[u] & mask) == pre) atomicAdd(&bins[(x[u] >> shift) & dm], 1);
     }
-    const int4 h = reinterpret_cast<const int4*>(bins)[63 - lane];
-    const int c[4] = {h.w, h.z, h.y, h.x};
-    const int s4 = c[0] + c[1] + c[2] + c[3];
-    const int incl = wave_incl_scan(s4);
-    int run = incl - s4;
-    int dg = -1, above = 0, cnt = 0;
-    if (run < need && incl >= need) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (dg < 0 && run + c[j] >= need) {
-          dg = 255 - 4 * lane - j;
-          above = run;
-          cnt = c[j];
-        }
-        run += c[j];
-      }
-    }
-    const uint64_t m = __ballot(dg >= 0);
-    const int src = m ? __ffsll(static_cast<long long>(m)) - 1 : 0;
-    dg = __builtin_amdgcn_readlane(dg, src);
-    above = __builtin_amdgcn_readlane(above, src);
-    cnt = __builtin_amdgcn_readlane(cnt, src);
-    if (dg < 0) return false;  // (cannot happen: the window's entries always cover need)
+    int dg, above, cnt;
+    if (!kb_pick(bins, need, &dg, &above, &cnt)) return false;  // (cannot happen: lo, hi bound the keys)
     pre |= static_cast<uint32_t>(dg) << shift;
     mask |= dm << shift;
     kept += above;
@@ -1792,7 +1780,7 @@ __device__ __forceinline__ bool kb_cut32(uint2* buf, int n, int k, int limit, in
     for (int u = 0; u < U; ++u) x[u] = buf[min(c0 + 64 * u + lane, n - 1)];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool kp = (c0 + 64 * u + lane < n) && (order_key(__uint_as_float(x[u].x)) & mask) >= pre;
+      const bool kp = (c0 + 64 * u + lane < n) && (x[u].x & mask) >= pre;
       const uint64_t b = __ballot(kp);
       if (kp) buf[run + lanes_below(b)] = x[u];
       run += __popcll(b);
@@ -1803,14 +1791,9 @@ __device__ __forceinline__ bool kb_cut32(uint2* buf, int n, int k, int limit, in
   return true;
 }
 
-// The cut of a list: on the scores, else on the composite keys.
-__device__ __forceinline__ uint64_t kb_cut_list(uint2* buf, int n, int k, int limit, int* bins, int* n_out);
-
-// One wave: cut buf[0, n) (n > limit >= k, keys distinct) in place and in
-// order to the entries whose key reaches a threshold that keeps at least the
-// k largest and at most `limit` of them; returns the threshold and the kept
-// count (*n_out). bins: 256 ints of this wave's own LDS.
-__device__ __forceinline__ uint64_t kb_cut(uint2* buf, int n, int k, int limit, int* bins, int* n_out) {
+// The same cut on the full composite keys (all distinct), for lists whose
+// scores tie: always succeeds.
+__device__ __forceinline__ uint64_t kb_cut64(uint2* buf, int n, int k, int limit, int* bins, int* n_out) {
   const int lane = threadIdx.x & 63;
   constexpr int U = 8;
   uint64_t lo = ~0ull, hi = 0ull;
@@ -1827,8 +1810,7 @@ __device__ __forceinline__ uint64_t kb_cut(uint2* buf, int n, int k, int limit, 
   }
   lo = wave_min_u64(lo);
   hi = wave_max_u64(hi);
-  // the first digit: the 8 bits whose top one is the highest bit where keys differ
-  const int hb = 63 - __clzll(static_cast<long long>(lo ^ hi));
+  const int hb = 63 - __clzll(static_cast<long long>(lo ^ hi));  // (n > 1 distinct keys: lo != hi)
   int shift = max(hb - 7, 0), width = min(hb + 1, 8);
   uint64_t mask = hb >= 63 ? 0ull : ~0ull << (hb + 1);
   uint64_t pre = lo & mask;
@@ -1846,30 +1828,8 @@ __device__ __forceinline__ uint64_t kb_cut(uint2* buf, int n, int k, int limit, 
         if (c0 + 64 * u + lane < n && (key & mask) == pre) atomicAdd(&bins[(key >> shift) & dm], 1);
       }
     }
-    // lane l owns digits 255-4l .. 252-4l (digits above dm are empty)
-    const int4 h = reinterpret_cast<const int4*>(bins)[63 - lane];
-    const int c[4] = {h.w, h.z, h.y, h.x};
-    const int s4 = c[0] + c[1] + c[2] + c[3];
-    const int incl = wave_incl_scan(s4);
-    int run = incl - s4;
-    int dg = -1, above = 0, cnt = 0;
-    if (run < need && incl >= need) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (dg < 0 && run + c[j] >= need) {
-          dg = 255 - 4 * lane - j;
-          above = run;
-          cnt = c[j];
-        }
-        run += c[j];
-      }
-    }
-    const uint64_t m = __ballot(dg >= 0);
-    const int src = m ? __ffsll(static_cast<long long>(m)) - 1 : 0;
-    dg = __builtin_amdgcn_readlane(dg, src);
-    above = __builtin_amdgcn_readlane(above, src);
-    cnt = __builtin_amdgcn_readlane(cnt, src);
-    if (dg < 0) break;  // (cannot happen: the window's entries always cover need)
+    int dg, above, cnt;
+    if (!kb_pick(bins, need, &dg, &above, &cnt)) break;  // (cannot happen: lo, hi bound the keys)
     pre |= static_cast<uint64_t>(dg) << shift;
     mask |= dm << shift;
     kept += above;
@@ -1895,15 +1855,27 @@ __device__ __forceinline__ uint64_t kb_cut(uint2* buf, int n, int k, int limit, 
   return pre;
 }
 
-__device__ __forceinline__ uint64_t kb_cut_list(uint2* buf, int n, int k, int limit, int* bins, int* n_out) {
+__device__ __forceinline__ uint64_t kb_cut(uint2* buf, int n, int k, int limit, uint32_t lo, uint32_t hi, int* bins,
+                                           int* n_out) {
   uint64_t th;
-  if (kb_cut32(buf, n, k, limit, bins, &th, n_out)) return th;
-  return kb_cut(buf, n, k, limit, bins, n_out);
+  if (kb_cut32(buf, n, k, limit, lo, hi, bins, &th, n_out)) return th;
+  return kb_cut64(buf, n, k, limit, bins, n_out);
 }
 
+// Per-head state of the lists of the current segment (static LDS).
+struct KbState {
+  int n[kMaxGroup];          // entries
+  uint64_t theta[kMaxGroup]; // admission threshold (composite key)
+  uint32_t lo[kMaxGroup];    // a lower bound of the entries' score keys
+  uint32_t hi[kMaxGroup];    // their maximum
+  int full[kMaxGroup];       // to be cut after this stage
+  int cnt[kKbMaxSeg][kMaxGroup];  // final length per segment
+};
+
 // One stage of scores (as qk_score) into the K-best lists, in row order:
-//  1. every lane with an exact head j counts, per tile, its four rows whose
-//     keys reach theta and writes the count to the stage's slot table;
+//  1. every lane with an exact head j finds, per tile, its four rows whose keys
+//     reach theta and writes their count to the stage's slot table (and folds
+//     their score keys into the head's range);
 //  2. a wave per head scans the head's table (slot order = row order) into
 //     list positions and moves the head's length on;
 //  3. the lanes write their entries;
@@ -1914,11 +1886,11 @@ __device__ __forceinline__ uint64_t kb_cut_list(uint2* buf, int n, int k, int li
 // Every thread of the block must call it.
 __device__ __forceinline__ void qk_score_kb(const Dims& d, const QkTiles& t, const bf16x8 (&bq)[4], int t0, int rend,
                                             int wave, int nw, int j, int kq, bool hv, uint64_t& theta, uint2* lists,
-                                            int cap, int* tc, int* s_n, uint64_t* s_theta, int* s_full,
-                                            unsigned emask, HeadShared& sh) {
+                                            int cap, int* tc, KbState& ks, unsigned emask, HeadShared& sh) {
   const int lane = threadIdx.x & 63;
-  float sc[kQkUnroll][4];
+  uint32_t ok[kQkUnroll][4];
   unsigned pass = 0u;
+  uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
   for (int u = 0; u < kQkUnroll; ++u) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1929,14 +1901,22 @@ __device__ __forceinline__ void qk_score_kb(const Dims& d, const QkTiles& t, con
     int c = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      sc[u][e] = acc[e];
-      const uint64_t ck = (static_cast<uint64_t>(order_key(acc[e])) << 32) |
+      ok[u][e] = order_key(acc[e]);
+      const uint64_t ck = (static_cast<uint64_t>(ok[u][e]) << 32) |
                           static_cast<uint64_t>(0xffffffffu - static_cast<uint32_t>(r + e));
       const bool pe = hv & (r + e < rend) & (ck >= theta);
       pass |= static_cast<unsigned>(pe) << (4 * u + e);
       c += pe;
+      if (pe) {
+        lo = min(lo, ok[u][e]);
+        hi = max(hi, ok[u][e]);
+      }
     }
     if (hv) tc[j * kKbTc + (u * nw + wave) * 4 + kq] = c;
+  }
+  if (pass) {
+    atomicMin(&ks.lo[j], lo);
+    atomicMax(&ks.hi[j], hi);
   }
   lds_barrier();
   const int room = cap - 16 * kQkUnroll * nw;  // a stage adds at most one entry per row
@@ -1945,18 +1925,18 @@ __device__ __forceinline__ void qk_score_kb(const Dims& d, const QkTiles& t, con
     int* row = tc + jj * kKbTc;
     const int a = row[2 * lane], b2 = row[2 * lane + 1];
     const int incl = wave_incl_scan(a + b2);
-    const int base = s_n[jj];
+    const int base = ks.n[jj];
     const int ex = base + incl - a - b2;
     row[2 * lane] = ex;
     row[2 * lane + 1] = ex + a;
     const int n = base + __builtin_amdgcn_readlane(incl, 63);
     if (lane == 0) {
-      s_n[jj] = n;
-      s_full[jj] = n > room;
+      ks.n[jj] = n;
+      ks.full[jj] = n > room;
     }
   }
   lds_barrier();
-  if (hv && pass) {
+  if (pass) {
     uint2* buf = lists + static_cast<long>(j) * cap;
 #pragma unroll
     for (int u = 0; u < kQkUnroll; ++u) {
@@ -1966,89 +1946,109 @@ __device__ __forceinline__ void qk_score_kb(const Dims& d, const QkTiles& t, con
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if ((pass >> (4 * u + e)) & 1u) {
-          if (slot < cap) buf[slot] = make_uint2(__float_as_uint(sc[u][e]), static_cast<uint32_t>(r + e));
+          if (slot < cap) buf[slot] = make_uint2(ok[u][e], static_cast<uint32_t>(r + e));
           ++slot;
         }
       }
     }
   }
   bool any = false;
-  for (int jj = 0; jj < d.G; ++jj) any |= s_full[jj] != 0;  // (set before the last barrier; uniform)
+  for (int jj = 0; jj < d.G; ++jj) any |= ks.full[jj] != 0;  // (set before the last barrier; uniform)
   if (any) {
     lds_barrier();  // the entries are in
     for (int jj = wave; jj < d.G; jj += nw) {
-      if (!s_full[jj]) continue;
-      const int n = min(s_n[jj], cap);
+      if (!ks.full[jj]) continue;
       int kept;
-      const uint64_t th =
-          kb_cut_list(lists + static_cast<long>(jj) * cap, n, d.K, d.K + kKbCutSlack, &sh.whist[wave][0], &kept);
+      const uint64_t th = kb_cut(lists + static_cast<long>(jj) * cap, min(ks.n[jj], cap), d.K, d.K + kKbCutSlack,
+                                 ks.lo[jj], ks.hi[jj], &sh.whist[wave][0], &kept);
       if (lane == 0) {
-        s_theta[jj] = th;
-        s_n[jj] = kept;
-        s_full[jj] = 0;
+        ks.theta[jj] = th;
+        ks.n[jj] = kept;
+        ks.lo[jj] = static_cast<uint32_t>(th >> 32);  // every kept score key reaches the threshold's
+        ks.full[jj] = 0;
       }
     }
     lds_barrier();
   }
-  theta = s_theta[j < d.G ? j : 0];
+  theta = ks.theta[j < d.G ? j : 0];
 }
 
-// End of a segment's scan: cut each list to at most kp entries (keeping its
-// K best), move the lists to stride kp (padded with row 0xffffffff), record
-// their lengths, and add their histograms (LDS first) into the call's half of
-// the heads' global histograms. Every thread of the block must call it.
-__device__ __forceinline__ void kb_close(const Dims& d, const BufsDev& b, int bb, int g, unsigned emask, int par,
-                                         uint2* lists, int cap, int kp, int* s_n, int* kcnt, HeadShared& sh) {
+// End of segment si's scan (of nseg). The first of two segments cuts its lists
+// to at most kp entries (keeping their K best) and moves them to stride kp,
+// making room for the next segment's; the last leaves them in place at stride
+// cap. Records the lists' lengths and adds their histograms into the call's
+// half of the heads' global histograms: one wave per head, over the bins the
+// head's score keys span, 256 at a time in the wave's own LDS. Returns the
+// lists' stride. Every thread of the block must call it.
+__device__ __forceinline__ int kb_close(const Dims& d, const BufsDev& b, int bb, int g, unsigned emask, int par,
+                                        uint2* lists, int cap, int kp, bool last, KbState& ks, int* kcnt,
+                                        HeadShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   lds_barrier();
+  int stride = cap;
   for (int jj = wave; jj < d.G; jj += nw) {
-    int n = min(s_n[jj], cap);
-    if (n > kp) kb_cut_list(lists + static_cast<long>(jj) * cap, n, d.K, kp, &sh.whist[wave][0], &n);
+    int n = min(ks.n[jj], cap);
+    if (!last && n > kp) kb_cut(lists + static_cast<long>(jj) * cap, n, d.K, kp, ks.lo[jj], ks.hi[jj],
+                                &sh.whist[wave][0], &n);
     if (lane == 0) kcnt[jj] = n;
   }
   lds_barrier();
-  // move: read a chunk into registers, then write it (a destination never
-  // lies past its own source, nor in the source of a later chunk)
-  const int total = d.G * kp;
-  for (int base = 0; base < total; base += 8 * kHeadThreads) {
-    uint2 x[8];
+  if (!last) {
+    // move: read a chunk into registers, then write it (a destination never
+    // lies past its own source, nor in the source of a later chunk)
+    const int total = d.G * kp;
+    for (int base = 0; base < total; base += 8 * kHeadThreads) {
+      uint2 x[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int xi = base + u * kHeadThreads + tid;
-      const int jj = xi / kp, i = xi - jj * kp;
-      x[u] = make_uint2(0u, 0xffffffffu);
-      if (xi < total && i < kcnt[jj]) x[u] = lists[static_cast<long>(jj) * cap + i];
-    }
-    lds_barrier();
+      for (int u = 0; u < 8; ++u) {
+        const int xi = base + u * kHeadThreads + tid;
+        const int jj = xi / kp, i = xi - jj * kp;
+        x[u] = make_uint2(0u, 0xffffffffu);
+        if (xi < total && i < kcnt[jj]) x[u] = lists[static_cast<long>(jj) * cap + i];
+      }
+      lds_barrier();
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int xi = base + u * kHeadThreads + tid;
-      if (xi < total) lists[xi] = x[u];
+      for (int u = 0; u < 8; ++u) {
+        const int xi = base + u * kHeadThreads + tid;
+        if (xi < total) lists[xi] = x[u];
+      }
+      lds_barrier();
     }
-    lds_barrier();
+    stride = kp;
   }
-  // histograms of the lists (LDS after them), then their non-zero bins
-  uint32_t* hist = reinterpret_cast<uint32_t*>(lists + total);
-  for (int i = tid; i < d.G * kNumBins; i += blockDim.x) hist[i] = 0u;
-  lds_barrier();
-  for (int xi = tid; xi < total; xi += blockDim.x) {
-    const int jj = xi / kp, i = xi - jj * kp;
-    if (i < kcnt[jj]) atomicAdd(&hist[jj * kNumBins + (order_key(__uint_as_float(lists[xi].x)) >> kHistShift)], 1u);
-  }
-  lds_barrier();
-  for (int jj = 0; jj < d.G; ++jj) {
-    if (!((emask >> jj) & 1)) continue;
+  for (int jj = wave; jj < d.G; jj += nw) {
+    if (!((emask >> jj) & 1u)) continue;
+    const int n = kcnt[jj];
+    const uint2* list = lists + static_cast<long>(jj) * stride;
+    int* bins = &sh.whist[wave][0];
     uint32_t* ghist = b.hist + (static_cast<long>(bb * d.Hq + g * d.G + jj) * 2 + par) * kNumBins;
-    for (int i = tid; i < kNumBins; i += blockDim.x) {
-      const uint32_t c = hist[jj * kNumBins + i];
-      if (c) atomicAdd(&ghist[i], c);
+    const int blo = static_cast<int>(ks.lo[jj] >> kHistShift), bhi = static_cast<int>(ks.hi[jj] >> kHistShift);
+    for (int b0 = blo; n > 0 && b0 <= bhi; b0 += 256) {
+      reinterpret_cast<int4*>(bins)[lane] = make_int4(0, 0, 0, 0);
+      for (int c0 = 0; c0 < n; c0 += 64 * 8) {
+        uint32_t x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = list[min(c0 + 64 * u + lane, n - 1)].x;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int bn = static_cast<int>(x[u] >> kHistShift) - b0;
+          if (c0 + 64 * u + lane < n && bn >= 0 && bn < 256) atomicAdd(&bins[bn], 1);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = bins[lane + 64 * i];
+        if (c && b0 + lane + 64 * i < kNumBins) atomicAdd(&ghist[b0 + lane + 64 * i], static_cast<uint32_t>(c));
+      }
     }
   }
+  return stride;
 }
 
-// Phase 2 from a list (sorted by row): as emit_segment, reading (score, row) entries.
+// Phase 2 from a list (sorted by row): as emit_segment, reading (score key,
+// row) entries.
 __device__ __forceinline__ void emit_kb(const Dims& d, const BufsDev& b, int bb, int g, unsigned emask, int row0,
-                                        int length, int w, int par, const uint2* lists, int kp,
+                                        int length, int w, int par, const uint2* lists, int stride,
                                         const int* kcnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int G = d.G;
@@ -2056,8 +2056,8 @@ __device__ __forceinline__ void emit_kb(const Dims& d, const BufsDev& b, int bb,
   for (int jj = wave; jj < G; jj += nw) {
     if (!((emask >> jj) & 1u)) continue;
     const int b1 = wave_boundary(b.hist + (static_cast<long>(h0 + jj) * 2 + par) * kNumBins, min(d.K, length)).x;
-    const uint32_t k0 = b1 == kNumBins / 2 ? 0x7fffffffu : static_cast<uint32_t>(b1) << kHistShift;
-    const uint2* list = lists + static_cast<long>(jj) * kp;
+    const uint32_t k0 = static_cast<uint32_t>(b1) << kHistShift;
+    const uint2* list = lists + static_cast<long>(jj) * stride;
     uint2* region = b.hits + static_cast<long>(h0 + jj) * d.max_len + row0;
     const int n = kcnt[jj];
     int run = 0;
@@ -2067,11 +2067,9 @@ __device__ __forceinline__ void emit_kb(const Dims& d, const BufsDev& b, int bb,
       for (int u = 0; u < kEmitU; ++u) x[u] = list[min(c0 + 64 * u + lane, max(n - 1, 0))];
 #pragma unroll
       for (int u = 0; u < kEmitU; ++u) {
-        const int i = c0 + 64 * u + lane;
-        const int sb = static_cast<int>(x[u].x);
-        const bool sv = (i < n) & ((static_cast<uint32_t>(sb) ^ (static_cast<uint32_t>(sb >> 31) | 0x80000000u)) >= k0);
+        const bool sv = (c0 + 64 * u + lane < n) & (x[u].x >= k0);
         const uint64_t m = __ballot(sv);
-        if (sv) store_shared(region + run + lanes_below(m), make_uint2(x[u].y, x[u].x));
+        if (sv) store_shared(region + run + lanes_below(m), make_uint2(x[u].y, okey_bits(x[u].x)));
         run += __popcll(m);
       }
     }
@@ -2092,8 +2090,8 @@ __device__ __forceinline__ void emit_kb(const Dims& d, const BufsDev& b, int bb,
 //     `need` = keff - (count above b1) best.
 //  3. A block scan over "kept" flags writes S_t in ascending index order.
 //
-// LDS (dynamic): candidate keys (kBoundaryLds), segment offsets (nW + 1) and
-// first rows (nW), S_t and its scores (K each).
+// LDS (dynamic): segment offsets (nW + 1) and first rows (nW), S_t and its
+// scores (K each), then the candidate keys (the rest: at least kBoundaryLds).
 // ---------------------------------------------------------------------------
 constexpr int kSU = 8;  // survivors per thread per round
 
@@ -2115,16 +2113,19 @@ __device__ __forceinline__ void finish_phase(const Dims& d, const BufsDev& b, in
   if (tid < nW) seg_rows(T, nW, length, ne, tid, e, slo, shi);
   const int cc = (tid < nW && slo < shi) ? load_shared(b.ccnt + static_cast<long>(bh) * d.n_cu + tid) : 0;
   const int fifo_slot = b.fifo[2 * bh], fifo_count = b.fifo[2 * bh + 1];
-  uint64_t* lkeys = reinterpret_cast<uint64_t*>(dyn);
-  int* aoff = reinterpret_cast<int*>(dyn + 8 * kBoundaryLds);
+  int* aoff = reinterpret_cast<int*>(dyn);
   int* srow0 = aoff + (nW + 4) / 4 * 4;
-  const size_t off_c = 8 * kBoundaryLds + 4 * static_cast<size_t>((nW + 4) / 4 * 4 + (nW + 3) / 4 * 4);
+  const size_t off_c = 4 * static_cast<size_t>((nW + 4) / 4 * 4 + (nW + 3) / 4 * 4);
   int32_t* s_sel = reinterpret_cast<int32_t*>(dyn + off_c);
   float* s_selsc = reinterpret_cast<float*>(dyn + off_c + 4 * static_cast<size_t>(d.K));
+  // the candidate keys take the rest of the LDS (at least kBoundaryLds of them)
+  const size_t off_k = (off_c + 8 * static_cast<size_t>(d.K) + 15) / 16 * 16;
+  uint64_t* lkeys = reinterpret_cast<uint64_t*>(dyn + off_k);
+  const int key_cap = static_cast<int>((kLdsLimit - off_k) / 8);
   const int keff = min(d.K, length);
   // (clamped: consistent scores and histogram never need it, but every index below stays in its row)
   const int b1 = bd.x, n_above = min(max(bd.y, 0), keff - 1), n_bd = min(max(bd.z, 0), length);
-  const bool keys_lds = n_bd <= kBoundaryLds;
+  const bool keys_lds = n_bd <= key_cap;
   uint64_t* gkeys = b.bkeys + static_cast<long>(bh) * d.max_len;
   const uint2* hits_row = b.hits + static_cast<long>(bh) * d.max_len;
 
@@ -2282,10 +2283,8 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
   __shared__ int s_eg[kMaxExactGroups];  // listed group | its exact heads << 16 (bit jj: head jj of the group)
   __shared__ int s_tmp[8];
   __shared__ uint32_t s_ex[kMaxExactGroups * kMaxGroup / 32];  // exact bit of every head
-  __shared__ int s_kbn[kMaxGroup];                  // K-best lists: entries per head (current segment)
-  __shared__ uint64_t s_kbtheta[kMaxGroup];         // ... admission threshold per head
-  __shared__ int s_kbfull[kMaxGroup];               // ... list to be cut after this stage
-  __shared__ int s_kbcnt[kKbMaxSeg][kMaxGroup];     // ... final length per segment and head
+  __shared__ KbState s_kb;                          // K-best lists of the current segment
+  __shared__ int s_kbstride[kKbMaxSeg];             // ... finished lists' stride per segment
   extern __shared__ __align__(16) unsigned char dyn[];
   // LDS: histograms [G, kNumBins] (phase 1), then the kept scores
   // [G, keep + 4] (phase 1 -> 3); phase 4 reuses all of it
@@ -2390,23 +2389,25 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
       int* tc = reinterpret_cast<int*>(dyn);  // two stages' slot tables
       uint2* lists = reinterpret_cast<uint2*>(dyn + kb_tc_bytes(d)) + static_cast<long>(si) * d.G * kp;
       if (threadIdx.x < d.G) {
-        s_kbn[threadIdx.x] = 0;
-        s_kbtheta[threadIdx.x] = 0ull;
-        s_kbfull[threadIdx.x] = 0;
+        s_kb.n[threadIdx.x] = 0;
+        s_kb.theta[threadIdx.x] = 0ull;
+        s_kb.lo[threadIdx.x] = 0xffffffffu;
+        s_kb.hi[threadIdx.x] = 0u;
+        s_kb.full[threadIdx.x] = 0;
       }
       lds_barrier();  // (also: the previous segment's histogram is read out)
       uint64_t theta = 0ull;
       const int kStage = 16 * kQkUnroll * nw;  // rows per stage
       for (int t0 = row0; t0 < rend; t0 += 2 * kStage) {
         qk_load(tb, kb, t0 + kStage, rend, wave, nw, j, kq);
-        qk_score_kb(d, ta, bq, t0, rend, wave, nw, j, kq, hv, theta, lists, cap, tc, s_kbn, s_kbtheta, s_kbfull,
-                    emask, sh);
+        qk_score_kb(d, ta, bq, t0, rend, wave, nw, j, kq, hv, theta, lists, cap, tc, s_kb, emask, sh);
         if (t0 + kStage >= rend) break;
         qk_load(ta, kb, t0 + 2 * kStage, rend, wave, nw, j, kq);
-        qk_score_kb(d, tb, bq, t0 + kStage, rend, wave, nw, j, kq, hv, theta, lists, cap, tc + d.G * kKbTc, s_kbn,
-                    s_kbtheta, s_kbfull, emask, sh);
+        qk_score_kb(d, tb, bq, t0 + kStage, rend, wave, nw, j, kq, hv, theta, lists, cap, tc + d.G * kKbTc, s_kb,
+                    emask, sh);
       }
-      kb_close(d, b, bb, g, emask, par, lists, cap, kp, s_kbn, s_kbcnt[si], sh);
+      const int stride = kb_close(d, b, bb, g, emask, par, lists, cap, kp, si == nseg - 1, s_kb, s_kb.cnt[si], sh);
+      if (threadIdx.x == 0) s_kbstride[si] = stride;
       ++si;
     }
   }
@@ -2480,8 +2481,8 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
     if (!wait_group(b.wdone, T, nW, length, ne, e, call_flag, b.err, &sh.i3)) return;
     if (use_kb) {
       emit_kb(d, b, bg / d.Hkv, bg % d.Hkv, static_cast<unsigned>(s_eg[e]) >> 16, row0, length, w, par,
-              reinterpret_cast<const uint2*>(dyn + kb_tc_bytes(d)) + static_cast<long>(si) * d.G * kp, kp,
-              s_kbcnt[si]);
+              reinterpret_cast<const uint2*>(dyn + kb_tc_bytes(d)) + static_cast<long>(si) * d.G * kp,
+              s_kbstride[si], s_kb.cnt[si]);
       ++si;
     } else if (keep > 0)
       emit_segment<true>(d, b, bg / d.Hkv, bg % d.Hkv, static_cast<unsigned>(s_eg[e]) >> 16, row0, rend, length, w,

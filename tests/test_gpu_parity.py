@@ -253,11 +253,12 @@ def test_exact_integer_ties():
 
 def test_exact_degenerate_all_equal():
     """Zero query: every score is 0, the support is the K lowest indices.
-    The boundary bin holds every key (more than the LDS capacity)."""
+    The boundary bin holds every key (at 20,000 more than the LDS holds, at
+    9,000 fewer)."""
     torch = _torch()
     B = _B()
     rng = np.random.default_rng(22)
-    L, K = 9000, 300
+    L, K = 20000, 300
     k = f32_to_bf16_bits(rng.standard_normal((1, 1, L, 128)).astype(np.float32))
     v = f32_to_bf16_bits(rng.standard_normal((1, 1, L, 128)).astype(np.float32))
     q = np.zeros((1, 1, 128), np.uint16)
@@ -265,10 +266,11 @@ def test_exact_degenerate_all_equal():
                           cache_cap=2, window=1, top_r=1, refresh_every=0, tau=0.5)
     out = torch.empty((1, 1, 128), dtype=torch.float32, device="cuda")
     sel = torch.empty((1, 1, K), dtype=torch.int32, device="cuda")
-    layer.exact_topk_attn(B.bf16_tensor(q), B.bf16_tensor(k), B.bf16_tensor(v), L, out, sel)
-    assert np.array_equal(sel.cpu().numpy()[0, 0], np.arange(K))
-    ref = O.bf16_to_f64(v[0, 0, :K]).mean(0)
-    np.testing.assert_allclose(out.cpu().numpy()[0, 0], ref, rtol=1e-4, atol=1e-5)
+    for length in (L, 9000):
+        layer.exact_topk_attn(B.bf16_tensor(q), B.bf16_tensor(k), B.bf16_tensor(v), length, out, sel)
+        assert np.array_equal(sel.cpu().numpy()[0, 0], np.arange(K)), length
+        ref = O.bf16_to_f64(v[0, 0, :K]).mean(0)
+        np.testing.assert_allclose(out.cpu().numpy()[0, 0], ref, rtol=1e-4, atol=1e-5)
     close_checked(layer)
 
 
