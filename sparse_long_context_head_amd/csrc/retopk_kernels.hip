@@ -958,7 +958,7 @@ constexpr int kCandWide = 24;  // ... for 577 .. 768 candidates: one round of 76
 // Every thread of the block must call it.
 template <int U>
 __device__ __forceinline__ void cand_scores(const uint16_t* kb, const int32_t* s_cand, int M, uint4 qw, int rg,
-                                            int rpr, int part, float* s_sc) {
+                                            int rpr, int part, float* s_sc, float& mn, float& mx) {
   for (int r0 = 0; r0 < M; r0 += rpr * U) {
     uint4 kv[U];
 #pragma unroll
@@ -974,7 +974,11 @@ __device__ __forceinline__ void cand_scores(const uint16_t* kb, const int32_t* s
       sc = dot2_bf16(kv[u].z, qw.z, sc);
       sc = dot2_bf16(kv[u].w, qw.w, sc);
       sc = row_sum(sc);
-      if (part == 0 && i < M) s_sc[i] = sc;
+      if (i < M) {
+        if (part == 0) s_sc[i] = sc;
+        mn = fminf(mn, sc);
+        mx = fmaxf(mx, sc);
+      }
     }
   }
 }
@@ -1326,7 +1330,8 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
     // window's bitmap go out a byte per thread, the rest a slice of words per
     // thread.
     M += bitmap_emit_split(bm, max(0, nwords - kDenseWords), nwords, base, s_cand + M, sh.tmp);
-    lds_barrier();
+    if (base + kBitmapWords * 32 < wlo) lds_barrier();  // (the next window clears the bitmap; after the
+                                                        // last one, the window append below is disjoint)
   }
   for (int x = wlo + tid; x < length; x += blockDim.x) s_cand[M + (x - wlo)] = x;
   M += length - wlo;
@@ -1341,23 +1346,36 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
   const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
   const uint16_t* vb = v + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
   const int rg = tid >> 4, rpr = blockDim.x >> 4;
+  float mx = kNegInf, mn = kPosInf;
   {
     // kCandU rows in flight per 16-lane group; a wider round for candidate
     // sets that one such round misses only by a little, so that they do not
     // pay a second dependent round trip
     const uint4 qw = *reinterpret_cast<const uint4*>(q + bb * q_sb + h * q_sh + 8 * part);
     if (M > rpr * kCandU && M <= rpr * kCandWide)
-      cand_scores<kCandWide>(kb, s_cand, M, qw, rg, rpr, part, s_sc);
+      cand_scores<kCandWide>(kb, s_cand, M, qw, rg, rpr, part, s_sc, mn, mx);
     else
-      cand_scores<kCandU>(kb, s_cand, M, qw, rg, rpr, part, s_sc);
+      cand_scores<kCandU>(kb, s_cand, M, qw, rg, rpr, part, s_sc, mn, mx);
   }
-  lds_barrier();
-  float mx = kNegInf, mn = kPosInf;
-  for (int i = tid; i < M; i += blockDim.x) {
-    mx = fmaxf(mx, s_sc[i]);
-    mn = fminf(mn, s_sc[i]);
+  // the scores' extremes: per wave before the barrier that publishes the
+  // scores, across the waves after it
+  {
+    float* tmpf = reinterpret_cast<float*>(sh.tmp);
+    mx = wave_max_f32(mx);
+    mn = -wave_max_f32(-mn);
+    if (lane == 0) {
+      tmpf[2 * wave] = mn;
+      tmpf[2 * wave + 1] = mx;
+    }
+    lds_barrier();
+    mn = kPosInf;
+    mx = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kHeadThreads / 64; ++w) {
+      mn = fminf(mn, tmpf[2 * w]);
+      mx = fmaxf(mx, tmpf[2 * w + 1]);
+    }
   }
-  block_minmax_f32(mn, mx, reinterpret_cast<float*>(sh.tmp), &mn, &mx);
 
   // ---- rerank (Eq. 11) ----
   // LDS after S_hat and its scores in region0: boundary flags of the linear rerank
