@@ -2574,8 +2574,11 @@ __global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, const Bufs* __res
               call_flag, w, sh);
   } else {
     const BufsDev b = *reinterpret_cast<const BufsDev*>(bp);
-    score_role<kLong>(d, b, q, q_sb, q_sh, k, v, out, sel_out, length, push, call_flag, w - BH, n_score,
-                      mode == kModeExact, keep, sh);
+    // every head is exact in an exact call and on a refresh step (Eq. 13):
+    // then there are no decisions to wait for
+    const bool all_exact = mode == kModeExact || (d.Tr > 0 && t_dec % d.Tr == 0);
+    score_role<kLong>(d, b, q, q_sb, q_sh, k, v, out, sel_out, length, push, call_flag, w - BH, n_score, all_exact,
+                      keep, sh);
   }
 }
 
