@@ -126,8 +126,9 @@ def _counter_rows(path):
 
 
 def _short_name(full):
-    """Kernel name without namespaces or arguments: "ns::(anonymous namespace)::k(int, ...)" -> "k"."""
-    return full.replace("(anonymous namespace)::", "").split("(")[0].split("::")[-1].strip()
+    """Kernel name without namespaces, template arguments or arguments:
+    "ns::(anonymous namespace)::k<true>(int, ...)" -> "k"."""
+    return full.replace("(anonymous namespace)::", "").split("(")[0].split("<")[0].split("::")[-1].strip()
 
 
 def _per_dispatch(rows, counter, last=None):

@@ -24,6 +24,7 @@ def test_short_kernel_names():
     assert bench._short_name("retopk::k_step(retopk::Dims, retopk::Bufs const*, int)") == "k_step"
     assert bench._short_name("retopk::(anonymous namespace)::k_dense(retopk::Dims, int)") == "k_dense"
     assert bench._short_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+    assert bench._short_name("void retopk::k_step<true>(retopk::Dims, retopk::Bufs const*, int)") == "k_step"
 
 
 def _rows(counter, spec):
