@@ -56,6 +56,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=64, help="untimed layer-steps before timing")
     ap.add_argument("--workload", default="headline128k")
     ap.add_argument("--layers", type=int, default=0, help="rotated layers (0: enough to exceed 1 GiB of KV)")
+    ap.add_argument("--from-start", action="store_true",
+                    help="every rotated layer starts at the first decode step (no spread of the layers' "
+                         "positions over the workload's steps): times the steps right after the cache "
+                         "initialisation, where candidate sets are largest")
     for flag, typ in (("top-k", int), ("top-r", int), ("window", int), ("cache-cap", int), ("tau", float),
                       ("refresh-every", int)):
         ap.add_argument(f"--{flag}", type=typ, default=None,
@@ -429,7 +433,7 @@ def main():
     if n_pos > wl.decode_steps:
         wl = wl.replace(decode_steps=n_pos)
     counts = [len(range(l, args.warmup + args.steps, nl)) for l in range(nl)]
-    offsets = layer_offsets(counts, wl.decode_steps)
+    offsets = [0] * nl if args.from_start else layer_offsets(counts, wl.decode_steps)
     L0, G = wl.prompt_len, wl.n_q_heads // wl.n_kv_heads
     log(f"workload {wl.name}: B={wl.batch} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} L0={L0} "
         f"K={wl.top_k}; {nl} rotated layers; {n_pos} decode positions per layer from offsets {offsets}")
