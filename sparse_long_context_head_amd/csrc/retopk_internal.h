@@ -25,6 +25,10 @@ constexpr int kLdsLimit = 124 * 1024;  // dynamic LDS a per-head kernel may use 
 constexpr int kMaxCand = 16384;      // R*K + W limit (candidate keys kept in LDS for reranking)
 constexpr int kDenseMaxGroup = 8;    // query heads per KV head the dense-attention kernel handles
 constexpr int kDensePart = 132;      // floats per (query head, row slice) partial: 128 sums, m, Z, 2 pad
+// Ints between two polled flags (decisions, hand-off flags): one per 128-byte
+// line, so that many work groups polling many flags do not all queue on the
+// same few lines.
+constexpr int kFlagStride = 32;
 
 // Problem dimensions, passed by value to every kernel.
 struct Dims {
@@ -58,9 +62,11 @@ struct Bufs {
                            //   (position, score bits); a score work group's segment [row0, rend)
                            //   writes its own in ascending position order from row0 on
   int32_t* ccnt;           // [BH, n_cu] survivors per score work group's segment
-  int32_t* dec;            // [BH] path decision of the current call: call flag | exact
+  int32_t* dec;            // [BH, kFlagStride] path decision of the current call: call flag | exact
+                           //   (one per 128-byte line)
   int32_t* err;            // [1]  sticky device error word (1: a wait of the step kernel timed out)
-  int32_t* wdone;          // [2, n_cu] per score work group, the call flag once its scores and histogram
+  int32_t* wdone;          // [2, n_cu, kFlagStride] per score work group (one per 128-byte line), the
+                           //   call flag once its scores and histogram
                            //   adds are out (row 0), once its survivors are out (row 1)
   uint64_t* bkeys;         // [BH, max_len] boundary-bin composite keys when more than the LDS holds
   int32_t* sel;            // [BH, K]   S_hat_t ascending

@@ -1230,7 +1230,7 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
       const int lo = d.recent ? max(0, count - d.R) : 0;
       const double mxr = wave_max_f64(lane < count && lane >= lo ? sh.rho[lane] : -INFINITY);
       if (lane == 0) {
-        store_shared(b.dec + bh, call_flag | ((refresh || count == 0 || mxr < d.tau) ? 1 : 0));
+        store_shared(b.dec + bh * kFlagStride, call_flag | ((refresh || count == 0 || mxr < d.tau) ? 1 : 0));
         if (d.recent) sh.d0 = mxr;
       }
     }
@@ -1282,7 +1282,7 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
   }
   // publish the decision to the score work groups (decode mode did so above;
   // the histogram half of this call was cleared during the previous one)
-  if (tid == 0 && mode != kModeDecode) store_shared(b.dec + bh, call_flag | (exact ? 1 : 0));
+  if (tid == 0 && mode != kModeDecode) store_shared(b.dec + bh * kFlagStride, call_flag | (exact ? 1 : 0));
   if (exact) {
     if (tid == 0) b.m[bh] = 0;
     return;
@@ -1518,7 +1518,7 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
 }
 
-// Wait until flags[ww] == call_flag for every work group ww with rows in list
+// Wait until flags[ww * kFlagStride] == call_flag for every work group ww with rows in list
 // group e (one thread per work group; bounded in time, a timeout sets the
 // device error word). Every thread of the block must call it.
 __device__ __forceinline__ bool wait_group(const int32_t* flags, long T, int nW, int length, int ne, int e,
@@ -1532,7 +1532,7 @@ __device__ __forceinline__ bool wait_group(const int32_t* flags, long T, int nW,
   }
   const long long t0 = __builtin_amdgcn_s_memrealtime();
   for (;;) {
-    const bool ok = !chk || load_shared(flags + tid) == call_flag;
+    const bool ok = !chk || load_shared(flags + tid * kFlagStride) == call_flag;
     if (__syncthreads_and(ok)) return true;
     if (tid == 0) *s_go = __builtin_amdgcn_s_memrealtime() - t0 >= kWaitTicks ? -1 : 0;
     lds_barrier();
@@ -2327,7 +2327,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
       lds_barrier();
       int mine = 1;
       for (int i = threadIdx.x; i < BH; i += blockDim.x) {
-        const int x = load_shared(b.dec + i);
+        const int x = load_shared(b.dec + i * kFlagStride);
         mine &= (x | 1) == (call_flag | 1);
         if (x & 1) atomicOr(&s_ex[i >> 5], 1u << (i & 31));
       }
@@ -2480,7 +2480,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
   }
   wait_vmem();      // this wave's histogram adds (and workspace scores) have completed ...
   __syncthreads();  // ... in every wave, before the flag that publishes them
-  if (threadIdx.x == 0) store_shared(b.wdone + w, call_flag);
+  if (threadIdx.x == 0) store_shared(b.wdone + w * kFlagStride, call_flag);
 
   // the heads this work group finishes: head m of group e when x_m (see
   // above) falls in [xa, xb)
@@ -2512,7 +2512,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
   }
   wait_vmem();      // this wave's survivor and count stores have completed ...
   __syncthreads();  // ... in every wave, before the flag that publishes them
-  if (threadIdx.x == 0) store_shared(b.wdone + d.n_cu + w, call_flag);
+  if (threadIdx.x == 0) store_shared(b.wdone + (d.n_cu + w) * kFlagStride, call_flag);
 
   // ---- phase 3: finish the owned heads ----
   for (int e = ea; e <= eb; ++e) {
@@ -2533,7 +2533,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
           sh.i2 = bd.z;
         }
       }
-      if (!wait_group(b.wdone + d.n_cu, T, nW, length, ne, e, call_flag, b.err, &sh.i3)) return;
+      if (!wait_group(b.wdone + d.n_cu * kFlagStride, T, nW, length, ne, e, call_flag, b.err, &sh.i3)) return;
       const int3 bd = make_int3(sh.i0, sh.i1, sh.i2);
       lds_barrier();  // (the finish reuses sh.i0 ..)
       finish_phase(d, b, bh, q, q_sb, q_sh, v, out, sel_out, length, push, T, nW, ne, e, bd, sh, dyn);
