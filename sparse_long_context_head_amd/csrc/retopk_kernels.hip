@@ -331,48 +331,40 @@ __device__ __forceinline__ void bitmap_clear(uint32_t* bm) {
 
 __device__ __forceinline__ void bitmap_set(uint32_t* bm, int x) { atomicOr(&bm[bm_at(x >> 5)], 1u << (x & 31)); }
 
-// Emit, in ascending order, the positions base + 32 * w + bit of every set bit
-// of words [0, nwords) of an LDS bitmap window. Words [0, wsplit) are taken a
-// slice of per = ceil(wsplit / blockDim) <= kSliceWords words per thread;
-// words [wsplit, nwords) (at most blockDim / 4) a byte (8 positions) per
-// thread, for dense stretches, where a thread owning whole words would emit
-// hundreds of bits one after another. One two-value block scan places both.
-// Returns the number emitted (the same value in every thread). Every thread of
-// the block must call it.
-__device__ __forceinline__ int bitmap_emit_split(const uint32_t* bm, int wsplit, int nwords, int base, int32_t* out,
-                                                 int* tmp) {
+// Per-word prefix counts of an LDS bitmap window, for ranking its set bits.
+// Thread t owns the slice of words 16t .. 16t+15 (the layout bitmap_clear
+// clears). pfx receives, for every word w, the number of set bits in words
+// [0, w), as 16-bit counts packed two per dword, with one pad dword after
+// every 32 so that the 64 lanes' stores spread over the banks. Returns the
+// total number of set bits (the same value in every thread). Ends with a
+// barrier. Every thread of the block must call it.
+constexpr int kPfxDwords = kBitmapWords / 2 + kBitmapWords / 64;
+__device__ __forceinline__ int bitmap_prefix(const uint32_t* bm, uint32_t* pfx, int* tmp) {
   const int t = threadIdx.x;
-  const int per = (wsplit + blockDim.x - 1) / blockDim.x;
-  uint32_t w[kSliceWords];
-  const int w0 = t * per;
-  int cnt = 0;
+  const uint32_t* p = bm + t * (kSliceWords + 1);
+  int c[kSliceWords];
+  int run = 0;
 #pragma unroll
   for (int i = 0; i < kSliceWords; ++i) {
-    w[i] = (i < per && w0 + i < wsplit) ? bm[bm_at(w0 + i)] : 0u;
-    cnt += __popc(w[i]);
+    c[i] = run;
+    run += __popc(p[i]);
   }
-  const int wd = wsplit + (t >> 2);
-  const uint32_t byte = wd < nwords ? (bm[bm_at(wd)] >> (8 * (t & 3))) & 0xffu : 0u;
-  int off, offd, tot, totd;
-  block_exclusive_scan2(cnt, __popc(byte), &off, &offd, &tot, &totd, tmp);
+  int tot;
+  const int base = block_exclusive_scan(run, &tot, tmp);
+  uint32_t* o = pfx + t * (kSliceWords / 2) + (t >> 2);
 #pragma unroll
-  for (int i = 0; i < kSliceWords; ++i) {
-    if (i >= per) break;  // uniform
-    uint32_t bits = w[i];
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      out[off++] = base + (w0 + i) * 32 + b;
-      bits &= bits - 1;
-    }
-  }
-  offd += tot;
-  uint32_t bits = byte;
-  while (bits) {
-    const int b = __ffs(bits) - 1;
-    out[offd++] = base + wd * 32 + 8 * (t & 3) + b;
-    bits &= bits - 1;
-  }
-  return tot + totd;
+  for (int i = 0; i < kSliceWords / 2; ++i)
+    o[i] = static_cast<uint32_t>(base + c[2 * i]) | (static_cast<uint32_t>(base + c[2 * i + 1]) << 16);
+  lds_barrier();
+  return tot;
+}
+
+// Rank of set bit y of the window among its set bits (the number of set bits
+// below it), from the prefix counts of bitmap_prefix.
+__device__ __forceinline__ int bitmap_rank(const uint32_t* bm, const uint32_t* pfx, int y) {
+  const int w = y >> 5;
+  const uint32_t below = (pfx[(w >> 1) + (w >> 6)] >> ((w & 1) << 4)) & 0xffffu;
+  return static_cast<int>(below) + __popc(bm[bm_at(w)] & ((1u << (y & 31)) - 1u));
 }
 
 // First dynamic-LDS region of the head kernel: the bitmap window, later S_hat
@@ -393,10 +385,12 @@ struct HeadShared {
   int moff[65];                        // merged union: start of each retrieved list's part below the window
   __align__(16) int whist[kHeadThreads / 64][256];   // one radix histogram per wave
   int tmp[32];
-  __align__(16) float red[kHeadThreads / 16][kHeadDim + 4];  // one row per 16-lane row group
+  __align__(16) float red[kHeadThreads / 16][kHeadDim + 4];  // one row per 16-lane row group (before
+                                                             // that, the union's bitmap prefix counts)
   int i0, i1, i2, i3;
   double d0;
 };
+static_assert(sizeof(HeadShared::red) >= kPfxDwords * 4, "bitmap prefix counts in the reduction rows");
 // the per-head kernels add at most 2 KiB of their own to it; LDS is 160 KiB per work group
 static_assert(sizeof(HeadShared) + 2048 + kLdsLimit <= 160 * 1024, "static + dynamic LDS of a per-head kernel");
 
@@ -982,7 +976,6 @@ __device__ __forceinline__ void cand_scores(const uint16_t* kb, const int32_t* s
     }
   }
 }
-constexpr int kDenseWords = kHeadThreads / 4;  // bitmap words emitted a byte per thread (4096 positions)
 constexpr int kMergeR = 8;                      // retrieved lists the merged union takes
 constexpr int kMergeE = 4;                      // entries per thread: R K <= 4 * 512
 
@@ -1295,13 +1288,17 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
   // are already covered).
   const int wlo = max(0, length - d.W);
   int M = 0;
+  // while the scores are not there yet: each retrieved support entry's
+  // position relative to the bitmap window, or -1 (outside it, or past the
+  // entry's support size)
+  int32_t* stash = reinterpret_cast<int32_t*>(s_sc);
+  uint32_t* pfx = reinterpret_cast<uint32_t*>(&sh.red[0][0]);
   // positions beyond one bitmap window: merge the sorted supports instead of
   // sweeping window after window
   const bool merged = wlo > kBitmapWords * 32 && n_ret <= kMergeR && n_ret * d.K <= kMergeE * kHeadThreads;
   if (merged) M = union_merge(d, b, bh, n_ret, wlo, s_cand, reinterpret_cast<int*>(s_sc), reinterpret_cast<int*>(dyn), sh);
   for (int base = 0; !merged && base < wlo; base += kBitmapWords * 32) {
     const int nbits = min(kBitmapWords * 32, wlo - base);
-    const int nwords = (nbits + 31) >> 5;
     if (base > 0) {
       bitmap_clear(bm);
       lds_barrier();
@@ -1320,16 +1317,22 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
         for (int u = 0; u < 4; ++u) {
           const int r = r0 + u;
           const int y = x[u] - base;
-          if (r < n_ret && j < sh.len[sh.rslot[min(r, n_ret - 1)]] && y >= 0 && y < nbits) bitmap_set(bm, y);
+          const bool in = r < n_ret && j < sh.len[sh.rslot[min(r, n_ret - 1)]] && y >= 0 && y < nbits;
+          if (in) bitmap_set(bm, y);
+          if (r < n_ret && j < d.K) stash[r * d.K + j] = in ? y : -1;
         }
       }
     }
     lds_barrier();
-    // Positions just below the window are dense (recent decode positions carry
-    // forward from support to support): the last kDenseWords words of the
-    // window's bitmap go out a byte per thread, the rest a slice of words per
-    // thread.
-    M += bitmap_emit_split(bm, max(0, nwords - kDenseWords), nwords, base, s_cand + M, sh.tmp);
+    // Every entry goes to its position's rank among the window's set bits, so
+    // the positions come out ascending; copies of one position in several
+    // supports write the same value to the same slot.
+    const int nset = bitmap_prefix(bm, pfx, sh.tmp);
+    for (int i = tid; i < n_ret * d.K; i += blockDim.x) {
+      const int y = stash[i];
+      if (y >= 0) s_cand[M + bitmap_rank(bm, pfx, y)] = base + y;
+    }
+    M += nset;
     if (base + kBitmapWords * 32 < wlo) lds_barrier();  // (the next window clears the bitmap; after the
                                                         // last one, the window append below is disjoint)
   }

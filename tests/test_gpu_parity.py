@@ -674,10 +674,24 @@ def test_stress_shape_forced_reuse_k2048():
 def test_scale_1m_every_head():
     """L0 = 1,048,576 (one-layer scaling): every head in lockstep for 4 steps
     with a refresh every 2 steps (the cache from the GPU's initialisation); the
-    reuse steps' unions span four LDS bitmap windows of 262,144 positions.
-    Then the Exact Top-K baseline on every head."""
+    reuse steps' unions merge the sorted supports (R K = 2048, beyond one LDS
+    bitmap window of 262,144 positions). Then the Exact Top-K baseline on
+    every head."""
     run_lockstep("scale1m", 4, override=dict(refresh_every=2), check_init=False, wl_kw=dict(decode_steps=8))
     run_exact("scale1m", [(1 << 20) + 3], wl_kw=dict(decode_steps=8))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_scale_1m_forced_reuse_k1024_bitmap_windows():
+    """L0 = 1,048,576 with K = 1024, KV group 1 forced onto the reuse path
+    (tau = -2, T_r = 0) for 3 lockstep steps: R K = 4096 is more than the
+    merged union takes, so the union sweeps four LDS bitmap windows of 262,144
+    positions, each ranked on its own and appended after the previous ones."""
+    r = run_lockstep("scale1m", 3, sub=(0, 1), override=dict(top_k=1024, tau=-2.0, refresh_every=0),
+                     check_init=False, wl_kw=dict(decode_steps=8))
+    assert not r["paths"].any()
+    assert max(r["ms"]) > 1024
 
 
 @pytest.mark.slow
@@ -686,8 +700,8 @@ def test_scale_4m_sampled():
     """L0 = 4,194,304 (K and V of the layer 8.6 GB; scores, survivors and
     boundary keys in their workspaces): KV group 1 in lockstep for 4 steps
     with a refresh every 2 steps (the cache from the GPU's initialisation), the
-    reuse unions spanning 16 LDS bitmap windows of 262,144 positions; then the
-    Exact Top-K baseline on KV group 3."""
+    reuse unions merging the sorted supports; then the Exact Top-K baseline on
+    KV group 3."""
     run_lockstep("scale4m", 4, sub=(0, 1), override=dict(refresh_every=2), check_init=False,
                  wl_kw=dict(decode_steps=8))
     run_exact("scale4m", [(1 << 22) + 3], sub=(0, 3), wl_kw=dict(decode_steps=8))
