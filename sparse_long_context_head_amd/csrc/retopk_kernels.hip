@@ -94,6 +94,12 @@ constexpr float kNegInf = -INFINITY;
 constexpr float kPosInf = INFINITY;
 constexpr float kInvSqrtD = 0.08838834764831845f;  // 1 / sqrt(128)
 
+// Every block of the step kernel has kHeadThreads threads (its only launch
+// shape), and its device code uses that constant rather than blockDim.x: the
+// runtime group size lives in the dispatch packet and, being memory, would be
+// read again (a dependent global round trip) after every barrier that clobbers
+// memory.
+
 // Barrier for data shared through LDS only: this wave's LDS operations are
 // complete, then s_barrier. Unlike __syncthreads() it does not wait for the
 // wave's outstanding global loads and stores (which no other wave of the
@@ -239,9 +245,9 @@ __device__ __forceinline__ int wave_slot(bool pred, int* counter) {
 }
 
 // Block-wide exclusive prefix sum of one int per thread. `tmp` holds at
-// least blockDim.x / 64 ints. Every thread of the block must call it.
+// least kHeadThreads / 64 ints. Every thread of the block must call it.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* tmp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kHeadThreads >> 6;
   const int incl = wave_incl_scan(v);
   if (lane == 63) tmp[wave] = incl;
   lds_barrier();
@@ -258,7 +264,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* tmp)
 
 // Block-wide minimum and maximum of one float per thread (tmp: 2 * waves floats).
 __device__ __forceinline__ void block_minmax_f32(float lo, float hi, float* tmp, float* mn, float* mx) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kHeadThreads >> 6;
   hi = wave_max_f32(hi);
   lo = -wave_max_f32(-lo);
   if (lane == 0) {
@@ -277,9 +283,9 @@ __device__ __forceinline__ void block_minmax_f32(float lo, float hi, float* tmp,
 }
 
 // Two block-wide exclusive prefix sums at once (one pair of barriers). tmp:
-// 2 * blockDim.x / 64 ints.
+// 2 * kHeadThreads / 64 ints.
 __device__ __forceinline__ void block_exclusive_scan2(int a, int b, int* ea, int* eb, int* ta, int* tb, int* tmp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kHeadThreads >> 6;
   const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
   if (lane == 63) {
     tmp[2 * wave] = ia;
@@ -303,8 +309,24 @@ __device__ __forceinline__ void block_exclusive_scan2(int a, int b, int* ea, int
   *tb = sb;
 }
 
+// Whether p holds in every thread of the block; also a barrier. votes: two
+// sets of per-wave words, used in turn (par flips at each call, in every
+// thread alike), so that a wave casting the next vote cannot overwrite one
+// that a slower wave is still reading. Every thread of the block must call it.
+__device__ __forceinline__ bool block_all(bool p, int* votes, int& par) {
+  int* v = votes + par * (kHeadThreads / 64);
+  par ^= 1;
+  const uint64_t m = __ballot(!p);
+  if ((threadIdx.x & 63) == 0) v[threadIdx.x >> 6] = m != 0ull ? 1 : 0;
+  lds_barrier();
+  int any = 0;
+#pragma unroll
+  for (int w = 0; w < kHeadThreads / 64; ++w) any |= v[w];
+  return any == 0;
+}
+
 __device__ __forceinline__ float block_max_f32(float v, float* tmp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kHeadThreads >> 6;
   v = wave_max_f32(v);
   if (lane == 0) tmp[wave] = v;
   lds_barrier();
@@ -388,6 +410,7 @@ struct HeadShared {
   __align__(16) float red[kHeadThreads / 16][kHeadDim + 4];  // one row per 16-lane row group (before
                                                              // that, the union's bitmap prefix counts)
   int i0, i1, i2, i3;
+  int vote[2 * (kHeadThreads / 64)];  // block_all's votes
   double d0;
 };
 static_assert(sizeof(HeadShared::red) >= kPfxDwords * 4, "bitmap prefix counts in the reduction rows");
@@ -455,7 +478,7 @@ __device__ __forceinline__ void pick_bin2048(HeadShared& sh, int rem) {
 
 __device__ __forceinline__ void clear_whist(HeadShared& sh) {
   int4* w = reinterpret_cast<int4*>(&sh.whist[0][0]);
-  for (int i = threadIdx.x; i < (kHeadThreads / 64) * 64; i += blockDim.x) w[i] = make_int4(0, 0, 0, 0);
+  for (int i = threadIdx.x; i < (kHeadThreads / 64) * 64; i += kHeadThreads) w[i] = make_int4(0, 0, 0, 0);
 }
 
 // Radix select of the k largest of n scores (LDS) under (score desc,
@@ -470,7 +493,7 @@ __device__ __forceinline__ uint32_t radix_kth(const float* sc, int n, int k, Hea
   int* bins = &sh.whist[0][0];  // 2048 bins for the first pass
   reinterpret_cast<int4*>(bins)[threadIdx.x] = make_int4(0, 0, 0, 0);
   lds_barrier();
-  for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&bins[order_key(sc[i]) >> 21], 1);
+  for (int i = threadIdx.x; i < n; i += kHeadThreads) atomicAdd(&bins[order_key(sc[i]) >> 21], 1);
   lds_barrier();
   {
     const int4 h = reinterpret_cast<const int4*>(bins)[511 - threadIdx.x];  // bins 2047-4t .. 2044-4t
@@ -500,7 +523,7 @@ __device__ __forceinline__ uint32_t radix_kth(const float* sc, int n, int k, Hea
     const uint32_t dmask = shift == 0 ? 31u : 255u;
     clear_whist(sh);
     lds_barrier();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    for (int i = threadIdx.x; i < n; i += kHeadThreads) {
       const uint32_t u = order_key(sc[i]);
       if ((u & mask) == prefix) atomicAdd(&sh.whist[wave][(u >> shift) & dmask], 1);
     }
@@ -523,7 +546,7 @@ __device__ __forceinline__ uint32_t radix_kth(const float* sc, int n, int k, Hea
 // call it.
 __device__ __forceinline__ int select_in_order(const int32_t* idx, const float* sc, int n, uint32_t T, uint32_t mask,
                                                int need, int32_t* out_idx, float* out_sc, HeadShared& sh) {
-  const int per = (n + blockDim.x - 1) / blockDim.x;
+  const int per = (n + kHeadThreads - 1) / kHeadThreads;
   const int i0 = threadIdx.x * per, i1 = min(i0 + per, n);
   int gt = 0, eq = 0;
   for (int i = i0; i < i1; ++i) {
@@ -567,7 +590,7 @@ __device__ __forceinline__ int rerank_linear(const int32_t* idx, const float* sc
   reinterpret_cast<int4*>(bins)[tid] = make_int4(0, 0, 0, 0);
   if (tid == 0) sh.i3 = 0;
   lds_barrier();
-  for (int i = tid; i < M; i += blockDim.x) atomicAdd(&bins[bin_of(sc[i])], 1);
+  for (int i = tid; i < M; i += kHeadThreads) atomicAdd(&bins[bin_of(sc[i])], 1);
   lds_barrier();
   {
     const int4 h = reinterpret_cast<const int4*>(bins)[511 - tid];  // bins 2047-4t .. 2044-4t
@@ -593,7 +616,7 @@ __device__ __forceinline__ int rerank_linear(const int32_t* idx, const float* sc
   if (need < cnt) {
     if (cnt > 64) return -1;  // uniform
     // the boundary bin's entries, listed by one wave-aggregated pass
-    for (int i0 = 0; i0 < M; i0 += blockDim.x) {
+    for (int i0 = 0; i0 < M; i0 += kHeadThreads) {
       const int i = i0 + tid;
       const bool in = i < M && bin_of(sc[min(i, M - 1)]) == b1;
       const int o = wave_slot(in, &sh.i3);
@@ -615,7 +638,7 @@ __device__ __forceinline__ int rerank_linear(const int32_t* idx, const float* sc
     lds_barrier();
   }
   // kept: bin > b1, or bin == b1 and (all of the bin kept, or flagged)
-  const int per = (M + blockDim.x - 1) / blockDim.x;
+  const int per = (M + kHeadThreads - 1) / kHeadThreads;
   const int i0 = tid * per, i1 = min(i0 + per, M);
   auto kept = [&](int i) {
     const int bn = bin_of(sc[i]);
@@ -642,7 +665,7 @@ __device__ __forceinline__ int rerank_linear(const int32_t* idx, const float* sc
 // threads add the rows of one dim each (conflict-free LDS columns) and write
 // out (see attend). Every thread of the block must call it.
 __device__ __forceinline__ void attend_reduce(float (&acc)[8], float z, float* out, float* out_z, HeadShared& sh) {
-  const int sub = threadIdx.x & 15, rg = threadIdx.x >> 4, nrg = blockDim.x >> 4;
+  const int sub = threadIdx.x & 15, rg = threadIdx.x >> 4, nrg = kHeadThreads >> 4;
   float4* r = reinterpret_cast<float4*>(&sh.red[rg][8 * sub]);
   r[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
   r[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
@@ -675,8 +698,8 @@ __device__ __forceinline__ void attend_reduce(float (&acc)[8], float z, float* o
 // the block must call it.
 __device__ __forceinline__ void attend(const int32_t* sel, float* sc, int n, float mx, const uint16_t* vb, float* out,
                                        float* out_z, HeadShared& sh) {
-  const int sub = threadIdx.x & 15, rg = threadIdx.x >> 4, rpr = blockDim.x >> 4;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) sc[i] = expf((sc[i] - mx) * kInvSqrtD);
+  const int sub = threadIdx.x & 15, rg = threadIdx.x >> 4, rpr = kHeadThreads >> 4;
+  for (int i = threadIdx.x; i < n; i += kHeadThreads) sc[i] = expf((sc[i] - mx) * kInvSqrtD);
   lds_barrier();
   constexpr int U = 16;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -735,8 +758,8 @@ template <typename Table>
 __device__ __forceinline__ void cache_push(const Dims& d, Table& b, int bh, int slot, int count, const float* qbar,
                                            const int32_t* sel, int n) {
   const long e = static_cast<long>(bh) * d.C + slot;
-  for (int t = threadIdx.x; t < kHeadDim; t += blockDim.x) b.cache_qbar[e * kHeadDim + t] = qbar[t];
-  for (int i = threadIdx.x; i < n; i += blockDim.x) b.cache_supp[e * d.K + i] = sel[i];
+  for (int t = threadIdx.x; t < kHeadDim; t += kHeadThreads) b.cache_qbar[e * kHeadDim + t] = qbar[t];
+  for (int i = threadIdx.x; i < n; i += kHeadThreads) b.cache_supp[e * d.K + i] = sel[i];
   if (threadIdx.x == 0) {
     b.cache_len[e] = n;
     b.fifo[2 * bh] = (slot + 1) % d.C;
@@ -996,7 +1019,7 @@ constexpr int kMergeE = 4;                      // entries per thread: R K <= 4 
 __device__ __forceinline__ int union_merge(const Dims& d, ConstBufs& b, int bh, int n_ret, int wlo, int32_t* out,
                                            int* lists, int* pre, HeadShared& sh) {
   const int tid = threadIdx.x;
-  for (int j0 = 0; j0 < d.K; j0 += blockDim.x) {
+  for (int j0 = 0; j0 < d.K; j0 += kHeadThreads) {
     const int j = j0 + tid;
     for (int r0 = 0; r0 < n_ret; r0 += 4) {
       int x[4];
@@ -1303,7 +1326,7 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
       bitmap_clear(bm);
       lds_barrier();
     }
-    for (int j0 = 0; j0 < d.K; j0 += blockDim.x) {
+    for (int j0 = 0; j0 < d.K; j0 += kHeadThreads) {
       const int j = j0 + tid;
       for (int r0 = 0; r0 < n_ret; r0 += 4) {
         int x[4];
@@ -1328,7 +1351,7 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
     // the positions come out ascending; copies of one position in several
     // supports write the same value to the same slot.
     const int nset = bitmap_prefix(bm, pfx, sh.tmp);
-    for (int i = tid; i < n_ret * d.K; i += blockDim.x) {
+    for (int i = tid; i < n_ret * d.K; i += kHeadThreads) {
       const int y = stash[i];
       if (y >= 0) s_cand[M + bitmap_rank(bm, pfx, y)] = base + y;
     }
@@ -1336,19 +1359,14 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
     if (base + kBitmapWords * 32 < wlo) lds_barrier();  // (the next window clears the bitmap; after the
                                                         // last one, the window append below is disjoint)
   }
-  for (int x = wlo + tid; x < length; x += blockDim.x) s_cand[M + (x - wlo)] = x;
+  for (int x = wlo + tid; x < length; x += kHeadThreads) s_cand[M + (x - wlo)] = x;
   M += length - wlo;
   lds_barrier();
-  for (int i = tid; i < M; i += blockDim.x) b.cand[static_cast<long>(bh) * d.cand_cap + i] = s_cand[i];
-  if (tid == 0) {
-    b.m[bh] = M;
-    if (stats_slot >= 0) b.st_m[static_cast<long>(stats_slot) * d.B * d.Hq + bh] = M;
-  }
 
   // ---- candidate scores (Eq. 10) ----
   const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
   const uint16_t* vb = v + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
-  const int rg = tid >> 4, rpr = blockDim.x >> 4;
+  const int rg = tid >> 4, rpr = kHeadThreads >> 4;
   float mx = kNegInf, mn = kPosInf;
   {
     // kCandU rows in flight per 16-lane group; a wider round for candidate
@@ -1359,6 +1377,13 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
       cand_scores<kCandWide>(kb, s_cand, M, qw, rg, rpr, part, s_sc, mn, mx);
     else
       cand_scores<kCandU>(kb, s_cand, M, qw, rg, rpr, part, s_sc, mn, mx);
+  }
+  // A_t and M_t (outputs only): stored once the key rows are in, so that no
+  // store is outstanding when their loads are issued
+  for (int i = tid; i < M; i += kHeadThreads) b.cand[static_cast<long>(bh) * d.cand_cap + i] = s_cand[i];
+  if (tid == 0) {
+    b.m[bh] = M;
+    if (stats_slot >= 0) b.st_m[static_cast<long>(stats_slot) * d.B * d.Hq + bh] = M;
   }
   // the scores' extremes: per wave before the barrier that publishes the
   // scores, across the waves after it
@@ -1385,7 +1410,7 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
   uint8_t* flag = reinterpret_cast<uint8_t*>(dyn + 8 * static_cast<size_t>(d.K));
   int n;
   if (M <= d.K) {
-    for (int i = tid; i < M; i += blockDim.x) {
+    for (int i = tid; i < M; i += kHeadThreads) {
       s_sel[i] = s_cand[i];
       s_selsc[i] = s_sc[i];
     }
@@ -1402,7 +1427,7 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
   }
 
   // ---- reuse path: softmax-V (Eq. 12) and cache update ----
-  for (int i = tid; i < n; i += blockDim.x) {
+  for (int i = tid; i < n; i += kHeadThreads) {
     b.sel[static_cast<long>(bh) * d.K + i] = s_sel[i];
     b.selsc[static_cast<long>(bh) * d.K + i] = s_selsc[i];
   }
@@ -1431,7 +1456,7 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const BufsDev& b, int
   const int tid = threadIdx.x;
   const int bb = bh / d.Hq, g = (bh % d.Hq) / d.G;
   float mx = kNegInf;
-  for (int i = tid; i < n; i += blockDim.x) {
+  for (int i = tid; i < n; i += kHeadThreads) {
     mx = fmaxf(mx, s_selsc[i]);
     b.sel[static_cast<long>(bh) * d.K + i] = s_sel[i];
     b.selsc[static_cast<long>(bh) * d.K + i] = s_selsc[i];
@@ -1439,7 +1464,7 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const BufsDev& b, int
   mx = block_max_f32(mx, reinterpret_cast<float*>(sh.tmp));
   if (tid == 0) b.sellen[bh] = n;
   if (sel_out != nullptr)
-    for (int i = tid; i < d.K; i += blockDim.x) sel_out[static_cast<long>(bh) * d.K + i] = i < n ? s_sel[i] : -1;
+    for (int i = tid; i < d.K; i += kHeadThreads) sel_out[static_cast<long>(bh) * d.K + i] = i < n ? s_sel[i] : -1;
   if (v != nullptr && out != nullptr) {
     const uint16_t* vb = v + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
     attend(s_sel, s_selsc, n, mx, vb, out + static_cast<long>(bh) * kHeadDim, nullptr, sh);
@@ -1525,7 +1550,7 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // group e (one thread per work group; bounded in time, a timeout sets the
 // device error word). Every thread of the block must call it.
 __device__ __forceinline__ bool wait_group(const int32_t* flags, long T, int nW, int length, int ne, int e,
-                                           int call_flag, int32_t* err, int* s_go) {
+                                           int call_flag, int32_t* err, int* s_go, int* votes, int& vpar) {
   const int tid = threadIdx.x;
   bool chk = false;
   if (tid < nW) {
@@ -1536,7 +1561,7 @@ __device__ __forceinline__ bool wait_group(const int32_t* flags, long T, int nW,
   const long long t0 = __builtin_amdgcn_s_memrealtime();
   for (;;) {
     const bool ok = !chk || load_shared(flags + tid * kFlagStride) == call_flag;
-    if (__syncthreads_and(ok)) return true;
+    if (block_all(ok, votes, vpar)) return true;
     if (tid == 0) *s_go = __builtin_amdgcn_s_memrealtime() - t0 >= kWaitTicks ? -1 : 0;
     lds_barrier();
     if (*s_go < 0) {
@@ -1606,7 +1631,7 @@ constexpr int kEmitUGlobal = 32;
 template <bool kLds>
 __device__ __forceinline__ void emit_segment(const Dims& d, const BufsDev& b, int bb, int g, unsigned emask, int row0,
                                              int rend, int length, int w, int par, const float* sc, int stride) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = kHeadThreads >> 6;
   const int G = d.G;
   const int h0 = bb * d.Hq + g * G;  // query head of jj = 0
   const int nrows = rend - row0;
@@ -2004,7 +2029,7 @@ __device__ __forceinline__ void qk_score_kb(const Dims& d, const QkTiles& t, con
 __device__ __forceinline__ int kb_close(const Dims& d, const BufsDev& b, int bb, int g, unsigned emask, int par,
                                         uint2* lists, int cap, int kp, bool last, KbState& ks, int* kcnt,
                                         HeadShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = kHeadThreads >> 6;
   lds_barrier();
   int stride = cap;
   for (int jj = wave; jj < d.G; jj += nw) {
@@ -2071,7 +2096,7 @@ __device__ __forceinline__ int kb_close(const Dims& d, const BufsDev& b, int bb,
 __device__ __forceinline__ void emit_kb(const Dims& d, const BufsDev& b, int bb, int g, unsigned emask, int row0,
                                         int length, int w, int par, const uint2* lists, int stride,
                                         const int* kcnt) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = kHeadThreads >> 6;
   const int G = d.G;
   const int h0 = bb * d.Hq + g * G;
   for (int jj = wave; jj < G; jj += nw) {
@@ -2238,12 +2263,12 @@ __device__ __forceinline__ void finish_phase(const Dims& d, const BufsDev& b, in
     reinterpret_cast<int4*>(bins)[tid] = make_int4(0, 0, 0, 0);
     lds_barrier();
     if (keys_lds) {
-      for (int i = tid; i < n_bd; i += blockDim.x) {
+      for (int i = tid; i < n_bd; i += kHeadThreads) {
         const uint64_t u = lkeys[i];
         if ((u & mask) == prefix) atomicAdd(&bins[(u >> shift) & dmask], 1);
       }
     } else {
-      for (int i = tid; i < n_bd; i += blockDim.x) {
+      for (int i = tid; i < n_bd; i += kHeadThreads) {
         const uint64_t u = gkeys[i];
         if ((u & mask) == prefix) atomicAdd(&bins[(u >> shift) & dmask], 1);
       }
@@ -2297,10 +2322,11 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
                                            const uint16_t* k, const uint16_t* v, float* out, int32_t* sel_out,
                                            int length, int push, int call_flag, int w, int nW, bool all_exact,
                                            int keep, HeadShared& sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kHeadThreads >> 6;
   const int j = lane & 15, kq = lane >> 4;
   const int NG = d.B * d.Hkv, BH = d.B * d.Hq;
   const int par = (call_flag >> 1) & 1;
+  int vpar = 0;  // block_all's vote set
   __shared__ int s_eg[kMaxExactGroups];  // listed group | its exact heads << 16 (bit jj: head jj of the group)
   __shared__ int s_tmp[8];
   __shared__ uint32_t s_ex[kMaxExactGroups * kMaxGroup / 32];  // exact bit of every head
@@ -2318,7 +2344,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
   for (int hh = static_cast<int>(static_cast<long>(w) * BH / nW); hh < static_cast<int>(static_cast<long>(w + 1) * BH / nW);
        ++hh) {
     uint4* hz = reinterpret_cast<uint4*>(b.hist + (static_cast<long>(hh) * 2 + (par ^ 1)) * kNumBins);
-    for (int i = threadIdx.x; i < kNumBins / 4; i += blockDim.x) hz[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = threadIdx.x; i < kNumBins / 4; i += kHeadThreads) hz[i] = make_uint4(0u, 0u, 0u, 0u);
   }
 
   // every head's decision of this call, published by the head work groups
@@ -2326,15 +2352,15 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
   if (!all_exact) {
     int done = 0;
     for (int it = 0; it < kPollRounds; ++it) {
-      for (int i = threadIdx.x; i < (BH + 31) / 32; i += blockDim.x) s_ex[i] = 0u;
+      for (int i = threadIdx.x; i < (BH + 31) / 32; i += kHeadThreads) s_ex[i] = 0u;
       lds_barrier();
       int mine = 1;
-      for (int i = threadIdx.x; i < BH; i += blockDim.x) {
+      for (int i = threadIdx.x; i < BH; i += kHeadThreads) {
         const int x = load_shared(b.dec + i * kFlagStride);
         mine &= (x | 1) == (call_flag | 1);
         if (x & 1) atomicOr(&s_ex[i >> 5], 1u << (i & 31));
       }
-      done = __syncthreads_and(mine);
+      done = block_all(mine, sh.vote, vpar);
       if (done) break;
       __builtin_amdgcn_s_sleep(kPollSleep);
     }
@@ -2347,7 +2373,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
   // ordered list of the KV groups holding an exact head
   int ne;
   {
-    const int per = (NG + blockDim.x - 1) / blockDim.x;
+    const int per = (NG + kHeadThreads - 1) / kHeadThreads;
     const int g0 = min(static_cast<int>(threadIdx.x) * per, NG), g1 = min(g0 + per, NG);
     int cnt = 0;
     for (int bg = g0; bg < g1; ++bg) {
@@ -2453,7 +2479,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
     lds_barrier();  // the previous segment's histogram flush is done
     for (int jj = 0; jj < d.G; ++jj)
       if ((emask >> jj) & 1)
-        for (int i = threadIdx.x; i < kNumBins; i += blockDim.x) s_hist[jj * kNumBins + i] = 0u;
+        for (int i = threadIdx.x; i < kNumBins; i += kHeadThreads) s_hist[jj * kNumBins + i] = 0u;
     lds_barrier();
     // row r of the segment goes to LDS row lb + (r - row0) of head j, or to
     // the workspace row
@@ -2474,7 +2500,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
     for (int jj = 0; jj < d.G; ++jj) {
       if (!((emask >> jj) & 1)) continue;
       uint32_t* ghist = b.hist + (static_cast<long>(bb * d.Hq + g * d.G + jj) * 2 + par) * kNumBins;
-      for (int i = threadIdx.x; i < kNumBins; i += blockDim.x) {
+      for (int i = threadIdx.x; i < kNumBins; i += kHeadThreads) {
         const uint32_t c = s_hist[jj * kNumBins + i];
         if (c) atomicAdd(&ghist[i], c);
       }
@@ -2499,7 +2525,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
     const int row0 = r, rend = e == e1 ? r1 : length;
     if (row0 >= rend) continue;
     const int bg = s_eg[e] & 0xffff;
-    if (!wait_group(b.wdone, T, nW, length, ne, e, call_flag, b.err, &sh.i3)) return;
+    if (!wait_group(b.wdone, T, nW, length, ne, e, call_flag, b.err, &sh.i3, sh.vote, vpar)) return;
     if (use_kb) {
       emit_kb(d, b, bg / d.Hkv, bg % d.Hkv, static_cast<unsigned>(s_eg[e]) >> 16, row0, length, w, par,
               reinterpret_cast<const uint2*>(dyn + kb_tc_bytes(d)) + static_cast<long>(si) * d.G * kp,
@@ -2527,7 +2553,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
       const int bh = (bg / d.Hkv) * d.Hq + (bg % d.Hkv) * d.G + nth_bit(emask, m);
       // the head's boundary (its group is fully scored once this work group's
       // own segments have passed phase 2; else wait for that here)
-      if (!wait_group(b.wdone, T, nW, length, ne, e, call_flag, b.err, &sh.i3)) return;
+      if (!wait_group(b.wdone, T, nW, length, ne, e, call_flag, b.err, &sh.i3, sh.vote, vpar)) return;
       if ((threadIdx.x >> 6) == 0) {
         const int3 bd = wave_boundary(b.hist + (static_cast<long>(bh) * 2 + par) * kNumBins, min(d.K, length));
         if (threadIdx.x == 0) {
@@ -2536,7 +2562,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
           sh.i2 = bd.z;
         }
       }
-      if (!wait_group(b.wdone + d.n_cu * kFlagStride, T, nW, length, ne, e, call_flag, b.err, &sh.i3)) return;
+      if (!wait_group(b.wdone + d.n_cu * kFlagStride, T, nW, length, ne, e, call_flag, b.err, &sh.i3, sh.vote, vpar)) return;
       const int3 bd = make_int3(sh.i0, sh.i1, sh.i2);
       lds_barrier();  // (the finish reuses sh.i0 ..)
       finish_phase(d, b, bh, q, q_sb, q_sh, v, out, sel_out, length, push, T, nW, ne, e, bd, sh, dyn);
