@@ -1362,6 +1362,11 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
   for (int x = wlo + tid; x < length; x += kHeadThreads) s_cand[M + (x - wlo)] = x;
   M += length - wlo;
   lds_barrier();
+  for (int i = tid; i < M; i += kHeadThreads) b.cand[static_cast<long>(bh) * d.cand_cap + i] = s_cand[i];
+  if (tid == 0) {
+    b.m[bh] = M;
+    if (stats_slot >= 0) b.st_m[static_cast<long>(stats_slot) * d.B * d.Hq + bh] = M;
+  }
 
   // ---- candidate scores (Eq. 10) ----
   const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
@@ -1377,13 +1382,6 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
       cand_scores<kCandWide>(kb, s_cand, M, qw, rg, rpr, part, s_sc, mn, mx);
     else
       cand_scores<kCandU>(kb, s_cand, M, qw, rg, rpr, part, s_sc, mn, mx);
-  }
-  // A_t and M_t (outputs only): stored once the key rows are in, so that no
-  // store is outstanding when their loads are issued
-  for (int i = tid; i < M; i += kHeadThreads) b.cand[static_cast<long>(bh) * d.cand_cap + i] = s_cand[i];
-  if (tid == 0) {
-    b.m[bh] = M;
-    if (stats_slot >= 0) b.st_m[static_cast<long>(stats_slot) * d.B * d.Hq + bh] = M;
   }
   // the scores' extremes: per wave before the barrier that publishes the
   // scores, across the waves after it
