@@ -541,11 +541,12 @@ __device__ __forceinline__ uint32_t radix_kth(const float* sc, int n, int k, Hea
 }
 
 // Keep, in position order, the entries with (key & mask) > T and the first
-// `need` entries with (key & mask) == T; write idx[i] / sc[i] of the kept
-// positions to out_idx / out_sc. Returns the number kept. Every thread must
-// call it.
+// `need` entries with (key & mask) == T; write idx[i] of the kept positions
+// to out_idx and g_idx, their weight exp((sc[i] - mx) / sqrt(d)) to out_w and
+// sc[i] to g_sc. Returns the number kept. Every thread must call it.
 __device__ __forceinline__ int select_in_order(const int32_t* idx, const float* sc, int n, uint32_t T, uint32_t mask,
-                                               int need, int32_t* out_idx, float* out_sc, HeadShared& sh) {
+                                               int need, float mx, int32_t* out_idx, float* out_w, int32_t* g_idx,
+                                               float* g_sc, HeadShared& sh) {
   const int per = (n + kHeadThreads - 1) / kHeadThreads;
   const int i0 = threadIdx.x * per, i1 = min(i0 + per, n);
   int gt = 0, eq = 0;
@@ -562,7 +563,9 @@ __device__ __forceinline__ int select_in_order(const int32_t* idx, const float* 
     const uint32_t u = order_key(sc[i]) & mask;
     if ((u > T) || (u == T && e < need)) {
       out_idx[o] = idx[i];
-      out_sc[o] = sc[i];
+      out_w[o] = expf((sc[i] - mx) * kInvSqrtD);
+      g_idx[o] = idx[i];
+      g_sc[o] = sc[i];
       ++o;
     }
     e += (u == T);
@@ -577,41 +580,45 @@ __device__ __forceinline__ int select_in_order(const int32_t* idx, const float* 
 // K-th largest is kept whole. When only some entries of that boundary bin are
 // kept (at most 64 of them), one wave ranks them exactly by (score desc,
 // index asc) and flags the kept ones. The kept entries are written in
-// candidate order (ascending index) to out_idx / out_sc; returns K, or -1
-// (nothing written) when the boundary bin is too crowded, for the caller's
-// order-key radix select. flag: M bytes of LDS scratch. Every thread must
-// call it.
+// candidate order (ascending index): their indices to out_idx and g_idx,
+// their weights exp((sc - mx) / sqrt(d)) to out_w and their scores to g_sc.
+// Returns K, or -1 (nothing written) when the boundary bin is too crowded,
+// for the caller's order-key radix select. The caller zeroes the 2048 bins
+// (sh.whist) and sh.i3 beforehand, with a barrier since. flag: M bytes of LDS
+// scratch. Every thread must call it.
 __device__ __forceinline__ int rerank_linear(const int32_t* idx, const float* sc, int M, int K, float mn, float mx,
-                                             int32_t* out_idx, float* out_sc, uint8_t* flag, HeadShared& sh) {
+                                             int32_t* out_idx, float* out_w, int32_t* g_idx, float* g_sc,
+                                             uint8_t* flag, HeadShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float scale = 2048.f / (mx - mn);
   auto bin_of = [&](float v) { return min(2047, static_cast<int>((v - mn) * scale)); };
   int* bins = &sh.whist[0][0];  // 2048 bins
-  reinterpret_cast<int4*>(bins)[tid] = make_int4(0, 0, 0, 0);
-  if (tid == 0) sh.i3 = 0;
-  lds_barrier();
   for (int i = tid; i < M; i += kHeadThreads) atomicAdd(&bins[bin_of(sc[i])], 1);
   lds_barrier();
-  {
-    const int4 h = reinterpret_cast<const int4*>(bins)[511 - tid];  // bins 2047-4t .. 2044-4t
-    const int c[4] = {h.w, h.z, h.y, h.x};
-    const int s4 = c[0] + c[1] + c[2] + c[3];
-    int tot;
-    int run = block_exclusive_scan(s4, &tot, sh.tmp);
-    if (run < K && run + s4 >= K) {
+  if (wave == 0) {
+    // the bin holding the K-th largest, from the top: lane l sums bins
+    // 2047 - 32l .. 2016 - 32l; then the lanes take the 32 bins of the lane
+    // where the count reaches K, one each (M > K, so there is one)
+    const int4* b4 = reinterpret_cast<const int4*>(bins) + (2016 - 32 * lane) / 4;
+    int s32 = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (run + c[j] >= K) {
-          sh.i0 = 2047 - 4 * tid - j;
-          sh.i1 = K - run;
-          sh.i2 = c[j];
-          break;
-        }
-        run += c[j];
-      }
+    for (int k = 0; k < 8; ++k) {
+      const int4 h = b4[k];
+      s32 += h.x + h.y + h.z + h.w;
     }
-    lds_barrier();
+    const int incl = wave_incl_scan(s32);
+    const int L = __ffsll(static_cast<long long>(__ballot(incl - s32 < K && incl >= K))) - 1;
+    const int runL = __builtin_amdgcn_readlane(incl - s32, L);
+    const int c = lane < 32 ? bins[2047 - 32 * L - lane] : 0;
+    const int ci = wave_incl_scan(c);
+    const int j = __ffsll(static_cast<long long>(__ballot(lane < 32 && runL + ci >= K))) - 1;
+    if (lane == j) {
+      sh.i0 = 2047 - 32 * L - j;
+      sh.i1 = K - (runL + ci - c);
+      sh.i2 = c;
+    }
   }
+  lds_barrier();
   const int b1 = sh.i0, need = sh.i1, cnt = sh.i2;
   if (need < cnt) {
     if (cnt > 64) return -1;  // uniform
@@ -651,7 +658,9 @@ __device__ __forceinline__ int rerank_linear(const int32_t* idx, const float* sc
   for (int i = i0; i < i1; ++i) {
     if (kept(i)) {
       out_idx[o] = idx[i];
-      out_sc[o] = sc[i];
+      out_w[o] = expf((sc[i] - mx) * kInvSqrtD);
+      g_idx[o] = idx[i];
+      g_sc[o] = sc[i];
       ++o;
     }
   }
@@ -696,11 +705,20 @@ __device__ __forceinline__ void attend_reduce(float (&acc)[8], float z, float* o
 // of the weights to *out_z, so that disjoint slices of one support can be
 // merged by adding them. Nothing is written when out is NULL. Every thread of
 // the block must call it.
+__device__ __forceinline__ void attend_w(const int32_t* sel, const float* sc, int n, const uint16_t* vb, float* out,
+                                         float* out_z, HeadShared& sh);
 __device__ __forceinline__ void attend(const int32_t* sel, float* sc, int n, float mx, const uint16_t* vb, float* out,
                                        float* out_z, HeadShared& sh) {
-  const int sub = threadIdx.x & 15, rg = threadIdx.x >> 4, rpr = kHeadThreads >> 4;
   for (int i = threadIdx.x; i < n; i += kHeadThreads) sc[i] = expf((sc[i] - mx) * kInvSqrtD);
   lds_barrier();
+  attend_w(sel, sc, n, vb, out, out_z, sh);
+}
+
+// The same with the weights already in sc[0 .. n) (LDS, published by a
+// barrier). Every thread of the block must call it.
+__device__ __forceinline__ void attend_w(const int32_t* sel, const float* sc, int n, const uint16_t* vb, float* out,
+                                         float* out_z, HeadShared& sh) {
+  const int sub = threadIdx.x & 15, rg = threadIdx.x >> 4, rpr = kHeadThreads >> 4;
   constexpr int U = 16;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float z = 0.f;
@@ -1362,6 +1380,9 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
   for (int x = wlo + tid; x < length; x += kHeadThreads) s_cand[M + (x - wlo)] = x;
   M += length - wlo;
   lds_barrier();
+  // the rerank's 2048 bins, zeroed now (ordered before it by the barriers in between)
+  reinterpret_cast<int4*>(&sh.whist[0][0])[tid] = make_int4(0, 0, 0, 0);
+  if (tid == 0) sh.i3 = 0;
   for (int i = tid; i < M; i += kHeadThreads) b.cand[static_cast<long>(bh) * d.cand_cap + i] = s_cand[i];
   if (tid == 0) {
     b.m[bh] = M;
@@ -1406,31 +1427,35 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
   // ---- rerank (Eq. 11) ----
   // LDS after S_hat and its scores in region0: boundary flags of the linear rerank
   uint8_t* flag = reinterpret_cast<uint8_t*>(dyn + 8 * static_cast<size_t>(d.K));
+  // S_t (ascending index) with the softmax weights of Eq. 12 in LDS, and
+  // with its scores to the step outputs
+  int32_t* g_sel = b.sel + static_cast<long>(bh) * d.K;
+  float* g_selsc = b.selsc + static_cast<long>(bh) * d.K;
   int n;
   if (M <= d.K) {
     for (int i = tid; i < M; i += kHeadThreads) {
-      s_sel[i] = s_cand[i];
-      s_selsc[i] = s_sc[i];
+      const int x = s_cand[i];
+      const float sv = s_sc[i];
+      s_sel[i] = x;
+      s_selsc[i] = expf((sv - mx) * kInvSqrtD);
+      g_sel[i] = x;
+      g_selsc[i] = sv;
     }
     n = M;
     lds_barrier();
   } else {
-    n = (mx > mn) ? rerank_linear(s_cand, s_sc, M, d.K, mn, mx, s_sel, s_selsc, flag, sh) : -1;
+    n = (mx > mn) ? rerank_linear(s_cand, s_sc, M, d.K, mn, mx, s_sel, s_selsc, g_sel, g_selsc, flag, sh) : -1;
     if (n < 0) {
       int need;
       uint32_t mask;
       const uint32_t T = radix_kth(s_sc, M, d.K, sh, &mask, &need);
-      n = select_in_order(s_cand, s_sc, M, T, mask, need, s_sel, s_selsc, sh);
+      n = select_in_order(s_cand, s_sc, M, T, mask, need, mx, s_sel, s_selsc, g_sel, g_selsc, sh);
     }
   }
 
   // ---- reuse path: softmax-V (Eq. 12) and cache update ----
-  for (int i = tid; i < n; i += kHeadThreads) {
-    b.sel[static_cast<long>(bh) * d.K + i] = s_sel[i];
-    b.selsc[static_cast<long>(bh) * d.K + i] = s_selsc[i];
-  }
   if (tid == 0) b.sellen[bh] = n;
-  attend(s_sel, s_selsc, n, mx, vb, out + static_cast<long>(bh) * kHeadDim, nullptr, sh);
+  attend_w(s_sel, s_selsc, n, vb, out + static_cast<long>(bh) * kHeadDim, nullptr, sh);
   cache_push(d, b, bh, fifo_head, count, sh.qbar, s_sel, n);
 }
 
