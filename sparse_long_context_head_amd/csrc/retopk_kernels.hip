@@ -411,7 +411,6 @@ struct HeadShared {
                                                              // that, the union's bitmap prefix counts)
   int i0, i1, i2, i3;
   int vote[2 * (kHeadThreads / 64)];  // block_all's votes
-  double d0;
 };
 static_assert(sizeof(HeadShared::red) >= kPfxDwords * 4, "bitmap prefix counts in the reduction rows");
 // the per-head kernels add at most 2 KiB of their own to it; LDS is 160 KiB per work group
@@ -1259,29 +1258,26 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
     }
     lds_barrier();
     // the path rule needs only rho_max: publish the decision before ranking
-    // (recent-R retrieval: rho_max over the R newest entries only)
-    if (wave == 0) {
-      const int lo = d.recent ? max(0, count - d.R) : 0;
-      const double mxr = wave_max_f64(lane < count && lane >= lo ? sh.rho[lane] : -INFINITY);
-      if (lane == 0) {
-        store_shared(b.dec + bh * kFlagStride, call_flag | ((refresh || count == 0 || mxr < d.tau) ? 1 : 0));
-        if (d.recent) sh.d0 = mxr;
-      }
-    }
+    // (recent-R retrieval: rho_max over the R newest entries only). Every
+    // wave finds it, and every wave finds the ranks below, so that the union
+    // needs no further barrier.
+    const double v = lane < count ? sh.rho[lane] : -INFINITY;  // FIFO position lane
+    const int lo = d.recent ? max(0, count - d.R) : 0;
+    const double mxr = wave_max_f64(lane < count && lane >= lo ? v : -INFINITY);
+    if (tid == 0)
+      store_shared(b.dec + bh * kFlagStride, call_flag | ((refresh || count == 0 || mxr < d.tau) ? 1 : 0));
     // Rank of FIFO position p under (rho desc, position asc), counted in
     // parallel: wave w compares every position with positions w, w+8, ...
     {
-      const int p = lane;
-      const double v = (p < count) ? sh.rho[p] : -INFINITY;
       int r = 0;
       for (int p2 = wave; p2 < count; p2 += kHeadThreads / 64) {
         const double u = sh.rho[p2];
-        r += (u > v) || (u == v && p2 < p);
+        r += (u > v) || (u == v && p2 < lane);
       }
-      s_rank[wave][p] = r;
+      s_rank[wave][lane] = r;
     }
     lds_barrier();
-    if (wave == 0) {
+    {
       int rank = 0;
 #pragma unroll
       for (int w = 0; w < kHeadThreads / 64; ++w) rank += s_rank[w][lane];
@@ -1289,15 +1285,17 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
       if (lane < count && rank < d.R) {
         int slot = oldest + lane;
         if (slot >= d.C) slot -= d.C;
-        b.ret[bh * d.R + rank] = lane;
-        b.retslot[bh * d.R + rank] = slot;
-        sh.rslot[rank] = slot;
-        if (rank == 0 && !d.recent) sh.d0 = sh.rho[lane];
+        sh.rslot[rank] = slot;  // the same value from every wave; each reads back its own
+        if (wave == 0) {
+          b.ret[bh * d.R + rank] = lane;
+          b.retslot[bh * d.R + rank] = slot;
+        }
       }
     }
     n_ret = min(d.R, count);
-    lds_barrier();
-    if (count > 0) rho_max = sh.d0;
+    // (the best entry's rho is the maximum: mxr over every entry, or over the
+    // R newest for recent-R, where the path rule takes it)
+    if (count > 0) rho_max = mxr;
     exact = refresh || count == 0 || rho_max < d.tau;
   }
   if (tid >= n_ret && tid < d.R) {
