@@ -245,7 +245,10 @@ __device__ __forceinline__ int wave_slot(bool pred, int* counter) {
 }
 
 // Block-wide exclusive prefix sum of one int per thread. `tmp` holds at
-// least kHeadThreads / 64 ints. Every thread of the block must call it.
+// least kHeadThreads / 64 ints. With kTail, a barrier at the end lets the
+// caller reuse tmp at once; without it, tmp must not be written again before
+// the next barrier. Every thread of the block must call it.
+template <bool kTail = true>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kHeadThreads >> 6;
   const int incl = wave_incl_scan(v);
@@ -257,7 +260,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* tmp)
     if (w < wave) before += x;
     tot += x;
   }
-  lds_barrier();
+  if (kTail) lds_barrier();
   *total = tot;
   return before + incl - v;
 }
@@ -372,7 +375,7 @@ __device__ __forceinline__ int bitmap_prefix(const uint32_t* bm, uint32_t* pfx, 
     run += __popc(p[i]);
   }
   int tot;
-  const int base = block_exclusive_scan(run, &tot, tmp);
+  const int base = block_exclusive_scan<false>(run, &tot, tmp);  // (tmp is next written after the barrier below)
   uint32_t* o = pfx + t * (kSliceWords / 2) + (t >> 2);
 #pragma unroll
   for (int i = 0; i < kSliceWords / 2; ++i)
@@ -1367,9 +1370,18 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
     // the positions come out ascending; copies of one position in several
     // supports write the same value to the same slot.
     const int nset = bitmap_prefix(bm, pfx, sh.tmp);
-    for (int i = tid; i < n_ret * d.K; i += kHeadThreads) {
-      const int y = stash[i];
-      if (y >= 0) s_cand[M + bitmap_rank(bm, pfx, y)] = base + y;
+    const int nrk = n_ret * d.K;
+    for (int i0 = 0; i0 < nrk; i0 += 4 * kHeadThreads) {
+      // four entries per thread at once, so that their LDS reads overlap
+      int y[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kHeadThreads + tid;
+        y[u] = i < nrk ? stash[i] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (y[u] >= 0) s_cand[M + bitmap_rank(bm, pfx, y[u])] = base + y[u];
     }
     M += nset;
     if (base + kBitmapWords * 32 < wlo) lds_barrier();  // (the next window clears the bitmap; after the
