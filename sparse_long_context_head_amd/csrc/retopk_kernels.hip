@@ -462,7 +462,7 @@ __device__ __forceinline__ void pick_bin2048(HeadShared& sh, int rem) {
   const int c[4] = {h.w, h.z, h.y, h.x};
   const int s4 = c[0] + c[1] + c[2] + c[3];
   int tot;
-  int run = block_exclusive_scan(s4, &tot, sh.tmp);
+  int run = block_exclusive_scan<false>(s4, &tot, sh.tmp);  // (tmp is next written after the barrier below)
   if (run < rem && run + s4 >= rem) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -502,7 +502,7 @@ __device__ __forceinline__ uint32_t radix_kth(const float* sc, int n, int k, Hea
     const int c[4] = {h.w, h.z, h.y, h.x};
     const int s4 = c[0] + c[1] + c[2] + c[3];
     int tot;
-    int run = block_exclusive_scan(s4, &tot, sh.tmp);
+    int run = block_exclusive_scan<false>(s4, &tot, sh.tmp);  // (tmp is next written after the barrier below)
     if (run < k && run + s4 >= k) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -558,7 +558,7 @@ __device__ __forceinline__ int select_in_order(const int32_t* idx, const float* 
     eq += u == T;
   }
   int tot;
-  const int pre = block_exclusive_scan((eq << 16) | gt, &tot, sh.tmp);  // n < 2^15
+  const int pre = block_exclusive_scan<false>((eq << 16) | gt, &tot, sh.tmp);  // n < 2^15; barrier below
   int e = pre >> 16;
   int o = (pre & 0xffff) + min(e, need);
   for (int i = i0; i < i1; ++i) {
@@ -656,7 +656,7 @@ __device__ __forceinline__ int rerank_linear(const int32_t* idx, const float* sc
   int k = 0;
   for (int i = i0; i < i1; ++i) k += kept(i);
   int tot;
-  int o = block_exclusive_scan(k, &tot, sh.tmp);
+  int o = block_exclusive_scan<false>(k, &tot, sh.tmp);  // (tmp is next written after the barrier below)
   for (int i = i0; i < i1; ++i) {
     if (kept(i)) {
       out_idx[o] = idx[i];
@@ -1133,7 +1133,7 @@ __device__ __forceinline__ int union_merge(const Dims& d, ConstBufs& b, int bh, 
     }
   }
   int total;
-  int run = block_exclusive_scan(cnt, &total, sh.tmp);
+  int run = block_exclusive_scan<false>(cnt, &total, sh.tmp);  // (tmp is next written after the barrier below)
 #pragma unroll
   for (int e = 0; e < kMergeE; ++e) {
     if (f0 + e < F) pre[f0 + e] = run;
