@@ -1557,11 +1557,23 @@ constexpr int kMaxExactGroups = 1024;  // KV groups (batch x KV heads) the row s
 constexpr int kPollRounds = 20000;     // polls of the decision flags before giving up (several ms)
 
 // Where work group ww's share starts: list position e and row r (rounded
-// down to 16 inside the group; e == ne, r == 0 at the end).
+// down to 16 inside the group; e == ne, r == 0 at the end). The share starts
+// at x = floor(ww T / nW) of the T = ne * length concatenated rows; with
+// ww ne = a nW + b (b < nW) that is x = a length + floor(b length / nW), whose
+// second term is below length: so e = a and r = floor(b length / nW), without
+// 64-bit integer divisions (they expand to long instruction sequences, and
+// every waiting thread evaluates this for its work group). b length < 2^42 is
+// exact in a double, and the quotient, below 2^24, is at least 1 / nW away
+// from the next integer unless it is one, far more than the division's
+// rounding error: its floor is exact.
 __device__ __forceinline__ void split_at(long T, int nW, int length, int ne, int ww, int& e, int& r) {
-  const long x = static_cast<long>(ww) * T / nW;
-  e = static_cast<int>(x / length);
-  r = e < ne ? static_cast<int>(x % length) & ~15 : 0;
+  (void)T;  // = ne * length
+  const uint32_t q = static_cast<uint32_t>(ww) * static_cast<uint32_t>(ne);  // <= 2^10 * 2^10
+  const uint32_t a = q / static_cast<uint32_t>(nW), bq = q - a * static_cast<uint32_t>(nW);
+  const double bl = static_cast<double>(bq) * static_cast<double>(length);
+  const uint32_t rr = static_cast<uint32_t>(bl / static_cast<double>(nW));
+  e = static_cast<int>(a);
+  r = e < ne ? static_cast<int>(rr) & ~15 : 0;
 }
 
 // Rows [lo, hi) of group e in work group ww's share (empty when lo >= hi).
