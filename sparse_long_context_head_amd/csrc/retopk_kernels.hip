@@ -1566,14 +1566,18 @@ constexpr int kPollRounds = 20000;     // polls of the decision flags before giv
 // exact in a double, and the quotient, below 2^24, is at least 1 / nW away
 // from the next integer unless it is one, far more than the division's
 // rounding error: its floor is exact.
+__device__ __forceinline__ void share_start(int nW, int length, int ne, int ww, int& a, int& rr) {
+  const uint32_t q = static_cast<uint32_t>(ww) * static_cast<uint32_t>(ne);  // <= 2^10 * 2^10
+  const uint32_t qa = q / static_cast<uint32_t>(nW), bq = q - qa * static_cast<uint32_t>(nW);
+  const double bl = static_cast<double>(bq) * static_cast<double>(length);
+  a = static_cast<int>(qa);
+  rr = static_cast<int>(bl / static_cast<double>(nW));
+}
 __device__ __forceinline__ void split_at(long T, int nW, int length, int ne, int ww, int& e, int& r) {
   (void)T;  // = ne * length
-  const uint32_t q = static_cast<uint32_t>(ww) * static_cast<uint32_t>(ne);  // <= 2^10 * 2^10
-  const uint32_t a = q / static_cast<uint32_t>(nW), bq = q - a * static_cast<uint32_t>(nW);
-  const double bl = static_cast<double>(bq) * static_cast<double>(length);
-  const uint32_t rr = static_cast<uint32_t>(bl / static_cast<double>(nW));
-  e = static_cast<int>(a);
-  r = e < ne ? static_cast<int>(rr) & ~15 : 0;
+  int rr;
+  share_start(nW, length, ne, ww, e, rr);
+  r = e < ne ? rr & ~15 : 0;
 }
 
 // Rows [lo, hi) of group e in work group ww's share (empty when lo >= hi).
@@ -2386,8 +2390,9 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
 
   // clear the other half of a slice of the heads' histograms for the next call
   // (first, so that a call that gives up below still leaves it clear)
-  for (int hh = static_cast<int>(static_cast<long>(w) * BH / nW); hh < static_cast<int>(static_cast<long>(w + 1) * BH / nW);
-       ++hh) {
+  // (w BH < 2^29: 32-bit divisions)
+  for (int hh = static_cast<int>(static_cast<uint32_t>(w * BH) / static_cast<uint32_t>(nW));
+       hh < static_cast<int>(static_cast<uint32_t>((w + 1) * BH) / static_cast<uint32_t>(nW)); ++hh) {
     uint4* hz = reinterpret_cast<uint4*>(b.hist + (static_cast<long>(hh) * 2 + (par ^ 1)) * kNumBins);
     for (int i = threadIdx.x; i < kNumBins / 4; i += kHeadThreads) hz[i] = make_uint4(0u, 0u, 0u, 0u);
   }
@@ -2558,10 +2563,16 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
 
   // the heads this work group finishes: head m of group e when x_m (see
   // above) falls in [xa, xb)
-  const long xa = static_cast<long>(w) * T / nW, xb = static_cast<long>(w + 1) * T / nW;
-  const int ea = static_cast<int>(xa / length), eb = xb > xa ? static_cast<int>((xb - 1) / length) : ea - 1;
+  // (no 64-bit divisions: the share bounds as in split_at, and
+  // (2m + 1) length < 2^29)
+  int ea, rra, ebb, rrb;
+  share_start(nW, length, ne, w, ea, rra);
+  share_start(nW, length, ne, w + 1, ebb, rrb);
+  const long xa = static_cast<long>(ea) * length + rra, xb = static_cast<long>(ebb) * length + rrb;
+  const int eb = xb > xa ? (rrb > 0 ? ebb : ebb - 1) : ea - 1;  // the group of row xb - 1
   auto owned = [&](int e, int m, int nex) {
-    const long xm = static_cast<long>(e) * length + (static_cast<long>(2 * m + 1) * length) / (2 * nex);
+    const long xm = static_cast<long>(e) * length +
+                    static_cast<uint32_t>((2 * m + 1) * length) / static_cast<uint32_t>(2 * nex);
     return xa <= xm && xm < xb;
   };
 
