@@ -1212,13 +1212,18 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
   const int count = scalar_read(b.fifo + 2 * bh + 1);
   // (also in the exact mode, which does not use them: a branch here made the
   // compiler consume the loads inside it, before the rest were requested)
+  // (a second round of 32 entries only for caches of more than 32)
+  const bool two = d.C > kHeadThreads / 16;
   float4 ent[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int c = min(i * (kHeadThreads / 16) + (tid >> 4), d.C - 1);
-    const float* e = b.cache_qbar + (static_cast<long>(bh) * d.C + c) * kHeadDim + 8 * part;
-    ent[i][0] = *reinterpret_cast<const float4*>(e);
-    ent[i][1] = *reinterpret_cast<const float4*>(e + 4);
+    ent[i][0] = ent[i][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i == 0 || two) {
+      const int c = min(i * (kHeadThreads / 16) + (tid >> 4), d.C - 1);
+      const float* e = b.cache_qbar + (static_cast<long>(bh) * d.C + c) * kHeadDim + 8 * part;
+      ent[i][0] = *reinterpret_cast<const float4*>(e);
+      ent[i][1] = *reinterpret_cast<const float4*>(e + 4);
+    }
   }
   const int len_c = b.cache_len[static_cast<long>(bh) * d.C + min(tid, d.C - 1)];
 
@@ -1240,6 +1245,7 @@ __device__ __forceinline__ void head_role(const Dims& d, ConstBufs& b, const uin
     refresh = d.Tr > 0 && (t_dec % d.Tr) == 0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      if (i == 1 && !two) break;
       const int c = i * (kHeadThreads / 16) + (tid >> 4);
       const float* t = sh.qbar + 8 * part;
       double s = 0.0;
