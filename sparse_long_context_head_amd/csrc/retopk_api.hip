@@ -112,7 +112,7 @@ struct Workspace {
     A(&b.ccnt, BH * d.n_cu);
     A(&b.dec, BH * kFlagStride);
     A(&b.err, 1);
-    A(&b.wdone, 2 * static_cast<size_t>(d.n_cu) * kFlagStride);
+    A(&b.wdone, static_cast<size_t>(d.n_cu) * kFlagStride);
     A(&b.bkeys, BH * d.max_len);
     A(&b.sel, BH * d.K);
     A(&b.selsc, BH * d.K);

@@ -61,13 +61,13 @@ struct Bufs {
   uint2* hits;             // [BH, max_len] survivors (scores in the boundary bin or above) as
                            //   (position, score bits); a score work group's segment [row0, rend)
                            //   writes its own in ascending position order from row0 on
-  int32_t* ccnt;           // [BH, n_cu] survivors per score work group's segment
+  uint2* ccnt;             // [BH, n_cu] (survivors of a score work group's segment, call flag),
+                           //   one 8-byte device-scope store once the survivors are out
   int32_t* dec;            // [BH, kFlagStride] path decision of the current call: call flag | exact
                            //   (one per 128-byte line)
   int32_t* err;            // [1]  sticky device error word (1: a wait of the step kernel timed out)
-  int32_t* wdone;          // [2, n_cu, kFlagStride] per score work group (one per 128-byte line), the
-                           //   call flag once its scores and histogram
-                           //   adds are out (row 0), once its survivors are out (row 1)
+  int32_t* wdone;          // [n_cu, kFlagStride] per score work group (one per 128-byte line), the
+                           //   call flag once its scores and histogram adds are out
   uint64_t* bkeys;         // [BH, max_len] boundary-bin composite keys when more than the LDS holds
   int32_t* sel;            // [BH, K]   S_hat_t ascending
   float* selsc;            // [BH, K]   q.k of S_hat_t

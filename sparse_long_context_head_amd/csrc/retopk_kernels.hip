@@ -63,7 +63,7 @@ struct BufsDev {
   gptr<float> score;
   gptr<uint32_t> hist;
   gptr<uint2> hits;
-  gptr<int32_t> ccnt;
+  gptr<uint2> ccnt;
   gptr<int32_t> dec;
   gptr<int32_t> err;
   gptr<int32_t> wdone;
@@ -1543,12 +1543,14 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const BufsDev& b, int
 //   per exact head reads the head's histogram, finds the bin b1 holding the
 //   K-th largest score, and writes the segment's positions and scores in bin
 //   b1 or above, in ascending position order, to the segment's own region of
-//   the head's survivor row (starting at row0), and their count; the work
-//   group then sets its survivor flag.
+//   the head's survivor row (starting at row0); once they are stored, the
+//   wave publishes their count together with the call flag (one 8-byte
+//   store per head and work group).
 // Phase 3, finish: exact head m (of n_ex) of group e belongs to the work group
 //   whose rows hold x = e L + floor((2m + 1) L / (2 n_ex)). That work group
-//   finds b1 and the counts above and in it from the histogram, waits for
-//   the survivor flags of the group's work groups, selects the K best survivors
+//   finds b1 and the counts above and in it from the histogram, polls the
+//   head's survivor counts of the group's work groups until each carries the
+//   call flag, selects the K best survivors
 //   (radix select over the key bits below bin b1), writes S_t, aggregates the
 //   values and pushes (q_bar_t, S_t).
 //
@@ -1683,14 +1685,31 @@ __device__ __forceinline__ int3 wave_boundary(const uint32_t* hist, int keff) {
 constexpr int kEmitU = 8;
 constexpr int kEmitUGlobal = 32;
 
+// End of phase 2 for one segment in one wave: lane i holds the survivor count
+// of the wave's i-th head (jj = wave + 4 i). Once the wave's survivor stores
+// are complete, each exact head's count goes out with the call flag as one
+// 8-byte device-scope store; the finishing work group polls these words, so
+// the count arrives with the flag that publishes it.
+__device__ __forceinline__ void publish_counts(uint2* ccnt, int h0, int n_cu, int w, int G, unsigned emask, int run,
+                                               int call_flag) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kHeadThreads >> 6;
+  const int jj = wave + nw * lane;
+  wait_vmem();
+  if (jj < G && ((emask >> (jj & 31)) & 1u))
+    store_shared(ccnt + static_cast<long>(h0 + jj) * n_cu + w,
+                 make_uint2(static_cast<uint32_t>(run), static_cast<uint32_t>(call_flag)));
+}
+
 template <bool kLds>
 __device__ __forceinline__ void emit_segment(const Dims& d, const BufsDev& b, int bb, int g, unsigned emask, int row0,
-                                             int rend, int length, int w, int par, const float* sc, int stride) {
+                                             int rend, int length, int w, int par, int call_flag, const float* sc,
+                                             int stride) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = kHeadThreads >> 6;
   const int G = d.G;
   const int h0 = bb * d.Hq + g * G;  // query head of jj = 0
   const int nrows = rend - row0;
-  for (int jj = wave; jj < G; jj += nw) {
+  int my_run = 0;  // lane i: the count of this wave's i-th head
+  for (int jj = wave, slot = 0; jj < G; jj += nw, ++slot) {
     if (!((emask >> jj) & 1u)) continue;
     const int b1 = wave_boundary(b.hist + (static_cast<long>(h0 + jj) * 2 + par) * kNumBins, min(d.K, length)).x;
     // bin(x) >= b1 as one unsigned compare: s ^ ((s >> 31) | 2^31) orders the
@@ -1716,8 +1735,9 @@ __device__ __forceinline__ void emit_segment(const Dims& d, const BufsDev& b, in
         run += __popcll(m);
       }
     }
-    if (lane == 0) store_shared(b.ccnt + static_cast<long>(h0 + jj) * d.n_cu + w, run);
+    if (lane == slot) my_run = run;
   }
+  publish_counts(b.ccnt, h0, d.n_cu, w, G, emask, my_run, call_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -2149,12 +2169,13 @@ __device__ __forceinline__ int kb_close(const Dims& d, const BufsDev& b, int bb,
 // Phase 2 from a list (sorted by row): as emit_segment, reading (score key,
 // row) entries.
 __device__ __forceinline__ void emit_kb(const Dims& d, const BufsDev& b, int bb, int g, unsigned emask, int row0,
-                                        int length, int w, int par, const uint2* lists, int stride,
+                                        int length, int w, int par, int call_flag, const uint2* lists, int stride,
                                         const int* kcnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = kHeadThreads >> 6;
   const int G = d.G;
   const int h0 = bb * d.Hq + g * G;
-  for (int jj = wave; jj < G; jj += nw) {
+  int my_run = 0;  // lane i: the count of this wave's i-th head
+  for (int jj = wave, slot = 0; jj < G; jj += nw, ++slot) {
     if (!((emask >> jj) & 1u)) continue;
     const int b1 = wave_boundary(b.hist + (static_cast<long>(h0 + jj) * 2 + par) * kNumBins, min(d.K, length)).x;
     const uint32_t k0 = static_cast<uint32_t>(b1) << kHistShift;
@@ -2174,8 +2195,9 @@ __device__ __forceinline__ void emit_kb(const Dims& d, const BufsDev& b, int bb,
         run += __popcll(m);
       }
     }
-    if (lane == 0) store_shared(b.ccnt + static_cast<long>(h0 + jj) * d.n_cu + w, run);
+    if (lane == slot) my_run = run;
   }
+  publish_counts(b.ccnt, h0, d.n_cu, w, G, emask, my_run, call_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -2198,10 +2220,10 @@ constexpr int kSU = 8;  // survivors per thread per round
 
 // Every thread of the block must call it.
 // bd: (b1, count above b1, count in b1).
-__device__ __forceinline__ void finish_phase(const Dims& d, const BufsDev& b, int bh, const uint16_t* q, long q_sb,
-                                             long q_sh, const uint16_t* v, float* out,
-                                             int32_t* sel_out, int length, int push, long T, int nW, int ne, int e,
-                                             int3 bd, HeadShared& sh, unsigned char* dyn) {
+__device__ __forceinline__ bool finish_phase(const Dims& d, const BufsDev& b, int bh, const uint16_t* q, long q_sb,
+                                             long q_sh, const uint16_t* v, float* out, int32_t* sel_out, int length,
+                                             int push, int call_flag, long T, int nW, int ne, int e, HeadShared& sh,
+                                             unsigned char* dyn, int& vpar) {
   const int tid = threadIdx.x;
   // one round of loads: this thread's segment count, the FIFO state and (for
   // the push) q_bar_t
@@ -2212,8 +2234,29 @@ __device__ __forceinline__ void finish_phase(const Dims& d, const BufsDev& b, in
                                         : 0u;
   int slo = 0, shi = 0;
   if (tid < nW) seg_rows(T, nW, length, ne, tid, e, slo, shi);
-  const int cc = (tid < nW && slo < shi) ? load_shared(b.ccnt + static_cast<long>(bh) * d.n_cu + tid) : 0;
   const int fifo_slot = b.fifo[2 * bh], fifo_count = b.fifo[2 * bh + 1];
+  // the survivor count of every segment of the group, polled until each
+  // carries this call's flag (one thread per work group; bounded in time)
+  int cc = 0;
+  {
+    const bool chk = tid < nW && slo < shi;
+    const uint2* crow = b.ccnt + static_cast<long>(bh) * d.n_cu + tid;
+    const long long t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+      const uint2 c2 = chk ? load_shared(crow) : make_uint2(0u, static_cast<uint32_t>(call_flag));
+      cc = static_cast<int>(c2.x);
+      if (block_all(c2.y == static_cast<uint32_t>(call_flag), sh.vote, vpar)) break;
+      if (tid == 0) sh.i3 = __builtin_amdgcn_s_memrealtime() - t0 >= kWaitTicks ? -1 : 0;
+      lds_barrier();
+      if (sh.i3 < 0) {
+        if (tid == 0) store_shared(b.err, 1);
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(kPollSleep);
+    }
+  }
+  // (b1, count above b1, count in b1), from wave 0 before the poll's barriers
+  const int3 bd = make_int3(sh.i0, sh.i1, sh.i2);
   int* aoff = reinterpret_cast<int*>(dyn);
   int* srow0 = aoff + (nW + 4) / 4 * 4;
   const size_t off_c = 4 * static_cast<size_t>((nW + 4) / 4 * 4 + (nW + 3) / 4 * 4);
@@ -2366,6 +2409,7 @@ __device__ __forceinline__ void finish_phase(const Dims& d, const BufsDev& b, in
   n = min(n, keff);
   lds_barrier();
   finish_tail(d, b, bh, n, v, out, sel_out, push, fifo_slot, fifo_count, sh, s_sel, s_selsc, qb0, qb1);
+  return true;
 }
 
 // w: this score work group's index among the nW of them. all_exact: every
@@ -2583,27 +2627,26 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
   };
 
   // ---- phase 2: survivors of every segment ----
+  uint64_t seen = 0;  // bit e - e0: list group e is known to be fully scored
   for (int e = e0, r = r0, lb = 0, si = 0; e < e1 || (e == e1 && r < r1); ++e, r = 0) {
     const int row0 = r, rend = e == e1 ? r1 : length;
     if (row0 >= rend) continue;
     const int bg = s_eg[e] & 0xffff;
     if (!wait_group(b.wdone, T, nW, length, ne, e, call_flag, b.err, &sh.i3, sh.vote, vpar)) return;
+    if (e - e0 < 64) seen |= 1ull << (e - e0);
     if (use_kb) {
-      emit_kb(d, b, bg / d.Hkv, bg % d.Hkv, static_cast<unsigned>(s_eg[e]) >> 16, row0, length, w, par,
+      emit_kb(d, b, bg / d.Hkv, bg % d.Hkv, static_cast<unsigned>(s_eg[e]) >> 16, row0, length, w, par, call_flag,
               reinterpret_cast<const uint2*>(dyn + kb_tc_bytes(d)) + static_cast<long>(si) * d.G * kp,
               s_kbstride[si], s_kb.cnt[si]);
       ++si;
     } else if (keep > 0)
       emit_segment<true>(d, b, bg / d.Hkv, bg % d.Hkv, static_cast<unsigned>(s_eg[e]) >> 16, row0, rend, length, w,
-                         par, s_sc + lb, stride);
+                         par, call_flag, s_sc + lb, stride);
     else
       emit_segment<false>(d, b, bg / d.Hkv, bg % d.Hkv, static_cast<unsigned>(s_eg[e]) >> 16, row0, rend, length, w,
-                          par, nullptr, stride);
+                          par, call_flag, nullptr, stride);
     lb += (rend - row0 + 15) & ~15;
   }
-  wait_vmem();      // this wave's survivor and count stores have completed ...
-  __syncthreads();  // ... in every wave, before the flag that publishes them
-  if (threadIdx.x == 0) store_shared(b.wdone + (d.n_cu + w) * kFlagStride, call_flag);
 
   // ---- phase 3: finish the owned heads ----
   for (int e = ea; e <= eb; ++e) {
@@ -2614,8 +2657,10 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
       if (!owned(e, m, nex)) continue;
       const int bh = (bg / d.Hkv) * d.Hq + (bg % d.Hkv) * d.G + nth_bit(emask, m);
       // the head's boundary (its group is fully scored once this work group's
-      // own segments have passed phase 2; else wait for that here)
-      if (!wait_group(b.wdone, T, nW, length, ne, e, call_flag, b.err, &sh.i3, sh.vote, vpar)) return;
+      // own segment of it has passed phase 2; else wait for that here), read
+      // by wave 0 into sh.i0 .. i2 while the finish polls the survivor counts
+      const bool scored = e - e0 < 64 && ((seen >> (e - e0)) & 1);
+      if (!scored && !wait_group(b.wdone, T, nW, length, ne, e, call_flag, b.err, &sh.i3, sh.vote, vpar)) return;
       if ((threadIdx.x >> 6) == 0) {
         const int3 bd = wave_boundary(b.hist + (static_cast<long>(bh) * 2 + par) * kNumBins, min(d.K, length));
         if (threadIdx.x == 0) {
@@ -2624,10 +2669,9 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
           sh.i2 = bd.z;
         }
       }
-      if (!wait_group(b.wdone + d.n_cu * kFlagStride, T, nW, length, ne, e, call_flag, b.err, &sh.i3, sh.vote, vpar)) return;
-      const int3 bd = make_int3(sh.i0, sh.i1, sh.i2);
-      lds_barrier();  // (the finish reuses sh.i0 ..)
-      finish_phase(d, b, bh, q, q_sb, q_sh, v, out, sel_out, length, push, T, nW, ne, e, bd, sh, dyn);
+      if (!finish_phase(d, b, bh, q, q_sb, q_sh, v, out, sel_out, length, push, call_flag, T, nW, ne, e, sh, dyn,
+                        vpar))
+        return;
       lds_barrier();  // the next finish reuses the LDS
     }
   }
@@ -2660,7 +2704,9 @@ __global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, const Bufs* __res
   // would keep it live through both roles: each role reads its own copy.
   const int BH = d.B * d.Hq;
   const int w = static_cast<int>(blockIdx.x);
-  if (w < BH) {
+  // (marked likely so that the head role's code comes first: its addresses
+  // then stay put when the score role's code changes size)
+  if (__builtin_expect(w < BH, 1)) {
     head_role(d, *(ConstBufs*)(reinterpret_cast<uintptr_t>(bp)), q, q_sb, q_sh, k, v, out, length, t_dec, mode, stats_slot,
               call_flag, w, sh);
   } else {
