@@ -2101,7 +2101,7 @@ __device__ __forceinline__ void qk_score_kb(const Dims& d, const QkTiles& t, con
 // half of the heads' global histograms: one wave per head, over the bins the
 // head's score keys span, 256 at a time in the wave's own LDS. Returns the
 // lists' stride. Every thread of the block must call it.
-__device__ __forceinline__ int kb_close(const Dims& d, const BufsDev& b, int bb, int g, unsigned emask, int par,
+__device__ __forceinline__ int kb_close(const Dims& d, ConstBufs& b, int bb, int g, unsigned emask, int par,
                                         uint2* lists, int cap, int kp, bool last, KbState& ks, int* kcnt,
                                         HeadShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = kHeadThreads >> 6;
@@ -2412,12 +2412,22 @@ __device__ __forceinline__ bool finish_phase(const Dims& d, const BufsDev& b, in
   return true;
 }
 
+// Clears the other half (the next call's) of score work group w's slice of
+// the heads' histograms. (w BH < 2^29: 32-bit divisions)
+__device__ __forceinline__ void clear_next_half(ConstBufs& b, int w, int nW, int BH, int par) {
+  for (int hh = static_cast<int>(static_cast<uint32_t>(w * BH) / static_cast<uint32_t>(nW));
+       hh < static_cast<int>(static_cast<uint32_t>((w + 1) * BH) / static_cast<uint32_t>(nW)); ++hh) {
+    uint4* hz = reinterpret_cast<uint4*>(b.hist + (static_cast<long>(hh) * 2 + (par ^ 1)) * kNumBins);
+    for (int i = threadIdx.x; i < kNumBins / 4; i += kHeadThreads) hz[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
 // w: this score work group's index among the nW of them. all_exact: every
 // head of the call is exact (no flags to wait for). keep: rows per head of
 // LDS for the scores of phase 1 (a multiple of 16; 0: they go to the score
 // workspace, or, with kLong, into K-best lists where those fit).
 template <bool kLong>
-__device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, const uint16_t* q, long q_sb, long q_sh,
+__device__ __forceinline__ void score_role(const Dims& d, ConstBufs& bt, const uint16_t* q, long q_sb, long q_sh,
                                            const uint16_t* k, const uint16_t* v, float* out, int32_t* sel_out,
                                            int length, int push, int call_flag, int w, int nW, bool all_exact,
                                            int keep, HeadShared& sh) {
@@ -2438,14 +2448,11 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
   const int stride = keep + 4;
   float* s_sc = reinterpret_cast<float*>(dyn + static_cast<size_t>(d.G) * kNumBins * 4);
 
-  // clear the other half of a slice of the heads' histograms for the next call
-  // (first, so that a call that gives up below still leaves it clear)
+  // clear the other half of a slice of the heads' histograms for the next
+  // call: once on every way out of the work group, in phase 1 after the first
+  // key loads are requested (the table read it needs then waits beside them)
   // (w BH < 2^29: 32-bit divisions)
-  for (int hh = static_cast<int>(static_cast<uint32_t>(w * BH) / static_cast<uint32_t>(nW));
-       hh < static_cast<int>(static_cast<uint32_t>((w + 1) * BH) / static_cast<uint32_t>(nW)); ++hh) {
-    uint4* hz = reinterpret_cast<uint4*>(b.hist + (static_cast<long>(hh) * 2 + (par ^ 1)) * kNumBins);
-    for (int i = threadIdx.x; i < kNumBins / 4; i += kHeadThreads) hz[i] = make_uint4(0u, 0u, 0u, 0u);
-  }
+  bool cleared = false;
 
   // every head's decision of this call, published by the head work groups
   // (lower block indices, so already running); bounded wait
@@ -2456,7 +2463,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
       lds_barrier();
       int mine = 1;
       for (int i = threadIdx.x; i < BH; i += kHeadThreads) {
-        const int x = load_shared(b.dec + i * kFlagStride);
+        const int x = load_shared(bt.dec + i * kFlagStride);
         mine &= (x | 1) == (call_flag | 1);
         if (x & 1) atomicOr(&s_ex[i >> 5], 1u << (i & 31));
       }
@@ -2465,7 +2472,8 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
       __builtin_amdgcn_s_sleep(kPollSleep);
     }
     if (!done) {
-      if (threadIdx.x == 0) store_shared(b.err, 1);
+      clear_next_half(bt, w, nW, BH, par);
+      if (threadIdx.x == 0) store_shared(bt.err, 1);
       return;
     }
   }
@@ -2486,7 +2494,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
       cnt += m != 0;
     }
     int o = block_exclusive_scan(cnt, &ne, s_tmp);
-    if (!all_exact && w == 0 && threadIdx.x == 0) b.hint[0] = ne;  // (host-mapped; sizes later launches)
+    if (!all_exact && w == 0 && threadIdx.x == 0) bt.hint[0] = ne;  // (host-mapped; sizes later launches)
     for (int bg = g0; bg < g1; ++bg) {
       const int bb = bg / d.Hkv, g = bg % d.Hkv;
       int m = all_exact ? (1 << d.G) - 1 : 0;
@@ -2498,7 +2506,10 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
     }
   }
   lds_barrier();
-  if (ne == 0) return;
+  if (ne == 0) {
+    clear_next_half(bt, w, nW, BH, par);
+    return;
+  }
   const long T = static_cast<long>(ne) * length;
   int e0, r0, e1, r1;
   split_at(T, nW, length, ne, w, e0, r0);
@@ -2532,6 +2543,10 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
       const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
       QkTiles ta, tb;
       qk_load(ta, kb, row0, rend, wave, nw, j, kq);
+      if (!cleared) {
+        clear_next_half(bt, w, nW, BH, par);
+        cleared = true;
+      }
       const int cap = kb_cap(d, si);
       int* tc = reinterpret_cast<int*>(dyn);  // two stages' slot tables
       uint2* lists = reinterpret_cast<uint2*>(dyn + kb_tc_bytes(d)) + static_cast<long>(si) * d.G * kp;
@@ -2553,7 +2568,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
         qk_score_kb(d, tb, bq, t0 + kStage, rend, wave, nw, j, kq, hv, theta, lists, cap, tc + d.G * kKbTc, s_kb,
                     emask, sh);
       }
-      const int stride = kb_close(d, b, bb, g, emask, par, lists, cap, kp, si == nseg - 1, s_kb, s_kb.cnt[si], sh);
+      const int stride = kb_close(d, bt, bb, g, emask, par, lists, cap, kp, si == nseg - 1, s_kb, s_kb.cnt[si], sh);
       if (threadIdx.x == 0) s_kbstride[si] = stride;
       ++si;
     }
@@ -2575,6 +2590,10 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
     const uint16_t* kb = k + static_cast<long>(bb * d.Hkv + g) * d.max_len * kHeadDim;
     QkTiles ta, tb;
     qk_load(ta, kb, row0, rend, wave, nw, j, kq);
+    if (!cleared) {
+      clear_next_half(bt, w, nW, BH, par);
+      cleared = true;
+    }
     const unsigned emask = static_cast<unsigned>(s_eg[e]) >> 16;
     lds_barrier();  // the previous segment's histogram flush is done
     for (int jj = 0; jj < d.G; ++jj)
@@ -2585,7 +2604,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
     // the workspace row
     const bool to_lds = keep > 0;
     lds_float* ldst = (lds_float*)(s_sc + (j < d.G ? j : 0) * stride);  // (address-space cast)
-    float* gdst = b.score + static_cast<long>(bb * d.Hq + h) * d.score_stride;
+    float* gdst = bt.score + static_cast<long>(bb * d.Hq + h) * d.score_stride;
     const int off = to_lds ? lb - row0 : 0;
     uint32_t* hrow = s_hist + j * kNumBins;
     const int kStage = 16 * kQkUnroll * nw;  // rows per stage
@@ -2599,7 +2618,7 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
     lds_barrier();
     for (int jj = 0; jj < d.G; ++jj) {
       if (!((emask >> jj) & 1)) continue;
-      uint32_t* ghist = b.hist + (static_cast<long>(bb * d.Hq + g * d.G + jj) * 2 + par) * kNumBins;
+      uint32_t* ghist = bt.hist + (static_cast<long>(bb * d.Hq + g * d.G + jj) * 2 + par) * kNumBins;
       for (int i = threadIdx.x; i < kNumBins; i += kHeadThreads) {
         const uint32_t c = s_hist[jj * kNumBins + i];
         if (c) atomicAdd(&ghist[i], c);
@@ -2607,9 +2626,15 @@ __device__ __forceinline__ void score_role(const Dims& d, const BufsDev& b, cons
     }
     lb += (rend - row0 + 15) & ~15;
   }
+  if (!cleared) clear_next_half(bt, w, nW, BH, par);  // (no rows in this call)
   wait_vmem();      // this wave's histogram adds (and workspace scores) have completed ...
   __syncthreads();  // ... in every wave, before the flag that publishes them
-  if (threadIdx.x == 0) store_shared(b.wdone + w * kFlagStride, call_flag);
+  if (threadIdx.x == 0) store_shared(bt.wdone + w * kFlagStride, call_flag);
+
+  // a copy of the table for the later phases (read while this work group
+  // scans: phase 1 reads its fields in place, so that its first key loads
+  // do not wait for the table)
+  const BufsDev b = bt;
 
   // the heads this work group finishes: head m of group e when x_m (see
   // above) falls in [xa, xb)
@@ -2710,7 +2735,7 @@ __global__ __launch_bounds__(kHeadThreads) void k_step(Dims d, const Bufs* __res
     head_role(d, *(ConstBufs*)(reinterpret_cast<uintptr_t>(bp)), q, q_sb, q_sh, k, v, out, length, t_dec, mode, stats_slot,
               call_flag, w, sh);
   } else {
-    const BufsDev b = *reinterpret_cast<const BufsDev*>(bp);
+    ConstBufs& b = *(ConstBufs*)(reinterpret_cast<uintptr_t>(bp));
     // every head is exact in an exact call and on a refresh step (Eq. 13):
     // then there are no decisions to wait for
     const bool all_exact = mode == kModeExact || (d.Tr > 0 && t_dec % d.Tr == 0);
