@@ -896,7 +896,7 @@ __device__ __forceinline__ void store_shared2(float* p, float a, float b) {
   store_shared(reinterpret_cast<uint2*>(p), make_uint2(__float_as_uint(a), __float_as_uint(b)));
 }
 
-constexpr int kPollSleep = 16;                // s_sleep between polls of a flag (about 0.4 us)
+constexpr int kPollSleep = 2;                 // s_sleep between polls of a flag (128 clocks, about 0.05 us)
 constexpr long long kWaitTicks = 20000000;    // give up a wait after 200 ms (s_memrealtime is 100 MHz)
 
 constexpr int kQkUnroll = 4;  // 16-row tiles per wave per stage: 512 rows per 8-wave work group
@@ -1562,7 +1562,7 @@ __device__ __forceinline__ void finish_tail(const Dims& d, const BufsDev& b, int
 // groups not yet resident get a CU as the head work groups end.
 // ---------------------------------------------------------------------------
 constexpr int kMaxExactGroups = 1024;  // KV groups (batch x KV heads) the row split can list
-constexpr int kPollRounds = 20000;     // polls of the decision flags before giving up (several ms)
+constexpr int kPollRounds = 20000;     // polls of the decision flags before giving up (tens of ms)
 
 // Where work group ww's share starts: list position e and row r (rounded
 // down to 16 inside the group; e == ne, r == 0 at the end). The share starts
