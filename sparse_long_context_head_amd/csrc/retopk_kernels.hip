@@ -1036,8 +1036,9 @@ constexpr int kMergeE = 4;                      // entries per thread: R K <= 4 
 // entries below x (a prefix count of the kept flags, pre). Writes the
 // distinct positions ascending to out and returns their number. Requires
 // n_ret * K <= kMergeE * 512. Every thread of the block must call it.
-__device__ __forceinline__ int union_merge(const Dims& d, ConstBufs& b, int bh, int n_ret, int wlo, int32_t* out,
-                                           int* lists, int* pre, HeadShared& sh) {
+template <int NR>
+__device__ __forceinline__ int union_merge_n(const Dims& d, ConstBufs& b, int bh, int n_ret, int wlo, int32_t* out,
+                                             int* lists, int* pre, HeadShared& sh) {
   const int tid = threadIdx.x;
   for (int j0 = 0; j0 < d.K; j0 += kHeadThreads) {
     const int j = j0 + tid;
@@ -1067,7 +1068,7 @@ __device__ __forceinline__ int union_merge(const Dims& d, ConstBufs& b, int bh, 
       cut = (c <= len && x < wlo) ? c : cut;
     }
     const int incl = wave_incl_scan(cut);
-    if (tid < n_ret) sh.moff[tid + 1] = incl;
+    if (tid < NR) sh.moff[tid + 1] = incl;  // (a list past n_ret: empty, at F)
     if (tid == 0) sh.moff[0] = 0;
   }
   lds_barrier();
@@ -1087,34 +1088,35 @@ __device__ __forceinline__ int union_merge(const Dims& d, ConstBufs& b, int bh, 
     }
   }
   // lb[e][r2]: entries of list r2 below xe[e]
-  int lb[kMergeE][kMergeR];
+  int lb[kMergeE][NR];
 #pragma unroll
   for (int e = 0; e < kMergeE; ++e)
 #pragma unroll
-    for (int r2 = 0; r2 < kMergeR; ++r2) lb[e][r2] = 0;
+    for (int r2 = 0; r2 < NR; ++r2) lb[e][r2] = 0;
   int step = 1;
   while (step * 2 <= nmax) step *= 2;
-  int nl[kMergeR];
+  // NR lists, those past n_ret empty (their searches never move) and read at
+  // list 0: no branch depends on n_ret, which keeps the loop's uniform values
+  // few (a branch per list held a lane mask per list through the loop)
+  int nl[NR], lo[NR];
 #pragma unroll
-  for (int r2 = 0; r2 < kMergeR; ++r2) nl[r2] = r2 < n_ret ? sh.moff[r2 + 1] - sh.moff[r2] : 0;
+  for (int r2 = 0; r2 < NR; ++r2) {
+    nl[r2] = sh.moff[r2 + 1] - sh.moff[r2];
+    lo[r2] = (r2 < n_ret ? r2 : 0) * d.K;
+  }
   // (every read is issued unconditionally at a clamped, valid index, so that
   // a round's reads are all in flight together)
   for (; step > 0; step >>= 1) {
-    int v[kMergeE][kMergeR];
+    int v[kMergeE][NR];
 #pragma unroll
-    for (int r2 = 0; r2 < kMergeR; ++r2) {
-      if (r2 >= n_ret) break;  // uniform
+    for (int r2 = 0; r2 < NR; ++r2)
 #pragma unroll
-      for (int e = 0; e < kMergeE; ++e)
-        v[e][r2] = lists[r2 * d.K + max(min(lb[e][r2] + step, nl[r2]) - 1, 0)];
-    }
+      for (int e = 0; e < kMergeE; ++e) v[e][r2] = lists[lo[r2] + max(min(lb[e][r2] + step, nl[r2]) - 1, 0)];
 #pragma unroll
-    for (int r2 = 0; r2 < kMergeR; ++r2) {
-      if (r2 >= n_ret) break;
+    for (int r2 = 0; r2 < NR; ++r2)
 #pragma unroll
       for (int e = 0; e < kMergeE; ++e)
         lb[e][r2] = (lb[e][r2] + step <= nl[r2] && v[e][r2] < xe[e]) ? lb[e][r2] + step : lb[e][r2];
-    }
   }
   uint32_t keep = 0u;
   int cnt = 0;
@@ -1122,9 +1124,8 @@ __device__ __forceinline__ int union_merge(const Dims& d, ConstBufs& b, int bh, 
   for (int e = 0; e < kMergeE; ++e) {
     bool dup = f0 + e >= F;
 #pragma unroll
-    for (int r2 = 0; r2 < kMergeR - 1; ++r2) {
-      if (r2 >= n_ret - 1) break;  // (the last list is never below another)
-      const int at = lists[r2 * d.K + min(lb[e][r2], max(nl[r2] - 1, 0))];
+    for (int r2 = 0; r2 < NR - 1; ++r2) {  // (the last list is never below another)
+      const int at = lists[lo[r2] + min(lb[e][r2], max(nl[r2] - 1, 0))];
       dup = dup || (r2 < re[e] && lb[e][r2] < nl[r2] && at == xe[e]);
     }
     if (!dup) {
@@ -1146,16 +1147,21 @@ __device__ __forceinline__ int union_merge(const Dims& d, ConstBufs& b, int bh, 
     if (!((keep >> e) & 1u)) continue;
     int pos = 0;
 #pragma unroll
-    for (int r2 = 0; r2 < kMergeR; ++r2) {
-      if (r2 >= n_ret) break;
+    for (int r2 = 0; r2 < NR; ++r2) {
       const int o2 = sh.moff[r2];
-      // (an entry's own list: lb is its index there, as the list is ascending)
+      // (an entry's own list: lb is its index there, as the list is ascending;
+      // an empty list at F adds pre[F] - pre[F] = 0)
       pos += pre[o2 + lb[e][r2]] - pre[o2];
     }
     out[pos] = xe[e];
   }
   lds_barrier();
   return total;
+}
+__device__ __forceinline__ int union_merge(const Dims& d, ConstBufs& b, int bh, int n_ret, int wlo, int32_t* out,
+                                           int* lists, int* pre, HeadShared& sh) {
+  return n_ret <= 4 ? union_merge_n<4>(d, b, bh, n_ret, wlo, out, lists, pre, sh)
+                    : union_merge_n<kMergeR>(d, b, bh, n_ret, wlo, out, lists, pre, sh);
 }
 
 // Bring all four 64-byte lines of the buffer table into the scalar cache at
