@@ -683,6 +683,21 @@ def test_scale_1m_every_head():
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
+def test_merged_union_with_empty_list_slots():
+    """Past one LDS bitmap window (L0 = 300,000) the reuse union merges the
+    retrieved supports, in a form compiled for 4 lists or for 8, with the slots
+    past the number retrieved left empty. R = 3 at K = 512 leaves one of 4 slots
+    empty; R = 6 at K = 256 (R K = 1536) takes the 8-list form with two empty.
+    KV group 1, every head forced onto the reuse path, 3 lockstep steps each."""
+    for top_r, top_k in ((3, 512), (6, 256)):
+        r = run_lockstep("scale1m", 3, sub=(0, 1), override=dict(top_k=top_k, top_r=top_r, tau=-2.0, refresh_every=0),
+                         check_init=False, wl_kw=dict(prompt_len=300000, decode_steps=8))
+        assert not r["paths"].any()
+        assert max(r["ms"]) > top_k
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_scale_1m_forced_reuse_k1024_bitmap_windows():
     """L0 = 1,048,576 with K = 1024, KV group 1 forced onto the reuse path
     (tau = -2, T_r = 0) for 3 lockstep steps: R K = 4096 is more than the
