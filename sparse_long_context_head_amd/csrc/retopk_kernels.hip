@@ -1692,10 +1692,10 @@ constexpr int kEmitU = 8;
 constexpr int kEmitUGlobal = 32;
 
 // End of phase 2 for one segment in one wave: lane i holds the survivor count
-// of the wave's i-th head (jj = wave + 4 i). Once the wave's survivor stores
-// are complete, each exact head's count goes out with the call flag as one
-// 8-byte device-scope store; the finishing work group polls these words, so
-// the count arrives with the flag that publishes it.
+// of the wave's i-th head (jj = wave + 8 i, 8 waves). Once the wave's survivor
+// stores are complete, each exact head's count goes out with the call flag as
+// one 8-byte device-scope store; the finishing work group polls these words,
+// so the count arrives with the flag that publishes it.
 __device__ __forceinline__ void publish_counts(uint2* ccnt, int h0, int n_cu, int w, int G, unsigned emask, int run,
                                                int call_flag) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = kHeadThreads >> 6;
@@ -2224,8 +2224,9 @@ __device__ __forceinline__ void emit_kb(const Dims& d, const BufsDev& b, int bb,
 // ---------------------------------------------------------------------------
 constexpr int kSU = 8;  // survivors per thread per round
 
-// Every thread of the block must call it.
-// bd: (b1, count above b1, count in b1).
+// Every thread of the block must call it. sh.i0 .. i2 hold (b1, count above
+// b1, count in b1), written by wave 0 before the call. Returns false when the
+// survivor-count poll timed out (the device error word is then set).
 __device__ __forceinline__ bool finish_phase(const Dims& d, const BufsDev& b, int bh, const uint16_t* q, long q_sb,
                                              long q_sh, const uint16_t* v, float* out, int32_t* sel_out, int length,
                                              int push, int call_flag, long T, int nW, int ne, int e, HeadShared& sh,
